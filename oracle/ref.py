@@ -1,0 +1,160 @@
+"""ctypes front end of the CPU oracle (``libbsa_ref.so``).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the GPU library or its binding.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbsa_ref.so")
+
+
+def build() -> str:
+    """Compile the oracle with gcc (plain C, OpenMP, no fast-math, no FMA contraction)."""
+    src = os.path.join(HERE, "bsa_ref.c")
+    tmp = LIB_PATH + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                           "-ffp-contract=off", "-Wall", "-Wno-unused-result", src, "-o", tmp, "-lm"])
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+class RefProblem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
+        ("sq", ctypes.c_int64), ("skv", ctypes.c_int64), ("d", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("bq", ctypes.POINTER(ctypes.c_int32)), ("bk", ctypes.POINTER(ctypes.c_int32)),
+        ("mask_broadcast", ctypes.c_int32), ("causal", ctypes.c_int32),
+        ("causal_offset", ctypes.c_int64), ("gqa_union", ctypes.c_int32),
+        ("paged", ctypes.c_int32), ("page_size", ctypes.c_int32),
+        ("pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+        ("scale", ctypes.c_double),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        L.ref_forward.argtypes = [P(RefProblem), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        L.ref_forward.restype = ctypes.c_int
+        L.ref_features.argtypes = [P(RefProblem), ctypes.c_void_p, ctypes.c_void_p]
+        L.ref_features.restype = ctypes.c_int
+        L.ref_plan.argtypes = [P(RefProblem), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_char_p,
+                               ctypes.c_void_p, ctypes.c_void_p, P(ctypes.c_size_t)]
+        L.ref_plan.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+class _Prob:
+    """Holds a RefProblem plus the arrays it points into."""
+
+    def __init__(self, w, scale: float = 0.0):
+        self.bq = np.ascontiguousarray(w.bq, dtype=np.int32)
+        self.bk = np.ascontiguousarray(w.bk, dtype=np.int32)
+        self.mask = np.ascontiguousarray(w.mask, dtype=np.uint8)
+        self.table = (np.ascontiguousarray(w.page_table, dtype=np.int32)
+                      if w.paged else None)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        self.s = RefProblem(
+            w.batch, w.hq, w.hkv, w.sq, w.skv, w.d, 0 if w.dtype == "bf16" else 1,
+            self.bq.ctypes.data_as(i32p), self.bk.ctypes.data_as(i32p),
+            int(w.mask_broadcast), int(w.causal), int(w.causal_offset), int(w.gqa_union),
+            int(w.paged), int(w.page_size), int(w.pages_per_seq), int(w.num_pages), float(scale))
+
+    def mask_ptr(self):
+        return self.mask.ctypes.data if self.mask.size else None
+
+    def table_ptr(self):
+        return self.table.ctypes.data if self.table is not None else None
+
+
+def _raw(x, dtype: str) -> np.ndarray:
+    """Contiguous numpy view of Q/K/V storage: uint16 bf16 bits or float32."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().contiguous()
+            if x.dtype == torch.bfloat16:
+                return x.view(torch.int16).numpy().view(np.uint16)
+            return x.numpy()
+    except ImportError:
+        pass
+    x = np.ascontiguousarray(x)
+    if dtype == "bf16":
+        assert x.dtype == np.uint16
+    else:
+        assert x.dtype == np.float32
+    return x
+
+
+def forward(w, q, k, v, mode: int = 1, rows=None, nthreads: int = 0, scale: float = 0.0):
+    """Oracle forward. Returns (o[n][d] float64, lse[n] float64).
+
+    rows: None for every (b, h, i) in order, or an int64 array of shape [n, 3].
+    """
+    P = _Prob(w, scale)
+    qa, ka, va = _raw(q, w.dtype), _raw(k, w.dtype), _raw(v, w.dtype)
+    if rows is None:
+        n = w.batch * w.hq * w.sq
+        rp = None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+        n = rows.shape[0]
+        rp = rows.ctypes.data
+    o = np.empty((max(n, 1), w.d), np.float64)
+    lse = np.empty(max(n, 1), np.float64)
+    rc = lib().ref_forward(ctypes.byref(P.s), P.mask_ptr(), P.table_ptr(), qa.ctypes.data,
+                           ka.ctypes.data, va.ctypes.data, mode, rp, n, o.ctypes.data,
+                           lse.ctypes.data, nthreads)
+    if rc:
+        raise ValueError(f"ref_forward rejected the problem ({rc})")
+    return o[:n], lse[:n]
+
+
+def features(w) -> np.ndarray:
+    P = _Prob(w)
+    nbm = 1 if w.mask_broadcast else w.batch
+    out = np.zeros((nbm, w.hq, 4), np.int64)
+    rc = lib().ref_features(ctypes.byref(P.s), P.mask_ptr(), out.ctypes.data)
+    if rc:
+        raise ValueError(f"ref_features rejected the problem ({rc})")
+    return out
+
+
+def plan(w, lut_text=None, force=None) -> bytes:
+    """Canonical plan image from the reference planner."""
+    P = _Prob(w)
+    f = None
+    if force is not None:
+        f = np.ascontiguousarray(force, dtype=np.int32)
+        assert f.size == 5
+    lut = lut_text.encode() if isinstance(lut_text, str) else lut_text
+    n = ctypes.c_size_t(0)
+    L = lib()
+    rc = L.ref_plan(ctypes.byref(P.s), P.mask_ptr(), P.table_ptr(), lut,
+                    f.ctypes.data if f is not None else None, None, ctypes.byref(n))
+    if rc:
+        raise ValueError(f"ref_plan failed ({rc})")
+    buf = np.zeros(n.value, np.uint8)
+    rc = L.ref_plan(ctypes.byref(P.s), P.mask_ptr(), P.table_ptr(), lut,
+                    f.ctypes.data if f is not None else None, buf.ctypes.data, ctypes.byref(n))
+    if rc:
+        raise ValueError(f"ref_plan failed ({rc})")
+    return buf.tobytes()
