@@ -1,0 +1,516 @@
+// libbsa C ABI: argument checking, regime lookup table, plan object, forward
+// launch, plan export and statistics.
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <fstream>
+#include <sstream>
+
+#include "bsa_internal.h"
+
+namespace bsa {
+
+static thread_local std::string g_err;
+
+bsa_status fail(bsa_status s, const std::string &msg) {
+  g_err = msg;
+  return s;
+}
+
+#define HIP_TRY(expr)                                                          \
+  do {                                                                         \
+    hipError_t e_ = (expr);                                                    \
+    if (e_ != hipSuccess)                                                      \
+      return fail(BSA_ERR_HIP, std::string(#expr ": ") + hipGetErrorString(e_)); \
+  } while (0)
+
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static bool is_block(int32_t x) { return x >= 16 && x <= 512 && (x & (x - 1)) == 0; }
+static int ilog2(int64_t x) {
+  int r = 0;
+  while ((int64_t(1) << (r + 1)) <= x) ++r;
+  return r;
+}
+static size_t aligned(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------------------
+// Regime lookup table (Tessera, abstract: profile-guided regime selection
+// through a lookup table constructed from offline profiling).
+// ---------------------------------------------------------------------------
+struct Rule {
+  int64_t key[4];  // D, dtype, union, paged (-1 = any)
+  int64_t lo[4], hi[4];
+  Regime r;
+};
+
+}  // namespace bsa
+
+struct bsa_lut_s {
+  std::vector<bsa::Rule> rules;
+};
+
+namespace bsa {
+
+static bool parse_i64(const std::string &t, int64_t *out) {
+  if (t.empty()) return false;
+  char *end = nullptr;
+  long long v = std::strtoll(t.c_str(), &end, 10);
+  if (*end) return false;
+  *out = v;
+  return true;
+}
+
+static bsa_status parse_lut(const char *text, bsa_lut_s *lut) {
+  // Tokenise, dropping '#' comments.
+  std::vector<std::string> tok;
+  std::istringstream lines(text);
+  std::string line;
+  while (std::getline(lines, line)) {
+    const size_t hash = line.find('#');
+    if (hash != std::string::npos) line.resize(hash);
+    std::istringstream ws(line);
+    std::string t;
+    while (ws >> t) tok.push_back(t);
+  }
+  size_t i = 0;
+  auto next = [&](std::string &t) {
+    if (i >= tok.size()) return false;
+    t = tok[i++];
+    return true;
+  };
+  std::string t;
+  int64_t x;
+  if (!next(t) || t != "bsa-lut" || !next(t) || !parse_i64(t, &x) || x != 1)
+    return fail(BSA_ERR_LUT, "lookup table must start with 'bsa-lut 1'");
+  while (next(t)) {
+    if (t != "rule") return fail(BSA_ERR_LUT, "expected 'rule', got '" + t + "'");
+    Rule r{};
+    for (int f = 0; f < 4; ++f) {
+      if (!next(t)) return fail(BSA_ERR_LUT, "truncated rule");
+      if (t == "*") r.key[f] = -1;
+      else if (f == 1 && t == "bf16") r.key[f] = BSA_BF16;
+      else if (f == 1 && t == "f32") r.key[f] = BSA_F32;
+      else if (f != 1 && parse_i64(t, &x) && x >= 0) r.key[f] = x;
+      else return fail(BSA_ERR_LUT, "bad rule key '" + t + "'");
+    }
+    for (int f = 0; f < 4; ++f) {
+      if (!next(t) || !parse_i64(t, &r.lo[f]) || !next(t) || !parse_i64(t, &r.hi[f]))
+        return fail(BSA_ERR_LUT, "bad rule range");
+    }
+    if (!next(t) || t != "->") return fail(BSA_ERR_LUT, "expected '->' in rule");
+    int64_t v[5];
+    for (int f = 0; f < 5; ++f) {
+      if (!next(t)) return fail(BSA_ERR_LUT, "truncated rule");
+      if (f == 2 && t == "local") v[f] = 0;
+      else if (f == 2 && t == "lpt") v[f] = 1;
+      else if (f == 2 || !parse_i64(t, &v[f])) return fail(BSA_ERR_LUT, "bad regime value '" + t + "'");
+    }
+    if (v[0] != 128 || (v[1] != 64 && v[1] != 128) || v[3] < 0 || v[3] > (1 << 30) ||
+        (v[4] != 0 && v[4] != 1))
+      return fail(BSA_ERR_LUT, "regime out of range (Tq 128, Tk 64|128, split >= 0, pack 0|1)");
+    r.r = Regime{(int)v[0], (int)v[1], (int)v[2], (int)v[3], (int)v[4]};
+    lut->rules.push_back(r);
+  }
+  return BSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Problem checks (all before any device work)
+// ---------------------------------------------------------------------------
+static bsa_status check_problem(const bsa_problem *p, const uint8_t *mask, const int32_t *table) {
+  if (!p) return fail(BSA_ERR_INVALID_ARG, "problem is NULL");
+  if (p->batch < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1)
+    return fail(BSA_ERR_INVALID_ARG, "batch and head counts must be >= 1");
+  if (p->num_q_heads % p->num_kv_heads)
+    return fail(BSA_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  if (p->seqlen_q < 0 || p->seqlen_kv < 0) return fail(BSA_ERR_INVALID_ARG, "negative sequence length");
+  if (p->seqlen_q > (int64_t(1) << 31) || p->seqlen_kv > (int64_t(1) << 31))
+    return fail(BSA_ERR_UNSUPPORTED, "sequence length above 2^31");
+  if (p->head_dim != 64 && p->head_dim != 128) return fail(BSA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (p->dtype != BSA_BF16 && p->dtype != BSA_F32) return fail(BSA_ERR_INVALID_ARG, "unknown dtype");
+  if (!p->block_q || !p->block_k) return fail(BSA_ERR_INVALID_ARG, "block_q / block_k is NULL");
+  for (int h = 0; h < p->num_q_heads; ++h)
+    if (!is_block(p->block_q[h]) || !is_block(p->block_k[h]))
+      return fail(BSA_ERR_UNSUPPORTED, "block sizes must be powers of two in [16, 512] (head " +
+                                           std::to_string(h) + ")");
+  if ((p->mask_batch_broadcast | p->causal | p->gqa_union | p->paged) & ~1)
+    return fail(BSA_ERR_INVALID_ARG, "flags must be 0 or 1");
+  if (!(p->softmax_scale >= 0.f) || std::isinf(p->softmax_scale))
+    return fail(BSA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  if (p->gqa_union) {
+    const int gs = p->num_q_heads / p->num_kv_heads;
+    for (int h = 0; h < p->num_q_heads; ++h)
+      if (p->block_k[h] != p->block_k[(h / gs) * gs])
+        return fail(BSA_ERR_INVALID_ARG, "gqa_union needs equal block_k within each kv group");
+  }
+  if (p->paged) {
+    if (p->page_size < 64 || p->page_size % 64)
+      return fail(BSA_ERR_UNSUPPORTED, "page_size must be a positive multiple of 64");
+    if (p->pages_per_seq < 1 || p->num_pages < 1)
+      return fail(BSA_ERR_INVALID_ARG, "pages_per_seq and num_pages must be >= 1");
+    if ((int64_t)p->page_size * p->pages_per_seq < p->seqlen_kv)
+      return fail(BSA_ERR_INVALID_ARG, "page table too short for seqlen_kv");
+    if (!table) return fail(BSA_ERR_INVALID_ARG, "paged problem needs a page table");
+  }
+  int64_t msize = 0;
+  for (int h = 0; h < p->num_q_heads; ++h)
+    msize += cdiv(p->seqlen_q, p->block_q[h]) * cdiv(p->seqlen_kv, p->block_k[h]);
+  if (msize > 0 && !mask) return fail(BSA_ERR_INVALID_ARG, "mask is NULL");
+  return BSA_OK;
+}
+
+static void free_plan(bsa_plan_s *p) {
+  if (!p) return;
+  if (p->pre) (void)hipFree(p->pre);
+  if (p->arena) (void)hipFree(p->arena);
+  delete p;
+}
+
+// Regime: forced by the table's first matching rule, then made valid.
+static bsa_status choose_regime(Plan &p, const bsa_lut_s *lut) {
+  Regime rg;
+  if (lut) {
+    const int64_t key[4] = {p.D, p.dtype, p.uni, p.paged};
+    const int64_t val[4] = {p.min_bq, p.min_bk, p.density_pm, p.imb16};
+    for (const Rule &r : lut->rules) {
+      bool ok = true;
+      for (int f = 0; f < 4; ++f) {
+        if (r.key[f] >= 0 && r.key[f] != key[f]) ok = false;
+        if (val[f] < r.lo[f] || val[f] > r.hi[f]) ok = false;
+      }
+      if (ok) {
+        rg = r.r;
+        break;
+      }
+    }
+  }
+  if (!(p.uni && (p.G == 2 || p.G == 4))) rg.pack = 0;
+  if (p.dtype == BSA_F32) rg.tk = 64;
+  if (p.paged && p.P % rg.tk) {
+    if (rg.tk == 128 && p.P % 64 == 0) rg.tk = 64;
+    else return fail(BSA_ERR_UNSUPPORTED, "page_size not a multiple of the key tile");
+  }
+  for (int pass = 0; pass < 2; ++pass) {
+    bool bad = false;
+    for (int h = 0; h < p.Hq; ++h) {
+      const int mq = (!p.uni && p.bq[h] < rg.tq) ? rg.tq / p.bq[h] : 1;
+      const int mk = p.bk[h] < rg.tk ? rg.tk / p.bk[h] : 1;
+      if (mq * mk > 32) bad = true;
+    }
+    if (!bad) break;
+    if (pass == 0 && rg.tk == 128) {
+      rg.tk = 64;
+      continue;
+    }
+    return fail(BSA_ERR_UNSUPPORTED, "block sizes too small for the tile (more than 32 sub-blocks)");
+  }
+  p.rg = rg;
+  return BSA_OK;
+}
+
+}  // namespace bsa
+
+using namespace bsa;
+
+extern "C" {
+
+int bsa_abi_version(void) { return BSA_ABI_VERSION; }
+
+const char *bsa_status_str(bsa_status s) {
+  switch (s) {
+    case BSA_OK: return "ok";
+    case BSA_ERR_INVALID_ARG: return "invalid argument";
+    case BSA_ERR_UNSUPPORTED: return "unsupported";
+    case BSA_ERR_SHAPE_MISMATCH: return "shape mismatch";
+    case BSA_ERR_OUT_OF_MEMORY: return "out of memory";
+    case BSA_ERR_HIP: return "HIP error";
+    case BSA_ERR_LUT: return "lookup table error";
+  }
+  return "unknown status";
+}
+
+const char *bsa_last_error(void) { return g_err.c_str(); }
+
+bsa_status bsa_lut_parse(const char *text, bsa_lut_t *out) {
+  if (!text || !out) return fail(BSA_ERR_INVALID_ARG, "text or out is NULL");
+  *out = nullptr;
+  auto *l = new bsa_lut_s;
+  if (bsa_status s = parse_lut(text, l)) {
+    delete l;
+    return s;
+  }
+  *out = l;
+  return BSA_OK;
+}
+
+bsa_status bsa_lut_load(const char *path, bsa_lut_t *out) {
+  if (!out) return fail(BSA_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!path) {
+    *out = new bsa_lut_s;
+    return BSA_OK;
+  }
+  std::ifstream f(path);
+  if (!f) return fail(BSA_ERR_LUT, std::string("cannot open lookup table ") + path);
+  std::stringstream ss;
+  ss << f.rdbuf();
+  return bsa_lut_parse(ss.str().c_str(), out);
+}
+
+void bsa_lut_free(bsa_lut_t lut) { delete lut; }
+
+bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *page_table,
+                    bsa_lut_t lut, void *stream, bsa_plan_t *out) {
+  if (!out) return fail(BSA_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (bsa_status s = check_problem(pr, mask, page_table)) return s;
+
+  bsa_plan_s *p = new bsa_plan_s();
+  Plan &P = *p;
+  P.B = pr->batch, P.Hq = pr->num_q_heads, P.Hkv = pr->num_kv_heads, P.G = P.Hq / P.Hkv;
+  P.D = pr->head_dim, P.dtype = pr->dtype, P.Sq = pr->seqlen_q, P.Skv = pr->seqlen_kv;
+  P.causal = pr->causal, P.off = pr->causal_kv_offset, P.uni = pr->gqa_union;
+  P.paged = pr->paged, P.P = pr->paged ? pr->page_size : 0, P.pps = pr->paged ? pr->pages_per_seq : 0;
+  P.npages = pr->paged ? pr->num_pages : 0, P.bcast = pr->mask_batch_broadcast;
+  P.scale = pr->softmax_scale > 0.f ? pr->softmax_scale : 1.f / std::sqrt((float)P.D);
+  P.bq.assign(pr->block_q, pr->block_q + P.Hq);
+  P.bk.assign(pr->block_k, pr->block_k + P.Hq);
+  P.nbm = P.bcast ? 1 : P.B;
+  P.nlb = (P.paged || !P.bcast) ? P.B : 1;
+  P.stream = (hipStream_t)stream;
+  P.unkb = 0;
+  for (int h = 0; h < P.Hq; ++h) P.unkb = std::max<int64_t>(P.unkb, cdiv(P.Skv, P.bk[h]));
+  if (hipGetDevice(&P.device) != hipSuccess) {
+    free_plan(p);
+    return fail(BSA_ERR_HIP, "hipGetDevice failed");
+  }
+
+  // ---- phase 1: features (one device-to-host read) ----
+  const size_t feat_bytes = sizeof(int64_t) * 4 * P.nbm * P.Hq;
+  const size_t pre_bytes = aligned(feat_bytes) + aligned(sizeof(int32_t) * CNT_N) +
+                           aligned(sizeof(HeadMeta) * P.Hq) +
+                           aligned((size_t)P.nbm * P.Hkv * std::max<int64_t>(P.unkb, 1));
+  if (hipMalloc(&P.pre, pre_bytes) != hipSuccess) {
+    free_plan(p);
+    return fail(BSA_ERR_OUT_OF_MEMORY, "device allocation of plan header failed");
+  }
+  uint8_t *pb = (uint8_t *)P.pre;
+  P.feat_dev = (unsigned long long *)pb;
+  pb += aligned(feat_bytes);
+  P.counters = (int32_t *)pb;
+  pb += aligned(sizeof(int32_t) * CNT_N);
+  P.hmeta = (HeadMeta *)pb;
+  pb += aligned(sizeof(HeadMeta) * P.Hq);
+  P.uni_bits = pb;
+  auto bail = [&](bsa_status s) {
+    free_plan(p);
+    return s;
+  };
+  if (hipMemsetAsync(P.pre, 0, aligned(feat_bytes) + aligned(sizeof(int32_t) * CNT_N), P.stream) != hipSuccess)
+    return bail(fail(BSA_ERR_HIP, "hipMemsetAsync failed"));
+  if (bsa_status s = plan_features(P, mask, page_table)) return bail(s);
+  std::vector<int64_t> host(feat_bytes / 8 + CNT_N);
+  if (hipMemcpyAsync(host.data(), P.feat_dev, feat_bytes, hipMemcpyDeviceToHost, P.stream) != hipSuccess ||
+      hipMemcpyAsync(host.data() + feat_bytes / 8, P.counters, sizeof(int32_t) * CNT_N,
+                     hipMemcpyDeviceToHost, P.stream) != hipSuccess ||
+      hipStreamSynchronize(P.stream) != hipSuccess)
+    return bail(fail(BSA_ERR_HIP, std::string("reading mask features failed: ") +
+                                      hipGetErrorString(hipGetLastError())));
+  P.feat.assign(host.begin(), host.begin() + feat_bytes / 8);
+  const int32_t *hc = (const int32_t *)(host.data() + feat_bytes / 8);
+  if (hc[CNT_BADPAGE]) return bail(fail(BSA_ERR_INVALID_ARG, "page table entry outside [0, num_pages)"));
+
+  // ---- aggregates and regime ----
+  P.total_nnz = P.total_blocks = P.imb16 = 0;
+  P.min_bq = P.min_bk = 1 << 30;
+  for (int64_t bm = 0; bm < P.nbm; ++bm)
+    for (int h = 0; h < P.Hq; ++h) {
+      const int64_t nq = cdiv(P.Sq, P.bq[h]), nk = cdiv(P.Skv, P.bk[h]);
+      const int64_t *f = &P.feat[(bm * P.Hq + h) * 4];
+      P.total_nnz += f[0];
+      P.total_blocks += nq * nk;
+      if (f[0] > 0) P.imb16 = std::max(P.imb16, 16 * f[1] * nq / f[0]);
+    }
+  for (int h = 0; h < P.Hq; ++h) {
+    P.min_bq = std::min<int64_t>(P.min_bq, P.bq[h]);
+    P.min_bk = std::min<int64_t>(P.min_bk, P.bk[h]);
+  }
+  P.density_pm = P.total_blocks ? 1000 * P.total_nnz / P.total_blocks : 0;
+  if (bsa_status s = choose_regime(P, lut)) return bail(s);
+
+  // ---- geometry and capacities ----
+  const int tq = P.rg.tq, tk = P.rg.tk;
+  P.tr = P.rg.pack ? tq / P.G : tq;
+  P.nqt = cdiv(P.Sq, P.tr);
+  P.nkt = cdiv(P.Skv, tk);
+  P.nlists = P.uni ? P.nlb * P.Hkv : P.nlb * P.Hq * P.nqt;
+  P.nrows = (int64_t)P.B * (P.rg.pack ? P.Hkv : P.Hq) * P.nqt;
+  int64_t row_total;  // upper bound on the sum of row lengths
+  if (P.uni) {
+    P.ent_cap = P.nlists * P.nkt;
+    row_total = P.nrows * P.nkt;
+  } else {
+    P.ent_cap = 0;
+    for (int64_t lb = 0; lb < P.nlb; ++lb)
+      for (int h = 0; h < P.Hq; ++h) {
+        const int64_t bm = P.nbm == 1 ? 0 : lb;
+        const int64_t sq = P.bq[h] > tq ? P.bq[h] / tq : 1, sk = P.bk[h] > tk ? P.bk[h] / tk : 1;
+        P.ent_cap += std::min(P.nqt * P.nkt, P.feat[(bm * P.Hq + h) * 4] * sq * sk);
+      }
+    row_total = P.ent_cap * (P.B / P.nlb);
+  }
+  const int64_t split = P.rg.split;
+  P.slot_cap = split > 0 ? std::min(2 * row_total / split + 1, P.nrows * cdiv(P.nkt, split)) : 0;
+  P.comb_cap = split > 0 ? std::min(P.nrows, row_total / (split + 1) + 1) : 0;
+  P.item_cap = P.nrows + P.slot_cap;
+  const int64_t lim = (int64_t(1) << 31) - 2;
+  if (P.ent_cap > lim || P.item_cap > lim || P.nrows > lim || P.nlists > lim)
+    return bail(fail(BSA_ERR_UNSUPPORTED, "plan too large (more than 2^31 entries or rows)"));
+  const size_t part_bytes = (size_t)P.slot_cap * 128 * (P.D + 1) * sizeof(float);
+  if (part_bytes > (size_t(64) << 30))
+    return bail(fail(BSA_ERR_UNSUPPORTED, "split threshold too small: partial buffers above 64 GiB"));
+
+  // ---- phase 2: the arena, then the rest of the planning on the stream ----
+  std::vector<std::pair<void **, size_t>> parts = {
+      {(void **)&P.list_off, sizeof(int32_t) * (P.nlists + 1)},
+      {(void **)&P.ent_kt, sizeof(int32_t) * std::max<int64_t>(P.ent_cap, 1)},
+      {(void **)&P.ent_page, P.paged ? sizeof(int32_t) * std::max<int64_t>(P.ent_cap, 1) : 0},
+      {(void **)&P.ent_live, sizeof(uint32_t) * std::max<int64_t>(P.ent_cap, 1)},
+      {(void **)&P.row_ent, sizeof(int32_t) * 2 * std::max<int64_t>(P.nrows, 1)},
+      {(void **)&P.items, sizeof(int32_t) * 4 * std::max<int64_t>(P.item_cap, 1)},
+      {(void **)&P.comb, sizeof(int32_t) * 3 * std::max<int64_t>(P.comb_cap, 1)},
+      {(void **)&P.part_o, sizeof(float) * P.slot_cap * 128 * P.D},
+      {(void **)&P.part_lse, sizeof(float) * P.slot_cap * 128},
+  };
+  size_t total = 0;
+  for (auto &pt : parts) total += aligned(pt.second);
+  const size_t scratch = plan_scratch_bytes(P);
+  total += scratch;
+  if (hipMalloc(&P.arena, total) != hipSuccess)
+    return bail(fail(BSA_ERR_OUT_OF_MEMORY, "device allocation of " + std::to_string(total) + " plan bytes failed"));
+  uint8_t *ap = (uint8_t *)P.arena;
+  for (auto &pt : parts) {
+    *pt.first = pt.second ? ap : nullptr;
+    ap += aligned(pt.second);
+  }
+  if (bsa_status s = plan_build(P, mask, page_table, ap, scratch)) return bail(s);
+  *out = p;
+  return BSA_OK;
+}
+
+bsa_status bsa_forward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v,
+                       bsa_tensor *o, float *lse, void *stream) {
+  if (!plan || !q || !k || !v || !o) return fail(BSA_ERR_INVALID_ARG, "NULL plan or tensor");
+  const Plan &P = *plan;
+  const bool any_q = P.B * (int64_t)P.Hq * P.Sq > 0;
+  if (any_q && (!q->data || !o->data || !lse)) return fail(BSA_ERR_INVALID_ARG, "NULL Q, O or LSE data");
+  if (any_q && P.Skv > 0 && (!k->data || !v->data)) return fail(BSA_ERR_INVALID_ARG, "NULL K or V data");
+  const int64_t esz = P.dtype == BSA_BF16 ? 2 : 4, vec = 16 / esz;
+  for (const bsa_tensor *t : {q, k, v, (const bsa_tensor *)o}) {
+    if (((uintptr_t)t->data) % 16)
+      return fail(BSA_ERR_INVALID_ARG, "tensor data must be 16-byte aligned");
+    if (t->stride_b % vec || t->stride_h % vec || t->stride_s % vec)
+      return fail(BSA_ERR_INVALID_ARG, "tensor strides must be multiples of 16 bytes");
+    if (t->stride_b < 0 || t->stride_h < 0 || t->stride_s < 0)
+      return fail(BSA_ERR_INVALID_ARG, "negative stride");
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != P.device)
+    return fail(BSA_ERR_INVALID_ARG, "current device differs from the plan's device");
+  AttnArgs a{};
+  a.q = q->data, a.k = k->data, a.v = v->data, a.o = o->data, a.lse = lse;
+  a.q_sb = q->stride_b, a.q_sh = q->stride_h, a.q_ss = q->stride_s;
+  a.k_sb = k->stride_b, a.k_sh = k->stride_h, a.k_ss = k->stride_s;
+  a.v_sb = v->stride_b, a.v_sh = v->stride_h, a.v_ss = v->stride_s;
+  a.o_sb = o->stride_b, a.o_sh = o->stride_h, a.o_ss = o->stride_s;
+  a.items = P.items, a.counters = P.counters, a.ent_kt = P.ent_kt, a.ent_page = P.ent_page;
+  a.ent_live = P.ent_live, a.hm = P.hmeta, a.part_o = P.part_o, a.part_lse = P.part_lse;
+  a.Sq = P.Sq, a.Skv = P.Skv, a.off = P.off, a.nqt = P.nqt;
+  a.Hq = P.Hq, a.Hkv = P.Hkv, a.G = P.G, a.tq = P.rg.tq, a.tr = P.tr, a.pack = P.rg.pack;
+  a.causal = P.causal, a.paged = P.paged, a.P = P.P;
+  a.scale_log2 = P.scale * 1.4426950408889634f;
+  if (P.nrows == 0) return BSA_OK;
+  return attention_launch(P, a, (hipStream_t)stream);
+}
+
+bsa_status bsa_plan_export(bsa_plan_t plan, void *host_buf, size_t *bytes) {
+  if (!plan || !bytes) return fail(BSA_ERR_INVALID_ARG, "NULL plan or bytes");
+  const Plan &P = *plan;
+  int32_t cnt[CNT_N];
+  HIP_TRY(hipStreamSynchronize(P.stream));
+  HIP_TRY(hipMemcpy(cnt, P.counters, sizeof cnt, hipMemcpyDeviceToHost));
+  const int64_t nent = cnt[CNT_ENT], nitems = cnt[CNT_ITEMS], nslots = cnt[CNT_SLOTS], ncomb = cnt[CNT_COMB];
+  std::vector<uint8_t> img;
+  auto put = [&](const void *src, size_t n) {
+    const uint8_t *s = (const uint8_t *)src;
+    img.insert(img.end(), s, s + n);
+  };
+  auto put_dev = [&](const void *src, size_t n) -> bsa_status {
+    const size_t at = img.size();
+    img.resize(at + n);
+    if (n) HIP_TRY(hipMemcpy(img.data() + at, src, n, hipMemcpyDeviceToHost));
+    return BSA_OK;
+  };
+  put("BSAPLAN1", 8);
+  int64_t hdr[40] = {1, P.B, P.Hq, P.Hkv, P.Sq, P.Skv, P.D, P.dtype, P.causal, P.off, P.uni, P.paged,
+                     P.P, P.pps, P.bcast, P.rg.tq, P.rg.tk, P.rg.sched, P.rg.split, P.rg.pack,
+                     P.nqt, P.nkt, P.nlists, nent, P.nrows, nitems, nslots, ncomb, P.total_nnz,
+                     P.total_blocks, P.density_pm, P.imb16, P.min_bq, P.min_bk, P.nlb};
+  put(hdr, sizeof hdr);
+  put(P.bq.data(), sizeof(int32_t) * P.Hq);
+  put(P.bk.data(), sizeof(int32_t) * P.Hq);
+  put(P.feat.data(), sizeof(int64_t) * P.feat.size());
+  if (bsa_status s = put_dev(P.list_off, sizeof(int32_t) * (P.nlists + 1))) return s;
+  if (bsa_status s = put_dev(P.ent_kt, sizeof(int32_t) * nent)) return s;
+  if (P.paged)
+    if (bsa_status s = put_dev(P.ent_page, sizeof(int32_t) * nent)) return s;
+  if (bsa_status s = put_dev(P.ent_live, sizeof(uint32_t) * nent)) return s;
+  if (bsa_status s = put_dev(P.row_ent, sizeof(int32_t) * 2 * P.nrows)) return s;
+  if (bsa_status s = put_dev(P.items, sizeof(int32_t) * 4 * nitems)) return s;
+  if (bsa_status s = put_dev(P.comb, sizeof(int32_t) * 3 * ncomb)) return s;
+  if (host_buf) {
+    if (*bytes < img.size()) {
+      *bytes = img.size();
+      return fail(BSA_ERR_INVALID_ARG, "export buffer too small");
+    }
+    std::memcpy(host_buf, img.data(), img.size());
+  }
+  *bytes = img.size();
+  return BSA_OK;
+}
+
+bsa_status bsa_plan_stats(bsa_plan_t plan, bsa_plan_info *out) {
+  if (!plan || !out) return fail(BSA_ERR_INVALID_ARG, "NULL plan or out");
+  const Plan &P = *plan;
+  int32_t cnt[CNT_N];
+  HIP_TRY(hipStreamSynchronize(P.stream));
+  HIP_TRY(hipMemcpy(cnt, P.counters, sizeof cnt, hipMemcpyDeviceToHost));
+  std::vector<uint32_t> live(cnt[CNT_ENT]);
+  if (!live.empty())
+    HIP_TRY(hipMemcpy(live.data(), P.ent_live, sizeof(uint32_t) * live.size(), hipMemcpyDeviceToHost));
+  std::memset(out, 0, sizeof *out);
+  out->tile_q = P.rg.tq, out->tile_k = P.rg.tk, out->sched = P.rg.sched, out->split = P.rg.split;
+  out->pack = P.rg.pack;
+  out->rows = P.nrows, out->entries = cnt[CNT_ENT], out->items = cnt[CNT_ITEMS];
+  out->partial_slots = cnt[CNT_SLOTS], out->combines = cnt[CNT_COMB];
+  out->logical_nnz = P.total_nnz, out->logical_blocks = P.total_blocks;
+  out->density_pm = P.density_pm, out->imbalance16 = P.imb16;
+  double flops = 0;
+  int64_t eff = 0;
+  for (int b = 0; b < P.B; ++b)
+    for (int h = 0; h < P.Hq; ++h) {
+      const int64_t e = P.feat[((P.nbm == 1 ? 0 : b) * (int64_t)P.Hq + h) * 4 + 3];
+      eff += e;
+      flops += 4.0 * P.bq[h] * P.bk[h] * P.D * (double)e;
+    }
+  out->effective_blocks = eff, out->effective_flops = flops;
+  int64_t bits = 0;
+  for (uint32_t w : live) bits += __builtin_popcount(w);
+  out->tile_live_subblocks = bits;
+  return BSA_OK;
+}
+
+void bsa_plan_free(bsa_plan_t plan) { free_plan(plan); }
+
+}  // extern "C"

@@ -1,0 +1,489 @@
+// Fused block-sparse attention forward for gfx950 (CDNA4).
+//
+// Computes, for every work item of a plan (one physical query tile and a range
+// of its key-tile list), exact softmax attention restricted to the selected
+// tiles (Tessera, abstract: compute only the blocks the logical mask selects)
+// with an online softmax, the tiling-and-fusion scheme of FlashAttention that
+// the related-work page describes (attention as matrix products interleaved
+// with a softmax).
+//
+// Layout of the work on the chip:
+//   - A workgroup is 4 waves; each wave owns 32 query rows, so a physical
+//     query tile is 128 rows (or, for a packed GQA group, 128/G positions of
+//     each of its G heads: the heads share every K/V tile).
+//   - Scores are computed transposed, S^T = K Q^T, with the 32x32 MFMA: each
+//     lane then holds one query and 16 keys per 32-key block, so the row max
+//     and row sum are in-lane reductions plus one exchange between the two
+//     half-waves. The key rows feeding the MFMA are permuted (bits 2 and 3 of
+//     the row index swapped) so that each lane's 8 consecutive accumulator
+//     values are 8 consecutive keys, which is exactly the B-operand layout of
+//     the following P V^T MFMA: P never leaves registers.
+//   - O is accumulated transposed, O^T = V^T P^T, so each lane owns one query
+//     and the online-softmax rescale is per lane.
+//   - K tiles are stored in LDS row-major; V tiles are stored transposed
+//     (d-major) so each MFMA operand is one 16-byte LDS read. Both are double
+//     buffered: the global loads of tile e+1 are in flight while tile e is
+//     computed. Rows beyond the sequence are zero-filled, never read.
+//   - Workgroups are persistent: each takes items i, i + grid, ... of the
+//     plan's work list; the block-to-item map is XCD-aware so that
+//     consecutive items (neighbouring query tiles that share key tiles) run
+//     on the same XCD and reuse its L2.
+#include "bsa_internal.h"
+
+#include <algorithm>
+#include <type_traits>
+
+namespace bsa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr int kTileQ = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+#define HIP_TRY(expr)                                                          \
+  do {                                                                         \
+    hipError_t e_ = (expr);                                                    \
+    if (e_ != hipSuccess)                                                      \
+      return fail(BSA_ERR_HIP, std::string(#expr ": ") + hipGetErrorString(e_)); \
+  } while (0)
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Key row (within a 32-key block) that MFMA A-operand lane m supplies, so that
+// output accumulator j of lane half hh holds key 16*(j/8) + 8*hh + (j%8).
+__device__ __forceinline__ int perm_bf16(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+// fp32 variant: accumulator j of half hh holds key 2*j + hh.
+__device__ __forceinline__ int perm_f32(int m) { return 8 * (m >> 3) + 2 * (m & 3) + ((m >> 2) & 1); }
+
+// Key offset (within a 32-key block) of accumulator j for lane half hh.
+template <bool BF>
+__device__ __forceinline__ int acc_key(int j, int hh) {
+  if constexpr (BF) return 16 * (j >> 3) + 8 * hh + (j & 7);
+  else return 2 * j + hh;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  __bf16 x = (__bf16)a, y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+// Geometry of the wave's 32 query rows for row r of the plan.
+struct RowGeo {
+  int b, head, g;
+  int64_t q0;  // first query position of this wave
+  int qbase;   // offset of the wave's first row within the physical tile (live bits)
+};
+
+__device__ __forceinline__ RowGeo row_geo(const AttnArgs &a, int r, int wave) {
+  RowGeo o;
+  const int nh = a.pack ? a.Hkv : a.Hq;
+  const int64_t qt = r % a.nqt;
+  const int hrow = (int)((r / a.nqt) % nh);
+  o.b = (int)(r / (a.nqt * nh));
+  if (a.pack) {
+    o.head = hrow * a.G + (32 * wave) / a.tr;
+    o.q0 = qt * a.tr + (32 * wave) % a.tr;
+    o.qbase = 0;
+  } else {
+    o.head = hrow;
+    o.q0 = qt * a.tq + 32 * wave;
+    o.qbase = 32 * wave;
+  }
+  o.g = o.head / a.G;
+  return o;
+}
+
+template <int D, int TK, bool BF>
+struct Cfg {
+  using E = typename std::conditional<BF, uint16_t, float>::type;
+  static constexpr int EPV = 16 / sizeof(E);            // elements per 16-byte vector
+  static constexpr int KS = D + EPV;                    // K row stride (elements), padded
+  static constexpr int VS = BF ? TK + 8 : D + EPV;      // V^T row stride (bf16) or V row stride
+  static constexpr int KBUF = TK * KS;
+  static constexpr int VBUF = BF ? D * VS : TK * VS;
+  static constexpr int BUF = KBUF + VBUF;
+  static constexpr int NKB = TK / 32;                   // 32-key score blocks
+  static constexpr int NDB = D / 32;                    // 32-wide output blocks
+  static constexpr int KCH = TK * D / EPV;              // 16-byte chunks per K tile
+  static constexpr int KPT = (KCH + kThreads - 1) / kThreads;
+  // bf16 V: blocks of 4 keys x 8 dims, transposed into LDS.
+  static constexpr int VBLK = BF ? (TK / 4) * (D / 8) : KCH;
+  static constexpr int VPT = (VBLK + kThreads - 1) / kThreads;
+};
+
+template <int D, int TK, bool BF>
+__global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
+  using C = Cfg<D, TK, BF>;
+  using E = typename C::E;
+  __shared__ __attribute__((aligned(16))) E lds[2 * C::BUF];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, hh = lane >> 5;
+  const int nitems = a.counters[CNT_ITEMS];
+  const int grid = gridDim.x;
+  int lid = blockIdx.x;
+  if ((grid & 7) == 0) lid = (blockIdx.x & 7) * (grid >> 3) + (blockIdx.x >> 3);
+
+  const E *__restrict__ Q = (const E *)a.q;
+  const E *__restrict__ K = (const E *)a.k;
+  const E *__restrict__ V = (const E *)a.v;
+
+  for (int it = lid; it < nitems; it += grid) {
+    const int4 item = ((const int4 *)a.items)[it];
+    const int r = item.x, e0 = item.y, e1 = item.z, slot = item.w;
+    const RowGeo geo = row_geo(a, r, wave);
+    // All waves of the workgroup share b and kv group g (packed heads are one group).
+    const RowGeo geo0 = row_geo(a, r, 0);
+    const HeadMeta hm = a.hm[geo.head];
+    const int64_t qpos = geo.q0 + n;
+    const bool qvalid = qpos < a.Sq;
+
+    // Q fragments (MFMA B operand of S^T = K Q^T), loaded once per item.
+    bf16x8 qb[BF ? D / 16 : 1];
+    float qf[BF ? 1 : D / 2];
+    {
+      const E *qp = Q + geo.b * a.q_sb + geo.head * a.q_sh + (qvalid ? qpos : 0) * a.q_ss;
+      if constexpr (BF) {
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+          uint4 x = qvalid ? *(const uint4 *)(qp + 16 * c + 8 * hh) : make_uint4(0, 0, 0, 0);
+          qb[c] = __builtin_bit_cast(bf16x8, x);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < D / 2; ++c) qf[c] = qvalid ? qp[2 * c + hh] : 0.f;
+      }
+    }
+
+    f32x16 o[C::NDB];
+#pragma unroll
+    for (int u = 0; u < C::NDB; ++u) o[u] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    // ---- K/V tile staging ----
+    uint4 kreg[C::KPT];
+    uint4 vreg[BF ? 4 * C::VPT : C::VPT];
+    // First row of key tile e in a K or V tensor (dense, or a page of the pool).
+    auto kv_base = [&](const E *base, int64_t sb, int64_t sh, int64_t ss, int e) -> const E * {
+      const int64_t k0 = (int64_t)a.ent_kt[e] * TK;
+      if (a.paged) return base + (int64_t)a.ent_page[e] * sb + (k0 % a.P) * ss + geo0.g * sh;
+      return base + geo0.b * sb + geo0.g * sh + k0 * ss;
+    };
+    auto load_tile = [&](int e) {
+      const int64_t left = a.Skv - (int64_t)a.ent_kt[e] * TK;  // rows of the tile that exist
+      const E *kb = kv_base(K, a.k_sb, a.k_sh, a.k_ss, e);
+      const E *vb = kv_base(V, a.v_sb, a.v_sh, a.v_ss, e);
+#pragma unroll
+      for (int u = 0; u < C::KPT; ++u) {
+        const int c = tid + kThreads * u;
+        const int row = c / (D / C::EPV), col = (c % (D / C::EPV)) * C::EPV;
+        kreg[u] = (c < C::KCH && row < left) ? *(const uint4 *)(kb + row * a.k_ss + col) : make_uint4(0, 0, 0, 0);
+      }
+      if constexpr (BF) {
+#pragma unroll
+        for (int u = 0; u < C::VPT; ++u) {
+          const int bi = tid + kThreads * u;
+          const int kg = bi % (TK / 4), dg = bi / (TK / 4);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int row = 4 * kg + rr;
+            vreg[4 * u + rr] = (bi < C::VBLK && row < left) ? *(const uint4 *)(vb + row * a.v_ss + 8 * dg)
+                                                            : make_uint4(0, 0, 0, 0);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < C::VPT; ++u) {
+          const int c = tid + kThreads * u;
+          const int row = c / (D / C::EPV), col = (c % (D / C::EPV)) * C::EPV;
+          vreg[u] = (c < C::KCH && row < left) ? *(const uint4 *)(vb + row * a.v_ss + col) : make_uint4(0, 0, 0, 0);
+        }
+      }
+    };
+    auto store_tile = [&](int buf) {
+      E *ks = lds + buf * C::BUF;
+      E *vs = ks + C::KBUF;
+#pragma unroll
+      for (int u = 0; u < C::KPT; ++u) {
+        const int c = tid + kThreads * u;
+        if (c < C::KCH) {
+          const int row = c / (D / C::EPV), col = (c % (D / C::EPV)) * C::EPV;
+          *(uint4 *)(ks + row * C::KS + col) = kreg[u];
+        }
+      }
+      if constexpr (BF) {
+#pragma unroll
+        for (int u = 0; u < C::VPT; ++u) {
+          const int bi = tid + kThreads * u;
+          if (bi < C::VBLK) {
+            const int kg = bi % (TK / 4), dg = bi / (TK / 4);
+            const uint32_t *w0 = (const uint32_t *)&vreg[4 * u + 0];
+            const uint32_t *w1 = (const uint32_t *)&vreg[4 * u + 1];
+            const uint32_t *w2 = (const uint32_t *)&vreg[4 * u + 2];
+            const uint32_t *w3 = (const uint32_t *)&vreg[4 * u + 3];
+#pragma unroll
+            for (int d2 = 0; d2 < 4; ++d2) {
+              // even dim 8*dg + 2*d2: low halves; odd dim: high halves.
+              uint2 ev, od;
+              ev.x = __builtin_amdgcn_perm(w1[d2], w0[d2], 0x05040100u);
+              ev.y = __builtin_amdgcn_perm(w3[d2], w2[d2], 0x05040100u);
+              od.x = __builtin_amdgcn_perm(w1[d2], w0[d2], 0x07060302u);
+              od.y = __builtin_amdgcn_perm(w3[d2], w2[d2], 0x07060302u);
+              *(uint2 *)(vs + (8 * dg + 2 * d2) * C::VS + 4 * kg) = ev;
+              *(uint2 *)(vs + (8 * dg + 2 * d2 + 1) * C::VS + 4 * kg) = od;
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < C::VPT; ++u) {
+          const int c = tid + kThreads * u;
+          if (c < C::KCH) {
+            const int row = c / (D / C::EPV), col = (c % (D / C::EPV)) * C::EPV;
+            *(uint4 *)(vs + row * C::VS + col) = vreg[u];
+          }
+        }
+      }
+    };
+
+    // Live bits of this wave's rows: sub-blocks iq_lo .. iq_lo + niq - 1.
+    const int iq_lo = geo.qbase >> hm.lq;
+    const int niq = hm.lq >= 5 ? 1 : (32 >> hm.lq);
+    const uint64_t wbits = ((1ull << (hm.mk * niq)) - 1ull) << (iq_lo * hm.mk);
+
+    if (e0 < e1) {
+      load_tile(e0);
+      store_tile(0);
+      __syncthreads();
+    }
+    for (int e = e0; e < e1; ++e) {
+      const int buf = (e - e0) & 1;
+      if (e + 1 < e1) load_tile(e + 1);
+      const E *ks = lds + buf * C::BUF;
+      const E *vs = ks + C::KBUF;
+
+      // ---- S^T = K Q^T ----
+      f32x16 s[C::NKB];
+#pragma unroll
+      for (int t = 0; t < C::NKB; ++t) {
+        s[t] = f32x16{};
+        if constexpr (BF) {
+          const E *kr = ks + (32 * t + perm_bf16(n)) * C::KS + 8 * hh;
+#pragma unroll
+          for (int c = 0; c < D / 16; ++c) {
+            bf16x8 af = __builtin_bit_cast(bf16x8, *(const uint4 *)(kr + 16 * c));
+            s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qb[c], s[t], 0, 0, 0);
+          }
+        } else {
+          const E *kr = ks + (32 * t + perm_f32(n)) * C::KS + hh;
+#pragma unroll
+          for (int c = 0; c < D / 2; ++c)
+            s[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(kr[2 * c], qf[c], s[t], 0, 0, 0);
+        }
+      }
+
+      // ---- mask (only tiles that need it) ----
+      const int64_t kbase = (int64_t)a.ent_kt[e] * TK;
+      const uint32_t live = a.ent_live[e];
+      const bool need = (kbase + TK > a.Skv) || (a.causal && kbase + TK - 1 > geo.q0 + a.off) ||
+                        ((uint64_t)live & wbits) != wbits;
+      if (need) {
+        const int qsub = ((geo.qbase + n) >> hm.lq) * hm.mk;
+#pragma unroll
+        for (int t = 0; t < C::NKB; ++t)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int kl = 32 * t + acc_key<BF>(j, hh);
+            const int64_t kpos = kbase + kl;
+            const bool ok = ((live >> (qsub + (kl >> hm.lk))) & 1u) && kpos < a.Skv &&
+                            (!a.causal || kpos <= qpos + a.off);
+            if (!ok) s[t][j] = -INFINITY;
+          }
+      }
+
+      // ---- online softmax (log2 domain) ----
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < C::NKB; ++t)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[t][j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx * a.scale_log2);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fexp2(m_run - m_use);
+      m_run = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int t = 0; t < C::NKB; ++t)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float p = fexp2(__builtin_fmaf(s[t][j], a.scale_log2, -m_use));
+          s[t][j] = p;
+          psum += p;
+        }
+      l_run = l_run * alpha + psum;
+#pragma unroll
+      for (int u = 0; u < C::NDB; ++u) o[u] *= alpha;
+
+      // ---- O^T += V^T P^T ----
+      if constexpr (BF) {
+        bf16x8 pb[C::NKB][2];
+#pragma unroll
+        for (int t = 0; t < C::NKB; ++t)
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) {
+            uint4 w;
+            w.x = pack_bf16x2(s[t][8 * c2 + 0], s[t][8 * c2 + 1]);
+            w.y = pack_bf16x2(s[t][8 * c2 + 2], s[t][8 * c2 + 3]);
+            w.z = pack_bf16x2(s[t][8 * c2 + 4], s[t][8 * c2 + 5]);
+            w.w = pack_bf16x2(s[t][8 * c2 + 6], s[t][8 * c2 + 7]);
+            pb[t][c2] = __builtin_bit_cast(bf16x8, w);
+          }
+#pragma unroll
+        for (int u = 0; u < C::NDB; ++u) {
+          const E *vr = vs + (32 * u + n) * C::VS + 8 * hh;
+#pragma unroll
+          for (int t = 0; t < C::NKB; ++t)
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+              bf16x8 af = __builtin_bit_cast(bf16x8, *(const uint4 *)(vr + 32 * t + 16 * c2));
+              o[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[t][c2], o[u], 0, 0, 0);
+            }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < C::NDB; ++u)
+#pragma unroll
+          for (int t = 0; t < C::NKB; ++t)
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+              const float av = vs[(32 * t + 2 * c + hh) * C::VS + 32 * u + n];
+              o[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, s[t][c], o[u], 0, 0, 0);
+            }
+      }
+
+      if (e + 1 < e1) store_tile(buf ^ 1);
+      __syncthreads();
+    }
+
+    // ---- finalize ----
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    if (slot < 0) {
+      if (qvalid) {
+        E *op = (E *)a.o + geo.b * a.o_sb + geo.head * a.o_sh + qpos * a.o_ss;
+#pragma unroll
+        for (int u = 0; u < C::NDB; ++u)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int d0 = 32 * u + 8 * q4 + 4 * hh;
+            const float x0 = o[u][4 * q4] * inv, x1 = o[u][4 * q4 + 1] * inv;
+            const float x2 = o[u][4 * q4 + 2] * inv, x3 = o[u][4 * q4 + 3] * inv;
+            if constexpr (BF) {
+              *(uint2 *)(op + d0) = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
+            } else {
+              *(float4 *)(op + d0) = make_float4(x0, x1, x2, x3);
+            }
+          }
+        if (hh == 0) a.lse[((int64_t)geo.b * a.Hq + geo.head) * a.Sq + qpos] = lse;
+      }
+    } else {
+      const int64_t prow = (int64_t)slot * kTileQ + 32 * wave + n;
+      float *pp = a.part_o + prow * D;
+#pragma unroll
+      for (int u = 0; u < C::NDB; ++u)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = 32 * u + 8 * q4 + 4 * hh;
+          *(float4 *)(pp + d0) = make_float4(o[u][4 * q4] * inv, o[u][4 * q4 + 1] * inv,
+                                             o[u][4 * q4 + 2] * inv, o[u][4 * q4 + 3] * inv);
+        }
+      if (hh == 0) a.part_lse[prow] = lse;
+    }
+  }
+}
+
+// Split-KV combine: O = sum_s w_s O_s / sum_s w_s with w_s = exp(lse_s - M),
+// LSE = M + ln sum_s w_s, M = max_s lse_s. A record covers one 128-row tile.
+template <int D, bool BF>
+__global__ __launch_bounds__(kThreads) void k_combine(AttnArgs a, const int32_t *__restrict__ comb) {
+  using E = typename std::conditional<BF, uint16_t, float>::type;
+  const int ncomb = a.counters[CNT_COMB];
+  const int row = threadIdx.x >> 1, half = threadIdx.x & 1;  // 128 rows x 2 threads
+  const int wave = row >> 5, n = row & 31;
+  for (int c = blockIdx.x; c < ncomb; c += gridDim.x) {
+    const int r = comb[3 * c], s0 = comb[3 * c + 1], k = comb[3 * c + 2];
+    const RowGeo geo = row_geo(a, r, wave);
+    const int64_t qpos = geo.q0 + n;
+    if (qpos >= a.Sq) continue;
+    float M = -INFINITY;
+    for (int s = 0; s < k; ++s) M = fmaxf(M, a.part_lse[(int64_t)(s0 + s) * kTileQ + row]);
+    E *op = (E *)a.o + geo.b * a.o_sb + geo.head * a.o_sh + qpos * a.o_ss;
+    if (M == -INFINITY) {
+      for (int d = half * (D / 2); d < (half + 1) * (D / 2); ++d) op[d] = (E)0;
+      if (half == 0) a.lse[((int64_t)geo.b * a.Hq + geo.head) * a.Sq + qpos] = -INFINITY;
+      continue;
+    }
+    float wsum = 0.f;
+    for (int s = 0; s < k; ++s) wsum += expf(a.part_lse[(int64_t)(s0 + s) * kTileQ + row] - M);
+    const float inv = 1.f / wsum;
+    for (int d4 = half * (D / 8); d4 < (half + 1) * (D / 8); ++d4) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int s = 0; s < k; ++s) {
+        const int64_t prow = (int64_t)(s0 + s) * kTileQ + row;
+        const float w = expf(a.part_lse[prow] - M);
+        const float4 x = *(const float4 *)(a.part_o + prow * D + 4 * d4);
+        acc.x += w * x.x, acc.y += w * x.y, acc.z += w * x.z, acc.w += w * x.w;
+      }
+      acc.x *= inv, acc.y *= inv, acc.z *= inv, acc.w *= inv;
+      if constexpr (BF) {
+        *(uint2 *)(op + 4 * d4) = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+      } else {
+        *(float4 *)(op + 4 * d4) = acc;
+      }
+    }
+    if (half == 0) a.lse[((int64_t)geo.b * a.Hq + geo.head) * a.Sq + qpos] = M + logf(wsum);
+  }
+}
+
+template <int D, int TK, bool BF>
+bsa_status launch_one(const Plan &p, const AttnArgs &a, hipStream_t s) {
+  static int grid = 0;
+  if (grid == 0) {
+    int dev = 0, cus = 0, occ = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_attn<D, TK, BF>, kThreads, 0));
+    grid = cus * (occ > 0 ? occ : 1);
+  }
+  int g = grid;
+  if (p.item_cap < g) g = (int)std::max<int64_t>(p.item_cap, 1);
+  hipLaunchKernelGGL((k_attn<D, TK, BF>), dim3(g), dim3(kThreads), 0, s, a);
+  if (p.rg.split > 0 && p.comb_cap > 0) {
+    const int cg = (int)std::min<int64_t>(p.comb_cap, 2048);
+    hipLaunchKernelGGL((k_combine<D, BF>), dim3(cg), dim3(kThreads), 0, s, a, p.comb);
+  }
+  HIP_TRY(hipGetLastError());
+  return BSA_OK;
+}
+
+}  // namespace
+
+bsa_status attention_launch(const Plan &p, const AttnArgs &a, hipStream_t s) {
+  const bool bf = p.dtype == BSA_BF16;
+  // fp32 tiles use 64 keys (the planner guarantees it): 128 would not fit LDS twice.
+  if (bf && p.D == 128 && p.rg.tk == 64) return launch_one<128, 64, true>(p, a, s);
+  if (bf && p.D == 128 && p.rg.tk == 128) return launch_one<128, 128, true>(p, a, s);
+  if (bf && p.D == 64 && p.rg.tk == 64) return launch_one<64, 64, true>(p, a, s);
+  if (bf && p.D == 64 && p.rg.tk == 128) return launch_one<64, 128, true>(p, a, s);
+  if (!bf && p.D == 128 && p.rg.tk == 64) return launch_one<128, 64, false>(p, a, s);
+  if (!bf && p.D == 64 && p.rg.tk == 64) return launch_one<64, 64, false>(p, a, s);
+  return fail(BSA_ERR_UNSUPPORTED, "no kernel for this head_dim / tile_k");
+}
+
+}  // namespace bsa

@@ -1,0 +1,94 @@
+// Internal declarations shared by the libbsa sources (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "bsa.h"
+
+namespace bsa {
+
+// Per query head, device resident. Live-bit decoding for a score at query
+// offset qloc within its physical tile and key offset kloc within its key
+// tile: bit = (qloc >> lq) * mk + (kloc >> lk).
+struct HeadMeta {
+  int64_t mask_off;  // offset of this head's [nqb][nkb] mask within one mask batch
+  int64_t row_off;   // number of logical rows of the heads before this one
+  int32_t nqb, nkb, bq, bk;
+  int32_t lq, lk, mk, pad;
+};
+
+// Counters written on the device by the planner.
+enum { CNT_ENT = 0, CNT_ITEMS = 1, CNT_SLOTS = 2, CNT_COMB = 3, CNT_BADPAGE = 4, CNT_N = 8 };
+
+struct Regime {
+  int tq = 128, tk = 64, sched = 0, split = 0, pack = 1;
+};
+
+// Host-side plan object. All device arrays live in two allocations.
+struct Plan {
+  // problem
+  int32_t B, Hq, Hkv, G, D, dtype;
+  int64_t Sq, Skv;
+  int32_t causal;
+  int64_t off;
+  int32_t uni, paged, P, pps, npages, bcast;
+  float scale;
+  std::vector<int32_t> bq, bk;
+  // regime and geometry
+  Regime rg;
+  int32_t tr;  // query positions per physical row
+  int64_t nqt, nkt, nlists, nrows, nlb, nbm, unkb;
+  int64_t ent_cap, item_cap, slot_cap, comb_cap;
+  // mask features (host copy) and aggregates
+  std::vector<int64_t> feat;  // [nbm][Hq][4]: nnz, max row, empty rows, effective blocks
+  int64_t total_nnz, total_blocks, density_pm, imb16, min_bq, min_bk;
+  // device memory
+  std::vector<HeadMeta> hmeta_host;  // host copy kept alive for the asynchronous uploads
+  void *pre = nullptr;    // features, counters, head metadata, union bits
+  void *arena = nullptr;  // lists, entries, rows, work list, partials, scratch
+  HeadMeta *hmeta;
+  unsigned long long *feat_dev;
+  int32_t *counters;
+  uint8_t *uni_bits;
+  int32_t *list_off, *ent_kt, *ent_page;
+  uint32_t *ent_live;
+  int32_t *row_ent, *items, *comb;
+  float *part_o, *part_lse;
+  hipStream_t stream;
+  int device;
+};
+
+struct AttnArgs {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  int64_t q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, v_sb, v_sh, v_ss, o_sb, o_sh, o_ss;
+  const int32_t *items, *counters, *ent_kt, *ent_page;
+  const uint32_t *ent_live;
+  const HeadMeta *hm;
+  float *part_o, *part_lse;
+  int64_t Sq, Skv, off, nqt;
+  int32_t Hq, Hkv, G, tq, tr, pack, causal, paged, P;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+// Error reporting (thread-local message).
+bsa_status fail(bsa_status s, const std::string &msg);
+
+// Planner entry points (bsa_planner.hip). Each returns BSA_OK or BSA_ERR_HIP.
+bsa_status plan_features(Plan &p, const uint8_t *mask, const int32_t *page_table);
+bsa_status plan_build(Plan &p, const uint8_t *mask, const int32_t *page_table, void *scratch,
+                      size_t scratch_bytes);
+size_t plan_scratch_bytes(const Plan &p);
+
+// Attention entry point (bsa_attention.hip).
+bsa_status attention_launch(const Plan &p, const AttnArgs &a, hipStream_t stream);
+
+}  // namespace bsa
+
+// The opaque plan handle of the C ABI.
+struct bsa_plan_s : public bsa::Plan {};

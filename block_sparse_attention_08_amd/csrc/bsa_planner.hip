@@ -1,0 +1,522 @@
+// Mask-to-tile planner kernels for gfx950.
+//
+// Tessera ("Decoupling Logical Masks from GPU Execution for Dynamic
+// Block-Sparse Attention", abstract) splits the work of a block-sparse request
+// into a physical mapping layer (keep, merge or subdivide logical blocks into
+// physical tiles while preserving the selected interactions), a task
+// organization layer (group and schedule tiles into GPU tasks) and a
+// profile-built lookup table that picks the execution plan. CompactAttention
+// (summary) builds per-group KV block tables from the union of a group's
+// selections and runs them zero-copy over a paged cache.
+//
+// Everything here is integer work done with wave-level ballots, prefix
+// popcounts and a three-phase exclusive scan, so the plan is bit-for-bit
+// reproducible: integer atomics only ever produce order-independent sums and
+// maxima, every list is emitted in ascending key-tile order, and the
+// longest-first order is a stable counting sort.
+#include "bsa_internal.h"
+
+#include <algorithm>
+#include <type_traits>
+
+namespace bsa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kScanBlock = 1024;  // elements per scan workgroup (4 per thread)
+constexpr int kLptKeys = 1024;    // longest-first key = min(item length, 1023)
+
+#define HIP_TRY(expr)                                                          \
+  do {                                                                         \
+    hipError_t e_ = (expr);                                                    \
+    if (e_ != hipSuccess)                                                      \
+      return fail(BSA_ERR_HIP, std::string(#expr ": ") + hipGetErrorString(e_)); \
+  } while (0)
+
+__device__ __forceinline__ int wave_sum(int x) {
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ int64_t lo_mask(int lane) { return (int64_t)((1ull << lane) - 1ull); }
+
+// -------------------------------------------------------------------------
+// Mask features and group union
+// -------------------------------------------------------------------------
+
+// Group union (CompactAttention: query-block union plus intra-group union):
+// U[bm][g][kb] = 1 iff some head of group g selects key block kb in some row.
+__global__ void k_union(const uint8_t *__restrict__ mask, const HeadMeta *__restrict__ hm,
+                        int64_t mask_bstride, int Hkv, int G, int nbm, int64_t unkb,
+                        uint8_t *__restrict__ U) {
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)nbm * Hkv * unkb) return;
+  const int64_t kb = idx % unkb, bg = idx / unkb;
+  const int g = (int)(bg % Hkv), bm = (int)(bg / Hkv);
+  uint8_t u = 0;
+  for (int hh = 0; hh < G && !u; ++hh) {
+    const HeadMeta m = hm[g * G + hh];
+    if (kb >= m.nkb) continue;
+    const uint8_t *col = mask + bm * mask_bstride + m.mask_off + kb;
+    for (int64_t qb = 0; qb < m.nqb; ++qb)
+      if (col[qb * m.nkb]) {
+        u = 1;
+        break;
+      }
+  }
+  U[idx] = u;
+}
+
+// One wave per logical row: popcount, and the count of effective blocks (the
+// union's in union mode) that the causal bound can reach. Per head: nnz (sum),
+// max row (max), empty rows (sum), effective blocks (sum).
+__global__ void k_features(const uint8_t *__restrict__ mask, const HeadMeta *__restrict__ hm,
+                           int Hq, int Hkv, int G, int nbm, int64_t rows_per_bm,
+                           int64_t mask_bstride, const uint8_t *__restrict__ U, int64_t unkb,
+                           int causal, int64_t off, int64_t Sq,
+                           unsigned long long *__restrict__ feat) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wv = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 6;
+  if (wv >= nbm * rows_per_bm) return;
+  const int bm = (int)(wv / rows_per_bm);
+  const int64_t r = wv % rows_per_bm;
+  int lo = 0, hi = Hq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (hm[mid].row_off <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  const int h = lo;
+  const HeadMeta m = hm[h];
+  const int64_t qb = r - m.row_off;
+  const uint8_t *row = mask + bm * mask_bstride + m.mask_off + qb * m.nkb;
+  const uint8_t *urow = U ? U + ((int64_t)bm * Hkv + h / G) * unkb : nullptr;
+  const int64_t qlast = min(Sq, (qb + 1) * (int64_t)m.bq) - 1;
+  int64_t kbmax = m.nkb - 1;
+  if (causal) kbmax = (qlast + off) < 0 ? -1 : (qlast + off) / m.bk;
+  int cnt = 0, eff = 0;
+  for (int64_t kb = lane; kb < m.nkb; kb += 64) {
+    const int sel = row[kb] != 0;
+    cnt += sel;
+    const int es = urow ? (urow[kb] != 0) : sel;
+    eff += es && kb <= kbmax;
+  }
+  cnt = wave_sum(cnt);
+  eff = wave_sum(eff);
+  if (lane == 0) {
+    unsigned long long *f = feat + ((int64_t)bm * Hq + h) * 4;
+    atomicAdd(&f[0], (unsigned long long)cnt);
+    atomicMax(&f[1], (unsigned long long)cnt);
+    atomicAdd(&f[2], (unsigned long long)(cnt == 0));
+    atomicAdd(&f[3], (unsigned long long)eff);
+  }
+}
+
+// Count page-table entries that the keys [0, Skv) use and that point outside
+// the pool.
+__global__ void k_check_pages(const int32_t *__restrict__ table, int B, int pps, int64_t used,
+                              int npages, int32_t *__restrict__ counters) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= (int64_t)B * used) return;
+  const int32_t pg = table[(i / used) * pps + i % used];
+  if (pg < 0 || pg >= npages) atomicAdd(&counters[CNT_BADPAGE], 1);
+}
+
+// -------------------------------------------------------------------------
+// Physical mapping (keep / merge / subdivide) with live bits
+// -------------------------------------------------------------------------
+
+struct MapArgs {
+  const uint8_t *mask, *U;
+  const HeadMeta *hm;
+  const int32_t *page_table;
+  int64_t mask_bstride, unkb, Sq, off, nqt, nkt, nlists;
+  int32_t Hq, Hkv, G, bcast, uni, paged, causal, tq, tk, pps, P;
+  int32_t *list_len;
+  const int32_t *list_off;
+  int32_t *ent_kt, *ent_page;
+  uint32_t *ent_live;
+};
+
+// Live bits of physical tile (qt, kt) for list head h: bit (iq * mk + ik) is
+// set iff the logical block covering query sub-block iq and key sub-block ik
+// is selected (by the union in union mode) and, when causal, the sub-block's
+// first key is not after its last query.
+__device__ __forceinline__ uint32_t live_bits(const MapArgs &a, int bm, int h, int g, int64_t qt,
+                                              int64_t kt) {
+  const HeadMeta m = a.hm[h];
+  const int64_t bq = m.bq, bk = m.bk;
+  const int mq = (!a.uni && bq < a.tq) ? (int)(a.tq / bq) : 1;
+  const int mk = bk < a.tk ? (int)(a.tk / bk) : 1;
+  const int64_t aq = bq < a.tq ? bq : a.tq, ak = bk < a.tk ? bk : a.tk;
+  const uint8_t *mb = a.mask + bm * a.mask_bstride + m.mask_off;
+  const uint8_t *u = a.uni ? a.U + ((int64_t)bm * a.Hkv + g) * a.unkb : nullptr;
+  uint32_t live = 0;
+  for (int iq = 0; iq < mq; ++iq) {
+    const int64_t qb = bq < a.tq ? qt * mq + iq : (qt * a.tq) / bq;
+    if (!u && qb >= m.nqb) continue;
+    for (int ik = 0; ik < mk; ++ik) {
+      const int64_t kb = bk < a.tk ? kt * mk + ik : (kt * a.tk) / bk;
+      if (kb >= m.nkb) continue;
+      if (!(u ? u[kb] : mb[qb * m.nkb + kb])) continue;
+      if (!u && a.causal) {
+        const int64_t q0 = qt * a.tq + iq * aq;
+        const int64_t qlast = min(q0 + aq, a.Sq) - 1;
+        if (kt * a.tk + ik * ak > qlast + a.off) continue;
+      }
+      live |= 1u << (iq * mk + ik);
+    }
+  }
+  return live;
+}
+
+// One wave per list. EMIT = false: count live tiles. EMIT = true: write them
+// at list_off[l] in ascending key-tile order (ballot + prefix popcount).
+template <bool EMIT>
+__global__ void k_map(MapArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t l = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 6;
+  if (l >= a.nlists) return;
+  int lb, h, g;
+  int64_t qt = 0;
+  if (a.uni) {
+    lb = (int)(l / a.Hkv), g = (int)(l % a.Hkv), h = g * a.G;
+  } else {
+    lb = (int)(l / ((int64_t)a.Hq * a.nqt)), h = (int)((l / a.nqt) % a.Hq), qt = l % a.nqt;
+    g = h / a.G;
+  }
+  const int bm = a.bcast ? 0 : lb;
+  const int64_t base = EMIT ? a.list_off[l] : 0;
+  int64_t run = 0;
+  for (int64_t k0 = 0; k0 < a.nkt; k0 += 64) {
+    const int64_t kt = k0 + lane;
+    const uint32_t live = kt < a.nkt ? live_bits(a, bm, h, g, qt, kt) : 0u;
+    const unsigned long long bal = __ballot(live != 0);
+    if (EMIT && live) {
+      const int64_t idx = base + run + __popcll(bal & (unsigned long long)lo_mask(lane));
+      a.ent_kt[idx] = (int32_t)kt;
+      a.ent_live[idx] = live;
+      if (a.paged) a.ent_page[idx] = a.page_table[(int64_t)lb * a.pps + kt * a.tk / a.P];
+    }
+    run += __popcll(bal);
+  }
+  if (!EMIT && lane == 0) a.list_len[l] = (int32_t)run;
+}
+
+// -------------------------------------------------------------------------
+// Exclusive prefix scan (int32, three phases)
+// -------------------------------------------------------------------------
+
+// Exclusive scan of one value per thread over a 256-thread workgroup.
+__device__ int block_excl_scan(int v, int *total) {
+  __shared__ int wsum[kThreads / 64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+  for (int i = 0; i < kThreads / 64; ++i) {
+    before += i < w ? wsum[i] : 0;
+    tot += wsum[i];
+  }
+  __syncthreads();
+  *total = tot;
+  return before + x - v;
+}
+
+__global__ void k_scan_reduce(const int32_t *__restrict__ in, int64_t n, int32_t *__restrict__ bsum) {
+  const int64_t base = blockIdx.x * (int64_t)kScanBlock + threadIdx.x * 4;
+  int s = 0;
+  for (int u = 0; u < 4; ++u)
+    if (base + u < n) s += in[base + u];
+  int tot;
+  block_excl_scan(s, &tot);
+  if (threadIdx.x == 0) bsum[blockIdx.x] = tot;
+}
+
+__global__ void k_scan_top(int32_t *__restrict__ bsum, int64_t nb) {
+  int carry = 0;
+  for (int64_t base = 0; base < nb; base += kScanBlock) {
+    int v[4], s = 0;
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = base + threadIdx.x * 4 + u;
+      v[u] = i < nb ? bsum[i] : 0;
+      s += v[u];
+    }
+    int tot;
+    int run = carry + block_excl_scan(s, &tot);
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = base + threadIdx.x * 4 + u;
+      if (i < nb) bsum[i] = run;
+      run += v[u];
+    }
+    carry += tot;
+  }
+}
+
+// out[i] = sum of in[0..i); out[n] = total. in and out may be the same array.
+__global__ void k_scan_apply(const int32_t *in, int64_t n, const int32_t *__restrict__ bsum,
+                             int32_t *out) {
+  const int64_t base = blockIdx.x * (int64_t)kScanBlock + threadIdx.x * 4;
+  int v[4], s = 0;
+  for (int u = 0; u < 4; ++u) {
+    v[u] = base + u < n ? in[base + u] : 0;
+    s += v[u];
+  }
+  int tot;
+  int run = bsum[blockIdx.x] + block_excl_scan(s, &tot);
+  for (int u = 0; u < 4; ++u) {
+    if (base + u < n) out[base + u] = run;
+    run += v[u];
+  }
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == kThreads - 1) out[n] = run;
+}
+
+bsa_status scan(const int32_t *in, int64_t n, int32_t *out, int32_t *bsum, hipStream_t s) {
+  const int64_t nb = n > 0 ? (n + kScanBlock - 1) / kScanBlock : 1;
+  hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)nb), dim3(kThreads), 0, s, in, n, bsum);
+  hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(kThreads), 0, s, bsum, nb);
+  hipLaunchKernelGGL(k_scan_apply, dim3((unsigned)nb), dim3(kThreads), 0, s, in, n, bsum, out);
+  HIP_TRY(hipGetLastError());
+  return BSA_OK;
+}
+
+// -------------------------------------------------------------------------
+// Rows and work list (task organization)
+// -------------------------------------------------------------------------
+
+struct RowArgs {
+  const int32_t *list_off, *ent_kt;
+  int32_t *row_ent, *cnt_items, *cnt_slots, *cnt_comb;
+  int64_t nrows, nqt, Sq, off;
+  int32_t Hq, Hkv, G, pack, uni, causal, nlb, tq, tr, tk, split;
+};
+
+// Row r = (b, head or group, q-tile). Union rows take the causal prefix of
+// their group's table; every row gets its item, partial-slot and combine counts.
+__global__ void k_rows(RowArgs a) {
+  const int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (r >= a.nrows) return;
+  const int nh = a.pack ? a.Hkv : a.Hq;
+  const int64_t qt = r % a.nqt;
+  const int hh = (int)((r / a.nqt) % nh);
+  const int b = (int)(r / (a.nqt * nh));
+  const int lb = a.nlb == 1 ? 0 : b;
+  const int64_t l = a.uni ? (int64_t)lb * a.Hkv + (a.pack ? hh : hh / a.G)
+                          : ((int64_t)lb * a.Hq + hh) * a.nqt + qt;
+  const int32_t e0 = a.list_off[l];
+  int32_t e1 = a.list_off[l + 1];
+  if (a.uni && a.causal) {
+    const int64_t lim = min((qt + 1) * a.tr, a.Sq) - 1 + a.off;
+    int32_t lo = e0, hi = e1;
+    while (lo < hi) {
+      const int32_t mid = lo + ((hi - lo) >> 1);
+      if ((int64_t)a.ent_kt[mid] * a.tk <= lim) lo = mid + 1;
+      else hi = mid;
+    }
+    e1 = lo;
+  }
+  a.row_ent[2 * r] = e0;
+  a.row_ent[2 * r + 1] = e1;
+  const int64_t n = e1 - e0;
+  const int64_t k = (a.split > 0 && n > a.split) ? (n + a.split - 1) / a.split : 1;
+  a.cnt_items[r] = (int32_t)k;
+  a.cnt_slots[r] = k > 1 ? (int32_t)k : 0;
+  a.cnt_comb[r] = k > 1 ? 1 : 0;
+}
+
+// Emit each row's items (balanced chunks of a split row) and combine record.
+__global__ void k_items(const int32_t *__restrict__ row_ent, const int32_t *__restrict__ item_off,
+                        const int32_t *__restrict__ slot_off, const int32_t *__restrict__ comb_off,
+                        int64_t nrows, int4 *__restrict__ items, int32_t *__restrict__ comb) {
+  const int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (r >= nrows) return;
+  const int64_t e0 = row_ent[2 * r], n = row_ent[2 * r + 1] - e0;
+  const int64_t k = item_off[r + 1] - item_off[r];
+  for (int64_t j = 0; j < k; ++j)
+    items[item_off[r] + j] = make_int4((int)r, (int)(e0 + j * n / k), (int)(e0 + (j + 1) * n / k),
+                                       k > 1 ? (int)(slot_off[r] + j) : -1);
+  if (k > 1) {
+    const int32_t c = comb_off[r];
+    comb[3 * c] = (int32_t)r, comb[3 * c + 1] = slot_off[r], comb[3 * c + 2] = (int32_t)k;
+  }
+}
+
+__global__ void k_totals(const int32_t *list_off, int64_t nlists, const int32_t *item_off,
+                         const int32_t *slot_off, const int32_t *comb_off, int64_t nrows,
+                         int32_t *counters) {
+  counters[CNT_ENT] = list_off[nlists];
+  counters[CNT_ITEMS] = item_off[nrows];
+  counters[CNT_SLOTS] = slot_off[nrows];
+  counters[CNT_COMB] = comb_off[nrows];
+}
+
+// Longest-first order: stable counting sort on key min(length, 1023),
+// descending. hist[k * nchunks + c] counts items of chunk c with key index
+// k = 1023 - key; its exclusive scan gives each (key, chunk) its first slot.
+__global__ void k_lpt_hist(const int4 *__restrict__ items, const int32_t *__restrict__ counters,
+                           int64_t nchunks, int32_t *__restrict__ hist) {
+  __shared__ int h[kLptKeys];
+  for (int i = threadIdx.x; i < kLptKeys; i += kThreads) h[i] = 0;
+  __syncthreads();
+  const int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x;
+  if (i < counters[CNT_ITEMS]) {
+    const int4 it = items[i];
+    atomicAdd(&h[kLptKeys - 1 - min(it.z - it.y, kLptKeys - 1)], 1);
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < kLptKeys; k += kThreads) hist[k * nchunks + blockIdx.x] = h[k];
+}
+
+__global__ void k_lpt_place(const int4 *__restrict__ items, const int32_t *__restrict__ counters,
+                            int64_t nchunks, const int32_t *__restrict__ start,
+                            int4 *__restrict__ out) {
+  __shared__ int keys[kThreads];
+  const int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x;
+  const bool valid = i < counters[CNT_ITEMS];
+  int4 it = make_int4(0, 0, 0, 0);
+  int key = -1;
+  if (valid) {
+    it = items[i];
+    key = kLptKeys - 1 - min(it.z - it.y, kLptKeys - 1);
+  }
+  keys[threadIdx.x] = key;
+  __syncthreads();
+  if (valid) {
+    int rank = 0;
+    for (int t = 0; t < (int)threadIdx.x; ++t) rank += keys[t] == key;
+    out[start[key * nchunks + blockIdx.x] + rank] = it;
+  }
+}
+
+unsigned grid_for(int64_t threads) { return (unsigned)((threads + kThreads - 1) / kThreads); }
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+bsa_status plan_features(Plan &p, const uint8_t *mask, const int32_t *page_table) {
+  hipStream_t s = p.stream;
+  int64_t rows_per_bm = 0, mask_bstride = 0;
+  std::vector<HeadMeta> &hm = p.hmeta_host;
+  hm.assign(p.Hq, HeadMeta{});
+  for (int h = 0; h < p.Hq; ++h) {
+    const int64_t nq = (p.Sq + p.bq[h] - 1) / p.bq[h], nk = (p.Skv + p.bk[h] - 1) / p.bk[h];
+    hm[h] = HeadMeta{mask_bstride, rows_per_bm, (int32_t)nq, (int32_t)nk, p.bq[h], p.bk[h], 0, 0, 0, 0};
+    rows_per_bm += nq;
+    mask_bstride += nq * nk;
+  }
+  HIP_TRY(hipMemcpyAsync(p.hmeta, hm.data(), sizeof(HeadMeta) * p.Hq, hipMemcpyHostToDevice, s));
+  if (p.uni && p.unkb > 0)
+    hipLaunchKernelGGL(k_union, dim3(grid_for((int64_t)p.nbm * p.Hkv * p.unkb)), dim3(kThreads), 0,
+                       s, mask, p.hmeta, mask_bstride, p.Hkv, p.G, (int)p.nbm, p.unkb, p.uni_bits);
+  if (p.nbm * rows_per_bm > 0)
+    hipLaunchKernelGGL(k_features, dim3(grid_for(p.nbm * rows_per_bm * 64)), dim3(kThreads), 0, s,
+                       mask, p.hmeta, p.Hq, p.Hkv, p.G, (int)p.nbm, rows_per_bm, mask_bstride,
+                       p.uni ? p.uni_bits : nullptr, p.unkb, p.causal, p.off, p.Sq, p.feat_dev);
+  if (p.paged && p.Skv > 0) {
+    const int64_t used = (p.Skv + p.P - 1) / p.P;
+    hipLaunchKernelGGL(k_check_pages, dim3(grid_for(p.B * used)), dim3(kThreads), 0, s, page_table,
+                       p.B, p.pps, used, p.npages, p.counters);
+  }
+  HIP_TRY(hipGetLastError());
+  return BSA_OK;
+}
+
+size_t plan_scratch_bytes(const Plan &p) {
+  const int64_t nchunks = (p.item_cap + kThreads - 1) / kThreads;
+  const int64_t big = std::max<int64_t>({p.nlists + 1, 3 * (p.nrows + 1), kLptKeys * nchunks + 1});
+  size_t b = 0;
+  b += align_up(sizeof(int32_t) * (p.nlists + 1));          // list lengths
+  b += align_up(sizeof(int32_t) * 3 * (p.nrows + 1));       // item / slot / combine counts
+  b += align_up(sizeof(int32_t) * 3 * (p.nrows + 1));       // their scans
+  b += align_up(sizeof(int32_t) * (big / kScanBlock + 2));  // scan block sums
+  b += align_up(sizeof(int32_t) * (kLptKeys * nchunks + 1)); // longest-first histogram
+  b += align_up(sizeof(int4) * (p.item_cap + 1));           // unsorted items
+  return b;
+}
+
+bsa_status plan_build(Plan &p, const uint8_t *mask, const int32_t *page_table, void *scratch,
+                      size_t scratch_bytes) {
+  hipStream_t s = p.stream;
+  uint8_t *sp = (uint8_t *)scratch;
+  auto take = [&](size_t bytes) {
+    uint8_t *r = sp;
+    sp += align_up(bytes);
+    return r;
+  };
+  const int64_t nchunks = (p.item_cap + kThreads - 1) / kThreads;
+  int32_t *list_len = (int32_t *)take(sizeof(int32_t) * (p.nlists + 1));
+  int32_t *cnt = (int32_t *)take(sizeof(int32_t) * 3 * (p.nrows + 1));
+  int32_t *off = (int32_t *)take(sizeof(int32_t) * 3 * (p.nrows + 1));
+  const int64_t big = std::max<int64_t>({p.nlists + 1, 3 * (p.nrows + 1), kLptKeys * nchunks + 1});
+  int32_t *bsum = (int32_t *)take(sizeof(int32_t) * (big / kScanBlock + 2));
+  int32_t *hist = (int32_t *)take(sizeof(int32_t) * (kLptKeys * nchunks + 1));
+  int4 *raw_items = (int4 *)take(sizeof(int4) * (p.item_cap + 1));
+  if ((size_t)(sp - (uint8_t *)scratch) > scratch_bytes)
+    return fail(BSA_ERR_HIP, "planner scratch too small");
+
+  // Live-bit decoding per head now that the tile shape is known: query
+  // sub-blocks of min(bq, Tq) rows (one sub-block in union mode, whose bits
+  // are per key sub-block only), key sub-blocks of min(bk, Tk) keys.
+  for (int h = 0; h < p.Hq; ++h) {
+    HeadMeta &m = p.hmeta_host[h];
+    const int aq = std::min(p.bq[h], p.rg.tq), ak = std::min(p.bk[h], p.rg.tk);
+    m.lq = p.uni ? 30 : __builtin_ctz(aq);
+    m.lk = __builtin_ctz(ak);
+    m.mk = p.rg.tk / ak;
+  }
+  HIP_TRY(hipMemcpyAsync(p.hmeta, p.hmeta_host.data(), sizeof(HeadMeta) * p.Hq,
+                         hipMemcpyHostToDevice, s));
+
+  MapArgs m{};
+  m.mask = mask, m.U = p.uni_bits, m.hm = p.hmeta, m.page_table = page_table;
+  int64_t mask_bstride = 0;
+  for (int h = 0; h < p.Hq; ++h)
+    mask_bstride += ((p.Sq + p.bq[h] - 1) / p.bq[h]) * ((p.Skv + p.bk[h] - 1) / p.bk[h]);
+  m.mask_bstride = mask_bstride, m.unkb = p.unkb, m.Sq = p.Sq, m.off = p.off;
+  m.nqt = p.nqt, m.nkt = p.nkt, m.nlists = p.nlists;
+  m.Hq = p.Hq, m.Hkv = p.Hkv, m.G = p.G, m.bcast = p.nbm == 1 ? 1 : 0, m.uni = p.uni;
+  m.paged = p.paged, m.causal = p.causal, m.tq = p.rg.tq, m.tk = p.rg.tk, m.pps = p.pps, m.P = p.P;
+  m.list_len = list_len, m.list_off = p.list_off;
+  m.ent_kt = p.ent_kt, m.ent_page = p.ent_page, m.ent_live = p.ent_live;
+
+  const unsigned gl = grid_for(p.nlists * 64);
+  if (p.nlists > 0) hipLaunchKernelGGL(k_map<false>, dim3(gl), dim3(kThreads), 0, s, m);
+  if (bsa_status st = scan(list_len, p.nlists, p.list_off, bsum, s)) return st;
+  if (p.nlists > 0) hipLaunchKernelGGL(k_map<true>, dim3(gl), dim3(kThreads), 0, s, m);
+
+  RowArgs ra{};
+  ra.list_off = p.list_off, ra.ent_kt = p.ent_kt, ra.row_ent = p.row_ent;
+  ra.cnt_items = cnt, ra.cnt_slots = cnt + (p.nrows + 1), ra.cnt_comb = cnt + 2 * (p.nrows + 1);
+  ra.nrows = p.nrows, ra.nqt = p.nqt, ra.Sq = p.Sq, ra.off = p.off;
+  ra.Hq = p.Hq, ra.Hkv = p.Hkv, ra.G = p.G, ra.pack = p.rg.pack, ra.uni = p.uni;
+  ra.causal = p.causal, ra.nlb = (int)p.nlb, ra.tq = p.rg.tq, ra.tr = p.tr, ra.tk = p.rg.tk;
+  ra.split = p.rg.split;
+  if (p.nrows > 0) hipLaunchKernelGGL(k_rows, dim3(grid_for(p.nrows)), dim3(kThreads), 0, s, ra);
+  int32_t *item_off = off, *slot_off = off + (p.nrows + 1), *comb_off = off + 2 * (p.nrows + 1);
+  if (bsa_status st = scan(ra.cnt_items, p.nrows, item_off, bsum, s)) return st;
+  if (bsa_status st = scan(ra.cnt_slots, p.nrows, slot_off, bsum, s)) return st;
+  if (bsa_status st = scan(ra.cnt_comb, p.nrows, comb_off, bsum, s)) return st;
+  int4 *dst = p.rg.sched == 1 ? raw_items : (int4 *)p.items;
+  if (p.nrows > 0)
+    hipLaunchKernelGGL(k_items, dim3(grid_for(p.nrows)), dim3(kThreads), 0, s, p.row_ent, item_off,
+                       slot_off, comb_off, p.nrows, dst, p.comb);
+  hipLaunchKernelGGL(k_totals, dim3(1), dim3(1), 0, s, p.list_off, p.nlists, item_off, slot_off,
+                     comb_off, p.nrows, p.counters);
+  if (p.rg.sched == 1 && nchunks > 0) {
+    hipLaunchKernelGGL(k_lpt_hist, dim3((unsigned)nchunks), dim3(kThreads), 0, s, raw_items,
+                       p.counters, nchunks, hist);
+    if (bsa_status st = scan(hist, kLptKeys * nchunks, hist, bsum, s)) return st;
+    hipLaunchKernelGGL(k_lpt_place, dim3((unsigned)nchunks), dim3(kThreads), 0, s, raw_items,
+                       p.counters, nchunks, hist, (int4 *)p.items);
+  }
+  HIP_TRY(hipGetLastError());
+  return BSA_OK;
+}
+
+}  // namespace bsa

@@ -1,0 +1,187 @@
+/*
+ * bsa.h -- libbsa: block-sparse scaled-dot-product attention for AMD MI355X
+ * (gfx950), C ABI.
+ *
+ * The operation (Tessera, "Decoupling Logical Masks from GPU Execution for
+ * Dynamic Block-Sparse Attention", abstract): block-sparse attention computes
+ * only the blocks that a logical mask selects; the mask specifies which
+ * attention interactions are computed. For query head h, query row i and key
+ * j, key j is allowed iff the head's logical mask selects the block pair
+ * (i / block_q[h], j / block_k[h]) and, when causal, j <= i + causal_kv_offset.
+ * The result is exact softmax attention over the allowed keys:
+ *   O[i]   = sum_j softmax_j(scale * q_i . k_j) v_j
+ *   LSE[i] = ln sum_j exp(scale * q_i . k_j)
+ * and a row with no allowed key gets O[i] = 0 and LSE[i] = -inf.
+ *
+ * With gqa_union set (CompactAttention, summary: the 2-D block mask is a KV
+ * selection signal; a query-block union plus an intra-group union give a
+ * per-group KV block table), every query head of a kv group attends to the
+ * union, over the group's heads and over all query blocks, of the selected
+ * key blocks (then the causal bound).
+ *
+ * The work is split in two calls, as the decoupling asks:
+ *   bsa_plan     maps the logical mask to a physical tile plan for gfx950 --
+ *                keeping, merging or subdividing logical blocks into physical
+ *                tiles, building per-query-tile key-tile lists, the GQA union
+ *                tables and paged tables, and the work list -- with the tile
+ *                shape and schedule picked by a lookup table built offline
+ *                (Tessera, abstract: physical mapping layer, task organization
+ *                layer, profile-guided regime selection).
+ *   bsa_forward  runs attention over Q/K/V with a plan and writes O and LSE.
+ *
+ * Conventions for every call:
+ *   - Functions never throw; they return a bsa_status. On failure a
+ *     thread-local message is available from bsa_last_error().
+ *   - Every argument is checked before any device work is queued, so an
+ *     error status means nothing was launched.
+ *   - "device pointer" means memory allocated on the current HIP device; the
+ *     caller owns it. "stream" is a hipStream_t passed as void* (NULL: the
+ *     null stream). Work is queued on that stream; bsa_forward never
+ *     synchronises.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSA_ABI_VERSION 1
+
+typedef enum {
+  BSA_OK = 0,
+  BSA_ERR_INVALID_ARG = 1,    /* null pointer, bad value, misaligned tensor */
+  BSA_ERR_UNSUPPORTED = 2,    /* valid but outside what this build supports */
+  BSA_ERR_SHAPE_MISMATCH = 3, /* tensors or dtype disagree with the plan */
+  BSA_ERR_OUT_OF_MEMORY = 4,  /* a device or host allocation failed */
+  BSA_ERR_HIP = 5,            /* a HIP runtime call failed (message names it) */
+  BSA_ERR_LUT = 6             /* lookup table file missing or malformed */
+} bsa_status;
+
+typedef enum { BSA_BF16 = 0, BSA_F32 = 1 } bsa_dtype;
+
+typedef struct bsa_plan_s *bsa_plan_t;
+typedef struct bsa_lut_s *bsa_lut_t;
+
+/* Problem description. Host memory; bsa_plan copies what it needs. */
+typedef struct {
+  int32_t batch;         /* >= 1 */
+  int32_t num_q_heads;   /* Hq >= 1 */
+  int32_t num_kv_heads;  /* Hkv >= 1, Hq % Hkv == 0; q head h reads kv head h / (Hq/Hkv) */
+  int64_t seqlen_q;      /* Sq >= 0, need not be a block multiple */
+  int64_t seqlen_kv;     /* Skv >= 0 */
+  int32_t head_dim;      /* D: 64 or 128 */
+  int32_t dtype;         /* bsa_dtype of Q, K, V and O; LSE is always fp32 */
+  const int32_t *block_q; /* [Hq] logical query block size per head: 16..512, power of 2 */
+  const int32_t *block_k; /* [Hq] logical key block size per head: 16..512, power of 2 */
+  int32_t mask_batch_broadcast; /* 1: one mask per head shared by every batch */
+  int32_t causal;        /* 1: key j allowed only if j <= i + causal_kv_offset */
+  int64_t causal_kv_offset;
+  int32_t gqa_union;     /* 1: union semantics above; heads of a group share block_k */
+  int32_t paged;         /* 1: K/V are page pools read through a page table */
+  int32_t page_size;     /* tokens per page; a multiple of 64 when paged */
+  int32_t pages_per_seq; /* page-table row length; page_size * pages_per_seq >= Skv */
+  int32_t num_pages;     /* pages in each pool; every table entry must be < num_pages */
+  float softmax_scale;   /* 0 => 1 / sqrt(head_dim) */
+} bsa_problem;
+
+/* A strided tensor whose last (head_dim) axis is contiguous. Strides count
+ * elements. data and every stride must be 16-byte aligned.
+ *   Q, O:  [batch][Hq][Sq][D]  -> stride_b, stride_h, stride_s
+ *   K, V:  [batch][Hkv][Skv][D], or when paged a pool [num_pages][page_size][Hkv][D]
+ *          with stride_b = page stride, stride_s = token stride within a page,
+ *          stride_h = kv-head stride. */
+typedef struct {
+  void *data;
+  int64_t stride_b, stride_h, stride_s;
+} bsa_tensor;
+
+/* Plan statistics, filled by bsa_plan_stats. */
+typedef struct {
+  int32_t tile_q, tile_k;   /* physical tile shape */
+  int32_t sched;            /* 0 = row order (locality), 1 = longest first */
+  int32_t split;            /* key tiles per work item before a row is split; 0 = never */
+  int32_t pack;             /* 1: a group's heads share each task */
+  int32_t reserved;
+  int64_t rows, entries, items, partial_slots, combines;
+  int64_t logical_nnz;      /* selected logical blocks in the mask (before any union) */
+  int64_t logical_blocks;   /* all logical blocks of the mask */
+  int64_t density_pm;       /* 1000 * logical_nnz / logical_blocks */
+  int64_t imbalance16;      /* 16 * heaviest row / mean row, worst head */
+  int64_t effective_blocks; /* blocks computed: after the union, causally feasible, all batches */
+  double effective_flops;   /* sum over effective blocks of 4 * bq * bk * D */
+  int64_t tile_live_subblocks; /* live (query sub-block, key sub-block) pairs over all entries */
+} bsa_plan_info;
+
+/* ABI version of the library (BSA_ABI_VERSION it was built with). */
+int bsa_abi_version(void);
+
+/* Static text for a status code. */
+const char *bsa_status_str(bsa_status s);
+
+/* Message of the last failure on the calling thread ("" if none). */
+const char *bsa_last_error(void);
+
+/* Lookup table of execution regimes (Tessera, abstract: plan selection through
+ * a lookup table built from offline profiling). Text format:
+ *   bsa-lut 1
+ *   rule D dtype union paged bq_lo bq_hi bk_lo bk_hi dens_lo dens_hi imb_lo imb_hi
+ *        -> Tq Tk sched split pack
+ * D, dtype (bf16|f32), union and paged (0|1) may be '*'; ranges are inclusive
+ * and match the smallest block_q, smallest block_k, density per mille and
+ * imbalance x16 of the mask; sched is local|lpt; the first matching rule
+ * wins; with no match the built-in default applies (128, 64, local, 0, 1).
+ * bsa_lut_load reads a file (path NULL: the built-in default with no rules);
+ * bsa_lut_parse reads text. The table is host memory owned by the library,
+ * immutable, and may be shared by threads; free it with bsa_lut_free. */
+bsa_status bsa_lut_load(const char *path, bsa_lut_t *out);
+bsa_status bsa_lut_parse(const char *text, bsa_lut_t *out);
+void bsa_lut_free(bsa_lut_t lut);
+
+/* Build a plan for one mask (Tessera, abstract: physical mapping layer and
+ * task organization layer; CompactAttention, summary: per-group KV block
+ * tables over a paged cache).
+ *   mask        device pointer, uint8, nonzero = selected. For each mask batch
+ *               bm (1 if mask_batch_broadcast, else batch) and head h, a
+ *               row-major [ceil(Sq/bq_h)][ceil(Skv/bk_h)] block, concatenated
+ *               in (bm, h) order. Read only during the call.
+ *   page_table  device pointer, int32 [batch][pages_per_seq] when paged, else
+ *               ignored. Read only during the call; entries are validated.
+ *   lut         regime table (NULL: built-in default).
+ *   stream      stream for the planning kernels.
+ * The call blocks once, on one small device-to-host read of the mask
+ * features; all other planning work is queued on the stream, so the plan is
+ * ready for any work queued on the same stream afterwards. The plan owns its
+ * device memory, is immutable, and can be used by any number of bsa_forward
+ * calls with matching tensors; free it with bsa_plan_free. */
+bsa_status bsa_plan(const bsa_problem *problem, const uint8_t *mask, const int32_t *page_table,
+                    bsa_lut_t lut, void *stream, bsa_plan_t *out);
+
+/* Attention forward over a plan (Tessera, abstract: compute only the blocks
+ * the logical mask selects). q, k, v, o: device tensors as described at
+ * bsa_tensor, in the plan's dtype; lse: device pointer, fp32 [batch][Hq][Sq].
+ * Every O row and LSE entry is written exactly once (empty rows included), so
+ * O need not be cleared. Queued on stream; never synchronises. O and LSE must
+ * not overlap Q, K or V. */
+bsa_status bsa_forward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k,
+                       const bsa_tensor *v, bsa_tensor *o, float *lse, void *stream);
+
+/* Canonical byte image of a plan (header, features, lists, entries, rows,
+ * work list), for comparison with the reference planner. With host_buf NULL
+ * only *bytes is set to the size needed; otherwise *bytes is the capacity on
+ * input and the size on output. Synchronises with the plan's stream. */
+bsa_status bsa_plan_export(bsa_plan_t plan, void *host_buf, size_t *bytes);
+
+/* Plan statistics. Synchronises with the plan's stream. */
+bsa_status bsa_plan_stats(bsa_plan_t plan, bsa_plan_info *out);
+
+/* Release a plan after all work using it has completed. NULL is ignored. */
+void bsa_plan_free(bsa_plan_t plan);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BSA_H */

@@ -443,6 +443,7 @@ int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_tabl
   }
   /* Adjustments that make the regime valid for this problem. */
   if (!(p->gqa_union && (gs == 2 || gs == 4))) rg.pack = 0;
+  if (p->dtype == 1) rg.tk = 64; /* fp32 tiles hold 64 keys */
   if (p->paged && p->page_size % rg.tk) {
     if (rg.tk == 128 && p->page_size % 64 == 0) rg.tk = 64;
     else {
@@ -581,7 +582,11 @@ int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_tabl
   }
   if (rg.sched == 1 && nitems > 1) {
     int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * 2 * nitems);
-    for (int64_t i = 0; i < nitems; ++i) keys[2 * i] = items[i].e1 - items[i].e0, keys[2 * i + 1] = i;
+    /* Key: item length capped at 1023 (longer items tie and keep row order). */
+    for (int64_t i = 0; i < nitems; ++i) {
+      int64_t len = items[i].e1 - items[i].e0;
+      keys[2 * i] = len < 1023 ? len : 1023, keys[2 * i + 1] = i;
+    }
     qsort(keys, nitems, 2 * sizeof(int64_t), item_cmp);
     item_t *sorted = (item_t *)malloc(sizeof(item_t) * nitems);
     for (int64_t i = 0; i < nitems; ++i) sorted[i] = items[keys[2 * i + 1]];

@@ -1,0 +1,109 @@
+"""Shared GPU-test helpers: run libbsa through its C ABI and compare with the
+oracle (plan images byte for byte, O/LSE within the stated tolerances)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import block_sparse_attention_08_amd as bsa
+from tests.plan_image import decode
+
+# Tolerances for bf16 inputs with fp32 accumulation (and fp32 inputs):
+# max |O_gpu - O_ref| <= 2e-2, mean <= 2e-3, |LSE_gpu - LSE_ref| <= 1e-3.
+O_MAX, O_MEAN, LSE_MAX = 2e-2, 2e-3, 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def forced_lut_text(tq=128, tk=64, sched="local", split=0, pack=1) -> str:
+    return ("bsa-lut 1\nrule * * * * 0 1000000 0 1000000 0 1000000 0 100000000 -> "
+            f"{tq} {tk} {sched} {split} {pack}\n")
+
+
+def plan_diff(a: bytes, b: bytes) -> str:
+    if len(a) >= 8 and len(b) >= 8:
+        try:
+            pa, pb = decode(a), decode(b)
+        except Exception as e:  # noqa: BLE001
+            return f"undecodable ({e})"
+        for k in pa.h:
+            if pa.h[k] != pb.h[k]:
+                return f"header {k}: gpu {pa.h[k]} ref {pb.h[k]}"
+        for f in ("feat", "list_off", "kt", "page", "live", "rows", "items", "comb"):
+            x, y = getattr(pa, f), getattr(pb, f)
+            if x is None:
+                continue
+            if x.shape != y.shape or not np.array_equal(x, y):
+                idx = np.argwhere(x.reshape(-1)[: y.size] != y.reshape(-1)[: x.size])
+                return f"{f}: shapes {x.shape} {y.shape}, first diff at {idx[:3].ravel()}"
+    return f"lengths {len(a)} vs {len(b)}"
+
+
+def to_device(w, device_gen=False):
+    import torch
+    q, k, v = w.make_qkv(device="cuda" if device_gen else "cpu")
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    mask = torch.from_numpy(np.ascontiguousarray(w.mask)).cuda()
+    table = torch.from_numpy(np.ascontiguousarray(w.page_table)).cuda() if w.paged else None
+    return q, k, v, mask, table
+
+
+def compare(w, o_gpu, lse_gpu, o_ref, lse_ref, rows):
+    """o_gpu/lse_gpu: values at the sampled rows (float64)."""
+    nonempty = np.isfinite(lse_ref)
+    err = np.abs(o_gpu - o_ref)
+    max_o, mean_o = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
+    lerr = np.abs(lse_gpu[nonempty] - lse_ref[nonempty])
+    max_l = float(lerr.max()) if lerr.size else 0.0
+    empty_ok = bool((o_gpu[~nonempty] == 0).all() and np.isneginf(lse_gpu[~nonempty]).all())
+    return dict(max_o=max_o, mean_o=mean_o, max_lse=max_l, empty_ok=empty_ok,
+                rows=len(rows), empty_rows=int((~nonempty).sum()))
+
+
+def run_case(ref, w, lut_text=None, rows=None, device_gen=False, check_plan=True, label=""):
+    """Plan + forward on the GPU, plan image and sampled O/LSE vs the oracle."""
+    import torch
+    say(f"[case] {label or w.name}: B={w.batch} Hq={w.hq} Hkv={w.hkv} Sq={w.sq} Skv={w.skv} "
+        f"D={w.d} {w.dtype} union={int(w.gqa_union)} paged={int(w.paged)} causal={int(w.causal)}")
+    q, k, v, mask, table = to_device(w, device_gen)
+    lut = bsa.Lut.parse(lut_text) if lut_text else bsa.Lut.load(bsa.DEFAULT_LUT)
+    text = lut_text if lut_text else open(bsa.DEFAULT_LUT).read()
+    plan = bsa.plan(w.problem_dict(), mask, table, lut)
+    res = {}
+    if check_plan:
+        img = plan.export()
+        ref_img = ref.plan(w, lut_text=text)
+        assert img == ref_img, "plan differs from the reference planner: " + plan_diff(img, ref_img)
+        res["plan_bytes"] = len(img)
+    o, lse = plan.forward(q, k, v)
+    torch.cuda.synchronize()
+    if rows is None:
+        B, H, S = w.batch, w.hq, w.sq
+        rows = np.stack(np.meshgrid(np.arange(B), np.arange(H), np.arange(S), indexing="ij"),
+                        -1).reshape(-1, 3)
+    rows = np.asarray(rows, np.int64).reshape(-1, 3)
+    qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
+    o_ref, lse_ref = ref.forward(w, qh, kh, vh, mode=1, rows=rows)
+    ridx = [torch.from_numpy(rows[:, i]).cuda() for i in range(3)]
+    o_g = o[ridx[0], ridx[1], ridx[2]].float().cpu().numpy().astype(np.float64)
+    l_g = lse[ridx[0], ridx[1], ridx[2]].cpu().numpy().astype(np.float64)
+    res.update(compare(w, o_g, l_g, o_ref, lse_ref, rows))
+    res["stats"] = plan.stats()
+    say(f"[result] {label or w.name}: max|dO|={res['max_o']:.3e} mean|dO|={res['mean_o']:.3e} "
+        f"max|dLSE|={res['max_lse']:.3e} rows={res['rows']} empty={res['empty_rows']}")
+    assert res["empty_ok"], "empty rows must be exactly O=0, LSE=-inf"
+    assert res["max_o"] <= O_MAX and res["mean_o"] <= O_MEAN and res["max_lse"] <= LSE_MAX, res
+    plan.free()
+    del q, k, v, o, lse
+    return res
+
+
+def sample_rows(w, n=256, seed=0, extra=()):
+    g = np.random.default_rng(seed)
+    rows = np.stack([g.integers(0, w.batch, n), g.integers(0, w.hq, n), g.integers(0, w.sq, n)], 1)
+    edge = [[0, 0, 0], [w.batch - 1, w.hq - 1, w.sq - 1]] + [list(e) for e in extra]
+    return np.concatenate([rows, np.array(edge, np.int64).reshape(-1, 3)])

@@ -43,8 +43,13 @@ def check_worklist(p):
         else:
             assert its[0][2] == -1 and r not in comb
     if h["sched"] == 1:
-        ln = items[:, 2] - items[:, 1]
+        ln = np.minimum(items[:, 2] - items[:, 1], 1023)
         assert (np.diff(ln) <= 0).all()
+        # Stable: equal keys keep the unsorted order (row, then chunk).
+        for key in np.unique(ln):
+            sel = items[ln == key]
+            order = sel[:, 0].astype(np.int64) * (1 << 31) + sel[:, 1]
+            assert (np.diff(order) > 0).all()
 
 
 def check_elements(w, p):
