@@ -1,0 +1,248 @@
+"""Benchmark of the block-sparse attention hot path on one MI355X.
+
+One step = one BSA request: bsa_plan (mask features, regime lookup, physical
+mapping, compaction and scans, work list) followed by bsa_forward (fused
+attention kernel and, when rows are split, the combine kernel) on one batch of
+seeded synthetic inputs already resident in HBM. The metric counts only the
+logical blocks the mask selects: 4 * bq * bk * D FLOPs per selected block.
+
+Prints one JSON line. ``--gpus N`` with N > 1 exits: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective sparse-attn TFLOP/s (selected tiles only) + % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA peak
+PEAK_HBM_GBS = 8000.0
+
+
+def workload(name: str):
+    from block_sparse_attention_08_amd import workloads as W
+    table = {
+        "video_dit": lambda: W.video_dit(),
+        "chunked_prefill": lambda: W.chunked_prefill(),
+        "affine_bs64": lambda: W.affine(bs=64),
+        "affine_bs32": lambda: W.affine(bs=32),
+        "affine_bs64_w4096": lambda: W.affine(bs=64, window=4096),
+        "affine_bs64_w8192": lambda: W.affine(bs=64, window=8192),
+        "long_video": lambda: W.long_video(),
+        "tiny": lambda: W.tiny(),
+    }
+    return table[name]()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("bsa_attention.hip", "bsa_internal.h"):
+        h.update(open(os.path.join(ROOT, "block_sparse_attention_08_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name: str, launches_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def allowed_keys_per_row(w, b: int, h: int) -> np.ndarray:
+    """Number of allowed keys of every query row of (b, h): the selected blocks
+    (the group's union in union mode), clipped to the sequence, then causal."""
+    bm = 0 if w.mask_broadcast else b
+    if w.gqa_union:
+        gs = w.hq // w.hkv
+        sel = np.zeros(w.nkb(h), bool)
+        for h2 in range((h // gs) * gs, (h // gs + 1) * gs):
+            sel |= w.head_mask(bm, h2).astype(bool).any(0)
+        blk = np.broadcast_to(sel, (w.nqb(h), w.nkb(h)))
+    else:
+        blk = w.head_mask(bm, h).astype(bool)
+    keys = np.arange(w.skv)
+    row_blk = np.arange(w.sq) // w.bq[h]
+    out = np.zeros(w.sq, np.int64)
+    for qb in range(w.nqb(h)):
+        allowed = blk[qb][keys // w.bk[h]]
+        rows = np.nonzero(row_blk == qb)[0]
+        if not w.causal:
+            out[rows] = allowed.sum()
+        else:
+            csum = np.cumsum(allowed)
+            lim = np.clip(rows + w.causal_offset, -1, w.skv - 1)
+            out[rows] = np.where(lim >= 0, csum[np.maximum(lim, 0)], 0)
+    return out
+
+
+def cpu_baseline(w, q, k, v, target_s: float = 12.0):
+    """The fp64 oracle timed on this host's cores over a bounded sample of
+    query rows (whole 128-row tiles, spread over heads), in TFLOP/s of
+    selected work."""
+    import torch
+    from oracle import ref
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
+
+    def rows_for(ntiles, seed=0):
+        g = np.random.default_rng(seed)
+        out = []
+        for t in range(ntiles):
+            b = int(g.integers(0, w.batch))
+            h = int(g.integers(0, w.hq))
+            t0 = int(g.integers(0, max(1, -(-w.sq // 128)))) * 128
+            for i in range(t0, min(w.sq, t0 + 128)):
+                out.append((b, h, i))
+        return np.array(out, np.int64)
+
+    def work(rows):
+        # 4 * D FLOPs per allowed (query, key) pair of the sampled rows.
+        tot = 0
+        cache = {}
+        for b, h, i in rows:
+            key = (int(b), int(h))
+            if key not in cache:
+                cache[key] = allowed_keys_per_row(w, *key)
+            tot += int(cache[key][i])
+        return 4.0 * w.d * tot
+
+    rows = rows_for(2)
+    t = time.perf_counter()
+    ref.forward(w, qh, kh, vh, mode=1, rows=rows, nthreads=threads)
+    dt = time.perf_counter() - t
+    ntiles = max(2, min(20000, int(2 * target_s / max(dt, 1e-3))))
+    rows = rows_for(ntiles, seed=1)
+    t = time.perf_counter()
+    ref.forward(w, qh, kh, vh, mode=1, rows=rows, nthreads=threads)
+    dt = time.perf_counter() - t
+    flops = work(rows)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} query rows ({ntiles} random 128-row tiles) of the {w.name} "
+                      f"workload, fp64 block-skipping oracle, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="video_dit")
+    ap.add_argument("--lut", default=None, help="regime table (default: the packaged gfx950 table)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs the block-sparse attention path on one GPU; --gpus {args.gpus} "
+              "is not supported (each GPU would run its own heads; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_08_amd as bsa
+
+    torch.cuda.set_device(0)
+    w = workload(args.workload)
+    q, k, v = w.make_qkv(device="cuda")
+    mask = torch.from_numpy(np.ascontiguousarray(w.mask)).cuda()
+    table = torch.from_numpy(np.ascontiguousarray(w.page_table)).cuda() if w.paged else None
+    lut = bsa.Lut.load(args.lut or bsa.DEFAULT_LUT)
+    prob = w.problem_dict()
+    o = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.hq, w.sq), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        p = bsa.plan(prob, mask, table, lut)
+        if ev is not None:
+            ev[0].record(stream)
+        p.forward(q, k, v, o, lse)
+        if ev is not None:
+            ev[1].record(stream)
+        return p
+
+    p0 = step()
+    stats = p0.stats()
+    p0.free()
+    eff_flops = stats["effective_flops"]
+    for _ in range(args.warmup):
+        p = step()
+        torch.cuda.synchronize()
+        p.free()
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    plans = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        plans.append(step(events[i]))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for p in plans:
+        p.free()
+    fwd_ms = [a.elapsed_time(b) for a, b in events]
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    fwd_avg = float(np.mean(fwd_ms))
+
+    # Plan-only timing (the planner's own cost, one feature readback included).
+    torch.cuda.synchronize()
+    tp = time.perf_counter()
+    for _ in range(5):
+        p = bsa.plan(prob, mask, table, lut)
+        torch.cuda.synchronize()
+        p.free()
+    plan_ms = (time.perf_counter() - tp) * 1e3 / 5
+
+    value = eff_flops / (ms_step * 1e-3) / 1e12
+    achieved = eff_flops / (fwd_avg * 1e-3) / 1e12
+    esz = 2 if w.dtype == "bf16" else 4
+    compulsory = esz * (q.numel() * 2 + k.numel() + v.numel()) + 4 * lse.numel()
+    traffic = measured_traffic(args.workload, None)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": w.batch, "q_heads": w.hq,
+                   "kv_heads": w.hkv, "seqlen_q": w.sq, "seqlen_kv": w.skv, "head_dim": w.d,
+                   "block_q": sorted(set(w.bq)), "block_k": sorted(set(w.bk)),
+                   "density_pm": stats["density_pm"], "effective_blocks": stats["effective_blocks"],
+                   "regime": {k2: stats[k2] for k2 in ("tile_q", "tile_k", "sched", "split", "pack")}},
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "forward_ms": round(fwd_avg, 4),
+        "forward_tflops": round(achieved, 3),
+        "plan_ms": round(plan_ms, 4),
+        "effective_flops": eff_flops,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "k_attn", "compulsory_bytes": compulsory},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

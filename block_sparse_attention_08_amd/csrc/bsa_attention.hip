@@ -408,6 +408,255 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 kernel: K/V tiles stream from HBM straight into LDS with buffer loads
+// (no register staging; rows past the end of the sequence read as zero from
+// the buffer range check), in an XOR-swizzled row-major layout that keeps the
+// MFMA operand reads free of bank conflicts. The V^T operand of P V^T is read
+// with the LDS transpose read (ds_read_b64_tr_b16): two reads give a lane 8
+// consecutive keys of one head-dim column. The online softmax rescales O only
+// when a row maximum has grown by more than 2^8 since the last rescale; the
+// final O / l is the same quantity either way.
+// ---------------------------------------------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D, int TK>
+struct CfgB {
+  static constexpr int ROWB = D * 2;                  // bytes per K/V row in LDS
+  static constexpr int CPR = D / 8;                   // 16-byte chunks per row
+  static constexpr int TILEB = TK * ROWB;             // bytes of one K (or V) tile
+  static constexpr int STAGEB = 2 * TILEB;            // K + V
+  static constexpr int LOADS = TILEB / (kThreads * 16);  // 16-byte loads per thread per tile
+  static constexpr int NKB = TK / 32;
+  static constexpr int NDB = D / 32;
+  // K rows: 16-byte chunk c of row r sits at chunk c ^ swz_k(r); V rows: c ^ swz_v(r).
+  static __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  static __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+};
+
+constexpr float kRescaleThreshold = 8.0f;  // log2 units: P values stay below 2^8
+
+template <int D, int TK>
+__global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(AttnArgs a) {
+  using C = CfgB<D, TK>;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::STAGEB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, hh = lane >> 5;
+  const int nitems = a.counters[CNT_ITEMS];
+  const int grid = gridDim.x;
+  int lid = blockIdx.x;
+  if ((grid & 7) == 0) lid = (blockIdx.x & 7) * (grid >> 3) + (blockIdx.x >> 3);
+  const uint16_t *__restrict__ Q = (const uint16_t *)a.q;
+
+  // Per-lane LDS byte offsets that do not depend on the tile.
+  // K operand row for score block t: 32 t + perm(n); chunk (2 cc + hh).
+  const int krow0 = perm_bf16(n);
+  // V^T operand: lane reads rows 16 c2 + 8 hh + (j >> 2) (+4) at column
+  // 32 u + 16 dsub + 4 (j & 3).
+  const int vj = lane & 15, vdsub = (lane >> 4) & 1;
+  const int vrow0 = 8 * hh + (vj >> 2);
+  const int vbyte = 8 * (vj & 1);
+
+  for (int it = lid; it < nitems; it += grid) {
+    const int4 item = ((const int4 *)a.items)[it];
+    const int r = item.x, e0 = item.y, e1 = item.z, slot = item.w;
+    const RowGeo geo = row_geo(a, r, wave);
+    const RowGeo geo0 = row_geo(a, r, 0);
+    const HeadMeta hm = a.hm[geo.head];
+    const int64_t qpos = geo.q0 + n;
+    const bool qvalid = qpos < a.Sq;
+
+    bf16x8 qb[D / 16];
+    {
+      const uint16_t *qp = Q + geo.b * a.q_sb + geo.head * a.q_sh + (qvalid ? qpos : 0) * a.q_ss;
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        uint4 x = qvalid ? *(const uint4 *)(qp + 16 * c + 8 * hh) : make_uint4(0, 0, 0, 0);
+        qb[c] = __builtin_bit_cast(bf16x8, x);
+      }
+    }
+    const uint16_t *kbase_ptr = (const uint16_t *)a.k + (a.paged ? 0 : geo0.b * a.k_sb) + geo0.g * a.k_sh;
+    const uint16_t *vbase_ptr = (const uint16_t *)a.v + (a.paged ? 0 : geo0.b * a.v_sb) + geo0.g * a.v_sh;
+
+    // Issue the buffer loads of tile e into stage st (all 256 threads).
+    auto issue = [&](int e, int st) {
+      const int64_t kt = a.ent_kt[e];
+      const int64_t k0 = kt * TK;
+      const int left = (int)min<int64_t>(a.Skv - k0, TK);  // rows that exist
+      const uint16_t *kb, *vb;
+      if (a.paged) {
+        const int64_t pg = a.ent_page[e];
+        kb = kbase_ptr + pg * a.k_sb + (k0 % a.P) * a.k_ss;
+        vb = vbase_ptr + pg * a.v_sb + (k0 % a.P) * a.v_ss;
+      } else {
+        kb = kbase_ptr + k0 * a.k_ss;
+        vb = vbase_ptr + k0 * a.v_ss;
+      }
+      const int kbytes = (int)((left - 1) * a.k_ss * 2 + D * 2);
+      const int vbytes = (int)((left - 1) * a.v_ss * 2 + D * 2);
+      const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void *)kb, 0, kbytes, 0x00020000);
+      const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void *)vb, 0, vbytes, 0x00020000);
+      uint8_t *ks = lds + st * C::STAGEB;
+#pragma unroll
+      for (int u = 0; u < C::LOADS; ++u) {
+        const int L = u * kThreads + tid;             // 16-byte LDS slot, lane-linear per wave
+        const int row = L / C::CPR, pos = L % C::CPR;
+        const int koff = row * (int)a.k_ss * 2 + ((pos ^ C::swz_k(row)) << 4);
+        const int voff = row * (int)a.v_ss * 2 + ((pos ^ C::swz_v(row)) << 4);
+        uint8_t *dst = ks + (u * kThreads + wave * 64) * 16;
+        // Rows past the sequence end fall outside the buffer range and read 0.
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void *)dst, 16, row < left ? koff : kbytes, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void *)(dst + C::TILEB), 16, row < left ? voff : vbytes, 0, 0, 0);
+      }
+    };
+
+    f32x16 o[C::NDB];
+#pragma unroll
+    for (int u = 0; u < C::NDB; ++u) o[u] = f32x16{};
+    float m_ref = -INFINITY, l_run = 0.f;
+
+    const int iq_lo = geo.qbase >> hm.lq;
+    const int niq = hm.lq >= 5 ? 1 : (32 >> hm.lq);
+    const uint64_t wbits = ((1ull << (hm.mk * niq)) - 1ull) << (iq_lo * hm.mk);
+    const int qsub = ((geo.qbase + n) >> hm.lq) * hm.mk;
+
+    if (e0 < e1) issue(e0, 0);
+    for (int e = e0; e < e1; ++e) {
+      const int st = (e - e0) & 1;
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's tile loads have landed
+      __syncthreads();                // ... and every wave's; stage st^1 is free
+      if (e + 1 < e1) issue(e + 1, st ^ 1);
+      const uint8_t *ks = lds + st * C::STAGEB;
+      const uint8_t *vs = ks + C::TILEB;
+
+      // ---- S^T = K Q^T ----
+      f32x16 s[C::NKB];
+#pragma unroll
+      for (int t = 0; t < C::NKB; ++t) {
+        s[t] = f32x16{};
+        const int row = 32 * t + krow0;
+        const uint8_t *kr = ks + row * C::ROWB;
+        const int sw = C::swz_k(row);
+#pragma unroll
+        for (int cc = 0; cc < D / 16; ++cc) {
+          const bf16x8 af = *(const bf16x8 *)(kr + (((2 * cc + hh) ^ sw) << 4));
+          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qb[cc], s[t], 0, 0, 0);
+        }
+      }
+
+      // ---- mask (tiles at a sequence end, the causal diagonal or a dead sub-block) ----
+      const int64_t kb0 = (int64_t)a.ent_kt[e] * TK;
+      const uint32_t live = a.ent_live[e];
+      const bool need = (kb0 + TK > a.Skv) || (a.causal && kb0 + TK - 1 > geo.q0 + a.off) ||
+                        ((uint64_t)live & wbits) != wbits;
+      if (need) {
+        const uint32_t lbits = live >> qsub;
+        int64_t lim = a.Skv - kb0;  // keys allowed from the tile start
+        if (a.causal) lim = min(lim, qpos + a.off + 1 - kb0);
+        const int klim = (int)max<int64_t>(-1, min<int64_t>(lim, TK));
+#pragma unroll
+        for (int t = 0; t < C::NKB; ++t)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int kl = 32 * t + acc_key<true>(j, hh);
+            if (!(kl < klim && ((lbits >> (kl >> hm.lk)) & 1u))) s[t][j] = -INFINITY;
+          }
+      }
+
+      // ---- online softmax, log2 domain, lazy rescale ----
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < C::NKB; ++t)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[t][j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float cand = mx * a.scale_log2;
+      if (__any(cand > m_ref + kRescaleThreshold)) {
+        const float m_new = fmaxf(m_ref, cand);
+        const float alpha = m_new == -INFINITY ? 1.f : fexp2(m_ref - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int u = 0; u < C::NDB; ++u) o[u] *= alpha;
+        m_ref = m_new;
+      }
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+      float psum = 0.f;
+      bf16x8 pb[C::NKB * 2];
+#pragma unroll
+      for (int t = 0; t < C::NKB; ++t)
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          float p[8];
+#pragma unroll
+          for (int e8 = 0; e8 < 8; ++e8) {
+            p[e8] = fexp2(__builtin_fmaf(s[t][8 * c2 + e8], a.scale_log2, -m_use));
+            psum += p[e8];
+          }
+          uint4 w;
+          w.x = pack_bf16x2(p[0], p[1]);
+          w.y = pack_bf16x2(p[2], p[3]);
+          w.z = pack_bf16x2(p[4], p[5]);
+          w.w = pack_bf16x2(p[6], p[7]);
+          pb[2 * t + c2] = __builtin_bit_cast(bf16x8, w);
+        }
+      l_run += psum;
+
+      // ---- O^T += V^T P^T (V^T fragments by transpose reads) ----
+#pragma unroll
+      for (int u = 0; u < C::NDB; ++u) {
+        const int col = 32 * u + 16 * vdsub + 4 * (vj & 3);
+        const int chunk = col >> 3;
+#pragma unroll
+        for (int c2 = 0; c2 < TK / 16; ++c2) {
+          const int ra = 16 * c2 + vrow0, rb = ra + 4;
+          const uint8_t *pa = vs + ra * C::ROWB + ((chunk ^ C::swz_v(ra)) << 4) + vbyte;
+          const uint8_t *pbp = vs + rb * C::ROWB + ((chunk ^ C::swz_v(rb)) << 4) + vbyte;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)pa);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)pbp);
+          const s16x4 both[2] = {lo, hi};
+          const bf16x8 af = __builtin_bit_cast(bf16x8, both);
+          o[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[c2], o[u], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();  // the next item's first loads reuse stage 0
+
+    // ---- finalize ----
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+    if (slot < 0) {
+      if (qvalid) {
+        uint16_t *op = (uint16_t *)a.o + geo.b * a.o_sb + geo.head * a.o_sh + qpos * a.o_ss;
+#pragma unroll
+        for (int u = 0; u < C::NDB; ++u)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int d0 = 32 * u + 8 * q4 + 4 * hh;
+            *(uint2 *)(op + d0) = make_uint2(pack_bf16x2(o[u][4 * q4] * inv, o[u][4 * q4 + 1] * inv),
+                                             pack_bf16x2(o[u][4 * q4 + 2] * inv, o[u][4 * q4 + 3] * inv));
+          }
+        if (hh == 0) a.lse[((int64_t)geo.b * a.Hq + geo.head) * a.Sq + qpos] = lse;
+      }
+    } else {
+      const int64_t prow = (int64_t)slot * kTileQ + 32 * wave + n;
+      float *pp = a.part_o + prow * D;
+#pragma unroll
+      for (int u = 0; u < C::NDB; ++u)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = 32 * u + 8 * q4 + 4 * hh;
+          *(float4 *)(pp + d0) = make_float4(o[u][4 * q4] * inv, o[u][4 * q4 + 1] * inv,
+                                             o[u][4 * q4 + 2] * inv, o[u][4 * q4 + 3] * inv);
+        }
+      if (hh == 0) a.part_lse[prow] = lse;
+    }
+  }
+}
+
 // Split-KV combine: O = sum_s w_s O_s / sum_s w_s with w_s = exp(lse_s - M),
 // LSE = M + ln sum_s w_s, M = max_s lse_s. A record covers one 128-row tile.
 template <int D, bool BF>
@@ -454,16 +703,17 @@ __global__ __launch_bounds__(kThreads) void k_combine(AttnArgs a, const int32_t 
 template <int D, int TK, bool BF>
 bsa_status launch_one(const Plan &p, const AttnArgs &a, hipStream_t s) {
   static int grid = 0;
+  auto kern = BF ? (void (*)(AttnArgs))k_attn_bf16<D, TK> : (void (*)(AttnArgs))k_attn<D, 64, false>;
   if (grid == 0) {
     int dev = 0, cus = 0, occ = 0;
     HIP_TRY(hipGetDevice(&dev));
     HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
-    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_attn<D, TK, BF>, kThreads, 0));
+    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, 0));
     grid = cus * (occ > 0 ? occ : 1);
   }
   int g = grid;
   if (p.item_cap < g) g = (int)std::max<int64_t>(p.item_cap, 1);
-  hipLaunchKernelGGL((k_attn<D, TK, BF>), dim3(g), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(kern, dim3(g), dim3(kThreads), 0, s, a);
   if (p.rg.split > 0 && p.comb_cap > 0) {
     const int cg = (int)std::min<int64_t>(p.comb_cap, 2048);
     hipLaunchKernelGGL((k_combine<D, BF>), dim3(cg), dim3(kThreads), 0, s, a, p.comb);
