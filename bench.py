@@ -31,6 +31,7 @@ def workload(name: str):
     from block_sparse_attention_08_amd import workloads as W
     table = {
         "video_dit": lambda: W.video_dit(),
+        "video_dit_window": lambda: W.video_dit(p_global=0.0),
         "chunked_prefill": lambda: W.chunked_prefill(),
         "affine_bs64": lambda: W.affine(bs=64),
         "affine_bs32": lambda: W.affine(bs=32),

@@ -15,7 +15,8 @@ import os
 from typing import Optional
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libbsa.so")
+# BSA_LIBRARY selects another build of the library (for example a profiling build).
+LIB_PATH = os.environ.get("BSA_LIBRARY") or os.path.join(PKG_DIR, "libbsa.so")
 DEFAULT_LUT = os.path.join(PKG_DIR, "lut", "gfx950.lut")
 
 BSA_OK = 0

@@ -31,6 +31,7 @@
 #include "bsa_internal.h"
 
 #include <algorithm>
+#include <cstdlib>
 #include <type_traits>
 
 namespace bsa {
@@ -66,9 +67,13 @@ __device__ __forceinline__ int acc_key(int j, int hh) {
   else return 2 * j + hh;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Geometry of the wave's 32 query rows for row r of the plan.
@@ -421,13 +426,17 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int D, int TK>
+// A workgroup owns a 128-row query tile split into four 32-row slices; each
+// wave owns NS slices (NS = 1: four waves; NS = 2: two waves, so every K and
+// V^T fragment read from LDS feeds two MFMAs).
+template <int D, int TK, int NS>
 struct CfgB {
-  static constexpr int ROWB = D * 2;                  // bytes per K/V row in LDS
-  static constexpr int CPR = D / 8;                   // 16-byte chunks per row
-  static constexpr int TILEB = TK * ROWB;             // bytes of one K (or V) tile
-  static constexpr int STAGEB = 2 * TILEB;            // K + V
-  static constexpr int LOADS = TILEB / (kThreads * 16);  // 16-byte loads per thread per tile
+  static constexpr int WAVES = 4 / NS;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int ROWB = D * 2;                     // bytes per K/V row in LDS
+  static constexpr int CPR = D / 8;                      // 16-byte chunks per row
+  static constexpr int TILEB = TK * ROWB;                // bytes of one K (or V) tile
+  static constexpr int LOADS = TILEB / (THREADS * 16);   // 16-byte loads per thread per tile
   static constexpr int NKB = TK / 32;
   static constexpr int NDB = D / 32;
   // K rows: 16-byte chunk c of row r sits at chunk c ^ swz_k(r); V rows: c ^ swz_v(r).
@@ -437,10 +446,27 @@ struct CfgB {
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: P values stay below 2^8
 
-template <int D, int TK>
-__global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(AttnArgs a) {
-  using C = CfgB<D, TK>;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::STAGEB];
+// Values that are the same on every lane (they derive from the work item and
+// the entry index only), moved to scalar registers so buffer descriptors and
+// LDS bases built from them stay scalar.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+template <typename T>
+__device__ __forceinline__ const T *uniform(const T *p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const T *)(((uint64_t)hi << 32) | lo);
+}
+
+template <int D, int TK, int NS>
+__global__ __launch_bounds__(64 * (4 / NS), (NS == 2 || TK == 128) ? 1 : 2) void k_attn_bf16(AttnArgs a) {
+  using C = CfgB<D, TK, NS>;
+  // Two K tiles and two V tiles. K runs one tile ahead of V: while the softmax
+  // of tile j runs, the S^T MFMAs of tile j+1 are already issued, and the
+  // loads of K tile j+2 and V tile j+1 are in flight.
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * C::TILEB];
+  auto kbuf = [&](int i) { return lds + (i & 1) * C::TILEB; };
+  auto vbuf = [&](int i) { return lds + (2 + (i & 1)) * C::TILEB; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -451,208 +477,263 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(AttnArgs a) {
   if ((grid & 7) == 0) lid = (blockIdx.x & 7) * (grid >> 3) + (blockIdx.x >> 3);
   const uint16_t *__restrict__ Q = (const uint16_t *)a.q;
 
-  // Per-lane LDS byte offsets that do not depend on the tile.
-  // K operand row for score block t: 32 t + perm(n); chunk (2 cc + hh).
-  const int krow0 = perm_bf16(n);
-  // V^T operand: lane reads rows 16 c2 + 8 hh + (j >> 2) (+4) at column
-  // 32 u + 16 dsub + 4 (j & 3).
+  // Per-lane LDS offsets that do not depend on the tile.
+  const int krow0 = perm_bf16(n);  // K operand row within a 32-key block
   const int vj = lane & 15, vdsub = (lane >> 4) & 1;
-  const int vrow0 = 8 * hh + (vj >> 2);
+  const int vrow0 = 8 * hh + (vj >> 2);  // V^T operand rows 16 c2 + vrow0 (+4)
   const int vbyte = 8 * (vj & 1);
+  const int nqt = (int)a.nqt;
 
   for (int it = lid; it < nitems; it += grid) {
     const int4 item = ((const int4 *)a.items)[it];
-    const int r = item.x, e0 = item.y, e1 = item.z, slot = item.w;
-    const RowGeo geo = row_geo(a, r, wave);
-    const RowGeo geo0 = row_geo(a, r, 0);
-    const HeadMeta hm = a.hm[geo.head];
-    const int64_t qpos = geo.q0 + n;
-    const bool qvalid = qpos < a.Sq;
-
-    bf16x8 qb[D / 16];
-    {
-      const uint16_t *qp = Q + geo.b * a.q_sb + geo.head * a.q_sh + (qvalid ? qpos : 0) * a.q_ss;
+    const int r = item.x, e0 = item.y, nent = item.z - item.y, slot = item.w;
+    // Row geometry (32-bit: rows, heads and tiles are all below 2^31).
+    const int nh = a.pack ? a.Hkv : a.Hq;
+    const int qt = r % nqt, hrow = (r / nqt) % nh, b = r / (nqt * nh);
+    const int g = (a.pack ? hrow * a.G : hrow) / a.G;
+    int head[NS], qbase[NS];
+    int64_t q0[NS], qpos[NS];
+    bool qvalid[NS];
+    HeadMeta hm[NS];
+    bf16x8 qb[NS][D / 16];
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) {
+      const int sl = wave * NS + ns;  // 32-row slice of the tile
+      head[ns] = a.pack ? hrow * a.G + (32 * sl) / a.tr : hrow;
+      qbase[ns] = a.pack ? 0 : 32 * sl;
+      q0[ns] = a.pack ? (int64_t)qt * a.tr + (32 * sl) % a.tr : (int64_t)qt * a.tq + 32 * sl;
+      hm[ns] = a.hm[head[ns]];
+      qpos[ns] = q0[ns] + n;
+      qvalid[ns] = qpos[ns] < a.Sq;
+      const uint16_t *qp = Q + b * a.q_sb + head[ns] * a.q_sh + (qvalid[ns] ? qpos[ns] : 0) * a.q_ss;
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        uint4 x = qvalid ? *(const uint4 *)(qp + 16 * c + 8 * hh) : make_uint4(0, 0, 0, 0);
-        qb[c] = __builtin_bit_cast(bf16x8, x);
+        uint4 x = qvalid[ns] ? *(const uint4 *)(qp + 16 * c + 8 * hh) : make_uint4(0, 0, 0, 0);
+        qb[ns][c] = __builtin_bit_cast(bf16x8, x);
       }
     }
-    const uint16_t *kbase_ptr = (const uint16_t *)a.k + (a.paged ? 0 : geo0.b * a.k_sb) + geo0.g * a.k_sh;
-    const uint16_t *vbase_ptr = (const uint16_t *)a.v + (a.paged ? 0 : geo0.b * a.v_sb) + geo0.g * a.v_sh;
+    const uint16_t *kbase_ptr = (const uint16_t *)a.k + (a.paged ? 0 : b * a.k_sb) + g * a.k_sh;
+    const uint16_t *vbase_ptr = (const uint16_t *)a.v + (a.paged ? 0 : b * a.v_sb) + g * a.v_sh;
 
-    // Issue the buffer loads of tile e into stage st (all 256 threads).
-    auto issue = [&](int e, int st) {
-      const int64_t kt = a.ent_kt[e];
-      const int64_t k0 = kt * TK;
-      const int left = (int)min<int64_t>(a.Skv - k0, TK);  // rows that exist
-      const uint16_t *kb, *vb;
-      if (a.paged) {
-        const int64_t pg = a.ent_page[e];
-        kb = kbase_ptr + pg * a.k_sb + (k0 % a.P) * a.k_ss;
-        vb = vbase_ptr + pg * a.v_sb + (k0 % a.P) * a.v_ss;
-      } else {
-        kb = kbase_ptr + k0 * a.k_ss;
-        vb = vbase_ptr + k0 * a.v_ss;
-      }
-      const int kbytes = (int)((left - 1) * a.k_ss * 2 + D * 2);
-      const int vbytes = (int)((left - 1) * a.v_ss * 2 + D * 2);
-      const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void *)kb, 0, kbytes, 0x00020000);
-      const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void *)vb, 0, vbytes, 0x00020000);
-      uint8_t *ks = lds + st * C::STAGEB;
+    // Buffer loads of one K or V tile of entry e into dst (every thread).
+    auto issue = [&](const uint16_t *base, int64_t sb, int64_t ss, int e, uint8_t *dst_tile, bool is_v) {
+      const int kt = a.ent_kt[e];
+      const int k0 = kt * TK;
+      const int left = (int)min<int64_t>(a.Skv - k0, TK);  // rows of the tile that exist
+      const uint16_t *tb = a.paged ? base + (int64_t)a.ent_page[e] * sb + (int64_t)(k0 % a.P) * ss
+                                   : base + (int64_t)k0 * ss;
+      tb = uniform(tb);
+      const int bytes = uniform((int)((left - 1) * ss * 2 + D * 2));
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)tb, 0, bytes, 0x00020000);
 #pragma unroll
       for (int u = 0; u < C::LOADS; ++u) {
-        const int L = u * kThreads + tid;             // 16-byte LDS slot, lane-linear per wave
+        const int L = u * C::THREADS + tid;  // 16-byte LDS slot, lane-linear per wave
         const int row = L / C::CPR, pos = L % C::CPR;
-        const int koff = row * (int)a.k_ss * 2 + ((pos ^ C::swz_k(row)) << 4);
-        const int voff = row * (int)a.v_ss * 2 + ((pos ^ C::swz_v(row)) << 4);
-        uint8_t *dst = ks + (u * kThreads + wave * 64) * 16;
+        const int sw = is_v ? C::swz_v(row) : C::swz_k(row);
+        const int off = row * (int)ss * 2 + ((pos ^ sw) << 4);
+        uint8_t *dst = dst_tile + (u * C::THREADS + wave * 64) * 16;
         // Rows past the sequence end fall outside the buffer range and read 0.
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void *)dst, 16, row < left ? koff : kbytes, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void *)(dst + C::TILEB), 16, row < left ? voff : vbytes, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, row < left ? off : bytes, 0, 0, 0);
       }
     };
+    auto issue_k = [&](int e, int j) { issue(kbase_ptr, a.k_sb, a.k_ss, e, kbuf(j), false); };
+    auto issue_v = [&](int e, int j) { issue(vbase_ptr, a.v_sb, a.v_ss, e, vbuf(j), true); };
+    auto kfrag = [&](const uint8_t *ks, int i) {
+      const int row = 32 * (i / (D / 16)) + krow0;
+      const int c = 2 * (i % (D / 16)) + hh;
+      return *(const bf16x8 *)(ks + row * C::ROWB + ((c ^ C::swz_k(row)) << 4));
+    };
 
-    f32x16 o[C::NDB];
+    f32x16 o[NS][C::NDB];
+    float m_ref[NS], l_run[NS];
+    uint64_t wbits[NS];
+    int qsub[NS];
 #pragma unroll
-    for (int u = 0; u < C::NDB; ++u) o[u] = f32x16{};
-    float m_ref = -INFINITY, l_run = 0.f;
-
-    const int iq_lo = geo.qbase >> hm.lq;
-    const int niq = hm.lq >= 5 ? 1 : (32 >> hm.lq);
-    const uint64_t wbits = ((1ull << (hm.mk * niq)) - 1ull) << (iq_lo * hm.mk);
-    const int qsub = ((geo.qbase + n) >> hm.lq) * hm.mk;
-
-    if (e0 < e1) issue(e0, 0);
-    for (int e = e0; e < e1; ++e) {
-      const int st = (e - e0) & 1;
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's tile loads have landed
-      __syncthreads();                // ... and every wave's; stage st^1 is free
-      if (e + 1 < e1) issue(e + 1, st ^ 1);
-      const uint8_t *ks = lds + st * C::STAGEB;
-      const uint8_t *vs = ks + C::TILEB;
-
-      // ---- S^T = K Q^T ----
-      f32x16 s[C::NKB];
+    for (int ns = 0; ns < NS; ++ns) {
 #pragma unroll
-      for (int t = 0; t < C::NKB; ++t) {
-        s[t] = f32x16{};
-        const int row = 32 * t + krow0;
-        const uint8_t *kr = ks + row * C::ROWB;
-        const int sw = C::swz_k(row);
+      for (int u = 0; u < C::NDB; ++u) o[ns][u] = f32x16{};
+      m_ref[ns] = -INFINITY, l_run[ns] = 0.f;
+      const int iq_lo = qbase[ns] >> hm[ns].lq;
+      const int niq = hm[ns].lq >= 5 ? 1 : (32 >> hm[ns].lq);
+      wbits[ns] = ((1ull << (hm[ns].mk * niq)) - 1ull) << (iq_lo * hm[ns].mk);
+      qsub[ns] = ((qbase[ns] + n) >> hm[ns].lq) * hm[ns].mk;
+    }
+
+    constexpr int STEPS = C::NKB * D / 16;     // K fragments per tile
+    constexpr int EPS = C::NKB * 16 / STEPS;   // scores per slice exponentiated per step (2 or 4)
+    f32x16 s_cur[NS][C::NKB];
+    if (nent > 0) {
+      issue_k(e0, 0);
+      issue_v(e0, 0);
+      if (nent > 1) issue_k(e0 + 1, 1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      const uint8_t *ks = kbuf(0);
 #pragma unroll
-        for (int cc = 0; cc < D / 16; ++cc) {
-          const bf16x8 af = *(const bf16x8 *)(kr + (((2 * cc + hh) ^ sw) << 4));
-          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qb[cc], s[t], 0, 0, 0);
-        }
+      for (int i = 0; i < STEPS; ++i) {
+        const bf16x8 kf = kfrag(ks, i);
+        const int t = i / (D / 16), cc = i % (D / 16);
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns)
+          s_cur[ns][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qb[ns][cc], cc == 0 ? f32x16{} : s_cur[ns][t], 0, 0, 0);
       }
+    }
+    for (int j = 0; j < nent; ++j) {
+      const int e = e0 + j;
+      __builtin_amdgcn_s_waitcnt(0);  // K tile j+1 and V tile j have landed (this wave)
+      __syncthreads();                // ... for every wave; K tile j and V tile j-1 are free
+      if (j + 2 < nent) issue_k(e + 2, j);
+      if (j + 1 < nent) issue_v(e + 1, j + 1);
 
-      // ---- mask (tiles at a sequence end, the causal diagonal or a dead sub-block) ----
+      // ---- mask tile j (sequence end, causal diagonal, dead sub-blocks) ----
       const int64_t kb0 = (int64_t)a.ent_kt[e] * TK;
       const uint32_t live = a.ent_live[e];
-      const bool need = (kb0 + TK > a.Skv) || (a.causal && kb0 + TK - 1 > geo.q0 + a.off) ||
-                        ((uint64_t)live & wbits) != wbits;
-      if (need) {
-        const uint32_t lbits = live >> qsub;
-        int64_t lim = a.Skv - kb0;  // keys allowed from the tile start
-        if (a.causal) lim = min(lim, qpos + a.off + 1 - kb0);
-        const int klim = (int)max<int64_t>(-1, min<int64_t>(lim, TK));
+      float m_use[NS];
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) {
+        const bool need = (kb0 + TK > a.Skv) || (a.causal && kb0 + TK - 1 > q0[ns] + a.off) ||
+                          ((uint64_t)live & wbits[ns]) != wbits[ns];
+        if (need) {
+          const uint32_t lbits = live >> qsub[ns];
+          int64_t lim = a.Skv - kb0;  // keys allowed from the tile start
+          if (a.causal) lim = min(lim, qpos[ns] + a.off + 1 - kb0);
+          const int klim = (int)max<int64_t>(-1, min<int64_t>(lim, TK));
+#pragma unroll
+          for (int t = 0; t < C::NKB; ++t)
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) {
+              const int kl = 32 * t + acc_key<true>(jj, hh);
+              if (!(kl < klim && ((lbits >> (kl >> hm[ns].lk)) & 1u))) s_cur[ns][t][jj] = -INFINITY;
+            }
+        }
+        // ---- online softmax of tile j, log2 domain, lazy rescale ----
+        float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < C::NKB; ++t)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int kl = 32 * t + acc_key<true>(j, hh);
-            if (!(kl < klim && ((lbits >> (kl >> hm.lk)) & 1u))) s[t][j] = -INFINITY;
-          }
-      }
-
-      // ---- online softmax, log2 domain, lazy rescale ----
-      float mx = -INFINITY;
+          for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s_cur[ns][t][jj]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float cand = mx * a.scale_log2;
+        if (__any(cand > m_ref[ns] + kRescaleThreshold)) {
+          const float m_new = fmaxf(m_ref[ns], cand);
+          const float alpha = m_new == -INFINITY ? 1.f : fexp2(m_ref[ns] - m_new);
+          l_run[ns] *= alpha;
 #pragma unroll
-      for (int t = 0; t < C::NKB; ++t)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[t][j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float cand = mx * a.scale_log2;
-      if (__any(cand > m_ref + kRescaleThreshold)) {
-        const float m_new = fmaxf(m_ref, cand);
-        const float alpha = m_new == -INFINITY ? 1.f : fexp2(m_ref - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int u = 0; u < C::NDB; ++u) o[u] *= alpha;
-        m_ref = m_new;
-      }
-      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-      float psum = 0.f;
-      bf16x8 pb[C::NKB * 2];
-#pragma unroll
-      for (int t = 0; t < C::NKB; ++t)
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          float p[8];
-#pragma unroll
-          for (int e8 = 0; e8 < 8; ++e8) {
-            p[e8] = fexp2(__builtin_fmaf(s[t][8 * c2 + e8], a.scale_log2, -m_use));
-            psum += p[e8];
-          }
-          uint4 w;
-          w.x = pack_bf16x2(p[0], p[1]);
-          w.y = pack_bf16x2(p[2], p[3]);
-          w.z = pack_bf16x2(p[4], p[5]);
-          w.w = pack_bf16x2(p[6], p[7]);
-          pb[2 * t + c2] = __builtin_bit_cast(bf16x8, w);
+          for (int u = 0; u < C::NDB; ++u) o[ns][u] *= alpha;
+          m_ref[ns] = m_new;
         }
-      l_run += psum;
+        m_use[ns] = m_ref[ns] == -INFINITY ? 0.f : m_ref[ns];
+      }
 
-      // ---- O^T += V^T P^T (V^T fragments by transpose reads) ----
+      // One straight-line block, in a fixed order: each K fragment of tile
+      // j+1 feeds NS S^T MFMAs (independent work), followed by the
+      // exponentials of a slice of tile j; the fragment read runs three steps
+      // ahead. Then each V^T fragment feeds NS P V^T MFMAs. sched_barrier(0)
+      // keeps the compiler from regrouping the steps. On the last tile the
+      // S^T of a stale buffer is computed and dropped.
+      f32x16 s_next[NS][C::NKB];
+      uint32_t pw[NS][C::NKB * 8];  // P as packed bf16 pairs
+      float psum[NS];
 #pragma unroll
-      for (int u = 0; u < C::NDB; ++u) {
-        const int col = 32 * u + 16 * vdsub + 4 * (vj & 3);
-        const int chunk = col >> 3;
+      for (int ns = 0; ns < NS; ++ns) psum[ns] = 0.f;
+      {
+        const uint8_t *ks = kbuf(j + 1);
+        bf16x8 kf[STEPS];
 #pragma unroll
-        for (int c2 = 0; c2 < TK / 16; ++c2) {
+        for (int i = 0; i < 3 && i < STEPS; ++i) kf[i] = kfrag(ks, i);
+#pragma unroll
+        for (int i = 0; i < STEPS; ++i) {
+          if (i + 3 < STEPS) kf[i + 3] = kfrag(ks, i + 3);
+          const int t = i / (D / 16), cc = i % (D / 16);
+#pragma unroll
+          for (int ns = 0; ns < NS; ++ns)
+            s_next[ns][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qb[ns][cc], cc == 0 ? f32x16{} : s_next[ns][t], 0, 0, 0);
+#pragma unroll
+          for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+            for (int k2 = 0; k2 < EPS; k2 += 2) {
+              const int x = i * EPS + k2;
+              const float p0 = fexp2(__builtin_fmaf(s_cur[ns][x / 16][x % 16], a.scale_log2, -m_use[ns]));
+              const float p1 = fexp2(__builtin_fmaf(s_cur[ns][x / 16][x % 16 + 1], a.scale_log2, -m_use[ns]));
+              psum[ns] += p0;
+              psum[ns] += p1;
+              pw[ns][x / 2] = pack_bf16x2(p0, p1);
+            }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) l_run[ns] += psum[ns];
+
+      // ---- O^T += V^T P^T, V^T fragments by transpose reads of V tile j ----
+      {
+        const uint8_t *vs = vbuf(j);
+        constexpr int PV = (TK / 16) * C::NDB;
+        auto vfrag = [&](int i) {
+          const int c2 = i / C::NDB, u = i % C::NDB;
           const int ra = 16 * c2 + vrow0, rb = ra + 4;
+          const int chunk = (32 * u + 16 * vdsub + 4 * (vj & 3)) >> 3;
           const uint8_t *pa = vs + ra * C::ROWB + ((chunk ^ C::swz_v(ra)) << 4) + vbyte;
           const uint8_t *pbp = vs + rb * C::ROWB + ((chunk ^ C::swz_v(rb)) << 4) + vbyte;
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)pa);
           const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)pbp);
           const s16x4 both[2] = {lo, hi};
-          const bf16x8 af = __builtin_bit_cast(bf16x8, both);
-          o[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pb[c2], o[u], 0, 0, 0);
+          return __builtin_bit_cast(bf16x8, both);
+        };
+        bf16x8 vf[PV];
+        vf[0] = vfrag(0);
+        vf[1] = vfrag(1);
+#pragma unroll
+        for (int i = 0; i < PV; ++i) {
+          if (i + 2 < PV) vf[i + 2] = vfrag(i + 2);
+          const int c2 = i / C::NDB, u = i % C::NDB;
+#pragma unroll
+          for (int ns = 0; ns < NS; ++ns) {
+            const uint4 w = make_uint4(pw[ns][4 * c2], pw[ns][4 * c2 + 1], pw[ns][4 * c2 + 2], pw[ns][4 * c2 + 3]);
+            o[ns][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], __builtin_bit_cast(bf16x8, w), o[ns][u], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+        for (int t = 0; t < C::NKB; ++t) s_cur[ns][t] = s_next[ns][t];
     }
-    __syncthreads();  // the next item's first loads reuse stage 0
+    __syncthreads();  // the next item's first loads reuse the buffers
 
     // ---- finalize ----
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const float lse = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
-    if (slot < 0) {
-      if (qvalid) {
-        uint16_t *op = (uint16_t *)a.o + geo.b * a.o_sb + geo.head * a.o_sh + qpos * a.o_ss;
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) {
+      const float l_tot = l_run[ns] + __shfl_xor(l_run[ns], 32);
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const float lse = l_tot > 0.f ? (m_ref[ns] + log2f(l_tot)) * kLn2 : -INFINITY;
+      if (slot < 0) {
+        if (qvalid[ns]) {
+          uint16_t *op = (uint16_t *)a.o + b * a.o_sb + head[ns] * a.o_sh + qpos[ns] * a.o_ss;
+#pragma unroll
+          for (int u = 0; u < C::NDB; ++u)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const int d0 = 32 * u + 8 * q4 + 4 * hh;
+              *(uint2 *)(op + d0) = make_uint2(pack_bf16x2(o[ns][u][4 * q4] * inv, o[ns][u][4 * q4 + 1] * inv),
+                                               pack_bf16x2(o[ns][u][4 * q4 + 2] * inv, o[ns][u][4 * q4 + 3] * inv));
+            }
+          if (hh == 0) a.lse[((int64_t)b * a.Hq + head[ns]) * a.Sq + qpos[ns]] = lse;
+        }
+      } else {
+        const int64_t prow = (int64_t)slot * kTileQ + 32 * (wave * NS + ns) + n;
+        float *pp = a.part_o + prow * D;
 #pragma unroll
         for (int u = 0; u < C::NDB; ++u)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
             const int d0 = 32 * u + 8 * q4 + 4 * hh;
-            *(uint2 *)(op + d0) = make_uint2(pack_bf16x2(o[u][4 * q4] * inv, o[u][4 * q4 + 1] * inv),
-                                             pack_bf16x2(o[u][4 * q4 + 2] * inv, o[u][4 * q4 + 3] * inv));
+            *(float4 *)(pp + d0) = make_float4(o[ns][u][4 * q4] * inv, o[ns][u][4 * q4 + 1] * inv,
+                                               o[ns][u][4 * q4 + 2] * inv, o[ns][u][4 * q4 + 3] * inv);
           }
-        if (hh == 0) a.lse[((int64_t)geo.b * a.Hq + geo.head) * a.Sq + qpos] = lse;
+        if (hh == 0) a.part_lse[prow] = lse;
       }
-    } else {
-      const int64_t prow = (int64_t)slot * kTileQ + 32 * wave + n;
-      float *pp = a.part_o + prow * D;
-#pragma unroll
-      for (int u = 0; u < C::NDB; ++u)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d0 = 32 * u + 8 * q4 + 4 * hh;
-          *(float4 *)(pp + d0) = make_float4(o[u][4 * q4] * inv, o[u][4 * q4 + 1] * inv,
-                                             o[u][4 * q4 + 2] * inv, o[u][4 * q4 + 3] * inv);
-        }
-      if (hh == 0) a.part_lse[prow] = lse;
     }
   }
 }
@@ -700,20 +781,35 @@ __global__ __launch_bounds__(kThreads) void k_combine(AttnArgs a, const int32_t 
   }
 }
 
-template <int D, int TK, bool BF>
+// Slices per wave of the bf16 kernel: 1 (four waves per workgroup, two
+// workgroups per CU). With 2, two waves each own two slices so every K/V
+// fragment feeds two MFMAs, but only one wave runs per SIMD and nothing hides
+// LDS and MFMA latency: measured 2-3x slower, kept for measurements only
+// (BSA_SLICES_PER_WAVE=2).
+static int slices_per_wave(int D) {
+  static int v = -1;
+  if (v < 0) {
+    const char *e = std::getenv("BSA_SLICES_PER_WAVE");
+    v = (e && (e[0] == '1' || e[0] == '2')) ? e[0] - '0' : 0;
+  }
+  return v ? v : 1;
+}
+
+template <int D, int TK, bool BF, int NS>
 bsa_status launch_one(const Plan &p, const AttnArgs &a, hipStream_t s) {
   static int grid = 0;
-  auto kern = BF ? (void (*)(AttnArgs))k_attn_bf16<D, TK> : (void (*)(AttnArgs))k_attn<D, 64, false>;
+  const int threads = BF ? 64 * (4 / NS) : kThreads;
+  auto kern = BF ? (void (*)(AttnArgs))k_attn_bf16<D, TK, NS> : (void (*)(AttnArgs))k_attn<D, 64, false>;
   if (grid == 0) {
     int dev = 0, cus = 0, occ = 0;
     HIP_TRY(hipGetDevice(&dev));
     HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
-    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, 0));
+    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, threads, 0));
     grid = cus * (occ > 0 ? occ : 1);
   }
   int g = grid;
   if (p.item_cap < g) g = (int)std::max<int64_t>(p.item_cap, 1);
-  hipLaunchKernelGGL(kern, dim3(g), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(kern, dim3(g), dim3(threads), 0, s, a);
   if (p.rg.split > 0 && p.comb_cap > 0) {
     const int cg = (int)std::min<int64_t>(p.comb_cap, 2048);
     hipLaunchKernelGGL((k_combine<D, BF>), dim3(cg), dim3(kThreads), 0, s, a, p.comb);
@@ -727,12 +823,15 @@ bsa_status launch_one(const Plan &p, const AttnArgs &a, hipStream_t s) {
 bsa_status attention_launch(const Plan &p, const AttnArgs &a, hipStream_t s) {
   const bool bf = p.dtype == BSA_BF16;
   // fp32 tiles use 64 keys (the planner guarantees it): 128 would not fit LDS twice.
-  if (bf && p.D == 128 && p.rg.tk == 64) return launch_one<128, 64, true>(p, a, s);
-  if (bf && p.D == 128 && p.rg.tk == 128) return launch_one<128, 128, true>(p, a, s);
-  if (bf && p.D == 64 && p.rg.tk == 64) return launch_one<64, 64, true>(p, a, s);
-  if (bf && p.D == 64 && p.rg.tk == 128) return launch_one<64, 128, true>(p, a, s);
-  if (!bf && p.D == 128 && p.rg.tk == 64) return launch_one<128, 64, false>(p, a, s);
-  if (!bf && p.D == 64 && p.rg.tk == 64) return launch_one<64, 64, false>(p, a, s);
+  const bool two = slices_per_wave(p.D) == 2;
+  if (bf && p.D == 128 && p.rg.tk == 64)
+    return two ? launch_one<128, 64, true, 2>(p, a, s) : launch_one<128, 64, true, 1>(p, a, s);
+  if (bf && p.D == 64 && p.rg.tk == 64)
+    return two ? launch_one<64, 64, true, 2>(p, a, s) : launch_one<64, 64, true, 1>(p, a, s);
+  if (bf && p.D == 128 && p.rg.tk == 128) return launch_one<128, 128, true, 1>(p, a, s);
+  if (bf && p.D == 64 && p.rg.tk == 128) return launch_one<64, 128, true, 1>(p, a, s);
+  if (!bf && p.D == 128 && p.rg.tk == 64) return launch_one<128, 64, false, 1>(p, a, s);
+  if (!bf && p.D == 64 && p.rg.tk == 64) return launch_one<64, 64, false, 1>(p, a, s);
   return fail(BSA_ERR_UNSUPPORTED, "no kernel for this head_dim / tile_k");
 }
 
