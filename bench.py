@@ -89,7 +89,7 @@ def allowed_keys_per_row(w, b: int, h: int) -> np.ndarray:
     return out
 
 
-def cpu_baseline(w, q, k, v, target_s: float = 12.0):
+def cpu_baseline(w, q, k, v, target_s: float = 20.0):
     """The fp64 oracle timed on this host's cores over a bounded sample of
     query rows (whole 128-row tiles, spread over heads), in TFLOP/s of
     selected work."""

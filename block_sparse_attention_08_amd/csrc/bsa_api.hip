@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstring>
 #include <fstream>
+#include <mutex>
 #include <sstream>
 
 #include "bsa_internal.h"
@@ -106,9 +107,9 @@ static bsa_status parse_lut(const char *text, bsa_lut_s *lut) {
       else if (f == 2 && t == "lpt") v[f] = 1;
       else if (f == 2 || !parse_i64(t, &v[f])) return fail(BSA_ERR_LUT, "bad regime value '" + t + "'");
     }
-    if (v[0] != 128 || (v[1] != 64 && v[1] != 128) || v[3] < 0 || v[3] > (1 << 30) ||
-        (v[4] != 0 && v[4] != 1))
-      return fail(BSA_ERR_LUT, "regime out of range (Tq 128, Tk 64|128, split >= 0, pack 0|1)");
+    if ((v[0] != 128 && v[0] != 256) || (v[1] != 64 && v[1] != 128) || v[3] < 0 ||
+        v[3] > (1 << 30) || (v[4] != 0 && v[4] != 1))
+      return fail(BSA_ERR_LUT, "regime out of range (Tq 128|256, Tk 64|128, split >= 0, pack 0|1)");
     r.r = Regime{(int)v[0], (int)v[1], (int)v[2], (int)v[3], (int)v[4]};
     lut->rules.push_back(r);
   }
@@ -160,10 +161,61 @@ static bsa_status check_problem(const bsa_problem *p, const uint8_t *mask, const
   return BSA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Cache of freed plan allocations. A block is reused for a request of at
+// most its size and at least half of it; at most kCacheBlocks blocks and
+// kCacheBytes bytes are kept per device; anything else goes back to hipFree.
+// ---------------------------------------------------------------------------
+namespace {
+struct CachedBlock {
+  void *ptr;
+  size_t bytes;
+  int device;
+};
+constexpr int kCacheBlocks = 16;
+constexpr size_t kCacheBytes = size_t(8) << 30;
+std::mutex g_cache_mu;
+std::vector<CachedBlock> g_cache;
+}  // namespace
+
+hipError_t cached_alloc(void **ptr, size_t bytes, int device) {
+  {
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    int best = -1;
+    for (int i = 0; i < (int)g_cache.size(); ++i) {
+      const CachedBlock &c = g_cache[i];
+      if (c.device == device && c.bytes >= bytes && c.bytes <= 2 * bytes + (1 << 20) &&
+          (best < 0 || c.bytes < g_cache[best].bytes))
+        best = i;
+    }
+    if (best >= 0) {
+      *ptr = g_cache[best].ptr;
+      g_cache.erase(g_cache.begin() + best);
+      return hipSuccess;
+    }
+  }
+  return hipMalloc(ptr, bytes);
+}
+
+void cached_free(void *ptr, size_t bytes, int device) {
+  if (!ptr) return;
+  {
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    size_t held = 0, count = 0;
+    for (const CachedBlock &c : g_cache)
+      if (c.device == device) held += c.bytes, ++count;
+    if (count < kCacheBlocks && held + bytes <= kCacheBytes) {
+      g_cache.push_back(CachedBlock{ptr, bytes, device});
+      return;
+    }
+  }
+  (void)hipFree(ptr);
+}
+
 static void free_plan(bsa_plan_s *p) {
   if (!p) return;
-  if (p->pre) (void)hipFree(p->pre);
-  if (p->arena) (void)hipFree(p->arena);
+  cached_free(p->pre, p->pre_bytes, p->device);
+  cached_free(p->arena, p->arena_bytes, p->device);
   delete p;
 }
 
@@ -186,12 +238,14 @@ static bsa_status choose_regime(Plan &p, const bsa_lut_s *lut) {
     }
   }
   if (!(p.uni && (p.G == 2 || p.G == 4))) rg.pack = 0;
-  if (p.dtype == BSA_F32) rg.tk = 64;
+  if (p.dtype == BSA_F32) rg.tq = 128, rg.tk = 64;  // fp32 tiles are 128 x 64
+  if (rg.tq == 256) rg.tk = 64;                      // 256-row tiles use 64 keys
   if (p.paged && p.P % rg.tk) {
     if (rg.tk == 128 && p.P % 64 == 0) rg.tk = 64;
     else return fail(BSA_ERR_UNSUPPORTED, "page_size not a multiple of the key tile");
   }
-  for (int pass = 0; pass < 2; ++pass) {
+  // At most 32 live bits per tile: shrink Tk to 64, then Tq to 128.
+  for (;;) {
     bool bad = false;
     for (int h = 0; h < p.Hq; ++h) {
       const int mq = (!p.uni && p.bq[h] < rg.tq) ? rg.tq / p.bq[h] : 1;
@@ -199,11 +253,9 @@ static bsa_status choose_regime(Plan &p, const bsa_lut_s *lut) {
       if (mq * mk > 32) bad = true;
     }
     if (!bad) break;
-    if (pass == 0 && rg.tk == 128) {
-      rg.tk = 64;
-      continue;
-    }
-    return fail(BSA_ERR_UNSUPPORTED, "block sizes too small for the tile (more than 32 sub-blocks)");
+    if (rg.tk == 128) rg.tk = 64;
+    else if (rg.tq == 256) rg.tq = 128;
+    else return fail(BSA_ERR_UNSUPPORTED, "block sizes too small for the tile (more than 32 sub-blocks)");
   }
   p.rg = rg;
   return BSA_OK;
@@ -288,26 +340,32 @@ bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *p
 
   // ---- phase 1: features (one device-to-host read) ----
   const size_t feat_bytes = sizeof(int64_t) * 4 * P.nbm * P.Hq;
-  const size_t pre_bytes = aligned(feat_bytes) + aligned(sizeof(int32_t) * CNT_N) +
+  int64_t rows_per_bm = 0;
+  for (int h = 0; h < P.Hq; ++h) rows_per_bm += cdiv(P.Sq, P.bq[h]);
+  const size_t pre_bytes = aligned(sizeof(int32_t) * CNT_N) + aligned(feat_bytes) +
                            aligned(sizeof(HeadMeta) * P.Hq) +
-                           aligned((size_t)P.nbm * P.Hkv * std::max<int64_t>(P.unkb, 1));
-  if (hipMalloc(&P.pre, pre_bytes) != hipSuccess) {
+                           aligned((size_t)P.nbm * P.Hkv * std::max<int64_t>(P.unkb, 1)) +
+                           aligned(sizeof(int32_t) * 2 * std::max<int64_t>(P.nbm * rows_per_bm, 1));
+  if (cached_alloc(&P.pre, pre_bytes, P.device) != hipSuccess) {
     free_plan(p);
     return fail(BSA_ERR_OUT_OF_MEMORY, "device allocation of plan header failed");
   }
+  P.pre_bytes = pre_bytes;
   uint8_t *pb = (uint8_t *)P.pre;
-  P.feat_dev = (unsigned long long *)pb;
-  pb += aligned(feat_bytes);
   P.counters = (int32_t *)pb;
   pb += aligned(sizeof(int32_t) * CNT_N);
+  P.feat_dev = (unsigned long long *)pb;
+  pb += aligned(feat_bytes);
   P.hmeta = (HeadMeta *)pb;
   pb += aligned(sizeof(HeadMeta) * P.Hq);
   P.uni_bits = pb;
+  pb += aligned((size_t)P.nbm * P.Hkv * std::max<int64_t>(P.unkb, 1));
+  P.row_feat = (int32_t *)pb;
   auto bail = [&](bsa_status s) {
     free_plan(p);
     return s;
   };
-  if (hipMemsetAsync(P.pre, 0, aligned(feat_bytes) + aligned(sizeof(int32_t) * CNT_N), P.stream) != hipSuccess)
+  if (hipMemsetAsync(P.counters, 0, sizeof(int32_t) * CNT_N, P.stream) != hipSuccess)
     return bail(fail(BSA_ERR_HIP, "hipMemsetAsync failed"));
   if (bsa_status s = plan_features(P, mask, page_table)) return bail(s);
   std::vector<int64_t> host(feat_bytes / 8 + CNT_N);
@@ -367,7 +425,7 @@ bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *p
   const int64_t lim = (int64_t(1) << 31) - 2;
   if (P.ent_cap > lim || P.item_cap > lim || P.nrows > lim || P.nlists > lim)
     return bail(fail(BSA_ERR_UNSUPPORTED, "plan too large (more than 2^31 entries or rows)"));
-  const size_t part_bytes = (size_t)P.slot_cap * 128 * (P.D + 1) * sizeof(float);
+  const size_t part_bytes = (size_t)P.slot_cap * tq * (P.D + 1) * sizeof(float);
   if (part_bytes > (size_t(64) << 30))
     return bail(fail(BSA_ERR_UNSUPPORTED, "split threshold too small: partial buffers above 64 GiB"));
 
@@ -380,15 +438,16 @@ bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *p
       {(void **)&P.row_ent, sizeof(int32_t) * 2 * std::max<int64_t>(P.nrows, 1)},
       {(void **)&P.items, sizeof(int32_t) * 4 * std::max<int64_t>(P.item_cap, 1)},
       {(void **)&P.comb, sizeof(int32_t) * 3 * std::max<int64_t>(P.comb_cap, 1)},
-      {(void **)&P.part_o, sizeof(float) * P.slot_cap * 128 * P.D},
-      {(void **)&P.part_lse, sizeof(float) * P.slot_cap * 128},
+      {(void **)&P.part_o, sizeof(float) * P.slot_cap * tq * P.D},
+      {(void **)&P.part_lse, sizeof(float) * P.slot_cap * tq},
   };
   size_t total = 0;
   for (auto &pt : parts) total += aligned(pt.second);
   const size_t scratch = plan_scratch_bytes(P);
   total += scratch;
-  if (hipMalloc(&P.arena, total) != hipSuccess)
+  if (cached_alloc(&P.arena, total, P.device) != hipSuccess)
     return bail(fail(BSA_ERR_OUT_OF_MEMORY, "device allocation of " + std::to_string(total) + " plan bytes failed"));
+  P.arena_bytes = total;
   uint8_t *ap = (uint8_t *)P.arena;
   for (auto &pt : parts) {
     *pt.first = pt.second ? ap : nullptr;

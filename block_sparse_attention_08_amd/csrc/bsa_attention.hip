@@ -426,12 +426,13 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-// A workgroup owns a 128-row query tile split into four 32-row slices; each
-// wave owns NS slices (NS = 1: four waves; NS = 2: two waves, so every K and
-// V^T fragment read from LDS feeds two MFMAs).
-template <int D, int TK, int NS>
+// A workgroup owns a TQ-row query tile (128 or 256) split into 32-row slices;
+// each wave owns NS slices (NS = 2 makes every K and V^T fragment read from
+// LDS feed two MFMAs).
+template <int D, int TK, int TQ, int NS>
 struct CfgB {
-  static constexpr int WAVES = 4 / NS;
+  static constexpr int SLICES = TQ / 32;
+  static constexpr int WAVES = SLICES / NS;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int ROWB = D * 2;                     // bytes per K/V row in LDS
   static constexpr int CPR = D / 8;                      // 16-byte chunks per row
@@ -458,9 +459,9 @@ __device__ __forceinline__ const T *uniform(const T *p) {
   return (const T *)(((uint64_t)hi << 32) | lo);
 }
 
-template <int D, int TK, int NS>
-__global__ __launch_bounds__(64 * (4 / NS), (NS == 2 || TK == 128) ? 1 : 2) void k_attn_bf16(AttnArgs a) {
-  using C = CfgB<D, TK, NS>;
+template <int D, int TK, int TQ, int NS>
+__global__ __launch_bounds__(64 * (TQ / 32 / NS), (NS == 2 || (TK == 128 && TQ == 128)) ? 1 : 2) void k_attn_bf16(AttnArgs a) {
+  using C = CfgB<D, TK, TQ, NS>;
   // Two K tiles and two V tiles. K runs one tile ahead of V: while the softmax
   // of tile j runs, the S^T MFMAs of tile j+1 are already issued, and the
   // loads of K tile j+2 and V tile j+1 are in flight.
@@ -722,7 +723,7 @@ __global__ __launch_bounds__(64 * (4 / NS), (NS == 2 || TK == 128) ? 1 : 2) void
           if (hh == 0) a.lse[((int64_t)b * a.Hq + head[ns]) * a.Sq + qpos[ns]] = lse;
         }
       } else {
-        const int64_t prow = (int64_t)slot * kTileQ + 32 * (wave * NS + ns) + n;
+        const int64_t prow = (int64_t)slot * TQ + 32 * (wave * NS + ns) + n;
         float *pp = a.part_o + prow * D;
 #pragma unroll
         for (int u = 0; u < C::NDB; ++u)
@@ -739,45 +740,47 @@ __global__ __launch_bounds__(64 * (4 / NS), (NS == 2 || TK == 128) ? 1 : 2) void
 }
 
 // Split-KV combine: O = sum_s w_s O_s / sum_s w_s with w_s = exp(lse_s - M),
-// LSE = M + ln sum_s w_s, M = max_s lse_s. A record covers one 128-row tile.
-template <int D, bool BF>
+// LSE = M + ln sum_s w_s, M = max_s lse_s. A record covers one TQ-row tile;
+// two threads per row, each half of the head dimension.
+template <int D, bool BF, int TQ>
 __global__ __launch_bounds__(kThreads) void k_combine(AttnArgs a, const int32_t *__restrict__ comb) {
   using E = typename std::conditional<BF, uint16_t, float>::type;
   const int ncomb = a.counters[CNT_COMB];
-  const int row = threadIdx.x >> 1, half = threadIdx.x & 1;  // 128 rows x 2 threads
-  const int wave = row >> 5, n = row & 31;
   for (int c = blockIdx.x; c < ncomb; c += gridDim.x) {
     const int r = comb[3 * c], s0 = comb[3 * c + 1], k = comb[3 * c + 2];
-    const RowGeo geo = row_geo(a, r, wave);
-    const int64_t qpos = geo.q0 + n;
-    if (qpos >= a.Sq) continue;
-    float M = -INFINITY;
-    for (int s = 0; s < k; ++s) M = fmaxf(M, a.part_lse[(int64_t)(s0 + s) * kTileQ + row]);
-    E *op = (E *)a.o + geo.b * a.o_sb + geo.head * a.o_sh + qpos * a.o_ss;
-    if (M == -INFINITY) {
-      for (int d = half * (D / 2); d < (half + 1) * (D / 2); ++d) op[d] = (E)0;
-      if (half == 0) a.lse[((int64_t)geo.b * a.Hq + geo.head) * a.Sq + qpos] = -INFINITY;
-      continue;
-    }
-    float wsum = 0.f;
-    for (int s = 0; s < k; ++s) wsum += expf(a.part_lse[(int64_t)(s0 + s) * kTileQ + row] - M);
-    const float inv = 1.f / wsum;
-    for (int d4 = half * (D / 8); d4 < (half + 1) * (D / 8); ++d4) {
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int s = 0; s < k; ++s) {
-        const int64_t prow = (int64_t)(s0 + s) * kTileQ + row;
-        const float w = expf(a.part_lse[prow] - M);
-        const float4 x = *(const float4 *)(a.part_o + prow * D + 4 * d4);
-        acc.x += w * x.x, acc.y += w * x.y, acc.z += w * x.z, acc.w += w * x.w;
+    for (int idx = threadIdx.x; idx < 2 * TQ; idx += kThreads) {
+      const int row = idx >> 1, half = idx & 1;
+      const RowGeo geo = row_geo(a, r, row >> 5);
+      const int64_t qpos = geo.q0 + (row & 31);
+      if (qpos >= a.Sq) continue;
+      float M = -INFINITY;
+      for (int s = 0; s < k; ++s) M = fmaxf(M, a.part_lse[(int64_t)(s0 + s) * TQ + row]);
+      E *op = (E *)a.o + geo.b * a.o_sb + geo.head * a.o_sh + qpos * a.o_ss;
+      if (M == -INFINITY) {
+        for (int d = half * (D / 2); d < (half + 1) * (D / 2); ++d) op[d] = (E)0;
+        if (half == 0) a.lse[((int64_t)geo.b * a.Hq + geo.head) * a.Sq + qpos] = -INFINITY;
+        continue;
       }
-      acc.x *= inv, acc.y *= inv, acc.z *= inv, acc.w *= inv;
-      if constexpr (BF) {
-        *(uint2 *)(op + 4 * d4) = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
-      } else {
-        *(float4 *)(op + 4 * d4) = acc;
+      float wsum = 0.f;
+      for (int s = 0; s < k; ++s) wsum += expf(a.part_lse[(int64_t)(s0 + s) * TQ + row] - M);
+      const float inv = 1.f / wsum;
+      for (int d4 = half * (D / 8); d4 < (half + 1) * (D / 8); ++d4) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int s = 0; s < k; ++s) {
+          const int64_t prow = (int64_t)(s0 + s) * TQ + row;
+          const float w = expf(a.part_lse[prow] - M);
+          const float4 x = *(const float4 *)(a.part_o + prow * D + 4 * d4);
+          acc.x += w * x.x, acc.y += w * x.y, acc.z += w * x.z, acc.w += w * x.w;
+        }
+        acc.x *= inv, acc.y *= inv, acc.z *= inv, acc.w *= inv;
+        if constexpr (BF) {
+          *(uint2 *)(op + 4 * d4) = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+        } else {
+          *(float4 *)(op + 4 * d4) = acc;
+        }
       }
+      if (half == 0) a.lse[((int64_t)geo.b * a.Hq + geo.head) * a.Sq + qpos] = M + logf(wsum);
     }
-    if (half == 0) a.lse[((int64_t)geo.b * a.Hq + geo.head) * a.Sq + qpos] = M + logf(wsum);
   }
 }
 
@@ -795,11 +798,11 @@ static int slices_per_wave(int D) {
   return v ? v : 1;
 }
 
-template <int D, int TK, bool BF, int NS>
+template <int D, int TK, bool BF, int TQ, int NS>
 bsa_status launch_one(const Plan &p, const AttnArgs &a, hipStream_t s) {
   static int grid = 0;
-  const int threads = BF ? 64 * (4 / NS) : kThreads;
-  auto kern = BF ? (void (*)(AttnArgs))k_attn_bf16<D, TK, NS> : (void (*)(AttnArgs))k_attn<D, 64, false>;
+  const int threads = BF ? 64 * (TQ / 32 / NS) : kThreads;
+  auto kern = BF ? (void (*)(AttnArgs))k_attn_bf16<D, TK, TQ, NS> : (void (*)(AttnArgs))k_attn<D, 64, false>;
   if (grid == 0) {
     int dev = 0, cus = 0, occ = 0;
     HIP_TRY(hipGetDevice(&dev));
@@ -812,7 +815,7 @@ bsa_status launch_one(const Plan &p, const AttnArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(kern, dim3(g), dim3(threads), 0, s, a);
   if (p.rg.split > 0 && p.comb_cap > 0) {
     const int cg = (int)std::min<int64_t>(p.comb_cap, 2048);
-    hipLaunchKernelGGL((k_combine<D, BF>), dim3(cg), dim3(kThreads), 0, s, a, p.comb);
+    hipLaunchKernelGGL((k_combine<D, BF, TQ>), dim3(cg), dim3(kThreads), 0, s, a, p.comb);
   }
   HIP_TRY(hipGetLastError());
   return BSA_OK;
@@ -824,14 +827,21 @@ bsa_status attention_launch(const Plan &p, const AttnArgs &a, hipStream_t s) {
   const bool bf = p.dtype == BSA_BF16;
   // fp32 tiles use 64 keys (the planner guarantees it): 128 would not fit LDS twice.
   const bool two = slices_per_wave(p.D) == 2;
-  if (bf && p.D == 128 && p.rg.tk == 64)
-    return two ? launch_one<128, 64, true, 2>(p, a, s) : launch_one<128, 64, true, 1>(p, a, s);
-  if (bf && p.D == 64 && p.rg.tk == 64)
-    return two ? launch_one<64, 64, true, 2>(p, a, s) : launch_one<64, 64, true, 1>(p, a, s);
-  if (bf && p.D == 128 && p.rg.tk == 128) return launch_one<128, 128, true, 1>(p, a, s);
-  if (bf && p.D == 64 && p.rg.tk == 128) return launch_one<64, 128, true, 1>(p, a, s);
-  if (!bf && p.D == 128 && p.rg.tk == 64) return launch_one<128, 64, false, 1>(p, a, s);
-  if (!bf && p.D == 64 && p.rg.tk == 64) return launch_one<64, 64, false, 1>(p, a, s);
+  const int tq = p.rg.tq, tk = p.rg.tk;
+  if (bf && tq == 128) {
+    if (p.D == 128 && tk == 64)
+      return two ? launch_one<128, 64, true, 128, 2>(p, a, s) : launch_one<128, 64, true, 128, 1>(p, a, s);
+    if (p.D == 64 && tk == 64)
+      return two ? launch_one<64, 64, true, 128, 2>(p, a, s) : launch_one<64, 64, true, 128, 1>(p, a, s);
+    if (p.D == 128 && tk == 128) return launch_one<128, 128, true, 128, 1>(p, a, s);
+    if (p.D == 64 && tk == 128) return launch_one<64, 128, true, 128, 1>(p, a, s);
+  }
+  if (bf && tq == 256) {
+    if (p.D == 128 && tk == 64) return launch_one<128, 64, true, 256, 1>(p, a, s);
+    if (p.D == 64 && tk == 64) return launch_one<64, 64, true, 256, 1>(p, a, s);
+  }
+  if (!bf && tq == 128 && p.D == 128 && tk == 64) return launch_one<128, 64, false, 128, 1>(p, a, s);
+  if (!bf && tq == 128 && p.D == 64 && tk == 64) return launch_one<64, 64, false, 128, 1>(p, a, s);
   return fail(BSA_ERR_UNSUPPORTED, "no kernel for this head_dim / tile_k");
 }
 

@@ -50,8 +50,10 @@ struct Plan {
   std::vector<HeadMeta> hmeta_host;  // host copy kept alive for the asynchronous uploads
   void *pre = nullptr;    // features, counters, head metadata, union bits
   void *arena = nullptr;  // lists, entries, rows, work list, partials, scratch
+  size_t pre_bytes = 0, arena_bytes = 0;
   HeadMeta *hmeta;
   unsigned long long *feat_dev;
+  int32_t *row_feat;  // per logical row: selected blocks, effective blocks
   int32_t *counters;
   uint8_t *uni_bits;
   int32_t *list_off, *ent_kt, *ent_page;
@@ -78,6 +80,11 @@ struct AttnArgs {
 
 // Error reporting (thread-local message).
 bsa_status fail(bsa_status s, const std::string &msg);
+
+// Device allocations of plans go through a small per-device cache of freed
+// blocks, so repeated requests do not pay hipMalloc / hipFree each time.
+hipError_t cached_alloc(void **ptr, size_t bytes, int device);
+void cached_free(void *ptr, size_t bytes, int device);
 
 // Planner entry points (bsa_planner.hip). Each returns BSA_OK or BSA_ERR_HIP.
 bsa_status plan_features(Plan &p, const uint8_t *mask, const int32_t *page_table);

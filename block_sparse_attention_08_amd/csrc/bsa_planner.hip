@@ -68,13 +68,12 @@ __global__ void k_union(const uint8_t *__restrict__ mask, const HeadMeta *__rest
 }
 
 // One wave per logical row: popcount, and the count of effective blocks (the
-// union's in union mode) that the causal bound can reach. Per head: nnz (sum),
-// max row (max), empty rows (sum), effective blocks (sum).
-__global__ void k_features(const uint8_t *__restrict__ mask, const HeadMeta *__restrict__ hm,
-                           int Hq, int Hkv, int G, int nbm, int64_t rows_per_bm,
-                           int64_t mask_bstride, const uint8_t *__restrict__ U, int64_t unkb,
-                           int causal, int64_t off, int64_t Sq,
-                           unsigned long long *__restrict__ feat) {
+// union's in union mode) that the causal bound can reach, written per row
+// (no atomics, so no contention and no clearing).
+__global__ void k_row_features(const uint8_t *__restrict__ mask, const HeadMeta *__restrict__ hm,
+                               int Hq, int Hkv, int G, int nbm, int64_t rows_per_bm,
+                               int64_t mask_bstride, const uint8_t *__restrict__ U, int64_t unkb,
+                               int causal, int64_t off, int64_t Sq, int32_t *__restrict__ rowf) {
   const int lane = threadIdx.x & 63;
   const int64_t wv = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 6;
   if (wv >= nbm * rows_per_bm) return;
@@ -104,11 +103,46 @@ __global__ void k_features(const uint8_t *__restrict__ mask, const HeadMeta *__r
   cnt = wave_sum(cnt);
   eff = wave_sum(eff);
   if (lane == 0) {
-    unsigned long long *f = feat + ((int64_t)bm * Hq + h) * 4;
-    atomicAdd(&f[0], (unsigned long long)cnt);
-    atomicMax(&f[1], (unsigned long long)cnt);
-    atomicAdd(&f[2], (unsigned long long)(cnt == 0));
-    atomicAdd(&f[3], (unsigned long long)eff);
+    rowf[2 * wv] = cnt;
+    rowf[2 * wv + 1] = eff;
+  }
+}
+
+// One workgroup per (mask batch, head): nnz (sum), max row (max), empty rows
+// (count), effective blocks (sum) over the head's rows.
+__global__ void k_head_features(const int32_t *__restrict__ rowf, const HeadMeta *__restrict__ hm,
+                                int Hq, int64_t rows_per_bm, unsigned long long *__restrict__ feat) {
+  __shared__ unsigned long long red[4][kThreads / 64];
+  const int bm = blockIdx.x / Hq, h = blockIdx.x % Hq;
+  const HeadMeta m = hm[h];
+  const int32_t *rf = rowf + 2 * ((int64_t)bm * rows_per_bm + m.row_off);
+  unsigned long long nnz = 0, mx = 0, empty = 0, eff = 0;
+  for (int64_t q = threadIdx.x; q < m.nqb; q += kThreads) {
+    const unsigned long long c = (unsigned)rf[2 * q];
+    nnz += c;
+    mx = c > mx ? c : mx;
+    empty += c == 0;
+    eff += (unsigned)rf[2 * q + 1];
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    nnz += __shfl_xor(nnz, o);
+    const unsigned long long t = __shfl_xor(mx, o);
+    mx = t > mx ? t : mx;
+    empty += __shfl_xor(empty, o);
+    eff += __shfl_xor(eff, o);
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[0][w] = nnz, red[1][w] = mx, red[2][w] = empty, red[3][w] = eff;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long f[4] = {0, 0, 0, 0};
+    for (int i = 0; i < kThreads / 64; ++i) {
+      f[0] += red[0][i];
+      f[1] = red[1][i] > f[1] ? red[1][i] : f[1];
+      f[2] += red[2][i];
+      f[3] += red[3][i];
+    }
+    for (int k = 0; k < 4; ++k) feat[(int64_t)blockIdx.x * 4 + k] = f[k];
   }
 }
 
@@ -276,8 +310,39 @@ __global__ void k_scan_apply(const int32_t *in, int64_t n, const int32_t *__rest
   if (blockIdx.x == gridDim.x - 1 && threadIdx.x == kThreads - 1) out[n] = run;
 }
 
+// Whole scan in one workgroup (small arrays): chunks of kScanBlock in order,
+// carrying the running total. in and out may be the same array.
+__global__ void k_scan_single(const int32_t *in, int64_t n, int32_t *out) {
+  int carry = 0;
+  for (int64_t base = 0; base < n || base == 0; base += kScanBlock) {
+    int v[4], s = 0;
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = base + threadIdx.x * 4 + u;
+      v[u] = i < n ? in[i] : 0;
+      s += v[u];
+    }
+    int tot;
+    int run = carry + block_excl_scan(s, &tot);
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = base + threadIdx.x * 4 + u;
+      if (i < n) out[i] = run;
+      run += v[u];
+    }
+    carry += tot;
+    if (base + kScanBlock >= n) break;
+  }
+  if (threadIdx.x == 0) out[n] = carry;
+}
+
+constexpr int64_t kSingleScanMax = 1 << 16;
+
 bsa_status scan(const int32_t *in, int64_t n, int32_t *out, int32_t *bsum, hipStream_t s) {
-  const int64_t nb = n > 0 ? (n + kScanBlock - 1) / kScanBlock : 1;
+  if (n <= kSingleScanMax) {
+    hipLaunchKernelGGL(k_scan_single, dim3(1), dim3(kThreads), 0, s, in, n, out);
+    HIP_TRY(hipGetLastError());
+    return BSA_OK;
+  }
+  const int64_t nb = (n + kScanBlock - 1) / kScanBlock;
   hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)nb), dim3(kThreads), 0, s, in, n, bsum);
   hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(kThreads), 0, s, bsum, nb);
   hipLaunchKernelGGL(k_scan_apply, dim3((unsigned)nb), dim3(kThreads), 0, s, in, n, bsum, out);
@@ -415,9 +480,11 @@ bsa_status plan_features(Plan &p, const uint8_t *mask, const int32_t *page_table
     hipLaunchKernelGGL(k_union, dim3(grid_for((int64_t)p.nbm * p.Hkv * p.unkb)), dim3(kThreads), 0,
                        s, mask, p.hmeta, mask_bstride, p.Hkv, p.G, (int)p.nbm, p.unkb, p.uni_bits);
   if (p.nbm * rows_per_bm > 0)
-    hipLaunchKernelGGL(k_features, dim3(grid_for(p.nbm * rows_per_bm * 64)), dim3(kThreads), 0, s,
-                       mask, p.hmeta, p.Hq, p.Hkv, p.G, (int)p.nbm, rows_per_bm, mask_bstride,
-                       p.uni ? p.uni_bits : nullptr, p.unkb, p.causal, p.off, p.Sq, p.feat_dev);
+    hipLaunchKernelGGL(k_row_features, dim3(grid_for(p.nbm * rows_per_bm * 64)), dim3(kThreads), 0,
+                       s, mask, p.hmeta, p.Hq, p.Hkv, p.G, (int)p.nbm, rows_per_bm, mask_bstride,
+                       p.uni ? p.uni_bits : nullptr, p.unkb, p.causal, p.off, p.Sq, p.row_feat);
+  hipLaunchKernelGGL(k_head_features, dim3((unsigned)(p.nbm * p.Hq)), dim3(kThreads), 0, s,
+                     p.row_feat, p.hmeta, p.Hq, rows_per_bm, p.feat_dev);
   if (p.paged && p.Skv > 0) {
     const int64_t used = (p.Skv + p.P - 1) / p.P;
     hipLaunchKernelGGL(k_check_pages, dim3(grid_for(p.B * used)), dim3(kThreads), 0, s, page_table,

@@ -1,0 +1,140 @@
+"""Build the regime lookup table by profiling on the local GPU.
+
+Tessera (abstract) picks an execution plan per request through a lookup table
+built from offline profiling. This script is that offline step for libbsa: for
+each mask-shape bucket it times every candidate regime (tile rows, key tile,
+schedule, split threshold, GQA packing) on a representative seeded workload,
+one request = bsa_plan + bsa_forward, and writes the fastest regime of each
+bucket as a rule, in bucket order, followed by a catch-all default.
+
+    python -m block_sparse_attention_08_amd.lut.build_lut [--out PATH] [--steps N]
+"""
+from __future__ import annotations
+
+import argparse
+import itertools
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BIG = "1000000"
+BIGIMB = "100000000"
+
+
+def buckets():
+    """(name, rule key fields and ranges, representative workload factory)."""
+    from block_sparse_attention_08_amd import workloads as W
+    return [
+        # GQA union over a paged cache (chunked prefill).
+        ("gqa-union", "* bf16 1 *  0 " + BIG + "  0 " + BIG + "  0 " + BIG + "  0 " + BIGIMB,
+         lambda: W.chunked_prefill()),
+        # Large blocks (>= 128), D=128, low density: 3-D video windows.
+        ("video-128", "128 bf16 0 *  128 " + BIG + "  128 " + BIG + "  0 400  0 " + BIGIMB,
+         lambda: W.video_dit()),
+        # Mixed block sizes with uneven rows (long video), D=128.
+        ("mixed-128", "128 bf16 0 *  16 127  16 " + BIG + "  0 " + BIG + "  0 " + BIGIMB,
+         lambda: W.long_video()),
+        # Small blocks, D=64, low density (regular patterns).
+        ("regular-64-sparse", "64 bf16 0 *  16 " + BIG + "  16 " + BIG + "  0 200  0 " + BIGIMB,
+         lambda: W.affine(bs=64)),
+        # Small blocks, D=64, dense windows.
+        ("regular-64-dense", "64 bf16 0 *  16 " + BIG + "  16 " + BIG + "  201 " + BIG + "  0 " + BIGIMB,
+         lambda: W.affine(bs=64, window=8192)),
+    ]
+
+
+def candidates(union: bool):
+    out = []
+    for tq, tk, sched, split in itertools.product((128, 256), (64, 128), ("local", "lpt"), (0, 128)):
+        if tq == 256 and tk == 128:
+            continue  # the planner turns it into 256 x 64
+        for pack in ((1, 0) if union else (0,)):
+            out.append((tq, tk, sched, split, pack))
+    return out
+
+
+def time_regime(bsa, w, tensors, regime, steps):
+    import torch
+    q, k, v, mask, table, o, lse = tensors
+    tq, tk, sched, split, pack = regime
+    lut = bsa.Lut.forced(tq, tk, sched, split, pack)
+    prob = w.problem_dict()
+    p = bsa.plan(prob, mask, table, lut)
+    p.forward(q, k, v, o, lse)
+    torch.cuda.synchronize()
+    p.free()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    plans = []
+    for _ in range(steps):
+        p = bsa.plan(prob, mask, table, lut)
+        p.forward(q, k, v, o, lse)
+        plans.append(p)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t) / steps
+    for p in plans:
+        p.free()
+    return dt
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default=os.path.join(HERE, "gfx950.lut"))
+    ap.add_argument("--steps", type=int, default=6)
+    args = ap.parse_args()
+    import torch
+    import block_sparse_attention_08_amd as bsa
+
+    dev = torch.cuda.get_device_properties(0)
+    lines = ["bsa-lut 1",
+             f"# Built by block_sparse_attention_08_amd/lut/build_lut.py on {dev.name} "
+             f"({dev.multi_processor_count} CUs), {args.steps} timed requests per regime.",
+             "#   rule D dtype union paged bq_lo bq_hi bk_lo bk_hi dens_lo dens_hi imb_lo imb_hi "
+             "-> Tq Tk sched split pack",
+             "# Each rule is the fastest regime (bsa_plan + bsa_forward) measured on the named"
+             " representative workload; first match wins."]
+    for name, key, make in buckets():
+        w = make()
+        q, k, v = w.make_qkv(device="cuda")
+        mask = torch.from_numpy(np.ascontiguousarray(w.mask)).cuda()
+        table = torch.from_numpy(np.ascontiguousarray(w.page_table)).cuda() if w.paged else None
+        o = torch.empty_like(q)
+        lse = torch.empty((w.batch, w.hq, w.sq), dtype=torch.float32, device="cuda")
+        tensors = (q, k, v, mask, table, o, lse)
+        res = []
+        for reg in candidates(w.gqa_union):
+            dt = time_regime(bsa, w, tensors, reg, args.steps)
+            res.append((dt, reg))
+            print(f"[lut] {name}: {reg} {dt * 1e3:.3f} ms", flush=True)
+        res.sort()
+        # Among regimes within 2% of the fastest, take the simplest one
+        # (no split, 128-row and 64-key tiles, row order, packing).
+        fastest = res[0][0]
+        close = [(dt, reg) for dt, reg in res if dt <= fastest * 1.02]
+        simplicity = lambda reg: (reg[3] != 0, reg[0] != 128, reg[1] != 64, reg[2] != "local", reg[4] == 0)
+        best_dt, best = min(close, key=lambda x: (simplicity(x[1]), x[0]))
+        second = res[1][0] if len(res) > 1 else best_dt
+        tq, tk, sched, split, pack = best
+        lines.append(f"# {name}: {w.name} B={w.batch} Hq={w.hq} S={w.sq}/{w.skv} D={w.d}; best "
+                     f"{best_dt * 1e3:.3f} ms per request (next {second * 1e3:.3f} ms)")
+        lines.append(f"rule {key} -> {tq} {tk} {sched} {split} {pack}")
+        del q, k, v, o, lse, mask, table
+        torch.cuda.empty_cache()
+    lines.append("# Anything else: 128 x 64 tiles, row order, no split, GQA packing when possible.")
+    lines.append("rule * * * * 0 " + BIG + " 0 " + BIG + " 0 " + BIG + " 0 " + BIGIMB + " -> 128 64 local 0 1")
+    text = "\n".join(lines) + "\n"
+    bsa.Lut.parse(text)  # validate
+    with open(args.out, "w") as f:
+        f.write(text)
+    print(text, flush=True)
+
+
+if __name__ == "__main__":
+    main()

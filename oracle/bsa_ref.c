@@ -339,8 +339,8 @@ static int parse_lut(const char *text, rule_t **rules_out, int *n_out) {
       else if (f != 2 && !parse_int(tok, &v[f])) {
       } else goto bad;
     }
-    if (v[0] != 128 || (v[1] != 64 && v[1] != 128) || v[3] < 0 || v[3] > (1 << 30) ||
-        (v[4] != 0 && v[4] != 1))
+    if ((v[0] != 128 && v[0] != 256) || (v[1] != 64 && v[1] != 128) || v[3] < 0 ||
+        v[3] > (1 << 30) || (v[4] != 0 && v[4] != 1))
       goto bad;
     r->r.tq = (int)v[0], r->r.tk = (int)v[1], r->r.sched = (int)v[2];
     r->r.split = (int)v[3], r->r.pack = (int)v[4];
@@ -414,7 +414,7 @@ int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_tabl
   regime_t rg = {128, 64, 0, 0, 1};
   if (force) {
     rg.tq = force[0], rg.tk = force[1], rg.sched = force[2], rg.split = force[3], rg.pack = force[4];
-    if (rg.tq != 128 || (rg.tk != 64 && rg.tk != 128) || rg.sched < 0 || rg.sched > 1 ||
+    if ((rg.tq != 128 && rg.tq != 256) || (rg.tk != 64 && rg.tk != 128) || rg.sched < 0 || rg.sched > 1 ||
         rg.split < 0 || rg.pack < 0 || rg.pack > 1) {
       free(moff), free(uni), free(feat);
       return -2;
@@ -443,7 +443,8 @@ int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_tabl
   }
   /* Adjustments that make the regime valid for this problem. */
   if (!(p->gqa_union && (gs == 2 || gs == 4))) rg.pack = 0;
-  if (p->dtype == 1) rg.tk = 64; /* fp32 tiles hold 64 keys */
+  if (p->dtype == 1) rg.tq = 128, rg.tk = 64; /* fp32 tiles are 128 x 64 */
+  if (rg.tq == 256) rg.tk = 64;                /* 256-row tiles use 64 keys */
   if (p->paged && p->page_size % rg.tk) {
     if (rg.tk == 128 && p->page_size % 64 == 0) rg.tk = 64;
     else {
@@ -451,7 +452,8 @@ int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_tabl
       return -3;
     }
   }
-  for (int pass = 0; pass < 2; ++pass) {
+  /* At most 32 live bits per tile: shrink Tk to 64, then Tq to 128. */
+  for (;;) {
     int bad = 0;
     for (int h = 0; h < p->hq; ++h) {
       int mq = (!p->gqa_union && p->bq[h] < rg.tq) ? rg.tq / p->bq[h] : 1;
@@ -459,12 +461,14 @@ int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_tabl
       if (mq * mk > 32) bad = 1;
     }
     if (!bad) break;
-    if (pass == 0 && rg.tk == 128) {
+    if (rg.tk == 128) {
       rg.tk = 64;
-      continue;
+    } else if (rg.tq == 256) {
+      rg.tq = 128;
+    } else {
+      free(moff), free(uni), free(feat);
+      return -3;
     }
-    free(moff), free(uni), free(feat);
-    return -3;
   }
   const int64_t tq = rg.tq, tk = rg.tk;
   const int64_t tr = rg.pack ? tq / gs : tq; /* query positions per physical row */

@@ -62,6 +62,8 @@ REGIMES = {
     "tk128_lpt": forced_lut_text(128, 128, "lpt", 0, 0),
     "split3_local": forced_lut_text(128, 64, "local", 3, 1),
     "split2_lpt_tk128": forced_lut_text(128, 128, "lpt", 2, 1),
+    "tq256_local": forced_lut_text(256, 64, "local", 0, 1),
+    "tq256_split3_lpt": forced_lut_text(256, 64, "lpt", 3, 1),
 }
 
 
@@ -76,6 +78,13 @@ def test_small_default(ref, case):
                                   "tiny_long_video"])
 def test_small_forced_regimes(ref, case, regime):
     run_case(ref, SMALL[case](), lut_text=REGIMES[regime], label=f"{case}/{regime}")
+
+
+@pytest.mark.parametrize("case", ["video_dit", "chunked_prefill"])
+def test_full_tq256(ref, case):
+    w = W.video_dit() if case == "video_dit" else W.chunked_prefill()
+    run_case(ref, w, lut_text=forced_lut_text(256, 64, "local", 0, 1), rows=sample_rows(w, 192),
+             device_gen=True, label=f"{case}_full/tq256")
 
 
 def test_zero_lengths(ref):

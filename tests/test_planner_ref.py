@@ -113,7 +113,8 @@ CASES = {
 
 
 @pytest.mark.parametrize("case", sorted(CASES))
-@pytest.mark.parametrize("regime", [(128, 64, 0, 0, 1), (128, 128, 1, 3, 1), (128, 64, 1, 2, 0)])
+@pytest.mark.parametrize("regime", [(128, 64, 0, 0, 1), (128, 128, 1, 3, 1), (128, 64, 1, 2, 0),
+                                    (256, 64, 0, 2, 1), (256, 128, 1, 0, 0)])
 def test_plan_element_coverage(ref, case, regime):
     w = W.random_problem(d=64, seed=sorted(CASES).index(case), **CASES[case])
     img = ref.plan(w, force=list(regime))
@@ -149,6 +150,17 @@ def test_regime_adjustments(ref):
     # 16x16 blocks cannot use 128-key tiles (8 x 8 live bits > 32).
     w = W.random_problem(batch=1, hq=1, sq=64, skv=256, bq=16, bk=16, d=64, seed=6)
     assert decode(ref.plan(w, force=[128, 128, 0, 0, 0])).h["tk"] == 64
+    # 256-row tiles use 64 keys; 16-row blocks cannot merge 16 ways and 4 ways at once.
+    w = W.random_problem(batch=1, hq=1, sq=512, skv=256, bq=64, bk=64, d=64, seed=8)
+    h = decode(ref.plan(w, force=[256, 128, 0, 0, 0])).h
+    assert (h["tq"], h["tk"]) == (256, 64)
+    w = W.random_problem(batch=1, hq=1, sq=512, skv=256, bq=16, bk=16, d=64, seed=9)
+    h = decode(ref.plan(w, force=[256, 64, 0, 0, 0])).h
+    assert (h["tq"], h["tk"]) == (128, 64)
+    # fp32 always uses 128 x 64 tiles.
+    w = W.random_problem(batch=1, hq=1, sq=512, skv=256, bq=64, bk=64, d=64, dtype="f32", seed=10)
+    h = decode(ref.plan(w, force=[256, 128, 0, 0, 0])).h
+    assert (h["tq"], h["tk"]) == (128, 64)
     # Unsupported block size.
     w = W.random_problem(batch=1, hq=1, sq=64, skv=64, bq=48, bk=64, d=64, seed=7)
     with pytest.raises(ValueError):
