@@ -31,7 +31,6 @@
 #include "bsa_internal.h"
 
 #include <algorithm>
-#include <cstdlib>
 #include <type_traits>
 
 namespace bsa {
@@ -426,26 +425,33 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-// A workgroup owns a TQ-row query tile (128 or 256) split into 32-row slices;
-// each wave owns NS slices (NS = 2 makes every K and V^T fragment read from
-// LDS feed two MFMAs).
-template <int D, int TK, int TQ, int NS>
+// A workgroup owns a TQ-row query tile (128 or 256) split into 32-row
+// slices, one per wave (four or eight waves).
+template <int D, int TK, int TQ>
 struct CfgB {
-  static constexpr int SLICES = TQ / 32;
-  static constexpr int WAVES = SLICES / NS;
+  static constexpr int WAVES = TQ / 32;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int ROWB = D * 2;                     // bytes per K/V row in LDS
   static constexpr int CPR = D / 8;                      // 16-byte chunks per row
   static constexpr int TILEB = TK * ROWB;                // bytes of one K (or V) tile
   static constexpr int LOADS = TILEB / (THREADS * 16);   // 16-byte loads per thread per tile
+  static constexpr int RPL = THREADS / CPR;              // tile rows covered by one load
   static constexpr int NKB = TK / 32;
   static constexpr int NDB = D / 32;
   // K rows: 16-byte chunk c of row r sits at chunk c ^ swz_k(r); V rows: c ^ swz_v(r).
   static __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
   static __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+  // A thread's slot in load u sits RPL rows below its slot in load 0 with the
+  // same swizzle, so one per-thread offset serves every load of a tile.
+  static_assert((D == 128 && RPL % 16 == 0) || (D == 64 && RPL % 4 == 0), "swizzle period");
 };
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: P values stay below 2^8
+
+// Plan arrays are read-only while a kernel runs; reading them through the
+// constant address space makes uniform loads scalar.
+typedef __attribute__((address_space(4))) const int32_t cint32;
+typedef __attribute__((address_space(4))) const uint32_t cuint32;
 
 // Values that are the same on every lane (they derive from the work item and
 // the entry index only), moved to scalar registers so buffer descriptors and
@@ -459,9 +465,9 @@ __device__ __forceinline__ const T *uniform(const T *p) {
   return (const T *)(((uint64_t)hi << 32) | lo);
 }
 
-template <int D, int TK, int TQ, int NS>
-__global__ __launch_bounds__(64 * (TQ / 32 / NS), (NS == 2 || (TK == 128 && TQ == 128)) ? 1 : 2) void k_attn_bf16(AttnArgs a) {
-  using C = CfgB<D, TK, TQ, NS>;
+template <int D, int TK, int TQ>
+__global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) void k_attn_bf16(AttnArgs a) {
+  using C = CfgB<D, TK, TQ>;
   // Two K tiles and two V tiles. K runs one tile ahead of V: while the softmax
   // of tile j runs, the S^T MFMAs of tile j+1 are already issued, and the
   // loads of K tile j+2 and V tile j+1 are in flight.
@@ -470,7 +476,7 @@ __global__ __launch_bounds__(64 * (TQ / 32 / NS), (NS == 2 || (TK == 128 && TQ =
   auto vbuf = [&](int i) { return lds + (2 + (i & 1)) * C::TILEB; };
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // = this wave's 32-row slice
   const int n = lane & 31, hh = lane >> 5;
   const int nitems = a.counters[CNT_ITEMS];
   const int grid = gridDim.x;
@@ -484,159 +490,146 @@ __global__ __launch_bounds__(64 * (TQ / 32 / NS), (NS == 2 || (TK == 128 && TQ =
   const int vrow0 = 8 * hh + (vj >> 2);  // V^T operand rows 16 c2 + vrow0 (+4)
   const int vbyte = 8 * (vj & 1);
   const int nqt = (int)a.nqt;
+  // Per-thread byte offsets of its 16-byte slot in load 0 of a K / V tile.
+  const int trow = tid / C::CPR, tpos = tid % C::CPR;
+  const int koff0 = trow * (int)a.k_ss * 2 + ((tpos ^ C::swz_k(trow)) << 4);
+  const int voff0 = trow * (int)a.v_ss * 2 + ((tpos ^ C::swz_v(trow)) << 4);
+  const int kstep = C::RPL * (int)a.k_ss * 2, vstep = C::RPL * (int)a.v_ss * 2;
 
   for (int it = lid; it < nitems; it += grid) {
     const int4 item = ((const int4 *)a.items)[it];
     const int r = item.x, e0 = item.y, nent = item.z - item.y, slot = item.w;
+
+    // Entry metadata through the constant address space, so the loads are
+    // scalar (SGPRs, no wait behind the tile loads). A rolling window holds
+    // entries j, j+1, j+2; entry j+3 is loaded one iteration ahead.
+    struct Meta {
+      int kt, pg;
+      uint32_t lv;
+    };
+    auto load_meta = [&](int j) {
+      const int ee = e0 + min(j, max(nent - 1, 0));
+      Meta m;
+      m.kt = ((const cint32 *)a.ent_kt)[ee];
+      m.pg = a.paged ? ((const cint32 *)a.ent_page)[ee] : 0;
+      m.lv = ((const cuint32 *)a.ent_live)[ee];
+      return m;
+    };
+    Meta m0 = load_meta(0), m1 = load_meta(1), m2 = load_meta(2);
+
     // Row geometry (32-bit: rows, heads and tiles are all below 2^31).
     const int nh = a.pack ? a.Hkv : a.Hq;
     const int qt = r % nqt, hrow = (r / nqt) % nh, b = r / (nqt * nh);
     const int g = (a.pack ? hrow * a.G : hrow) / a.G;
-    int head[NS], qbase[NS];
-    int64_t q0[NS], qpos[NS];
-    bool qvalid[NS];
-    HeadMeta hm[NS];
-    bf16x8 qb[NS][D / 16];
-#pragma unroll
-    for (int ns = 0; ns < NS; ++ns) {
-      const int sl = wave * NS + ns;  // 32-row slice of the tile
-      head[ns] = a.pack ? hrow * a.G + (32 * sl) / a.tr : hrow;
-      qbase[ns] = a.pack ? 0 : 32 * sl;
-      q0[ns] = a.pack ? (int64_t)qt * a.tr + (32 * sl) % a.tr : (int64_t)qt * a.tq + 32 * sl;
-      hm[ns] = a.hm[head[ns]];
-      qpos[ns] = q0[ns] + n;
-      qvalid[ns] = qpos[ns] < a.Sq;
-      const uint16_t *qp = Q + b * a.q_sb + head[ns] * a.q_sh + (qvalid[ns] ? qpos[ns] : 0) * a.q_ss;
+    const int head = a.pack ? hrow * a.G + (32 * wave) / a.tr : hrow;
+    const int qbase = a.pack ? 0 : 32 * wave;
+    const int64_t q0 = a.pack ? (int64_t)qt * a.tr + (32 * wave) % a.tr : (int64_t)qt * a.tq + 32 * wave;
+    const HeadMeta hm = a.hm[head];
+    const int64_t qpos = q0 + n;
+    const bool qvalid = qpos < a.Sq;
+    bf16x8 qb[D / 16];
+    {
+      const uint16_t *qp = Q + b * a.q_sb + head * a.q_sh + (qvalid ? qpos : 0) * a.q_ss;
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        uint4 x = qvalid[ns] ? *(const uint4 *)(qp + 16 * c + 8 * hh) : make_uint4(0, 0, 0, 0);
-        qb[ns][c] = __builtin_bit_cast(bf16x8, x);
+        uint4 x = qvalid ? *(const uint4 *)(qp + 16 * c + 8 * hh) : make_uint4(0, 0, 0, 0);
+        qb[c] = __builtin_bit_cast(bf16x8, x);
       }
     }
     const uint16_t *kbase_ptr = (const uint16_t *)a.k + (a.paged ? 0 : b * a.k_sb) + g * a.k_sh;
     const uint16_t *vbase_ptr = (const uint16_t *)a.v + (a.paged ? 0 : b * a.v_sb) + g * a.v_sh;
 
-    // Buffer loads of one K or V tile of entry e into dst (every thread).
-    auto issue = [&](const uint16_t *base, int64_t sb, int64_t ss, int e, uint8_t *dst_tile, bool is_v) {
-      const int kt = a.ent_kt[e];
-      const int k0 = kt * TK;
+    // Buffer loads of one K or V tile of local entry j into dst (every thread).
+    // Rows past the sequence end lie beyond the descriptor's range and read 0.
+    auto issue = [&](const uint16_t *base, int64_t sb, int64_t ss, const Meta &m, uint8_t *dst_tile,
+                     int off0, int step) {
+      const int k0 = m.kt * TK;
       const int left = (int)min<int64_t>(a.Skv - k0, TK);  // rows of the tile that exist
-      const uint16_t *tb = a.paged ? base + (int64_t)a.ent_page[e] * sb + (int64_t)(k0 % a.P) * ss
+      const uint16_t *tb = a.paged ? base + (int64_t)m.pg * sb + (int64_t)(k0 % a.P) * ss
                                    : base + (int64_t)k0 * ss;
       tb = uniform(tb);
       const int bytes = uniform((int)((left - 1) * ss * 2 + D * 2));
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)tb, 0, bytes, 0x00020000);
 #pragma unroll
       for (int u = 0; u < C::LOADS; ++u) {
-        const int L = u * C::THREADS + tid;  // 16-byte LDS slot, lane-linear per wave
-        const int row = L / C::CPR, pos = L % C::CPR;
-        const int sw = is_v ? C::swz_v(row) : C::swz_k(row);
-        const int off = row * (int)ss * 2 + ((pos ^ sw) << 4);
-        uint8_t *dst = dst_tile + (u * C::THREADS + wave * 64) * 16;
-        // Rows past the sequence end fall outside the buffer range and read 0.
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, row < left ? off : bytes, 0, 0, 0);
+        uint8_t *dst = dst_tile + (u * C::THREADS + wave * 64) * 16;  // lane-linear 1 KiB per wave
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, off0 + u * step, 0, 0, 0);
       }
     };
-    auto issue_k = [&](int e, int j) { issue(kbase_ptr, a.k_sb, a.k_ss, e, kbuf(j), false); };
-    auto issue_v = [&](int e, int j) { issue(vbase_ptr, a.v_sb, a.v_ss, e, vbuf(j), true); };
+    auto issue_k = [&](int j, const Meta &m) { issue(kbase_ptr, a.k_sb, a.k_ss, m, kbuf(j), koff0, kstep); };
+    auto issue_v = [&](int j, const Meta &m) { issue(vbase_ptr, a.v_sb, a.v_ss, m, vbuf(j), voff0, vstep); };
     auto kfrag = [&](const uint8_t *ks, int i) {
       const int row = 32 * (i / (D / 16)) + krow0;
       const int c = 2 * (i % (D / 16)) + hh;
       return *(const bf16x8 *)(ks + row * C::ROWB + ((c ^ C::swz_k(row)) << 4));
     };
 
-    f32x16 o[NS][C::NDB];
-    float m_ref[NS], l_run[NS];
-    uint64_t wbits[NS];
-    int qsub[NS];
+    f32x16 o[C::NDB];
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns) {
-#pragma unroll
-      for (int u = 0; u < C::NDB; ++u) o[ns][u] = f32x16{};
-      m_ref[ns] = -INFINITY, l_run[ns] = 0.f;
-      const int iq_lo = qbase[ns] >> hm[ns].lq;
-      const int niq = hm[ns].lq >= 5 ? 1 : (32 >> hm[ns].lq);
-      wbits[ns] = ((1ull << (hm[ns].mk * niq)) - 1ull) << (iq_lo * hm[ns].mk);
-      qsub[ns] = ((qbase[ns] + n) >> hm[ns].lq) * hm[ns].mk;
-    }
+    for (int u = 0; u < C::NDB; ++u) o[u] = f32x16{};
+    float m_ref = -INFINITY, l_run = 0.f;
+    const int iq_lo = qbase >> hm.lq;
+    const int niq = hm.lq >= 5 ? 1 : (32 >> hm.lq);
+    const uint64_t wbits = ((1ull << (hm.mk * niq)) - 1ull) << (iq_lo * hm.mk);
+    const int qsub = ((qbase + n) >> hm.lq) * hm.mk;
 
     constexpr int STEPS = C::NKB * D / 16;     // K fragments per tile
-    constexpr int EPS = C::NKB * 16 / STEPS;   // scores per slice exponentiated per step (2 or 4)
-    f32x16 s_cur[NS][C::NKB];
-    if (nent > 0) {
-      issue_k(e0, 0);
-      issue_v(e0, 0);
-      if (nent > 1) issue_k(e0 + 1, 1);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      const uint8_t *ks = kbuf(0);
-#pragma unroll
-      for (int i = 0; i < STEPS; ++i) {
-        const bf16x8 kf = kfrag(ks, i);
-        const int t = i / (D / 16), cc = i % (D / 16);
-#pragma unroll
-        for (int ns = 0; ns < NS; ++ns)
-          s_cur[ns][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qb[ns][cc], cc == 0 ? f32x16{} : s_cur[ns][t], 0, 0, 0);
-      }
-    }
-    for (int j = 0; j < nent; ++j) {
-      const int e = e0 + j;
+    constexpr int EPS = C::NKB * 16 / STEPS;   // scores exponentiated per step (2 or 4)
+
+    // One tile iteration: softmax of tile j (scores in s_cur), S^T of tile
+    // j+1 into s_next, O += V^T P^T of tile j.
+    auto tile = [&](int j, f32x16 (&s_cur)[C::NKB], f32x16 (&s_next)[C::NKB]) {
       __builtin_amdgcn_s_waitcnt(0);  // K tile j+1 and V tile j have landed (this wave)
       __syncthreads();                // ... for every wave; K tile j and V tile j-1 are free
-      if (j + 2 < nent) issue_k(e + 2, j);
-      if (j + 1 < nent) issue_v(e + 1, j + 1);
+      const Meta m3 = load_meta(j + 3);
+      if (j + 2 < nent) issue_k(j + 2, m2);
+      if (j + 1 < nent) issue_v(j + 1, m1);
 
       // ---- mask tile j (sequence end, causal diagonal, dead sub-blocks) ----
-      const int64_t kb0 = (int64_t)a.ent_kt[e] * TK;
-      const uint32_t live = a.ent_live[e];
-      float m_use[NS];
-#pragma unroll
-      for (int ns = 0; ns < NS; ++ns) {
-        const bool need = (kb0 + TK > a.Skv) || (a.causal && kb0 + TK - 1 > q0[ns] + a.off) ||
-                          ((uint64_t)live & wbits[ns]) != wbits[ns];
-        if (need) {
-          const uint32_t lbits = live >> qsub[ns];
-          int64_t lim = a.Skv - kb0;  // keys allowed from the tile start
-          if (a.causal) lim = min(lim, qpos[ns] + a.off + 1 - kb0);
-          const int klim = (int)max<int64_t>(-1, min<int64_t>(lim, TK));
-#pragma unroll
-          for (int t = 0; t < C::NKB; ++t)
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj) {
-              const int kl = 32 * t + acc_key<true>(jj, hh);
-              if (!(kl < klim && ((lbits >> (kl >> hm[ns].lk)) & 1u))) s_cur[ns][t][jj] = -INFINITY;
-            }
-        }
-        // ---- online softmax of tile j, log2 domain, lazy rescale ----
-        float mx = -INFINITY;
+      const int64_t kb0 = (int64_t)m0.kt * TK;
+      const uint32_t live = m0.lv;
+      const bool need = (kb0 + TK > a.Skv) || (a.causal && kb0 + TK - 1 > q0 + a.off) ||
+                        ((uint64_t)live & wbits) != wbits;
+      if (need) {
+        const uint32_t lbits = live >> qsub;
+        int64_t lim = a.Skv - kb0;  // keys allowed from the tile start
+        if (a.causal) lim = min(lim, qpos + a.off + 1 - kb0);
+        const int klim = (int)max<int64_t>(-1, min<int64_t>(lim, TK));
 #pragma unroll
         for (int t = 0; t < C::NKB; ++t)
 #pragma unroll
-          for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s_cur[ns][t][jj]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float cand = mx * a.scale_log2;
-        if (__any(cand > m_ref[ns] + kRescaleThreshold)) {
-          const float m_new = fmaxf(m_ref[ns], cand);
-          const float alpha = m_new == -INFINITY ? 1.f : fexp2(m_ref[ns] - m_new);
-          l_run[ns] *= alpha;
-#pragma unroll
-          for (int u = 0; u < C::NDB; ++u) o[ns][u] *= alpha;
-          m_ref[ns] = m_new;
-        }
-        m_use[ns] = m_ref[ns] == -INFINITY ? 0.f : m_ref[ns];
+          for (int jj = 0; jj < 16; ++jj) {
+            const int kl = 32 * t + acc_key<true>(jj, hh);
+            if (!(kl < klim && ((lbits >> (kl >> hm.lk)) & 1u))) s_cur[t][jj] = -INFINITY;
+          }
       }
 
-      // One straight-line block, in a fixed order: each K fragment of tile
-      // j+1 feeds NS S^T MFMAs (independent work), followed by the
-      // exponentials of a slice of tile j; the fragment read runs three steps
-      // ahead. Then each V^T fragment feeds NS P V^T MFMAs. sched_barrier(0)
-      // keeps the compiler from regrouping the steps. On the last tile the
-      // S^T of a stale buffer is computed and dropped.
-      f32x16 s_next[NS][C::NKB];
-      uint32_t pw[NS][C::NKB * 8];  // P as packed bf16 pairs
-      float psum[NS];
+      // ---- online softmax of tile j, log2 domain, lazy rescale ----
+      float mx = -INFINITY;
 #pragma unroll
-      for (int ns = 0; ns < NS; ++ns) psum[ns] = 0.f;
+      for (int t = 0; t < C::NKB; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s_cur[t][jj]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float cand = mx * a.scale_log2;
+      if (__any(cand > m_ref + kRescaleThreshold)) {
+        const float m_new = fmaxf(m_ref, cand);
+        const float alpha = m_new == -INFINITY ? 1.f : fexp2(m_ref - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int u = 0; u < C::NDB; ++u) o[u] *= alpha;
+        m_ref = m_new;
+      }
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+
+      // One straight-line block, in a fixed order: each S^T MFMA of tile j+1
+      // (independent work) is followed by the exponentials of a slice of tile
+      // j, with its K-operand read issued three steps ahead; then the P V^T
+      // MFMAs follow their transpose reads. sched_barrier(0) keeps the
+      // compiler from regrouping the steps. On the last tile the S^T of a
+      // stale buffer is computed and dropped.
+      uint32_t pw[C::NKB * 8];  // P as packed bf16 pairs
+      float psum = 0.f;
       {
         const uint8_t *ks = kbuf(j + 1);
         bf16x8 kf[STEPS];
@@ -646,25 +639,20 @@ __global__ __launch_bounds__(64 * (TQ / 32 / NS), (NS == 2 || (TK == 128 && TQ =
         for (int i = 0; i < STEPS; ++i) {
           if (i + 3 < STEPS) kf[i + 3] = kfrag(ks, i + 3);
           const int t = i / (D / 16), cc = i % (D / 16);
+          s_next[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qb[cc], cc == 0 ? f32x16{} : s_next[t], 0, 0, 0);
 #pragma unroll
-          for (int ns = 0; ns < NS; ++ns)
-            s_next[ns][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qb[ns][cc], cc == 0 ? f32x16{} : s_next[ns][t], 0, 0, 0);
-#pragma unroll
-          for (int ns = 0; ns < NS; ++ns)
-#pragma unroll
-            for (int k2 = 0; k2 < EPS; k2 += 2) {
-              const int x = i * EPS + k2;
-              const float p0 = fexp2(__builtin_fmaf(s_cur[ns][x / 16][x % 16], a.scale_log2, -m_use[ns]));
-              const float p1 = fexp2(__builtin_fmaf(s_cur[ns][x / 16][x % 16 + 1], a.scale_log2, -m_use[ns]));
-              psum[ns] += p0;
-              psum[ns] += p1;
-              pw[ns][x / 2] = pack_bf16x2(p0, p1);
-            }
+          for (int k2 = 0; k2 < EPS; k2 += 2) {
+            const int x = i * EPS + k2;
+            const float p0 = fexp2(__builtin_fmaf(s_cur[x / 16][x % 16], a.scale_log2, -m_use));
+            const float p1 = fexp2(__builtin_fmaf(s_cur[x / 16][x % 16 + 1], a.scale_log2, -m_use));
+            psum += p0;
+            psum += p1;
+            pw[x / 2] = pack_bf16x2(p0, p1);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-#pragma unroll
-      for (int ns = 0; ns < NS; ++ns) l_run[ns] += psum[ns];
+      l_run += psum;
 
       // ---- O^T += V^T P^T, V^T fragments by transpose reads of V tile j ----
       {
@@ -688,53 +676,66 @@ __global__ __launch_bounds__(64 * (TQ / 32 / NS), (NS == 2 || (TK == 128 && TQ =
         for (int i = 0; i < PV; ++i) {
           if (i + 2 < PV) vf[i + 2] = vfrag(i + 2);
           const int c2 = i / C::NDB, u = i % C::NDB;
-#pragma unroll
-          for (int ns = 0; ns < NS; ++ns) {
-            const uint4 w = make_uint4(pw[ns][4 * c2], pw[ns][4 * c2 + 1], pw[ns][4 * c2 + 2], pw[ns][4 * c2 + 3]);
-            o[ns][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], __builtin_bit_cast(bf16x8, w), o[ns][u], 0, 0, 0);
-          }
+          const uint4 w = make_uint4(pw[4 * c2], pw[4 * c2 + 1], pw[4 * c2 + 2], pw[4 * c2 + 3]);
+          o[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], __builtin_bit_cast(bf16x8, w), o[u], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      m0 = m1, m1 = m2, m2 = m3;
+    };
+
+    // Prologue: K tiles 0 and 1, V tile 0; S^T of tile 0. Then tiles two at a
+    // time, the two score buffers swapping roles (no register copies).
+    f32x16 sa[C::NKB], sb[C::NKB];
+    if (nent > 0) {
+      issue_k(0, m0);
+      issue_v(0, m0);
+      if (nent > 1) issue_k(1, m1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      const uint8_t *ks = kbuf(0);
 #pragma unroll
-      for (int ns = 0; ns < NS; ++ns)
+      for (int i = 0; i < STEPS; ++i) {
+        const int t = i / (D / 16), cc = i % (D / 16);
+        sa[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(ks, i), qb[cc], cc == 0 ? f32x16{} : sa[t], 0, 0, 0);
+      }
+    }
+    for (int j = 0; j < nent; ++j) {
+      tile(j, sa, sb);
 #pragma unroll
-        for (int t = 0; t < C::NKB; ++t) s_cur[ns][t] = s_next[ns][t];
+      for (int t = 0; t < C::NKB; ++t) sa[t] = sb[t];
     }
     __syncthreads();  // the next item's first loads reuse the buffers
 
     // ---- finalize ----
-#pragma unroll
-    for (int ns = 0; ns < NS; ++ns) {
-      const float l_tot = l_run[ns] + __shfl_xor(l_run[ns], 32);
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      const float lse = l_tot > 0.f ? (m_ref[ns] + log2f(l_tot)) * kLn2 : -INFINITY;
-      if (slot < 0) {
-        if (qvalid[ns]) {
-          uint16_t *op = (uint16_t *)a.o + b * a.o_sb + head[ns] * a.o_sh + qpos[ns] * a.o_ss;
-#pragma unroll
-          for (int u = 0; u < C::NDB; ++u)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-              const int d0 = 32 * u + 8 * q4 + 4 * hh;
-              *(uint2 *)(op + d0) = make_uint2(pack_bf16x2(o[ns][u][4 * q4] * inv, o[ns][u][4 * q4 + 1] * inv),
-                                               pack_bf16x2(o[ns][u][4 * q4 + 2] * inv, o[ns][u][4 * q4 + 3] * inv));
-            }
-          if (hh == 0) a.lse[((int64_t)b * a.Hq + head[ns]) * a.Sq + qpos[ns]] = lse;
-        }
-      } else {
-        const int64_t prow = (int64_t)slot * TQ + 32 * (wave * NS + ns) + n;
-        float *pp = a.part_o + prow * D;
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+    if (slot < 0) {
+      if (qvalid) {
+        uint16_t *op = (uint16_t *)a.o + b * a.o_sb + head * a.o_sh + qpos * a.o_ss;
 #pragma unroll
         for (int u = 0; u < C::NDB; ++u)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
             const int d0 = 32 * u + 8 * q4 + 4 * hh;
-            *(float4 *)(pp + d0) = make_float4(o[ns][u][4 * q4] * inv, o[ns][u][4 * q4 + 1] * inv,
-                                               o[ns][u][4 * q4 + 2] * inv, o[ns][u][4 * q4 + 3] * inv);
+            *(uint2 *)(op + d0) = make_uint2(pack_bf16x2(o[u][4 * q4] * inv, o[u][4 * q4 + 1] * inv),
+                                             pack_bf16x2(o[u][4 * q4 + 2] * inv, o[u][4 * q4 + 3] * inv));
           }
-        if (hh == 0) a.part_lse[prow] = lse;
+        if (hh == 0) a.lse[((int64_t)b * a.Hq + head) * a.Sq + qpos] = lse;
       }
+    } else {
+      const int64_t prow = (int64_t)slot * TQ + 32 * wave + n;
+      float *pp = a.part_o + prow * D;
+#pragma unroll
+      for (int u = 0; u < C::NDB; ++u)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = 32 * u + 8 * q4 + 4 * hh;
+          *(float4 *)(pp + d0) = make_float4(o[u][4 * q4] * inv, o[u][4 * q4 + 1] * inv,
+                                             o[u][4 * q4 + 2] * inv, o[u][4 * q4 + 3] * inv);
+        }
+      if (hh == 0) a.part_lse[prow] = lse;
     }
   }
 }
@@ -784,25 +785,11 @@ __global__ __launch_bounds__(kThreads) void k_combine(AttnArgs a, const int32_t 
   }
 }
 
-// Slices per wave of the bf16 kernel: 1 (four waves per workgroup, two
-// workgroups per CU). With 2, two waves each own two slices so every K/V
-// fragment feeds two MFMAs, but only one wave runs per SIMD and nothing hides
-// LDS and MFMA latency: measured 2-3x slower, kept for measurements only
-// (BSA_SLICES_PER_WAVE=2).
-static int slices_per_wave(int D) {
-  static int v = -1;
-  if (v < 0) {
-    const char *e = std::getenv("BSA_SLICES_PER_WAVE");
-    v = (e && (e[0] == '1' || e[0] == '2')) ? e[0] - '0' : 0;
-  }
-  return v ? v : 1;
-}
-
-template <int D, int TK, bool BF, int TQ, int NS>
+template <int D, int TK, bool BF, int TQ>
 bsa_status launch_one(const Plan &p, const AttnArgs &a, hipStream_t s) {
   static int grid = 0;
-  const int threads = BF ? 64 * (TQ / 32 / NS) : kThreads;
-  auto kern = BF ? (void (*)(AttnArgs))k_attn_bf16<D, TK, TQ, NS> : (void (*)(AttnArgs))k_attn<D, 64, false>;
+  const int threads = BF ? 64 * (TQ / 32) : kThreads;
+  auto kern = BF ? (void (*)(AttnArgs))k_attn_bf16<D, TK, TQ> : (void (*)(AttnArgs))k_attn<D, 64, false>;
   if (grid == 0) {
     int dev = 0, cus = 0, occ = 0;
     HIP_TRY(hipGetDevice(&dev));
@@ -826,22 +813,19 @@ bsa_status launch_one(const Plan &p, const AttnArgs &a, hipStream_t s) {
 bsa_status attention_launch(const Plan &p, const AttnArgs &a, hipStream_t s) {
   const bool bf = p.dtype == BSA_BF16;
   // fp32 tiles use 64 keys (the planner guarantees it): 128 would not fit LDS twice.
-  const bool two = slices_per_wave(p.D) == 2;
   const int tq = p.rg.tq, tk = p.rg.tk;
   if (bf && tq == 128) {
-    if (p.D == 128 && tk == 64)
-      return two ? launch_one<128, 64, true, 128, 2>(p, a, s) : launch_one<128, 64, true, 128, 1>(p, a, s);
-    if (p.D == 64 && tk == 64)
-      return two ? launch_one<64, 64, true, 128, 2>(p, a, s) : launch_one<64, 64, true, 128, 1>(p, a, s);
-    if (p.D == 128 && tk == 128) return launch_one<128, 128, true, 128, 1>(p, a, s);
-    if (p.D == 64 && tk == 128) return launch_one<64, 128, true, 128, 1>(p, a, s);
+    if (p.D == 128 && tk == 64) return launch_one<128, 64, true, 128>(p, a, s);
+    if (p.D == 64 && tk == 64) return launch_one<64, 64, true, 128>(p, a, s);
+    if (p.D == 128 && tk == 128) return launch_one<128, 128, true, 128>(p, a, s);
+    if (p.D == 64 && tk == 128) return launch_one<64, 128, true, 128>(p, a, s);
   }
   if (bf && tq == 256) {
-    if (p.D == 128 && tk == 64) return launch_one<128, 64, true, 256, 1>(p, a, s);
-    if (p.D == 64 && tk == 64) return launch_one<64, 64, true, 256, 1>(p, a, s);
+    if (p.D == 128 && tk == 64) return launch_one<128, 64, true, 256>(p, a, s);
+    if (p.D == 64 && tk == 64) return launch_one<64, 64, true, 256>(p, a, s);
   }
-  if (!bf && tq == 128 && p.D == 128 && tk == 64) return launch_one<128, 64, false, 128, 1>(p, a, s);
-  if (!bf && tq == 128 && p.D == 64 && tk == 64) return launch_one<64, 64, false, 128, 1>(p, a, s);
+  if (!bf && tq == 128 && p.D == 128 && tk == 64) return launch_one<128, 64, false, 128>(p, a, s);
+  if (!bf && tq == 128 && p.D == 64 && tk == 64) return launch_one<64, 64, false, 128>(p, a, s);
   return fail(BSA_ERR_UNSUPPORTED, "no kernel for this head_dim / tile_k");
 }
 
