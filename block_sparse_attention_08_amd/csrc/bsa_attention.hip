@@ -448,6 +448,18 @@ struct CfgB {
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: P values stay below 2^8
 
+// max over lanes l and l ^ 32 (the two half-waves hold the two key halves).
+__device__ __forceinline__ float halfwave_max(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)pr[0]), __builtin_bit_cast(float, (uint32_t)pr[1]));
+}
+__device__ __forceinline__ float halfwave_sum(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, (uint32_t)pr[0]) + __builtin_bit_cast(float, (uint32_t)pr[1]);
+}
+
 // Plan arrays are read-only while a kernel runs; reading them through the
 // constant address space makes uniform loads scalar.
 typedef __attribute__((address_space(4))) const int32_t cint32;
@@ -465,7 +477,7 @@ __device__ __forceinline__ const T *uniform(const T *p) {
   return (const T *)(((uint64_t)hi << 32) | lo);
 }
 
-template <int D, int TK, int TQ>
+template <int D, int TK, int TQ, bool PAGED>
 __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) void k_attn_bf16(AttnArgs a) {
   using C = CfgB<D, TK, TQ>;
   // Two K tiles and two V tiles. K runs one tile ahead of V: while the softmax
@@ -495,6 +507,9 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
   const int koff0 = trow * (int)a.k_ss * 2 + ((tpos ^ C::swz_k(trow)) << 4);
   const int voff0 = trow * (int)a.v_ss * 2 + ((tpos ^ C::swz_v(trow)) << 4);
   const int kstep = C::RPL * (int)a.k_ss * 2, vstep = C::RPL * (int)a.v_ss * 2;
+  const int skv32 = (int)a.Skv;  // sequence lengths are below 2^31
+  const int ptiles = PAGED ? a.P / TK : 1;  // key tiles per page
+  const bool ptiles_pow2 = (ptiles & (ptiles - 1)) == 0;
 
   for (int it = lid; it < nitems; it += grid) {
     const int4 item = ((const int4 *)a.items)[it];
@@ -511,7 +526,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
       const int ee = e0 + min(j, max(nent - 1, 0));
       Meta m;
       m.kt = ((const cint32 *)a.ent_kt)[ee];
-      m.pg = a.paged ? ((const cint32 *)a.ent_page)[ee] : 0;
+      m.pg = PAGED ? ((const cint32 *)a.ent_page)[ee] : 0;
       m.lv = ((const cuint32 *)a.ent_live)[ee];
       return m;
     };
@@ -536,19 +551,20 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
         qb[c] = __builtin_bit_cast(bf16x8, x);
       }
     }
-    const uint16_t *kbase_ptr = (const uint16_t *)a.k + (a.paged ? 0 : b * a.k_sb) + g * a.k_sh;
-    const uint16_t *vbase_ptr = (const uint16_t *)a.v + (a.paged ? 0 : b * a.v_sb) + g * a.v_sh;
+    const uint16_t *kbase_ptr = (const uint16_t *)a.k + (PAGED ? 0 : b * a.k_sb) + g * a.k_sh;
+    const uint16_t *vbase_ptr = (const uint16_t *)a.v + (PAGED ? 0 : b * a.v_sb) + g * a.v_sh;
 
     // Buffer loads of one K or V tile of local entry j into dst (every thread).
     // Rows past the sequence end lie beyond the descriptor's range and read 0.
     auto issue = [&](const uint16_t *base, int64_t sb, int64_t ss, const Meta &m, uint8_t *dst_tile,
                      int off0, int step) {
       const int k0 = m.kt * TK;
-      const int left = (int)min<int64_t>(a.Skv - k0, TK);  // rows of the tile that exist
-      const uint16_t *tb = a.paged ? base + (int64_t)m.pg * sb + (int64_t)(k0 % a.P) * ss
-                                   : base + (int64_t)k0 * ss;
-      tb = uniform(tb);
-      const int bytes = uniform((int)((left - 1) * ss * 2 + D * 2));
+      const int left = min(skv32 - k0, TK);  // rows of the tile that exist
+      // Row of the tile within its page (pages hold whole key tiles).
+      const int prow = ptiles_pow2 ? (m.kt & (ptiles - 1)) * TK : (m.kt % max(ptiles, 1)) * TK;
+      const uint16_t *tb = PAGED ? base + (int64_t)m.pg * sb + (int64_t)prow * ss
+                                 : base + (int64_t)k0 * ss;
+      const int bytes = (left - 1) * (int)ss * 2 + D * 2;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)tb, 0, bytes, 0x00020000);
 #pragma unroll
       for (int u = 0; u < C::LOADS; ++u) {
@@ -591,16 +607,35 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
       const bool need = (kb0 + TK > a.Skv) || (a.causal && kb0 + TK - 1 > q0 + a.off) ||
                         ((uint64_t)live & wbits) != wbits;
       if (need) {
+        // Allowed keys of this lane's query as bit masks over the tile (64
+        // keys per mask): live key sub-blocks, then the prefix of keys that
+        // exist and satisfy the causal bound.
         const uint32_t lbits = live >> qsub;
-        int64_t lim = a.Skv - kb0;  // keys allowed from the tile start
+        int64_t lim = a.Skv - kb0;
         if (a.causal) lim = min(lim, qpos + a.off + 1 - kb0);
-        const int klim = (int)max<int64_t>(-1, min<int64_t>(lim, TK));
+        const int klim = (int)max<int64_t>(0, min<int64_t>(lim, TK));
+        const int ak = 1 << hm.lk;  // keys per live bit
+        const uint64_t sub = ak >= 64 ? ~0ull : ((1ull << ak) - 1ull);
+        uint64_t km[(TK + 63) / 64];
+#pragma unroll
+        for (int w64 = 0; w64 < (TK + 63) / 64; ++w64) {
+          uint64_t m = 0;
+          for (int ik = 0; ik < hm.mk; ++ik)
+            if ((lbits >> ik) & 1u) {
+              const int k0b = ik * ak - 64 * w64;  // first key of the sub-block in this mask
+              if (k0b >= 64 || k0b + ak <= 0) continue;
+              m |= k0b >= 0 ? sub << k0b : sub >> -k0b;
+            }
+          const int lo = klim - 64 * w64;
+          m &= lo >= 64 ? ~0ull : (lo <= 0 ? 0ull : ((1ull << lo) - 1ull));
+          km[w64] = m >> (8 * hh);  // accumulator keys are offset by 8 on the upper half-wave
+        }
 #pragma unroll
         for (int t = 0; t < C::NKB; ++t)
 #pragma unroll
           for (int jj = 0; jj < 16; ++jj) {
-            const int kl = 32 * t + acc_key<true>(jj, hh);
-            if (!(kl < klim && ((lbits >> (kl >> hm.lk)) & 1u))) s_cur[t][jj] = -INFINITY;
+            const int kl = 32 * t + 16 * (jj >> 3) + (jj & 7);  // key offset without the 8*hh term
+            if (!((km[kl / 64] >> (kl % 64)) & 1ull)) s_cur[t][jj] = -INFINITY;
           }
       }
 
@@ -610,7 +645,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
       for (int t = 0; t < C::NKB; ++t)
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s_cur[t][jj]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = halfwave_max(mx);
       const float cand = mx * a.scale_log2;
       if (__any(cand > m_ref + kRescaleThreshold)) {
         const float m_new = fmaxf(m_ref, cand);
@@ -708,7 +743,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
     __syncthreads();  // the next item's first loads reuse the buffers
 
     // ---- finalize ----
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = halfwave_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
     if (slot < 0) {
@@ -785,11 +820,13 @@ __global__ __launch_bounds__(kThreads) void k_combine(AttnArgs a, const int32_t 
   }
 }
 
-template <int D, int TK, bool BF, int TQ>
+template <int D, int TK, bool BF, int TQ, bool PAGED = false>
 bsa_status launch_one(const Plan &p, const AttnArgs &a, hipStream_t s) {
+  if constexpr (BF && !PAGED)
+    if (a.paged) return launch_one<D, TK, BF, TQ, true>(p, a, s);
   static int grid = 0;
   const int threads = BF ? 64 * (TQ / 32) : kThreads;
-  auto kern = BF ? (void (*)(AttnArgs))k_attn_bf16<D, TK, TQ> : (void (*)(AttnArgs))k_attn<D, 64, false>;
+  auto kern = BF ? (void (*)(AttnArgs))k_attn_bf16<D, TK, TQ, PAGED> : (void (*)(AttnArgs))k_attn<D, 64, false>;
   if (grid == 0) {
     int dev = 0, cus = 0, occ = 0;
     HIP_TRY(hipGetDevice(&dev));
