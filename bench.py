@@ -144,6 +144,9 @@ def main():
     ap.add_argument("--workload", default="video_dit")
     ap.add_argument("--lut", default=None, help="regime table (default: the packaged gfx950 table)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run three device copies of a 1 GiB tensor (1 GiB read and 1 GiB "
+                         "written per launch), to scale HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs the block-sparse attention path on one GPU; --gpus {args.gpus} "
@@ -155,6 +158,15 @@ def main():
     import block_sparse_attention_08_amd as bsa
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        x = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").normal_()
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": 1 << 30,
+                          "bytes_written": 1 << 30, "launches": 3}), flush=True)
+        return
     w = workload(args.workload)
     q, k, v = w.make_qkv(device="cuda")
     mask = torch.from_numpy(np.ascontiguousarray(w.mask)).cuda()
