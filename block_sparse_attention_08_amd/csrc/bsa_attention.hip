@@ -523,8 +523,9 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
       uint32_t lv;
     };
     auto load_meta = [&](int j) {
-      const int ee = e0 + min(j, max(nent - 1, 0));
-      Meta m;
+      Meta m{0, 0, 0};
+      if (nent <= 0) return m;  // an item without entries reads no metadata
+      const int ee = e0 + min(j, nent - 1);
       m.kt = ((const cint32 *)a.ent_kt)[ee];
       m.pg = PAGED ? ((const cint32 *)a.ent_page)[ee] : 0;
       m.lv = ((const cuint32 *)a.ent_live)[ee];
