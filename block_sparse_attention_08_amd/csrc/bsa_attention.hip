@@ -543,6 +543,10 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
     const HeadMeta hm = a.hm[head];
     const int64_t qpos = q0 + n;
     const bool qvalid = qpos < a.Sq;
+    // Largest key position the wave's first query may see under the causal
+    // bound (query q0 + n sees keys up to q0 + n + off), clamped to
+    // [-64, Skv]: beyond either end the tests below give the same answers.
+    const int qlim0 = (int)max<int64_t>(-64, min<int64_t>(q0 + a.off, a.Skv));
     bf16x8 qb[D / 16];
     {
       const uint16_t *qp = Q + b * a.q_sb + head * a.q_sh + (qvalid ? qpos : 0) * a.q_ss;
@@ -603,18 +607,19 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
       if (j + 1 < nent) issue_v(j + 1, m1);
 
       // ---- mask tile j (sequence end, causal diagonal, dead sub-blocks) ----
-      const int64_t kb0 = (int64_t)m0.kt * TK;
+      // 32-bit scalar tests: positions and the causal offset are below 2^31.
+      const int kb0 = m0.kt * TK;
       const uint32_t live = m0.lv;
-      const bool need = (kb0 + TK > a.Skv) || (a.causal && kb0 + TK - 1 > q0 + a.off) ||
+      const bool need = (kb0 + TK > skv32) || (a.causal && kb0 + TK - 1 > qlim0) ||
                         ((uint64_t)live & wbits) != wbits;
       if (need) {
         // Allowed keys of this lane's query as bit masks over the tile (64
         // keys per mask): live key sub-blocks, then the prefix of keys that
         // exist and satisfy the causal bound.
         const uint32_t lbits = live >> qsub;
-        int64_t lim = a.Skv - kb0;
-        if (a.causal) lim = min(lim, qpos + a.off + 1 - kb0);
-        const int klim = (int)max<int64_t>(0, min<int64_t>(lim, TK));
+        int lim = skv32 - kb0;
+        if (a.causal) lim = min(lim, qlim0 + n + 1 - kb0);
+        const int klim = max(0, min(lim, TK));
         const int ak = 1 << hm.lk;  // keys per live bit
         const uint64_t sub = ak >= 64 ? ~0ull : ((1ull << ak) - 1ull);
         uint64_t km[(TK + 63) / 64];
