@@ -342,7 +342,8 @@ bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *p
   const size_t feat_bytes = sizeof(int64_t) * 4 * P.nbm * P.Hq;
   int64_t rows_per_bm = 0;
   for (int h = 0; h < P.Hq; ++h) rows_per_bm += cdiv(P.Sq, P.bq[h]);
-  const size_t pre_bytes = aligned(sizeof(int32_t) * CNT_N) + aligned(feat_bytes) +
+  const size_t pre_bytes = aligned(sizeof(int32_t) * CNT_N) +
+                           aligned(sizeof(int32_t) * kQueuesPerSet * kQueueSets) + aligned(feat_bytes) +
                            aligned(sizeof(HeadMeta) * P.Hq) +
                            aligned((size_t)P.nbm * P.Hkv * std::max<int64_t>(P.unkb, 1)) +
                            aligned(sizeof(int32_t) * 2 * std::max<int64_t>(P.nbm * rows_per_bm, 1));
@@ -354,6 +355,8 @@ bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *p
   uint8_t *pb = (uint8_t *)P.pre;
   P.counters = (int32_t *)pb;
   pb += aligned(sizeof(int32_t) * CNT_N);
+  P.queues = (int32_t *)pb;
+  pb += aligned(sizeof(int32_t) * kQueuesPerSet * kQueueSets);
   P.feat_dev = (unsigned long long *)pb;
   pb += aligned(feat_bytes);
   P.hmeta = (HeadMeta *)pb;
@@ -487,7 +490,8 @@ bsa_status bsa_forward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k
   a.ent_live = P.ent_live, a.hm = P.hmeta, a.part_o = P.part_o, a.part_lse = P.part_lse;
   a.Sq = P.Sq, a.Skv = P.Skv, a.off = P.off, a.nqt = P.nqt;
   a.Hq = P.Hq, a.Hkv = P.Hkv, a.G = P.G, a.tq = P.rg.tq, a.tr = P.tr, a.pack = P.rg.pack;
-  a.causal = P.causal, a.paged = P.paged, a.P = P.P;
+  a.causal = P.causal, a.paged = P.paged, a.P = P.P, a.sched = P.rg.sched;
+  a.queue = P.queues + kQueuesPerSet * (P.qseq.fetch_add(1) % kQueueSets);
   a.scale_log2 = P.scale * 1.4426950408889634f;
   if (P.nrows == 0) return BSA_OK;
   return attention_launch(P, a, (hipStream_t)stream);

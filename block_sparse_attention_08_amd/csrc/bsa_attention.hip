@@ -491,9 +491,20 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // = this wave's 32-row slice
   const int n = lane & 31, hh = lane >> 5;
   const int nitems = a.counters[CNT_ITEMS];
-  const int grid = gridDim.x;
-  int lid = blockIdx.x;
-  if ((grid & 7) == 0) lid = (blockIdx.x & 7) * (grid >> 3) + (blockIdx.x >> 3);
+  // Work distribution: workgroups are dispatched round-robin over the 8 XCDs,
+  // so workgroup b runs on XCD b % 8 (when the grid is a multiple of 8). Each
+  // XCD owns a queue of items: a contiguous stretch of the work list in row
+  // order (neighbouring query tiles share K/V in that XCD's L2), every 8th
+  // item in longest-first order (the XCDs get equal shares of long and short
+  // items). Its workgroups take items from it with an atomic ticket, so an
+  // XCD's workgroups finish together however the item lengths vary.
+  const int nq = (gridDim.x & 7) == 0 ? kQueuesPerSet : 1;
+  const int xq = blockIdx.x % nq;
+  const bool strided = a.sched != 0;
+  const int qbeg = strided ? xq : (int)((int64_t)xq * nitems / nq);
+  const int qcnt = strided ? (nitems - xq + nq - 1) / nq : (int)((int64_t)(xq + 1) * nitems / nq) - qbeg;
+  int *const qctr = a.queue + xq;
+  __shared__ int s_ticket;
   const uint16_t *__restrict__ Q = (const uint16_t *)a.q;
 
   // Per-lane LDS offsets that do not depend on the tile.
@@ -511,7 +522,13 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
   const int ptiles = PAGED ? a.P / TK : 1;  // key tiles per page
   const bool ptiles_pow2 = (ptiles & (ptiles - 1)) == 0;
 
-  for (int it = lid; it < nitems; it += grid) {
+  if (tid == 0) s_ticket = atomicAdd(qctr, 1);
+  __syncthreads();
+  for (int tk = __builtin_amdgcn_readfirstlane(s_ticket); tk < qcnt;) {
+    // The next ticket is taken now; its value is needed only after this item.
+    int next_ticket = 0;
+    if (tid == 0) next_ticket = atomicAdd(qctr, 1);
+    const int it = strided ? qbeg + tk * nq : qbeg + tk;
     const int4 item = ((const int4 *)a.items)[it];
     const int r = item.x, e0 = item.y, nent = item.z - item.y, slot = item.w;
 
@@ -778,6 +795,10 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
         }
       if (hh == 0) a.part_lse[prow] = lse;
     }
+    // Every thread read the current ticket before the barriers of this item.
+    if (tid == 0) s_ticket = next_ticket;
+    __syncthreads();
+    tk = __builtin_amdgcn_readfirstlane(s_ticket);
   }
 }
 
@@ -826,6 +847,12 @@ __global__ __launch_bounds__(kThreads) void k_combine(AttnArgs a, const int32_t 
   }
 }
 
+// Zeroes one call's work-queue counters (a kernel, not a memset, so the
+// forward stays capturable in a graph).
+__global__ void k_zero_queues(int *q) {
+  if (threadIdx.x < kQueuesPerSet) q[threadIdx.x] = 0;
+}
+
 template <int D, int TK, bool BF, int TQ, bool PAGED = false>
 bsa_status launch_one(const Plan &p, const AttnArgs &a, hipStream_t s) {
   if constexpr (BF && !PAGED)
@@ -842,6 +869,7 @@ bsa_status launch_one(const Plan &p, const AttnArgs &a, hipStream_t s) {
   }
   int g = grid;
   if (p.item_cap < g) g = (int)std::max<int64_t>(p.item_cap, 1);
+  if constexpr (BF) hipLaunchKernelGGL(k_zero_queues, dim3(1), dim3(64), 0, s, a.queue);
   hipLaunchKernelGGL(kern, dim3(g), dim3(threads), 0, s, a);
   if (p.rg.split > 0 && p.comb_cap > 0) {
     const int cg = (int)std::min<int64_t>(p.comb_cap, 2048);

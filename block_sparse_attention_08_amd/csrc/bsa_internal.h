@@ -5,6 +5,7 @@
 
 #include <cstdint>
 #include <string>
+#include <atomic>
 #include <vector>
 
 #include "bsa.h"
@@ -23,6 +24,10 @@ struct HeadMeta {
 
 // Counters written on the device by the planner.
 enum { CNT_ENT = 0, CNT_ITEMS = 1, CNT_SLOTS = 2, CNT_COMB = 3, CNT_BADPAGE = 4, CNT_N = 8 };
+// Work-queue counters of the attention kernel: one per XCD (8), in a ring of
+// sets so that forward calls on one plan that overlap in time (up to
+// kQueueSets of them) each count on their own set.
+constexpr int kQueuesPerSet = 8, kQueueSets = 64;
 
 struct Regime {
   int tq = 128, tk = 64, sched = 0, split = 0, pack = 1;
@@ -55,6 +60,8 @@ struct Plan {
   unsigned long long *feat_dev;
   int32_t *row_feat;  // per logical row: selected blocks, effective blocks
   int32_t *counters;
+  int32_t *queues;                           // kQueueSets x kQueuesPerSet
+  mutable std::atomic<uint32_t> qseq{0};     // next queue set
   uint8_t *uni_bits;
   int32_t *list_off, *ent_kt, *ent_page;
   uint32_t *ent_live;
@@ -70,11 +77,12 @@ struct AttnArgs {
   float *lse;
   int64_t q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, v_sb, v_sh, v_ss, o_sb, o_sh, o_ss;
   const int32_t *items, *counters, *ent_kt, *ent_page;
+  int32_t *queue;  // this call's kQueuesPerSet work-queue counters
   const uint32_t *ent_live;
   const HeadMeta *hm;
   float *part_o, *part_lse;
   int64_t Sq, Skv, off, nqt;
-  int32_t Hq, Hkv, G, tq, tr, pack, causal, paged, P;
+  int32_t Hq, Hkv, G, tq, tr, pack, causal, paged, P, sched;
   float scale_log2;  // softmax scale * log2(e)
 };
 

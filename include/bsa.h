@@ -155,8 +155,11 @@ void bsa_lut_free(bsa_lut_t lut);
  * The call blocks once, on one small device-to-host read of the mask
  * features; all other planning work is queued on the stream, so the plan is
  * ready for any work queued on the same stream afterwards. The plan owns its
- * device memory, is immutable, and can be used by any number of bsa_forward
- * calls with matching tensors; free it with bsa_plan_free. */
+ * device memory and can be used by any number of bsa_forward calls with
+ * matching tensors; its tile lists are immutable, and each forward call takes
+ * its own set of work-queue counters from a ring of 64 held by the plan, so
+ * up to 64 calls on one plan may be in flight at once (on any streams). Free
+ * it with bsa_plan_free. */
 bsa_status bsa_plan(const bsa_problem *problem, const uint8_t *mask, const int32_t *page_table,
                     bsa_lut_t lut, void *stream, bsa_plan_t *out);
 
@@ -165,7 +168,9 @@ bsa_status bsa_plan(const bsa_problem *problem, const uint8_t *mask, const int32
  * bsa_tensor, in the plan's dtype; lse: device pointer, fp32 [batch][Hq][Sq].
  * Every O row and LSE entry is written exactly once (empty rows included), so
  * O need not be cleared. Queued on stream; never synchronises. O and LSE must
- * not overlap Q, K or V. */
+ * not overlap Q, K or V. Work items are taken from per-XCD queues in the
+ * order the plan's schedule gives, so which workgroup computes a row varies
+ * from call to call; the values written do not. */
 bsa_status bsa_forward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k,
                        const bsa_tensor *v, bsa_tensor *o, float *lse, void *stream);
 
