@@ -6,6 +6,12 @@ attention kernel and, when rows are split, the combine kernel) on one batch of
 seeded synthetic inputs already resident in HBM. The metric counts only the
 logical blocks the mask selects: 4 * bq * bk * D FLOPs per selected block.
 
+Plan and forward of a request run back to back on one stream. With
+``--pipeline`` the line also reports requests pipelined as a serving runtime
+could run them (the plan of request i+1 built on a second stream while the
+forward of request i runs, each forward waiting for its plan through an
+event); every step still plans and runs its request in full.
+
 Prints one JSON line. ``--gpus N`` with N > 1 exits: this path runs on one GPU.
 """
 from __future__ import annotations
@@ -144,6 +150,8 @@ def main():
     ap.add_argument("--workload", default="video_dit")
     ap.add_argument("--lut", default=None, help="regime table (default: the packaged gfx950 table)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="also time requests with the next plan overlapping the current forward")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run three device copies of a 1 GiB tensor (1 GiB read and 1 GiB "
                          "written per launch), to scale HBM byte counters")
@@ -176,15 +184,37 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty((w.batch, w.hq, w.sq), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
+    plan_stream = torch.cuda.Stream()
 
-    def step(ev=None):
-        p = bsa.plan(prob, mask, table, lut)
+    def step(ev=None, serial=True):
+        if serial:
+            p = bsa.plan(prob, mask, table, lut, stream=stream)
+        else:
+            p = bsa.plan(prob, mask, table, lut, stream=plan_stream)
+            ready = torch.cuda.Event()
+            ready.record(plan_stream)
+            stream.wait_event(ready)
         if ev is not None:
             ev[0].record(stream)
-        p.forward(q, k, v, o, lse)
+        p.forward(q, k, v, o, lse, stream=stream)
         if ev is not None:
             ev[1].record(stream)
         return p
+
+    def timed(serial):
+        """(ms per step, per-forward HIP-event ms) over args.steps requests."""
+        events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+        plans = []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            plans.append(step(events[i], serial))
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for p in plans:
+            p.free()
+        return (t1 - t0) * 1e3 / args.steps, [a.elapsed_time(b) for a, b in events]
 
     p0 = step()
     stats = p0.stats()
@@ -195,20 +225,9 @@ def main():
         torch.cuda.synchronize()
         p.free()
 
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    plans = []
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        plans.append(step(events[i]))
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for p in plans:
-        p.free()
-    fwd_ms = [a.elapsed_time(b) for a, b in events]
-    ms_step = (t1 - t0) * 1e3 / args.steps
+    ms_step, fwd_ms = timed(True)
     fwd_avg = float(np.mean(fwd_ms))
+    ms_pipe = timed(False)[0] if args.pipeline else None
 
     # Plan-only timing (the planner's own cost, one feature readback included).
     torch.cuda.synchronize()
@@ -232,6 +251,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_pipelined": round(ms_pipe, 4) if ms_pipe is not None else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

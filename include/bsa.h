@@ -154,7 +154,8 @@ void bsa_lut_free(bsa_lut_t lut);
  *   stream      stream for the planning kernels.
  * The call blocks once, on one small device-to-host read of the mask
  * features; all other planning work is queued on the stream, so the plan is
- * ready for any work queued on the same stream afterwards. The plan owns its
+ * ready for any work queued on the same stream afterwards (work on another
+ * stream must first wait for an event recorded on this one). The plan owns its
  * device memory and can be used by any number of bsa_forward calls with
  * matching tensors; its tile lists are immutable, and each forward call takes
  * its own set of work-queue counters from a ring of 64 held by the plan, so
