@@ -209,7 +209,13 @@ def main():
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
-            plans.append(step(events[i], serial))
+            p = step(events[i], serial)
+            if serial:
+                # Freed in stream order: the next plan on this stream reuses
+                # the memory only after this forward has run.
+                p.free()
+            else:
+                plans.append(p)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         for p in plans:
@@ -221,9 +227,8 @@ def main():
     p0.free()
     eff_flops = stats["effective_flops"]
     for _ in range(args.warmup):
-        p = step()
-        torch.cuda.synchronize()
-        p.free()
+        step().free()
+    torch.cuda.synchronize()
 
     ms_step, fwd_ms = timed(True)
     fwd_avg = float(np.mean(fwd_ms))

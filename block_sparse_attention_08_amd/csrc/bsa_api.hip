@@ -162,60 +162,42 @@ static bsa_status check_problem(const bsa_problem *p, const uint8_t *mask, const
 }
 
 // ---------------------------------------------------------------------------
-// Cache of freed plan allocations. A block is reused for a request of at
-// most its size and at least half of it; at most kCacheBlocks blocks and
-// kCacheBytes bytes are kept per device; anything else goes back to hipFree.
+// Plan memory comes from the device's default stream-ordered pool
+// (hipMallocAsync / hipFreeAsync on the plan's stream). A block freed by one
+// plan is reused by the next plan built on the same stream without waiting:
+// stream order already places the new plan's kernels after the work that
+// used the old one. The pool keeps freed memory (release threshold raised
+// once per device) instead of returning it to the driver at each
+// synchronisation.
 // ---------------------------------------------------------------------------
 namespace {
-struct CachedBlock {
-  void *ptr;
-  size_t bytes;
-  int device;
-};
-constexpr int kCacheBlocks = 16;
-constexpr size_t kCacheBytes = size_t(8) << 30;
-std::mutex g_cache_mu;
-std::vector<CachedBlock> g_cache;
+std::mutex g_pool_mu;
+std::vector<int> g_pool_ready;  // devices whose pool threshold is set
 }  // namespace
 
-hipError_t cached_alloc(void **ptr, size_t bytes, int device) {
+hipError_t plan_alloc(void **ptr, size_t bytes, int device, hipStream_t stream) {
   {
-    std::lock_guard<std::mutex> lk(g_cache_mu);
-    int best = -1;
-    for (int i = 0; i < (int)g_cache.size(); ++i) {
-      const CachedBlock &c = g_cache[i];
-      if (c.device == device && c.bytes >= bytes && c.bytes <= 2 * bytes + (1 << 20) &&
-          (best < 0 || c.bytes < g_cache[best].bytes))
-        best = i;
-    }
-    if (best >= 0) {
-      *ptr = g_cache[best].ptr;
-      g_cache.erase(g_cache.begin() + best);
-      return hipSuccess;
+    std::lock_guard<std::mutex> lk(g_pool_mu);
+    if (std::find(g_pool_ready.begin(), g_pool_ready.end(), device) == g_pool_ready.end()) {
+      hipMemPool_t pool;
+      if (hipDeviceGetDefaultMemPool(&pool, device) == hipSuccess) {
+        uint64_t keep = UINT64_MAX;
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+      }
+      g_pool_ready.push_back(device);
     }
   }
-  return hipMalloc(ptr, bytes);
+  return hipMallocAsync(ptr, bytes, stream);
 }
 
-void cached_free(void *ptr, size_t bytes, int device) {
-  if (!ptr) return;
-  {
-    std::lock_guard<std::mutex> lk(g_cache_mu);
-    size_t held = 0, count = 0;
-    for (const CachedBlock &c : g_cache)
-      if (c.device == device) held += c.bytes, ++count;
-    if (count < kCacheBlocks && held + bytes <= kCacheBytes) {
-      g_cache.push_back(CachedBlock{ptr, bytes, device});
-      return;
-    }
-  }
-  (void)hipFree(ptr);
+void plan_release(void *ptr, hipStream_t stream) {
+  if (ptr) (void)hipFreeAsync(ptr, stream);
 }
 
 static void free_plan(bsa_plan_s *p) {
   if (!p) return;
-  cached_free(p->pre, p->pre_bytes, p->device);
-  cached_free(p->arena, p->arena_bytes, p->device);
+  plan_release(p->pre, p->stream);
+  plan_release(p->arena, p->stream);
   delete p;
 }
 
@@ -347,7 +329,7 @@ bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *p
                            aligned(sizeof(HeadMeta) * P.Hq) +
                            aligned((size_t)P.nbm * P.Hkv * std::max<int64_t>(P.unkb, 1)) +
                            aligned(sizeof(int32_t) * 2 * std::max<int64_t>(P.nbm * rows_per_bm, 1));
-  if (cached_alloc(&P.pre, pre_bytes, P.device) != hipSuccess) {
+  if (plan_alloc(&P.pre, pre_bytes, P.device, P.stream) != hipSuccess) {
     free_plan(p);
     return fail(BSA_ERR_OUT_OF_MEMORY, "device allocation of plan header failed");
   }
@@ -448,7 +430,7 @@ bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *p
   for (auto &pt : parts) total += aligned(pt.second);
   const size_t scratch = plan_scratch_bytes(P);
   total += scratch;
-  if (cached_alloc(&P.arena, total, P.device) != hipSuccess)
+  if (plan_alloc(&P.arena, total, P.device, P.stream) != hipSuccess)
     return bail(fail(BSA_ERR_OUT_OF_MEMORY, "device allocation of " + std::to_string(total) + " plan bytes failed"));
   P.arena_bytes = total;
   uint8_t *ap = (uint8_t *)P.arena;

@@ -89,10 +89,10 @@ struct AttnArgs {
 // Error reporting (thread-local message).
 bsa_status fail(bsa_status s, const std::string &msg);
 
-// Device allocations of plans go through a small per-device cache of freed
-// blocks, so repeated requests do not pay hipMalloc / hipFree each time.
-hipError_t cached_alloc(void **ptr, size_t bytes, int device);
-void cached_free(void *ptr, size_t bytes, int device);
+// Device allocations of plans: stream-ordered (the device's default pool), on
+// the plan's stream, so repeated requests reuse freed blocks without waiting.
+hipError_t plan_alloc(void **ptr, size_t bytes, int device, hipStream_t stream);
+void plan_release(void *ptr, hipStream_t stream);
 
 // Planner entry points (bsa_planner.hip). Each returns BSA_OK or BSA_ERR_HIP.
 bsa_status plan_features(Plan &p, const uint8_t *mask, const int32_t *page_table);
