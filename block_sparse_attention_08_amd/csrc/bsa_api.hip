@@ -173,6 +173,36 @@ static bsa_status check_problem(const bsa_problem *p, const uint8_t *mask, const
 namespace {
 std::mutex g_pool_mu;
 std::vector<int> g_pool_ready;  // devices whose pool threshold is set
+
+// Pinned host blocks for the planner's read-back, kept for reuse (one per
+// concurrently planning thread at most).
+std::mutex g_pin_mu;
+std::vector<std::pair<void *, size_t>> g_pin_free;
+
+struct PinnedBuf {
+  void *p = nullptr;
+  size_t n = 0;
+  explicit PinnedBuf(size_t bytes) {
+    {
+      std::lock_guard<std::mutex> lk(g_pin_mu);
+      for (size_t i = 0; i < g_pin_free.size(); ++i)
+        if (g_pin_free[i].second >= bytes) {
+          p = g_pin_free[i].first, n = g_pin_free[i].second;
+          g_pin_free.erase(g_pin_free.begin() + i);
+          return;
+        }
+    }
+    n = std::max<size_t>(bytes, size_t(64) << 10);
+    if (hipHostMalloc(&p, n, hipHostMallocDefault) != hipSuccess) p = nullptr, n = 0;
+  }
+  ~PinnedBuf() {
+    if (!p) return;
+    std::lock_guard<std::mutex> lk(g_pin_mu);
+    g_pin_free.emplace_back(p, n);
+  }
+  PinnedBuf(const PinnedBuf &) = delete;
+  PinnedBuf &operator=(const PinnedBuf &) = delete;
+};
 }  // namespace
 
 hipError_t plan_alloc(void **ptr, size_t bytes, int device, hipStream_t stream) {
@@ -324,8 +354,8 @@ bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *p
   const size_t feat_bytes = sizeof(int64_t) * 4 * P.nbm * P.Hq;
   int64_t rows_per_bm = 0;
   for (int h = 0; h < P.Hq; ++h) rows_per_bm += cdiv(P.Sq, P.bq[h]);
-  const size_t pre_bytes = aligned(sizeof(int32_t) * CNT_N) +
-                           aligned(sizeof(int32_t) * kQueuesPerSet * kQueueSets) + aligned(feat_bytes) +
+  const size_t pre_bytes = aligned(sizeof(int32_t) * CNT_N) + aligned(feat_bytes) +
+                           aligned(sizeof(int32_t) * kQueuesPerSet * kQueueSets) +
                            aligned(sizeof(HeadMeta) * P.Hq) +
                            aligned((size_t)P.nbm * P.Hkv * std::max<int64_t>(P.unkb, 1)) +
                            aligned(sizeof(int32_t) * 2 * std::max<int64_t>(P.nbm * rows_per_bm, 1));
@@ -335,12 +365,13 @@ bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *p
   }
   P.pre_bytes = pre_bytes;
   uint8_t *pb = (uint8_t *)P.pre;
+  // Counters and features are adjacent: the one read-back copies both.
   P.counters = (int32_t *)pb;
   pb += aligned(sizeof(int32_t) * CNT_N);
-  P.queues = (int32_t *)pb;
-  pb += aligned(sizeof(int32_t) * kQueuesPerSet * kQueueSets);
   P.feat_dev = (unsigned long long *)pb;
   pb += aligned(feat_bytes);
+  P.queues = (int32_t *)pb;
+  pb += aligned(sizeof(int32_t) * kQueuesPerSet * kQueueSets);
   P.hmeta = (HeadMeta *)pb;
   pb += aligned(sizeof(HeadMeta) * P.Hq);
   P.uni_bits = pb;
@@ -353,15 +384,18 @@ bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *p
   if (hipMemsetAsync(P.counters, 0, sizeof(int32_t) * CNT_N, P.stream) != hipSuccess)
     return bail(fail(BSA_ERR_HIP, "hipMemsetAsync failed"));
   if (bsa_status s = plan_features(P, mask, page_table)) return bail(s);
-  std::vector<int64_t> host(feat_bytes / 8 + CNT_N);
-  if (hipMemcpyAsync(host.data(), P.feat_dev, feat_bytes, hipMemcpyDeviceToHost, P.stream) != hipSuccess ||
-      hipMemcpyAsync(host.data() + feat_bytes / 8, P.counters, sizeof(int32_t) * CNT_N,
-                     hipMemcpyDeviceToHost, P.stream) != hipSuccess ||
+  // The one read-back of planning: counters and mask features, into pinned
+  // host memory (a direct DMA, no staging through pageable memory).
+  const size_t head_bytes = aligned(sizeof(int32_t) * CNT_N) + feat_bytes;
+  PinnedBuf pin(head_bytes);
+  if (!pin.p) return bail(fail(BSA_ERR_OUT_OF_MEMORY, "pinned host allocation failed"));
+  if (hipMemcpyAsync(pin.p, P.counters, head_bytes, hipMemcpyDeviceToHost, P.stream) != hipSuccess ||
       hipStreamSynchronize(P.stream) != hipSuccess)
     return bail(fail(BSA_ERR_HIP, std::string("reading mask features failed: ") +
                                       hipGetErrorString(hipGetLastError())));
-  P.feat.assign(host.begin(), host.begin() + feat_bytes / 8);
-  const int32_t *hc = (const int32_t *)(host.data() + feat_bytes / 8);
+  const int32_t *hc = (const int32_t *)pin.p;
+  const int64_t *hf = (const int64_t *)((const uint8_t *)pin.p + aligned(sizeof(int32_t) * CNT_N));
+  P.feat.assign(hf, hf + feat_bytes / 8);
   if (hc[CNT_BADPAGE]) return bail(fail(BSA_ERR_INVALID_ARG, "page table entry outside [0, num_pages)"));
 
   // ---- aggregates and regime ----

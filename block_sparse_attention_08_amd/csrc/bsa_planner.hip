@@ -464,6 +464,19 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
+// Live-bit geometry of each head for tiles of tq x tk: query sub-blocks of
+// min(bq, tq) rows (one sub-block in union mode, whose bits are per key
+// sub-block only), key sub-blocks of min(bk, tk) keys, mk key sub-blocks per
+// tile. Block sizes are powers of two.
+__global__ void k_live_geom(HeadMeta *hm, int Hq, int tq, int tk, int uni) {
+  for (int h = threadIdx.x; h < Hq; h += blockDim.x) {
+    const int aq = min(hm[h].bq, tq), ak = min(hm[h].bk, tk);
+    hm[h].lq = uni ? 30 : __ffs(aq) - 1;
+    hm[h].lk = __ffs(ak) - 1;
+    hm[h].mk = tk / ak;
+  }
+}
+
 bsa_status plan_features(Plan &p, const uint8_t *mask, const int32_t *page_table) {
   hipStream_t s = p.stream;
   int64_t rows_per_bm = 0, mask_bstride = 0;
@@ -527,18 +540,11 @@ bsa_status plan_build(Plan &p, const uint8_t *mask, const int32_t *page_table, v
   if ((size_t)(sp - (uint8_t *)scratch) > scratch_bytes)
     return fail(BSA_ERR_HIP, "planner scratch too small");
 
-  // Live-bit decoding per head now that the tile shape is known: query
-  // sub-blocks of min(bq, Tq) rows (one sub-block in union mode, whose bits
-  // are per key sub-block only), key sub-blocks of min(bk, Tk) keys.
-  for (int h = 0; h < p.Hq; ++h) {
-    HeadMeta &m = p.hmeta_host[h];
-    const int aq = std::min(p.bq[h], p.rg.tq), ak = std::min(p.bk[h], p.rg.tk);
-    m.lq = p.uni ? 30 : __builtin_ctz(aq);
-    m.lk = __builtin_ctz(ak);
-    m.mk = p.rg.tk / ak;
-  }
-  HIP_TRY(hipMemcpyAsync(p.hmeta, p.hmeta_host.data(), sizeof(HeadMeta) * p.Hq,
-                         hipMemcpyHostToDevice, s));
+  // Live-bit decoding per head now that the tile shape is known (written on
+  // the device, so no host upload sits between the read-back and the
+  // mapping kernels).
+  hipLaunchKernelGGL(k_live_geom, dim3(1), dim3(kThreads), 0, s, p.hmeta, p.Hq, p.rg.tq, p.rg.tk,
+                     (int)p.uni);
 
   MapArgs m{};
   m.mask = mask, m.U = p.uni_bits, m.hm = p.hmeta, m.page_table = page_table;
