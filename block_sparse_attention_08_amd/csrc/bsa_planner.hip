@@ -311,8 +311,11 @@ __global__ void k_scan_apply(const int32_t *in, int64_t n, const int32_t *__rest
 }
 
 // Whole scan in one workgroup (small arrays): chunks of kScanBlock in order,
-// carrying the running total. in and out may be the same array.
-__global__ void k_scan_single(const int32_t *in, int64_t n, int32_t *out) {
+// carrying the running total. in and out may be the same array. Workgroup g
+// scans the g-th of gridDim.x arrays laid out `stride` elements apart.
+__global__ void k_scan_single(const int32_t *in, int64_t n, int32_t *out, int64_t stride) {
+  in += blockIdx.x * stride;
+  out += blockIdx.x * stride;
   int carry = 0;
   for (int64_t base = 0; base < n || base == 0; base += kScanBlock) {
     int v[4], s = 0;
@@ -338,7 +341,7 @@ constexpr int64_t kSingleScanMax = 1 << 16;
 
 bsa_status scan(const int32_t *in, int64_t n, int32_t *out, int32_t *bsum, hipStream_t s) {
   if (n <= kSingleScanMax) {
-    hipLaunchKernelGGL(k_scan_single, dim3(1), dim3(kThreads), 0, s, in, n, out);
+    hipLaunchKernelGGL(k_scan_single, dim3(1), dim3(kThreads), 0, s, in, n, out, (int64_t)0);
     HIP_TRY(hipGetLastError());
     return BSA_OK;
   }
@@ -572,9 +575,15 @@ bsa_status plan_build(Plan &p, const uint8_t *mask, const int32_t *page_table, v
   ra.split = p.rg.split;
   if (p.nrows > 0) hipLaunchKernelGGL(k_rows, dim3(grid_for(p.nrows)), dim3(kThreads), 0, s, ra);
   int32_t *item_off = off, *slot_off = off + (p.nrows + 1), *comb_off = off + 2 * (p.nrows + 1);
-  if (bsa_status st = scan(ra.cnt_items, p.nrows, item_off, bsum, s)) return st;
-  if (bsa_status st = scan(ra.cnt_slots, p.nrows, slot_off, bsum, s)) return st;
-  if (bsa_status st = scan(ra.cnt_comb, p.nrows, comb_off, bsum, s)) return st;
+  if (p.nrows <= kSingleScanMax) {
+    // The three row counts (items, partial slots, combine records) in one launch.
+    hipLaunchKernelGGL(k_scan_single, dim3(3), dim3(kThreads), 0, s, ra.cnt_items, p.nrows, item_off,
+                       p.nrows + 1);
+  } else {
+    if (bsa_status st = scan(ra.cnt_items, p.nrows, item_off, bsum, s)) return st;
+    if (bsa_status st = scan(ra.cnt_slots, p.nrows, slot_off, bsum, s)) return st;
+    if (bsa_status st = scan(ra.cnt_comb, p.nrows, comb_off, bsum, s)) return st;
+  }
   int4 *dst = p.rg.sched == 1 ? raw_items : (int4 *)p.items;
   if (p.nrows > 0)
     hipLaunchKernelGGL(k_items, dim3(grid_for(p.nrows)), dim3(kThreads), 0, s, p.row_ent, item_off,
