@@ -184,7 +184,10 @@ bsa_status bsa_plan_export(bsa_plan_t plan, void *host_buf, size_t *bytes);
 /* Plan statistics. Synchronises with the plan's stream. */
 bsa_status bsa_plan_stats(bsa_plan_t plan, bsa_plan_info *out);
 
-/* Release a plan after all work using it has completed. NULL is ignored. */
+/* Release a plan. Its device memory is returned in stream order on the plan's
+ * stream, so the call may follow the last bsa_forward queued on that stream
+ * directly; forward calls queued on other streams must have completed (or be
+ * ordered before the plan's stream by an event). NULL is ignored. */
 void bsa_plan_free(bsa_plan_t plan);
 
 #ifdef __cplusplus
