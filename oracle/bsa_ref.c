@@ -631,3 +631,114 @@ int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_tabl
   free(row_ent), free(items), free(comb);
   return rc;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Block selection from pooled scores (the mask producer)                    */
+/* ------------------------------------------------------------------------ */
+/*
+ * The pages name the mechanism, not a formula: hierarchical sparse attention
+ * picks the top-k key/value blocks by coarse attention scores (DashAttention
+ * page, summary of NSA and InfLLMv2); CompactAttention (summary) treats the
+ * block mask as a KV selection signal for chunked prefill; Sol-Attn (summary)
+ * thresholds per query. The coarse score here is the dot product of the mean
+ * of a query block's rows with the mean of a key block's rows, and each
+ * query block keeps its best key blocks among the causally feasible ones.
+ *
+ * Floating point decides which blocks are kept, so the arithmetic is fixed
+ * and done in fp32, in this order, on both sides:
+ *   mean[d] = (x_first[d] + x_second[d] + ... + x_last[d]) / n   (rows in
+ *             ascending order, one fp32 addition each, one fp32 division);
+ *   score   = fma(qm[D-1], km[D-1], ... fma(qm[1], km[1], fma(qm[0], km[0], 0)))
+ *             (d ascending, fused multiply-add, no scale: a positive scale
+ *             does not change the order).
+ * Key blocks are ranked by score, higher first, ties to the lower block
+ * index, under the total order of fp32 bit patterns (-NaN < -inf < ... <
+ * +inf < +NaN). A query block with n candidates keeps min(top_k, n) of them
+ * when top_k > 0, else ceil(n * keep_tenths / 10).
+ */
+
+/* fp32 value of element idx (bf16 bit pattern or fp32). */
+static float load_f32(const void *base, int dtype, int64_t idx) {
+  if (dtype == 0) {
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return f;
+  }
+  return ((const float *)base)[idx];
+}
+
+/* Order-preserving map of an fp32 bit pattern to an unsigned integer. */
+static uint32_t order_key(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+typedef struct {
+  uint32_t key;
+  int32_t kb;
+} cand_t;
+
+static int cand_cmp(const void *a, const void *b) {
+  const cand_t *x = (const cand_t *)a, *y = (const cand_t *)b;
+  if (x->key != y->key) return x->key > y->key ? -1 : 1;  /* higher score first */
+  return x->kb < y->kb ? -1 : (x->kb > y->kb);             /* then lower block */
+}
+
+int ref_select(const ref_problem *p, const int32_t *page_table, const void *q, const void *k,
+               int32_t keep_tenths, int32_t top_k, uint8_t *mask) {
+  if (check_problem(p) || p->mask_broadcast || !mask) return -1;
+  if (top_k <= 0 && (keep_tenths < 1 || keep_tenths > 10)) return -1;
+  const int gs = p->hq / p->hkv;
+  const int D = p->d;
+  int64_t *moff = mask_offsets(p);
+  float *qm = (float *)malloc(sizeof(float) * D);
+  for (int b = 0; b < p->batch; ++b)
+    for (int h = 0; h < p->hq; ++h) {
+      const int g = h / gs;
+      const int64_t bq = p->bq[h], bk = p->bk[h];
+      const int64_t nqb = ceil_div(p->sq, bq), nkb = ceil_div(p->skv, bk);
+      /* pooled key blocks of (b, g) at this head's key block size */
+      float *km = (float *)malloc(sizeof(float) * (size_t)(nkb > 0 ? nkb : 1) * D);
+      for (int64_t kb = 0; kb < nkb; ++kb) {
+        const int64_t j0 = kb * bk, j1 = (kb + 1) * bk < p->skv ? (kb + 1) * bk : p->skv;
+        for (int d = 0; d < D; ++d) {
+          float s = 0.0f;
+          for (int64_t j = j0; j < j1; ++j) s = s + load_f32(k, p->dtype, kv_index(p, page_table, b, g, j) + d);
+          km[kb * D + d] = s / (float)(j1 - j0);
+        }
+      }
+      cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (size_t)(nkb > 0 ? nkb : 1));
+      for (int64_t qb = 0; qb < nqb; ++qb) {
+        const int64_t i0 = qb * bq, i1 = (qb + 1) * bq < p->sq ? (qb + 1) * bq : p->sq;
+        for (int d = 0; d < D; ++d) {
+          float s = 0.0f;
+          for (int64_t i = i0; i < i1; ++i)
+            s = s + load_f32(q, p->dtype, (((int64_t)b * p->hq + h) * p->sq + i) * D + d);
+          qm[d] = s / (float)(i1 - i0);
+        }
+        uint8_t *row = mask + moff[b * p->hq + h] + qb * nkb;
+        memset(row, 0, (size_t)nkb);
+        int64_t n = 0;
+        for (int64_t kb = 0; kb < nkb; ++kb) {
+          /* causally feasible: the block's first key is not after the block's
+             last query position plus the offset */
+          if (p->causal && kb * bk > (i1 - 1) + p->causal_offset) continue;
+          float sc = 0.0f;
+          for (int d = 0; d < D; ++d) sc = fmaf(qm[d], km[kb * D + d], sc);
+          c[n].key = order_key(sc);
+          c[n].kb = (int32_t)kb;
+          ++n;
+        }
+        qsort(c, (size_t)n, sizeof(cand_t), cand_cmp);
+        const int64_t keep = top_k > 0 ? (top_k < n ? top_k : n) : (n * keep_tenths + 9) / 10;
+        for (int64_t t = 0; t < keep; ++t) row[c[t].kb] = 1;
+      }
+      free(c);
+      free(km);
+    }
+  free(qm);
+  free(moff);
+  return 0;
+}

@@ -69,6 +69,16 @@ int ref_features(const ref_problem *p, const uint8_t *mask, int64_t *out);
 int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_table,
              const char *lut_text, const int32_t *force, uint8_t *image, size_t *bytes);
 
+/* Block selection from pooled scores (mask producer): for every batch b,
+ * query head h and query block, the mean of the block's query rows is scored
+ * against the mean of every causally feasible key block of h's kv group (fp32,
+ * fixed order: see bsa_ref.c), and the best min(top_k, n) blocks (top_k > 0)
+ * or ceil(n * keep_tenths / 10) blocks are kept, ties to the lower block.
+ * Writes the uint8 mask in the layout ref_forward reads, one mask per batch
+ * (mask_broadcast must be 0). Returns 0, or -1 for invalid arguments. */
+int ref_select(const ref_problem *p, const int32_t *page_table, const void *q, const void *k,
+               int32_t keep_tenths, int32_t top_k, uint8_t *mask);
+
 #ifdef __cplusplus
 }
 #endif

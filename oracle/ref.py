@@ -58,6 +58,9 @@ def lib():
         L.ref_plan.argtypes = [P(RefProblem), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_char_p,
                                ctypes.c_void_p, ctypes.c_void_p, P(ctypes.c_size_t)]
         L.ref_plan.restype = ctypes.c_int
+        L.ref_select.argtypes = [P(RefProblem), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+        L.ref_select.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -158,3 +161,20 @@ def plan(w, lut_text=None, force=None) -> bytes:
     if rc:
         raise ValueError(f"ref_plan failed ({rc})")
     return buf.tobytes()
+
+
+def select(w, q, k, keep_tenths: int = 1, top_k: int = 0) -> np.ndarray:
+    """Oracle block selection (mask producer) for the shapes of workload w
+    (its own mask is ignored; mask_broadcast must be off). Returns the uint8
+    mask, head-concatenated per batch, as ref_forward reads it."""
+    P = _Prob(w)
+    qa, ka = _raw(q, w.dtype), _raw(k, w.dtype)
+    nb = sum(-(-w.sq // w.bq[h]) * -(-w.skv // w.bk[h]) for h in range(w.hq))
+    out = np.zeros(max(w.batch * nb, 1), np.uint8)
+    s = RefProblem.from_buffer_copy(P.s)
+    s.mask_broadcast = 0
+    rc = lib().ref_select(ctypes.byref(s), P.table_ptr(), qa.ctypes.data, ka.ctypes.data,
+                          int(keep_tenths), int(top_k), out.ctypes.data)
+    if rc:
+        raise ValueError(f"ref_select rejected the problem ({rc})")
+    return out[: w.batch * nb]
