@@ -59,6 +59,10 @@ class PlanInfo(ctypes.Structure):
                [("effective_flops", ctypes.c_double), ("tile_live_subblocks", ctypes.c_int64)]
 
 
+class SelectParams(ctypes.Structure):
+    _fields_ = [("keep_tenths", ctypes.c_int32), ("top_k", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -84,8 +88,9 @@ def lib() -> ctypes.CDLL:
         L.bsa_plan_stats.argtypes = [vp, P(PlanInfo)]
         L.bsa_plan_free.argtypes = [vp]
         L.bsa_plan_free.restype = None
+        L.bsa_select_blocks.argtypes = [P(Problem), P(SelectParams), P(Tensor), P(Tensor), vp, vp, vp]
         for f in ("bsa_lut_load", "bsa_lut_parse", "bsa_plan", "bsa_forward", "bsa_plan_export",
-                  "bsa_plan_stats"):
+                  "bsa_plan_stats", "bsa_select_blocks"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -237,3 +242,32 @@ def lut_load(path: Optional[str] = DEFAULT_LUT) -> Lut:
 
 def lut_parse(text: str) -> Lut:
     return Lut.parse(text)
+
+
+def mask_size(problem: dict) -> int:
+    """Bytes of the per-batch logical mask of a problem (bsa_plan's layout)."""
+    sq, skv = int(problem["seqlen_q"]), int(problem["seqlen_kv"])
+    per = sum(-(-sq // int(bq)) * -(-skv // int(bk))
+              for bq, bk in zip(problem["block_q"], problem["block_k"]))
+    nb = 1 if problem.get("mask_batch_broadcast", 0) else int(problem["batch"])
+    return nb * per
+
+
+def select_blocks(problem: dict, q, k, page_table=None, keep_tenths: int = 1, top_k: int = 0,
+                  out=None, stream=None):
+    """bsa_select_blocks: the logical mask (uint8 torch tensor on q's device)
+    chosen from pooled query/key block scores; keep_tenths of each query
+    block's causal candidates, or top_k of them when top_k > 0."""
+    import torch
+    s, keep = make_problem(problem)
+    n = mask_size(problem)
+    if out is None:
+        out = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)[:n]
+    prm = SelectParams(int(keep_tenths), int(top_k))
+    paged = bool(problem.get("paged", 0))
+    tq, tk = _tensor(q), _tensor(k, paged)
+    _check(lib().bsa_select_blocks(ctypes.byref(s), ctypes.byref(prm), ctypes.byref(tq),
+                                   ctypes.byref(tk),
+                                   page_table.data_ptr() if page_table is not None else None,
+                                   out.data_ptr() if n else None, _stream_handle(stream)))
+    return out

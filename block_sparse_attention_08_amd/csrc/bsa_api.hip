@@ -513,6 +513,25 @@ bsa_status bsa_forward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k
   return attention_launch(P, a, (hipStream_t)stream);
 }
 
+bsa_status bsa_select_blocks(const bsa_problem *problem, const bsa_select_params *params,
+                             const bsa_tensor *q, const bsa_tensor *k, const int32_t *page_table,
+                             uint8_t *mask, void *stream) {
+  if (!params || !q || !k) return fail(BSA_ERR_INVALID_ARG, "NULL params or tensor");
+  if (bsa_status st = check_problem(problem, mask, page_table)) return st;
+  if (problem->mask_batch_broadcast)
+    return fail(BSA_ERR_INVALID_ARG, "block selection writes one mask per batch (mask_batch_broadcast = 0)");
+  if (params->top_k < 0 || (params->top_k == 0 && (params->keep_tenths < 1 || params->keep_tenths > 10)))
+    return fail(BSA_ERR_INVALID_ARG, "keep_tenths must be in [1, 10] when top_k is 0; top_k must be >= 0");
+  const bool any = problem->seqlen_q > 0;
+  if (any && (!q->data || (problem->seqlen_kv > 0 && !k->data)))
+    return fail(BSA_ERR_INVALID_ARG, "NULL Q or K data");
+  if (q->stride_b < 0 || q->stride_h < 0 || q->stride_s < 0 || k->stride_b < 0 || k->stride_h < 0 ||
+      k->stride_s < 0)
+    return fail(BSA_ERR_INVALID_ARG, "negative stride");
+  return select_blocks(*problem, params->keep_tenths, params->top_k, *q, *k, page_table, mask,
+                       (hipStream_t)stream);
+}
+
 bsa_status bsa_plan_export(bsa_plan_t plan, void *host_buf, size_t *bytes) {
   if (!plan || !bytes) return fail(BSA_ERR_INVALID_ARG, "NULL plan or bytes");
   const Plan &P = *plan;

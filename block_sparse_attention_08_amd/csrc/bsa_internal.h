@@ -100,6 +100,10 @@ bsa_status plan_build(Plan &p, const uint8_t *mask, const int32_t *page_table, v
                       size_t scratch_bytes);
 size_t plan_scratch_bytes(const Plan &p);
 
+// Block selection from pooled scores (bsa_select.hip).
+bsa_status select_blocks(const bsa_problem &pr, int keep_tenths, int top_k, const bsa_tensor &q,
+                         const bsa_tensor &k, const int32_t *page_table, uint8_t *mask, hipStream_t s);
+
 // Attention entry point (bsa_attention.hip).
 bsa_status attention_launch(const Plan &p, const AttnArgs &a, hipStream_t stream);
 

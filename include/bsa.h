@@ -184,6 +184,38 @@ bsa_status bsa_plan_export(bsa_plan_t plan, void *host_buf, size_t *bytes);
 /* Plan statistics. Synchronises with the plan's stream. */
 bsa_status bsa_plan_stats(bsa_plan_t plan, bsa_plan_info *out);
 
+/* Parameters of block selection. */
+typedef struct {
+  int32_t keep_tenths; /* keep ceil(n * keep_tenths / 10) of a query block's n candidates (1..10) */
+  int32_t top_k;       /* > 0: keep min(top_k, n) candidates instead; 0: use keep_tenths */
+} bsa_select_params;
+
+/* Block selection from pooled scores: writes the logical mask that bsa_plan
+ * reads, from Q and K on the GPU. Hierarchical sparse attention selects the
+ * key/value blocks with the best coarse attention scores (DashAttention page,
+ * summary of NSA and InfLLMv2); CompactAttention (summary) treats the chunked-
+ * prefill block mask as a KV selection signal; Sol-Attn (summary) thresholds
+ * per query. Here, for batch b, query head h and query block qb, the coarse
+ * score of key block kb (of h's kv group) is the dot product of the mean of
+ * the query block's rows with the mean of the key block's rows; among the key
+ * blocks that are causally feasible (first key <= last query of qb +
+ * causal_kv_offset, or all blocks without causal masking) the best are kept
+ * (params), ties to the lower block. All of it is fp32 in a fixed order (row
+ * sums in ascending order, one division per mean, fused multiply-adds over d
+ * ascending), so the mask is reproducible bit for bit.
+ *   problem: shapes, block sizes, causal flag and offset, paging, dtype
+ *            (mask_batch_broadcast must be 0: one mask per batch).
+ *   q, k:    device tensors as for bsa_forward (k may be a paged pool read
+ *            through page_table; pool entries outside [0, num_pages) are not
+ *            followed).
+ *   mask:    device pointer, uint8 [batch][per head: nqb_h x nkb_h], every
+ *            byte written (0 or 1).
+ * Up to 64 query heads and 8192 key blocks per head. Queued on stream; uses
+ * scratch from the device's stream-ordered pool, returned in stream order. */
+bsa_status bsa_select_blocks(const bsa_problem *problem, const bsa_select_params *params,
+                             const bsa_tensor *q, const bsa_tensor *k, const int32_t *page_table,
+                             uint8_t *mask, void *stream);
+
 /* Release a plan. Its device memory is returned in stream order on the plan's
  * stream, so the call may follow the last bsa_forward queued on that stream
  * directly; forward calls queued on other streams must have completed (or be

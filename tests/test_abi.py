@@ -115,3 +115,33 @@ def test_default_lut_accepted_by_oracle(ref):
     from block_sparse_attention_08_amd import workloads as W
     w = W.random_problem(batch=1, hq=2, sq=128, skv=128, bq=64, bk=64, d=64, seed=1)
     ref.plan(w, lut_text=open(bsa.DEFAULT_LUT).read())
+
+
+def test_select_blocks_rejects_bad_arguments(L):
+    """Block selection checks its arguments before queueing anything."""
+    s, keep = bsa.make_problem(BASE)
+    t = bsa.Tensor(16, 0, 0, 0)
+    prm = bsa.SelectParams(1, 0)
+    assert L.bsa_select_blocks(ctypes.byref(s), None, ctypes.byref(t), ctypes.byref(t), None, 1,
+                               None) == 1
+    assert L.bsa_select_blocks(ctypes.byref(s), ctypes.byref(prm), ctypes.byref(t), ctypes.byref(t),
+                               None, None, None) == 1
+    assert "mask" in L.bsa_last_error().decode()
+    for bad in (bsa.SelectParams(0, 0), bsa.SelectParams(11, 0), bsa.SelectParams(1, -1)):
+        assert L.bsa_select_blocks(ctypes.byref(s), ctypes.byref(bad), ctypes.byref(t),
+                                   ctypes.byref(t), None, 1, None) == 1
+        assert "keep_tenths" in L.bsa_last_error().decode()
+    sb, keep2 = bsa.make_problem(dict(BASE, mask_batch_broadcast=1))
+    assert L.bsa_select_blocks(ctypes.byref(sb), ctypes.byref(prm), ctypes.byref(t), ctypes.byref(t),
+                               None, 1, None) == 1
+    assert "one mask per batch" in L.bsa_last_error().decode()
+    sp, keep3 = bsa.make_problem(dict(BASE, paged=1, page_size=64, pages_per_seq=4, num_pages=4))
+    assert L.bsa_select_blocks(ctypes.byref(sp), ctypes.byref(prm), ctypes.byref(t), ctypes.byref(t),
+                               None, 1, None) == 1
+    assert "page table" in L.bsa_last_error().decode()
+
+
+def test_mask_size_matches_layout():
+    p = dict(BASE, batch=3, block_q=[32, 64, 128, 64], block_k=[64, 128, 32, 64], seqlen_q=300,
+             seqlen_kv=500)
+    assert bsa.mask_size(p) == 3 * (10 * 8 + 5 * 4 + 3 * 16 + 5 * 8)
