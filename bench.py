@@ -49,6 +49,12 @@ def workload(name: str):
     return table[name]()
 
 
+# Workloads whose mask is chosen on the GPU in every step (bsa_select_blocks,
+# keeping this many tenths of each query block's causal candidates) from the
+# step's own Q and K, before the plan and the forward.
+SELECTED = {"chunked_prefill_selected": ("chunked_prefill", 1)}
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in ("bsa_attention.hip", "bsa_internal.h"):
@@ -166,6 +172,11 @@ def main():
     import block_sparse_attention_08_amd as bsa
 
     torch.cuda.set_device(0)
+    sel_keep = None
+    if args.workload in SELECTED:
+        base_name, sel_keep = SELECTED[args.workload]
+    else:
+        base_name = args.workload
     if args.calibrate_copy:
         x = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").normal_()
         y = torch.empty_like(x)
@@ -175,18 +186,24 @@ def main():
         print(json.dumps({"calibration": "device copy", "bytes_read": 1 << 30,
                           "bytes_written": 1 << 30, "launches": 3}), flush=True)
         return
-    w = workload(args.workload)
+    w = workload(base_name)
     q, k, v = w.make_qkv(device="cuda")
     mask = torch.from_numpy(np.ascontiguousarray(w.mask)).cuda()
     table = torch.from_numpy(np.ascontiguousarray(w.page_table)).cuda() if w.paged else None
     lut = bsa.Lut.load(args.lut or bsa.DEFAULT_LUT)
     prob = w.problem_dict()
+    if sel_keep is not None:
+        prob["mask_batch_broadcast"] = 0
+        mask = torch.empty(bsa.mask_size(prob), dtype=torch.uint8, device="cuda")
     o = torch.empty_like(q)
     lse = torch.empty((w.batch, w.hq, w.sq), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     plan_stream = torch.cuda.Stream()
 
     def step(ev=None, serial=True):
+        if sel_keep is not None:
+            bsa.select_blocks(prob, q, k, table, keep_tenths=sel_keep, out=mask,
+                              stream=stream if serial else plan_stream)
         if serial:
             p = bsa.plan(prob, mask, table, lut, stream=stream)
         else:
@@ -243,6 +260,24 @@ def main():
         p.free()
     plan_ms = (time.perf_counter() - tp) * 1e3 / 5
 
+    select = None
+    if sel_keep is not None:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(10)]
+        for a, b in ev:
+            a.record(stream)
+            bsa.select_blocks(prob, q, k, table, keep_tenths=sel_keep, out=mask, stream=stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        sel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        esz = 2 if w.dtype == "bf16" else 4
+        # Q and K read once (the heads of a group share their pooled key
+        # blocks), one mask byte written per block pair.
+        sel_bytes = esz * (q.numel() + w.batch * w.hkv * w.skv * w.d) + mask.numel()
+        select = {"ms": round(sel_ms, 4), "keep_tenths": sel_keep, "hbm_bytes": int(sel_bytes),
+                  "gbs": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1),
+                  "frac_of_hbm_peak": round(sel_bytes / (sel_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
     value = eff_flops / (ms_step * 1e-3) / 1e12
     achieved = eff_flops / (fwd_avg * 1e-3) / 1e12
     esz = 2 if w.dtype == "bf16" else 4
@@ -277,6 +312,8 @@ def main():
                      "traffic": traffic, "kernel": "k_attn", "compulsory_bytes": compulsory},
         "cpu_baseline": None,
     }
+    if select is not None:
+        line["select"] = select
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, q, k, v)
     print(json.dumps(line), flush=True)

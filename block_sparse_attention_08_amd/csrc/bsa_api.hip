@@ -525,9 +525,13 @@ bsa_status bsa_select_blocks(const bsa_problem *problem, const bsa_select_params
   const bool any = problem->seqlen_q > 0;
   if (any && (!q->data || (problem->seqlen_kv > 0 && !k->data)))
     return fail(BSA_ERR_INVALID_ARG, "NULL Q or K data");
-  if (q->stride_b < 0 || q->stride_h < 0 || q->stride_s < 0 || k->stride_b < 0 || k->stride_h < 0 ||
-      k->stride_s < 0)
-    return fail(BSA_ERR_INVALID_ARG, "negative stride");
+  const int64_t vec = problem->dtype == BSA_BF16 ? 8 : 4;  // elements per 16 bytes
+  for (const bsa_tensor *t : {q, k}) {
+    if (t->stride_b < 0 || t->stride_h < 0 || t->stride_s < 0)
+      return fail(BSA_ERR_INVALID_ARG, "negative stride");
+    if (((uintptr_t)t->data) % 16 || t->stride_b % vec || t->stride_h % vec || t->stride_s % vec)
+      return fail(BSA_ERR_INVALID_ARG, "tensor data and strides must be 16-byte aligned");
+  }
   return select_blocks(*problem, params->keep_tenths, params->top_k, *q, *k, page_table, mask,
                        (hipStream_t)stream);
 }

@@ -65,51 +65,91 @@ __device__ __forceinline__ int2 query_block(const SelHeads &hs, int x) {
   return make_int2(h, x - hs.qm_off[h]);
 }
 
-// One workgroup per (batch, head, query block): thread d sums column d over
-// the block's rows in order, then divides by the row count.
-__global__ __launch_bounds__(kSelThreads) void k_pool_q(SelArgs a, SelHeads hs) {
-  const int b = blockIdx.y;
-  const int2 hq = query_block(hs, blockIdx.x);
-  const int h = hq.x, qb = hq.y;
-  const int64_t i0 = (int64_t)qb * hs.bq[h];
-  const int64_t i1 = min<int64_t>(a.Sq, i0 + hs.bq[h]);
-  float *out = a.qm + ((int64_t)b * a.qm_rows + hs.qm_off[h] + qb) * a.D;
-  const int64_t base = b * a.q_sb + h * a.q_sh;
-  for (int d = threadIdx.x; d < a.D; d += blockDim.x) {
-    float s = 0.0f;
-    for (int64_t i = i0; i < i1; ++i) s = __fadd_rn(s, load_el(a, a.q, base + i * a.q_ss + d));
-    out[d] = __fdiv_rn(s, (float)(i1 - i0));
+// 8 consecutive elements (columns c0 .. c0+7 of one row) as fp32.
+__device__ __forceinline__ void load8(const SelArgs &a, const void *base, int64_t idx, float (&x)[8]) {
+  if (a.bf16) {
+    const uint4 v = *(const uint4 *)((const uint16_t *)base + idx);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      x[2 * u] = __uint_as_float(w[u] << 16);
+      x[2 * u + 1] = __uint_as_float(w[u] & 0xffff0000u);
+    }
+  } else {
+    const float4 p = *(const float4 *)((const float *)base + idx);
+    const float4 q = *(const float4 *)((const float *)base + idx + 4);
+    x[0] = p.x, x[1] = p.y, x[2] = p.z, x[3] = p.w, x[4] = q.x, x[5] = q.y, x[6] = q.z, x[7] = q.w;
   }
 }
 
-// One workgroup per (batch, pooled key block): the key blocks of each
-// distinct (kv group, block size) pair are pooled once, through the page
-// table when K is paged.
+// Block means: a lane owns 8 consecutive columns of one block and sums them
+// over the block's rows in order (one fp32 addition per row and column), 4
+// rows of loads in flight; a workgroup pools kSelThreads / (D / 8) blocks.
+// row_at(r) gives the element index of column 0 of row r.
+template <typename RowAt>
+__device__ __forceinline__ void pool8(const SelArgs &a, const void *base, int64_t r0, int64_t r1, int c0,
+                                      RowAt row_at, float *out) {
+  float s[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) s[u] = 0.0f;
+  int64_t r = r0;
+  for (; r + 4 <= r1; r += 4) {
+    float x[4][8];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) load8(a, base, row_at(r + v) + c0, x[v]);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s[u] = __fadd_rn(s[u], x[v][u]);
+  }
+  for (; r < r1; ++r) {
+    float x[8];
+    load8(a, base, row_at(r) + c0, x);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s[u] = __fadd_rn(s[u], x[u]);
+  }
+  const float n = (float)(r1 - r0);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) out[c0 + u] = __fdiv_rn(s[u], n);
+}
+
+// Query block means of one batch: block x of the concatenation over heads.
+__global__ __launch_bounds__(kSelThreads) void k_pool_q(SelArgs a, SelHeads hs) {
+  const int b = blockIdx.y;
+  const int lanes = a.D / 8, per = kSelThreads / lanes;
+  const int x = blockIdx.x * per + threadIdx.x / lanes;
+  if (threadIdx.x >= per * lanes || x >= a.qm_rows) return;
+  const int2 hq = query_block(hs, x);
+  const int h = hq.x, qb = hq.y;
+  const int64_t i0 = (int64_t)qb * hs.bq[h];
+  const int64_t i1 = min<int64_t>(a.Sq, i0 + hs.bq[h]);
+  const int64_t base = b * a.q_sb + h * a.q_sh;
+  pool8(a, a.q, i0, i1, 8 * (threadIdx.x % lanes), [&](int64_t i) { return base + i * a.q_ss; },
+        a.qm + ((int64_t)b * a.qm_rows + x) * a.D);
+}
+
+// Key block means of one batch: the key blocks of each distinct (kv group,
+// block size) pair are pooled once, through the page table when K is paged.
 __global__ __launch_bounds__(kSelThreads) void k_pool_k(SelArgs a, SelHeads hs) {
   const int b = blockIdx.y;
-  const int row = blockIdx.x;
+  const int lanes = a.D / 8, per = kSelThreads / lanes;
+  const int row = blockIdx.x * per + threadIdx.x / lanes;
+  if (threadIdx.x >= per * lanes || row >= a.km_rows) return;
   int h = 0;
   while (h < hs.n && !(hs.lead[h] && row >= hs.km_off[h] && row < hs.km_off[h] + hs.nkb[h])) ++h;
-  if (h == hs.n) return;  // not reached: the grid covers exactly the leaders' key blocks
+  if (h == hs.n) return;  // not reached: the rows are exactly the leaders' key blocks
   const int g = hs.g[h], bk = hs.bk[h], kb = row - hs.km_off[h];
   const int64_t j0 = (int64_t)kb * bk, j1 = min<int64_t>(a.Skv, j0 + bk);
-  float *out = a.km + ((int64_t)b * a.km_rows + row) * a.D;
-  for (int d = threadIdx.x; d < a.D; d += blockDim.x) {
-    float s = 0.0f;
-    for (int64_t j = j0; j < j1; ++j) {
-      int64_t idx;
-      if (a.paged) {
-        // entries outside [0, num_pages) are not followed (page 0 is read)
-        int64_t page = a.page_table[(int64_t)b * a.pps + j / a.P];
-        page = (page < 0 || page >= a.npages) ? 0 : page;
-        idx = page * a.k_sb + (j % a.P) * a.k_ss + g * a.k_sh + d;
-      } else {
-        idx = b * a.k_sb + g * a.k_sh + j * a.k_ss + d;
-      }
-      s = __fadd_rn(s, load_el(a, a.k, idx));
+  auto row_at = [&](int64_t j) -> int64_t {
+    if (a.paged) {
+      // entries outside [0, num_pages) are not followed (page 0 is read)
+      int64_t page = a.page_table[(int64_t)b * a.pps + j / a.P];
+      page = (page < 0 || page >= a.npages) ? 0 : page;
+      return page * a.k_sb + (j % a.P) * a.k_ss + g * a.k_sh;
     }
-    out[d] = __fdiv_rn(s, (float)(j1 - j0));
-  }
+    return b * a.k_sb + g * a.k_sh + j * a.k_ss;
+  };
+  pool8(a, a.k, j0, j1, 8 * (threadIdx.x % lanes), row_at, a.km + ((int64_t)b * a.km_rows + row) * a.D);
 }
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -238,9 +278,12 @@ bsa_status select_blocks(const bsa_problem &pr, int keep_tenths, int top_k, cons
   a.qm = (float *)scratch;
   a.km = (float *)((uint8_t *)scratch + ((qm_bytes + 255) & ~size_t(255)));
   a.mask = mask;
-  hipLaunchKernelGGL(k_pool_q, dim3((unsigned)qrows, (unsigned)B), dim3(kSelThreads), 0, s, a, hs);
+  const int per = kSelThreads / (pr.head_dim / 8);  // blocks pooled per workgroup
+  hipLaunchKernelGGL(k_pool_q, dim3((unsigned)((qrows + per - 1) / per), (unsigned)B), dim3(kSelThreads),
+                     0, s, a, hs);
   if (krows > 0 && pr.seqlen_kv > 0)
-    hipLaunchKernelGGL(k_pool_k, dim3((unsigned)krows, (unsigned)B), dim3(kSelThreads), 0, s, a, hs);
+    hipLaunchKernelGGL(k_pool_k, dim3((unsigned)((krows + per - 1) / per), (unsigned)B), dim3(kSelThreads),
+                       0, s, a, hs);
   const size_t lds = sizeof(unsigned long long) * kcap + sizeof(float) * 256 + ((maxk + 15) & ~15);
   hipError_t e = hipSuccess;
   if (lds > (size_t(64) << 10))
