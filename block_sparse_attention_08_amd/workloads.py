@@ -36,7 +36,7 @@ import numpy as np
 # Workload ids used as the first word of every SeedSequence.
 WID_TINY, WID_VIDEO, WID_PREFILL, WID_AFFINE, WID_LONG, WID_RANDOM = 1, 2, 3, 4, 5, 9
 # Second word: which stream of random numbers.
-STREAM_QKV, STREAM_MASK, STREAM_PAGES = 0, 1, 2
+STREAM_QKV, STREAM_MASK, STREAM_PAGES, STREAM_DOUT = 0, 1, 2, 3
 
 
 def _rng(*words: int) -> np.random.Generator:
@@ -138,6 +138,23 @@ class Workload:
                     t = torch.from_numpy(x)
                 out.append(t.reshape(shp))
             return tuple(out)
+
+    def make_dout(self, device: str = "cpu"):
+        """Upstream gradient dL/dO for a backward pass: N(0,1) of Q's shape and
+        dtype, from its own stream of the workload seed (numpy on the CPU,
+        torch's seeded generator on a GPU, as for make_qkv)."""
+        import torch
+
+        tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        shp = self.q_shape()
+        if device == "cpu":
+            x = _rng(*self.seed, STREAM_DOUT).standard_normal(int(np.prod(shp)), dtype=np.float32)
+            if self.dtype == "bf16":
+                return torch.from_numpy(f32_to_bf16_bits(x).view(np.int16)).view(torch.bfloat16).reshape(shp)
+            return torch.from_numpy(x).reshape(shp)
+        gen = torch.Generator(device=device)
+        gen.manual_seed(int(np.random.SeedSequence(list(self.seed) + [STREAM_DOUT]).generate_state(1)[0]))
+        return torch.randn(shp, generator=gen, device=device, dtype=torch.float32).to(tdt)
         gen = torch.Generator(device=device)
         gen.manual_seed(int(np.random.SeedSequence(list(self.seed) + [STREAM_QKV]).generate_state(1)[0]))
         out = []

@@ -210,6 +210,171 @@ int ref_forward(const ref_problem *p, const uint8_t *mask, const int32_t *page_t
 }
 
 /* ------------------------------------------------------------------------ */
+/* Backward: gradients of the restricted softmax attention                  */
+/* ------------------------------------------------------------------------ */
+
+/* Keys that query row i of head h (batch b) may see, ascending: the selected
+ * blocks of its selection row, cut at the causal bound (the same set the
+ * forward's mode 1 visits). Returns the count written to js. */
+static int64_t allowed_keys(const ref_problem *p, const uint8_t *sel, int64_t bk, int64_t i,
+                            int64_t *js) {
+  const int64_t nkb = ceil_div(p->skv, bk);
+  int64_t n = 0;
+  for (int64_t kb = 0; kb < nkb; ++kb) {
+    if (!sel[kb]) continue;
+    int64_t j1 = (kb + 1) * bk < p->skv ? (kb + 1) * bk : p->skv;
+    for (int64_t j = kb * bk; j < j1; ++j) {
+      if (p->causal && j > i + p->causal_offset) break;
+      js[n++] = j;
+    }
+  }
+  return n;
+}
+
+typedef struct {
+  const ref_problem *p;
+  const uint8_t *mask, *uni;
+  const int64_t *moff;
+  int64_t unkb;
+  const void *q, *k, *v, *dout;
+  double scale;
+} bwd_ctx;
+
+/* Allowed keys js[0..n) of query row i of head h in batch b. Returns n. */
+static int64_t row_keys(const bwd_ctx *c, int64_t b, int64_t h, int64_t i, int64_t *js) {
+  const ref_problem *p = c->p;
+  const int g = (int)(h / (p->hq / p->hkv)), bm = p->mask_broadcast ? 0 : (int)b;
+  const int64_t bk = p->bk[h];
+  const uint8_t *sel = p->gqa_union ? c->uni + ((int64_t)bm * p->hkv + g) * c->unkb
+                                    : c->mask + c->moff[bm * p->hq + h] + (i / p->bq[h]) * ceil_div(p->skv, bk);
+  return allowed_keys(p, sel, bk, i, js);
+}
+
+/* Over the n allowed keys js of row (b, h, i): S (s), P (pr), dP (dp) and dS
+ * (ds) as defined below. */
+static void row_gradients(const bwd_ctx *c, int64_t b, int64_t h, int64_t i, const int64_t *js,
+                          int64_t n, double *s, double *pr, double *dp, double *ds) {
+  const ref_problem *p = c->p;
+  const int d = p->d, g = (int)(h / (p->hq / p->hkv));
+  const int64_t qbase = ((b * p->hq + h) * p->sq + i) * (int64_t)d;
+  double m = -INFINITY;
+  for (int64_t e = 0; e < n; ++e) {
+    const int64_t kbase = kv_index(p, NULL, (int)b, g, js[e]);
+    double dot = 0.0;
+    for (int t = 0; t < d; ++t)
+      dot += load_value(c->q, p->dtype, qbase + t) * load_value(c->k, p->dtype, kbase + t);
+    s[e] = c->scale * dot;
+    if (s[e] > m) m = s[e];
+  }
+  double l = 0.0;
+  for (int64_t e = 0; e < n; ++e) l += exp(s[e] - m);
+  double Di = 0.0;
+  for (int64_t e = 0; e < n; ++e) {
+    pr[e] = exp(s[e] - m) / l;
+    const int64_t vbase = kv_index(p, NULL, (int)b, g, js[e]);
+    double dot = 0.0;
+    for (int t = 0; t < d; ++t)
+      dot += load_value(c->dout, p->dtype, qbase + t) * load_value(c->v, p->dtype, vbase + t);
+    dp[e] = dot;
+    Di += pr[e] * dp[e];
+  }
+  for (int64_t e = 0; e < n; ++e) ds[e] = pr[e] * (dp[e] - Di);
+}
+
+/* Backward of the forward above for a scalar loss L with dO = dL/dO. Over the
+ * allowed keys of a row, O_i = sum_j P_ij V_j with P_ij = softmax_j(S_ij) and
+ * S_ij = scale Q_i . K_j. The chain rule, with the softmax Jacobian
+ * dP_ij/dS_ik = P_ij (delta_jk - P_ik), gives
+ *   dV_j  = sum_i P_ij dO_i
+ *   dP_ij = dO_i . V_j,   D_i = sum_j P_ij dP_ij
+ *   dS_ij = P_ij (dP_ij - D_i)
+ *   dQ_i  = scale sum_j dS_ij K_j,   dK_j = scale sum_i dS_ij Q_i.
+ * Keys no row may see get zero gradients; a row with no allowed key gets
+ * dQ_i = 0 and adds nothing to dK, dV. */
+int ref_backward(const ref_problem *p, const uint8_t *mask, const void *q, const void *k,
+                 const void *v, const void *dout, const int64_t *qrows, int64_t nqrows,
+                 int64_t klo, int64_t khi, double *dq, double *dk, double *dv, int nthreads) {
+  if (check_problem(p) || p->paged) return -1;
+  if (klo < 0) klo = 0;
+  if (khi > p->skv) khi = p->skv;
+  const int d = p->d, gs = p->hq / p->hkv;
+  const int64_t kw = khi > klo ? khi - klo : 0;
+  bwd_ctx c;
+  c.p = p, c.mask = mask, c.q = q, c.k = k, c.v = v, c.dout = dout;
+  c.scale = p->scale > 0 ? p->scale : 1.0 / sqrt((double)d);
+  int64_t *moff = mask_offsets(p);
+  c.moff = moff, c.unkb = 0;
+  uint8_t *uni = p->gqa_union ? group_union(p, mask, moff, &c.unkb) : NULL;
+  c.uni = uni;
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+  const int64_t nq = qrows ? nqrows : (int64_t)p->batch * p->hq * p->sq;
+  const int64_t nbg = (int64_t)p->batch * p->hkv;
+
+#pragma omp parallel num_threads(nthreads)
+  {
+    const size_t cap = (size_t)(p->skv ? p->skv : 1);
+    double *s = (double *)malloc(sizeof(double) * cap), *pr = (double *)malloc(sizeof(double) * cap);
+    double *dp = (double *)malloc(sizeof(double) * cap), *ds = (double *)malloc(sizeof(double) * cap);
+    int64_t *js = (int64_t *)malloc(sizeof(int64_t) * cap);
+
+    /* dQ of the requested rows (rows are independent). */
+    if (dq) {
+#pragma omp for schedule(dynamic, 8)
+      for (int64_t r = 0; r < nq; ++r) {
+        int64_t b, h, i;
+        if (qrows) {
+          b = qrows[3 * r], h = qrows[3 * r + 1], i = qrows[3 * r + 2];
+        } else {
+          b = r / ((int64_t)p->hq * p->sq), h = (r / p->sq) % p->hq, i = r % p->sq;
+        }
+        const int64_t n = row_keys(&c, b, h, i, js);
+        row_gradients(&c, b, h, i, js, n, s, pr, dp, ds);
+        const int g = (int)(h / gs);
+        double *out = dq + r * d;
+        for (int t = 0; t < d; ++t) out[t] = 0.0;
+        for (int64_t e = 0; e < n; ++e) {
+          const int64_t kbase = kv_index(p, NULL, (int)b, g, js[e]);
+          for (int t = 0; t < d; ++t) out[t] += ds[e] * load_value(k, p->dtype, kbase + t);
+        }
+        for (int t = 0; t < d; ++t) out[t] *= c.scale;
+      }
+    }
+
+    /* dK, dV of keys [klo, khi): one (batch, kv head) per thread, rows of the
+       group's heads in (head, query) order. Output [batch][hkv][kw][d]. */
+    if (dk && dv && kw > 0) {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t bg = 0; bg < nbg; ++bg) {
+        const int64_t b = bg / p->hkv, g = bg % p->hkv;
+        double *gk = dk + bg * kw * d, *gv = dv + bg * kw * d;
+        for (int64_t x = 0; x < kw * d; ++x) gk[x] = 0.0, gv[x] = 0.0;
+        for (int64_t h = g * gs; h < (g + 1) * gs; ++h)
+          for (int64_t i = 0; i < p->sq; ++i) {
+            const int64_t n = row_keys(&c, b, h, i, js);
+            int64_t hit = 0;  /* rows that see no key of the window add nothing */
+            for (int64_t e = 0; e < n && !hit; ++e) hit = js[e] >= klo && js[e] < khi;
+            if (!hit) continue;
+            row_gradients(&c, b, h, i, js, n, s, pr, dp, ds);
+            const int64_t qbase = ((b * p->hq + h) * p->sq + i) * (int64_t)d;
+            for (int64_t e = 0; e < n; ++e) {
+              if (js[e] < klo || js[e] >= khi) continue;
+              const int64_t o = (js[e] - klo) * d;
+              for (int t = 0; t < d; ++t) {
+                gk[o + t] += c.scale * ds[e] * load_value(q, p->dtype, qbase + t);
+                gv[o + t] += pr[e] * load_value(dout, p->dtype, qbase + t);
+              }
+            }
+          }
+      }
+    }
+    free(s), free(pr), free(dp), free(ds), free(js);
+  }
+  free(moff);
+  free(uni);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Mask features                                                             */
 /* ------------------------------------------------------------------------ */
 

@@ -56,6 +56,17 @@ int ref_forward(const ref_problem *p, const uint8_t *mask, const int32_t *page_t
                 const void *q, const void *k, const void *v, int mode, const int64_t *rows,
                 int64_t nrows, double *o, double *lse, int nthreads);
 
+/* Backward (dense K/V only): gradients of a scalar loss L given dout =
+ * dL/dO ([batch][hq][sq][d], same dtype as Q), by the chain rule through the
+ * softmax over each row's allowed keys (see bsa_ref.c). dq receives nqrows
+ * rows (qrows as in ref_forward; NULL: every row) as [nqrows][d]; dk and dv
+ * receive the keys [klo, khi) of every (batch, kv head) as
+ * [batch][hkv][khi-klo][d]. dq, or dk and dv, may be NULL to skip them.
+ * Returns 0, or -1 for an invalid or paged problem. */
+int ref_backward(const ref_problem *p, const uint8_t *mask, const void *q, const void *k,
+                 const void *v, const void *dout, const int64_t *qrows, int64_t nqrows,
+                 int64_t klo, int64_t khi, double *dq, double *dk, double *dv, int nthreads);
+
 /* Per (mask batch, head): nnz, max row popcount, empty rows, effective blocks
  * (selected and causally feasible, after the union in union mode).
  * out has mask_batches * hq * 4 entries. */

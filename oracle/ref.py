@@ -61,6 +61,11 @@ def lib():
         L.ref_select.argtypes = [P(RefProblem), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
         L.ref_select.restype = ctypes.c_int
+        L.ref_backward.argtypes = [P(RefProblem), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_int]
+        L.ref_backward.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -178,3 +183,38 @@ def select(w, q, k, keep_tenths: int = 1, top_k: int = 0) -> np.ndarray:
     if rc:
         raise ValueError(f"ref_select rejected the problem ({rc})")
     return out[: w.batch * nb]
+
+
+def backward(w, q, k, v, dout, rows=None, kv_range=None, want_dq: bool = True,
+             want_dkv: bool = True, nthreads: int = 0, scale: float = 0.0):
+    """Oracle backward (dense K/V). dout has Q's shape and dtype.
+
+    Returns (dq, dk, dv) in float64: dq is [n][d] for the requested rows
+    (rows as in forward; None = every (b, h, i) in order), dk and dv are
+    [batch][hkv][hi - lo][d] for the key range kv_range = (lo, hi) (None = all
+    keys). A part not wanted is returned as None.
+    """
+    P = _Prob(w, scale)
+    qa, ka, va, da = (_raw(x, w.dtype) for x in (q, k, v, dout))
+    if rows is None:
+        n = w.batch * w.hq * w.sq
+        rp = None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+        n = rows.shape[0]
+        rp = rows.ctypes.data
+    lo, hi = (0, w.skv) if kv_range is None else (max(0, kv_range[0]), min(w.skv, kv_range[1]))
+    kw = max(hi - lo, 0)
+    dq = np.zeros((max(n, 1), w.d), np.float64) if want_dq else None
+    dk = np.zeros((w.batch, w.hkv, max(kw, 1), w.d), np.float64) if want_dkv else None
+    dv = np.zeros_like(dk) if want_dkv else None
+    rc = lib().ref_backward(ctypes.byref(P.s), P.mask_ptr(), qa.ctypes.data, ka.ctypes.data,
+                            va.ctypes.data, da.ctypes.data, rp, n, lo, hi,
+                            dq.ctypes.data if want_dq else None,
+                            dk.ctypes.data if want_dkv else None,
+                            dv.ctypes.data if want_dkv else None, nthreads)
+    if rc:
+        raise ValueError(f"ref_backward rejected the problem ({rc})")
+    return (dq[:n] if want_dq else None,
+            dk[:, :, :kw] if want_dkv else None,
+            dv[:, :, :kw] if want_dkv else None)
