@@ -88,8 +88,10 @@ def lib() -> ctypes.CDLL:
         L.bsa_plan_stats.argtypes = [vp, P(PlanInfo)]
         L.bsa_plan_free.argtypes = [vp]
         L.bsa_plan_free.restype = None
+        L.bsa_backward.argtypes = [vp, P(Tensor), P(Tensor), P(Tensor), P(Tensor), vp, P(Tensor),
+                                   P(Tensor), P(Tensor), P(Tensor), vp]
         L.bsa_select_blocks.argtypes = [P(Problem), P(SelectParams), P(Tensor), P(Tensor), vp, vp, vp]
-        for f in ("bsa_lut_load", "bsa_lut_parse", "bsa_plan", "bsa_forward", "bsa_plan_export",
+        for f in ("bsa_lut_load", "bsa_lut_parse", "bsa_plan", "bsa_forward", "bsa_backward", "bsa_plan_export",
                   "bsa_plan_stats", "bsa_select_blocks"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -207,6 +209,19 @@ class Plan:
                                  ctypes.byref(to), lse.data_ptr() if lse.numel() else None,
                                  _stream_handle(stream)))
         return o, lse
+
+    def backward(self, q, k, v, o, lse, dout, dq=None, dk=None, dv=None, stream=None):
+        """dQ, dK, dV for upstream gradient dout, given the forward's inputs
+        and outputs (torch tensors on the plan's device)."""
+        import torch
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(k) if dk is None else dk
+        dv = torch.empty_like(v) if dv is None else dv
+        ts = [_tensor(x) for x in (q, k, v, o, dout, dq, dk, dv)]
+        _check(lib().bsa_backward(self._h, *(ctypes.byref(t) for t in ts[:4]),
+                                  lse.data_ptr() if lse.numel() else None, ctypes.byref(ts[4]),
+                                  *(ctypes.byref(t) for t in ts[5:]), _stream_handle(stream)))
+        return dq, dk, dv
 
     def export(self) -> bytes:
         n = ctypes.c_size_t(0)

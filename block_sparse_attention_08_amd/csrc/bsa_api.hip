@@ -513,6 +513,63 @@ bsa_status bsa_forward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k
   return attention_launch(P, a, (hipStream_t)stream);
 }
 
+bsa_status bsa_backward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k,
+                        const bsa_tensor *v, const bsa_tensor *o, const float *lse,
+                        const bsa_tensor *dout, bsa_tensor *dq, bsa_tensor *dk, bsa_tensor *dv,
+                        void *stream) {
+  if (!plan || !q || !k || !v || !o || !dout || !dq || !dk || !dv)
+    return fail(BSA_ERR_INVALID_ARG, "NULL plan or tensor");
+  const Plan &P = *plan;
+  if (P.dtype != BSA_BF16) return fail(BSA_ERR_UNSUPPORTED, "backward supports bf16 only");
+  if (P.paged) return fail(BSA_ERR_UNSUPPORTED, "backward needs dense K/V (paged plans are not supported)");
+  const bool any_q = P.B * (int64_t)P.Hq * P.Sq > 0, any_k = P.B * (int64_t)P.Hkv * P.Skv > 0;
+  if (any_q && (!q->data || !o->data || !dout->data || !dq->data || !lse))
+    return fail(BSA_ERR_INVALID_ARG, "NULL Q, O, dO, dQ or LSE data");
+  if (any_k && (!k->data || !v->data || !dk->data || !dv->data))
+    return fail(BSA_ERR_INVALID_ARG, "NULL K, V, dK or dV data");
+  for (const bsa_tensor *t : {q, k, v, o, dout, (const bsa_tensor *)dq, (const bsa_tensor *)dk,
+                              (const bsa_tensor *)dv}) {
+    if (((uintptr_t)t->data) % 16)
+      return fail(BSA_ERR_INVALID_ARG, "tensor data must be 16-byte aligned");
+    if (t->stride_b % 8 || t->stride_h % 8 || t->stride_s % 8)
+      return fail(BSA_ERR_INVALID_ARG, "tensor strides must be multiples of 16 bytes");
+    if (t->stride_b < 0 || t->stride_h < 0 || t->stride_s < 0)
+      return fail(BSA_ERR_INVALID_ARG, "negative stride");
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != P.device)
+    return fail(BSA_ERR_INVALID_ARG, "current device differs from the plan's device");
+  if (!any_q && !any_k) return BSA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  BwdArgs a{};
+  a.q = q->data, a.k = k->data, a.v = v->data, a.o = o->data, a.dout = dout->data, a.lse = lse;
+  a.dq = dq->data, a.dk = dk->data, a.dv = dv->data;
+  a.q_sb = q->stride_b, a.q_sh = q->stride_h, a.q_ss = q->stride_s;
+  a.k_sb = k->stride_b, a.k_sh = k->stride_h, a.k_ss = k->stride_s;
+  a.v_sb = v->stride_b, a.v_sh = v->stride_h, a.v_ss = v->stride_s;
+  a.o_sb = o->stride_b, a.o_sh = o->stride_h, a.o_ss = o->stride_s;
+  a.do_sb = dout->stride_b, a.do_sh = dout->stride_h, a.do_ss = dout->stride_s;
+  a.dq_sb = dq->stride_b, a.dq_sh = dq->stride_h, a.dq_ss = dq->stride_s;
+  a.dk_sb = dk->stride_b, a.dk_sh = dk->stride_h, a.dk_ss = dk->stride_s;
+  a.dv_sb = dv->stride_b, a.dv_sh = dv->stride_h, a.dv_ss = dv->stride_s;
+  a.row_ent = P.row_ent, a.list_off = P.list_off, a.ent_kt = P.ent_kt, a.ent_live = P.ent_live;
+  a.hm = P.hmeta;
+  a.Sq = P.Sq, a.Skv = P.Skv, a.off = P.off, a.nqt = P.nqt, a.nkt = P.nkt;
+  a.Hq = P.Hq, a.Hkv = P.Hkv, a.G = P.G, a.tq = P.rg.tq, a.tr = P.tr, a.tk = P.rg.tk;
+  a.pack = P.rg.pack, a.uni = P.uni, a.causal = P.causal, a.nlb = (int)P.nlb;
+  a.scale = P.scale, a.scale_log2 = P.scale * 1.4426950408889634f;
+  // Delta (dO . O per query row): stream-ordered scratch, returned after the kernels.
+  void *delta = nullptr;
+  if (any_q) {
+    const hipError_t e = plan_alloc(&delta, sizeof(float) * (size_t)(P.B * (int64_t)P.Hq * P.Sq), P.device, s);
+    if (e != hipSuccess) return fail(BSA_ERR_OUT_OF_MEMORY, std::string("backward scratch: ") + hipGetErrorString(e));
+  }
+  a.delta = (float *)delta;
+  const bsa_status st = backward_launch(P, a, s);
+  if (delta) plan_release(delta, s);
+  return st;
+}
+
 bsa_status bsa_select_blocks(const bsa_problem *problem, const bsa_select_params *params,
                              const bsa_tensor *q, const bsa_tensor *k, const int32_t *page_table,
                              uint8_t *mask, void *stream) {

@@ -86,6 +86,22 @@ struct AttnArgs {
   float scale_log2;  // softmax scale * log2(e)
 };
 
+struct BwdArgs {
+  const void *q, *k, *v, *o, *dout;
+  const float *lse;
+  float *delta;  // [B][Hq][Sq]: dO . O per query row, written by the dQ kernel
+  void *dq, *dk, *dv;
+  int64_t q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh, o_ss, do_sb, do_sh, do_ss, dq_sb, dq_sh, dq_ss;
+  int64_t dk_sb, dk_sh, dk_ss, dv_sb, dv_sh, dv_ss;
+  const int32_t *row_ent, *list_off, *ent_kt;
+  const uint32_t *ent_live;
+  const HeadMeta *hm;
+  int64_t Sq, Skv, off, nqt, nkt;
+  int32_t Hq, Hkv, G, tq, tr, tk, pack, uni, causal, nlb;
+  float scale, scale_log2;
+};
+
 // Error reporting (thread-local message).
 bsa_status fail(bsa_status s, const std::string &msg);
 
@@ -106,6 +122,9 @@ bsa_status select_blocks(const bsa_problem &pr, int keep_tenths, int top_k, cons
 
 // Attention entry point (bsa_attention.hip).
 bsa_status attention_launch(const Plan &p, const AttnArgs &a, hipStream_t stream);
+
+// Backward entry point (bsa_backward.hip).
+bsa_status backward_launch(const Plan &p, const BwdArgs &a, hipStream_t stream);
 
 }  // namespace bsa
 

@@ -139,6 +139,15 @@ class Workload:
                 out.append(t.reshape(shp))
             return tuple(out)
 
+        gen = torch.Generator(device=device)
+        gen.manual_seed(int(np.random.SeedSequence(list(self.seed) + [STREAM_QKV]).generate_state(1)[0]))
+        out = []
+        for shp in shapes:
+            x = torch.randn(shp, generator=gen, device=device, dtype=torch.float32)
+            out.append(x.to(tdt))
+            del x
+        return tuple(out)
+
     def make_dout(self, device: str = "cpu"):
         """Upstream gradient dL/dO for a backward pass: N(0,1) of Q's shape and
         dtype, from its own stream of the workload seed (numpy on the CPU,
@@ -155,14 +164,6 @@ class Workload:
         gen = torch.Generator(device=device)
         gen.manual_seed(int(np.random.SeedSequence(list(self.seed) + [STREAM_DOUT]).generate_state(1)[0]))
         return torch.randn(shp, generator=gen, device=device, dtype=torch.float32).to(tdt)
-        gen = torch.Generator(device=device)
-        gen.manual_seed(int(np.random.SeedSequence(list(self.seed) + [STREAM_QKV]).generate_state(1)[0]))
-        out = []
-        for shp in shapes:
-            x = torch.randn(shp, generator=gen, device=device, dtype=torch.float32)
-            out.append(x.to(tdt))
-            del x
-        return tuple(out)
 
     def problem_dict(self) -> dict:
         return dict(

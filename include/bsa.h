@@ -175,6 +175,31 @@ bsa_status bsa_plan(const bsa_problem *problem, const uint8_t *mask, const int32
 bsa_status bsa_forward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k,
                        const bsa_tensor *v, bsa_tensor *o, float *lse, void *stream);
 
+/* Backward of bsa_forward over the same plan: for a scalar loss with
+ * dout = dL/dO, writes dq = dL/dQ, dk = dL/dK and dv = dL/dV. By the chain
+ * rule through the softmax over each query row's allowed keys (Tessera,
+ * abstract: only the selected blocks are computed, in training as in
+ * inference):
+ *   dV_j = sum_i P_ij dO_i,   dS_ij = P_ij (dO_i . V_j - dO_i . O_i),
+ *   dQ_i = scale sum_j dS_ij K_j,   dK_j = scale sum_i dS_ij Q_i,
+ * with P_ij = exp(scale Q_i . K_j - LSE_i) recomputed over the allowed keys.
+ *   q, k, v:  the forward's inputs (bf16, dense K/V: paged plans are not
+ *             supported);
+ *   o, lse:   the forward's outputs for those inputs (lse fp32 [batch][Hq][Sq]);
+ *   dout:     bf16, Q's shape [batch][Hq][Sq][D];
+ *   dq:       bf16, Q's shape; dk, dv: bf16, K's shape [batch][Hkv][Skv][D].
+ * Every element of dq, dk and dv is written exactly once (zero for rows
+ * without keys and keys no query sees), by one workgroup in a fixed order,
+ * so the results are the same bit for bit on every call. Outputs must not
+ * overlap the inputs. Queued on stream; never synchronises; uses
+ * batch * Hq * Sq * 4 bytes of scratch from the device's stream-ordered
+ * pool, returned in stream order. BSA_ERR_UNSUPPORTED for fp32 or paged
+ * plans. */
+bsa_status bsa_backward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k,
+                        const bsa_tensor *v, const bsa_tensor *o, const float *lse,
+                        const bsa_tensor *dout, bsa_tensor *dq, bsa_tensor *dk, bsa_tensor *dv,
+                        void *stream);
+
 /* Canonical byte image of a plan (header, features, lists, entries, rows,
  * work list), for comparison with the reference planner. With host_buf NULL
  * only *bytes is set to the size needed; otherwise *bytes is the capacity on

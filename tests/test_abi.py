@@ -82,6 +82,9 @@ def test_forward_and_export_null_plan(L):
     t = bsa.Tensor(None, 0, 0, 0)
     assert L.bsa_forward(None, ctypes.byref(t), ctypes.byref(t), ctypes.byref(t),
                          ctypes.byref(t), None, None) == 1
+    tt = [ctypes.byref(t)] * 4
+    assert L.bsa_backward(None, *tt, None, *tt, None) == 1
+    assert "NULL" in L.bsa_last_error().decode()
     n = ctypes.c_size_t(0)
     assert L.bsa_plan_export(None, None, ctypes.byref(n)) == 1
     info = bsa.PlanInfo()

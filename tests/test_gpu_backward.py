@@ -1,0 +1,173 @@
+"""GPU parity of the backward pass (bsa_backward) against the oracle's
+ref_backward: dQ, dK and dV from the GPU forward's O and LSE, compared on
+every element for small cases (several tiles, ragged tails, every regime the
+planner can pick) and on sampled rows and a window of keys at the full
+video-DiT shape. Repeated calls must agree bit for bit.
+
+Tolerance (bf16 inputs and outputs, fp32 accumulation): every gradient
+element is a sum of products in which one factor (P or dS) is rounded to
+bf16 before its MFMA (relative error <= 2^-9) and the result is rounded to
+bf16 once more (<= 2^-9); with independent rounding errors the expected
+relative error of a sum is about 2^-9, so per tensor
+  mean |G_gpu - G_ref| <= 1e-2 * mean |G_ref|   (about 5x the expected 2e-3)
+  max  |G_gpu - G_ref| <= 3e-2 * max  |G_ref|   (about six standard deviations
+                                                of 2^-9 at the largest values)
+and the gradients that must vanish (dK, dV of keys no query sees; dQ of rows
+with no allowed key) are exactly zero.
+"""
+import numpy as np
+import pytest
+
+import block_sparse_attention_08_amd as bsa
+from block_sparse_attention_08_amd import workloads as W
+from tests.gpu_helpers import forced_lut_text, say, to_device
+from tests.test_oracle_pins import element_mask
+
+pytestmark = pytest.mark.gpu
+
+G_MAX, G_MEAN = 3e-2, 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _cmp(name, g, r):
+    g = np.asarray(g, np.float64)
+    r = np.asarray(r, np.float64)
+    err = np.abs(g - r)
+    mx, mean = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
+    rmx, rmean = float(np.abs(r).max()) if r.size else 0.0, float(np.abs(r).mean()) if r.size else 0.0
+    say(f"[result] {name}: max|err|={mx:.3e} (ref max {rmx:.3e}) mean|err|={mean:.3e} (ref mean {rmean:.3e})")
+    assert mx <= G_MAX * rmx + 1e-30, (name, mx, rmx)
+    assert mean <= G_MEAN * rmean + 1e-30, (name, mean, rmean)
+
+
+def _structural_zeros(w):
+    """Query rows with no allowed key [B][Hq][Sq] and keys no query of their
+    kv head sees [B][Hkv][Skv], from the definition of the allowed set."""
+    gs = w.hq // w.hkv
+    empty_rows = np.zeros((w.batch, w.hq, w.sq), bool)
+    seen = np.zeros((w.batch, w.hkv, w.skv), bool)
+    for b in range(w.batch):
+        for h in range(w.hq):
+            m = element_mask(w, b, h)
+            empty_rows[b, h] = ~m.any(1)
+            seen[b, h // gs] |= m.any(0)
+    return empty_rows, ~seen
+
+
+def _run(ref, w, lut_text=None, label=""):
+    import torch
+    say(f"[case] backward {label or w.name}: B={w.batch} Hq={w.hq} Hkv={w.hkv} Sq={w.sq} Skv={w.skv} "
+        f"D={w.d} union={int(w.gqa_union)} causal={int(w.causal)} lut={lut_text is not None}")
+    q, k, v, mask, _ = to_device(w)
+    dout = w.make_dout().cuda()
+    lut = bsa.Lut.parse(lut_text) if lut_text else None
+    plan = bsa.plan(w.problem_dict(), mask, None, lut)
+    o, lse = plan.forward(q, k, v)
+    dq, dk, dv = plan.backward(q, k, v, o, lse, dout)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = ref.backward(w, q.cpu(), k.cpu(), v.cpu(), dout.cpu())
+    gdq, gdk, gdv = (x.float().cpu().numpy() for x in (dq, dk, dv))
+    _cmp("dq", gdq.reshape(rdq.shape), rdq)
+    _cmp("dk", gdk, rdk)
+    _cmp("dv", gdv, rdv)
+    # rows without keys and keys no query sees: exactly zero
+    empty_rows, unseen = _structural_zeros(w)
+    assert np.all(gdq[empty_rows] == 0.0)
+    assert np.all(gdk[unseen] == 0.0) and np.all(gdv[unseen] == 0.0)
+    say(f"[result] exact zeros: {int(empty_rows.sum())} rows, {int(unseen.sum())} keys")
+    # bit-for-bit on a second call into fresh (NaN-filled) outputs
+    dq2, dk2, dv2 = (torch.full_like(x, float("nan")) for x in (dq, dk, dv))
+    plan.backward(q, k, v, o, lse, dout, dq2, dk2, dv2)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    plan.free()
+
+
+CASES = {
+    "plain_d128": lambda: W.random_problem(batch=2, hq=2, sq=300, skv=333, d=128, bq=64, bk=64,
+                                           density=0.4, empty_rows=0.1, seed=401),
+    "gqa_causal_mixed_d64": lambda: W.random_problem(batch=1, hq=4, hkv=2, sq=450, skv=520, d=64,
+                                                     bq=[16, 32, 64, 128], bk=[32, 64, 16, 128],
+                                                     density=0.3, causal=True, causal_offset=70,
+                                                     seed=402),
+    "union_g4_causal": lambda: W.random_problem(batch=2, hq=8, hkv=2, sq=256, skv=700, d=128, bq=128,
+                                                bk=128, density=0.08, gqa_union=True, causal=True,
+                                                causal_offset=444, seed=403),
+    "union_g2_ragged_d64": lambda: W.random_problem(batch=1, hq=4, hkv=2, sq=150, skv=333, d=64,
+                                                    bq=64, bk=32, density=0.1, gqa_union=True,
+                                                    causal=True, causal_offset=183, seed=404),
+    "broadcast_big_blocks": lambda: W.random_problem(batch=2, hq=2, sq=600, skv=640, d=128,
+                                                     bq=[256, 512], bk=[512, 256], density=0.5,
+                                                     mask_broadcast=True, seed=405),
+    "negative_offset": lambda: W.random_problem(batch=1, hq=2, sq=200, skv=150, d=64, bq=32, bk=32,
+                                                density=0.7, causal=True, causal_offset=-60, seed=406),
+    "all_empty": lambda: W.random_problem(batch=1, hq=2, sq=130, skv=140, d=64, bq=64, bk=64,
+                                          density=0.0, seed=407),
+    "tiny_video": lambda: W.video_dit(heads=2, grid=(16, 6, 12), seed=1),
+    "tiny_affine32": lambda: W.affine(bs=32, batch=2, heads=3, s=1024, window=128),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_backward_default_regime(ref, case):
+    _run(ref, CASES[case](), label=case)
+
+
+REGIMES = [(128, 64, 0), (128, 128, 0), (256, 64, 0), (256, 64, 1), (128, 128, 1)]
+
+
+@pytest.mark.parametrize("tq,tk,pack", REGIMES, ids=lambda x: str(x))
+@pytest.mark.parametrize("case", ["gqa_causal_mixed_d64", "union_g4_causal", "plain_d128"])
+def test_backward_regimes(ref, case, tq, tk, pack):
+    _run(ref, CASES[case](), lut_text=forced_lut_text(tq, tk, "local", 0, pack),
+         label=f"{case} {tq}x{tk} pack={pack}")
+
+
+def test_backward_full_video_sampled(ref):
+    """The full video-DiT shape (24 heads, 24960 tokens, D = 128): dQ on sampled
+    rows, dK and dV on one window of 160 keys crossing a block boundary."""
+    import torch
+    w = W.video_dit()
+    say("[case] backward video_dit full (sampled)")
+    q, k, v, mask, _ = to_device(w, device_gen=True)
+    dout = w.make_dout(device="cuda")
+    plan = bsa.plan(w.problem_dict(), mask, None)
+    o, lse = plan.forward(q, k, v)
+    dq, dk, dv = plan.backward(q, k, v, o, lse, dout)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(5)
+    rows = np.stack([np.zeros(192, np.int64), g.integers(0, w.hq, 192), g.integers(0, w.sq, 192)], 1)
+    rows = np.concatenate([rows, [[0, 0, 0], [0, w.hq - 1, w.sq - 1]]]).astype(np.int64)
+    lo, hi = 12 * 128 + 64, 12 * 128 + 224
+    qc, kc, vc, dc = q.cpu(), k.cpu(), v.cpu(), dout.cpu()
+    rdq, _, _ = ref.backward(w, qc, kc, vc, dc, rows=rows, want_dkv=False)
+    _, rdk, rdv = ref.backward(w, qc, kc, vc, dc, kv_range=(lo, hi), want_dq=False)
+    ri = [torch.from_numpy(rows[:, i]).cuda() for i in range(3)]
+    _cmp("dq[sampled]", dq[ri[0], ri[1], ri[2]].float().cpu().numpy(), rdq)
+    _cmp("dk[window]", dk[:, :, lo:hi].float().cpu().numpy(), rdk)
+    _cmp("dv[window]", dv[:, :, lo:hi].float().cpu().numpy(), rdv)
+    plan.free()
+
+
+def test_backward_rejects_paged_and_fp32():
+    import torch
+    w = W.random_problem(batch=1, hq=2, sq=64, skv=128, d=64, bq=64, bk=64, paged=True, seed=408)
+    q, k, v, mask, table = to_device(w)
+    plan = bsa.plan(w.problem_dict(), mask, table)
+    o, lse = plan.forward(q, k, v)
+    with pytest.raises(bsa.BsaError):
+        plan.backward(q, k, v, o, lse, torch.zeros_like(q))
+    plan.free()
+    w = W.random_problem(batch=1, hq=2, sq=64, skv=128, d=64, dtype="f32", bq=64, bk=64, seed=409)
+    q, k, v, mask, table = to_device(w)
+    plan = bsa.plan(w.problem_dict(), mask, table)
+    o, lse = plan.forward(q, k, v)
+    with pytest.raises(bsa.BsaError):
+        plan.backward(q, k, v, o, lse, torch.zeros_like(q))
+    plan.free()
