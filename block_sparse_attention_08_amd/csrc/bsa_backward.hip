@@ -22,15 +22,14 @@
 //               dP^T = V dO^T put one query in each lane (per-lane LSE and
 //               Delta); dQ^T += K^T dS^T reads K^T with LDS transpose reads.
 //               It also writes Delta (from O and dO) for the second kernel.
-//   k_bwd_dkdv  one workgroup per (batch, kv head, key tile), one wave per 32
-//               keys, K and V rows held in registers. It finds the query
-//               tiles that visit its key tile by searching each plan row's
-//               sorted key-tile list (or, in GQA-union mode, the group's
-//               table once), then streams their queries through LDS in
-//               32-row chunks, the next chunk's loads in flight while the
-//               current one is computed: S = Q K^T and dP = dO V^T put one
-//               key in each lane; dV^T += dO^T P and dK^T += Q^T dS take P
-//               and dS straight from the accumulators as MFMA operands.
+//   k_bwd_dkdv  one workgroup per (batch, kv head, 128 keys), one wave per 32
+//               keys, K and V rows held in registers. The query chunks that
+//               visit its keys come from a key-major index built per call
+//               from the plan's sorted lists (planner: k_kv_chunks); they
+//               stream through LDS three chunks ahead of the arithmetic.
+//               S = Q K^T and dP = dO V^T put one key in each lane;
+//               dV^T += dO^T P and dK^T += Q^T dS take P and dS straight from
+//               the accumulators as MFMA operands.
 #include "bsa_internal.h"
 
 namespace bsa {
@@ -265,208 +264,166 @@ __global__ __launch_bounds__(2 * TQ) void k_bwd_dq(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV per (batch, kv head, key tile)
+// dK, dV per (batch, kv head, 128 keys)
 // ---------------------------------------------------------------------------
-template <int D, int TK>
-__global__ __launch_bounds__(2 * TK) void k_bwd_dkdv(BwdArgs a) {
-  constexpr int T = 2 * TK;                     // 64 lanes per 32 keys
-  constexpr int RS = D + 8;
-  constexpr int CH = 32 * RS;                   // one 32-row chunk of Q or dO
-  constexpr int CPR = D / 8;
-  constexpr int LPT = (32 * CPR + T - 1) / T;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(4))) const int32_t cint32;
+typedef __attribute__((address_space(4))) const uint32_t cuint32;
+
+// XOR swizzle of the 16-byte chunks of an LDS row of D bf16: chunk c of row r
+// sits at slot c ^ swz(r), which keeps both the 16-byte row reads and the
+// transpose reads of a 32-row chunk spread over the banks.
+template <int D>
+__device__ __forceinline__ int swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+
+// 16-byte row read: dims 8*c .. 8*c + 7 of row r.
+template <int D>
+__device__ __forceinline__ bf16x8 row_frag(const uint8_t *t, int r, int c) {
+  return *(const bf16x8 *)(t + r * (2 * D) + ((c ^ swz<D>(r)) << 4));
+}
+
+// Transpose read of a swizzled tile: lane (n, hh) gets X[r0 + 8hh + i][c0 + n], i = 0..7.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag_s(const uint8_t *t, int r0, int c0, int lane) {
+  const int vj = lane & 15, vsub = (lane >> 4) & 1, hh = lane >> 5;
+  const int ra = r0 + 8 * hh + (vj >> 2), rb = ra + 4;
+  const int col = c0 + 16 * vsub + 4 * (vj & 3);
+  const int ch = col >> 3, byte = (col & 7) * 2;
+  const uint8_t *pa = t + ra * (2 * D) + ((ch ^ swz<D>(ra)) << 4) + byte;
+  const uint8_t *pb = t + rb * (2 * D) + ((ch ^ swz<D>(rb)) << 4) + byte;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)pa);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)pb);
+  const s16x4 both[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8, both);
+}
+
+// Values equal on every lane, moved to scalar registers (so buffer
+// descriptors built from them are scalar).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+template <typename T>
+__device__ __forceinline__ T *uni(T *p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T *)(((uint64_t)hi << 32) | lo);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (<= n).
+#define BSA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// A workgroup owns 128 consecutive keys: NKT = 128 / TKP key tiles of the
+// plan (TKP = 64 or 128), four waves of 32 keys. The query chunks (32 rows)
+// that may see them come from the key-major chunk index built for the call;
+// they stream through a ring of four LDS buffers with direct-to-LDS buffer
+// loads issued three chunks ahead.
+template <int D, int TKP>
+__global__ __launch_bounds__(256) void k_bwd_dkdv(BwdArgs a) {
+  constexpr int T = 256, KW = 128, NKT = KW / TKP, NBUF = 4;
+  constexpr int ROWB = 2 * D;                   // bytes per row in LDS
+  constexpr int CHB = 32 * ROWB;                // one 32-row chunk of Q or dO
+  constexpr int CPR = D / 8;                    // 16-byte chunks per row
+  constexpr int RPL = T / CPR;                  // rows covered by one load
+  constexpr int LOADS = 32 / RPL;               // loads per thread per chunk and tensor
+  constexpr int BUFB = 2 * CHB + 1024;          // Q, dO, LSE (256 B), Delta (256 B), spare
+  constexpr int LPC = 2 * LOADS + 1;            // vector-memory ops per thread per chunk
   constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * CH];  // Q, dO; two buffers
-  __shared__ float s_lse[2][32], s_del[2][32];
+  static_assert((D == 128 && RPL % 16 == 0) || (D == 64 && RPL % 16 == 0), "swizzle period");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * BUFB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hh = lane >> 5;
   const int nkt = (int)a.nkt, nqt = (int)a.nqt;
+  const int nkp = (nkt + NKT - 1) / NKT;
   const int item = blockIdx.x;
-  const int kt = item % nkt, g = (item / nkt) % a.Hkv, b = item / (nkt * a.Hkv);
-  const int kb0 = kt * TK;
-  const int klocal = 32 * wave + n;            // this lane's key within the tile
-  const int key = kb0 + klocal;
+  const int kp = item % nkp, g = (item / nkp) % a.Hkv, b = item / (nkp * a.Hkv);
+  const int kt0 = kp * NKT;
+  const int kb0 = kp * KW;                      // first key of the workgroup
+  const int wkt = (32 * wave) / TKP;            // this wave's tile within the group
+  const int kloc = (32 * wave) % TKP + n;       // this lane's key within its tile
+  const int key = kb0 + 32 * wave + n;
   const int skv32 = (int)a.Skv, sq32 = (int)a.Sq;  // sequence lengths are below 2^31
   const bool kvalid = key < skv32;
+  const int lb = a.nlb == 1 ? 0 : b;
 
   // K and V rows of this lane's key as B operands (dims 16c + 8hh .. +8).
   bf16x8 kb[D / 16], vb[D / 16];
   {
-    const uint16_t *kp = (const uint16_t *)a.k + b * a.k_sb + g * a.k_sh + (int64_t)(kvalid ? key : 0) * a.k_ss;
-    const uint16_t *vp = (const uint16_t *)a.v + b * a.v_sb + g * a.v_sh + (int64_t)(kvalid ? key : 0) * a.v_ss;
+    const uint16_t *kp_ = (const uint16_t *)a.k + b * a.k_sb + g * a.k_sh + (int64_t)(kvalid ? key : 0) * a.k_ss;
+    const uint16_t *vp_ = (const uint16_t *)a.v + b * a.v_sb + g * a.v_sh + (int64_t)(kvalid ? key : 0) * a.v_ss;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      kb[c] = __builtin_bit_cast(bf16x8, kvalid ? *(const uint4 *)(kp + 16 * c + 8 * hh) : make_uint4(0, 0, 0, 0));
-      vb[c] = __builtin_bit_cast(bf16x8, kvalid ? *(const uint4 *)(vp + 16 * c + 8 * hh) : make_uint4(0, 0, 0, 0));
+      kb[c] = __builtin_bit_cast(bf16x8, kvalid ? *(const uint4 *)(kp_ + 16 * c + 8 * hh) : make_uint4(0, 0, 0, 0));
+      vb[c] = __builtin_bit_cast(bf16x8, kvalid ? *(const uint4 *)(vp_ + 16 * c + 8 * hh) : make_uint4(0, 0, 0, 0));
     }
   }
   f32x16 dk[NDB], dv[NDB];
 #pragma unroll
   for (int u = 0; u < NDB; ++u) dk[u] = f32x16{}, dv[u] = f32x16{};
 
-  // ---- enumeration of the query chunks that visit this key tile ----
-  // A chunk is 32 consecutive queries of one head. Non-union: the rows
-  // (b, h, qt) of the group's heads whose sorted key-tile list holds kt
-  // (binary search, 64 rows per ballot), then the row's chunks. Union: the
-  // group's table holds kt or not; if it does, every causally feasible chunk
-  // of every head of the group visits it.
-  const int cpr = a.tq / 32;                    // chunks per plan row (non-union)
-  const int nch = (sq32 + 31) / 32;             // chunks per head (union)
-  const int lb = a.nlb == 1 ? 0 : b;
-  int h = g * a.G - 1, qtb = 0, qt = 0, ci = 0, cend = 0;
-  uint64_t bal = 0;
-  uint32_t lvl = 0, rl = 0;
-  HeadMeta hm{};
-  uint32_t ulive = 0;
-  if (a.uni) {
-    const int l = lb * a.Hkv + g;
-    int lo = a.list_off[l], hi = a.list_off[l + 1];
-    while (lo < hi) {
-      const int mid = lo + ((hi - lo) >> 1);
-      if (a.ent_kt[mid] < kt) lo = mid + 1;
-      else hi = mid;
-    }
-    ulive = (lo < a.list_off[l + 1] && a.ent_kt[lo] == kt) ? a.ent_live[lo] : 0u;
-  }
-  auto search = [&]() {
-    const int q = qtb + lane;
-    uint32_t lv = 0;
-    if (q < nqt) {
-      const int64_t row = ((int64_t)b * a.Hq + h) * a.nqt + q;
-      int lo = a.row_ent[2 * row], hi = a.row_ent[2 * row + 1];
-      const int end = hi;
-      while (lo < hi) {
-        const int mid = lo + ((hi - lo) >> 1);
-        if (a.ent_kt[mid] < kt) lo = mid + 1;
-        else hi = mid;
-      }
-      if (lo < end && a.ent_kt[lo] == kt) lv = a.ent_live[lo];
-    }
-    lvl = lv;
-    bal = __ballot(lv != 0u);
-  };
-  // Next chunk: its head, first query, offset within its plan row, live bits.
-  struct Chunk {
-    int h, q0, qoff;
-    uint32_t live;
-    int lq, lk, mk;
-  };
-  auto next = [&](Chunk &o) -> bool {
-    for (;;) {
-      if (ci < cend) {
-        const int cc = ci++;
-        const int cq0 = a.uni ? 32 * cc : qt * a.tq + 32 * cc;
-        if (cq0 >= sq32) {
-          ci = cend;
-          continue;
-        }
-        const int last = min(cq0 + 31, sq32 - 1);
-        if (a.causal && (int64_t)kb0 > (int64_t)last + a.off) continue;
-        const int qoff = a.uni ? 0 : 32 * cc;
-        const uint32_t live = a.uni ? ulive : rl;
-        if (!a.uni) {
-          const int iq0 = qoff >> hm.lq, niq = hm.lq >= 5 ? 1 : (32 >> hm.lq);
-          const uint64_t cb = ((1ull << (hm.mk * niq)) - 1ull) << (iq0 * hm.mk);
-          if (((uint64_t)live & cb) == 0) continue;
-        }
-        o = Chunk{h, cq0, qoff, live, hm.lq, hm.lk, hm.mk};
-        return true;
-      }
-      if (!a.uni && bal) {
-        const int bit = __builtin_ctzll(bal);
-        bal &= bal - 1;
-        qt = qtb + bit;
-        rl = __builtin_amdgcn_readlane(lvl, bit);
-        ci = 0, cend = cpr;
-        continue;
-      }
-      if (!a.uni && h >= g * a.G && qtb + 64 < nqt) {
-        qtb += 64;
-        search();
-        continue;
-      }
-      if (++h >= (g + 1) * a.G) return false;
-      hm = a.hm[h];
-      if (a.uni) {
-        if (ulive == 0) return false;
-        // first chunk whose last query can reach the tile's first key
-        const int64_t need = (int64_t)kb0 - a.off - 31;
-        ci = (!a.causal || need <= 0) ? 0 : (int)min<int64_t>((need + 31) / 32, nch);
-        cend = nch;
-      } else {
-        qtb = 0;
-        search();
-      }
-    }
-  };
+  // The query chunks that may see these keys: entries [e0, e1) of the
+  // key-major chunk index (first query, packed head / geometry word, live
+  // words), read with scalar loads.
+  const int bucket = (lb * a.Hkv + g) * nkp + kp;
+  const int e0 = ((const cint32 *)a.t_off)[bucket], e1 = ((const cint32 *)a.t_off)[bucket + 1];
 
-  // ---- chunk staging: Q and dO rows, LSE (log2, +inf for no keys) and Delta ----
-  uint4 qr[LPT], dr[LPT];
-  float lse_r = 0.f, del_r = 0.f;
-  auto load = [&](const Chunk &c) {
-    const uint16_t *Qp = (const uint16_t *)a.q + b * a.q_sb + c.h * a.q_sh;
-    const uint16_t *Dp = (const uint16_t *)a.dout + b * a.do_sb + c.h * a.do_sh;
+  // ---- chunk loads straight into LDS ----
+  // Thread tid fills 16-byte slot tid of each 4 KiB block of a chunk: row
+  // tid / CPR, slot tid % CPR, which holds the row's chunk slot ^ swz(row).
+  const int trow = tid / CPR, tpos = tid % CPR;
+  const int qoff0 = trow * (int)a.q_ss * 2 + ((tpos ^ swz<D>(trow)) << 4);
+  const int doff0 = trow * (int)a.do_ss * 2 + ((tpos ^ swz<D>(trow)) << 4);
+  auto issue = [&](int e, int buf) {
+    const int q0 = ((const cint32 *)a.t_q0)[e];
+    const int h = g * a.G + (((const cint32 *)a.t_meta)[e] & 255);
+    uint8_t *dst = lds + buf * BUFB;
+    const int rows = min(sq32 - q0, 32);        // rows of the chunk that exist (>= 1)
+    const uint16_t *qb_ = (const uint16_t *)a.q + b * a.q_sb + h * a.q_sh + (int64_t)q0 * a.q_ss;
+    const uint16_t *db_ = (const uint16_t *)a.dout + b * a.do_sb + h * a.do_sh + (int64_t)q0 * a.do_ss;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)qb_, 0, (rows - 1) * (int)a.q_ss * 2 + D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc((void *)db_, 0, (rows - 1) * (int)a.do_ss * 2 + D * 2, 0x00020000);
 #pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int x = tid + T * u;
-      const int row = x / CPR, col = (x % CPR) * 8;
-      const bool ok = x < 32 * CPR && c.q0 + row < sq32;
-      qr[u] = ok ? *(const uint4 *)(Qp + (int64_t)(c.q0 + row) * a.q_ss + col) : make_uint4(0, 0, 0, 0);
-      dr[u] = ok ? *(const uint4 *)(Dp + (int64_t)(c.q0 + row) * a.do_ss + col) : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < LOADS; ++u) {
+      uint8_t *dq_ = dst + (u * T + wave * 64) * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)dq_, 16, qoff0 + u * RPL * (int)a.q_ss * 2, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void *)(dq_ + CHB), 16, doff0 + u * RPL * (int)a.do_ss * 2, 0, 0, 0);
     }
-    if (tid < 32) {
-      const bool ok = c.q0 + tid < sq32;
-      const int64_t ix = ((int64_t)b * a.Hq + c.h) * a.Sq + c.q0 + tid;
-      const float L = ok ? a.lse[ix] : -INFINITY;
-      lse_r = L == -INFINITY ? INFINITY : L * kLog2e;
-      del_r = ok ? a.delta[ix] : 0.f;
-    }
-  };
-  auto store = [&](int buf) {
-    uint16_t *qs = lds + buf * 2 * CH, *ds = qs + CH;
-#pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int x = tid + T * u;
-      if (x < 32 * CPR) {
-        const int row = x / CPR, col = (x % CPR) * 8;
-        *(uint4 *)(qs + row * RS + col) = qr[u];
-        *(uint4 *)(ds + row * RS + col) = dr[u];
-      }
-    }
-    if (tid < 32) s_lse[buf][tid] = lse_r, s_del[buf][tid] = del_r;
+    // LSE (wave 0) and Delta (wave 1) of the chunk's rows, one dword per lane;
+    // waves 2 and 3 repeat the LSE load into a spare area so that every wave
+    // has the same number of loads in flight per chunk.
+    const int64_t rix = ((int64_t)b * a.Hq + h) * a.Sq + q0;
+    const float *src = wave == 1 ? a.delta + rix : a.lse + rix;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)src, 0, rows * 4, 0x00020000);
+    uint8_t *dl = dst + 2 * CHB + (wave == 1 ? 256 : (wave == 0 ? 0 : 512 + 256 * (wave - 2)));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dl, 4, lane * 4, 0, 0, 0);
   };
 
-  Chunk cur{}, nxt{};
-  bool have = next(cur);
-  if (have) {
-    load(cur);
-    store(0);
-    __syncthreads();
-  }
-  int buf = 0;
-  while (have) {
-    const bool more = next(nxt);
-    if (more) load(nxt);
-    const uint16_t *qs = lds + buf * 2 * CH, *dos = qs + CH;
-
+  // One chunk's arithmetic on buffer t (Q at t, dO at t + CHB, LSE and Delta after them).
+  auto compute = [&](int e, const uint8_t *__restrict__ t) {
+    const int q0 = ((const cint32 *)a.t_q0)[e];
+    const int meta = ((const cint32 *)a.t_meta)[e];
+    uint32_t live = ((const cuint32 *)a.t_live)[NKT * e];
+    if (NKT == 2 && wkt == 1) live = ((const cuint32 *)a.t_live)[NKT * e + 1];
+    const int qoff = 32 * ((meta >> 8) & 7), lq = (meta >> 11) & 31, lk = (meta >> 16) & 31, mk = (meta >> 21) & 63;
+    const uint8_t *qs = t, *dos = t + CHB;
+    const float *lse_s = (const float *)(t + 2 * CHB), *del_s = lse_s + 64;
     // S = Q K^T and dP = dO V^T: lane = key n, accumulator j = query row
     // 16*(j/8) + 8*hh + (j%8) of the chunk.
     f32x16 s = f32x16{}, dp = f32x16{};
-    const uint16_t *qrow = qs + perm_rows(n) * RS + 8 * hh;
-    const uint16_t *drow = dos + perm_rows(n) * RS + 8 * hh;
+    const int pr = perm_rows(n);
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(qrow + 16 * c), kb[c], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(drow + 16 * c), vb[c], dp, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(qs, pr, 2 * c + hh), kb[c], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(dos, pr, 2 * c + hh), vb[c], dp, 0, 0, 0);
     }
     // Is every (query, key) pair of this wave's 32 x 32 block allowed?
-    const int ik0 = (32 * wave) >> cur.lk, nik = cur.lk >= 5 ? 1 : (32 >> cur.lk);
-    const int iq0 = cur.qoff >> cur.lq, niq = cur.lq >= 5 ? 1 : (32 >> cur.lq);
-    uint64_t wb = 0;
-    for (int iq = 0; iq < niq; ++iq) wb |= ((1ull << nik) - 1ull) << ((iq0 + iq) * cur.mk + ik0);
-    const bool need = ((uint64_t)cur.live & wb) != wb || kb0 + 32 * wave + 31 >= skv32 ||
-                      cur.q0 + 31 >= sq32 || (a.causal && (int64_t)kb0 + 32 * wave + 31 > (int64_t)cur.q0 + a.off);
+    const int ik0 = ((32 * wave) % TKP) >> lk, nik = lk >= 5 ? 1 : (32 >> lk);
+    const int iq0 = qoff >> lq, niq = lq >= 5 ? 1 : (32 >> lq);
+    uint64_t wb = ((1ull << nik) - 1ull) << (iq0 * mk + ik0);
+    if (niq == 2) wb |= wb << mk;
+    const int wk0 = kb0 + 32 * wave;
+    const bool need = ((uint64_t)live & wb) != wb || wk0 + 31 >= skv32 || q0 + 31 >= sq32 ||
+                      (a.causal && (int64_t)wk0 + 31 > (int64_t)q0 + a.off);
     uint32_t pw[8], dw[8];
 #pragma unroll
     for (int jj = 0; jj < 16; jj += 2) {
@@ -476,13 +433,14 @@ __global__ __launch_bounds__(2 * TK) void k_bwd_dkdv(BwdArgs a) {
         const int qrw = 16 * ((jj + x) >> 3) + 8 * hh + ((jj + x) & 7);
         bool ok = true;
         if (need) {
-          const int bit = ((cur.qoff + qrw) >> cur.lq) * cur.mk + (klocal >> cur.lk);
-          ok = ((cur.live >> bit) & 1u) && kvalid && cur.q0 + qrw < sq32 &&
-               (!a.causal || (int64_t)key <= (int64_t)cur.q0 + qrw + a.off);
+          const int bit = ((qoff + qrw) >> lq) * mk + (kloc >> lk);
+          ok = ((live >> bit) & 1u) & kvalid & (q0 + qrw < sq32) &
+               (!a.causal || (int64_t)key <= (int64_t)q0 + qrw + a.off);
         }
-        const float p = ok ? fexp2(__builtin_fmaf(s[jj + x], a.scale_log2, -s_lse[buf][qrw])) : 0.f;
+        // Allowed pairs have a finite LSE (the row has a key).
+        const float p = ok ? fexp2(__builtin_fmaf(s[jj + x], a.scale_log2, -lse_s[qrw] * kLog2e)) : 0.f;
         pp[x] = p;
-        dd[x] = p * (dp[jj + x] - s_del[buf][qrw]);
+        dd[x] = p * (dp[jj + x] - del_s[qrw]);
       }
       pw[jj / 2] = pack_bf16x2(pp[0], pp[1]);
       dw[jj / 2] = pack_bf16x2(dd[0], dd[1]);
@@ -494,29 +452,37 @@ __global__ __launch_bounds__(2 * TK) void k_bwd_dkdv(BwdArgs a) {
       const bf16x8 db = as_bf16x8(dw[4 * c2], dw[4 * c2 + 1], dw[4 * c2 + 2], dw[4 * c2 + 3]);
 #pragma unroll
       for (int u = 0; u < NDB; ++u) {
-        dv[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(dos, RS, 16 * c2, 32 * u, lane), pb, dv[u], 0, 0, 0);
-        dk[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(qs, RS, 16 * c2, 32 * u, lane), db, dk[u], 0, 0, 0);
+        dv[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag_s<D>(dos, 16 * c2, 32 * u, lane), pb, dv[u], 0, 0, 0);
+        dk[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag_s<D>(qs, 16 * c2, 32 * u, lane), db, dk[u], 0, 0, 0);
       }
     }
-    if (more) store(buf ^ 1);
-    __syncthreads();
-    cur = nxt;
-    have = more;
-    buf ^= 1;
+  };
+
+  // ---- pipeline: chunk e computed while chunks e+1 .. e+3 load ----
+  for (int j = 0; j < NBUF - 1 && e0 + j < e1; ++j) issue(e0 + j, j);
+  for (int e = e0; e < e1; ++e) {
+    // chunk e's loads (this wave's) are done when at most the later chunks' remain
+    const int ahead = min(e1 - 1 - e, NBUF - 2);
+    if (ahead >= 2) BSA_WAIT_VM(2 * LPC);
+    else if (ahead == 1) BSA_WAIT_VM(LPC);
+    else BSA_WAIT_VM(0);
+    __syncthreads();  // every wave's part of chunk e is in LDS; chunk e-1's buffer is free
+    if (e + NBUF - 1 < e1) issue(e + NBUF - 1, (e - e0 + NBUF - 1) & (NBUF - 1));
+    compute(e, lds + ((e - e0) & (NBUF - 1)) * BUFB);
   }
 
   if (kvalid) {
-    uint16_t *kp = (uint16_t *)a.dk + b * a.dk_sb + g * a.dk_sh + (int64_t)key * a.dk_ss;
-    uint16_t *vp = (uint16_t *)a.dv + b * a.dv_sb + g * a.dv_sh + (int64_t)key * a.dv_ss;
+    uint16_t *kp_ = (uint16_t *)a.dk + b * a.dk_sb + g * a.dk_sh + (int64_t)key * a.dk_ss;
+    uint16_t *vp_ = (uint16_t *)a.dv + b * a.dv_sb + g * a.dv_sh + (int64_t)key * a.dv_ss;
 #pragma unroll
     for (int u = 0; u < NDB; ++u)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d0 = 32 * u + 8 * q4 + 4 * hh;
-        *(uint2 *)(kp + d0) = make_uint2(pack_bf16x2(dk[u][4 * q4] * a.scale, dk[u][4 * q4 + 1] * a.scale),
-                                         pack_bf16x2(dk[u][4 * q4 + 2] * a.scale, dk[u][4 * q4 + 3] * a.scale));
-        *(uint2 *)(vp + d0) = make_uint2(pack_bf16x2(dv[u][4 * q4], dv[u][4 * q4 + 1]),
-                                         pack_bf16x2(dv[u][4 * q4 + 2], dv[u][4 * q4 + 3]));
+        *(uint2 *)(kp_ + d0) = make_uint2(pack_bf16x2(dk[u][4 * q4] * a.scale, dk[u][4 * q4 + 1] * a.scale),
+                                          pack_bf16x2(dk[u][4 * q4 + 2] * a.scale, dk[u][4 * q4 + 3] * a.scale));
+        *(uint2 *)(vp_ + d0) = make_uint2(pack_bf16x2(dv[u][4 * q4], dv[u][4 * q4 + 1]),
+                                          pack_bf16x2(dv[u][4 * q4 + 2], dv[u][4 * q4 + 3]));
       }
   }
 }
@@ -535,14 +501,14 @@ void launch_d(const BwdArgs &a, unsigned dq_grid, unsigned kv_grid, hipStream_t 
   }
   if (kv_grid) {
     if (a.tk == 128) hipLaunchKernelGGL((k_bwd_dkdv<D, 128>), dim3(kv_grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_bwd_dkdv<D, 64>), dim3(kv_grid), dim3(128), 0, s, a);
+    else hipLaunchKernelGGL((k_bwd_dkdv<D, 64>), dim3(kv_grid), dim3(256), 0, s, a);
   }
 }
 
 }  // namespace
 
 bsa_status backward_launch(const Plan &p, const BwdArgs &a, hipStream_t s) {
-  const int64_t kv_items = (int64_t)p.B * p.Hkv * p.nkt;
+  const int64_t kv_items = (int64_t)p.B * p.Hkv * ((p.nkt * p.rg.tk + 127) / 128);
   if (p.nrows > 0x7fffffff || kv_items > 0x7fffffff)
     return fail(BSA_ERR_UNSUPPORTED, "too many tiles for one launch");
   const unsigned dq_grid = (unsigned)p.nrows, kv_grid = (unsigned)kv_items;

@@ -96,6 +96,8 @@ struct BwdArgs {
   int64_t dk_sb, dk_sh, dk_ss, dv_sb, dv_sh, dv_ss;
   const int32_t *row_ent, *list_off, *ent_kt;
   const uint32_t *ent_live;
+  const int32_t *t_off, *t_q0, *t_meta;  // key-major chunk index
+  const uint32_t *t_live;
   const HeadMeta *hm;
   int64_t Sq, Skv, off, nqt, nkt;
   int32_t Hq, Hkv, G, tq, tr, tk, pack, uni, causal, nlb;
@@ -115,6 +117,20 @@ bsa_status plan_features(Plan &p, const uint8_t *mask, const int32_t *page_table
 bsa_status plan_build(Plan &p, const uint8_t *mask, const int32_t *page_table, void *scratch,
                       size_t scratch_bytes);
 size_t plan_scratch_bytes(const Plan &p);
+
+// Key-major chunk index of a plan for the backward pass: for every (list
+// batch, kv head, group of nkt_per consecutive key tiles = 128 keys), the
+// 32-query chunks that may see one of its keys, in (head, query) order: first
+// query, a packed word (head within the group | chunk index within its plan
+// row << 8 | lq << 11 | lk << 16 | mk << 21) and nkt_per live words. Built
+// into caller-provided scratch.
+struct KvIndex {
+  const int32_t *off, *q0, *meta;
+  const uint32_t *live;
+  int64_t nkp;
+};
+size_t plan_kv_index_bytes(const Plan &p, int nkt_per);
+bsa_status plan_kv_index(const Plan &p, int nkt_per, void *scratch, KvIndex *out, hipStream_t s);
 
 // Block selection from pooled scores (bsa_select.hip).
 bsa_status select_blocks(const bsa_problem &pr, int keep_tenths, int top_k, const bsa_tensor &q,

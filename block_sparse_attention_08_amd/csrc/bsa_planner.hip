@@ -467,6 +467,127 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
+// -------------------------------------------------------------------------
+// Key-major chunk index for the backward pass
+// -------------------------------------------------------------------------
+
+struct KvIndexArgs {
+  const int32_t *list_off, *ent_kt;
+  const uint32_t *ent_live;
+  const HeadMeta *hm;
+  int64_t Sq, off, nqt, nkt, nbuckets;
+  int32_t Hq, Hkv, G, nkp, tq, uni, causal;
+  int32_t *cnt;
+  const int32_t *boff;
+  int32_t *q0, *meta;
+  uint32_t *live;
+};
+
+// Lower bound of kt0 in the sorted list [lo, hi), then the live words of
+// tiles kt0 .. kt0 + NKT - 1 (0 for a tile the list does not hold).
+template <int NKT>
+__device__ __forceinline__ void tile_live(const KvIndexArgs &a, int lo, int hi, int kt0, uint32_t (&lv)[NKT]) {
+  const int end = hi;
+  while (lo < hi) {
+    const int mid = lo + ((hi - lo) >> 1);
+    if (a.ent_kt[mid] < kt0) lo = mid + 1;
+    else hi = mid;
+  }
+  for (int t = 0; t < NKT; ++t) {
+    lv[t] = 0u;
+    if (lo < end && a.ent_kt[lo] == kt0 + t) lv[t] = a.ent_live[lo++];
+  }
+}
+
+// One wave per bucket (list batch lb, kv head g, group kp of NKT consecutive
+// key tiles = 128 keys). A chunk is 32 consecutive queries of one head that
+// may see a key of the group: its row's list holds one of the tiles (in
+// union mode the group's table does), its queries exist, it is causally
+// feasible for the group's first key, and a live bit of its query
+// sub-blocks is set. Chunks are emitted in (head, query) order with their
+// first query, a packed word (head within the group | chunk index within
+// the plan row << 8 | lq << 11 | lk << 16 | mk << 21) and the NKT live words.
+// EMIT = false counts them.
+template <bool EMIT, int NKT>
+__global__ void k_kv_chunks(KvIndexArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t bk = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 6;
+  if (bk >= a.nbuckets) return;
+  const int kp = (int)(bk % a.nkp), g = (int)((bk / a.nkp) % a.Hkv), lb = (int)(bk / ((int64_t)a.nkp * a.Hkv));
+  const int kt0 = kp * NKT;
+  const int64_t kb0 = (int64_t)kp * 128;
+  const int cpr = a.tq / 32;
+  const int64_t base = EMIT ? a.boff[bk] : 0;
+  int64_t run = 0;
+  // Emit the chunks of one query range whose flags are in bal (lane = chunk).
+  auto emit = [&](unsigned long long bal, int64_t q0, int hloc, int cidx, const HeadMeta &m,
+                  const uint32_t (&lv)[NKT]) {
+    if (EMIT && ((bal >> lane) & 1ull)) {
+      const int64_t idx = base + run + __popcll(bal & (unsigned long long)lo_mask(lane));
+      a.q0[idx] = (int32_t)q0;
+      a.meta[idx] = hloc | (cidx << 8) | (m.lq << 11) | (m.lk << 16) | (m.mk << 21);
+      for (int t = 0; t < NKT; ++t) a.live[NKT * idx + t] = lv[t];
+    }
+    run += __popcll(bal);
+  };
+  auto feasible = [&](int64_t q0) {
+    if (q0 >= a.Sq) return false;
+    const int64_t last = min(q0 + 31, a.Sq - 1);
+    return !(a.causal && kb0 > last + a.off);
+  };
+  if (a.uni) {
+    const int64_t l = (int64_t)lb * a.Hkv + g;
+    uint32_t lv[NKT];
+    tile_live<NKT>(a, a.list_off[l], a.list_off[l + 1], kt0, lv);
+    bool any = false;
+    for (int t = 0; t < NKT; ++t) any |= lv[t] != 0u;
+    if (any) {
+      const int64_t nch = (a.Sq + 31) / 32;
+      for (int h = g * a.G; h < (g + 1) * a.G; ++h) {
+        const HeadMeta m = a.hm[h];
+        for (int64_t c0 = 0; c0 < nch; c0 += 64) {
+          const int64_t q0 = 32 * (c0 + lane);
+          emit(__ballot(c0 + lane < nch && feasible(q0)), q0, h - g * a.G, 0, m, lv);
+        }
+      }
+    }
+  } else {
+    for (int h = g * a.G; h < (g + 1) * a.G; ++h) {
+      const HeadMeta m = a.hm[h];
+      const int niq = m.lq >= 5 ? 1 : (32 >> m.lq);
+      for (int64_t qb = 0; qb < a.nqt; qb += 64) {
+        const int64_t qt = qb + lane;
+        uint32_t lv[NKT];
+        bool any = false;
+        for (int t = 0; t < NKT; ++t) lv[t] = 0u;
+        if (qt < a.nqt) {
+          const int64_t l = ((int64_t)lb * a.Hq + h) * a.nqt + qt;
+          tile_live<NKT>(a, a.list_off[l], a.list_off[l + 1], kt0, lv);
+          for (int t = 0; t < NKT; ++t) any |= lv[t] != 0u;
+        }
+        unsigned long long rows = __ballot(any);
+        while (rows) {
+          const int bit = __builtin_ctzll(rows);
+          rows &= rows - 1;
+          uint32_t rl[NKT];
+          for (int t = 0; t < NKT; ++t) rl[t] = __shfl(lv[t], bit);
+          const int64_t q0 = (qb + bit) * a.tq + 32 * lane;  // lane = chunk of the row
+          bool ok = lane < cpr && feasible(q0);
+          if (ok) {
+            const int iq0 = (32 * lane) >> m.lq;
+            const uint64_t cb = ((1ull << (m.mk * niq)) - 1ull) << (iq0 * m.mk);
+            bool hit = false;
+            for (int t = 0; t < NKT; ++t) hit |= ((uint64_t)rl[t] & cb) != 0;
+            ok = hit;
+          }
+          emit(__ballot(ok), q0, h - g * a.G, lane, m, rl);
+        }
+      }
+    }
+  }
+  if (!EMIT && lane == 0) a.cnt[bk] = (int32_t)run;
+}
+
 // Live-bit geometry of each head for tiles of tq x tk: query sub-blocks of
 // min(bq, tq) rows (one sub-block in union mode, whose bits are per key
 // sub-block only), key sub-blocks of min(bk, tk) keys, mk key sub-blocks per
@@ -597,6 +718,61 @@ bsa_status plan_build(Plan &p, const uint8_t *mask, const int32_t *page_table, v
     hipLaunchKernelGGL(k_lpt_place, dim3((unsigned)nchunks), dim3(kThreads), 0, s, raw_items,
                        p.counters, nchunks, hist, (int4 *)p.items);
   }
+  HIP_TRY(hipGetLastError());
+  return BSA_OK;
+}
+
+// Upper bound on the chunks of the key-major index.
+static int64_t kv_chunk_cap(const Plan &p, int nkt_per) {
+  const int64_t nkp = (p.nkt + nkt_per - 1) / nkt_per;
+  if (p.uni) return std::max<int64_t>((int64_t)p.nlb * p.Hkv * nkp * p.G * ((p.Sq + 31) / 32), 1);
+  return std::max<int64_t>(p.ent_cap * (p.rg.tq / 32), 1);
+}
+
+size_t plan_kv_index_bytes(const Plan &p, int nkt_per) {
+  const int64_t nkp = (p.nkt + nkt_per - 1) / nkt_per;
+  const int64_t nb = (int64_t)p.nlb * p.Hkv * nkp;
+  const int64_t cap = kv_chunk_cap(p, nkt_per);
+  size_t b = 0;
+  b += align_up(sizeof(int32_t) * (nb + 1));              // counts
+  b += align_up(sizeof(int32_t) * (nb + 1));              // offsets
+  b += align_up(sizeof(int32_t) * (nb / kScanBlock + 2)); // scan block sums
+  b += align_up(sizeof(int32_t) * cap);                   // first queries
+  b += align_up(sizeof(int32_t) * cap);                   // packed words
+  b += align_up(sizeof(uint32_t) * nkt_per * cap);        // live words
+  return b;
+}
+
+bsa_status plan_kv_index(const Plan &p, int nkt_per, void *scratch, KvIndex *out, hipStream_t s) {
+  const int64_t nkp = (p.nkt + nkt_per - 1) / nkt_per;
+  const int64_t nb = (int64_t)p.nlb * p.Hkv * nkp;
+  const int64_t cap = kv_chunk_cap(p, nkt_per);
+  uint8_t *sp = (uint8_t *)scratch;
+  auto take = [&](size_t bytes) {
+    uint8_t *r = sp;
+    sp += align_up(bytes);
+    return r;
+  };
+  KvIndexArgs a{};
+  a.list_off = p.list_off, a.ent_kt = p.ent_kt, a.ent_live = p.ent_live, a.hm = p.hmeta;
+  a.Sq = p.Sq, a.off = p.off, a.nqt = p.nqt, a.nkt = p.nkt, a.nbuckets = nb;
+  a.Hq = p.Hq, a.Hkv = p.Hkv, a.G = p.G, a.nkp = (int32_t)nkp, a.tq = p.rg.tq;
+  a.uni = p.uni, a.causal = p.causal;
+  a.cnt = (int32_t *)take(sizeof(int32_t) * (nb + 1));
+  int32_t *off = (int32_t *)take(sizeof(int32_t) * (nb + 1));
+  int32_t *bsum = (int32_t *)take(sizeof(int32_t) * (nb / kScanBlock + 2));
+  a.boff = off;
+  a.q0 = (int32_t *)take(sizeof(int32_t) * cap);
+  a.meta = (int32_t *)take(sizeof(int32_t) * cap);
+  a.live = (uint32_t *)take(sizeof(uint32_t) * nkt_per * cap);
+  out->off = off, out->q0 = a.q0, out->meta = a.meta, out->live = a.live, out->nkp = nkp;
+  if (nb == 0) return BSA_OK;
+  const unsigned grid = grid_for(nb * 64);
+  if (nkt_per == 2) hipLaunchKernelGGL((k_kv_chunks<false, 2>), dim3(grid), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL((k_kv_chunks<false, 1>), dim3(grid), dim3(kThreads), 0, s, a);
+  if (bsa_status st = scan(a.cnt, nb, off, bsum, s)) return st;
+  if (nkt_per == 2) hipLaunchKernelGGL((k_kv_chunks<true, 2>), dim3(grid), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL((k_kv_chunks<true, 1>), dim3(grid), dim3(kThreads), 0, s, a);
   HIP_TRY(hipGetLastError());
   return BSA_OK;
 }
