@@ -82,190 +82,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, 
   return __builtin_bit_cast(bf16x8, make_uint4(a, b, c, d));
 }
 
-// ---------------------------------------------------------------------------
-// dQ (and Delta) per plan row
-// ---------------------------------------------------------------------------
-template <int D, int TK, int TQ>
-__global__ __launch_bounds__(2 * TQ) void k_bwd_dq(BwdArgs a) {
-  constexpr int T = 2 * TQ;                     // 64 lanes per 32 query rows
-  constexpr int RS = D + 8;                     // LDS row stride (elements), padded
-  constexpr int TILE = TK * RS;
-  constexpr int CPR = D / 8;                    // 16-byte chunks per row
-  constexpr int LPT = (TK * CPR + T - 1) / T;   // 16-byte loads per thread per tile
-  constexpr int NKB = TK / 32, NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * TILE];  // K, V; two buffers
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 31, hh = lane >> 5;
-  const int r = blockIdx.x;
-  const int nqt = (int)a.nqt;
-  const int nh = a.pack ? a.Hkv : a.Hq;
-  const int qt = r % nqt, hrow = (r / nqt) % nh, b = r / (nqt * nh);
-  const int head = a.pack ? hrow * a.G + (32 * wave) / a.tr : hrow;
-  const int g = (a.pack ? hrow * a.G : hrow) / a.G;
-  const int qbase = a.pack ? 0 : 32 * wave;
-  const int64_t q0 = a.pack ? (int64_t)qt * a.tr + (32 * wave) % a.tr : (int64_t)qt * a.tq + 32 * wave;
-  const int64_t qpos = q0 + n;
-  const bool qvalid = qpos < a.Sq;
-  const HeadMeta hm = a.hm[head];
-
-  // Q and dO rows as B operands (lane: query n, dims 16c + 8hh .. +8); Delta.
-  const uint16_t *Qp = (const uint16_t *)a.q + b * a.q_sb + head * a.q_sh + (qvalid ? qpos : 0) * a.q_ss;
-  const uint16_t *Dp = (const uint16_t *)a.dout + b * a.do_sb + head * a.do_sh + (qvalid ? qpos : 0) * a.do_ss;
-  const uint16_t *Op = (const uint16_t *)a.o + b * a.o_sb + head * a.o_sh + (qvalid ? qpos : 0) * a.o_ss;
-  bf16x8 qb[D / 16], dob[D / 16];
-  float dpart = 0.f;
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    const uint4 xq = qvalid ? *(const uint4 *)(Qp + 16 * c + 8 * hh) : make_uint4(0, 0, 0, 0);
-    const uint4 xd = qvalid ? *(const uint4 *)(Dp + 16 * c + 8 * hh) : make_uint4(0, 0, 0, 0);
-    const uint4 xo = qvalid ? *(const uint4 *)(Op + 16 * c + 8 * hh) : make_uint4(0, 0, 0, 0);
-    qb[c] = __builtin_bit_cast(bf16x8, xq);
-    dob[c] = __builtin_bit_cast(bf16x8, xd);
-    const bf16x8 ov = __builtin_bit_cast(bf16x8, xo);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dpart = __builtin_fmaf((float)ov[i], (float)dob[c][i], dpart);
-  }
-  const float delta = halfwave_sum(dpart);
-  const int64_t rowix = ((int64_t)b * a.Hq + head) * a.Sq + qpos;
-  if (qvalid && hh == 0) a.delta[rowix] = delta;
-  const float L = qvalid ? a.lse[rowix] : -INFINITY;
-  // exp2(s * scale_log2 - lse2) is P; +inf makes P = 0 for rows without keys
-  // and for padding rows past the sequence end.
-  const float lse2 = L == -INFINITY ? INFINITY : L * kLog2e;
-
-  const int e0 = a.row_ent[2 * r], e1 = a.row_ent[2 * r + 1];
-  const uint16_t *Kb = (const uint16_t *)a.k + b * a.k_sb + g * a.k_sh;
-  const uint16_t *Vb = (const uint16_t *)a.v + b * a.v_sb + g * a.v_sh;
-  uint4 kr[LPT], vr[LPT];
-  auto load = [&](int e) {
-    const int64_t k0 = (int64_t)a.ent_kt[e] * TK;
-    const int64_t left = a.Skv - k0;
-#pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int c = tid + T * u;
-      const int row = c / CPR, col = (c % CPR) * 8;
-      const bool ok = c < TK * CPR && row < left;
-      kr[u] = ok ? *(const uint4 *)(Kb + (k0 + row) * a.k_ss + col) : make_uint4(0, 0, 0, 0);
-      vr[u] = ok ? *(const uint4 *)(Vb + (k0 + row) * a.v_ss + col) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store = [&](int buf) {
-    uint16_t *ks = lds + buf * 2 * TILE, *vs = ks + TILE;
-#pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int c = tid + T * u;
-      if (c < TK * CPR) {
-        const int row = c / CPR, col = (c % CPR) * 8;
-        *(uint4 *)(ks + row * RS + col) = kr[u];
-        *(uint4 *)(vs + row * RS + col) = vr[u];
-      }
-    }
-  };
-
-  // Live-bit geometry of this wave's rows (as in the forward).
-  const int iq_lo = qbase >> hm.lq;
-  const int niq = hm.lq >= 5 ? 1 : (32 >> hm.lq);
-  const uint64_t wbits = ((1ull << (hm.mk * niq)) - 1ull) << (iq_lo * hm.mk);
-  const int qsub = ((qbase + n) >> hm.lq) * hm.mk;
-  const int skv32 = (int)a.Skv;
-  const int qlim0 = (int)max<int64_t>(-64, min<int64_t>(q0 + a.off, a.Skv));
-
-  f32x16 dq[NDB];
-#pragma unroll
-  for (int u = 0; u < NDB; ++u) dq[u] = f32x16{};
-
-  if (e0 < e1) {
-    load(e0);
-    store(0);
-    __syncthreads();
-  }
-  for (int e = e0; e < e1; ++e) {
-    const int buf = (e - e0) & 1;
-    if (e + 1 < e1) load(e + 1);
-    const uint16_t *ks = lds + buf * 2 * TILE, *vs = ks + TILE;
-    const int kb0 = a.ent_kt[e] * TK;
-    const uint32_t live = a.ent_live[e];
-    const bool need = (kb0 + TK > skv32) || (a.causal && kb0 + TK - 1 > qlim0) ||
-                      ((uint64_t)live & wbits) != wbits;
-    // Allowed keys of this lane's query as bit masks over the tile.
-    uint64_t km[(TK + 63) / 64];
-#pragma unroll
-    for (int w64 = 0; w64 < (TK + 63) / 64; ++w64) km[w64] = ~0ull;
-    if (need) {
-      const uint32_t lbits = live >> qsub;
-      int lim = skv32 - kb0;
-      if (a.causal) lim = min(lim, qlim0 + n + 1 - kb0);
-      const int klim = max(0, min(lim, TK));
-      const int ak = 1 << hm.lk;
-      const uint64_t sub = ak >= 64 ? ~0ull : ((1ull << ak) - 1ull);
-#pragma unroll
-      for (int w64 = 0; w64 < (TK + 63) / 64; ++w64) {
-        uint64_t m = 0;
-        for (int ik = 0; ik < hm.mk; ++ik)
-          if ((lbits >> ik) & 1u) {
-            const int k0b = ik * ak - 64 * w64;
-            if (k0b >= 64 || k0b + ak <= 0) continue;
-            m |= k0b >= 0 ? sub << k0b : sub >> -k0b;
-          }
-        const int lo = klim - 64 * w64;
-        m &= lo >= 64 ? ~0ull : (lo <= 0 ? 0ull : ((1ull << lo) - 1ull));
-        km[w64] = m >> (8 * hh);  // accumulator keys are offset by 8 on the upper half-wave
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < NKB; ++t) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-      const uint16_t *kr0 = ks + (32 * t + perm_rows(n)) * RS + 8 * hh;
-      const uint16_t *vr0 = vs + (32 * t + perm_rows(n)) * RS + 8 * hh;
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(kr0 + 16 * c), qb[c], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(vr0 + 16 * c), dob[c], dp, 0, 0, 0);
-      }
-      uint32_t dsw[8];
-#pragma unroll
-      for (int jj = 0; jj < 16; jj += 2) {
-        float ds2[2];
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const int kl = 32 * t + 16 * ((jj + x) >> 3) + ((jj + x) & 7);  // without the 8*hh term
-          const bool ok = (km[kl / 64] >> (kl % 64)) & 1ull;
-          const float p = ok ? fexp2(__builtin_fmaf(s[jj + x], a.scale_log2, -lse2)) : 0.f;
-          ds2[x] = p * (dp[jj + x] - delta);
-        }
-        dsw[jj / 2] = pack_bf16x2(ds2[0], ds2[1]);
-      }
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const bf16x8 bop = as_bf16x8(dsw[4 * c2], dsw[4 * c2 + 1], dsw[4 * c2 + 2], dsw[4 * c2 + 3]);
-#pragma unroll
-        for (int u = 0; u < NDB; ++u)
-          dq[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(ks, RS, 32 * t + 16 * c2, 32 * u, lane),
-                                                          bop, dq[u], 0, 0, 0);
-      }
-    }
-    if (e + 1 < e1) store(buf ^ 1);
-    __syncthreads();
-  }
-
-  if (qvalid) {
-    uint16_t *dp = (uint16_t *)a.dq + b * a.dq_sb + head * a.dq_sh + qpos * a.dq_ss;
-#pragma unroll
-    for (int u = 0; u < NDB; ++u)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * u + 8 * q4 + 4 * hh;
-        *(uint2 *)(dp + d0) = make_uint2(pack_bf16x2(dq[u][4 * q4] * a.scale, dq[u][4 * q4 + 1] * a.scale),
-                                         pack_bf16x2(dq[u][4 * q4 + 2] * a.scale, dq[u][4 * q4 + 3] * a.scale));
-      }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// dK, dV per (batch, kv head, 128 keys)
-// ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(4))) const int32_t cint32;
 typedef __attribute__((address_space(4))) const uint32_t cuint32;
@@ -311,6 +127,185 @@ __device__ __forceinline__ T *uni(T *p) {
 // s_waitcnt with only the vector-memory counter constrained (<= n).
 #define BSA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
+// ---------------------------------------------------------------------------
+// dQ (and Delta) per plan row
+// ---------------------------------------------------------------------------
+// K and V tiles stream from HBM straight into LDS (buffer loads to LDS, rows
+// past the sequence end read as zero), two buffers, the next tile's loads in
+// flight while the current one is computed. K is read as rows (the S^T
+// operand) and transposed (the K^T operand of dQ^T); V as rows.
+template <int D, int TK, int TQ>
+__global__ __launch_bounds__(2 * TQ, TQ == 128 ? 2 : 1) void k_bwd_dq(BwdArgs a) {
+  constexpr int T = 2 * TQ;                     // 64 lanes per 32 query rows
+  constexpr int WAVES = TQ / 32;
+  constexpr int ROWB = 2 * D;
+  constexpr int TILEB = TK * ROWB;              // one K (or V) tile
+  constexpr int CPR = D / 8;
+  constexpr int RPL = T / CPR;                  // tile rows covered by one load
+  constexpr int LOADS = TILEB / (T * 16);       // loads per thread per tile
+  constexpr int NKB = TK / 32, NDB = D / 32;
+  static_assert(RPL % 16 == 0 && LOADS >= 1, "load geometry");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * TILEB];  // K, V; two buffers
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, hh = lane >> 5;
+  const int r = blockIdx.x;
+  const int nqt = (int)a.nqt;
+  const int nh = a.pack ? a.Hkv : a.Hq;
+  const int qt = r % nqt, hrow = (r / nqt) % nh, b = r / (nqt * nh);
+  const int head = a.pack ? hrow * a.G + (32 * wave) / a.tr : hrow;
+  const int g = (a.pack ? hrow * a.G : hrow) / a.G;
+  const int qbase = a.pack ? 0 : 32 * wave;
+  const int64_t q0 = a.pack ? (int64_t)qt * a.tr + (32 * wave) % a.tr : (int64_t)qt * a.tq + 32 * wave;
+  const int64_t qpos = q0 + n;
+  const bool qvalid = qpos < a.Sq;
+  const HeadMeta hm = a.hm[head];
+  (void)WAVES;
+
+  // Q and dO rows as B operands (lane: query n, dims 16c + 8hh .. +8); Delta.
+  const uint16_t *Qp = (const uint16_t *)a.q + b * a.q_sb + head * a.q_sh + (qvalid ? qpos : 0) * a.q_ss;
+  const uint16_t *Dp = (const uint16_t *)a.dout + b * a.do_sb + head * a.do_sh + (qvalid ? qpos : 0) * a.do_ss;
+  const uint16_t *Op = (const uint16_t *)a.o + b * a.o_sb + head * a.o_sh + (qvalid ? qpos : 0) * a.o_ss;
+  bf16x8 qb[D / 16], dob[D / 16];
+  float dpart = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    const uint4 xq = qvalid ? *(const uint4 *)(Qp + 16 * c + 8 * hh) : make_uint4(0, 0, 0, 0);
+    const uint4 xd = qvalid ? *(const uint4 *)(Dp + 16 * c + 8 * hh) : make_uint4(0, 0, 0, 0);
+    const uint4 xo = qvalid ? *(const uint4 *)(Op + 16 * c + 8 * hh) : make_uint4(0, 0, 0, 0);
+    qb[c] = __builtin_bit_cast(bf16x8, xq);
+    dob[c] = __builtin_bit_cast(bf16x8, xd);
+    const bf16x8 ov = __builtin_bit_cast(bf16x8, xo);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dpart = __builtin_fmaf((float)ov[i], (float)dob[c][i], dpart);
+  }
+  const float delta = halfwave_sum(dpart);
+  const int64_t rowix = ((int64_t)b * a.Hq + head) * a.Sq + qpos;
+  if (qvalid && hh == 0) a.delta[rowix] = delta;
+  const float L = qvalid ? a.lse[rowix] : -INFINITY;
+  // exp2(s * scale_log2 - lse2) is P; +inf makes P = 0 for rows without keys
+  // and for padding rows past the sequence end.
+  const float lse2 = L == -INFINITY ? INFINITY : L * kLog2e;
+
+  const int e0 = a.row_ent[2 * r], nent = a.row_ent[2 * r + 1] - e0;
+  const uint16_t *Kb = (const uint16_t *)a.k + b * a.k_sb + g * a.k_sh;
+  const uint16_t *Vb = (const uint16_t *)a.v + b * a.v_sb + g * a.v_sh;
+  const int skv32 = (int)a.Skv;  // sequence lengths are below 2^31
+  const int trow = tid / CPR, tpos = tid % CPR;
+  const int koff0 = trow * (int)a.k_ss * 2 + ((tpos ^ swz<D>(trow)) << 4);
+  const int voff0 = trow * (int)a.v_ss * 2 + ((tpos ^ swz<D>(trow)) << 4);
+  // Loads of tile j (entry e0 + j) into buffer j & 1: K at 2 * buf * TILEB, V after it.
+  auto issue = [&](int j) {
+    const int k0 = ((const cint32 *)a.ent_kt)[e0 + j] * TK;
+    const int left = min(skv32 - k0, TK);
+    uint8_t *dst = lds + 2 * (j & 1) * TILEB;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(Kb + (int64_t)k0 * a.k_ss), 0, (left - 1) * (int)a.k_ss * 2 + D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(Vb + (int64_t)k0 * a.v_ss), 0, (left - 1) * (int)a.v_ss * 2 + D * 2, 0x00020000);
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      uint8_t *d = dst + (u * T + wave * 64) * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)d, 16, koff0 + u * RPL * (int)a.k_ss * 2, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(d + TILEB), 16, voff0 + u * RPL * (int)a.v_ss * 2, 0, 0, 0);
+    }
+  };
+
+  // Live-bit geometry of this wave's rows (as in the forward).
+  const int iq_lo = qbase >> hm.lq;
+  const int niq = hm.lq >= 5 ? 1 : (32 >> hm.lq);
+  const uint64_t wbits = ((1ull << (hm.mk * niq)) - 1ull) << (iq_lo * hm.mk);
+  const int qsub = ((qbase + n) >> hm.lq) * hm.mk;
+  const int qlim0 = (int)max<int64_t>(-64, min<int64_t>(q0 + a.off, a.Skv));
+
+  f32x16 dq[NDB];
+#pragma unroll
+  for (int u = 0; u < NDB; ++u) dq[u] = f32x16{};
+
+  if (nent > 0) issue(0);
+  for (int j = 0; j < nent; ++j) {
+    __builtin_amdgcn_s_waitcnt(0);  // tile j has landed (this wave's part)
+    __syncthreads();                // ... every wave's; tile j-1's buffer is free
+    if (j + 1 < nent) issue(j + 1);
+    const uint8_t *__restrict__ ks = lds + 2 * (j & 1) * TILEB;
+    const uint8_t *__restrict__ vs = ks + TILEB;
+    const int kb0 = ((const cint32 *)a.ent_kt)[e0 + j] * TK;
+    const uint32_t live = ((const cuint32 *)a.ent_live)[e0 + j];
+    const bool need = (kb0 + TK > skv32) || (a.causal && kb0 + TK - 1 > qlim0) ||
+                      ((uint64_t)live & wbits) != wbits;
+    // Allowed keys of this lane's query as bit masks over the tile.
+    uint64_t km[(TK + 63) / 64];
+#pragma unroll
+    for (int w64 = 0; w64 < (TK + 63) / 64; ++w64) km[w64] = ~0ull;
+    if (need) {
+      const uint32_t lbits = live >> qsub;
+      int lim = skv32 - kb0;
+      if (a.causal) lim = min(lim, qlim0 + n + 1 - kb0);
+      const int klim = max(0, min(lim, TK));
+      const int ak = 1 << hm.lk;
+      const uint64_t sub = ak >= 64 ? ~0ull : ((1ull << ak) - 1ull);
+#pragma unroll
+      for (int w64 = 0; w64 < (TK + 63) / 64; ++w64) {
+        uint64_t m = 0;
+        for (int ik = 0; ik < hm.mk; ++ik)
+          if ((lbits >> ik) & 1u) {
+            const int k0b = ik * ak - 64 * w64;
+            if (k0b >= 64 || k0b + ak <= 0) continue;
+            m |= k0b >= 0 ? sub << k0b : sub >> -k0b;
+          }
+        const int lo = klim - 64 * w64;
+        m &= lo >= 64 ? ~0ull : (lo <= 0 ? 0ull : ((1ull << lo) - 1ull));
+        km[w64] = m >> (8 * hh);  // accumulator keys are offset by 8 on the upper half-wave
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NKB; ++t) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+      const int kr = 32 * t + perm_rows(n);
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(ks, kr, 2 * c + hh), qb[c], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(vs, kr, 2 * c + hh), dob[c], dp, 0, 0, 0);
+      }
+      uint32_t dsw[8];
+#pragma unroll
+      for (int jj = 0; jj < 16; jj += 2) {
+        float ds2[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int kl = 32 * t + 16 * ((jj + x) >> 3) + ((jj + x) & 7);  // without the 8*hh term
+          const bool ok = (km[kl / 64] >> (kl % 64)) & 1ull;
+          const float p = ok ? fexp2(__builtin_fmaf(s[jj + x], a.scale_log2, -lse2)) : 0.f;
+          ds2[x] = p * (dp[jj + x] - delta);
+        }
+        dsw[jj / 2] = pack_bf16x2(ds2[0], ds2[1]);
+      }
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const bf16x8 bop = as_bf16x8(dsw[4 * c2], dsw[4 * c2 + 1], dsw[4 * c2 + 2], dsw[4 * c2 + 3]);
+#pragma unroll
+        for (int u = 0; u < NDB; ++u)
+          dq[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag_s<D>(ks, 32 * t + 16 * c2, 32 * u, lane),
+                                                          bop, dq[u], 0, 0, 0);
+      }
+    }
+  }
+
+  if (qvalid) {
+    uint16_t *dp = (uint16_t *)a.dq + b * a.dq_sb + head * a.dq_sh + qpos * a.dq_ss;
+#pragma unroll
+    for (int u = 0; u < NDB; ++u)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * u + 8 * q4 + 4 * hh;
+        *(uint2 *)(dp + d0) = make_uint2(pack_bf16x2(dq[u][4 * q4] * a.scale, dq[u][4 * q4 + 1] * a.scale),
+                                         pack_bf16x2(dq[u][4 * q4 + 2] * a.scale, dq[u][4 * q4 + 3] * a.scale));
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV per (batch, kv head, 128 keys)
+// ---------------------------------------------------------------------------
 // A workgroup owns 128 consecutive keys: NKT = 128 / TKP key tiles of the
 // plan (TKP = 64 or 128), four waves of 32 keys. The query chunks (32 rows)
 // that may see them come from the key-major chunk index built for the call;
@@ -398,54 +393,68 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdArgs a) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dl, 4, lane * 4, 0, 0, 0);
   };
 
-  // One chunk's arithmetic on buffer t (Q at t, dO at t + CHB, LSE and Delta after them).
-  auto compute = [&](int e, const uint8_t *__restrict__ t) {
+  // S = Q K^T and dP = dO V^T of the chunk in buffer t (Q at t, dO at
+  // t + CHB): lane = key n, accumulator j = query row 16*(j/8) + 8*hh + (j%8).
+  auto sdp = [&](const uint8_t *__restrict__ t, f32x16 &s, f32x16 &dp) {
+    const int pr = perm_rows(n);
+    s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(t, pr, 2 * c + hh), kb[c], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(t + CHB, pr, 2 * c + hh), vb[c], dp, 0, 0, 0);
+    }
+  };
+  // P and dS of chunk e from its S and dP, then dV^T += dO^T P and
+  // dK^T += Q^T dS (rows d, columns keys).
+  auto finish = [&](int e, const uint8_t *__restrict__ t, const f32x16 &s, const f32x16 &dp) {
     const int q0 = ((const cint32 *)a.t_q0)[e];
     const int meta = ((const cint32 *)a.t_meta)[e];
     uint32_t live = ((const cuint32 *)a.t_live)[NKT * e];
     if (NKT == 2 && wkt == 1) live = ((const cuint32 *)a.t_live)[NKT * e + 1];
     const int qoff = 32 * ((meta >> 8) & 7), lq = (meta >> 11) & 31, lk = (meta >> 16) & 31, mk = (meta >> 21) & 63;
-    const uint8_t *qs = t, *dos = t + CHB;
-    const float *lse_s = (const float *)(t + 2 * CHB), *del_s = lse_s + 64;
-    // S = Q K^T and dP = dO V^T: lane = key n, accumulator j = query row
-    // 16*(j/8) + 8*hh + (j%8) of the chunk.
-    f32x16 s = f32x16{}, dp = f32x16{};
-    const int pr = perm_rows(n);
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(qs, pr, 2 * c + hh), kb[c], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(dos, pr, 2 * c + hh), vb[c], dp, 0, 0, 0);
+    // Allowed query rows of this lane's key, as a 32-bit mask: live query
+    // sub-blocks (at least 16 rows each, so rows 0-15 and 16-31 each lie in
+    // one), rows that exist, and the causal bound.
+    const int ik = kloc >> lk;
+    const uint32_t lo16 = (live >> ((qoff >> lq) * mk + ik)) & 1u;
+    const uint32_t hi16 = (live >> (((qoff + 16) >> lq) * mk + ik)) & 1u;
+    uint32_t rows = (lo16 ? 0x0000ffffu : 0u) | (hi16 ? 0xffff0000u : 0u);
+    const int nrow = sq32 - q0;
+    if (nrow < 32) rows &= (1u << nrow) - 1u;
+    if (a.causal) {
+      const int64_t first = (int64_t)key - q0 - a.off;  // first query row that may see the key
+      rows = first <= 0 ? rows : (first >= 32 ? 0u : rows & ~((1u << first) - 1u));
     }
-    // Is every (query, key) pair of this wave's 32 x 32 block allowed?
-    const int ik0 = ((32 * wave) % TKP) >> lk, nik = lk >= 5 ? 1 : (32 >> lk);
-    const int iq0 = qoff >> lq, niq = lq >= 5 ? 1 : (32 >> lq);
-    uint64_t wb = ((1ull << nik) - 1ull) << (iq0 * mk + ik0);
-    if (niq == 2) wb |= wb << mk;
-    const int wk0 = kb0 + 32 * wave;
-    const bool need = ((uint64_t)live & wb) != wb || wk0 + 31 >= skv32 || q0 + 31 >= sq32 ||
-                      (a.causal && (int64_t)wk0 + 31 > (int64_t)q0 + a.off);
+    if (!kvalid) rows = 0u;
+    const uint32_t myrows = rows >> (8 * hh);  // bit 16*(j/8) + (j%8) <-> accumulator j
+    const float *lse_s = (const float *)(t + 2 * CHB), *del_s = lse_s + 64;
+    float lrow[16], drow[16];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const float4 l0 = *(const float4 *)(lse_s + 16 * h2 + 8 * hh), l1 = *(const float4 *)(lse_s + 16 * h2 + 8 * hh + 4);
+      const float4 d0 = *(const float4 *)(del_s + 16 * h2 + 8 * hh), d1 = *(const float4 *)(del_s + 16 * h2 + 8 * hh + 4);
+      lrow[8 * h2 + 0] = l0.x, lrow[8 * h2 + 1] = l0.y, lrow[8 * h2 + 2] = l0.z, lrow[8 * h2 + 3] = l0.w;
+      lrow[8 * h2 + 4] = l1.x, lrow[8 * h2 + 5] = l1.y, lrow[8 * h2 + 6] = l1.z, lrow[8 * h2 + 7] = l1.w;
+      drow[8 * h2 + 0] = d0.x, drow[8 * h2 + 1] = d0.y, drow[8 * h2 + 2] = d0.z, drow[8 * h2 + 3] = d0.w;
+      drow[8 * h2 + 4] = d1.x, drow[8 * h2 + 5] = d1.y, drow[8 * h2 + 6] = d1.z, drow[8 * h2 + 7] = d1.w;
+    }
     uint32_t pw[8], dw[8];
 #pragma unroll
     for (int jj = 0; jj < 16; jj += 2) {
       float pp[2], dd[2];
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
-        const int qrw = 16 * ((jj + x) >> 3) + 8 * hh + ((jj + x) & 7);
-        bool ok = true;
-        if (need) {
-          const int bit = ((qoff + qrw) >> lq) * mk + (kloc >> lk);
-          ok = ((live >> bit) & 1u) & kvalid & (q0 + qrw < sq32) &
-               (!a.causal || (int64_t)key <= (int64_t)q0 + qrw + a.off);
-        }
+        const int j = jj + x;
+        const bool ok = (myrows >> (16 * (j >> 3) + (j & 7))) & 1u;
         // Allowed pairs have a finite LSE (the row has a key).
-        const float p = ok ? fexp2(__builtin_fmaf(s[jj + x], a.scale_log2, -lse_s[qrw] * kLog2e)) : 0.f;
+        const float p = ok ? fexp2(__builtin_fmaf(s[j], a.scale_log2, -lrow[j] * kLog2e)) : 0.f;
         pp[x] = p;
-        dd[x] = p * (dp[jj + x] - del_s[qrw]);
+        dd[x] = p * (dp[j] - drow[j]);
       }
       pw[jj / 2] = pack_bf16x2(pp[0], pp[1]);
       dw[jj / 2] = pack_bf16x2(dd[0], dd[1]);
     }
-    // dV^T += dO^T P and dK^T += Q^T dS (rows d, columns keys).
+    const uint8_t *qs = t, *dos = t + CHB;
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
       const bf16x8 pb = as_bf16x8(pw[4 * c2], pw[4 * c2 + 1], pw[4 * c2 + 2], pw[4 * c2 + 3]);
@@ -457,18 +466,30 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdArgs a) {
       }
     }
   };
+  auto buf_of = [&](int e) { return lds + ((e - e0) & (NBUF - 1)) * BUFB; };
 
-  // ---- pipeline: chunk e computed while chunks e+1 .. e+3 load ----
+  // ---- pipeline ----
+  // Iteration e: chunk e+1 has landed and chunk e is still in LDS; chunks
+  // e+2 and e+3 are loading. The S and dP MFMAs of chunk e+1 are issued next
+  // to the exponentials of chunk e, then chunk e's dV, dK MFMAs follow.
   for (int j = 0; j < NBUF - 1 && e0 + j < e1; ++j) issue(e0 + j, j);
-  for (int e = e0; e < e1; ++e) {
-    // chunk e's loads (this wave's) are done when at most the later chunks' remain
-    const int ahead = min(e1 - 1 - e, NBUF - 2);
-    if (ahead >= 2) BSA_WAIT_VM(2 * LPC);
-    else if (ahead == 1) BSA_WAIT_VM(LPC);
+  f32x16 sa, da, sb, db2;
+  if (e0 < e1) {
+    if (e0 + 2 < e1) BSA_WAIT_VM(2 * LPC);
+    else if (e0 + 1 < e1) BSA_WAIT_VM(LPC);
     else BSA_WAIT_VM(0);
-    __syncthreads();  // every wave's part of chunk e is in LDS; chunk e-1's buffer is free
-    if (e + NBUF - 1 < e1) issue(e + NBUF - 1, (e - e0 + NBUF - 1) & (NBUF - 1));
-    compute(e, lds + ((e - e0) & (NBUF - 1)) * BUFB);
+    __syncthreads();
+    sdp(buf_of(e0), sa, da);
+  }
+  for (int e = e0; e < e1; ++e) {
+    if (e + 2 < e1) BSA_WAIT_VM(LPC);
+    else BSA_WAIT_VM(0);
+    __syncthreads();
+    if (e + 3 < e1) issue(e + 3, (e - e0 + 3) & (NBUF - 1));
+    // (on the last chunk this reads a stale buffer; the result is dropped)
+    sdp(buf_of(e + 1), sb, db2);
+    finish(e, buf_of(e), sa, da);
+    sa = sb, da = db2;
   }
 
   if (kvalid) {
