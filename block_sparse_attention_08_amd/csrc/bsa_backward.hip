@@ -87,10 +87,19 @@ typedef __attribute__((address_space(4))) const int32_t cint32;
 typedef __attribute__((address_space(4))) const uint32_t cuint32;
 
 // XOR swizzle of the 16-byte chunks of an LDS row of D bf16: chunk c of row r
-// sits at slot c ^ swz(r), which keeps both the 16-byte row reads and the
-// transpose reads of a 32-row chunk spread over the banks.
+// sits at slot c ^ swz(r). Two read patterns must both spread over the 64
+// banks: a 16-byte row read has 16 lanes on 16 rows of one aligned group of
+// 16 (so swz must differ across those rows), and a transpose read has 32
+// lanes on 4 consecutive rows by 4 consecutive chunks of an aligned group of
+// 4 (so bits 2-3 of swz must differ across those rows). D = 128 (16 chunks,
+// 256-byte rows): swz = (r & 3) << 2 | (r >> 2) & 3. D = 64 (8 chunks,
+// two rows per 256 bytes): the same on the row pair index s = r >> 1,
+// swz = (s & 1) << 2 | (s >> 1) & 3.
 template <int D>
-__device__ __forceinline__ int swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 
 // 16-byte row read: dims 8*c .. 8*c + 7 of row r.
 template <int D>
@@ -368,9 +377,9 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdArgs a) {
   const int trow = tid / CPR, tpos = tid % CPR;
   const int qoff0 = trow * (int)a.q_ss * 2 + ((tpos ^ swz<D>(trow)) << 4);
   const int doff0 = trow * (int)a.do_ss * 2 + ((tpos ^ swz<D>(trow)) << 4);
-  auto issue = [&](int e, int buf) {
-    const int q0 = ((const cint32 *)a.t_q0)[e];
-    const int h = g * a.G + (((const cint32 *)a.t_meta)[e] & 255);
+  // Loads of the chunk with first query q0 and packed word meta into buffer buf.
+  auto issue_qm = [&](int q0, int meta, int buf) {
+    const int h = g * a.G + (meta & 255);
     uint8_t *dst = lds + buf * BUFB;
     const int rows = min(sq32 - q0, 32);        // rows of the chunk that exist (>= 1)
     const uint16_t *qb_ = (const uint16_t *)a.q + b * a.q_sb + h * a.q_sh + (int64_t)q0 * a.q_ss;
@@ -392,29 +401,64 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdArgs a) {
     uint8_t *dl = dst + 2 * CHB + (wave == 1 ? 256 : (wave == 0 ? 0 : 512 + 256 * (wave - 2)));
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dl, 4, lane * 4, 0, 0, 0);
   };
-
-  // S = Q K^T and dP = dO V^T of the chunk in buffer t (Q at t, dO at
-  // t + CHB): lane = key n, accumulator j = query row 16*(j/8) + 8*hh + (j%8).
-  auto sdp = [&](const uint8_t *__restrict__ t, f32x16 &s, f32x16 &dp) {
-    const int pr = perm_rows(n);
-    s = f32x16{}, dp = f32x16{};
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(t, pr, 2 * c + hh), kb[c], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(t + CHB, pr, 2 * c + hh), vb[c], dp, 0, 0, 0);
-    }
+  auto issue = [&](int e, int buf) {
+    issue_qm(((const cint32 *)a.t_q0)[e], ((const cint32 *)a.t_meta)[e], buf);
   };
-  // P and dS of chunk e from its S and dP, then dV^T += dO^T P and
-  // dK^T += Q^T dS (rows d, columns keys).
-  auto finish = [&](int e, const uint8_t *__restrict__ t, const f32x16 &s, const f32x16 &dp) {
+
+  auto buf_of = [&](int e) { return lds + ((e - e0) & (NBUF - 1)) * BUFB; };
+  const int pr = perm_rows(n);
+  // A-operand fragment i of the S, dP MFMAs of the chunk in buffer t: even i
+  // = Q rows, odd i = dO rows, dims 16 * (i / 2) + 8 * hh.
+  auto sdp_frag = [&](const uint8_t *t, int i) { return row_frag<D>(t + (i & 1) * CHB, pr, 2 * (i >> 1) + hh); };
+  // A-operand fragment i of the dV, dK MFMAs: i = 2 * (NDB * c2 + u) + (0: dO^T, 1: Q^T).
+  auto dkv_frag = [&](const uint8_t *t, int i) {
+    const int c2 = (i >> 1) / NDB, u = (i >> 1) % NDB;
+    return tr_frag_s<D>(t + ((i & 1) ? 0 : CHB), 16 * c2, 32 * u, lane);
+  };
+  constexpr int SD = 2 * (D / 16);   // S and dP MFMAs per chunk
+  constexpr int KV = 4 * NDB;        // dV and dK MFMAs per chunk
+
+  // ---- pipeline ----
+  // Iteration e: chunk e+1 has landed and chunk e is still in LDS; chunks
+  // e+2 and e+3 are loading. One straight-line block in a fixed order: each
+  // S or dP MFMA of chunk e+1 is followed by a slice of chunk e's
+  // exponentials (its S and dP came from the previous iteration), with LDS
+  // operands read three steps ahead; then chunk e's dV and dK MFMAs with
+  // their transpose reads two steps ahead. sched_barrier(0) keeps the
+  // compiler from regrouping the steps.
+  for (int j = 0; j < NBUF - 1 && e0 + j < e1; ++j) issue(e0 + j, j);
+  f32x16 sa = f32x16{}, da = f32x16{};
+  if (e0 < e1) {
+    if (e0 + 2 < e1) BSA_WAIT_VM(2 * LPC);
+    else if (e0 + 1 < e1) BSA_WAIT_VM(LPC);
+    else BSA_WAIT_VM(0);
+    __syncthreads();
+    const uint8_t *t = buf_of(e0);
+#pragma unroll
+    for (int i = 0; i < SD; ++i) {
+      const bf16x8 f = sdp_frag(t, i);
+      if (i & 1) da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, vb[i >> 1], da, 0, 0, 0);
+      else sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, kb[i >> 1], sa, 0, 0, 0);
+    }
+  }
+  for (int e = e0; e < e1; ++e) {
+    // chunk e's metadata (scalar loads, completed before the LDS work)
     const int q0 = ((const cint32 *)a.t_q0)[e];
     const int meta = ((const cint32 *)a.t_meta)[e];
     uint32_t live = ((const cuint32 *)a.t_live)[NKT * e];
     if (NKT == 2 && wkt == 1) live = ((const cuint32 *)a.t_live)[NKT * e + 1];
+    const int e3 = min(e + 3, e1 - 1);  // chunk e+3 (clamped: unused past the end)
+    const int q03 = ((const cint32 *)a.t_q0)[e3], meta3 = ((const cint32 *)a.t_meta)[e3];
+    if (e + 2 < e1) BSA_WAIT_VM(LPC);
+    else BSA_WAIT_VM(0);
+    __syncthreads();  // chunk e+1 is in LDS; chunk e-1's buffer is free
+    if (e + 3 < e1) issue_qm(q03, meta3, (e - e0 + 3) & (NBUF - 1));
+    const uint8_t *tc = buf_of(e), *tn = buf_of(e + 1);  // tn is stale on the last chunk
+
+    // Allowed query rows of this lane's key in chunk e, as a 32-bit mask:
+    // live query sub-blocks (at least 16 rows each, so rows 0-15 and 16-31
+    // each lie in one), rows that exist, and the causal bound.
     const int qoff = 32 * ((meta >> 8) & 7), lq = (meta >> 11) & 31, lk = (meta >> 16) & 31, mk = (meta >> 21) & 63;
-    // Allowed query rows of this lane's key, as a 32-bit mask: live query
-    // sub-blocks (at least 16 rows each, so rows 0-15 and 16-31 each lie in
-    // one), rows that exist, and the causal bound.
     const int ik = kloc >> lk;
     const uint32_t lo16 = (live >> ((qoff >> lq) * mk + ik)) & 1u;
     const uint32_t hi16 = (live >> (((qoff + 16) >> lq) * mk + ik)) & 1u;
@@ -427,7 +471,7 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdArgs a) {
     }
     if (!kvalid) rows = 0u;
     const uint32_t myrows = rows >> (8 * hh);  // bit 16*(j/8) + (j%8) <-> accumulator j
-    const float *lse_s = (const float *)(t + 2 * CHB), *del_s = lse_s + 64;
+    const float *lse_s = (const float *)(tc + 2 * CHB), *del_s = lse_s + 64;
     float lrow[16], drow[16];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
@@ -438,57 +482,56 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdArgs a) {
       drow[8 * h2 + 0] = d0.x, drow[8 * h2 + 1] = d0.y, drow[8 * h2 + 2] = d0.z, drow[8 * h2 + 3] = d0.w;
       drow[8 * h2 + 4] = d1.x, drow[8 * h2 + 5] = d1.y, drow[8 * h2 + 6] = d1.z, drow[8 * h2 + 7] = d1.w;
     }
-    uint32_t pw[8], dw[8];
-#pragma unroll
-    for (int jj = 0; jj < 16; jj += 2) {
-      float pp[2], dd[2];
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int j = jj + x;
-        const bool ok = (myrows >> (16 * (j >> 3) + (j & 7))) & 1u;
-        // Allowed pairs have a finite LSE (the row has a key).
-        const float p = ok ? fexp2(__builtin_fmaf(s[j], a.scale_log2, -lrow[j] * kLog2e)) : 0.f;
-        pp[x] = p;
-        dd[x] = p * (dp[j] - drow[j]);
-      }
-      pw[jj / 2] = pack_bf16x2(pp[0], pp[1]);
-      dw[jj / 2] = pack_bf16x2(dd[0], dd[1]);
-    }
-    const uint8_t *qs = t, *dos = t + CHB;
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      const bf16x8 pb = as_bf16x8(pw[4 * c2], pw[4 * c2 + 1], pw[4 * c2 + 2], pw[4 * c2 + 3]);
-      const bf16x8 db = as_bf16x8(dw[4 * c2], dw[4 * c2 + 1], dw[4 * c2 + 2], dw[4 * c2 + 3]);
-#pragma unroll
-      for (int u = 0; u < NDB; ++u) {
-        dv[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag_s<D>(dos, 16 * c2, 32 * u, lane), pb, dv[u], 0, 0, 0);
-        dk[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag_s<D>(qs, 16 * c2, 32 * u, lane), db, dk[u], 0, 0, 0);
-      }
-    }
-  };
-  auto buf_of = [&](int e) { return lds + ((e - e0) & (NBUF - 1)) * BUFB; };
 
-  // ---- pipeline ----
-  // Iteration e: chunk e+1 has landed and chunk e is still in LDS; chunks
-  // e+2 and e+3 are loading. The S and dP MFMAs of chunk e+1 are issued next
-  // to the exponentials of chunk e, then chunk e's dV, dK MFMAs follow.
-  for (int j = 0; j < NBUF - 1 && e0 + j < e1; ++j) issue(e0 + j, j);
-  f32x16 sa, da, sb, db2;
-  if (e0 < e1) {
-    if (e0 + 2 < e1) BSA_WAIT_VM(2 * LPC);
-    else if (e0 + 1 < e1) BSA_WAIT_VM(LPC);
-    else BSA_WAIT_VM(0);
-    __syncthreads();
-    sdp(buf_of(e0), sa, da);
-  }
-  for (int e = e0; e < e1; ++e) {
-    if (e + 2 < e1) BSA_WAIT_VM(LPC);
-    else BSA_WAIT_VM(0);
-    __syncthreads();
-    if (e + 3 < e1) issue(e + 3, (e - e0 + 3) & (NBUF - 1));
-    // (on the last chunk this reads a stale buffer; the result is dropped)
-    sdp(buf_of(e + 1), sb, db2);
-    finish(e, buf_of(e), sa, da);
+    f32x16 sb, db2;
+    uint32_t pw[8], dw[8];
+    float pe = 0.f, de = 0.f;
+    {
+      bf16x8 fr[SD];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) fr[i] = sdp_frag(tn, i);
+#pragma unroll
+      for (int i = 0; i < SD; ++i) {
+        if (i + 3 < SD) fr[i + 3] = sdp_frag(tn, i + 3);
+        if (i & 1) db2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i], vb[i >> 1], i == 1 ? f32x16{} : db2, 0, 0, 0);
+        else sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i], kb[i >> 1], i == 0 ? f32x16{} : sb, 0, 0, 0);
+        // P and dS of chunk e: 16 / SD accumulators per step, packed to bf16
+        // pairs as the odd element of each pair is done.
+#pragma unroll
+        for (int k2 = 0; k2 < 16 / SD; ++k2) {
+          const int x = i * (16 / SD) + k2;  // accumulator index
+          const bool ok = (myrows >> (16 * (x >> 3) + (x & 7))) & 1u;
+          // Allowed pairs have a finite LSE (the row has a key).
+          const float p = ok ? fexp2(__builtin_fmaf(sa[x], a.scale_log2, -lrow[x] * kLog2e)) : 0.f;
+          const float dd = p * (da[x] - drow[x]);
+          if (x & 1) {
+            pw[x >> 1] = pack_bf16x2(pe, p);
+            dw[x >> 1] = pack_bf16x2(de, dd);
+          } else {
+            pe = p, de = dd;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    {
+      bf16x8 fr[KV];
+      fr[0] = dkv_frag(tc, 0);
+      fr[1] = dkv_frag(tc, 1);
+#pragma unroll
+      for (int i = 0; i < KV; ++i) {
+        if (i + 2 < KV) fr[i + 2] = dkv_frag(tc, i + 2);
+        const int c2 = (i >> 1) / NDB, u = (i >> 1) % NDB;
+        if (i & 1) {
+          const bf16x8 db = as_bf16x8(dw[4 * c2], dw[4 * c2 + 1], dw[4 * c2 + 2], dw[4 * c2 + 3]);
+          dk[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i], db, dk[u], 0, 0, 0);
+        } else {
+          const bf16x8 pb = as_bf16x8(pw[4 * c2], pw[4 * c2 + 1], pw[4 * c2 + 2], pw[4 * c2 + 3]);
+          dv[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i], pb, dv[u], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     sa = sb, da = db2;
   }
 
