@@ -158,6 +158,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pipeline", action="store_true",
                     help="also time requests with the next plan overlapping the current forward")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward-pass measurement (dense bf16 workloads only)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run three device copies of a 1 GiB tensor (1 GiB read and 1 GiB "
                          "written per launch), to scale HBM byte counters")
@@ -278,6 +280,36 @@ def main():
                   "gbs": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1),
                   "frac_of_hbm_peak": round(sel_bytes / (sel_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
+    # Backward over one plan (dense bf16 workloads): bsa_backward calls timed
+    # with HIP events on the stream they run on, after a forward that gives O
+    # and LSE. FLOPs by the usual five-product count (S recomputed, dP, dV,
+    # dK, dQ: 2.5x the forward's); the kernels execute seven products (S and
+    # dP are formed once per kernel).
+    backward = None
+    if not args.no_backward and not w.paged and w.dtype == "bf16" and sel_keep is None:
+        dout = w.make_dout(device="cuda")
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        pb = bsa.plan(prob, mask, table, lut, stream=stream)
+        pb.forward(q, k, v, o, lse, stream=stream)
+        for _ in range(max(args.warmup, 1)):
+            pb.backward(q, k, v, o, lse, dout, dq, dk, dv, stream=stream)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for a, b in ev:
+            a.record(stream)
+            pb.backward(q, k, v, o, lse, dout, dq, dk, dv, stream=stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        bwd_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        pb.free()
+        bwd_tf = 2.5 * eff_flops / (bwd_ms * 1e-3) / 1e12
+        backward = {"ms": round(bwd_ms, 4), "tflops": round(bwd_tf, 3),
+                    "flops_convention": "2.5 x forward (S, dP, dV, dK, dQ)",
+                    "frac_of_bf16_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+                    "executed_tflops": round(3.5 * eff_flops / (bwd_ms * 1e-3) / 1e12, 3),
+                    "kernels": ["k_bwd_dq", "k_bwd_dkdv", "k_kv_chunks"]}
+        del dout, dq, dk, dv
+
     value = eff_flops / (ms_step * 1e-3) / 1e12
     achieved = eff_flops / (fwd_avg * 1e-3) / 1e12
     esz = 2 if w.dtype == "bf16" else 4
@@ -314,6 +346,8 @@ def main():
     }
     if select is not None:
         line["select"] = select
+    if backward is not None:
+        line["backward"] = backward
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, q, k, v)
     print(json.dumps(line), flush=True)
