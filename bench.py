@@ -44,9 +44,17 @@ def workload(name: str):
         "affine_bs64_w4096": lambda: W.affine(bs=64, window=4096),
         "affine_bs64_w8192": lambda: W.affine(bs=64, window=8192),
         "long_video": lambda: W.long_video(),
+        "decode": lambda: W.decode(q_len=1),
+        "decode_q16": lambda: W.decode(q_len=16),
         "tiny": lambda: W.tiny(),
     }
     return table[name]()
+
+
+# Memory-bound workloads (a few queries per sequence over a long cache): their
+# roofline is HBM bytes, the K and V rows of the selected blocks read once per
+# (sequence, kv group) plus Q, O and LSE, per forward launch.
+HBM_BOUND = {"decode", "decode_q16"}
 
 
 # Workloads whose mask is chosen on the GPU in every step (bsa_select_blocks,
@@ -99,6 +107,37 @@ def allowed_keys_per_row(w, b: int, h: int) -> np.ndarray:
             lim = np.clip(rows + w.causal_offset, -1, w.skv - 1)
             out[rows] = np.where(lim >= 0, csum[np.maximum(lim, 0)], 0)
     return out
+
+
+def effective_flops(w) -> float:
+    """4 * D * (rows x keys) summed over the effective logical blocks of every
+    (batch, head): selected (the group's union in union mode) and causally
+    feasible (first key <= last query + offset), with a block at the end of a
+    sequence counting only the rows and keys that exist. Equal to the plan's
+    whole-block count when the lengths are block multiples; for decode (one
+    query in a 128-row block) it counts the one row."""
+    tot = 0.0
+    for bm in range(w.mask_batches):
+        nb = w.batch if w.mask_broadcast else 1
+        for h in range(w.hq):
+            if w.gqa_union:
+                gs = w.hq // w.hkv
+                u = np.zeros(w.nkb(h), bool)
+                for h2 in range((h // gs) * gs, (h // gs + 1) * gs):
+                    u |= w.head_mask(bm, h2).astype(bool).any(0)
+                blk = np.broadcast_to(u, (w.nqb(h), w.nkb(h))).copy()
+            else:
+                blk = w.head_mask(bm, h).astype(bool).copy()
+            bq, bk = w.bq[h], w.bk[h]
+            q0 = np.arange(w.nqb(h)) * bq
+            k0 = np.arange(w.nkb(h)) * bk
+            rq = np.minimum(bq, w.sq - q0).astype(np.float64)
+            rk = np.minimum(bk, w.skv - k0).astype(np.float64)
+            if w.causal:
+                last_q = np.minimum(q0 + bq, w.sq) - 1
+                blk &= k0[None, :] <= (last_q + w.causal_offset)[:, None]
+            tot += nb * float(rq @ blk.astype(np.float64) @ rk)
+    return 4.0 * w.d * tot
 
 
 def cpu_baseline(w, q, k, v, target_s: float = 20.0):
@@ -244,7 +283,7 @@ def main():
     p0 = step()
     stats = p0.stats()
     p0.free()
-    eff_flops = stats["effective_flops"]
+    eff_flops = effective_flops(w)
     for _ in range(args.warmup):
         step().free()
     torch.cuda.synchronize()
@@ -315,6 +354,20 @@ def main():
     esz = 2 if w.dtype == "bf16" else 4
     compulsory = esz * (q.numel() * 2 + k.numel() + v.numel()) + 4 * lse.numel()
     traffic = measured_traffic(args.workload, None)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "kernel": "k_attn", "compulsory_bytes": compulsory}
+    if args.workload in HBM_BOUND:
+        # Union tables: every head of a group selects the same blocks, so the
+        # group reads effective_blocks / G blocks of K and of V once.
+        G = w.hq // w.hkv
+        bk = int(w.bk[0])
+        kv_bytes = stats["effective_blocks"] // G * bk * w.d * esz * 2
+        alg = kv_bytes + esz * 2 * q.numel() + 4 * lse.numel()
+        gbs = alg / (fwd_avg * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": "k_attn",
+                    "algorithmic_bytes": int(alg)}
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -339,9 +392,7 @@ def main():
         "forward_tflops": round(achieved, 3),
         "plan_ms": round(plan_ms, 4),
         "effective_flops": eff_flops,
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "k_attn", "compulsory_bytes": compulsory},
+        "roofline": roofline,
         "cpu_baseline": None,
     }
     if select is not None:

@@ -10,6 +10,8 @@
 
 #include "bsa_internal.h"
 
+#include <climits>
+
 namespace bsa {
 
 static thread_local std::string g_err;
@@ -41,7 +43,7 @@ static size_t aligned(size_t x) { return (x + 255) & ~(size_t)255; }
 // ---------------------------------------------------------------------------
 struct Rule {
   int64_t key[4];  // D, dtype, union, paged (-1 = any)
-  int64_t lo[4], hi[4];
+  int64_t lo[5], hi[5];  // min bq, min bk, density per mille, imbalance x16, Sq (version 2)
   Regime r;
 };
 
@@ -82,8 +84,9 @@ static bsa_status parse_lut(const char *text, bsa_lut_s *lut) {
   };
   std::string t;
   int64_t x;
-  if (!next(t) || t != "bsa-lut" || !next(t) || !parse_i64(t, &x) || x != 1)
-    return fail(BSA_ERR_LUT, "lookup table must start with 'bsa-lut 1'");
+  if (!next(t) || t != "bsa-lut" || !next(t) || !parse_i64(t, &x) || (x != 1 && x != 2))
+    return fail(BSA_ERR_LUT, "lookup table must start with 'bsa-lut 1' or 'bsa-lut 2'");
+  const int nranges = x == 2 ? 5 : 4;  // version 2 adds a range on the query length
   while (next(t)) {
     if (t != "rule") return fail(BSA_ERR_LUT, "expected 'rule', got '" + t + "'");
     Rule r{};
@@ -95,7 +98,8 @@ static bsa_status parse_lut(const char *text, bsa_lut_s *lut) {
       else if (f != 1 && parse_i64(t, &x) && x >= 0) r.key[f] = x;
       else return fail(BSA_ERR_LUT, "bad rule key '" + t + "'");
     }
-    for (int f = 0; f < 4; ++f) {
+    r.lo[4] = 0, r.hi[4] = INT64_MAX;
+    for (int f = 0; f < nranges; ++f) {
       if (!next(t) || !parse_i64(t, &r.lo[f]) || !next(t) || !parse_i64(t, &r.hi[f]))
         return fail(BSA_ERR_LUT, "bad rule range");
     }
@@ -236,13 +240,13 @@ static bsa_status choose_regime(Plan &p, const bsa_lut_s *lut) {
   Regime rg;
   if (lut) {
     const int64_t key[4] = {p.D, p.dtype, p.uni, p.paged};
-    const int64_t val[4] = {p.min_bq, p.min_bk, p.density_pm, p.imb16};
+    const int64_t val[5] = {p.min_bq, p.min_bk, p.density_pm, p.imb16, p.Sq};
     for (const Rule &r : lut->rules) {
       bool ok = true;
-      for (int f = 0; f < 4; ++f) {
+      for (int f = 0; f < 4; ++f)
         if (r.key[f] >= 0 && r.key[f] != key[f]) ok = false;
+      for (int f = 0; f < 5; ++f)
         if (val[f] < r.lo[f] || val[f] > r.hi[f]) ok = false;
-      }
       if (ok) {
         rg = r.r;
         break;

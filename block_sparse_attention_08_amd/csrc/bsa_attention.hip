@@ -396,7 +396,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
           }
         if (hh == 0) a.lse[((int64_t)geo.b * a.Hq + geo.head) * a.Sq + qpos] = lse;
       }
-    } else {
+    } else if (qvalid) {  // the combine reads partials of existing rows only
       const int64_t prow = (int64_t)slot * kTileQ + 32 * wave + n;
       float *pp = a.part_o + prow * D;
 #pragma unroll
@@ -782,7 +782,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
           }
         if (hh == 0) a.lse[((int64_t)b * a.Hq + head) * a.Sq + qpos] = lse;
       }
-    } else {
+    } else if (qvalid) {  // the combine reads partials of existing rows only
       const int64_t prow = (int64_t)slot * TQ + 32 * wave + n;
       float *pp = a.part_o + prow * D;
 #pragma unroll

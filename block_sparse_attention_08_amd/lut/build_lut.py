@@ -1,7 +1,8 @@
 """Build the regime lookup table by profiling on the local GPU.
 
 Tessera (abstract) picks an execution plan per request through a lookup table
-built from offline profiling. This script is that offline step for libbsa: for
+built from offline profiling. Table format 2: each rule also matches a range of
+the query length, so decode and short chunks get their own regime. This script is that offline step for libbsa: for
 each mask-shape bucket it times every candidate regime (tile rows, key tile,
 schedule, split threshold, GQA packing) on a representative seeded workload,
 one request = bsa_plan + bsa_forward, and writes the fastest regime of each
@@ -28,26 +29,43 @@ BIG = "1000000"
 BIGIMB = "100000000"
 
 
+ANYSQ = "  0 " + BIG
+
+
 def buckets():
-    """(name, rule key fields and ranges, representative workload factory)."""
+    """(name, rule key fields and ranges, representative workload factory,
+    candidate regimes or None for the default set). Rules carry a fifth range
+    on the query length (table format 2); first match wins."""
     from block_sparse_attention_08_amd import workloads as W
     return [
+        # Decode and short chunks: a few queries per sequence over a long paged
+        # cache with GQA union tables (split-KV keeps every CU busy).
+        ("decode", "* bf16 1 1  0 " + BIG + "  0 " + BIG + "  0 " + BIG + "  0 " + BIGIMB + "  1 64",
+         lambda: W.decode(), decode_candidates()),
         # GQA union over a paged cache (chunked prefill).
-        ("gqa-union", "* bf16 1 *  0 " + BIG + "  0 " + BIG + "  0 " + BIG + "  0 " + BIGIMB,
-         lambda: W.chunked_prefill()),
+        ("gqa-union", "* bf16 1 *  0 " + BIG + "  0 " + BIG + "  0 " + BIG + "  0 " + BIGIMB + ANYSQ,
+         lambda: W.chunked_prefill(), None),
         # Large blocks (>= 128), D=128, low density: 3-D video windows.
-        ("video-128", "128 bf16 0 *  128 " + BIG + "  128 " + BIG + "  0 400  0 " + BIGIMB,
-         lambda: W.video_dit()),
+        ("video-128", "128 bf16 0 *  128 " + BIG + "  128 " + BIG + "  0 400  0 " + BIGIMB + ANYSQ,
+         lambda: W.video_dit(), None),
         # Mixed block sizes with uneven rows (long video), D=128.
-        ("mixed-128", "128 bf16 0 *  16 127  16 " + BIG + "  0 " + BIG + "  0 " + BIGIMB,
-         lambda: W.long_video()),
+        ("mixed-128", "128 bf16 0 *  16 127  16 " + BIG + "  0 " + BIG + "  0 " + BIGIMB + ANYSQ,
+         lambda: W.long_video(), None),
         # Small blocks, D=64, low density (regular patterns).
-        ("regular-64-sparse", "64 bf16 0 *  16 " + BIG + "  16 " + BIG + "  0 200  0 " + BIGIMB,
-         lambda: W.affine(bs=64)),
+        ("regular-64-sparse", "64 bf16 0 *  16 " + BIG + "  16 " + BIG + "  0 200  0 " + BIGIMB + ANYSQ,
+         lambda: W.affine(bs=64), None),
         # Small blocks, D=64, dense windows.
-        ("regular-64-dense", "64 bf16 0 *  16 " + BIG + "  16 " + BIG + "  201 " + BIG + "  0 " + BIGIMB,
-         lambda: W.affine(bs=64, window=8192)),
+        ("regular-64-dense", "64 bf16 0 *  16 " + BIG + "  16 " + BIG + "  201 " + BIG + "  0 " + BIGIMB + ANYSQ,
+         lambda: W.affine(bs=64, window=8192), None),
     ]
+
+
+def decode_candidates():
+    """64-key tiles (the cache's 64-token pages hold whole tiles), finer splits."""
+    out = []
+    for sched, split, pack in itertools.product(("local", "lpt"), (0, 16, 24, 32, 48, 64), (1, 0)):
+        out.append((128, 64, sched, split, pack))
+    return out
 
 
 def candidates(union: bool):
@@ -93,14 +111,14 @@ def main():
     import block_sparse_attention_08_amd as bsa
 
     dev = torch.cuda.get_device_properties(0)
-    lines = ["bsa-lut 1",
+    lines = ["bsa-lut 2",
              f"# Built by block_sparse_attention_08_amd/lut/build_lut.py on {dev.name} "
              f"({dev.multi_processor_count} CUs), {args.steps} timed requests per regime.",
              "#   rule D dtype union paged bq_lo bq_hi bk_lo bk_hi dens_lo dens_hi imb_lo imb_hi "
-             "-> Tq Tk sched split pack",
+             "sq_lo sq_hi -> Tq Tk sched split pack",
              "# Each rule is the fastest regime (bsa_plan + bsa_forward) measured on the named"
              " representative workload; first match wins."]
-    for name, key, make in buckets():
+    for name, key, make, cands in buckets():
         w = make()
         q, k, v = w.make_qkv(device="cuda")
         mask = torch.from_numpy(np.ascontiguousarray(w.mask)).cuda()
@@ -109,7 +127,7 @@ def main():
         lse = torch.empty((w.batch, w.hq, w.sq), dtype=torch.float32, device="cuda")
         tensors = (q, k, v, mask, table, o, lse)
         res = []
-        for reg in candidates(w.gqa_union):
+        for reg in (cands or candidates(w.gqa_union)):
             dt = time_regime(bsa, w, tensors, reg, args.steps)
             res.append((dt, reg))
             print(f"[lut] {name}: {reg} {dt * 1e3:.3f} ms", flush=True)
@@ -128,7 +146,7 @@ def main():
         del q, k, v, o, lse, mask, table
         torch.cuda.empty_cache()
     lines.append("# Anything else: 128 x 64 tiles, row order, no split, GQA packing when possible.")
-    lines.append("rule * * * * 0 " + BIG + " 0 " + BIG + " 0 " + BIG + " 0 " + BIGIMB + " -> 128 64 local 0 1")
+    lines.append("rule * * * * 0 " + BIG + " 0 " + BIG + " 0 " + BIG + " 0 " + BIGIMB + ANYSQ + " -> 128 64 local 0 1")
     text = "\n".join(lines) + "\n"
     bsa.Lut.parse(text)  # validate
     with open(args.out, "w") as f:

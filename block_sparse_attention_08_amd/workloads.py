@@ -34,7 +34,7 @@ from typing import List, Optional, Tuple
 import numpy as np
 
 # Workload ids used as the first word of every SeedSequence.
-WID_TINY, WID_VIDEO, WID_PREFILL, WID_AFFINE, WID_LONG, WID_RANDOM = 1, 2, 3, 4, 5, 9
+WID_TINY, WID_VIDEO, WID_PREFILL, WID_AFFINE, WID_LONG, WID_DECODE, WID_RANDOM = 1, 2, 3, 4, 5, 6, 9
 # Second word: which stream of random numbers.
 STREAM_QKV, STREAM_MASK, STREAM_PAGES, STREAM_DOUT = 0, 1, 2, 3
 
@@ -264,6 +264,49 @@ def chunked_prefill(hq: int = 32, hkv: int = 8, d: int = 128, chunk: int = 4096,
                     causal_offset=off, gqa_union=True, paged=True, page_size=page,
                     pages_per_seq=pps, num_pages=pps, page_table=table,
                     seed=(WID_PREFILL, seed))
+
+
+# --------------------------------------------------------------------------
+# Decode and short chunks over a paged cache
+# --------------------------------------------------------------------------
+def decode(batch: int = 16, hq: int = 32, hkv: int = 8, d: int = 128, q_len: int = 1,
+           context: int = 65536, page: int = 64, block: int = 128, keep_tenths: int = 1,
+           seed: int = 0) -> Workload:
+    """A batch of sequences, each with ``q_len`` new tokens at the end of a
+    ``context``-token paged cache (decode: one token; a short chunk, such as
+    speculative verification: a few).
+
+    Query i of a sequence sits at ``context - q_len + i``; key j is allowed
+    only if ``j <= i + context - q_len``. Per sequence and head, the query
+    block keeps the top ceil(n * keep_tenths / 10) of its n causal candidate
+    key blocks by i.i.d. N(0,1) logit (ties to the lower block), and the
+    heads of a kv group attend to the union of their selections, as in
+    chunked prefill. Every sequence reads its own pages of one pool through
+    a random permutation.
+    """
+    assert context % block == 0 and context % page == 0 and 1 <= q_len <= context
+    off = context - q_len
+    nqb, nkb = cdiv(q_len, block), context // block
+    blocks = []
+    for b in range(batch):
+        for h in range(hq):
+            g = _rng(WID_DECODE, seed, STREAM_MASK, b, h)
+            logits = g.standard_normal((nqb, nkb))
+            m = np.zeros((nqb, nkb), np.uint8)
+            for qb in range(nqb):
+                last_q = off + min((qb + 1) * block, q_len) - 1
+                ncand = last_q // block + 1
+                k = (ncand * keep_tenths + 9) // 10
+                order = np.lexsort((np.arange(ncand), -logits[qb, :ncand]))
+                m[qb, order[:k]] = 1
+            blocks.append(m)
+    pps = context // page
+    gp = _rng(WID_DECODE, seed, STREAM_PAGES)
+    table = gp.permutation(batch * pps).astype(np.int32).reshape(batch, pps)
+    return Workload("decode", batch, hq, hkv, q_len, context, d, "bf16", [block] * hq,
+                    [block] * hq, _concat(blocks), causal=True, causal_offset=off, gqa_union=True,
+                    paged=True, page_size=page, pages_per_seq=pps, num_pages=batch * pps,
+                    page_table=table, seed=(WID_DECODE, seed, q_len))
 
 
 # --------------------------------------------------------------------------

@@ -130,10 +130,16 @@ const char *bsa_last_error(void);
  *   bsa-lut 1
  *   rule D dtype union paged bq_lo bq_hi bk_lo bk_hi dens_lo dens_hi imb_lo imb_hi
  *        -> Tq Tk sched split pack
+ * or, with a fifth range on the query length seqlen_q (decode and short
+ * chunks want their own regime):
+ *   bsa-lut 2
+ *   rule D dtype union paged bq_lo bq_hi bk_lo bk_hi dens_lo dens_hi imb_lo imb_hi
+ *        sq_lo sq_hi -> Tq Tk sched split pack
  * D, dtype (bf16|f32), union and paged (0|1) may be '*'; ranges are inclusive
  * and match the smallest block_q, smallest block_k, density per mille and
- * imbalance x16 of the mask; sched is local|lpt; the first matching rule
- * wins; with no match the built-in default applies (128, 64, local, 0, 1).
+ * imbalance x16 of the mask (and seqlen_q); sched is local|lpt; the first
+ * matching rule wins; with no match the built-in default applies
+ * (128, 64, local, 0, 1).
  * bsa_lut_load reads a file (path NULL: the built-in default with no rules);
  * bsa_lut_parse reads text. The table is host memory owned by the library,
  * immutable, and may be shared by threads; free it with bsa_lut_free. */

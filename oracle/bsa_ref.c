@@ -430,7 +430,7 @@ typedef struct {
 
 typedef struct {
   int64_t key[4];   /* D, dtype, union, paged; -1 = any */
-  int64_t lo[4], hi[4]; /* min bq, min bk, density per mille, imbalance x16 */
+  int64_t lo[5], hi[5]; /* min bq, min bk, density per mille, imbalance x16, Sq (version 2) */
   regime_t r;
 } rule_t;
 
@@ -474,7 +474,8 @@ static int parse_lut(const char *text, rule_t **rules_out, int *n_out) {
   char tok[64];
   int64_t x;
   if (next_token(&cur, tok, sizeof tok) != 1 || strcmp(tok, "bsa-lut")) return -1;
-  if (next_token(&cur, tok, sizeof tok) != 1 || parse_int(tok, &x) || x != 1) return -1;
+  if (next_token(&cur, tok, sizeof tok) != 1 || parse_int(tok, &x) || (x != 1 && x != 2)) return -1;
+  const int nranges = x == 2 ? 5 : 4; /* version 2 adds a range on the query length */
   int cap = 16, n = 0;
   rule_t *rules = (rule_t *)malloc(sizeof(rule_t) * cap);
   for (;;) {
@@ -491,7 +492,8 @@ static int parse_lut(const char *text, rule_t **rules_out, int *n_out) {
       else if (f != 1 && !parse_int(tok, &x) && x >= 0) r->key[f] = x;
       else goto bad;
     }
-    for (int f = 0; f < 4; ++f) {
+    r->lo[4] = 0, r->hi[4] = INT64_MAX;
+    for (int f = 0; f < nranges; ++f) {
       if (next_token(&cur, tok, sizeof tok) != 1 || parse_int(tok, &r->lo[f])) goto bad;
       if (next_token(&cur, tok, sizeof tok) != 1 || parse_int(tok, &r->hi[f])) goto bad;
     }
@@ -592,13 +594,13 @@ int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_tabl
       return -2;
     }
     int64_t key[4] = {p->d, p->dtype, p->gqa_union ? 1 : 0, p->paged ? 1 : 0};
-    int64_t val[4] = {min_bq, min_bk, density_pm, imb16};
+    int64_t val[5] = {min_bq, min_bk, density_pm, imb16, p->sq};
     for (int i = 0; i < nr; ++i) {
       int ok = 1;
-      for (int f = 0; f < 4; ++f) {
+      for (int f = 0; f < 4; ++f)
         if (rules[i].key[f] >= 0 && rules[i].key[f] != key[f]) ok = 0;
+      for (int f = 0; f < 5; ++f)
         if (val[f] < rules[i].lo[f] || val[f] > rules[i].hi[f]) ok = 0;
-      }
       if (ok) {
         rg = rules[i].r;
         break;

@@ -55,6 +55,9 @@ SMALL = {
     "tiny_prefill": lambda: W.chunked_prefill(hq=8, hkv=2, chunk=512, context=4096, seed=1),
     "tiny_affine32": lambda: W.affine(bs=32, batch=2, heads=3, s=1024, window=128),
     "tiny_long_video": lambda: W.long_video(heads=3, grid=(4, 16, 32), seed=1),
+    "decode_q1": lambda: W.decode(batch=3, hq=8, hkv=2, q_len=1, context=4096, seed=1),
+    "decode_q5": lambda: W.decode(batch=2, hq=8, hkv=2, q_len=5, context=3072, seed=2),
+    "short_chunk_q16": lambda: W.decode(batch=2, hq=4, hkv=1, d=64, q_len=16, context=2048, seed=3),
 }
 
 REGIMES = {
@@ -77,6 +80,14 @@ def test_small_default(ref, case):
                                   "union_paged_causal", "union_g2_ragged", "tiny_fp32",
                                   "tiny_long_video"])
 def test_small_forced_regimes(ref, case, regime):
+    run_case(ref, SMALL[case](), lut_text=REGIMES[regime], label=f"{case}/{regime}")
+
+
+@pytest.mark.parametrize("regime", ["split3_local", "split2_lpt_tk128", "tq256_split3_lpt"])
+@pytest.mark.parametrize("case", ["decode_q1", "decode_q5", "short_chunk_q16"])
+def test_decode_split_regimes(ref, case, regime):
+    """Split-KV on packed decode rows, where most rows of a packed tile do not
+    exist: partials are written and combined for existing rows only."""
     run_case(ref, SMALL[case](), lut_text=REGIMES[regime], label=f"{case}/{regime}")
 
 
@@ -110,6 +121,13 @@ def test_full_chunked_prefill(ref):
 def test_full_affine(ref, bs):
     w = W.affine(bs=bs)
     run_case(ref, w, rows=sample_rows(w, 256), device_gen=True, label=f"affine_bs{bs}_full")
+
+
+@pytest.mark.parametrize("q_len", [1, 16])
+def test_full_decode(ref, q_len):
+    """16 sequences x 32 query heads over 8 kv heads, 65,536-token paged cache."""
+    w = W.decode(q_len=q_len)
+    run_case(ref, w, rows=sample_rows(w, 256), device_gen=True, label=f"decode_q{q_len}_full")
 
 
 def test_full_long_video(ref):

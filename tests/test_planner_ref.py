@@ -188,11 +188,29 @@ def test_lut_rules_first_match(ref):
     assert (h["tk"], h["sched"], h["split"]) == (64, 1, 7)
     h = decode(ref.plan(w)).h    # no table: built-in default
     assert (h["tq"], h["tk"], h["sched"], h["split"]) == (128, 64, 0, 0)
-    for bad in ["", "bsa-lut 2\n", "bsa-lut 1\nrule 1 2 3\n",
+    for bad in ["", "bsa-lut 3\n", "bsa-lut 1\nrule 1 2 3\n",
+                "bsa-lut 2\nrule * * * * 0 1 0 1 0 1 0 1 -> 128 64 local 0 0\n",
                 "bsa-lut 1\nrule * * * * 0 1 0 1 0 1 0 1 -> 128 96 local 0 0\n",
                 "bsa-lut 1\nrule * x * * 0 1 0 1 0 1 0 1 -> 128 64 local 0 0\n"]:
         with pytest.raises(ValueError):
             ref.plan(w, lut_text=bad)
+
+
+LUT2 = """\
+bsa-lut 2
+# ... sq_lo sq_hi -> Tq Tk sched split pack
+rule * * * *  0 1000  0 1000  0 1000  0 100000  1 64 -> 128 64 local 32 0
+rule * * * *  0 1000  0 1000  0 1000  0 100000  0 1000000 -> 128 64 lpt 5 0
+"""
+
+
+def test_lut_version2_query_length_range(ref):
+    """Format 2 adds a range on Sq: the first rule applies to 1..64 queries only."""
+    for sq, want in ((1, (0, 32)), (64, (0, 32)), (65, (1, 5)), (300, (1, 5))):
+        w = W.random_problem(batch=1, hq=2, sq=sq, skv=700, bq=64, bk=64, d=64, density=0.5,
+                             seed=10)
+        h = decode(ref.plan(w, lut_text=LUT2)).h
+        assert (h["sched"], h["split"]) == want, (sq, h["sched"], h["split"])
 
 
 def test_features_in_header(ref):
