@@ -165,6 +165,27 @@ class Workload:
         gen.manual_seed(int(np.random.SeedSequence(list(self.seed) + [STREAM_DOUT]).generate_state(1)[0]))
         return torch.randn(shp, generator=gen, device=device, dtype=torch.float32).to(tdt)
 
+    def make_kv8(self, k, v):
+        """K and V quantized to OCP FP8 E4M3 with one fp32 scale per kv head
+        (max |x| of the head maps to 448, the largest finite e4m3 value),
+        rounded to nearest by torch's float8_e4m3fn conversion. Returns
+        (k8, v8, k_scale, v_scale): uint8 tensors of K's layout and fp32 [Hkv]
+        scales, on K's device."""
+        import torch
+
+        head_axis = 2 if self.paged else 1
+        out = []
+        for x in (k, v):
+            xf = x.float()
+            dims = [i for i in range(4) if i != head_axis]
+            amax = xf.abs().amax(dim=dims)
+            scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+            shp = [1, 1, 1, 1]
+            shp[head_axis] = -1
+            q8 = (xf / scale.view(shp)).to(torch.float8_e4m3fn).view(torch.uint8)
+            out.append((q8.contiguous(), scale.contiguous()))
+        return out[0][0], out[1][0], out[0][1], out[1][1]
+
     def problem_dict(self) -> dict:
         return dict(
             batch=self.batch, num_q_heads=self.hq, num_kv_heads=self.hkv,

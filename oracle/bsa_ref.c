@@ -99,6 +99,18 @@ static double load_value(const void *base, int dtype, int64_t idx) {
   return (double)((const float *)base)[idx];
 }
 
+/* OCP FP8 E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits with bias 7, 3
+ * mantissa bits. Exponent field 0 holds subnormals m * 2^-9; S.1111.111 is
+ * NaN; there are no infinities, so the largest finite value is 1.75 * 2^8. */
+double ref_e4m3(uint8_t b) {
+  const int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m, -9);
+  else v = ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
 /* Element index of K/V row j of kv-head g in batch b (dense or paged). */
 static int64_t kv_index(const ref_problem *p, const int32_t *page_table, int b, int g, int64_t j) {
   if (p->paged) {
@@ -112,9 +124,17 @@ static int64_t kv_index(const ref_problem *p, const int32_t *page_table, int b, 
 /* Forward: exact softmax attention restricted to the allowed keys           */
 /* ------------------------------------------------------------------------ */
 
-int ref_forward(const ref_problem *p, const uint8_t *mask, const int32_t *page_table,
-                const void *q, const void *k, const void *v, int mode, const int64_t *rows,
-                int64_t nrows, double *o, double *lse, int nthreads) {
+/* K and V element idx of kv head g: the problem's dtype, or, when k_scale is
+ * set, an e4m3 byte times the head's scale. */
+static double kv_value(const ref_problem *p, const void *base, const float *scale, int g, int64_t idx) {
+  if (scale) return (double)scale[g] * ref_e4m3(((const uint8_t *)base)[idx]);
+  return load_value(base, p->dtype, idx);
+}
+
+static int forward_impl(const ref_problem *p, const uint8_t *mask, const int32_t *page_table,
+                        const void *q, const void *k, const void *v, const float *k_scale,
+                        const float *v_scale, int mode, const int64_t *rows, int64_t nrows,
+                        double *o, double *lse, int nthreads) {
   if (check_problem(p) || (p->paged && !page_table)) return -1;
   const int d = p->d, gs = p->hq / p->hkv;
   const double scale = p->scale > 0 ? p->scale : 1.0 / sqrt((double)d);
@@ -156,7 +176,7 @@ int ref_forward(const ref_problem *p, const uint8_t *mask, const int32_t *page_t
             int64_t kbase = kv_index(p, page_table, (int)b, g, j);
             double dot = 0.0;
             for (int t = 0; t < d; ++t)
-              dot += load_value(q, p->dtype, qbase + t) * load_value(k, p->dtype, kbase + t);
+              dot += load_value(q, p->dtype, qbase + t) * kv_value(p, k, k_scale, g, kbase + t);
             s[j] = scale * dot;
           } else {
             s[j] = -INFINITY;
@@ -175,7 +195,7 @@ int ref_forward(const ref_problem *p, const uint8_t *mask, const int32_t *page_t
             int64_t kbase = kv_index(p, page_table, (int)b, g, j);
             double dot = 0.0;
             for (int t = 0; t < d; ++t)
-              dot += load_value(q, p->dtype, qbase + t) * load_value(k, p->dtype, kbase + t);
+              dot += load_value(q, p->dtype, qbase + t) * kv_value(p, k, k_scale, g, kbase + t);
             s[n] = scale * dot;
             js[n] = j;
             if (s[n] > m) m = s[n];
@@ -195,7 +215,7 @@ int ref_forward(const ref_problem *p, const uint8_t *mask, const int32_t *page_t
         double w = exp(s[e] - m);
         l += w;
         int64_t vbase = kv_index(p, page_table, (int)b, g, js[e]);
-        for (int t = 0; t < d; ++t) acc[t] += w * load_value(v, p->dtype, vbase + t);
+        for (int t = 0; t < d; ++t) acc[t] += w * kv_value(p, v, v_scale, g, vbase + t);
       }
       for (int t = 0; t < d; ++t) orow[t] = acc[t] / l;
       lse[r] = m + log(l);
@@ -372,6 +392,21 @@ int ref_backward(const ref_problem *p, const uint8_t *mask, const void *q, const
   free(moff);
   free(uni);
   return 0;
+}
+
+int ref_forward(const ref_problem *p, const uint8_t *mask, const int32_t *page_table,
+                const void *q, const void *k, const void *v, int mode, const int64_t *rows,
+                int64_t nrows, double *o, double *lse, int nthreads) {
+  return forward_impl(p, mask, page_table, q, k, v, NULL, NULL, mode, rows, nrows, o, lse, nthreads);
+}
+
+int ref_forward_kv8(const ref_problem *p, const uint8_t *mask, const int32_t *page_table,
+                    const void *q, const uint8_t *k, const uint8_t *v, const float *k_scale,
+                    const float *v_scale, int mode, const int64_t *rows, int64_t nrows, double *o,
+                    double *lse, int nthreads) {
+  if (!k_scale || !v_scale || p->dtype != 0) return -1;
+  return forward_impl(p, mask, page_table, q, k, v, k_scale, v_scale, mode, rows, nrows, o, lse,
+                      nthreads);
 }
 
 /* ------------------------------------------------------------------------ */

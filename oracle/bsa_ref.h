@@ -56,6 +56,19 @@ int ref_forward(const ref_problem *p, const uint8_t *mask, const int32_t *page_t
                 const void *q, const void *k, const void *v, int mode, const int64_t *rows,
                 int64_t nrows, double *o, double *lse, int nthreads);
 
+/* Forward with K and V stored as OCP FP8 E4M3 bytes (same layouts as
+ * ref_forward, one byte per element) and one fp32 scale per kv head: the
+ * attention reads K = k_scale[g] * e4m3(k), V = v_scale[g] * e4m3(v). Q is
+ * bf16 (p->dtype must be 0). Returns 0, or -1 for invalid arguments. */
+int ref_forward_kv8(const ref_problem *p, const uint8_t *mask, const int32_t *page_table,
+                    const void *q, const uint8_t *k, const uint8_t *v, const float *k_scale,
+                    const float *v_scale, int mode, const int64_t *rows, int64_t nrows, double *o,
+                    double *lse, int nthreads);
+
+/* Value of an OCP FP8 E4M3 byte (bias 7, subnormals, NaN at S.1111.111, no
+ * infinities). */
+double ref_e4m3(uint8_t b);
+
 /* Backward (dense K/V only): gradients of a scalar loss L given dout =
  * dL/dO ([batch][hq][sq][d], same dtype as Q), by the chain rule through the
  * softmax over each row's allowed keys (see bsa_ref.c). dq receives nqrows

@@ -66,6 +66,13 @@ def lib():
                                    ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_void_p, ctypes.c_int]
         L.ref_backward.restype = ctypes.c_int
+        L.ref_forward_kv8.argtypes = [P(RefProblem), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_int]
+        L.ref_forward_kv8.restype = ctypes.c_int
+        L.ref_e4m3.argtypes = [ctypes.c_uint8]
+        L.ref_e4m3.restype = ctypes.c_double
         _lib = L
     return _lib
 
@@ -218,3 +225,43 @@ def backward(w, q, k, v, dout, rows=None, kv_range=None, want_dq: bool = True,
     return (dq[:n] if want_dq else None,
             dk[:, :, :kw] if want_dkv else None,
             dv[:, :, :kw] if want_dkv else None)
+
+
+def e4m3(code: int) -> float:
+    """Value of one OCP FP8 E4M3 byte."""
+    return lib().ref_e4m3(int(code))
+
+
+def _bytes(x) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return x.detach().cpu().contiguous().view(torch.uint8).numpy()
+    except ImportError:
+        pass
+    return np.ascontiguousarray(x, dtype=np.uint8)
+
+
+def forward_kv8(w, q, k8, v8, k_scale, v_scale, mode: int = 1, rows=None, nthreads: int = 0):
+    """Oracle forward with K, V as e4m3 bytes (the workload's K/V layout) and
+    fp32 per-kv-head scales; Q bf16. Returns (o[n][d], lse[n]) in float64."""
+    P = _Prob(w)
+    qa = _raw(q, "bf16")
+    ka, va = _bytes(k8), _bytes(v8)
+    ks = np.ascontiguousarray(np.asarray(k_scale, dtype=np.float32).reshape(-1))
+    vs = np.ascontiguousarray(np.asarray(v_scale, dtype=np.float32).reshape(-1))
+    if rows is None:
+        n = w.batch * w.hq * w.sq
+        rp = None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+        n = rows.shape[0]
+        rp = rows.ctypes.data
+    o = np.empty((max(n, 1), w.d), np.float64)
+    lse = np.empty(max(n, 1), np.float64)
+    rc = lib().ref_forward_kv8(ctypes.byref(P.s), P.mask_ptr(), P.table_ptr(), qa.ctypes.data,
+                               ka.ctypes.data, va.ctypes.data, ks.ctypes.data, vs.ctypes.data, mode,
+                               rp, n, o.ctypes.data, lse.ctypes.data, nthreads)
+    if rc:
+        raise ValueError(f"ref_forward_kv8 rejected the problem ({rc})")
+    return o[:n], lse[:n]
