@@ -54,7 +54,10 @@ def workload(name: str):
 # Memory-bound workloads (a few queries per sequence over a long cache): their
 # roofline is HBM bytes, the K and V rows of the selected blocks read once per
 # (sequence, kv group) plus Q, O and LSE, per forward launch.
-HBM_BOUND = {"decode", "decode_q16"}
+HBM_BOUND = {"decode", "decode_q16", "decode_kv8"}
+# Workloads run with K and V as OCP FP8 E4M3 (bsa_forward_kv8), quantized once
+# per kv head from the bf16 workload before timing.
+KV8 = {"decode_kv8": "decode"}
 
 
 # Workloads whose mask is chosen on the GPU in every step (bsa_select_blocks,
@@ -140,7 +143,7 @@ def effective_flops(w) -> float:
     return 4.0 * w.d * tot
 
 
-def cpu_baseline(w, q, k, v, target_s: float = 20.0):
+def cpu_baseline(w, q, k, v, target_s: float = 20.0, kv8=None):
     """The fp64 oracle timed on this host's cores over a bounded sample of
     query rows (whole 128-row tiles, spread over heads), in TFLOP/s of
     selected work."""
@@ -172,14 +175,21 @@ def cpu_baseline(w, q, k, v, target_s: float = 20.0):
             tot += int(cache[key][i])
         return 4.0 * w.d * tot
 
+    def run(rows):
+        if kv8 is None:
+            ref.forward(w, qh, kh, vh, mode=1, rows=rows, nthreads=threads)
+        else:
+            ref.forward_kv8(w, qh, kh, vh, kv8[2].cpu().numpy(), kv8[3].cpu().numpy(), mode=1,
+                            rows=rows, nthreads=threads)
+
     rows = rows_for(2)
     t = time.perf_counter()
-    ref.forward(w, qh, kh, vh, mode=1, rows=rows, nthreads=threads)
+    run(rows)
     dt = time.perf_counter() - t
     ntiles = max(2, min(20000, int(2 * target_s / max(dt, 1e-3))))
     rows = rows_for(ntiles, seed=1)
     t = time.perf_counter()
-    ref.forward(w, qh, kh, vh, mode=1, rows=rows, nthreads=threads)
+    run(rows)
     dt = time.perf_counter() - t
     flops = work(rows)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
@@ -216,6 +226,8 @@ def main():
     sel_keep = None
     if args.workload in SELECTED:
         base_name, sel_keep = SELECTED[args.workload]
+    elif args.workload in KV8:
+        base_name = KV8[args.workload]
     else:
         base_name = args.workload
     if args.calibrate_copy:
@@ -229,6 +241,10 @@ def main():
         return
     w = workload(base_name)
     q, k, v = w.make_qkv(device="cuda")
+    kv8 = None
+    if args.workload in KV8:
+        kv8 = w.make_kv8(k, v)
+        k, v = kv8[0], kv8[1]
     mask = torch.from_numpy(np.ascontiguousarray(w.mask)).cuda()
     table = torch.from_numpy(np.ascontiguousarray(w.page_table)).cuda() if w.paged else None
     lut = bsa.Lut.load(args.lut or bsa.DEFAULT_LUT)
@@ -254,7 +270,10 @@ def main():
             stream.wait_event(ready)
         if ev is not None:
             ev[0].record(stream)
-        p.forward(q, k, v, o, lse, stream=stream)
+        if kv8 is not None:
+            p.forward_kv8(q, k, v, kv8[2], kv8[3], o, lse, stream=stream)
+        else:
+            p.forward(q, k, v, o, lse, stream=stream)
         if ev is not None:
             ev[1].record(stream)
         return p
@@ -325,7 +344,7 @@ def main():
     # dK, dQ: 2.5x the forward's); the kernels execute seven products (S and
     # dP are formed once per kernel).
     backward = None
-    if not args.no_backward and not w.paged and w.dtype == "bf16" and sel_keep is None:
+    if not args.no_backward and not w.paged and w.dtype == "bf16" and sel_keep is None and kv8 is None:
         dout = w.make_dout(device="cuda")
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         pb = bsa.plan(prob, mask, table, lut, stream=stream)
@@ -362,7 +381,8 @@ def main():
         # group reads effective_blocks / G blocks of K and of V once.
         G = w.hq // w.hkv
         bk = int(w.bk[0])
-        kv_bytes = stats["effective_blocks"] // G * bk * w.d * esz * 2
+        kv_esz = 1 if kv8 is not None else esz
+        kv_bytes = stats["effective_blocks"] // G * bk * w.d * kv_esz * 2
         alg = kv_bytes + esz * 2 * q.numel() + 4 * lse.numel()
         gbs = alg / (fwd_avg * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -400,7 +420,7 @@ def main():
     if backward is not None:
         line["backward"] = backward
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, q, k, v)
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, kv8=kv8)
     print(json.dumps(line), flush=True)
 
 

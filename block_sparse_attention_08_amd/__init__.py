@@ -90,8 +90,9 @@ def lib() -> ctypes.CDLL:
         L.bsa_plan_free.restype = None
         L.bsa_backward.argtypes = [vp, P(Tensor), P(Tensor), P(Tensor), P(Tensor), vp, P(Tensor),
                                    P(Tensor), P(Tensor), P(Tensor), vp]
+        L.bsa_forward_kv8.argtypes = [vp, P(Tensor), P(Tensor), P(Tensor), vp, vp, P(Tensor), vp, vp]
         L.bsa_select_blocks.argtypes = [P(Problem), P(SelectParams), P(Tensor), P(Tensor), vp, vp, vp]
-        for f in ("bsa_lut_load", "bsa_lut_parse", "bsa_plan", "bsa_forward", "bsa_backward", "bsa_plan_export",
+        for f in ("bsa_lut_load", "bsa_lut_parse", "bsa_plan", "bsa_forward", "bsa_forward_kv8", "bsa_backward", "bsa_plan_export",
                   "bsa_plan_stats", "bsa_select_blocks"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -208,6 +209,23 @@ class Plan:
         _check(lib().bsa_forward(self._h, ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv),
                                  ctypes.byref(to), lse.data_ptr() if lse.numel() else None,
                                  _stream_handle(stream)))
+        return o, lse
+
+    def forward_kv8(self, q, k8, v8, k_scale, v_scale, o=None, lse=None, stream=None):
+        """O and LSE with K, V as e4m3 bytes (uint8 tensors of K's layout) and
+        fp32 per-kv-head scales (device tensors [Hkv])."""
+        import torch
+        p = self.problem
+        if o is None:
+            o = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((p["batch"], p["num_q_heads"], p["seqlen_q"]), dtype=torch.float32,
+                              device=q.device)
+        paged = bool(p.get("paged", 0))
+        tq, tk, tv, to = _tensor(q), _tensor(k8, paged), _tensor(v8, paged), _tensor(o)
+        _check(lib().bsa_forward_kv8(self._h, ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv),
+                                     k_scale.data_ptr(), v_scale.data_ptr(), ctypes.byref(to),
+                                     lse.data_ptr() if lse.numel() else None, _stream_handle(stream)))
         return o, lse
 
     def backward(self, q, k, v, o, lse, dout, dq=None, dk=None, dv=None, stream=None):

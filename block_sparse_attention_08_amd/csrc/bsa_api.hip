@@ -481,18 +481,40 @@ bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *p
   return BSA_OK;
 }
 
+static bsa_status forward_common(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k,
+                                 const bsa_tensor *v, bsa_tensor *o, float *lse, const float *k_scale,
+                                 const float *v_scale, void *stream);
+
 bsa_status bsa_forward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v,
                        bsa_tensor *o, float *lse, void *stream) {
+  return forward_common(plan, q, k, v, o, lse, nullptr, nullptr, stream);
+}
+
+bsa_status bsa_forward_kv8(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k,
+                           const bsa_tensor *v, const float *k_scale, const float *v_scale,
+                           bsa_tensor *o, float *lse, void *stream) {
+  if (!plan) return fail(BSA_ERR_INVALID_ARG, "NULL plan or tensor");
+  if (plan->dtype != BSA_BF16) return fail(BSA_ERR_UNSUPPORTED, "FP8 K/V needs a bf16 plan (bf16 Q and O)");
+  const bool any = plan->B * (int64_t)plan->Hq * plan->Sq > 0 && plan->Skv > 0;
+  if (any && (!k_scale || !v_scale)) return fail(BSA_ERR_INVALID_ARG, "NULL k_scale or v_scale");
+  return forward_common(plan, q, k, v, o, lse, k_scale, v_scale, stream);
+}
+
+static bsa_status forward_common(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k,
+                                 const bsa_tensor *v, bsa_tensor *o, float *lse, const float *k_scale,
+                                 const float *v_scale, void *stream) {
   if (!plan || !q || !k || !v || !o) return fail(BSA_ERR_INVALID_ARG, "NULL plan or tensor");
   const Plan &P = *plan;
+  const bool kv8 = k_scale != nullptr;
   const bool any_q = P.B * (int64_t)P.Hq * P.Sq > 0;
   if (any_q && (!q->data || !o->data || !lse)) return fail(BSA_ERR_INVALID_ARG, "NULL Q, O or LSE data");
   if (any_q && P.Skv > 0 && (!k->data || !v->data)) return fail(BSA_ERR_INVALID_ARG, "NULL K or V data");
   const int64_t esz = P.dtype == BSA_BF16 ? 2 : 4, vec = 16 / esz;
   for (const bsa_tensor *t : {q, k, v, (const bsa_tensor *)o}) {
+    const int64_t tv = (kv8 && (t == k || t == v)) ? 16 : vec;  // e4m3: one byte per element
     if (((uintptr_t)t->data) % 16)
       return fail(BSA_ERR_INVALID_ARG, "tensor data must be 16-byte aligned");
-    if (t->stride_b % vec || t->stride_h % vec || t->stride_s % vec)
+    if (t->stride_b % tv || t->stride_h % tv || t->stride_s % tv)
       return fail(BSA_ERR_INVALID_ARG, "tensor strides must be multiples of 16 bytes");
     if (t->stride_b < 0 || t->stride_h < 0 || t->stride_s < 0)
       return fail(BSA_ERR_INVALID_ARG, "negative stride");
@@ -513,6 +535,7 @@ bsa_status bsa_forward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k
   a.causal = P.causal, a.paged = P.paged, a.P = P.P, a.sched = P.rg.sched;
   a.queue = P.queues + kQueuesPerSet * (P.qseq.fetch_add(1) % kQueueSets);
   a.scale_log2 = P.scale * 1.4426950408889634f;
+  a.kv8 = kv8 ? 1 : 0, a.k_scale = k_scale, a.v_scale = v_scale;
   if (P.nrows == 0) return BSA_OK;
   return attention_launch(P, a, (hipStream_t)stream);
 }

@@ -477,7 +477,22 @@ __device__ __forceinline__ const T *uniform(const T *p) {
   return (const T *)(((uint64_t)hi << 32) | lo);
 }
 
-template <int D, int TK, int TQ, bool PAGED>
+// OCP FP8 E4M3 to bf16 for 8 bytes (every e4m3 value is exact in bf16).
+__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 w) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false), a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+  const f2 b0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false), b1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+  return make_uint4(pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a1[0], a1[1]), pack_bf16x2(b0[0], b0[1]),
+                    pack_bf16x2(b1[0], b1[1]));
+}
+
+// KV8: K and V are OCP FP8 E4M3 bytes with one fp32 scale per kv head. Their
+// tiles are loaded into registers where the bf16 path issues its
+// direct-to-LDS loads, and written, widened to bf16, to the same LDS layout at
+// the end of the tile (K tile j+2 and V tile j+1 go to buffers no wave reads
+// during tile j), so the arithmetic is the bf16 path's; the K scale is folded
+// into the softmax scale and the V scale into the final 1/l.
+template <int D, int TK, int TQ, bool PAGED, bool KV8 = false>
 __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) void k_attn_bf16(AttnArgs a) {
   using C = CfgB<D, TK, TQ>;
   // Two K tiles and two V tiles. K runs one tile ahead of V: while the softmax
@@ -575,6 +590,44 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
     }
     const uint16_t *kbase_ptr = (const uint16_t *)a.k + (PAGED ? 0 : b * a.k_sb) + g * a.k_sh;
     const uint16_t *vbase_ptr = (const uint16_t *)a.v + (PAGED ? 0 : b * a.v_sb) + g * a.v_sh;
+    // Softmax scale * log2(e) (times the K scale for e4m3 K); only the e4m3
+    // path reads the scales, the bf16 path reads the argument as it is.
+#define BSA_SL2 (KV8 ? a.scale_log2 * a.k_scale[g] : a.scale_log2)
+
+    // KV8 tile staging: 16 e4m3 bytes per load, row x / (D/16), columns
+    // 16 * (x % (D/16)) .., written as two 16-byte bf16 chunks.
+    constexpr int L8 = KV8 ? (TK * D / 16 + C::THREADS - 1) / C::THREADS : 0;
+    uint4 k8r[L8 > 0 ? L8 : 1], v8r[L8 > 0 ? L8 : 1];
+    // e4m3 tensors: one byte per element, so strides count bytes.
+    const uint8_t *k8base = (const uint8_t *)a.k + (PAGED ? 0 : b * a.k_sb) + g * a.k_sh;
+    const uint8_t *v8base = (const uint8_t *)a.v + (PAGED ? 0 : b * a.v_sb) + g * a.v_sh;
+    auto load8 = [&](const void *base_, int64_t sb, int64_t ss, const Meta &m, uint4 (&r)[L8 > 0 ? L8 : 1]) {
+      const uint8_t *base = (const uint8_t *)base_;
+      const int k0 = m.kt * TK;
+      const int left = min(skv32 - k0, TK);
+      const int prow = ptiles_pow2 ? (m.kt & (ptiles - 1)) * TK : (m.kt % max(ptiles, 1)) * TK;
+      const uint8_t *tb = PAGED ? base + (int64_t)m.pg * sb + (int64_t)prow * ss : base + (int64_t)k0 * ss;
+#pragma unroll
+      for (int u = 0; u < L8; ++u) {
+        const int x = tid + C::THREADS * u;
+        const int row = x / (D / 16), c8 = x % (D / 16);
+        r[u] = (x < TK * D / 16 && row < left) ? *(const uint4 *)(tb + (int64_t)row * ss + 16 * c8)
+                                               : make_uint4(0, 0, 0, 0);
+      }
+    };
+    auto store8 = [&](const uint4 (&r)[L8 > 0 ? L8 : 1], uint8_t *dst, bool is_v) {
+#pragma unroll
+      for (int u = 0; u < L8; ++u) {
+        const int x = tid + C::THREADS * u;
+        if (x < TK * D / 16) {
+          const int row = x / (D / 16), c8 = x % (D / 16);
+          const int sw = is_v ? C::swz_v(row) : C::swz_k(row);
+          *(uint4 *)(dst + row * C::ROWB + (((2 * c8) ^ sw) << 4)) = e4m3x8_to_bf16(make_uint2(r[u].x, r[u].y));
+          *(uint4 *)(dst + row * C::ROWB + (((2 * c8 + 1) ^ sw) << 4)) = e4m3x8_to_bf16(make_uint2(r[u].z, r[u].w));
+        }
+      }
+    };
+    (void)k8r, (void)v8r;
 
     // Buffer loads of one K or V tile of local entry j into dst (every thread).
     // Rows past the sequence end lie beyond the descriptor's range and read 0.
@@ -620,8 +673,13 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
       __builtin_amdgcn_s_waitcnt(0);  // K tile j+1 and V tile j have landed (this wave)
       __syncthreads();                // ... for every wave; K tile j and V tile j-1 are free
       const Meta m3 = load_meta(j + 3);
-      if (j + 2 < nent) issue_k(j + 2, m2);
-      if (j + 1 < nent) issue_v(j + 1, m1);
+      if constexpr (KV8) {
+        if (j + 2 < nent) load8(k8base, a.k_sb, a.k_ss, m2, k8r);
+        if (j + 1 < nent) load8(v8base, a.v_sb, a.v_ss, m1, v8r);
+      } else {
+        if (j + 2 < nent) issue_k(j + 2, m2);
+        if (j + 1 < nent) issue_v(j + 1, m1);
+      }
 
       // ---- mask tile j (sequence end, causal diagonal, dead sub-blocks) ----
       // 32-bit scalar tests: positions and the causal offset are below 2^31.
@@ -669,7 +727,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s_cur[t][jj]);
       mx = halfwave_max(mx);
-      const float cand = mx * a.scale_log2;
+      const float cand = mx * BSA_SL2;
       if (__any(cand > m_ref + kRescaleThreshold)) {
         const float m_new = fmaxf(m_ref, cand);
         const float alpha = m_new == -INFINITY ? 1.f : fexp2(m_ref - m_new);
@@ -701,8 +759,8 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
 #pragma unroll
           for (int k2 = 0; k2 < EPS; k2 += 2) {
             const int x = i * EPS + k2;
-            const float p0 = fexp2(__builtin_fmaf(s_cur[x / 16][x % 16], a.scale_log2, -m_use));
-            const float p1 = fexp2(__builtin_fmaf(s_cur[x / 16][x % 16 + 1], a.scale_log2, -m_use));
+            const float p0 = fexp2(__builtin_fmaf(s_cur[x / 16][x % 16], BSA_SL2, -m_use));
+            const float p1 = fexp2(__builtin_fmaf(s_cur[x / 16][x % 16 + 1], BSA_SL2, -m_use));
             psum += p0;
             psum += p1;
             pw[x / 2] = pack_bf16x2(p0, p1);
@@ -739,6 +797,10 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      if constexpr (KV8) {
+        if (j + 2 < nent) store8(k8r, kbuf(j + 2), false);
+        if (j + 1 < nent) store8(v8r, vbuf(j + 1), true);
+      }
       m0 = m1, m1 = m2, m2 = m3;
     };
 
@@ -746,9 +808,20 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
     // time, the two score buffers swapping roles (no register copies).
     f32x16 sa[C::NKB], sb[C::NKB];
     if (nent > 0) {
-      issue_k(0, m0);
-      issue_v(0, m0);
-      if (nent > 1) issue_k(1, m1);
+      if constexpr (KV8) {
+        load8(k8base, a.k_sb, a.k_ss, m0, k8r);
+        load8(v8base, a.v_sb, a.v_ss, m0, v8r);
+        store8(k8r, kbuf(0), false);
+        store8(v8r, vbuf(0), true);
+        if (nent > 1) {
+          load8(k8base, a.k_sb, a.k_ss, m1, k8r);
+          store8(k8r, kbuf(1), false);
+        }
+      } else {
+        issue_k(0, m0);
+        issue_v(0, m0);
+        if (nent > 1) issue_k(1, m1);
+      }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       const uint8_t *ks = kbuf(0);
@@ -767,7 +840,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
 
     // ---- finalize ----
     const float l_tot = halfwave_sum(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = l_tot > 0.f ? (KV8 ? a.v_scale[g] : 1.f) / l_tot : 0.f;
     const float lse = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
     if (slot < 0) {
       if (qvalid) {
@@ -805,6 +878,8 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
 // Split-KV combine: O = sum_s w_s O_s / sum_s w_s with w_s = exp(lse_s - M),
 // LSE = M + ln sum_s w_s, M = max_s lse_s. A record covers one TQ-row tile;
 // two threads per row, each half of the head dimension.
+#undef BSA_SL2
+
 template <int D, bool BF, int TQ>
 __global__ __launch_bounds__(kThreads) void k_combine(AttnArgs a, const int32_t *__restrict__ comb) {
   using E = typename std::conditional<BF, uint16_t, float>::type;
@@ -853,13 +928,15 @@ __global__ void k_zero_queues(int *q) {
   if (threadIdx.x < kQueuesPerSet) q[threadIdx.x] = 0;
 }
 
-template <int D, int TK, bool BF, int TQ, bool PAGED = false>
+template <int D, int TK, bool BF, int TQ, bool PAGED = false, bool KV8 = false>
 bsa_status launch_one(const Plan &p, const AttnArgs &a, hipStream_t s) {
+  if constexpr (BF && !KV8)
+    if (a.kv8) return launch_one<D, TK, BF, TQ, PAGED, true>(p, a, s);
   if constexpr (BF && !PAGED)
-    if (a.paged) return launch_one<D, TK, BF, TQ, true>(p, a, s);
+    if (a.paged) return launch_one<D, TK, BF, TQ, true, KV8>(p, a, s);
   static int grid = 0;
   const int threads = BF ? 64 * (TQ / 32) : kThreads;
-  auto kern = BF ? (void (*)(AttnArgs))k_attn_bf16<D, TK, TQ, PAGED> : (void (*)(AttnArgs))k_attn<D, 64, false>;
+  auto kern = BF ? (void (*)(AttnArgs))k_attn_bf16<D, TK, TQ, PAGED, KV8> : (void (*)(AttnArgs))k_attn<D, 64, false>;
   if (grid == 0) {
     int dev = 0, cus = 0, occ = 0;
     HIP_TRY(hipGetDevice(&dev));

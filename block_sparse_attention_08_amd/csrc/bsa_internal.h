@@ -84,6 +84,8 @@ struct AttnArgs {
   int64_t Sq, Skv, off, nqt;
   int32_t Hq, Hkv, G, tq, tr, pack, causal, paged, P, sched;
   float scale_log2;  // softmax scale * log2(e)
+  int32_t kv8;       // K and V are OCP FP8 E4M3 bytes scaled per kv head by k_scale, v_scale
+  const float *k_scale, *v_scale;
 };
 
 struct BwdArgs {

@@ -181,6 +181,21 @@ bsa_status bsa_plan(const bsa_problem *problem, const uint8_t *mask, const int32
 bsa_status bsa_forward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k,
                        const bsa_tensor *v, bsa_tensor *o, float *lse, void *stream);
 
+/* Attention forward with K and V stored as OCP FP8 E4M3 bytes (one byte per
+ * element: sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+ * infinities), the low-precision KV cache of serving (CompactAttention
+ * summary: zero-copy execution over the paged cache; the quantized-attention
+ * line of the related-work page). The attention reads
+ *   K = k_scale[g] * e4m3(k),  V = v_scale[g] * e4m3(v)
+ * for kv head g, and is otherwise bsa_forward: same plan (bf16 dtype: Q and O
+ * bf16), same layouts for k and v (dense or paged pool) with strides counted
+ * in bytes (multiples of 16), k_scale and v_scale device pointers to fp32
+ * [Hkv]. Every e4m3 value is exact in bf16, so the products are bf16 MFMAs on
+ * the exact K and V values. BSA_ERR_UNSUPPORTED for fp32 plans. */
+bsa_status bsa_forward_kv8(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k,
+                           const bsa_tensor *v, const float *k_scale, const float *v_scale,
+                           bsa_tensor *o, float *lse, void *stream);
+
 /* Backward of bsa_forward over the same plan: for a scalar loss with
  * dout = dL/dO, writes dq = dL/dQ, dk = dL/dK and dv = dL/dV. By the chain
  * rule through the softmax over each query row's allowed keys (Tessera,
