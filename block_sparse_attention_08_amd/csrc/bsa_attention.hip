@@ -486,12 +486,14 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 w) {
                     pack_bf16x2(b1[0], b1[1]));
 }
 
-// KV8: K and V are OCP FP8 E4M3 bytes with one fp32 scale per kv head. Their
-// tiles are loaded into registers where the bf16 path issues its
-// direct-to-LDS loads, and written, widened to bf16, to the same LDS layout at
-// the end of the tile (K tile j+2 and V tile j+1 go to buffers no wave reads
-// during tile j), so the arithmetic is the bf16 path's; the K scale is folded
-// into the softmax scale and the V scale into the final 1/l.
+// KV8: K and V are OCP FP8 E4M3 bytes with one fp32 scale per kv head. At
+// D = 128 the e4m3 tiles stream into LDS like bf16 ones and are widened to
+// bf16 as the MFMA operands are read (K rows by 8-byte reads, V^T by 8-bit
+// transpose reads). At D = 64 they are loaded into registers where the bf16
+// path issues its loads and written, widened, to the bf16 layout at the end of
+// the tile (K tile j+2 and V tile j+1 go to buffers no wave reads during tile
+// j). Either way the MFMAs are the bf16 path's on exact values; the K scale
+// is folded into the softmax scale and the V scale into the final 1/l.
 template <int D, int TK, int TQ, bool PAGED, bool KV8 = false>
 __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) void k_attn_bf16(AttnArgs a) {
   using C = CfgB<D, TK, TQ>;
@@ -596,7 +598,10 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
 
     // KV8 tile staging: 16 e4m3 bytes per load, row x / (D/16), columns
     // 16 * (x % (D/16)) .., written as two 16-byte bf16 chunks.
-    constexpr int L8 = KV8 ? (TK * D / 16 + C::THREADS - 1) / C::THREADS : 0;
+    // D = 128: e4m3 tiles stream straight into LDS like bf16 ones (KD) and are
+    // widened when the MFMA operands are read; D = 64: register staging.
+    constexpr bool KD = KV8 && D == 128;
+    constexpr int L8 = (KV8 && !KD) ? (TK * D / 16 + C::THREADS - 1) / C::THREADS : 0;
     uint4 k8r[L8 > 0 ? L8 : 1], v8r[L8 > 0 ? L8 : 1];
     // e4m3 tensors: one byte per element, so strides count bytes.
     const uint8_t *k8base = (const uint8_t *)a.k + (PAGED ? 0 : b * a.k_sb) + g * a.k_sh;
@@ -649,10 +654,44 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
     };
     auto issue_k = [&](int j, const Meta &m) { issue(kbase_ptr, a.k_sb, a.k_ss, m, kbuf(j), koff0, kstep); };
     auto issue_v = [&](int j, const Meta &m) { issue(vbase_ptr, a.v_sb, a.v_ss, m, vbuf(j), voff0, vstep); };
+    // e4m3 tiles (KD): rows of D bytes, 16-byte chunk c of row r at slot
+    // c ^ swz8(r). K rows are read 8 bytes at a time by 32 lanes on 32 rows
+    // (swz8_k spreads rows of one parity over the 8 slots); V is read by
+    // 8-bit transpose reads, 8 rows x 2 chunks per 16-lane pair (swz8_v gives
+    // rows r, r+2, r+4, r+6 disjoint chunk pairs).
+    constexpr int CPR8 = D / 16, RPL8 = C::THREADS / CPR8;
+    constexpr int LOADS8 = (TK * D) / (C::THREADS * 16);
+    auto swz8_k = [](int r) { return (r >> 1) & 7; };
+    auto swz8_v = [](int r) { return 2 * ((r >> 1) & 3); };
+    const int trow8 = tid / CPR8, tpos8 = tid % CPR8;
+    const int k8off0 = trow8 * (int)a.k_ss + ((tpos8 ^ swz8_k(trow8)) << 4);
+    const int v8off0 = trow8 * (int)a.v_ss + ((tpos8 ^ swz8_v(trow8)) << 4);
+    auto issue8 = [&](const uint8_t *base, int64_t sb, int64_t ss, const Meta &m, uint8_t *dst_tile, int off0) {
+      const int k0 = m.kt * TK;
+      const int left = min(skv32 - k0, TK);
+      const int prow = ptiles_pow2 ? (m.kt & (ptiles - 1)) * TK : (m.kt % max(ptiles, 1)) * TK;
+      const uint8_t *tb = PAGED ? base + (int64_t)m.pg * sb + (int64_t)prow * ss : base + (int64_t)k0 * ss;
+      const int bytes = (left - 1) * (int)ss + D;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)tb, 0, bytes, 0x00020000);
+#pragma unroll
+      for (int u = 0; u < LOADS8; ++u) {
+        uint8_t *dst = dst_tile + (u * C::THREADS + wave * 64) * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, off0 + u * RPL8 * (int)ss, 0, 0, 0);
+      }
+    };
+    auto issue_k8 = [&](int j, const Meta &m) { issue8(k8base, a.k_sb, a.k_ss, m, kbuf(j), k8off0); };
+    auto issue_v8 = [&](int j, const Meta &m) { issue8(v8base, a.v_sb, a.v_ss, m, vbuf(j), v8off0); };
+    (void)issue_k8, (void)issue_v8;
     auto kfrag = [&](const uint8_t *ks, int i) {
       const int row = 32 * (i / (D / 16)) + krow0;
-      const int c = 2 * (i % (D / 16)) + hh;
-      return *(const bf16x8 *)(ks + row * C::ROWB + ((c ^ C::swz_k(row)) << 4));
+      if constexpr (KD) {
+        const int c8 = i % (D / 16);  // 16 e4m3 bytes per k-step, 8 per half-wave
+        const uint2 w = *(const uint2 *)(ks + row * D + ((c8 ^ swz8_k(row)) << 4) + 8 * hh);
+        return __builtin_bit_cast(bf16x8, e4m3x8_to_bf16(w));
+      } else {
+        const int c = 2 * (i % (D / 16)) + hh;
+        return *(const bf16x8 *)(ks + row * C::ROWB + ((c ^ C::swz_k(row)) << 4));
+      }
     };
 
     f32x16 o[C::NDB];
@@ -673,7 +712,10 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
       __builtin_amdgcn_s_waitcnt(0);  // K tile j+1 and V tile j have landed (this wave)
       __syncthreads();                // ... for every wave; K tile j and V tile j-1 are free
       const Meta m3 = load_meta(j + 3);
-      if constexpr (KV8) {
+      if constexpr (KD) {
+        if (j + 2 < nent) issue_k8(j + 2, m2);
+        if (j + 1 < nent) issue_v8(j + 1, m1);
+      } else if constexpr (KV8) {
         if (j + 2 < nent) load8(k8base, a.k_sb, a.k_ss, m2, k8r);
         if (j + 1 < nent) load8(v8base, a.v_sb, a.v_ss, m1, v8r);
       } else {
@@ -776,6 +818,18 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
         constexpr int PV = (TK / 16) * C::NDB;
         auto vfrag = [&](int i) {
           const int c2 = i / C::NDB, u = i % C::NDB;
+          if constexpr (KD) {
+            // one 8-bit transpose read: each 16-lane group reads 8 key rows x
+            // 16 columns and lane j receives column j of them, i.e. 8
+            // consecutive keys of head-dim column 32u + n
+            const int i16 = lane & 15, grp = (lane >> 4) & 1;
+            const int row = 16 * c2 + 8 * hh + (i16 >> 1);
+            const int col = 32 * u + 16 * grp + 8 * (i16 & 1);
+            typedef int v2i __attribute__((ext_vector_type(2)));
+            const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) v2i *)(vs + row * D + (((col >> 4) ^ swz8_v(row)) << 4) + (col & 15)));
+            return __builtin_bit_cast(bf16x8, e4m3x8_to_bf16(make_uint2((uint32_t)r[0], (uint32_t)r[1])));
+          }
           const int ra = 16 * c2 + vrow0, rb = ra + 4;
           const int chunk = (32 * u + 16 * vdsub + 4 * (vj & 3)) >> 3;
           const uint8_t *pa = vs + ra * C::ROWB + ((chunk ^ C::swz_v(ra)) << 4) + vbyte;
@@ -797,7 +851,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if constexpr (KV8) {
+      if constexpr (KV8 && !KD) {
         if (j + 2 < nent) store8(k8r, kbuf(j + 2), false);
         if (j + 1 < nent) store8(v8r, vbuf(j + 1), true);
       }
@@ -808,7 +862,11 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
     // time, the two score buffers swapping roles (no register copies).
     f32x16 sa[C::NKB], sb[C::NKB];
     if (nent > 0) {
-      if constexpr (KV8) {
+      if constexpr (KD) {
+        issue_k8(0, m0);
+        issue_v8(0, m0);
+        if (nent > 1) issue_k8(1, m1);
+      } else if constexpr (KV8) {
         load8(k8base, a.k_sb, a.k_ss, m0, k8r);
         load8(v8base, a.v_sb, a.v_ss, m0, v8r);
         store8(k8r, kbuf(0), false);
