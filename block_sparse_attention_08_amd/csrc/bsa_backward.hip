@@ -62,22 +62,6 @@ __device__ __forceinline__ float halfwave_sum(float x) {
   return __builtin_bit_cast(float, (uint32_t)pr[0]) + __builtin_bit_cast(float, (uint32_t)pr[1]);
 }
 
-// A operand X^T of a 32x32x16 MFMA, for a row-major bf16 tile X in LDS whose
-// rows are the contraction index: lane (n, hh) receives X[r0 + 8hh + i][c0 + n]
-// for i = 0..7, by two transpose reads (each 16-lane group reads a 4 x 16
-// block and every lane gets one column of it).
-__device__ __forceinline__ bf16x8 tr_frag(const uint16_t *x, int stride, int r0, int c0, int lane) {
-  const int vj = lane & 15, vsub = (lane >> 4) & 1, hh = lane >> 5;
-  const int ra = r0 + 8 * hh + (vj >> 2);
-  const int col = c0 + 16 * vsub + 4 * (vj & 3);
-  const uint16_t *pa = x + ra * stride + col;
-  const uint16_t *pb = pa + 4 * stride;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)pa);
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)pb);
-  const s16x4 both[2] = {lo, hi};
-  return __builtin_bit_cast(bf16x8, both);
-}
-
 __device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   return __builtin_bit_cast(bf16x8, make_uint4(a, b, c, d));
 }
@@ -120,17 +104,6 @@ __device__ __forceinline__ bf16x8 tr_frag_s(const uint8_t *t, int r0, int c0, in
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)pb);
   const s16x4 both[2] = {lo, hi};
   return __builtin_bit_cast(bf16x8, both);
-}
-
-// Values equal on every lane, moved to scalar registers (so buffer
-// descriptors built from them are scalar).
-__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
-template <typename T>
-__device__ __forceinline__ T *uni(T *p) {
-  const uint64_t v = (uint64_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (T *)(((uint64_t)hi << 32) | lo);
 }
 
 // s_waitcnt with only the vector-memory counter constrained (<= n).
