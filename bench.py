@@ -64,6 +64,9 @@ KV8 = {"decode_kv8": "decode"}
 # keeping this many tenths of each query block's causal candidates) from the
 # step's own Q and K, before the plan and the forward.
 SELECTED = {"chunked_prefill_selected": ("chunked_prefill", 1)}
+# Workloads planned from affine runs (bsa_plan_acsr) instead of a mask: the
+# same problem and plan as the named mask workload, no mask and no read-back.
+ACSR = {"affine_acsr_bs64": "affine_bs64", "affine_acsr_bs32": "affine_bs32"}
 
 
 def kernel_source_hash() -> str:
@@ -228,6 +231,8 @@ def main():
         base_name, sel_keep = SELECTED[args.workload]
     elif args.workload in KV8:
         base_name = KV8[args.workload]
+    elif args.workload in ACSR:
+        base_name = ACSR[args.workload]
     else:
         base_name = args.workload
     if args.calibrate_copy:
@@ -257,14 +262,21 @@ def main():
     stream = torch.cuda.current_stream()
     plan_stream = torch.cuda.Stream()
 
+    acsr = w.acsr if args.workload in ACSR else None
+
+    def make_plan(s):
+        if acsr is not None:
+            return bsa.plan_acsr(prob, acsr, lut, stream=s)
+        return bsa.plan(prob, mask, table, lut, stream=s)
+
     def step(ev=None, serial=True):
         if sel_keep is not None:
             bsa.select_blocks(prob, q, k, table, keep_tenths=sel_keep, out=mask,
                               stream=stream if serial else plan_stream)
         if serial:
-            p = bsa.plan(prob, mask, table, lut, stream=stream)
+            p = make_plan(stream)
         else:
-            p = bsa.plan(prob, mask, table, lut, stream=plan_stream)
+            p = make_plan(plan_stream)
             ready = torch.cuda.Event()
             ready.record(plan_stream)
             stream.wait_event(ready)
@@ -311,11 +323,12 @@ def main():
     fwd_avg = float(np.mean(fwd_ms))
     ms_pipe = timed(False)[0] if args.pipeline else None
 
-    # Plan-only timing (the planner's own cost, one feature readback included).
+    # Plan-only timing (the planner's own cost, one feature readback included
+    # for mask plans).
     torch.cuda.synchronize()
     tp = time.perf_counter()
     for _ in range(5):
-        p = bsa.plan(prob, mask, table, lut)
+        p = make_plan(stream)
         torch.cuda.synchronize()
         p.free()
     plan_ms = (time.perf_counter() - tp) * 1e3 / 5

@@ -59,6 +59,30 @@ class PlanInfo(ctypes.Structure):
                [("effective_flops", ctypes.c_double), ("tile_live_subblocks", ctypes.c_int64)]
 
 
+class AcsrRun(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("row_num", "row_den", "offset", "stride", "count")]
+
+
+ACSR_MAX_RUNS = 4
+
+
+class AcsrHead(ctypes.Structure):
+    _fields_ = [("num_runs", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("runs", AcsrRun * ACSR_MAX_RUNS)]
+
+
+def acsr_heads(heads):
+    """bsa_acsr_head array from a per-head list of runs, each run a tuple
+    (row_num, row_den, offset, stride, count)."""
+    arr = (AcsrHead * max(len(heads), 1))()
+    for h, runs in enumerate(heads):
+        runs = list(runs)
+        arr[h].num_runs = len(runs)
+        for j, r in enumerate(runs[:ACSR_MAX_RUNS]):
+            arr[h].runs[j] = AcsrRun(*[int(x) for x in r])
+    return arr
+
+
 class SelectParams(ctypes.Structure):
     _fields_ = [("keep_tenths", ctypes.c_int32), ("top_k", ctypes.c_int32)]
 
@@ -92,8 +116,10 @@ def lib() -> ctypes.CDLL:
                                    P(Tensor), P(Tensor), P(Tensor), vp]
         L.bsa_forward_kv8.argtypes = [vp, P(Tensor), P(Tensor), P(Tensor), vp, vp, P(Tensor), vp, vp]
         L.bsa_select_blocks.argtypes = [P(Problem), P(SelectParams), P(Tensor), P(Tensor), vp, vp, vp]
+        L.bsa_plan_acsr.argtypes = [P(Problem), P(AcsrHead), vp, vp, P(vp)]
+        L.bsa_acsr_features.argtypes = [P(Problem), P(AcsrHead), P(ctypes.c_int64)]
         for f in ("bsa_lut_load", "bsa_lut_parse", "bsa_plan", "bsa_forward", "bsa_forward_kv8", "bsa_backward", "bsa_plan_export",
-                  "bsa_plan_stats", "bsa_select_blocks"):
+                  "bsa_plan_stats", "bsa_select_blocks", "bsa_plan_acsr", "bsa_acsr_features"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -184,15 +210,20 @@ class Plan:
     """A physical tile plan (bsa_plan_t) for one problem and mask."""
 
     def __init__(self, problem: dict, mask, page_table=None, lut: Optional[Lut] = None,
-                 stream=None):
+                 stream=None, _acsr=None):
         self.problem = dict(problem)
         s, keep = make_problem(problem)
         h = ctypes.c_void_p()
         self._lut = lut
-        _check(lib().bsa_plan(ctypes.byref(s), mask.data_ptr() if mask is not None and mask.numel() else None,
-                              page_table.data_ptr() if page_table is not None else None,
-                              lut.handle if lut is not None else None, _stream_handle(stream),
-                              ctypes.byref(h)))
+        if _acsr is not None:
+            _check(lib().bsa_plan_acsr(ctypes.byref(s), acsr_heads(_acsr),
+                                       lut.handle if lut is not None else None,
+                                       _stream_handle(stream), ctypes.byref(h)))
+        else:
+            _check(lib().bsa_plan(ctypes.byref(s), mask.data_ptr() if mask is not None and mask.numel() else None,
+                                  page_table.data_ptr() if page_table is not None else None,
+                                  lut.handle if lut is not None else None, _stream_handle(stream),
+                                  ctypes.byref(h)))
         self._h = h
 
     def forward(self, q, k, v, o=None, lse=None, stream=None):
@@ -267,6 +298,24 @@ class Plan:
 
 def plan(problem: dict, mask, page_table=None, lut: Optional[Lut] = None, stream=None) -> Plan:
     return Plan(problem, mask, page_table, lut, stream)
+
+
+def plan_acsr(problem: dict, heads, lut: Optional[Lut] = None, stream=None) -> Plan:
+    """bsa_plan_acsr: a plan from affine row descriptors (per head a list of
+    runs (row_num, row_den, offset, stride, count)) instead of a mask; the
+    problem needs mask_batch_broadcast = 1, no union and no paging."""
+    return Plan(problem, None, None, lut, stream, _acsr=heads)
+
+
+def acsr_features(problem: dict, heads):
+    """bsa_acsr_features: per head (selected blocks, largest row, empty rows,
+    causally reachable blocks) counted on the host from the runs; no device
+    is needed."""
+    s, keep = make_problem(problem)
+    hq = int(problem["num_q_heads"])
+    out = (ctypes.c_int64 * (4 * hq))()
+    _check(lib().bsa_acsr_features(ctypes.byref(s), acsr_heads(heads), out))
+    return [tuple(out[4 * h:4 * h + 4]) for h in range(hq)]
 
 
 def lut_load(path: Optional[str] = DEFAULT_LUT) -> Lut:

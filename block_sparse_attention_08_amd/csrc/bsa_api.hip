@@ -123,7 +123,9 @@ static bsa_status parse_lut(const char *text, bsa_lut_s *lut) {
 // ---------------------------------------------------------------------------
 // Problem checks (all before any device work)
 // ---------------------------------------------------------------------------
-static bsa_status check_problem(const bsa_problem *p, const uint8_t *mask, const int32_t *table) {
+// need_mask = false: an ACSR plan, which reads neither a mask nor a page table.
+static bsa_status check_problem(const bsa_problem *p, const uint8_t *mask, const int32_t *table,
+                                bool need_mask = true) {
   if (!p) return fail(BSA_ERR_INVALID_ARG, "problem is NULL");
   if (p->batch < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1)
     return fail(BSA_ERR_INVALID_ARG, "batch and head counts must be >= 1");
@@ -156,12 +158,12 @@ static bsa_status check_problem(const bsa_problem *p, const uint8_t *mask, const
       return fail(BSA_ERR_INVALID_ARG, "pages_per_seq and num_pages must be >= 1");
     if ((int64_t)p->page_size * p->pages_per_seq < p->seqlen_kv)
       return fail(BSA_ERR_INVALID_ARG, "page table too short for seqlen_kv");
-    if (!table) return fail(BSA_ERR_INVALID_ARG, "paged problem needs a page table");
+    if (need_mask && !table) return fail(BSA_ERR_INVALID_ARG, "paged problem needs a page table");
   }
   int64_t msize = 0;
   for (int h = 0; h < p->num_q_heads; ++h)
     msize += cdiv(p->seqlen_q, p->block_q[h]) * cdiv(p->seqlen_kv, p->block_k[h]);
-  if (msize > 0 && !mask) return fail(BSA_ERR_INVALID_ARG, "mask is NULL");
+  if (need_mask && msize > 0 && !mask) return fail(BSA_ERR_INVALID_ARG, "mask is NULL");
   return BSA_OK;
 }
 
@@ -328,12 +330,8 @@ bsa_status bsa_lut_load(const char *path, bsa_lut_t *out) {
 
 void bsa_lut_free(bsa_lut_t lut) { delete lut; }
 
-bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *page_table,
-                    bsa_lut_t lut, void *stream, bsa_plan_t *out) {
-  if (!out) return fail(BSA_ERR_INVALID_ARG, "out is NULL");
-  *out = nullptr;
-  if (bsa_status s = check_problem(pr, mask, page_table)) return s;
-
+// The plan object of a checked problem (host fields only).
+static bsa_plan_s *new_plan(const bsa_problem *pr, void *stream) {
   bsa_plan_s *p = new bsa_plan_s();
   Plan &P = *p;
   P.B = pr->batch, P.Hq = pr->num_q_heads, P.Hkv = pr->num_kv_heads, P.G = P.Hq / P.Hkv;
@@ -349,24 +347,25 @@ bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *p
   P.stream = (hipStream_t)stream;
   P.unkb = 0;
   for (int h = 0; h < P.Hq; ++h) P.unkb = std::max<int64_t>(P.unkb, cdiv(P.Skv, P.bk[h]));
-  if (hipGetDevice(&P.device) != hipSuccess) {
-    free_plan(p);
-    return fail(BSA_ERR_HIP, "hipGetDevice failed");
-  }
+  return p;
+}
 
-  // ---- phase 1: features (one device-to-host read) ----
+// Device header of a plan: counters, features, work queues, head metadata,
+// union bits, per-row features and (ACSR plans) the affine descriptors.
+// Returns the descriptors' device address in *acsr_dev when acsr is set.
+static bsa_status alloc_header(Plan &P, bool acsr, bsa_acsr_head **acsr_dev) {
   const size_t feat_bytes = sizeof(int64_t) * 4 * P.nbm * P.Hq;
   int64_t rows_per_bm = 0;
   for (int h = 0; h < P.Hq; ++h) rows_per_bm += cdiv(P.Sq, P.bq[h]);
+  const size_t acsr_bytes = acsr ? sizeof(bsa_acsr_head) * P.Hq : 0;
   const size_t pre_bytes = aligned(sizeof(int32_t) * CNT_N) + aligned(feat_bytes) +
                            aligned(sizeof(int32_t) * kQueuesPerSet * kQueueSets) +
                            aligned(sizeof(HeadMeta) * P.Hq) +
                            aligned((size_t)P.nbm * P.Hkv * std::max<int64_t>(P.unkb, 1)) +
-                           aligned(sizeof(int32_t) * 2 * std::max<int64_t>(P.nbm * rows_per_bm, 1));
-  if (plan_alloc(&P.pre, pre_bytes, P.device, P.stream) != hipSuccess) {
-    free_plan(p);
+                           aligned(sizeof(int32_t) * 2 * std::max<int64_t>(acsr ? 1 : P.nbm * rows_per_bm, 1)) +
+                           aligned(acsr_bytes);
+  if (plan_alloc(&P.pre, pre_bytes, P.device, P.stream) != hipSuccess)
     return fail(BSA_ERR_OUT_OF_MEMORY, "device allocation of plan header failed");
-  }
   P.pre_bytes = pre_bytes;
   uint8_t *pb = (uint8_t *)P.pre;
   // Counters and features are adjacent: the one read-back copies both.
@@ -381,27 +380,16 @@ bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *p
   P.uni_bits = pb;
   pb += aligned((size_t)P.nbm * P.Hkv * std::max<int64_t>(P.unkb, 1));
   P.row_feat = (int32_t *)pb;
-  auto bail = [&](bsa_status s) {
-    free_plan(p);
-    return s;
-  };
+  pb += aligned(sizeof(int32_t) * 2 * std::max<int64_t>(acsr ? 1 : P.nbm * rows_per_bm, 1));
+  if (acsr_dev) *acsr_dev = acsr ? (bsa_acsr_head *)pb : nullptr;
   if (hipMemsetAsync(P.counters, 0, sizeof(int32_t) * CNT_N, P.stream) != hipSuccess)
-    return bail(fail(BSA_ERR_HIP, "hipMemsetAsync failed"));
-  if (bsa_status s = plan_features(P, mask, page_table)) return bail(s);
-  // The one read-back of planning: counters and mask features, into pinned
-  // host memory (a direct DMA, no staging through pageable memory).
-  const size_t head_bytes = aligned(sizeof(int32_t) * CNT_N) + feat_bytes;
-  PinnedBuf pin(head_bytes);
-  if (!pin.p) return bail(fail(BSA_ERR_OUT_OF_MEMORY, "pinned host allocation failed"));
-  if (hipMemcpyAsync(pin.p, P.counters, head_bytes, hipMemcpyDeviceToHost, P.stream) != hipSuccess ||
-      hipStreamSynchronize(P.stream) != hipSuccess)
-    return bail(fail(BSA_ERR_HIP, std::string("reading mask features failed: ") +
-                                      hipGetErrorString(hipGetLastError())));
-  const int32_t *hc = (const int32_t *)pin.p;
-  const int64_t *hf = (const int64_t *)((const uint8_t *)pin.p + aligned(sizeof(int32_t) * CNT_N));
-  P.feat.assign(hf, hf + feat_bytes / 8);
-  if (hc[CNT_BADPAGE]) return bail(fail(BSA_ERR_INVALID_ARG, "page table entry outside [0, num_pages)"));
+    return fail(BSA_ERR_HIP, "hipMemsetAsync failed");
+  return BSA_OK;
+}
 
+// Everything after the features (host copy in P.feat): aggregates, regime,
+// geometry and capacities, the arena, and the planning kernels.
+static bsa_status finish_plan(Plan &P, bsa_lut_t lut, const uint8_t *mask, const int32_t *page_table) {
   // ---- aggregates and regime ----
   P.total_nnz = P.total_blocks = P.imb16 = 0;
   P.min_bq = P.min_bk = 1 << 30;
@@ -418,7 +406,7 @@ bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *p
     P.min_bk = std::min<int64_t>(P.min_bk, P.bk[h]);
   }
   P.density_pm = P.total_blocks ? 1000 * P.total_nnz / P.total_blocks : 0;
-  if (bsa_status s = choose_regime(P, lut)) return bail(s);
+  if (bsa_status s = choose_regime(P, lut)) return s;
 
   // ---- geometry and capacities ----
   const int tq = P.rg.tq, tk = P.rg.tk;
@@ -447,12 +435,12 @@ bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *p
   P.item_cap = P.nrows + P.slot_cap;
   const int64_t lim = (int64_t(1) << 31) - 2;
   if (P.ent_cap > lim || P.item_cap > lim || P.nrows > lim || P.nlists > lim)
-    return bail(fail(BSA_ERR_UNSUPPORTED, "plan too large (more than 2^31 entries or rows)"));
+    return fail(BSA_ERR_UNSUPPORTED, "plan too large (more than 2^31 entries or rows)");
   const size_t part_bytes = (size_t)P.slot_cap * tq * (P.D + 1) * sizeof(float);
   if (part_bytes > (size_t(64) << 30))
-    return bail(fail(BSA_ERR_UNSUPPORTED, "split threshold too small: partial buffers above 64 GiB"));
+    return fail(BSA_ERR_UNSUPPORTED, "split threshold too small: partial buffers above 64 GiB");
 
-  // ---- phase 2: the arena, then the rest of the planning on the stream ----
+  // ---- the arena, then the rest of the planning on the stream ----
   std::vector<std::pair<void **, size_t>> parts = {
       {(void **)&P.list_off, sizeof(int32_t) * (P.nlists + 1)},
       {(void **)&P.ent_kt, sizeof(int32_t) * std::max<int64_t>(P.ent_cap, 1)},
@@ -469,14 +457,80 @@ bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *p
   const size_t scratch = plan_scratch_bytes(P);
   total += scratch;
   if (plan_alloc(&P.arena, total, P.device, P.stream) != hipSuccess)
-    return bail(fail(BSA_ERR_OUT_OF_MEMORY, "device allocation of " + std::to_string(total) + " plan bytes failed"));
+    return fail(BSA_ERR_OUT_OF_MEMORY, "device allocation of " + std::to_string(total) + " plan bytes failed");
   P.arena_bytes = total;
   uint8_t *ap = (uint8_t *)P.arena;
   for (auto &pt : parts) {
     *pt.first = pt.second ? ap : nullptr;
     ap += aligned(pt.second);
   }
-  if (bsa_status s = plan_build(P, mask, page_table, ap, scratch)) return bail(s);
+  return plan_build(P, mask, page_table, ap, scratch);
+}
+
+bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *page_table,
+                    bsa_lut_t lut, void *stream, bsa_plan_t *out) {
+  if (!out) return fail(BSA_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (bsa_status s = check_problem(pr, mask, page_table)) return s;
+
+  bsa_plan_s *p = new_plan(pr, stream);
+  Plan &P = *p;
+  auto bail = [&](bsa_status s) {
+    free_plan(p);
+    return s;
+  };
+  if (hipGetDevice(&P.device) != hipSuccess) return bail(fail(BSA_ERR_HIP, "hipGetDevice failed"));
+
+  // ---- phase 1: features (one device-to-host read) ----
+  if (bsa_status s = alloc_header(P, false, nullptr)) return bail(s);
+  if (bsa_status s = plan_features(P, mask, page_table)) return bail(s);
+  // The one read-back of planning: counters and mask features, into pinned
+  // host memory (a direct DMA, no staging through pageable memory).
+  const size_t feat_bytes = sizeof(int64_t) * 4 * P.nbm * P.Hq;
+  const size_t head_bytes = aligned(sizeof(int32_t) * CNT_N) + feat_bytes;
+  PinnedBuf pin(head_bytes);
+  if (!pin.p) return bail(fail(BSA_ERR_OUT_OF_MEMORY, "pinned host allocation failed"));
+  if (hipMemcpyAsync(pin.p, P.counters, head_bytes, hipMemcpyDeviceToHost, P.stream) != hipSuccess ||
+      hipStreamSynchronize(P.stream) != hipSuccess)
+    return bail(fail(BSA_ERR_HIP, std::string("reading mask features failed: ") +
+                                      hipGetErrorString(hipGetLastError())));
+  const int32_t *hc = (const int32_t *)pin.p;
+  const int64_t *hf = (const int64_t *)((const uint8_t *)pin.p + aligned(sizeof(int32_t) * CNT_N));
+  P.feat.assign(hf, hf + feat_bytes / 8);
+  if (hc[CNT_BADPAGE]) return bail(fail(BSA_ERR_INVALID_ARG, "page table entry outside [0, num_pages)"));
+
+  if (bsa_status s = finish_plan(P, lut, mask, page_table)) return bail(s);
+  *out = p;
+  return BSA_OK;
+}
+
+bsa_status bsa_acsr_features(const bsa_problem *pr, const bsa_acsr_head *heads, int64_t *out) {
+  if (!out) return fail(BSA_ERR_INVALID_ARG, "out is NULL");
+  if (bsa_status s = check_problem(pr, nullptr, nullptr, false)) return s;
+  if (bsa_status s = acsr_check(*pr, heads)) return s;
+  acsr_features(*pr, heads, out);
+  return BSA_OK;
+}
+
+bsa_status bsa_plan_acsr(const bsa_problem *pr, const bsa_acsr_head *heads, bsa_lut_t lut,
+                         void *stream, bsa_plan_t *out) {
+  if (!out) return fail(BSA_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (bsa_status s = check_problem(pr, nullptr, nullptr, false)) return s;
+  if (bsa_status s = acsr_check(*pr, heads)) return s;
+
+  bsa_plan_s *p = new_plan(pr, stream);
+  Plan &P = *p;
+  auto bail = [&](bsa_status s) {
+    free_plan(p);
+    return s;
+  };
+  if (hipGetDevice(&P.device) != hipSuccess) return bail(fail(BSA_ERR_HIP, "hipGetDevice failed"));
+  bsa_acsr_head *dev_heads = nullptr;
+  if (bsa_status s = alloc_header(P, true, &dev_heads)) return bail(s);
+  // features from the runs on the host: no read-back, so nothing blocks
+  if (bsa_status s = plan_features_acsr(P, heads, dev_heads, *pr)) return bail(s);
+  if (bsa_status s = finish_plan(P, lut, nullptr, nullptr)) return bail(s);
   *out = p;
   return BSA_OK;
 }

@@ -63,6 +63,7 @@ struct Plan {
   int32_t *queues;                           // kQueueSets x kQueuesPerSet
   mutable std::atomic<uint32_t> qseq{0};     // next queue set
   uint8_t *uni_bits;
+  const bsa_acsr_head *acsr = nullptr;  // device copy of the affine row descriptors (ACSR plans)
   int32_t *list_off, *ent_kt, *ent_page;
   uint32_t *ent_live;
   int32_t *row_ent, *items, *comb;
@@ -119,6 +120,36 @@ bsa_status plan_features(Plan &p, const uint8_t *mask, const int32_t *page_table
 bsa_status plan_build(Plan &p, const uint8_t *mask, const int32_t *page_table, void *scratch,
                       size_t scratch_bytes);
 size_t plan_scratch_bytes(const Plan &p);
+
+// Affine-compressed rows (bsa_acsr.hip). floor(a / b) for b > 0.
+__host__ __device__ inline int64_t floor_div(int64_t a, int64_t b) {
+  const int64_t q = a / b;
+  return (a % b != 0 && a < 0) ? q - 1 : q;
+}
+// First key block of run u in logical query block r.
+__host__ __device__ inline int64_t acsr_first(const bsa_acsr_run &u, int64_t r) {
+  return (u.row_den == 1 ? u.row_num * r : floor_div(u.row_num * r, u.row_den)) + u.offset;
+}
+// Whether key block kb is one of run u's blocks in a row whose first block is f.
+__host__ __device__ inline bool acsr_in_run(const bsa_acsr_run &u, int64_t f, int64_t kb) {
+  const int64_t d = kb - f;
+  if (d < 0) return false;
+  if (u.stride == 1) return d < u.count;
+  if (d < (int64_t(1) << 32) && u.stride < (int64_t(1) << 32)) {
+    const uint32_t qq = (uint32_t)d / (uint32_t)u.stride;
+    return (uint32_t)d == qq * (uint32_t)u.stride && qq < u.count;
+  }
+  return d % u.stride == 0 && d / u.stride < u.count;
+}
+// Argument checks of bsa_plan_acsr / bsa_acsr_features (host only, no device
+// work), and the per-head mask features [Hq][4] counted from the runs.
+bsa_status acsr_check(const bsa_problem &pr, const bsa_acsr_head *heads);
+void acsr_features(const bsa_problem &pr, const bsa_acsr_head *heads, int64_t *out);
+// Planner side of an ACSR plan: head metadata and descriptors to the device
+// through kernel arguments (no host buffer has to outlive the call), features
+// on the host.
+bsa_status plan_features_acsr(Plan &p, const bsa_acsr_head *heads, bsa_acsr_head *dev_heads,
+                              const bsa_problem &pr);
 
 // Key-major chunk index of a plan for the backward pass: for every (list
 // batch, kv head, group of nkt_per consecutive key tiles = 128 keys), the

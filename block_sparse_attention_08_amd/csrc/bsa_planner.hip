@@ -17,6 +17,7 @@
 #include "bsa_internal.h"
 
 #include <algorithm>
+#include <cstring>
 #include <type_traits>
 
 namespace bsa {
@@ -162,6 +163,7 @@ __global__ void k_check_pages(const int32_t *__restrict__ table, int B, int pps,
 
 struct MapArgs {
   const uint8_t *mask, *U;
+  const bsa_acsr_head *acsr;  // affine row descriptors in place of mask bytes (ACSR plans)
   const HeadMeta *hm;
   const int32_t *page_table;
   int64_t mask_bstride, unkb, Sq, off, nqt, nkt, nlists;
@@ -174,8 +176,9 @@ struct MapArgs {
 
 // Live bits of physical tile (qt, kt) for list head h: bit (iq * mk + ik) is
 // set iff the logical block covering query sub-block iq and key sub-block ik
-// is selected (by the union in union mode) and, when causal, the sub-block's
-// first key is not after its last query.
+// is selected (by the union in union mode, by one of the head's affine runs
+// in an ACSR plan) and, when causal, the sub-block's first key is not after
+// its last query.
 __device__ __forceinline__ uint32_t live_bits(const MapArgs &a, int bm, int h, int g, int64_t qt,
                                               int64_t kt) {
   const HeadMeta m = a.hm[h];
@@ -183,16 +186,25 @@ __device__ __forceinline__ uint32_t live_bits(const MapArgs &a, int bm, int h, i
   const int mq = (!a.uni && bq < a.tq) ? (int)(a.tq / bq) : 1;
   const int mk = bk < a.tk ? (int)(a.tk / bk) : 1;
   const int64_t aq = bq < a.tq ? bq : a.tq, ak = bk < a.tk ? bk : a.tk;
-  const uint8_t *mb = a.mask + bm * a.mask_bstride + m.mask_off;
+  const uint8_t *mb = a.acsr ? nullptr : a.mask + bm * a.mask_bstride + m.mask_off;
   const uint8_t *u = a.uni ? a.U + ((int64_t)bm * a.Hkv + g) * a.unkb : nullptr;
   uint32_t live = 0;
   for (int iq = 0; iq < mq; ++iq) {
     const int64_t qb = bq < a.tq ? qt * mq + iq : (qt * a.tq) / bq;
     if (!u && qb >= m.nqb) continue;
+    int64_t first[BSA_ACSR_MAX_RUNS];
+    const int nruns = a.acsr ? a.acsr[h].num_runs : 0;
+    for (int j = 0; j < nruns; ++j) first[j] = acsr_first(a.acsr[h].runs[j], qb);
     for (int ik = 0; ik < mk; ++ik) {
       const int64_t kb = bk < a.tk ? kt * mk + ik : (kt * a.tk) / bk;
       if (kb >= m.nkb) continue;
-      if (!(u ? u[kb] : mb[qb * m.nkb + kb])) continue;
+      if (a.acsr) {
+        bool sel = false;
+        for (int j = 0; j < nruns && !sel; ++j) sel = acsr_in_run(a.acsr[h].runs[j], first[j], kb);
+        if (!sel) continue;
+      } else if (!(u ? u[kb] : mb[qb * m.nkb + kb])) {
+        continue;
+      }
       if (!u && a.causal) {
         const int64_t q0 = qt * a.tq + iq * aq;
         const int64_t qlast = min(q0 + aq, a.Sq) - 1;
@@ -209,7 +221,10 @@ __device__ __forceinline__ uint32_t live_bits(const MapArgs &a, int bm, int h, i
 template <bool EMIT>
 __global__ void k_map(MapArgs a) {
   const int lane = threadIdx.x & 63;
-  const int64_t l = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 6;
+  // one list per wave: the index is wave-uniform, so head metadata and
+  // descriptors come through scalar loads
+  const int64_t l = (int64_t)__builtin_amdgcn_readfirstlane(
+      (int)((blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 6));
   if (l >= a.nlists) return;
   int lb, h, g;
   int64_t qt = 0;
@@ -310,38 +325,50 @@ __global__ void k_scan_apply(const int32_t *in, int64_t n, const int32_t *__rest
   if (blockIdx.x == gridDim.x - 1 && threadIdx.x == kThreads - 1) out[n] = run;
 }
 
-// Whole scan in one workgroup (small arrays): chunks of kScanBlock in order,
-// carrying the running total. in and out may be the same array. Workgroup g
-// scans the g-th of gridDim.x arrays laid out `stride` elements apart.
-__global__ void k_scan_single(const int32_t *in, int64_t n, int32_t *out, int64_t stride) {
+// Whole scan in one workgroup (small arrays): each of 1024 threads owns a
+// contiguous segment, sums it (all loads in flight at once), the workgroup
+// scans the sums, and each thread rewrites its segment from its prefix. in
+// and out may be the same array (a thread reads each element before writing
+// it and touches only its own segment). Workgroup g scans the g-th of
+// gridDim.x arrays laid out `stride` elements apart.
+constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kScanThreads) void k_scan_single(const int32_t *in, int64_t n,
+                                                              int32_t *out, int64_t stride) {
+  __shared__ int wsum[kScanThreads / 64];
   in += blockIdx.x * stride;
   out += blockIdx.x * stride;
-  int carry = 0;
-  for (int64_t base = 0; base < n || base == 0; base += kScanBlock) {
-    int v[4], s = 0;
-    for (int u = 0; u < 4; ++u) {
-      const int64_t i = base + threadIdx.x * 4 + u;
-      v[u] = i < n ? in[i] : 0;
-      s += v[u];
-    }
-    int tot;
-    int run = carry + block_excl_scan(s, &tot);
-    for (int u = 0; u < 4; ++u) {
-      const int64_t i = base + threadIdx.x * 4 + u;
-      if (i < n) out[i] = run;
-      run += v[u];
-    }
-    carry += tot;
-    if (base + kScanBlock >= n) break;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int64_t seg = (n + kScanThreads - 1) / kScanThreads;
+  const int64_t b0 = min(n, (int64_t)t * seg), b1 = min(n, b0 + seg);
+  int sum = 0;
+#pragma unroll 8
+  for (int64_t i = b0; i < b1; ++i) sum += in[i];
+  int x = sum;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
   }
-  if (threadIdx.x == 0) out[n] = carry;
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+  for (int i = 0; i < kScanThreads / 64; ++i) {
+    before += i < w ? wsum[i] : 0;
+    tot += wsum[i];
+  }
+  int run = before + x - sum;
+  for (int64_t i = b0; i < b1; ++i) {
+    const int v = in[i];
+    out[i] = run;
+    run += v;
+  }
+  if (t == 0) out[n] = tot;
 }
 
 constexpr int64_t kSingleScanMax = 1 << 16;
 
 bsa_status scan(const int32_t *in, int64_t n, int32_t *out, int32_t *bsum, hipStream_t s) {
   if (n <= kSingleScanMax) {
-    hipLaunchKernelGGL(k_scan_single, dim3(1), dim3(kThreads), 0, s, in, n, out, (int64_t)0);
+    hipLaunchKernelGGL(k_scan_single, dim3(1), dim3(kScanThreads), 0, s, in, n, out, (int64_t)0);
     HIP_TRY(hipGetLastError());
     return BSA_OK;
   }
@@ -631,6 +658,53 @@ bsa_status plan_features(Plan &p, const uint8_t *mask, const int32_t *page_table
   return BSA_OK;
 }
 
+// Small host data to device memory through kernel arguments: the arguments
+// are captured at launch, so the call neither waits for the stream nor keeps
+// a host buffer alive until a copy has run.
+struct PutArgs {
+  void *dst;
+  uint32_t words;
+  uint32_t data[448];
+};
+__global__ void k_put(PutArgs a) {
+  for (uint32_t i = threadIdx.x; i < a.words; i += blockDim.x) ((uint32_t *)a.dst)[i] = a.data[i];
+}
+
+static bsa_status put_async(void *dst, const void *src, size_t bytes, hipStream_t s) {
+  constexpr size_t kChunk = sizeof(PutArgs::data);
+  for (size_t o = 0; o < bytes; o += kChunk) {
+    PutArgs a;
+    const size_t n = std::min(kChunk, bytes - o);
+    a.dst = (uint8_t *)dst + o;
+    a.words = (uint32_t)(n / 4);
+    memcpy(a.data, (const uint8_t *)src + o, n);
+    hipLaunchKernelGGL(k_put, dim3(1), dim3(kThreads), 0, s, a);
+  }
+  HIP_TRY(hipGetLastError());
+  return BSA_OK;
+}
+
+bsa_status plan_features_acsr(Plan &p, const bsa_acsr_head *heads, bsa_acsr_head *dev_heads,
+                              const bsa_problem &pr) {
+  std::vector<HeadMeta> &hm = p.hmeta_host;
+  hm.assign(p.Hq, HeadMeta{});
+  int64_t rows = 0, mask_off = 0;
+  for (int h = 0; h < p.Hq; ++h) {
+    const int64_t nq = (p.Sq + p.bq[h] - 1) / p.bq[h], nk = (p.Skv + p.bk[h] - 1) / p.bk[h];
+    hm[h] = HeadMeta{mask_off, rows, (int32_t)nq, (int32_t)nk, p.bq[h], p.bk[h], 0, 0, 0, 0};
+    rows += nq;
+    mask_off += nq * nk;
+  }
+  // (the head metadata goes up with its live-bit geometry once the tile
+  // shape is known, in plan_build)
+  static_assert(sizeof(HeadMeta) % 4 == 0 && sizeof(bsa_acsr_head) % 4 == 0, "word copies");
+  if (bsa_status st = put_async(dev_heads, heads, sizeof(bsa_acsr_head) * p.Hq, p.stream)) return st;
+  p.acsr = dev_heads;
+  p.feat.assign(4 * (size_t)p.Hq, 0);
+  acsr_features(pr, heads, p.feat.data());
+  return BSA_OK;
+}
+
 size_t plan_scratch_bytes(const Plan &p) {
   const int64_t nchunks = (p.item_cap + kThreads - 1) / kThreads;
   const int64_t big = std::max<int64_t>({p.nlists + 1, 3 * (p.nrows + 1), kLptKeys * nchunks + 1});
@@ -664,14 +738,24 @@ bsa_status plan_build(Plan &p, const uint8_t *mask, const int32_t *page_table, v
   if ((size_t)(sp - (uint8_t *)scratch) > scratch_bytes)
     return fail(BSA_ERR_HIP, "planner scratch too small");
 
-  // Live-bit decoding per head now that the tile shape is known (written on
-  // the device, so no host upload sits between the read-back and the
-  // mapping kernels).
-  hipLaunchKernelGGL(k_live_geom, dim3(1), dim3(kThreads), 0, s, p.hmeta, p.Hq, p.rg.tq, p.rg.tk,
-                     (int)p.uni);
+  // Live-bit decoding per head now that the tile shape is known: written on
+  // the device for mask plans (so no host upload sits between the read-back
+  // and the mapping kernels); an ACSR plan has had no read-back and sends
+  // the finished head metadata in one go.
+  if (p.acsr) {
+    for (int h = 0; h < p.Hq; ++h) {
+      HeadMeta &m = p.hmeta_host[h];
+      const int aq = std::min(m.bq, p.rg.tq), ak = std::min(m.bk, p.rg.tk);
+      m.lq = __builtin_ctz(aq), m.lk = __builtin_ctz(ak), m.mk = p.rg.tk / ak;
+    }
+    if (bsa_status st = put_async(p.hmeta, p.hmeta_host.data(), sizeof(HeadMeta) * p.Hq, s)) return st;
+  } else {
+    hipLaunchKernelGGL(k_live_geom, dim3(1), dim3(kThreads), 0, s, p.hmeta, p.Hq, p.rg.tq, p.rg.tk,
+                       (int)p.uni);
+  }
 
   MapArgs m{};
-  m.mask = mask, m.U = p.uni_bits, m.hm = p.hmeta, m.page_table = page_table;
+  m.mask = mask, m.U = p.uni_bits, m.acsr = p.acsr, m.hm = p.hmeta, m.page_table = page_table;
   int64_t mask_bstride = 0;
   for (int h = 0; h < p.Hq; ++h)
     mask_bstride += ((p.Sq + p.bq[h] - 1) / p.bq[h]) * ((p.Skv + p.bk[h] - 1) / p.bk[h]);
@@ -698,7 +782,7 @@ bsa_status plan_build(Plan &p, const uint8_t *mask, const int32_t *page_table, v
   int32_t *item_off = off, *slot_off = off + (p.nrows + 1), *comb_off = off + 2 * (p.nrows + 1);
   if (p.nrows <= kSingleScanMax) {
     // The three row counts (items, partial slots, combine records) in one launch.
-    hipLaunchKernelGGL(k_scan_single, dim3(3), dim3(kThreads), 0, s, ra.cnt_items, p.nrows, item_off,
+    hipLaunchKernelGGL(k_scan_single, dim3(3), dim3(kScanThreads), 0, s, ra.cnt_items, p.nrows, item_off,
                        p.nrows + 1);
   } else {
     if (bsa_status st = scan(ra.cnt_items, p.nrows, item_off, bsum, s)) return st;

@@ -83,6 +83,9 @@ class Workload:
     num_pages: int = 0
     page_table: Optional[np.ndarray] = None   # int32 [batch][pages_per_seq]
     seed: Tuple[int, ...] = (0,)
+    # per head, the pattern as affine runs (row_num, row_den, offset, stride,
+    # count) when the workload is defined by one (the input of bsa_plan_acsr)
+    acsr: Optional[List[List[Tuple[int, int, int, int, int]]]] = None
 
     # ---- geometry helpers (pure bookkeeping, no attention arithmetic) ----
     @property
@@ -347,6 +350,22 @@ def affine_pattern(kind: int, nb: int, bs: int, window: int, stride: int = 8,
     return m.astype(np.uint8)
 
 
+def affine_runs(kind: int, nb: int, bs: int, window: int, stride: int = 8,
+                n_global: int = 2) -> List[Tuple[int, int, int, int, int]]:
+    """The pattern of affine_pattern(kind, ...) as affine runs (row_num,
+    row_den, offset, stride, count): the window |qb - kb| <= w is the run of
+    2w + 1 blocks from qb - w; the dilated pattern kb = qb (mod stride) is a
+    run of that stride from far enough below 0 to past nb; the global columns
+    are a run of slope 0."""
+    wb = window // bs
+    reach = -(-nb // stride)
+    if kind == 0:
+        return [(1, 1, -wb, 1, 2 * wb + 1)]
+    if kind == 1:
+        return [(1, 1, -stride * reach, stride, 2 * reach + 1)]
+    return [(1, 1, -wb, 1, 2 * wb + 1), (0, 1, 0, 1, n_global)]
+
+
 def affine(bs: int = 64, batch: int = 2, heads: int = 16, s: int = 16384, d: int = 64,
            window: int = 1024, seed: int = 0) -> Workload:
     """Per head h the pattern h mod 3: window, stride-8 dilated, window+first-2 columns."""
@@ -354,7 +373,35 @@ def affine(bs: int = 64, batch: int = 2, heads: int = 16, s: int = 16384, d: int
     blocks = [affine_pattern(h % 3, nb, bs, window) for h in range(heads)]
     return Workload(f"affine_bs{bs}", batch, heads, heads, s, s, d, "bf16", [bs] * heads,
                     [bs] * heads, _concat(blocks), mask_broadcast=True,
-                    seed=(WID_AFFINE, seed, bs, window))
+                    seed=(WID_AFFINE, seed, bs, window),
+                    acsr=[affine_runs(h % 3, nb, bs, window) for h in range(heads)])
+
+
+def random_acsr(batch: int = 1, hq: int = 3, hkv: Optional[int] = None, sq: int = 700,
+                skv: int = 900, d: int = 64, bq=64, bk=64, max_runs: int = 3,
+                causal: bool = False, causal_offset: int = 0, seed: int = 0) -> Workload:
+    """Random affine runs per head (slopes 0, 1/2, 1, 3/2, 2 and -1, offsets,
+    strides 1..5, counts, overlapping runs). The mask is left empty: it is
+    what the runs expand to, which the oracle computes."""
+    hkv = hq if hkv is None else hkv
+    bqs = list(bq) if isinstance(bq, (list, tuple)) else [bq] * hq
+    bks = list(bk) if isinstance(bk, (list, tuple)) else [bk] * hq
+    g = _rng(WID_RANDOM, seed, STREAM_MASK)
+    slopes = [(0, 1), (1, 2), (1, 1), (3, 2), (2, 1), (-1, 1)]
+    heads = []
+    for h in range(hq):
+        nk = cdiv(skv, bks[h])
+        runs = []
+        for _ in range(int(g.integers(1, max_runs + 1))):
+            num, den = slopes[int(g.integers(0, len(slopes)))]
+            st = int(g.integers(1, 6))
+            cnt = int(g.integers(1, max(2, nk // st + 2)))
+            off = int(g.integers(-nk, nk))
+            runs.append((num, den, off, st, cnt))
+        heads.append(runs)
+    return Workload("random_acsr", batch, hq, hkv, sq, skv, d, "bf16", bqs, bks,
+                    np.zeros(0, np.uint8), mask_broadcast=True, causal=causal,
+                    causal_offset=causal_offset, seed=(WID_RANDOM, seed, 77), acsr=heads)
 
 
 # --------------------------------------------------------------------------

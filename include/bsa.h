@@ -262,6 +262,57 @@ bsa_status bsa_select_blocks(const bsa_problem *problem, const bsa_select_params
                              const bsa_tensor *q, const bsa_tensor *k, const int32_t *page_table,
                              uint8_t *mask, void *stream);
 
+/* Affine-compressed sparse rows (SPLAT, abstract: the masks of common sparse
+ * attention patterns have regular geometric properties, and its ACSR format
+ * stores such a mask by an affine function of the row instead of per-row
+ * column lists). Here a head's logical mask is given by up to
+ * BSA_ACSR_MAX_RUNS runs; run j selects, in logical query block r, the key
+ * blocks
+ *   c = floor(row_num_j * r / row_den_j) + offset_j + stride_j * i,
+ *       0 <= i < count_j,  kept when 0 <= c < ceil(Skv / block_k[h]),
+ * and the row's selection is the union of its runs (runs may overlap). A
+ * sliding window of w blocks is one run (1, 1, -w, 1, 2w + 1); a dilated
+ * pattern (key block = query block mod s) is one run of stride s; global
+ * columns are a run with row_num 0. */
+#define BSA_ACSR_MAX_RUNS 4
+typedef struct {
+  int64_t row_num;  /* |row_num| <= 2^20 */
+  int64_t row_den;  /* 1 .. 2^20 */
+  int64_t offset;   /* |offset| <= 2^40 */
+  int64_t stride;   /* 1 .. 2^31 */
+  int64_t count;    /* 0 .. 2^40, and stride * count <= 2^50 */
+} bsa_acsr_run;
+
+typedef struct {
+  int32_t num_runs; /* 0 .. BSA_ACSR_MAX_RUNS; 0 selects nothing */
+  int32_t reserved; /* 0 */
+  bsa_acsr_run runs[BSA_ACSR_MAX_RUNS];
+} bsa_acsr_head;
+
+/* Build a plan from affine row descriptors instead of a mask: the plan (and
+ * its bsa_plan_export image) is the one bsa_plan builds from the mask the
+ * descriptors expand to, but no mask exists anywhere and the call does not
+ * block: the mask features are counted on the host from the runs (inclusion
+ * and exclusion over the runs, congruences combined by the Chinese remainder
+ * theorem), so there is no device-to-host read, and the planning kernels
+ * evaluate the runs where bsa_plan reads mask bytes.
+ *   problem: as for bsa_plan, with mask_batch_broadcast = 1 (one pattern for
+ *            every batch), gqa_union = 0 and paged = 0 (BSA_ERR_UNSUPPORTED
+ *            otherwise).
+ *   heads:   host pointer, [Hq] descriptors; copied during the call.
+ *   lut, stream, out: as for bsa_plan.
+ * Every argument is checked before any device work is queued. */
+bsa_status bsa_plan_acsr(const bsa_problem *problem, const bsa_acsr_head *heads, bsa_lut_t lut,
+                         void *stream, bsa_plan_t *out);
+
+/* The mask features that bsa_plan_acsr counts on the host, without a device:
+ * for each head h, out[4h..4h+3] = selected logical blocks, the largest row
+ * count, the number of empty rows, and the blocks that the causal bound
+ * leaves reachable (every selected block when not causal) -- the per-head
+ * values bsa_plan computes from the expanded mask. Same argument rules as
+ * bsa_plan_acsr; out is host memory of 4 * Hq int64. */
+bsa_status bsa_acsr_features(const bsa_problem *problem, const bsa_acsr_head *heads, int64_t *out);
+
 /* Release a plan. Its device memory is returned in stream order on the plan's
  * stream, so the call may follow the last bsa_forward queued on that stream
  * directly; forward calls queued on other streams must have completed (or be

@@ -265,3 +265,33 @@ def forward_kv8(w, q, k8, v8, k_scale, v_scale, mode: int = 1, rows=None, nthrea
     if rc:
         raise ValueError(f"ref_forward_kv8 rejected the problem ({rc})")
     return o[:n], lse[:n]
+
+
+def acsr_mask(w, heads=None) -> np.ndarray:
+    """Logical mask (uint8, one mask batch, heads concatenated) that affine
+    runs describe: SPLAT's affine-compressed sparse rows (abstract), read as
+    follows. Run (row_num, row_den, offset, stride, count) selects, in query
+    block r of a head, the key blocks floor(row_num * r / row_den) + offset
+    + stride * i for 0 <= i < count, those inside [0, nkb); a row selects the
+    union of its head's runs.
+
+    heads: per head a list of run tuples (default: w.acsr)."""
+    heads = w.acsr if heads is None else heads
+    out = []
+    for h in range(w.hq):
+        nq, nk = w.nqb(h), w.nkb(h)
+        m = np.zeros((nq, nk), np.uint8)
+        for num, den, off, stride, count in heads[h]:
+            assert den >= 1 and stride >= 1 and count >= 0
+            for r in range(nq):
+                first = (num * r) // den + off  # Python's // is the floor
+                # only the i whose block can fall inside [0, nk)
+                i_lo = max(0, -(first // stride))
+                i_hi = min(count - 1, (nk - 1 - first) // stride)
+                if i_lo > i_hi:
+                    continue
+                cols = first + stride * np.arange(i_lo, i_hi + 1, dtype=np.int64)
+                cols = cols[(cols >= 0) & (cols < nk)]
+                m[r, cols] = 1
+        out.append(m.reshape(-1))
+    return np.ascontiguousarray(np.concatenate(out) if out else np.zeros(0, np.uint8))
