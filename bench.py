@@ -46,6 +46,8 @@ def workload(name: str):
         "long_video": lambda: W.long_video(),
         "decode": lambda: W.decode(q_len=1),
         "decode_q16": lambda: W.decode(q_len=16),
+        "decode_hnd": lambda: W.decode(q_len=1, kv_layout="hnd"),
+        "decode_q16_hnd": lambda: W.decode(q_len=16, kv_layout="hnd"),
         "tiny": lambda: W.tiny(),
     }
     return table[name]()
@@ -54,10 +56,10 @@ def workload(name: str):
 # Memory-bound workloads (a few queries per sequence over a long cache): their
 # roofline is HBM bytes, the K and V rows of the selected blocks read once per
 # (sequence, kv group) plus Q, O and LSE, per forward launch.
-HBM_BOUND = {"decode", "decode_q16", "decode_kv8"}
+HBM_BOUND = {"decode", "decode_q16", "decode_kv8", "decode_hnd", "decode_q16_hnd", "decode_kv8_hnd"}
 # Workloads run with K and V as OCP FP8 E4M3 (bsa_forward_kv8), quantized once
 # per kv head from the bf16 workload before timing.
-KV8 = {"decode_kv8": "decode"}
+KV8 = {"decode_kv8": "decode", "decode_kv8_hnd": "decode_hnd"}
 
 
 # Workloads whose mask is chosen on the GPU in every step (bsa_select_blocks,

@@ -112,8 +112,8 @@ static bsa_status parse_lut(const char *text, bsa_lut_s *lut) {
       else if (f == 2 || !parse_i64(t, &v[f])) return fail(BSA_ERR_LUT, "bad regime value '" + t + "'");
     }
     if ((v[0] != 128 && v[0] != 256) || (v[1] != 64 && v[1] != 128) || v[3] < 0 ||
-        v[3] > (1 << 30) || (v[4] != 0 && v[4] != 1))
-      return fail(BSA_ERR_LUT, "regime out of range (Tq 128|256, Tk 64|128, split >= 0, pack 0|1)");
+        v[3] > (1 << 30) || v[4] < 0 || v[4] > 2)
+      return fail(BSA_ERR_LUT, "regime out of range (Tq 128|256, Tk 64|128, split >= 0, pack 0|1|2)");
     r.r = Regime{(int)v[0], (int)v[1], (int)v[2], (int)v[3], (int)v[4]};
     lut->rules.push_back(r);
   }
@@ -586,6 +586,9 @@ static bsa_status forward_common(bsa_plan_t plan, const bsa_tensor *q, const bsa
   a.ent_live = P.ent_live, a.hm = P.hmeta, a.part_o = P.part_o, a.part_lse = P.part_lse;
   a.Sq = P.Sq, a.Skv = P.Skv, a.off = P.off, a.nqt = P.nqt;
   a.Hq = P.Hq, a.Hkv = P.Hkv, a.G = P.G, a.tq = P.rg.tq, a.tr = P.tr, a.pack = P.rg.pack;
+  // The fp32 kernel lays packed tiles out head after head only (its combine
+  // reads the same layout).
+  if (P.dtype == BSA_F32 && a.pack) a.pack = 1;
   a.causal = P.causal, a.paged = P.paged, a.P = P.P, a.sched = P.rg.sched;
   a.queue = P.queues + kQueuesPerSet * (P.qseq.fetch_add(1) % kQueueSets);
   a.scale_log2 = P.scale * 1.4426950408889634f;
@@ -637,7 +640,9 @@ bsa_status bsa_backward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *
   a.hm = P.hmeta;
   a.Sq = P.Sq, a.Skv = P.Skv, a.off = P.off, a.nqt = P.nqt, a.nkt = P.nkt;
   a.Hq = P.Hq, a.Hkv = P.Hkv, a.G = P.G, a.tq = P.rg.tq, a.tr = P.tr, a.tk = P.rg.tk;
-  a.pack = P.rg.pack, a.uni = P.uni, a.causal = P.causal, a.nlb = (int)P.nlb;
+  // (an interleaved forward regime has the same rows; the backward lays
+  // them out head after head)
+  a.pack = P.rg.pack ? 1 : 0, a.uni = P.uni, a.causal = P.causal, a.nlb = (int)P.nlb;
   a.scale = P.scale, a.scale_log2 = P.scale * 1.4426950408889634f;
   // Scratch, stream-ordered and returned after the kernels: Delta (dO . O per
   // query row) and the key-major chunk index (groups of 128 keys) that the

@@ -101,6 +101,31 @@ __device__ __forceinline__ RowGeo row_geo(const AttnArgs &a, int r, int wave) {
   return o;
 }
 
+// Batch, head and query position of row R (0 .. Tq-1) of plan row r. Packed
+// tiles (pack 1) hold the group's heads one after another, tr positions each;
+// interleaved tiles (pack 2) hold position-major rows, heads interleaved
+// (row R: head R mod G, position R / G), so the rows of a few positions all
+// fall in the first wave.
+struct RowPos {
+  int b, head;
+  int64_t q;
+};
+__device__ __forceinline__ RowPos tile_row(const AttnArgs &a, int r, int R) {
+  const int nh = a.pack ? a.Hkv : a.Hq;
+  const int64_t qt = r % a.nqt;
+  const int hrow = (int)((r / a.nqt) % nh);
+  RowPos o;
+  o.b = (int)(r / (a.nqt * nh));
+  if (a.pack == 2) {
+    o.head = hrow * a.G + R % a.G, o.q = qt * a.tr + R / a.G;
+  } else if (a.pack) {
+    o.head = hrow * a.G + R / a.tr, o.q = qt * a.tr + R % a.tr;
+  } else {
+    o.head = hrow, o.q = qt * a.tq + R;
+  }
+  return o;
+}
+
 template <int D, int TK, bool BF>
 struct Cfg {
   using E = typename std::conditional<BF, uint16_t, float>::type;
@@ -446,6 +471,25 @@ struct CfgB {
   static_assert((D == 128 && RPL % 16 == 0) || (D == 64 && RPL % 4 == 0), "swizzle period");
 };
 
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+// One 16-byte-per-lane buffer load into LDS at M0 (lane l writes M0 + 16 l),
+// written as assembly: the compiler then does not treat every later LDS read
+// as possibly aliasing it (it would wait for all such loads at the first LDS
+// read, emptying a deep ring). The deep-ring kernels order these loads and
+// the reads of their tiles themselves (partial waits, then a barrier).
+__device__ __forceinline__ void dma16(v4u32 rsrc, int voff, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "s"(lds_addr)
+      : "m0");
+}
+
+// s_waitcnt with only the vector-memory counter constrained (<= n, n < 64).
+#define BSA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: P values stay below 2^8
 
 // max over lanes l and l ^ 32 (the two half-waves hold the two key halves).
@@ -464,6 +508,7 @@ __device__ __forceinline__ float halfwave_sum(float x) {
 // constant address space makes uniform loads scalar.
 typedef __attribute__((address_space(4))) const int32_t cint32;
 typedef __attribute__((address_space(4))) const uint32_t cuint32;
+typedef __attribute__((address_space(4))) const float cfloat;
 
 // Values that are the same on every lane (they derive from the work item and
 // the entry index only), moved to scalar registers so buffer descriptors and
@@ -494,15 +539,25 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 w) {
 // the tile (K tile j+2 and V tile j+1 go to buffers no wave reads during tile
 // j). Either way the MFMAs are the bf16 path's on exact values; the K scale
 // is folded into the softmax scale and the V scale into the final 1/l.
-template <int D, int TK, int TQ, bool PAGED, bool KV8 = false>
+//
+// NS = stages of the K and V rings. NS = 2: two K tiles and two V tiles; K
+// runs one tile ahead of V: while the softmax of tile j runs, the S^T MFMAs
+// of tile j+1 are already issued, and the loads of K tile j+2 and V tile j+1
+// are in flight. NS = 4 (e4m3 tiles of a few live rows, such as decode
+// steps, whose time goes to waiting on loads rather than to arithmetic): K
+// tile j+4 and V tile j+3 are issued at tile j, so three tiles stream while
+// one is used, with partial waits on the vector-memory counter.
+template <int D, int TK, int TQ, bool PAGED, bool KV8 = false, int NS = 2>
 __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) void k_attn_bf16(AttnArgs a) {
   using C = CfgB<D, TK, TQ>;
-  // Two K tiles and two V tiles. K runs one tile ahead of V: while the softmax
-  // of tile j runs, the S^T MFMAs of tile j+1 are already issued, and the
-  // loads of K tile j+2 and V tile j+1 are in flight.
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * C::TILEB];
-  auto kbuf = [&](int i) { return lds + (i & 1) * C::TILEB; };
-  auto vbuf = [&](int i) { return lds + (2 + (i & 1)) * C::TILEB; };
+  // e4m3 tiles at D = 128 stream into LDS as they are (KD)
+  constexpr bool KD = KV8 && D == 128;
+  static_assert(NS == 2 || (NS == 4 && KD), "stages");
+  // one ring slot: a bf16 tile, or for deep e4m3 rings the e4m3 tile itself
+  constexpr int SLOT = (NS > 2 && KD) ? TK * D : C::TILEB;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * NS * SLOT];
+  auto kbuf = [&](int i) { return lds + (i & (NS - 1)) * SLOT; };
+  auto vbuf = [&](int i) { return lds + (NS + (i & (NS - 1))) * SLOT; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // = this wave's 32-row slice
@@ -566,19 +621,31 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
       return m;
     };
     Meta m0 = load_meta(0), m1 = load_meta(1), m2 = load_meta(2);
+    Meta m3{0, 0, 0}, m4{0, 0, 0};  // deep rings: entries j+3, j+4
+    if constexpr (NS == 4) m3 = load_meta(3), m4 = load_meta(4);
 
     // Row geometry (32-bit: rows, heads and tiles are all below 2^31).
     const int nh = a.pack ? a.Hkv : a.Hq;
     const int qt = r % nqt, hrow = (r / nqt) % nh, b = r / (nqt * nh);
     const int g = (a.pack ? hrow * a.G : hrow) / a.G;
-    const int head = a.pack ? hrow * a.G + (32 * wave) / a.tr : hrow;
+    const bool ilv = a.pack == 2;  // heads interleaved row by row
+    // wave-uniform head (an interleaved tile's heads are one union group and
+    // share their key blocks, so the group's first head gives the live-bit
+    // geometry) and the lane's own head
+    const int head_w = a.pack ? hrow * a.G + (ilv ? 0 : (32 * wave) / a.tr) : hrow;
+    const int head = ilv ? head_w + (32 * wave + n) % a.G : head_w;
     const int qbase = a.pack ? 0 : 32 * wave;
-    const int64_t q0 = a.pack ? (int64_t)qt * a.tr + (32 * wave) % a.tr : (int64_t)qt * a.tq + 32 * wave;
-    const HeadMeta hm = a.hm[head];
-    const int64_t qpos = q0 + n;
+    const int64_t q0 = ilv ? (int64_t)qt * a.tr + (32 * wave) / a.G
+                           : (a.pack ? (int64_t)qt * a.tr + (32 * wave) % a.tr : (int64_t)qt * a.tq + 32 * wave);
+    const int qd = ilv ? n / a.G : n;  // the lane's query is q0 + qd
+    const HeadMeta hm = a.hm[head_w];
+    const int64_t qpos = q0 + qd;
     const bool qvalid = qpos < a.Sq;
+    // A wave none of whose rows exist skips the arithmetic (it still loads
+    // its share of every tile and meets every barrier).
+    const bool wlive = __any(qvalid);
     // Largest key position the wave's first query may see under the causal
-    // bound (query q0 + n sees keys up to q0 + n + off), clamped to
+    // bound (query q0 + qd sees keys up to q0 + qd + off), clamped to
     // [-64, Skv]: beyond either end the tests below give the same answers.
     const int qlim0 = (int)max<int64_t>(-64, min<int64_t>(q0 + a.off, a.Skv));
     bf16x8 qb[D / 16];
@@ -590,17 +657,25 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
         qb[c] = __builtin_bit_cast(bf16x8, x);
       }
     }
+    // Deep rings: Q has landed before any tile load is issued, so the
+    // compiler has no load of its own outstanding in the tile loop (it would
+    // otherwise wait for every load, tile loads included, before using Q).
+    if constexpr (NS == 4) BSA_WAIT_VM(0);
     const uint16_t *kbase_ptr = (const uint16_t *)a.k + (PAGED ? 0 : b * a.k_sb) + g * a.k_sh;
     const uint16_t *vbase_ptr = (const uint16_t *)a.v + (PAGED ? 0 : b * a.v_sb) + g * a.v_sh;
     // Softmax scale * log2(e) (times the K scale for e4m3 K); only the e4m3
-    // path reads the scales, the bf16 path reads the argument as it is.
-#define BSA_SL2 (KV8 ? a.scale_log2 * a.k_scale[g] : a.scale_log2)
+    // path reads the scales (once per item, by a scalar load: a vector load
+    // inside the tile loop would make the compiler wait for the tile loads),
+    // the bf16 path reads the argument as it is.
+    const int g_u = uniform(g);
+    float sl2_kv8 = 0.f;
+    if constexpr (KV8) sl2_kv8 = a.scale_log2 * ((const cfloat *)a.k_scale)[g_u];
+#define BSA_SL2 (KV8 ? sl2_kv8 : a.scale_log2)
 
     // KV8 tile staging: 16 e4m3 bytes per load, row x / (D/16), columns
     // 16 * (x % (D/16)) .., written as two 16-byte bf16 chunks.
     // D = 128: e4m3 tiles stream straight into LDS like bf16 ones (KD) and are
     // widened when the MFMA operands are read; D = 64: register staging.
-    constexpr bool KD = KV8 && D == 128;
     constexpr int L8 = (KV8 && !KD) ? (TK * D / 16 + C::THREADS - 1) / C::THREADS : 0;
     uint4 k8r[L8 > 0 ? L8 : 1], v8r[L8 > 0 ? L8 : 1];
     // e4m3 tensors: one byte per element, so strides count bytes.
@@ -645,11 +720,21 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
       const uint16_t *tb = PAGED ? base + (int64_t)m.pg * sb + (int64_t)prow * ss
                                  : base + (int64_t)k0 * ss;
       const int bytes = (left - 1) * (int)ss * 2 + D * 2;
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)tb, 0, bytes, 0x00020000);
+      if constexpr (NS == 4) {
+        const uint64_t tbv = (uint64_t)tb;
+        const v4u32 rs = {(uint32_t)tbv, (uint32_t)(tbv >> 32) & 0xffffu, (uint32_t)bytes, 0x00020000u};
 #pragma unroll
-      for (int u = 0; u < C::LOADS; ++u) {
-        uint8_t *dst = dst_tile + (u * C::THREADS + wave * 64) * 16;  // lane-linear 1 KiB per wave
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, off0 + u * step, 0, 0, 0);
+        for (int u = 0; u < C::LOADS; ++u) {
+          uint8_t *dst = dst_tile + (u * C::THREADS + wave * 64) * 16;
+          dma16(rs, off0 + u * step, (uint32_t)(uintptr_t)(lds_void *)dst);
+        }
+      } else {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)tb, 0, bytes, 0x00020000);
+#pragma unroll
+        for (int u = 0; u < C::LOADS; ++u) {
+          uint8_t *dst = dst_tile + (u * C::THREADS + wave * 64) * 16;  // lane-linear 1 KiB per wave
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, off0 + u * step, 0, 0, 0);
+        }
       }
     };
     auto issue_k = [&](int j, const Meta &m) { issue(kbase_ptr, a.k_sb, a.k_ss, m, kbuf(j), koff0, kstep); };
@@ -672,11 +757,21 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
       const int prow = ptiles_pow2 ? (m.kt & (ptiles - 1)) * TK : (m.kt % max(ptiles, 1)) * TK;
       const uint8_t *tb = PAGED ? base + (int64_t)m.pg * sb + (int64_t)prow * ss : base + (int64_t)k0 * ss;
       const int bytes = (left - 1) * (int)ss + D;
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)tb, 0, bytes, 0x00020000);
+      if constexpr (NS == 4) {
+        const uint64_t tbv = (uint64_t)tb;
+        const v4u32 rs = {(uint32_t)tbv, (uint32_t)(tbv >> 32) & 0xffffu, (uint32_t)bytes, 0x00020000u};
 #pragma unroll
-      for (int u = 0; u < LOADS8; ++u) {
-        uint8_t *dst = dst_tile + (u * C::THREADS + wave * 64) * 16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, off0 + u * RPL8 * (int)ss, 0, 0, 0);
+        for (int u = 0; u < LOADS8; ++u) {
+          uint8_t *dst = dst_tile + (u * C::THREADS + wave * 64) * 16;
+          dma16(rs, off0 + u * RPL8 * (int)ss, (uint32_t)(uintptr_t)(lds_void *)dst);
+        }
+      } else {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)tb, 0, bytes, 0x00020000);
+#pragma unroll
+        for (int u = 0; u < LOADS8; ++u) {
+          uint8_t *dst = dst_tile + (u * C::THREADS + wave * 64) * 16;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, off0 + u * RPL8 * (int)ss, 0, 0, 0);
+        }
       }
     };
     auto issue_k8 = [&](int j, const Meta &m) { issue8(k8base, a.k_sb, a.k_ss, m, kbuf(j), k8off0); };
@@ -709,10 +804,36 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
     // One tile iteration: softmax of tile j (scores in s_cur), S^T of tile
     // j+1 into s_next, O += V^T P^T of tile j.
     auto tile = [&](int j, f32x16 (&s_cur)[C::NKB], f32x16 (&s_next)[C::NKB]) {
-      __builtin_amdgcn_s_waitcnt(0);  // K tile j+1 and V tile j have landed (this wave)
-      __syncthreads();                // ... for every wave; K tile j and V tile j-1 are free
-      const Meta m3 = load_meta(j + 3);
-      if constexpr (KD) {
+      // K tile j+1 and V tile j have landed (this wave) ...
+      if constexpr (NS == 2) {
+        __builtin_amdgcn_s_waitcnt(0);
+      } else {
+        // ... while the loads issued after them (K tiles j+2 .. j+NS-1 and V
+        // tiles j+1 .. j+NS-2 that exist) may still be in flight; loads
+        // complete in issue order, so waiting until at most that many remain
+        // is enough.
+        constexpr int L = KD ? LOADS8 : C::LOADS;
+        const int nk = max(0, min(j + NS - 1, nent - 1) - j - 1);
+        const int nv = max(0, min(j + NS - 1, nent) - j - 1);
+        switch (nk + nv) {
+          case 4: BSA_WAIT_VM(4 * L); break;
+          case 3: BSA_WAIT_VM(3 * L); break;
+          case 2: BSA_WAIT_VM(2 * L); break;
+          case 1: BSA_WAIT_VM(L); break;
+          default: BSA_WAIT_VM(0); break;
+        }
+      }
+      __syncthreads();  // ... for every wave; K tile j and V tile j-1 are free
+      const Meta mn = load_meta(j + NS + 1);
+      if constexpr (NS == 4) {
+        if constexpr (KD) {
+          if (j + 4 < nent) issue_k8(j + 4, m4);
+          if (j + 3 < nent) issue_v8(j + 3, m3);
+        } else {
+          if (j + 4 < nent) issue_k(j + 4, m4);
+          if (j + 3 < nent) issue_v(j + 3, m3);
+        }
+      } else if constexpr (KD) {
         if (j + 2 < nent) issue_k8(j + 2, m2);
         if (j + 1 < nent) issue_v8(j + 1, m1);
       } else if constexpr (KV8) {
@@ -723,6 +844,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
         if (j + 1 < nent) issue_v(j + 1, m1);
       }
 
+      if (wlive) {
       // ---- mask tile j (sequence end, causal diagonal, dead sub-blocks) ----
       // 32-bit scalar tests: positions and the causal offset are below 2^31.
       const int kb0 = m0.kt * TK;
@@ -735,7 +857,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
         // exist and satisfy the causal bound.
         const uint32_t lbits = live >> qsub;
         int lim = skv32 - kb0;
-        if (a.causal) lim = min(lim, qlim0 + n + 1 - kb0);
+        if (a.causal) lim = min(lim, qlim0 + qd + 1 - kb0);
         const int klim = max(0, min(lim, TK));
         const int ak = 1 << hm.lk;  // keys per live bit
         const uint64_t sub = ak >= 64 ? ~0ull : ((1ull << ak) - 1ull);
@@ -851,18 +973,50 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      }  // wlive
       if constexpr (KV8 && !KD) {
         if (j + 2 < nent) store8(k8r, kbuf(j + 2), false);
         if (j + 1 < nent) store8(v8r, vbuf(j + 1), true);
       }
-      m0 = m1, m1 = m2, m2 = m3;
+      if constexpr (NS == 4) m0 = m1, m1 = m2, m2 = m3, m3 = m4, m4 = mn;
+      else m0 = m1, m1 = m2, m2 = mn;
     };
 
     // Prologue: K tiles 0 and 1, V tile 0; S^T of tile 0. Then tiles two at a
     // time, the two score buffers swapping roles (no register copies).
     f32x16 sa[C::NKB], sb[C::NKB];
     if (nent > 0) {
-      if constexpr (KD) {
+      if constexpr (NS == 4) {
+        // K tile 0, then (K tile i, V tile i-1) for i = 1, 2, 3: the order in
+        // which the tile loop counts them; S^T of tile 0 waits for K tile 0
+        // alone.
+        auto ik = [&](int i, const Meta &m) {
+          if (i < nent) {
+            if constexpr (KD) issue_k8(i, m);
+            else issue_k(i, m);
+          }
+        };
+        auto iv = [&](int i, const Meta &m) {
+          if (i < nent) {
+            if constexpr (KD) issue_v8(i, m);
+            else issue_v(i, m);
+          }
+        };
+        ik(0, m0);
+        ik(1, m1), iv(0, m0);
+        ik(2, m2), iv(1, m1);
+        ik(3, m3), iv(2, m2);
+        constexpr int L = KD ? LOADS8 : C::LOADS;
+        switch (min(3, nent - 1) + min(3, nent)) {
+          case 6: BSA_WAIT_VM(6 * L); break;
+          case 5: BSA_WAIT_VM(5 * L); break;
+          case 4: BSA_WAIT_VM(4 * L); break;
+          case 3: BSA_WAIT_VM(3 * L); break;
+          case 2: BSA_WAIT_VM(2 * L); break;
+          case 1: BSA_WAIT_VM(L); break;
+          default: BSA_WAIT_VM(0); break;
+        }
+      } else if constexpr (KD) {
         issue_k8(0, m0);
         issue_v8(0, m0);
         if (nent > 1) issue_k8(1, m1);
@@ -880,13 +1034,15 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
         issue_v(0, m0);
         if (nent > 1) issue_k(1, m1);
       }
-      __builtin_amdgcn_s_waitcnt(0);
+      if constexpr (NS == 2) __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       const uint8_t *ks = kbuf(0);
+      if (wlive) {
 #pragma unroll
-      for (int i = 0; i < STEPS; ++i) {
-        const int t = i / (D / 16), cc = i % (D / 16);
-        sa[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(ks, i), qb[cc], cc == 0 ? f32x16{} : sa[t], 0, 0, 0);
+        for (int i = 0; i < STEPS; ++i) {
+          const int t = i / (D / 16), cc = i % (D / 16);
+          sa[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(ks, i), qb[cc], cc == 0 ? f32x16{} : sa[t], 0, 0, 0);
+        }
       }
     }
     for (int j = 0; j < nent; ++j) {
@@ -898,7 +1054,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
 
     // ---- finalize ----
     const float l_tot = halfwave_sum(l_run);
-    const float inv = l_tot > 0.f ? (KV8 ? a.v_scale[g] : 1.f) / l_tot : 0.f;
+    const float inv = l_tot > 0.f ? (KV8 ? ((const cfloat *)a.v_scale)[g_u] : 1.f) / l_tot : 0.f;
     const float lse = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
     if (slot < 0) {
       if (qvalid) {
@@ -946,8 +1102,8 @@ __global__ __launch_bounds__(kThreads) void k_combine(AttnArgs a, const int32_t 
     const int r = comb[3 * c], s0 = comb[3 * c + 1], k = comb[3 * c + 2];
     for (int idx = threadIdx.x; idx < 2 * TQ; idx += kThreads) {
       const int row = idx >> 1, half = idx & 1;
-      const RowGeo geo = row_geo(a, r, row >> 5);
-      const int64_t qpos = geo.q0 + (row & 31);
+      const RowPos geo = tile_row(a, r, row);
+      const int64_t qpos = geo.q;
       if (qpos >= a.Sq) continue;
       float M = -INFINITY;
       for (int s = 0; s < k; ++s) M = fmaxf(M, a.part_lse[(int64_t)(s0 + s) * TQ + row]);
@@ -986,15 +1142,20 @@ __global__ void k_zero_queues(int *q) {
   if (threadIdx.x < kQueuesPerSet) q[threadIdx.x] = 0;
 }
 
-template <int D, int TK, bool BF, int TQ, bool PAGED = false, bool KV8 = false>
+template <int D, int TK, bool BF, int TQ, bool PAGED = false, bool KV8 = false, int NS = 2>
 bsa_status launch_one(const Plan &p, const AttnArgs &a, hipStream_t s) {
-  if constexpr (BF && !KV8)
+  if constexpr (BF && !KV8 && NS == 2)
     if (a.kv8) return launch_one<D, TK, BF, TQ, PAGED, true>(p, a, s);
-  if constexpr (BF && !PAGED)
+  if constexpr (BF && !PAGED && NS == 2)
     if (a.paged) return launch_one<D, TK, BF, TQ, true, KV8>(p, a, s);
+  // Interleaved tiles (a few live rows each: decode steps) of e4m3 K/V stream
+  // four deep (eight 8 KiB slots, two workgroups per CU). A bf16 ring that
+  // deep needs 128 KiB of LDS, one workgroup per CU, and measured slower.
+  if constexpr (BF && NS == 2 && D == 128 && TK == 64 && TQ == 128 && KV8)
+    if (a.pack == 2) return launch_one<D, TK, BF, TQ, PAGED, KV8, 4>(p, a, s);
   static int grid = 0;
   const int threads = BF ? 64 * (TQ / 32) : kThreads;
-  auto kern = BF ? (void (*)(AttnArgs))k_attn_bf16<D, TK, TQ, PAGED, KV8> : (void (*)(AttnArgs))k_attn<D, 64, false>;
+  auto kern = BF ? (void (*)(AttnArgs))k_attn_bf16<D, TK, TQ, PAGED, KV8, NS> : (void (*)(AttnArgs))k_attn<D, 64, false>;
   if (grid == 0) {
     int dev = 0, cus = 0, occ = 0;
     HIP_TRY(hipGetDevice(&dev));

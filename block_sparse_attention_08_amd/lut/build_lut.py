@@ -63,7 +63,7 @@ def buckets():
 def decode_candidates():
     """64-key tiles (the cache's 64-token pages hold whole tiles), finer splits."""
     out = []
-    for sched, split, pack in itertools.product(("local", "lpt"), (0, 16, 24, 32, 48, 64), (1, 0)):
+    for sched, split, pack in itertools.product(("local", "lpt"), (0, 16, 24, 32, 48, 64), (2, 1, 0)):
         out.append((128, 64, sched, split, pack))
     return out
 

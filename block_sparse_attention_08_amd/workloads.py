@@ -86,6 +86,10 @@ class Workload:
     # per head, the pattern as affine runs (row_num, row_den, offset, stride,
     # count) when the workload is defined by one (the input of bsa_plan_acsr)
     acsr: Optional[List[List[Tuple[int, int, int, int, int]]]] = None
+    # storage order inside a page of a paged pool: "nhd" (token, head, dim)
+    # or "hnd" (head, token, dim: one kv head's rows of a page contiguous);
+    # the tensors keep the logical [page][token][head][dim] shape either way
+    kv_layout: str = "nhd"
 
     # ---- geometry helpers (pure bookkeeping, no attention arithmetic) ----
     @property
@@ -140,7 +144,7 @@ class Workload:
                 else:
                     t = torch.from_numpy(x)
                 out.append(t.reshape(shp))
-            return tuple(out)
+            return tuple(self._layout(t, i) for i, t in enumerate(out))
 
         gen = torch.Generator(device=device)
         gen.manual_seed(int(np.random.SeedSequence(list(self.seed) + [STREAM_QKV]).generate_state(1)[0]))
@@ -149,7 +153,15 @@ class Workload:
             x = torch.randn(shp, generator=gen, device=device, dtype=torch.float32)
             out.append(x.to(tdt))
             del x
-        return tuple(out)
+        return tuple(self._layout(t, i) for i, t in enumerate(out))
+
+    def _layout(self, t, i: int):
+        """K and V (i = 1, 2) of a paged pool in the workload's in-page order:
+        the same values, stored head-major for "hnd"."""
+        if i == 0 or not self.paged or self.kv_layout == "nhd":
+            return t
+        assert self.kv_layout == "hnd"
+        return t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
 
     def make_dout(self, device: str = "cpu"):
         """Upstream gradient dL/dO for a backward pass: N(0,1) of Q's shape and
@@ -186,7 +198,7 @@ class Workload:
             shp = [1, 1, 1, 1]
             shp[head_axis] = -1
             q8 = (xf / scale.view(shp)).to(torch.float8_e4m3fn).view(torch.uint8)
-            out.append((q8.contiguous(), scale.contiguous()))
+            out.append((self._layout(q8.contiguous(), 1), scale.contiguous()))
         return out[0][0], out[1][0], out[0][1], out[1][1]
 
     def problem_dict(self) -> dict:
@@ -295,6 +307,7 @@ def chunked_prefill(hq: int = 32, hkv: int = 8, d: int = 128, chunk: int = 4096,
 # --------------------------------------------------------------------------
 def decode(batch: int = 16, hq: int = 32, hkv: int = 8, d: int = 128, q_len: int = 1,
            context: int = 65536, page: int = 64, block: int = 128, keep_tenths: int = 1,
+           kv_layout: str = "nhd",
            seed: int = 0) -> Workload:
     """A batch of sequences, each with ``q_len`` new tokens at the end of a
     ``context``-token paged cache (decode: one token; a short chunk, such as
@@ -330,7 +343,7 @@ def decode(batch: int = 16, hq: int = 32, hkv: int = 8, d: int = 128, q_len: int
     return Workload("decode", batch, hq, hkv, q_len, context, d, "bf16", [block] * hq,
                     [block] * hq, _concat(blocks), causal=True, causal_offset=off, gqa_union=True,
                     paged=True, page_size=page, pages_per_seq=pps, num_pages=batch * pps,
-                    page_table=table, seed=(WID_DECODE, seed, q_len))
+                    page_table=table, seed=(WID_DECODE, seed, q_len), kv_layout=kv_layout)
 
 
 # --------------------------------------------------------------------------

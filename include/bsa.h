@@ -104,7 +104,9 @@ typedef struct {
   int32_t tile_q, tile_k;   /* physical tile shape */
   int32_t sched;            /* 0 = row order (locality), 1 = longest first */
   int32_t split;            /* key tiles per work item before a row is split; 0 = never */
-  int32_t pack;             /* 1: a group's heads share each task */
+  int32_t pack;             /* 1: a group's heads share each task, head after head;
+                               2: the same tasks with the heads interleaved row by row
+                               (the few rows of a decode step sit in one wave) */
   int32_t reserved;
   int64_t rows, entries, items, partial_slots, combines;
   int64_t logical_nnz;      /* selected logical blocks in the mask (before any union) */
@@ -135,6 +137,8 @@ const char *bsa_last_error(void);
  *   bsa-lut 2
  *   rule D dtype union paged bq_lo bq_hi bk_lo bk_hi dens_lo dens_hi imb_lo imb_hi
  *        sq_lo sq_hi -> Tq Tk sched split pack
+ * pack is 0, 1 or 2 (see bsa_plan_info.pack; packing applies to union plans
+ * with 2 or 4 query heads per kv head, else it is 0).
  * D, dtype (bf16|f32), union and paged (0|1) may be '*'; ranges are inclusive
  * and match the smallest block_q, smallest block_k, density per mille and
  * imbalance x16 of the mask (and seqlen_q); sched is local|lpt; the first

@@ -542,7 +542,7 @@ static int parse_lut(const char *text, rule_t **rules_out, int *n_out) {
       } else goto bad;
     }
     if ((v[0] != 128 && v[0] != 256) || (v[1] != 64 && v[1] != 128) || v[3] < 0 ||
-        v[3] > (1 << 30) || (v[4] != 0 && v[4] != 1))
+        v[3] > (1 << 30) || v[4] < 0 || v[4] > 2)
       goto bad;
     r->r.tq = (int)v[0], r->r.tk = (int)v[1], r->r.sched = (int)v[2];
     r->r.split = (int)v[3], r->r.pack = (int)v[4];
@@ -617,7 +617,7 @@ int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_tabl
   if (force) {
     rg.tq = force[0], rg.tk = force[1], rg.sched = force[2], rg.split = force[3], rg.pack = force[4];
     if ((rg.tq != 128 && rg.tq != 256) || (rg.tk != 64 && rg.tk != 128) || rg.sched < 0 || rg.sched > 1 ||
-        rg.split < 0 || rg.pack < 0 || rg.pack > 1) {
+        rg.split < 0 || rg.pack < 0 || rg.pack > 2) {
       free(moff), free(uni), free(feat);
       return -2;
     }

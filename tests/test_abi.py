@@ -96,6 +96,7 @@ def test_forward_and_export_null_plan(L):
     ("", "bsa-lut 1"), ("bsa-lut 3", "bsa-lut 1"),
     ("bsa-lut 2\nrule * * * * 0 1 0 1 0 1 0 1 -> 128 64 local 0 0", "bad rule range"), ("bsa-lut 1\nrul", "expected 'rule'"),
     ("bsa-lut 1\nrule * * * * 0 1 0 1 0 1 0 1 -> 128 96 local 0 0", "out of range"),
+    ("bsa-lut 1\nrule * * * * 0 1 0 1 0 1 0 1 -> 128 64 local 0 3", "out of range"),
     ("bsa-lut 1\nrule * x * * 0 1 0 1 0 1 0 1 -> 128 64 local 0 0", "bad rule key"),
     ("bsa-lut 1\nrule * * * * 0 1 0 1 0 1 0 1 128 64 local 0 0", "'->'"),
     ("bsa-lut 1\nrule * * * * 0 1 0 1 0 1 0 1 -> 128 64 fifo 0 0", "bad regime"),

@@ -61,6 +61,8 @@ def _run(ref, w, lut_text=None, rows=None, random_codes=False, device_gen=False,
 
 CASES = {
     "decode_q1": lambda: W.decode(batch=3, hq=8, hkv=2, q_len=1, context=4096, seed=1),
+    "decode_q1_hnd": lambda: W.decode(batch=3, hq=8, hkv=2, q_len=1, context=4096, seed=5,
+                                      kv_layout="hnd"),
     "decode_q5_d64": lambda: W.decode(batch=2, hq=8, hkv=2, d=64, q_len=5, context=3072, seed=2),
     "dense_ragged_d128": lambda: W.random_problem(batch=2, hq=4, hkv=2, sq=300, skv=333, d=128, bq=64,
                                                   bk=64, density=0.4, empty_rows=0.1, causal=True,
@@ -84,8 +86,9 @@ def test_kv8_all_codes(ref, case):
 
 
 @pytest.mark.parametrize("regime", [(128, 128, "lpt", 0, 0), (128, 64, "local", 3, 1),
-                                    (256, 64, "lpt", 2, 1)], ids=str)
-@pytest.mark.parametrize("case", ["dense_ragged_d128", "union_paged", "dense_mixed_d64"])
+                                    (256, 64, "lpt", 2, 1), (128, 64, "local", 3, 2),
+                                    (256, 64, "lpt", 2, 2)], ids=str)
+@pytest.mark.parametrize("case", ["dense_ragged_d128", "union_paged", "dense_mixed_d64", "decode_q1"])
 def test_kv8_regimes(ref, case, regime):
     _run(ref, CASES[case](), lut_text=forced_lut_text(*regime), label=f"{case}/{regime}")
 
@@ -93,6 +96,12 @@ def test_kv8_regimes(ref, case, regime):
 def test_kv8_full_decode(ref):
     w = W.decode(q_len=1)
     _run(ref, w, rows=sample_rows(w, 192), device_gen=True, label="decode_full")
+
+
+def test_kv8_full_decode_interleaved(ref):
+    w = W.decode(q_len=1)
+    _run(ref, w, rows=sample_rows(w, 192), device_gen=True,
+         lut_text=forced_lut_text(128, 64, "local", 32, 2), label="decode_full/ilv")
 
 
 def test_kv8_rejects_fp32_and_null_scales():

@@ -58,6 +58,8 @@ SMALL = {
     "decode_q1": lambda: W.decode(batch=3, hq=8, hkv=2, q_len=1, context=4096, seed=1),
     "decode_q5": lambda: W.decode(batch=2, hq=8, hkv=2, q_len=5, context=3072, seed=2),
     "short_chunk_q16": lambda: W.decode(batch=2, hq=4, hkv=1, d=64, q_len=16, context=2048, seed=3),
+    "decode_q5_hnd": lambda: W.decode(batch=2, hq=8, hkv=2, q_len=5, context=3072, seed=4,
+                                      kv_layout="hnd"),
 }
 
 REGIMES = {
@@ -67,6 +69,11 @@ REGIMES = {
     "split2_lpt_tk128": forced_lut_text(128, 128, "lpt", 2, 1),
     "tq256_local": forced_lut_text(256, 64, "local", 0, 1),
     "tq256_split3_lpt": forced_lut_text(256, 64, "lpt", 3, 1),
+    # heads interleaved row by row in packed tiles
+    "ilv_local": forced_lut_text(128, 64, "local", 0, 2),
+    "ilv_split3": forced_lut_text(128, 64, "local", 3, 2),
+    "ilv_tq256_split2_lpt": forced_lut_text(256, 64, "lpt", 2, 2),
+    "ilv_tk128_split2": forced_lut_text(128, 128, "lpt", 2, 2),
 }
 
 
@@ -83,8 +90,10 @@ def test_small_forced_regimes(ref, case, regime):
     run_case(ref, SMALL[case](), lut_text=REGIMES[regime], label=f"{case}/{regime}")
 
 
-@pytest.mark.parametrize("regime", ["split3_local", "split2_lpt_tk128", "tq256_split3_lpt"])
-@pytest.mark.parametrize("case", ["decode_q1", "decode_q5", "short_chunk_q16"])
+@pytest.mark.parametrize("regime", ["split3_local", "split2_lpt_tk128", "tq256_split3_lpt",
+                                    "ilv_local", "ilv_split3", "ilv_tq256_split2_lpt",
+                                    "ilv_tk128_split2"])
+@pytest.mark.parametrize("case", ["decode_q1", "decode_q5", "short_chunk_q16", "decode_q5_hnd"])
 def test_decode_split_regimes(ref, case, regime):
     """Split-KV on packed decode rows, where most rows of a packed tile do not
     exist: partials are written and combined for existing rows only."""
@@ -128,6 +137,15 @@ def test_full_decode(ref, q_len):
     """16 sequences x 32 query heads over 8 kv heads, 65,536-token paged cache."""
     w = W.decode(q_len=q_len)
     run_case(ref, w, rows=sample_rows(w, 256), device_gen=True, label=f"decode_q{q_len}_full")
+
+
+@pytest.mark.parametrize("q_len", [1, 16])
+def test_full_decode_interleaved(ref, q_len):
+    """The full decode shapes with the group's heads interleaved row by row
+    (split at 32 key tiles)."""
+    w = W.decode(q_len=q_len)
+    run_case(ref, w, lut_text=forced_lut_text(128, 64, "local", 32, 2), rows=sample_rows(w, 256),
+             device_gen=True, label=f"decode_q{q_len}_full/ilv")
 
 
 def test_full_long_video(ref):

@@ -140,6 +140,15 @@ def test_pack_mode_geometry(ref):
     w3 = W.random_problem(batch=1, hq=6, hkv=2, sq=100, skv=300, bq=64, bk=64, density=0.1,
                           gqa_union=True, d=64, seed=4)
     assert decode(ref.plan(w3, force=[128, 64, 0, 0, 1])).h["pack"] == 0
+    # Interleaved packing (pack 2) is an in-tile row order: the plan's rows,
+    # lists and items are those of pack 1.
+    p2 = decode(ref.plan(w, force=[128, 64, 0, 0, 2]))
+    assert p2.h["pack"] == 2
+    for f in ("list_off", "kt", "live", "rows", "items"):
+        assert np.array_equal(getattr(p2, f), getattr(p, f)), f
+    assert decode(ref.plan(w3, force=[128, 64, 0, 0, 2])).h["pack"] == 0
+    with pytest.raises(ValueError):
+        ref.plan(w, force=[128, 64, 0, 0, 3])
 
 
 def test_regime_adjustments(ref):
