@@ -555,9 +555,30 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
   static_assert(NS == 2 || (NS == 4 && KD), "stages");
   // one ring slot: a bf16 tile, or for deep e4m3 rings the e4m3 tile itself
   constexpr int SLOT = (NS > 2 && KD) ? TK * D : C::TILEB;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * NS * SLOT];
-  auto kbuf = [&](int i) { return lds + (i & (NS - 1)) * SLOT; };
-  auto vbuf = [&](int i) { return lds + (NS + (i & (NS - 1))) * SLOT; };
+  // D = 128, two stages: one LDS variable per buffer, chosen by the tile
+  // index's parity, which the tile loop (unrolled by two) knows at compile
+  // time. Every access then names one variable, so the compiler can tell the
+  // reads of a tile from the loads that are filling the other buffer and
+  // does not wait for those loads before the reads. Otherwise one array,
+  // indexed at run time (at D = 64 the unrolled loop needs more registers
+  // than three waves per SIMD allow).
+  constexpr bool RING = NS > 2 || D != 128;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_ring[RING ? 2 * NS * SLOT : 64];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_k0[RING ? 64 : SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_k1[RING ? 64 : SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_v0[RING ? 64 : SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_v1[RING ? 64 : SLOT];
+  // Buffer of K / V tile i; par is std::integral_constant<int, i & 1>.
+  auto kbuf = [&](int i, auto par) -> uint8_t * {
+    if constexpr (RING) return lds_ring + (i & (NS - 1)) * SLOT;
+    else return decltype(par)::value ? lds_k1 : lds_k0;
+  };
+  auto vbuf = [&](int i, auto par) -> uint8_t * {
+    if constexpr (RING) return lds_ring + (NS + (i & (NS - 1))) * SLOT;
+    else return decltype(par)::value ? lds_v1 : lds_v0;
+  };
+  using Even = std::integral_constant<int, 0>;
+  using Odd = std::integral_constant<int, 1>;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // = this wave's 32-row slice
@@ -737,8 +758,8 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
         }
       }
     };
-    auto issue_k = [&](int j, const Meta &m) { issue(kbase_ptr, a.k_sb, a.k_ss, m, kbuf(j), koff0, kstep); };
-    auto issue_v = [&](int j, const Meta &m) { issue(vbase_ptr, a.v_sb, a.v_ss, m, vbuf(j), voff0, vstep); };
+    auto issue_k = [&](int j, auto par, const Meta &m) { issue(kbase_ptr, a.k_sb, a.k_ss, m, kbuf(j, par), koff0, kstep); };
+    auto issue_v = [&](int j, auto par, const Meta &m) { issue(vbase_ptr, a.v_sb, a.v_ss, m, vbuf(j, par), voff0, vstep); };
     // e4m3 tiles (KD): rows of D bytes, 16-byte chunk c of row r at slot
     // c ^ swz8(r). K rows are read 8 bytes at a time by 32 lanes on 32 rows
     // (swz8_k spreads rows of one parity over the 8 slots); V is read by
@@ -774,8 +795,8 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
         }
       }
     };
-    auto issue_k8 = [&](int j, const Meta &m) { issue8(k8base, a.k_sb, a.k_ss, m, kbuf(j), k8off0); };
-    auto issue_v8 = [&](int j, const Meta &m) { issue8(v8base, a.v_sb, a.v_ss, m, vbuf(j), v8off0); };
+    auto issue_k8 = [&](int j, auto par, const Meta &m) { issue8(k8base, a.k_sb, a.k_ss, m, kbuf(j, par), k8off0); };
+    auto issue_v8 = [&](int j, auto par, const Meta &m) { issue8(v8base, a.v_sb, a.v_ss, m, vbuf(j, par), v8off0); };
     (void)issue_k8, (void)issue_v8;
     auto kfrag = [&](const uint8_t *ks, int i) {
       const int row = 32 * (i / (D / 16)) + krow0;
@@ -803,7 +824,9 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
 
     // One tile iteration: softmax of tile j (scores in s_cur), S^T of tile
     // j+1 into s_next, O += V^T P^T of tile j.
-    auto tile = [&](int j, f32x16 (&s_cur)[C::NKB], f32x16 (&s_next)[C::NKB]) {
+    // par is the parity of j (std::integral_constant); flip that of j + 1.
+    auto tile = [&](int j, auto par, f32x16 (&s_cur)[C::NKB], f32x16 (&s_next)[C::NKB]) {
+      const std::integral_constant<int, 1 - decltype(par)::value> flip;
       // K tile j+1 and V tile j have landed (this wave) ...
       if constexpr (NS == 2) {
         __builtin_amdgcn_s_waitcnt(0);
@@ -827,21 +850,21 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
       const Meta mn = load_meta(j + NS + 1);
       if constexpr (NS == 4) {
         if constexpr (KD) {
-          if (j + 4 < nent) issue_k8(j + 4, m4);
-          if (j + 3 < nent) issue_v8(j + 3, m3);
+          if (j + 4 < nent) issue_k8(j + 4, par, m4);
+          if (j + 3 < nent) issue_v8(j + 3, flip, m3);
         } else {
-          if (j + 4 < nent) issue_k(j + 4, m4);
-          if (j + 3 < nent) issue_v(j + 3, m3);
+          if (j + 4 < nent) issue_k(j + 4, par, m4);
+          if (j + 3 < nent) issue_v(j + 3, flip, m3);
         }
       } else if constexpr (KD) {
-        if (j + 2 < nent) issue_k8(j + 2, m2);
-        if (j + 1 < nent) issue_v8(j + 1, m1);
+        if (j + 2 < nent) issue_k8(j + 2, par, m2);
+        if (j + 1 < nent) issue_v8(j + 1, flip, m1);
       } else if constexpr (KV8) {
         if (j + 2 < nent) load8(k8base, a.k_sb, a.k_ss, m2, k8r);
         if (j + 1 < nent) load8(v8base, a.v_sb, a.v_ss, m1, v8r);
       } else {
-        if (j + 2 < nent) issue_k(j + 2, m2);
-        if (j + 1 < nent) issue_v(j + 1, m1);
+        if (j + 2 < nent) issue_k(j + 2, par, m2);
+        if (j + 1 < nent) issue_v(j + 1, flip, m1);
       }
 
       if (wlive) {
@@ -911,7 +934,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
       uint32_t pw[C::NKB * 8];  // P as packed bf16 pairs
       float psum = 0.f;
       {
-        const uint8_t *ks = kbuf(j + 1);
+        const uint8_t *ks = kbuf(j + 1, flip);
         bf16x8 kf[STEPS];
 #pragma unroll
         for (int i = 0; i < 3 && i < STEPS; ++i) kf[i] = kfrag(ks, i);
@@ -936,7 +959,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
 
       // ---- O^T += V^T P^T, V^T fragments by transpose reads of V tile j ----
       {
-        const uint8_t *vs = vbuf(j);
+        const uint8_t *vs = vbuf(j, par);
         constexpr int PV = (TK / 16) * C::NDB;
         auto vfrag = [&](int i) {
           const int c2 = i / C::NDB, u = i % C::NDB;
@@ -975,8 +998,8 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
       }
       }  // wlive
       if constexpr (KV8 && !KD) {
-        if (j + 2 < nent) store8(k8r, kbuf(j + 2), false);
-        if (j + 1 < nent) store8(v8r, vbuf(j + 1), true);
+        if (j + 2 < nent) store8(k8r, kbuf(j + 2, par), false);
+        if (j + 1 < nent) store8(v8r, vbuf(j + 1, flip), true);
       }
       if constexpr (NS == 4) m0 = m1, m1 = m2, m2 = m3, m3 = m4, m4 = mn;
       else m0 = m1, m1 = m2, m2 = mn;
@@ -992,14 +1015,14 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
         // alone.
         auto ik = [&](int i, const Meta &m) {
           if (i < nent) {
-            if constexpr (KD) issue_k8(i, m);
-            else issue_k(i, m);
+            if constexpr (KD) issue_k8(i, Even{}, m);
+            else issue_k(i, Even{}, m);
           }
         };
         auto iv = [&](int i, const Meta &m) {
           if (i < nent) {
-            if constexpr (KD) issue_v8(i, m);
-            else issue_v(i, m);
+            if constexpr (KD) issue_v8(i, Even{}, m);
+            else issue_v(i, Even{}, m);
           }
         };
         ik(0, m0);
@@ -1017,26 +1040,26 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
           default: BSA_WAIT_VM(0); break;
         }
       } else if constexpr (KD) {
-        issue_k8(0, m0);
-        issue_v8(0, m0);
-        if (nent > 1) issue_k8(1, m1);
+        issue_k8(0, Even{}, m0);
+        issue_v8(0, Even{}, m0);
+        if (nent > 1) issue_k8(1, Odd{}, m1);
       } else if constexpr (KV8) {
         load8(k8base, a.k_sb, a.k_ss, m0, k8r);
         load8(v8base, a.v_sb, a.v_ss, m0, v8r);
-        store8(k8r, kbuf(0), false);
-        store8(v8r, vbuf(0), true);
+        store8(k8r, kbuf(0, Even{}), false);
+        store8(v8r, vbuf(0, Even{}), true);
         if (nent > 1) {
           load8(k8base, a.k_sb, a.k_ss, m1, k8r);
-          store8(k8r, kbuf(1), false);
+          store8(k8r, kbuf(1, Odd{}), false);
         }
       } else {
-        issue_k(0, m0);
-        issue_v(0, m0);
-        if (nent > 1) issue_k(1, m1);
+        issue_k(0, Even{}, m0);
+        issue_v(0, Even{}, m0);
+        if (nent > 1) issue_k(1, Odd{}, m1);
       }
       if constexpr (NS == 2) __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      const uint8_t *ks = kbuf(0);
+      const uint8_t *ks = kbuf(0, Even{});
       if (wlive) {
 #pragma unroll
         for (int i = 0; i < STEPS; ++i) {
@@ -1045,10 +1068,17 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
         }
       }
     }
-    for (int j = 0; j < nent; ++j) {
-      tile(j, sa, sb);
+    if constexpr (!RING) {
+      for (int j = 0; j < nent; j += 2) {
+        tile(j, Even{}, sa, sb);
+        if (j + 1 < nent) tile(j + 1, Odd{}, sb, sa);
+      }
+    } else {
+      for (int j = 0; j < nent; ++j) {
+        tile(j, Even{}, sa, sb);  // the buffers follow j itself
 #pragma unroll
-      for (int t = 0; t < C::NKB; ++t) sa[t] = sb[t];
+        for (int t = 0; t < C::NKB; ++t) sa[t] = sb[t];
+      }
     }
     __syncthreads();  // the next item's first loads reuse the buffers
 
