@@ -931,6 +931,10 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
       // MFMAs follow their transpose reads. sched_barrier(0) keeps the
       // compiler from regrouping the steps. On the last tile the S^T of a
       // stale buffer is computed and dropped.
+      // The wave takes issue priority over the other waves of its SIMD while
+      // it interleaves the S^T MFMAs with the exponentials (measured: 2-4%
+      // faster than equal priorities, or than raising it for P·V as well).
+      __builtin_amdgcn_s_setprio(1);
       uint32_t pw[C::NKB * 8];  // P as packed bf16 pairs
       float psum = 0.f;
       {
@@ -955,6 +959,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       l_run += psum;
 
       // ---- O^T += V^T P^T, V^T fragments by transpose reads of V tile j ----
