@@ -183,20 +183,24 @@ __device__ __forceinline__ uint32_t live_bits(const MapArgs &a, int bm, int h, i
                                               int64_t kt) {
   const HeadMeta m = a.hm[h];
   const int64_t bq = m.bq, bk = m.bk;
-  const int mq = (!a.uni && bq < a.tq) ? (int)(a.tq / bq) : 1;
-  const int mk = bk < a.tk ? (int)(a.tk / bk) : 1;
+  // Block and tile sizes are powers of two: index arithmetic by shifts (a
+  // 64-bit division per lane would dominate the kernel).
+  const int lbq = __builtin_ctz(m.bq), lbk = __builtin_ctz(m.bk);
+  const int ltq = __builtin_ctz(a.tq), ltk = __builtin_ctz(a.tk);
+  const int mq = (!a.uni && bq < a.tq) ? 1 << (ltq - lbq) : 1;
+  const int mk = bk < a.tk ? 1 << (ltk - lbk) : 1;
   const int64_t aq = bq < a.tq ? bq : a.tq, ak = bk < a.tk ? bk : a.tk;
   const uint8_t *mb = a.acsr ? nullptr : a.mask + bm * a.mask_bstride + m.mask_off;
   const uint8_t *u = a.uni ? a.U + ((int64_t)bm * a.Hkv + g) * a.unkb : nullptr;
   uint32_t live = 0;
   for (int iq = 0; iq < mq; ++iq) {
-    const int64_t qb = bq < a.tq ? qt * mq + iq : (qt * a.tq) / bq;
+    const int64_t qb = bq < a.tq ? qt * mq + iq : (qt << ltq) >> lbq;
     if (!u && qb >= m.nqb) continue;
     int64_t first[BSA_ACSR_MAX_RUNS];
     const int nruns = a.acsr ? a.acsr[h].num_runs : 0;
     for (int j = 0; j < nruns; ++j) first[j] = acsr_first(a.acsr[h].runs[j], qb);
     for (int ik = 0; ik < mk; ++ik) {
-      const int64_t kb = bk < a.tk ? kt * mk + ik : (kt * a.tk) / bk;
+      const int64_t kb = bk < a.tk ? kt * mk + ik : (kt << ltk) >> lbk;
       if (kb >= m.nkb) continue;
       if (a.acsr) {
         bool sel = false;
@@ -245,7 +249,8 @@ __global__ void k_map(MapArgs a) {
       const int64_t idx = base + run + __popcll(bal & (unsigned long long)lo_mask(lane));
       a.ent_kt[idx] = (int32_t)kt;
       a.ent_live[idx] = live;
-      if (a.paged) a.ent_page[idx] = a.page_table[(int64_t)lb * a.pps + kt * a.tk / a.P];
+      // key positions are below 2^31: a 32-bit division
+      if (a.paged) a.ent_page[idx] = a.page_table[(int64_t)lb * a.pps + (int)(kt * a.tk) / a.P];
     }
     run += __popcll(bal);
   }
