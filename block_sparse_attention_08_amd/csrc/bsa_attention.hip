@@ -751,9 +751,14 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
         }
       } else {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)tb, 0, bytes, 0x00020000);
+        // The wave's byte offset, opaque to the compiler: the LDS addresses
+        // of the loads are then formed per call from one scalar, instead of
+        // one kept live per load and buffer (which spills scalar registers).
+        int wofs = wave * 64 * 16;
+        asm volatile("" : "+s"(wofs));
 #pragma unroll
         for (int u = 0; u < C::LOADS; ++u) {
-          uint8_t *dst = dst_tile + (u * C::THREADS + wave * 64) * 16;  // lane-linear 1 KiB per wave
+          uint8_t *dst = dst_tile + u * C::THREADS * 16 + wofs;  // lane-linear 1 KiB per wave
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, off0 + u * step, 0, 0, 0);
         }
       }
