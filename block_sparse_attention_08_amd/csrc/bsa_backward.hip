@@ -109,6 +109,42 @@ __device__ __forceinline__ bf16x8 tr_frag_s(const uint8_t *t, int r0, int c0, in
 // s_waitcnt with only the vector-memory counter constrained (<= n).
 #define BSA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+// Buffer resource of `bytes` bytes at base (raw buffer, no swizzle).
+__device__ __forceinline__ v4u32 raw_rsrc(const void *base, int bytes) {
+  const uint64_t v = (uint64_t)base;
+  return v4u32{(uint32_t)v, (uint32_t)(v >> 32) & 0xffffu, (uint32_t)bytes, 0x00020000u};
+}
+// Buffer loads straight into LDS at M0 (lane l writes M0 + 16 l, or M0 + 4 l
+// for the dword form), written as assembly: the compiler then does not treat
+// the later LDS reads of the other ring buffers as possibly aliasing them
+// (it would wait for every load in flight, three chunks ahead included,
+// before the first such read). The chunk pipeline orders the loads and the
+// reads of their buffers itself (partial vmcnt waits, then a barrier). The
+// address operand is read at issue; no register receives data. M0 has no
+// other user in this kernel.
+__device__ __forceinline__ void dma_b128(v4u32 rsrc, int voff, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "s"(lds_addr)
+      : "m0");
+}
+__device__ __forceinline__ void dma_b32(v4u32 rsrc, int voff, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "s"(lds_addr)
+      : "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr_of(const uint8_t *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)p);
+}
+
 // ---------------------------------------------------------------------------
 // dQ (and Delta) per plan row
 // ---------------------------------------------------------------------------
@@ -182,13 +218,15 @@ __global__ __launch_bounds__(2 * TQ, TQ == 128 ? 2 : 1) void k_bwd_dq(BwdArgs a)
     const int k0 = ((const cint32 *)a.ent_kt)[e0 + j] * TK;
     const int left = min(skv32 - k0, TK);
     uint8_t *dst = lds + 2 * (j & 1) * TILEB;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(Kb + (int64_t)k0 * a.k_ss), 0, (left - 1) * (int)a.k_ss * 2 + D * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(Vb + (int64_t)k0 * a.v_ss), 0, (left - 1) * (int)a.v_ss * 2 + D * 2, 0x00020000);
+    const v4u32 rk = raw_rsrc(Kb + (int64_t)k0 * a.k_ss, (left - 1) * (int)a.k_ss * 2 + D * 2);
+    const v4u32 rv = raw_rsrc(Vb + (int64_t)k0 * a.v_ss, (left - 1) * (int)a.v_ss * 2 + D * 2);
+    // (assembly-issued: the reads of tile j do not wait for tile j+1's
+    // loads; the loop waits for them at its top)
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       uint8_t *d = dst + (u * T + wave * 64) * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)d, 16, koff0 + u * RPL * (int)a.k_ss * 2, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(d + TILEB), 16, voff0 + u * RPL * (int)a.v_ss * 2, 0, 0, 0);
+      dma_b128(rk, koff0 + u * RPL * (int)a.k_ss * 2, lds_addr_of(d));
+      dma_b128(rv, voff0 + u * RPL * (int)a.v_ss * 2, lds_addr_of(d + TILEB));
     }
   };
 
@@ -357,22 +395,21 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdArgs a) {
     const int rows = min(sq32 - q0, 32);        // rows of the chunk that exist (>= 1)
     const uint16_t *qb_ = (const uint16_t *)a.q + b * a.q_sb + h * a.q_sh + (int64_t)q0 * a.q_ss;
     const uint16_t *db_ = (const uint16_t *)a.dout + b * a.do_sb + h * a.do_sh + (int64_t)q0 * a.do_ss;
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)qb_, 0, (rows - 1) * (int)a.q_ss * 2 + D * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc((void *)db_, 0, (rows - 1) * (int)a.do_ss * 2 + D * 2, 0x00020000);
+    const v4u32 rq = raw_rsrc(qb_, (rows - 1) * (int)a.q_ss * 2 + D * 2);
+    const v4u32 rd = raw_rsrc(db_, (rows - 1) * (int)a.do_ss * 2 + D * 2);
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       uint8_t *dq_ = dst + (u * T + wave * 64) * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)dq_, 16, qoff0 + u * RPL * (int)a.q_ss * 2, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void *)(dq_ + CHB), 16, doff0 + u * RPL * (int)a.do_ss * 2, 0, 0, 0);
+      dma_b128(rq, qoff0 + u * RPL * (int)a.q_ss * 2, lds_addr_of(dq_));
+      dma_b128(rd, doff0 + u * RPL * (int)a.do_ss * 2, lds_addr_of(dq_ + CHB));
     }
     // LSE (wave 0) and Delta (wave 1) of the chunk's rows, one dword per lane;
     // waves 2 and 3 repeat the LSE load into a spare area so that every wave
     // has the same number of loads in flight per chunk.
     const int64_t rix = ((int64_t)b * a.Hq + h) * a.Sq + q0;
     const float *src = wave == 1 ? a.delta + rix : a.lse + rix;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)src, 0, rows * 4, 0x00020000);
     uint8_t *dl = dst + 2 * CHB + (wave == 1 ? 256 : (wave == 0 ? 0 : 512 + 256 * (wave - 2)));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dl, 4, lane * 4, 0, 0, 0);
+    dma_b32(raw_rsrc(src, rows * 4), lane * 4, lds_addr_of(dl));
   };
   auto issue = [&](int e, int buf) {
     issue_qm(((const cint32 *)a.t_q0)[e], ((const cint32 *)a.t_meta)[e], buf);
