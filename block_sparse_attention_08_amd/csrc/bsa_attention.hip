@@ -741,7 +741,10 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
       const uint16_t *tb = PAGED ? base + (int64_t)m.pg * sb + (int64_t)prow * ss
                                  : base + (int64_t)k0 * ss;
       const int bytes = (left - 1) * (int)ss * 2 + D * 2;
-      if constexpr (NS == 4) {
+      // One LDS array (deep rings, D = 64): the loads are issued from
+      // assembly, so the reads of tile j do not wait for the loads filling
+      // the other buffers; the tile loop waits for them itself.
+      if constexpr (RING) {
         const uint64_t tbv = (uint64_t)tb;
         const v4u32 rs = {(uint32_t)tbv, (uint32_t)(tbv >> 32) & 0xffffu, (uint32_t)bytes, 0x00020000u};
 #pragma unroll
