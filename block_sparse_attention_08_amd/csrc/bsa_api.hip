@@ -109,6 +109,7 @@ static bsa_status parse_lut(const char *text, bsa_lut_s *lut) {
       if (!next(t)) return fail(BSA_ERR_LUT, "truncated rule");
       if (f == 2 && t == "local") v[f] = 0;
       else if (f == 2 && t == "lpt") v[f] = 1;
+      else if (f == 2 && t == "dealt") v[f] = 2;
       else if (f == 2 || !parse_i64(t, &v[f])) return fail(BSA_ERR_LUT, "bad regime value '" + t + "'");
     }
     if ((v[0] != 128 && v[0] != 256) || (v[1] != 64 && v[1] != 128) || v[3] < 0 ||

@@ -586,16 +586,28 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
   const int nitems = a.counters[CNT_ITEMS];
   // Work distribution: workgroups are dispatched round-robin over the 8 XCDs,
   // so workgroup b runs on XCD b % 8 (when the grid is a multiple of 8). Each
-  // XCD owns a queue of items: a contiguous stretch of the work list in row
-  // order (neighbouring query tiles share K/V in that XCD's L2), every 8th
-  // item in longest-first order (the XCDs get equal shares of long and short
-  // items). Its workgroups take items from it with an atomic ticket, so an
-  // XCD's workgroups finish together however the item lengths vary.
+  // XCD owns a queue of items:
+  //   sched 0: a contiguous stretch of the work list in row order
+  //            (neighbouring query tiles share K/V in that XCD's L2);
+  //   sched 1: every 8th item in longest-first order (the XCDs get equal
+  //            shares of long and short items);
+  //   sched 2: row order dealt in blocks of kDeal items to the XCDs in turn
+  //            (neighbouring tiles still share an XCD, and all XCDs work in
+  //            one region of the list at a time, so the K/V they stream
+  //            together fits the last-level cache; balanced when the rows'
+  //            lengths change along the list).
+  // Its workgroups take items from it with an atomic ticket, so an XCD's
+  // workgroups finish together however the item lengths vary.
   const int nq = (gridDim.x & 7) == 0 ? kQueuesPerSet : 1;
   const int xq = blockIdx.x % nq;
-  const bool strided = a.sched != 0;
-  const int qbeg = strided ? xq : (int)((int64_t)xq * nitems / nq);
-  const int qcnt = strided ? (nitems - xq + nq - 1) / nq : (int)((int64_t)(xq + 1) * nitems / nq) - qbeg;
+  const bool strided = a.sched == 1, dealt = a.sched == 2;
+  constexpr int kDeal = 64;
+  const int nfull = nitems / kDeal, rem = nitems % kDeal;
+  const int qbeg = strided ? xq : (dealt ? 0 : (int)((int64_t)xq * nitems / nq));
+  const int qcnt = strided ? (nitems - xq + nq - 1) / nq
+                   : dealt ? (nfull > xq ? (nfull - xq + nq - 1) / nq : 0) * kDeal +
+                                 ((rem > 0 && nfull % nq == xq) ? rem : 0)
+                           : (int)((int64_t)(xq + 1) * nitems / nq) - qbeg;
   int *const qctr = a.queue + xq;
   __shared__ int s_ticket;
   const uint16_t *__restrict__ Q = (const uint16_t *)a.q;
@@ -621,7 +633,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
     // The next ticket is taken now; its value is needed only after this item.
     int next_ticket = 0;
     if (tid == 0) next_ticket = atomicAdd(qctr, 1);
-    const int it = strided ? qbeg + tk * nq : qbeg + tk;
+    const int it = strided ? qbeg + tk * nq : dealt ? ((tk / kDeal) * nq + xq) * kDeal + tk % kDeal : qbeg + tk;
     const int4 item = ((const int4 *)a.items)[it];
     const int r = item.x, e0 = item.y, nent = item.z - item.y, slot = item.w;
 

@@ -70,7 +70,8 @@ def decode_candidates():
 
 def candidates(union: bool):
     out = []
-    for tq, tk, sched, split in itertools.product((128, 256), (64, 128), ("local", "lpt"), (0, 128, 256)):
+    for tq, tk, sched, split in itertools.product((128, 256), (64, 128), ("local", "lpt", "dealt"),
+                                                  (0, 128, 256)):
         if tq == 256 and tk == 128:
             continue  # the planner turns it into 256 x 64
         for pack in ((1, 0) if union else (0,)):

@@ -102,7 +102,8 @@ typedef struct {
 /* Plan statistics, filled by bsa_plan_stats. */
 typedef struct {
   int32_t tile_q, tile_k;   /* physical tile shape */
-  int32_t sched;            /* 0 = row order (locality), 1 = longest first */
+  int32_t sched;            /* 0 = row order (locality), 1 = longest first,
+                               2 = row order dealt to the XCDs in blocks of 64 */
   int32_t split;            /* key tiles per work item before a row is split; 0 = never */
   int32_t pack;             /* 1: a group's heads share each task, head after head;
                                2: the same tasks with the heads interleaved row by row
@@ -141,7 +142,7 @@ const char *bsa_last_error(void);
  * with 2 or 4 query heads per kv head, else it is 0).
  * D, dtype (bf16|f32), union and paged (0|1) may be '*'; ranges are inclusive
  * and match the smallest block_q, smallest block_k, density per mille and
- * imbalance x16 of the mask (and seqlen_q); sched is local|lpt; the first
+ * imbalance x16 of the mask (and seqlen_q); sched is local|lpt|dealt; the first
  * matching rule wins; with no match the built-in default applies
  * (128, 64, local, 0, 1).
  * bsa_lut_load reads a file (path NULL: the built-in default with no rules);

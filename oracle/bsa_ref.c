@@ -538,6 +538,7 @@ static int parse_lut(const char *text, rule_t **rules_out, int *n_out) {
       if (next_token(&cur, tok, sizeof tok) != 1) goto bad;
       if (f == 2 && !strcmp(tok, "local")) v[f] = 0;
       else if (f == 2 && !strcmp(tok, "lpt")) v[f] = 1;
+      else if (f == 2 && !strcmp(tok, "dealt")) v[f] = 2;
       else if (f != 2 && !parse_int(tok, &v[f])) {
       } else goto bad;
     }
@@ -616,7 +617,7 @@ int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_tabl
   regime_t rg = {128, 64, 0, 0, 1};
   if (force) {
     rg.tq = force[0], rg.tk = force[1], rg.sched = force[2], rg.split = force[3], rg.pack = force[4];
-    if ((rg.tq != 128 && rg.tq != 256) || (rg.tk != 64 && rg.tk != 128) || rg.sched < 0 || rg.sched > 1 ||
+    if ((rg.tq != 128 && rg.tq != 256) || (rg.tk != 64 && rg.tk != 128) || rg.sched < 0 || rg.sched > 2 ||
         rg.split < 0 || rg.pack < 0 || rg.pack > 2) {
       free(moff), free(uni), free(feat);
       return -2;

@@ -107,6 +107,11 @@ def test_lut_parse_errors(L, text, needle):
     assert e.value.status == 6 and needle in str(e.value)
 
 
+def test_lut_schedules(L):
+    for sched in ("local", "lpt", "dealt"):
+        assert bsa.Lut.parse(f"bsa-lut 1\nrule * * * * 0 1 0 1 0 1 0 1 -> 128 64 {sched} 0 0").handle.value
+
+
 def test_lut_files(L):
     lut = bsa.Lut.load(bsa.DEFAULT_LUT)
     assert lut.handle.value

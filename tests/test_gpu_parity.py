@@ -74,6 +74,9 @@ REGIMES = {
     "ilv_split3": forced_lut_text(128, 64, "local", 3, 2),
     "ilv_tq256_split2_lpt": forced_lut_text(256, 64, "lpt", 2, 2),
     "ilv_tk128_split2": forced_lut_text(128, 128, "lpt", 2, 2),
+    # row order dealt to the XCDs in blocks
+    "dealt": forced_lut_text(128, 64, "dealt", 0, 1),
+    "dealt_split3_tq256": forced_lut_text(256, 64, "dealt", 3, 0),
 }
 
 
@@ -92,7 +95,7 @@ def test_small_forced_regimes(ref, case, regime):
 
 @pytest.mark.parametrize("regime", ["split3_local", "split2_lpt_tk128", "tq256_split3_lpt",
                                     "ilv_local", "ilv_split3", "ilv_tq256_split2_lpt",
-                                    "ilv_tk128_split2"])
+                                    "ilv_tk128_split2", "dealt_split3_tq256"])
 @pytest.mark.parametrize("case", ["decode_q1", "decode_q5", "short_chunk_q16", "decode_q5_hnd"])
 def test_decode_split_regimes(ref, case, regime):
     """Split-KV on packed decode rows, where most rows of a packed tile do not

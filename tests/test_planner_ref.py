@@ -212,6 +212,23 @@ rule * * * *  0 1000  0 1000  0 1000  0 100000  1 64 -> 128 64 local 32 0
 rule * * * *  0 1000  0 1000  0 1000  0 100000  0 1000000 -> 128 64 lpt 5 0
 """
 
+LUT_DEALT = """\
+bsa-lut 1
+rule * * * *  0 1000  0 1000  0 1000  0 100000 -> 128 64 dealt 3 0
+"""
+
+
+def test_lut_dealt_schedule(ref):
+    """'dealt' is schedule 2: the plan's items stay in row order (the kernel
+    deals them to the XCDs in blocks); everything else equals 'local'."""
+    w = W.random_problem(batch=1, hq=3, sq=700, skv=900, bq=64, bk=64, d=64, density=0.4,
+                         seed=21)
+    pd = decode(ref.plan(w, lut_text=LUT_DEALT))
+    pl = decode(ref.plan(w, lut_text=LUT_DEALT.replace("dealt", "local")))
+    assert (pd.h["sched"], pd.h["split"]) == (2, 3) and pl.h["sched"] == 0
+    assert np.array_equal(pd.items, pl.items)
+    assert {k: v for k, v in pd.h.items() if k != "sched"} == {k: v for k, v in pl.h.items() if k != "sched"}
+
 
 def test_lut_version2_query_length_range(ref):
     """Format 2 adds a range on Sq: the first rule applies to 1..64 queries only."""
