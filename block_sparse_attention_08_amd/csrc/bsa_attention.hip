@@ -560,9 +560,10 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
   // time. Every access then names one variable, so the compiler can tell the
   // reads of a tile from the loads that are filling the other buffer and
   // does not wait for those loads before the reads. Otherwise one array,
-  // indexed at run time (at D = 64 the unrolled loop needs more registers
-  // than three waves per SIMD allow).
-  constexpr bool RING = NS > 2 || D != 128;
+  // indexed at run time (at D = 64, and for e4m3 tiles, the unrolled loop
+  // needs more registers than the occupancy allows), whose loads are issued
+  // from assembly for the same reason.
+  constexpr bool RING = NS > 2 || D != 128 || KV8;
   __shared__ __attribute__((aligned(1024))) uint8_t lds_ring[RING ? 2 * NS * SLOT : 64];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_k0[RING ? 64 : SLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_k1[RING ? 64 : SLOT];
@@ -798,7 +799,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
       const int prow = ptiles_pow2 ? (m.kt & (ptiles - 1)) * TK : (m.kt % max(ptiles, 1)) * TK;
       const uint8_t *tb = PAGED ? base + (int64_t)m.pg * sb + (int64_t)prow * ss : base + (int64_t)k0 * ss;
       const int bytes = (left - 1) * (int)ss + D;
-      if constexpr (NS == 4) {
+      if constexpr (RING) {  // assembly-issued, as for bf16 tiles in one array
         const uint64_t tbv = (uint64_t)tb;
         const v4u32 rs = {(uint32_t)tbv, (uint32_t)(tbv >> 32) & 0xffffu, (uint32_t)bytes, 0x00020000u};
 #pragma unroll
@@ -1108,34 +1109,52 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
     __syncthreads();  // the next item's first loads reuse the buffers
 
     // ---- finalize ----
-    const float l_tot = halfwave_sum(l_run);
-    const float inv = l_tot > 0.f ? (KV8 ? ((const cfloat *)a.v_scale)[g_u] : 1.f) / l_tot : 0.f;
-    const float lse = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
-    if (slot < 0) {
-      if (qvalid) {
-        uint16_t *op = (uint16_t *)a.o + b * a.o_sb + head * a.o_sh + qpos * a.o_ss;
+    // bf16 tiles at D = 128, contiguous K/V: the output arguments are read
+    // again here, from the kernel-argument segment (which holds `a` at
+    // offset 0) through a pointer the compiler cannot see through, instead
+    // of being kept in scalar registers through the tile loop (whose scalar
+    // spills then vanish; video-DiT -1.8%). Elsewhere it measured slower
+    // (paged K/V: +0.7%) or costs vector registers (D = 64 no longer fits
+    // three waves per SIMD), so `a` is read as before.
+    constexpr bool RELOAD = D == 128 && !KV8 && !PAGED;
+    auto store_out = [&](const AttnArgs &oa) {
+      const float l_tot = halfwave_sum(l_run);
+      const float inv = l_tot > 0.f ? (KV8 ? ((const cfloat *)a.v_scale)[g_u] : 1.f) / l_tot : 0.f;
+      const float lse = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+      if (slot < 0) {
+        if (qvalid) {
+          uint16_t *op = (uint16_t *)oa.o + b * oa.o_sb + head * oa.o_sh + qpos * oa.o_ss;
+#pragma unroll
+          for (int u = 0; u < C::NDB; ++u)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const int d0 = 32 * u + 8 * q4 + 4 * hh;
+              *(uint2 *)(op + d0) = make_uint2(pack_bf16x2(o[u][4 * q4] * inv, o[u][4 * q4 + 1] * inv),
+                                               pack_bf16x2(o[u][4 * q4 + 2] * inv, o[u][4 * q4 + 3] * inv));
+            }
+          if (hh == 0) oa.lse[((int64_t)b * oa.Hq + head) * oa.Sq + qpos] = lse;
+        }
+      } else if (qvalid) {  // the combine reads partials of existing rows only
+        const int64_t prow = (int64_t)slot * TQ + 32 * wave + n;
+        float *pp = oa.part_o + prow * D;
 #pragma unroll
         for (int u = 0; u < C::NDB; ++u)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
             const int d0 = 32 * u + 8 * q4 + 4 * hh;
-            *(uint2 *)(op + d0) = make_uint2(pack_bf16x2(o[u][4 * q4] * inv, o[u][4 * q4 + 1] * inv),
-                                             pack_bf16x2(o[u][4 * q4 + 2] * inv, o[u][4 * q4 + 3] * inv));
+            *(float4 *)(pp + d0) = make_float4(o[u][4 * q4] * inv, o[u][4 * q4 + 1] * inv,
+                                               o[u][4 * q4 + 2] * inv, o[u][4 * q4 + 3] * inv);
           }
-        if (hh == 0) a.lse[((int64_t)b * a.Hq + head) * a.Sq + qpos] = lse;
+        if (hh == 0) oa.part_lse[prow] = lse;
       }
-    } else if (qvalid) {  // the combine reads partials of existing rows only
-      const int64_t prow = (int64_t)slot * TQ + 32 * wave + n;
-      float *pp = a.part_o + prow * D;
-#pragma unroll
-      for (int u = 0; u < C::NDB; ++u)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d0 = 32 * u + 8 * q4 + 4 * hh;
-          *(float4 *)(pp + d0) = make_float4(o[u][4 * q4] * inv, o[u][4 * q4 + 1] * inv,
-                                             o[u][4 * q4 + 2] * inv, o[u][4 * q4 + 3] * inv);
-        }
-      if (hh == 0) a.part_lse[prow] = lse;
+    };
+    if constexpr (RELOAD) {
+      const __attribute__((address_space(4))) AttnArgs *kp =
+          (const __attribute__((address_space(4))) AttnArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+      asm volatile("" : "+s"(kp));
+      store_out(*(const AttnArgs *)kp);
+    } else {
+      store_out(a);
     }
     // Every thread read the current ticket before the barriers of this item.
     if (tid == 0) s_ticket = next_ticket;
