@@ -649,17 +649,17 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
       Meta m{0, 0, 0};
       if (nent <= 0) return m;  // an item without entries reads no metadata
       const int ee = e0 + min(j, nent - 1);
-      if constexpr (PAGED && !KV8) {
-        // paged bf16 kernels: the entry arrays' addresses are read from the
-        // kernel-argument segment per call (scalar loads one tile ahead)
-        // rather than kept in scalar registers (whose spills were restored
-        // in the tile loop: chunked prefill -3.7%; e4m3 decode +1%, so it
-        // keeps the plain reads)
+      if constexpr ((PAGED || D == 64) && !KV8) {
+        // paged and D = 64 bf16 kernels: the entry arrays' addresses are read
+        // from the kernel-argument segment per call (scalar loads one tile
+        // ahead) rather than kept in scalar registers (whose spills were
+        // restored in the tile loop: chunked prefill -3.7%, affine -1 to
+        // -2%; e4m3 decode +1%, so it keeps the plain reads)
         const __attribute__((address_space(4))) AttnArgs *kp =
             (const __attribute__((address_space(4))) AttnArgs *)__builtin_amdgcn_kernarg_segment_ptr();
         asm volatile("" : "+s"(kp));
         m.kt = ((const cint32 *)kp->ent_kt)[ee];
-        m.pg = ((const cint32 *)kp->ent_page)[ee];
+        m.pg = PAGED ? ((const cint32 *)kp->ent_page)[ee] : 0;
         m.lv = ((const cuint32 *)kp->ent_live)[ee];
       } else {
         m.kt = ((const cint32 *)a.ent_kt)[ee];
