@@ -20,14 +20,17 @@
 //     the following P V^T MFMA: P never leaves registers.
 //   - O is accumulated transposed, O^T = V^T P^T, so each lane owns one query
 //     and the online-softmax rescale is per lane.
-//   - K tiles are stored in LDS row-major; V tiles are stored transposed
-//     (d-major) so each MFMA operand is one 16-byte LDS read. Both are double
-//     buffered: the global loads of tile e+1 are in flight while tile e is
-//     computed. Rows beyond the sequence are zero-filled, never read.
-//   - Workgroups are persistent: each takes items i, i + grid, ... of the
-//     plan's work list; the block-to-item map is XCD-aware so that
-//     consecutive items (neighbouring query tiles that share key tiles) run
-//     on the same XCD and reuse its L2.
+//   - K and V tiles are double buffered in LDS: the loads of the next tiles
+//     are in flight while the current one is computed. The bf16 kernel
+//     loads them straight from HBM into XOR-swizzled row-major LDS (buffer
+//     loads with an LDS destination) and reads the V^T operands with LDS
+//     transpose reads; the fp32 kernel stages its tiles through registers.
+//     Rows beyond the sequence read as zero and are masked.
+//   - Workgroups are persistent (the bf16 kernel: one queue of items per XCD,
+//     taken with atomic tickets, in row order, longest-first, or row order
+//     dealt to the XCDs in blocks; the fp32 kernel: items i, i + grid, ...),
+//     so consecutive items (neighbouring query tiles that share key tiles)
+//     run on the same XCD and reuse its L2.
 #include "bsa_internal.h"
 
 #include <algorithm>
@@ -475,8 +478,10 @@ typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 // One 16-byte-per-lane buffer load into LDS at M0 (lane l writes M0 + 16 l),
 // written as assembly: the compiler then does not treat every later LDS read
 // as possibly aliasing it (it would wait for all such loads at the first LDS
-// read, emptying a deep ring). The deep-ring kernels order these loads and
-// the reads of their tiles themselves (partial waits, then a barrier).
+// read, emptying a deep ring). The kernels that keep their tiles in one LDS
+// array (deep rings, D = 64, e4m3 tiles) issue all their tile loads this way
+// and order them and the reads of their tiles themselves (waits, then a
+// barrier); M0 has no other user in those kernels.
 __device__ __forceinline__ void dma16(v4u32 rsrc, int voff, uint32_t lds_addr) {
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
