@@ -20,8 +20,10 @@ LIB_PATH = os.environ.get("BSA_LIBRARY") or os.path.join(PKG_DIR, "libbsa.so")
 DEFAULT_LUT = os.path.join(PKG_DIR, "lut", "gfx950.lut")
 
 BSA_OK = 0
+BSA_WARN_LUT_DEFAULT = 7
 STATUS_NAMES = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "shape mismatch",
-                4: "out of memory", 5: "HIP error", 6: "lookup table error"}
+                4: "out of memory", 5: "HIP error", 6: "lookup table error",
+                7: "lookup table replaced by the built-in default"}
 DTYPES = {"bf16": 0, "f32": 1}
 
 
@@ -147,8 +149,15 @@ class Lut:
 
     @classmethod
     def load(cls, path: Optional[str] = DEFAULT_LUT) -> "Lut":
+        """bsa_lut_load: path None gives the built-in table; a missing or
+        malformed file also gives it, with a Python warning."""
         h = ctypes.c_void_p()
-        _check(lib().bsa_lut_load(path.encode() if path else None, ctypes.byref(h)))
+        st = lib().bsa_lut_load(path.encode() if path else None, ctypes.byref(h))
+        if st == BSA_WARN_LUT_DEFAULT:
+            import warnings
+            warnings.warn("libbsa: " + lib().bsa_last_error().decode(), RuntimeWarning, stacklevel=2)
+        else:
+            _check(st)
         return cls(h.value)
 
     @classmethod

@@ -38,90 +38,6 @@ static int ilog2(int64_t x) {
 static size_t aligned(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // ---------------------------------------------------------------------------
-// Regime lookup table (Tessera, abstract: profile-guided regime selection
-// through a lookup table constructed from offline profiling).
-// ---------------------------------------------------------------------------
-struct Rule {
-  int64_t key[4];  // D, dtype, union, paged (-1 = any)
-  int64_t lo[5], hi[5];  // min bq, min bk, density per mille, imbalance x16, Sq (version 2)
-  Regime r;
-};
-
-}  // namespace bsa
-
-struct bsa_lut_s {
-  std::vector<bsa::Rule> rules;
-};
-
-namespace bsa {
-
-static bool parse_i64(const std::string &t, int64_t *out) {
-  if (t.empty()) return false;
-  char *end = nullptr;
-  long long v = std::strtoll(t.c_str(), &end, 10);
-  if (*end) return false;
-  *out = v;
-  return true;
-}
-
-static bsa_status parse_lut(const char *text, bsa_lut_s *lut) {
-  // Tokenise, dropping '#' comments.
-  std::vector<std::string> tok;
-  std::istringstream lines(text);
-  std::string line;
-  while (std::getline(lines, line)) {
-    const size_t hash = line.find('#');
-    if (hash != std::string::npos) line.resize(hash);
-    std::istringstream ws(line);
-    std::string t;
-    while (ws >> t) tok.push_back(t);
-  }
-  size_t i = 0;
-  auto next = [&](std::string &t) {
-    if (i >= tok.size()) return false;
-    t = tok[i++];
-    return true;
-  };
-  std::string t;
-  int64_t x;
-  if (!next(t) || t != "bsa-lut" || !next(t) || !parse_i64(t, &x) || (x != 1 && x != 2))
-    return fail(BSA_ERR_LUT, "lookup table must start with 'bsa-lut 1' or 'bsa-lut 2'");
-  const int nranges = x == 2 ? 5 : 4;  // version 2 adds a range on the query length
-  while (next(t)) {
-    if (t != "rule") return fail(BSA_ERR_LUT, "expected 'rule', got '" + t + "'");
-    Rule r{};
-    for (int f = 0; f < 4; ++f) {
-      if (!next(t)) return fail(BSA_ERR_LUT, "truncated rule");
-      if (t == "*") r.key[f] = -1;
-      else if (f == 1 && t == "bf16") r.key[f] = BSA_BF16;
-      else if (f == 1 && t == "f32") r.key[f] = BSA_F32;
-      else if (f != 1 && parse_i64(t, &x) && x >= 0) r.key[f] = x;
-      else return fail(BSA_ERR_LUT, "bad rule key '" + t + "'");
-    }
-    r.lo[4] = 0, r.hi[4] = INT64_MAX;
-    for (int f = 0; f < nranges; ++f) {
-      if (!next(t) || !parse_i64(t, &r.lo[f]) || !next(t) || !parse_i64(t, &r.hi[f]))
-        return fail(BSA_ERR_LUT, "bad rule range");
-    }
-    if (!next(t) || t != "->") return fail(BSA_ERR_LUT, "expected '->' in rule");
-    int64_t v[5];
-    for (int f = 0; f < 5; ++f) {
-      if (!next(t)) return fail(BSA_ERR_LUT, "truncated rule");
-      if (f == 2 && t == "local") v[f] = 0;
-      else if (f == 2 && t == "lpt") v[f] = 1;
-      else if (f == 2 && t == "dealt") v[f] = 2;
-      else if (f == 2 || !parse_i64(t, &v[f])) return fail(BSA_ERR_LUT, "bad regime value '" + t + "'");
-    }
-    if ((v[0] != 128 && v[0] != 256) || (v[1] != 64 && v[1] != 128) || v[3] < 0 ||
-        v[3] > (1 << 30) || v[4] < 0 || v[4] > 2)
-      return fail(BSA_ERR_LUT, "regime out of range (Tq 128|256, Tk 64|128, split >= 0, pack 0|1|2)");
-    r.r = Regime{(int)v[0], (int)v[1], (int)v[2], (int)v[3], (int)v[4]};
-    lut->rules.push_back(r);
-  }
-  return BSA_OK;
-}
-
-// ---------------------------------------------------------------------------
 // Problem checks (all before any device work)
 // ---------------------------------------------------------------------------
 // need_mask = false: an ACSR plan, which reads neither a mask nor a page table.
@@ -190,6 +106,7 @@ struct PinnedBuf {
   void *p = nullptr;
   size_t n = 0;
   explicit PinnedBuf(size_t bytes) {
+    if (alloc_fault_injected()) return;
     {
       std::lock_guard<std::mutex> lk(g_pin_mu);
       for (size_t i = 0; i < g_pin_free.size(); ++i)
@@ -212,7 +129,29 @@ struct PinnedBuf {
 };
 }  // namespace
 
+// Allocation-failure injection (BSA_TEST_FAIL_ALLOC=n): the countdown is
+// reset whenever the variable's value changes, and the allocation that brings
+// it to zero fails; later ones succeed until the value changes again.
+bool alloc_fault_injected() {
+  static std::mutex mu;
+  static std::string last;
+  static long countdown = 0;
+  const char *v = std::getenv("BSA_TEST_FAIL_ALLOC");
+  std::lock_guard<std::mutex> lk(mu);
+  const std::string cur = v ? v : "";
+  if (cur != last) {
+    last = cur;
+    countdown = v ? std::strtol(v, nullptr, 10) : 0;
+  }
+  if (countdown <= 0) return false;
+  return --countdown == 0;
+}
+
 hipError_t plan_alloc(void **ptr, size_t bytes, int device, hipStream_t stream) {
+  if (alloc_fault_injected()) {
+    *ptr = nullptr;
+    return hipErrorOutOfMemory;
+  }
   {
     std::lock_guard<std::mutex> lk(g_pool_mu);
     if (std::find(g_pool_ready.begin(), g_pool_ready.end(), device) == g_pool_ready.end()) {
@@ -231,8 +170,28 @@ void plan_release(void *ptr, hipStream_t stream) {
   if (ptr) (void)hipFreeAsync(ptr, stream);
 }
 
+bsa_status note_stream_use(const Plan &p, hipStream_t s) {
+  if (s == p.stream) return BSA_OK;
+  std::lock_guard<std::mutex> lk(p.use_mu);
+  hipEvent_t ev = nullptr;
+  for (auto &u : p.used_on)
+    if (u.first == s) ev = u.second;
+  if (!ev) {
+    HIP_TRY(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    p.used_on.emplace_back(s, ev);
+  }
+  HIP_TRY(hipEventRecord(ev, s));
+  return BSA_OK;
+}
+
 static void free_plan(bsa_plan_s *p) {
   if (!p) return;
+  // Work queued on other streams that reads the plan comes first.
+  for (auto &u : p->used_on) {
+    (void)hipStreamWaitEvent(p->stream, u.second, 0);
+    (void)hipEventDestroy(u.second);
+  }
+  p->used_on.clear();
   plan_release(p->pre, p->stream);
   plan_release(p->arena, p->stream);
   delete p;
@@ -244,17 +203,7 @@ static bsa_status choose_regime(Plan &p, const bsa_lut_s *lut) {
   if (lut) {
     const int64_t key[4] = {p.D, p.dtype, p.uni, p.paged};
     const int64_t val[5] = {p.min_bq, p.min_bk, p.density_pm, p.imb16, p.Sq};
-    for (const Rule &r : lut->rules) {
-      bool ok = true;
-      for (int f = 0; f < 4; ++f)
-        if (r.key[f] >= 0 && r.key[f] != key[f]) ok = false;
-      for (int f = 0; f < 5; ++f)
-        if (val[f] < r.lo[f] || val[f] > r.hi[f]) ok = false;
-      if (ok) {
-        rg = r.r;
-        break;
-      }
-    }
+    (void)lut_match(*lut, key, val, &rg);
   }
   if (!(p.uni && (p.G == 2 || p.G == 4))) rg.pack = 0;
   if (p.dtype == BSA_F32) rg.tq = 128, rg.tk = 64;  // fp32 tiles are 128 x 64
@@ -280,6 +229,15 @@ static bsa_status choose_regime(Plan &p, const bsa_lut_s *lut) {
   return BSA_OK;
 }
 
+FwdScratch fwd_scratch_layout(const Plan &P) {
+  FwdScratch f;
+  f.queue_off = 0;
+  f.part_o_off = aligned(sizeof(int32_t) * kQueuesPerSet);
+  f.part_lse_off = f.part_o_off + aligned(sizeof(float) * (size_t)P.slot_cap * P.rg.tq * P.D);
+  f.bytes = f.part_lse_off + aligned(sizeof(float) * (size_t)P.slot_cap * P.rg.tq);
+  return f;
+}
+
 }  // namespace bsa
 
 using namespace bsa;
@@ -297,6 +255,7 @@ const char *bsa_status_str(bsa_status s) {
     case BSA_ERR_OUT_OF_MEMORY: return "out of memory";
     case BSA_ERR_HIP: return "HIP error";
     case BSA_ERR_LUT: return "lookup table error";
+    case BSA_WARN_LUT_DEFAULT: return "warning: lookup table replaced by the built-in default";
   }
   return "unknown status";
 }
@@ -318,15 +277,36 @@ bsa_status bsa_lut_parse(const char *text, bsa_lut_t *out) {
 bsa_status bsa_lut_load(const char *path, bsa_lut_t *out) {
   if (!out) return fail(BSA_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
-  if (!path) {
-    *out = new bsa_lut_s;
+  // The built-in default: the packaged table compiled into the library.
+  auto builtin = [&]() -> bsa_status {
+    auto *l = new bsa_lut_s;
+    if (bsa_status s = parse_lut(kDefaultLutText, l)) {
+      delete l;
+      return s;
+    }
+    *out = l;
     return BSA_OK;
-  }
+  };
+  if (!path) return builtin();
   std::ifstream f(path);
-  if (!f) return fail(BSA_ERR_LUT, std::string("cannot open lookup table ") + path);
-  std::stringstream ss;
-  ss << f.rdbuf();
-  return bsa_lut_parse(ss.str().c_str(), out);
+  std::string why;
+  if (!f) {
+    why = std::string("cannot open lookup table ") + path;
+  } else {
+    std::stringstream ss;
+    ss << f.rdbuf();
+    auto *l = new bsa_lut_s;
+    if (parse_lut(ss.str().c_str(), l) == BSA_OK) {
+      *out = l;
+      return BSA_OK;
+    }
+    delete l;
+    why = std::string("malformed lookup table ") + path + ": " + g_err;
+  }
+  // Missing or malformed file: the built-in table, with a warning status.
+  if (bsa_status s = builtin()) return s;
+  g_err = why + "; using the built-in default table";
+  return BSA_WARN_LUT_DEFAULT;
 }
 
 void bsa_lut_free(bsa_lut_t lut) { delete lut; }
@@ -351,7 +331,7 @@ static bsa_plan_s *new_plan(const bsa_problem *pr, void *stream) {
   return p;
 }
 
-// Device header of a plan: counters, features, work queues, head metadata,
+// Device header of a plan: counters, features, head metadata,
 // union bits, per-row features and (ACSR plans) the affine descriptors.
 // Returns the descriptors' device address in *acsr_dev when acsr is set.
 static bsa_status alloc_header(Plan &P, bool acsr, bsa_acsr_head **acsr_dev) {
@@ -360,7 +340,6 @@ static bsa_status alloc_header(Plan &P, bool acsr, bsa_acsr_head **acsr_dev) {
   for (int h = 0; h < P.Hq; ++h) rows_per_bm += cdiv(P.Sq, P.bq[h]);
   const size_t acsr_bytes = acsr ? sizeof(bsa_acsr_head) * P.Hq : 0;
   const size_t pre_bytes = aligned(sizeof(int32_t) * CNT_N) + aligned(feat_bytes) +
-                           aligned(sizeof(int32_t) * kQueuesPerSet * kQueueSets) +
                            aligned(sizeof(HeadMeta) * P.Hq) +
                            aligned((size_t)P.nbm * P.Hkv * std::max<int64_t>(P.unkb, 1)) +
                            aligned(sizeof(int32_t) * 2 * std::max<int64_t>(acsr ? 1 : P.nbm * rows_per_bm, 1)) +
@@ -374,8 +353,6 @@ static bsa_status alloc_header(Plan &P, bool acsr, bsa_acsr_head **acsr_dev) {
   pb += aligned(sizeof(int32_t) * CNT_N);
   P.feat_dev = (unsigned long long *)pb;
   pb += aligned(feat_bytes);
-  P.queues = (int32_t *)pb;
-  pb += aligned(sizeof(int32_t) * kQueuesPerSet * kQueueSets);
   P.hmeta = (HeadMeta *)pb;
   pb += aligned(sizeof(HeadMeta) * P.Hq);
   P.uni_bits = pb;
@@ -450,8 +427,6 @@ static bsa_status finish_plan(Plan &P, bsa_lut_t lut, const uint8_t *mask, const
       {(void **)&P.row_ent, sizeof(int32_t) * 2 * std::max<int64_t>(P.nrows, 1)},
       {(void **)&P.items, sizeof(int32_t) * 4 * std::max<int64_t>(P.item_cap, 1)},
       {(void **)&P.comb, sizeof(int32_t) * 3 * std::max<int64_t>(P.comb_cap, 1)},
-      {(void **)&P.part_o, sizeof(float) * P.slot_cap * tq * P.D},
-      {(void **)&P.part_lse, sizeof(float) * P.slot_cap * tq},
   };
   size_t total = 0;
   for (auto &pt : parts) total += aligned(pt.second);
@@ -584,18 +559,35 @@ static bsa_status forward_common(bsa_plan_t plan, const bsa_tensor *q, const bsa
   a.v_sb = v->stride_b, a.v_sh = v->stride_h, a.v_ss = v->stride_s;
   a.o_sb = o->stride_b, a.o_sh = o->stride_h, a.o_ss = o->stride_s;
   a.items = P.items, a.counters = P.counters, a.ent_kt = P.ent_kt, a.ent_page = P.ent_page;
-  a.ent_live = P.ent_live, a.hm = P.hmeta, a.part_o = P.part_o, a.part_lse = P.part_lse;
+  a.ent_live = P.ent_live, a.hm = P.hmeta;
   a.Sq = P.Sq, a.Skv = P.Skv, a.off = P.off, a.nqt = P.nqt;
   a.Hq = P.Hq, a.Hkv = P.Hkv, a.G = P.G, a.tq = P.rg.tq, a.tr = P.tr, a.pack = P.rg.pack;
   // The fp32 kernel lays packed tiles out head after head only (its combine
   // reads the same layout).
   if (P.dtype == BSA_F32 && a.pack) a.pack = 1;
   a.causal = P.causal, a.paged = P.paged, a.P = P.P, a.sched = P.rg.sched;
-  a.queue = P.queues + kQueuesPerSet * (P.qseq.fetch_add(1) % kQueueSets);
   a.scale_log2 = P.scale * 1.4426950408889634f;
   a.kv8 = kv8 ? 1 : 0, a.k_scale = k_scale, a.v_scale = v_scale;
   if (P.nrows == 0) return BSA_OK;
-  return attention_launch(P, a, (hipStream_t)stream);
+  // This call's scratch (work-queue counters, split-KV partials), taken from
+  // the stream-ordered pool on the call's stream and returned after the
+  // combine in stream order: calls on one plan that overlap in time (on any
+  // streams) never share it.
+  const FwdScratch fs = fwd_scratch_layout(P);
+  hipStream_t s = (hipStream_t)stream;
+  void *scratch = nullptr;
+  const hipError_t e = plan_alloc(&scratch, fs.bytes, P.device, s);
+  if (e != hipSuccess)
+    return fail(BSA_ERR_OUT_OF_MEMORY, "forward scratch of " + std::to_string(fs.bytes) +
+                                           " bytes: " + hipGetErrorString(e));
+  uint8_t *sb = (uint8_t *)scratch;
+  a.queue = (int32_t *)(sb + fs.queue_off);
+  a.part_o = fs.part_o_off != fs.part_lse_off ? (float *)(sb + fs.part_o_off) : nullptr;
+  a.part_lse = fs.part_lse_off != fs.bytes ? (float *)(sb + fs.part_lse_off) : nullptr;
+  bsa_status st = attention_launch(P, a, s);
+  plan_release(scratch, s);
+  if (st == BSA_OK) st = note_stream_use(P, s);
+  return st;
 }
 
 bsa_status bsa_backward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k,
@@ -661,6 +653,7 @@ bsa_status bsa_backward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *
   a.t_off = ix.off, a.t_q0 = ix.q0, a.t_meta = ix.meta, a.t_live = ix.live;
   if (st == BSA_OK) st = backward_launch(P, a, s);
   plan_release(scratch, s);
+  if (st == BSA_OK) st = note_stream_use(P, s);
   return st;
 }
 

@@ -34,6 +34,7 @@
 #include "bsa_internal.h"
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 namespace bsa {
@@ -1246,17 +1247,22 @@ bsa_status launch_one(const Plan &p, const AttnArgs &a, hipStream_t s) {
   // deep needs 128 KiB of LDS, one workgroup per CU, and measured slower.
   if constexpr (BF && NS == 2 && D == 128 && TK == 64 && TQ == 128 && KV8)
     if (a.pack == 2) return launch_one<D, TK, BF, TQ, PAGED, KV8, 4>(p, a, s);
-  static int grid = 0;
+  // Persistent grid: CUs x resident workgroups, per device (devices may
+  // differ in CU count).
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> grids[kMaxDev];
   const int threads = BF ? 64 * (TQ / 32) : kThreads;
   auto kern = BF ? (void (*)(AttnArgs))k_attn_bf16<D, TK, TQ, PAGED, KV8, NS> : (void (*)(AttnArgs))k_attn<D, 64, false>;
-  if (grid == 0) {
-    int dev = 0, cus = 0, occ = 0;
-    HIP_TRY(hipGetDevice(&dev));
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  int g = (dev >= 0 && dev < kMaxDev) ? grids[dev].load(std::memory_order_relaxed) : 0;
+  if (g == 0) {
+    int cus = 0, occ = 0;
     HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
     HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, threads, 0));
-    grid = cus * (occ > 0 ? occ : 1);
+    g = cus * (occ > 0 ? occ : 1);
+    if (dev >= 0 && dev < kMaxDev) grids[dev].store(g, std::memory_order_relaxed);
   }
-  int g = grid;
   if (p.item_cap < g) g = (int)std::max<int64_t>(p.item_cap, 1);
   if constexpr (BF) hipLaunchKernelGGL(k_zero_queues, dim3(1), dim3(64), 0, s, a.queue);
   hipLaunchKernelGGL(kern, dim3(g), dim3(threads), 0, s, a);

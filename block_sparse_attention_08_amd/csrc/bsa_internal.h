@@ -6,9 +6,11 @@
 #include <cstdint>
 #include <string>
 #include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "bsa.h"
+#include "bsa_lut.h"
 
 namespace bsa {
 
@@ -24,14 +26,10 @@ struct HeadMeta {
 
 // Counters written on the device by the planner.
 enum { CNT_ENT = 0, CNT_ITEMS = 1, CNT_SLOTS = 2, CNT_COMB = 3, CNT_BADPAGE = 4, CNT_N = 8 };
-// Work-queue counters of the attention kernel: one per XCD (8), in a ring of
-// sets so that forward calls on one plan that overlap in time (up to
-// kQueueSets of them) each count on their own set.
-constexpr int kQueuesPerSet = 8, kQueueSets = 64;
-
-struct Regime {
-  int tq = 128, tk = 64, sched = 0, split = 0, pack = 1;
-};
+// Work-queue counters of the attention kernel: one per XCD (8). Each forward
+// call has its own set, in the call's scratch (with its split-KV partials),
+// so calls that overlap in time never share counters or partials.
+constexpr int kQueuesPerSet = 8;
 
 // Host-side plan object. All device arrays live in two allocations.
 struct Plan {
@@ -60,17 +58,21 @@ struct Plan {
   unsigned long long *feat_dev;
   int32_t *row_feat;  // per logical row: selected blocks, effective blocks
   int32_t *counters;
-  int32_t *queues;                           // kQueueSets x kQueuesPerSet
-  mutable std::atomic<uint32_t> qseq{0};     // next queue set
   uint8_t *uni_bits;
   const bsa_acsr_head *acsr = nullptr;  // device copy of the affine row descriptors (ACSR plans)
   int32_t *list_off, *ent_kt, *ent_page;
   uint32_t *ent_live;
   int32_t *row_ent, *items, *comb;
-  float *part_o, *part_lse;
   hipStream_t stream;
   int device;
+  // Streams other than the plan's that forward or backward calls used, each
+  // with an event recorded after the call's last kernel: bsa_plan_free makes
+  // the plan's stream wait for them before the memory is returned.
+  mutable std::mutex use_mu;
+  mutable std::vector<std::pair<hipStream_t, hipEvent_t>> used_on;
 };
+// Records that a call on stream s used the plan (no-op on the plan's stream).
+bsa_status note_stream_use(const Plan &p, hipStream_t s);
 
 struct AttnArgs {
   const void *q, *k, *v;
@@ -107,13 +109,21 @@ struct BwdArgs {
   float scale, scale_log2;
 };
 
-// Error reporting (thread-local message).
-bsa_status fail(bsa_status s, const std::string &msg);
-
-// Device allocations of plans: stream-ordered (the device's default pool), on
-// the plan's stream, so repeated requests reuse freed blocks without waiting.
+// Device allocations of plans and per-call scratch: stream-ordered (the
+// device's default pool), on the stream that uses them, so repeated requests
+// reuse freed blocks without waiting. With BSA_TEST_FAIL_ALLOC=n set, the
+// n-th allocation (device or pinned host) counted from when the variable
+// took that value fails, for tests of the out-of-memory paths.
 hipError_t plan_alloc(void **ptr, size_t bytes, int device, hipStream_t stream);
 void plan_release(void *ptr, hipStream_t stream);
+bool alloc_fault_injected();
+
+// Per-call scratch of a forward call: one set of work-queue counters, then
+// the split-KV partial O (fp32 [slot][Tq][D]) and LSE (fp32 [slot][Tq]).
+struct FwdScratch {
+  size_t queue_off, part_o_off, part_lse_off, bytes;
+};
+FwdScratch fwd_scratch_layout(const Plan &p);
 
 // Planner entry points (bsa_planner.hip). Each returns BSA_OK or BSA_ERR_HIP.
 bsa_status plan_features(Plan &p, const uint8_t *mask, const int32_t *page_table);

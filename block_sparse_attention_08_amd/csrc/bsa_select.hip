@@ -264,7 +264,9 @@ bsa_status select_blocks(const bsa_problem &pr, int keep_tenths, int top_k, cons
   const size_t qm_bytes = sizeof(float) * (size_t)B * qrows * pr.head_dim;
   const size_t km_bytes = sizeof(float) * (size_t)B * std::max(krows, 1) * pr.head_dim;
   void *scratch = nullptr;
-  if (hipMallocAsync(&scratch, ((qm_bytes + 255) & ~size_t(255)) + km_bytes, s) != hipSuccess)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(BSA_ERR_HIP, "hipGetDevice failed");
+  if (plan_alloc(&scratch, ((qm_bytes + 255) & ~size_t(255)) + km_bytes, dev, s) != hipSuccess)
     return fail(BSA_ERR_OUT_OF_MEMORY, "device allocation of block-selection scratch failed");
   SelArgs a{};
   a.q = q.data, a.k = k.data, a.page_table = page_table;
@@ -292,7 +294,7 @@ bsa_status select_blocks(const bsa_problem &pr, int keep_tenths, int top_k, cons
     hipLaunchKernelGGL(k_select, dim3((unsigned)qrows, (unsigned)B), dim3(kSelThreads), lds, s, a, hs);
     e = hipGetLastError();
   }
-  (void)hipFreeAsync(scratch, s);
+  plan_release(scratch, s);
   if (e != hipSuccess) return fail(BSA_ERR_HIP, std::string("block selection launch failed: ") + hipGetErrorString(e));
   return BSA_OK;
 }

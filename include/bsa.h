@@ -58,7 +58,10 @@ typedef enum {
   BSA_ERR_SHAPE_MISMATCH = 3, /* tensors or dtype disagree with the plan */
   BSA_ERR_OUT_OF_MEMORY = 4,  /* a device or host allocation failed */
   BSA_ERR_HIP = 5,            /* a HIP runtime call failed (message names it) */
-  BSA_ERR_LUT = 6             /* lookup table file missing or malformed */
+  BSA_ERR_LUT = 6,            /* lookup table text malformed */
+  BSA_WARN_LUT_DEFAULT = 7    /* not a failure: bsa_lut_load could not use the file it
+                                 was given (missing or malformed) and returned the
+                                 built-in default table instead (message says why) */
 } bsa_status;
 
 typedef enum { BSA_BF16 = 0, BSA_F32 = 1 } bsa_dtype;
@@ -145,9 +148,14 @@ const char *bsa_last_error(void);
  * imbalance x16 of the mask (and seqlen_q); sched is local|lpt|dealt; the first
  * matching rule wins; with no match the built-in default applies
  * (128, 64, local, 0, 1).
- * bsa_lut_load reads a file (path NULL: the built-in default with no rules);
- * bsa_lut_parse reads text. The table is host memory owned by the library,
- * immutable, and may be shared by threads; free it with bsa_lut_free. */
+ * bsa_lut_load reads a file. path NULL gives the built-in default table (the
+ * packaged gfx950 table, compiled into the library). A file that cannot be
+ * opened or does not parse also gives the built-in table, with status
+ * BSA_WARN_LUT_DEFAULT (not an error: *out is set and must be freed; the
+ * reason is in bsa_last_error). bsa_lut_parse reads text and returns
+ * BSA_ERR_LUT on malformed text (no fallback). The table is host memory owned
+ * by the library, immutable, and may be shared by threads; free it with
+ * bsa_lut_free. */
 bsa_status bsa_lut_load(const char *path, bsa_lut_t *out);
 bsa_status bsa_lut_parse(const char *text, bsa_lut_t *out);
 void bsa_lut_free(bsa_lut_t lut);
@@ -168,10 +176,12 @@ void bsa_lut_free(bsa_lut_t lut);
  * ready for any work queued on the same stream afterwards (work on another
  * stream must first wait for an event recorded on this one). The plan owns its
  * device memory and can be used by any number of bsa_forward calls with
- * matching tensors; its tile lists are immutable, and each forward call takes
- * its own set of work-queue counters from a ring of 64 held by the plan, so
- * up to 64 calls on one plan may be in flight at once (on any streams). Free
- * it with bsa_plan_free. */
+ * matching tensors; its tile lists are immutable and are only read by those
+ * calls. Everything a forward call writes besides O and LSE (work-queue
+ * counters, split-KV partial results) lives in scratch that the call takes
+ * from the device's stream-ordered pool on its own stream and returns there,
+ * so any number of calls on one plan may be in flight at once, on any
+ * streams, with any inputs. Free it with bsa_plan_free. */
 bsa_status bsa_plan(const bsa_problem *problem, const uint8_t *mask, const int32_t *page_table,
                     bsa_lut_t lut, void *stream, bsa_plan_t *out);
 
@@ -182,7 +192,11 @@ bsa_status bsa_plan(const bsa_problem *problem, const uint8_t *mask, const int32
  * O need not be cleared. Queued on stream; never synchronises. O and LSE must
  * not overlap Q, K or V. Work items are taken from per-XCD queues in the
  * order the plan's schedule gives, so which workgroup computes a row varies
- * from call to call; the values written do not. */
+ * from call to call; the values written do not. Scratch: one set of queue
+ * counters plus, when the plan splits rows, partial O and LSE of
+ * partial_slots capacity (fp32, Tq x (D + 1) per slot), from the device's
+ * stream-ordered pool on this stream, returned in stream order after the
+ * combine; BSA_ERR_OUT_OF_MEMORY if the pool cannot provide it. */
 bsa_status bsa_forward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k,
                        const bsa_tensor *v, bsa_tensor *o, float *lse, void *stream);
 
@@ -320,8 +334,10 @@ bsa_status bsa_acsr_features(const bsa_problem *problem, const bsa_acsr_head *he
 
 /* Release a plan. Its device memory is returned in stream order on the plan's
  * stream, so the call may follow the last bsa_forward queued on that stream
- * directly; forward calls queued on other streams must have completed (or be
- * ordered before the plan's stream by an event). NULL is ignored. */
+ * directly. Forward and backward calls queued on other streams record an
+ * event there after their kernels, and the release first makes the plan's
+ * stream wait for those events, so it may also follow them directly (the
+ * streams may be destroyed in between). NULL is ignored. */
 void bsa_plan_free(bsa_plan_t plan);
 
 #ifdef __cplusplus

@@ -64,8 +64,10 @@ def compare(w, o_gpu, lse_gpu, o_ref, lse_ref, rows):
                 rows=len(rows), empty_rows=int((~nonempty).sum()))
 
 
-def run_case(ref, w, lut_text=None, rows=None, device_gen=False, check_plan=True, label=""):
-    """Plan + forward on the GPU, plan image and sampled O/LSE vs the oracle."""
+def run_gpu(ref, w, lut_text=None, device_gen=False, check_plan=True, label=""):
+    """Plan + forward on the GPU into NaN-filled outputs; the plan image is
+    compared with the reference planner's and the whole output is checked to
+    be written. Returns (q, k, v, o, lse, stats) as GPU tensors."""
     import torch
     say(f"[case] {label or w.name}: B={w.batch} Hq={w.hq} Hkv={w.hkv} Sq={w.sq} Skv={w.skv} "
         f"D={w.d} {w.dtype} union={int(w.gqa_union)} paged={int(w.paged)} causal={int(w.causal)}")
@@ -73,33 +75,69 @@ def run_case(ref, w, lut_text=None, rows=None, device_gen=False, check_plan=True
     lut = bsa.Lut.parse(lut_text) if lut_text else bsa.Lut.load(bsa.DEFAULT_LUT)
     text = lut_text if lut_text else open(bsa.DEFAULT_LUT).read()
     plan = bsa.plan(w.problem_dict(), mask, table, lut)
-    res = {}
     if check_plan:
         img = plan.export()
         ref_img = ref.plan(w, lut_text=text)
         assert img == ref_img, "plan differs from the reference planner: " + plan_diff(img, ref_img)
-        res["plan_bytes"] = len(img)
-    o, lse = plan.forward(q, k, v)
+    # Outputs start as NaN: a row the forward leaves unwritten cannot pass.
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((w.batch, w.hq, w.sq), float("nan"), dtype=torch.float32, device=q.device)
+    plan.forward(q, k, v, o, lse)
     torch.cuda.synchronize()
-    if rows is None:
-        B, H, S = w.batch, w.hq, w.sq
-        rows = np.stack(np.meshgrid(np.arange(B), np.arange(H), np.arange(S), indexing="ij"),
-                        -1).reshape(-1, 3)
+    check_written(o, lse, label or w.name)
+    stats = plan.stats()
+    plan.free()
+    return q, k, v, o, lse, stats
+
+
+def compare_rows(ref, w, qkv_host, o, lse, rows, label=""):
+    """O/LSE at rows (b, h, i) against the oracle, within the tolerances."""
+    import torch
     rows = np.asarray(rows, np.int64).reshape(-1, 3)
-    qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
+    qh, kh, vh = qkv_host
     o_ref, lse_ref = ref.forward(w, qh, kh, vh, mode=1, rows=rows)
-    ridx = [torch.from_numpy(rows[:, i]).cuda() for i in range(3)]
+    ridx = [torch.from_numpy(rows[:, i]).to(o.device) for i in range(3)]
     o_g = o[ridx[0], ridx[1], ridx[2]].float().cpu().numpy().astype(np.float64)
     l_g = lse[ridx[0], ridx[1], ridx[2]].cpu().numpy().astype(np.float64)
-    res.update(compare(w, o_g, l_g, o_ref, lse_ref, rows))
-    res["stats"] = plan.stats()
+    res = compare(w, o_g, l_g, o_ref, lse_ref, rows)
     say(f"[result] {label or w.name}: max|dO|={res['max_o']:.3e} mean|dO|={res['mean_o']:.3e} "
         f"max|dLSE|={res['max_lse']:.3e} rows={res['rows']} empty={res['empty_rows']}")
     assert res["empty_ok"], "empty rows must be exactly O=0, LSE=-inf"
     assert res["max_o"] <= O_MAX and res["mean_o"] <= O_MEAN and res["max_lse"] <= LSE_MAX, res
-    plan.free()
+    return res
+
+
+def run_case(ref, w, lut_text=None, rows=None, device_gen=False, check_plan=True, label=""):
+    """Plan + forward on the GPU; plan image, whole-output checks, and O/LSE
+    at rows (default: every row) against the oracle."""
+    q, k, v, o, lse, stats = run_gpu(ref, w, lut_text, device_gen, check_plan, label)
+    if rows is None:
+        rows = all_rows(w)
+    res = compare_rows(ref, w, (q.cpu(), k.cpu(), v.cpu()), o, lse, rows, label)
+    res["stats"] = stats
     del q, k, v, o, lse
     return res
+
+
+def check_written(o, lse, label=""):
+    """Every output row was written: no NaN anywhere; a row with LSE = -inf
+    is exactly zero, every other row is finite (checked on the GPU over the
+    whole output, at no oracle cost)."""
+    import torch
+    assert not torch.isnan(lse).any().item(), f"{label}: LSE entries left unwritten"
+    empty = torch.isneginf(lse)
+    assert torch.isfinite(lse[~empty]).all().item(), f"{label}: LSE +inf"
+    of = o.float()
+    assert not torch.isnan(of).any().item(), f"{label}: O rows left unwritten"
+    assert (of[empty] == 0).all().item(), f"{label}: rows without keys must be zero"
+    assert torch.isfinite(of).all().item(), f"{label}: O not finite"
+
+
+def all_rows(w, heads=None):
+    """(b, h, i) of every query row, optionally of some heads only."""
+    hs = np.arange(w.hq) if heads is None else np.asarray(list(heads))
+    return np.stack(np.meshgrid(np.arange(w.batch), hs, np.arange(w.sq), indexing="ij"),
+                    -1).reshape(-1, 3)
 
 
 def sample_rows(w, n=256, seed=0, extra=()):

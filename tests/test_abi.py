@@ -35,6 +35,7 @@ def test_exports_every_declared_symbol(L):
 def test_version_and_status_strings(L):
     assert L.bsa_abi_version() == 1
     assert L.bsa_status_str(0) == b"ok" and L.bsa_status_str(6) == b"lookup table error"
+    assert L.bsa_status_str(4) == b"out of memory"
 
 
 BASE = dict(batch=1, num_q_heads=4, num_kv_heads=2, seqlen_q=256, seqlen_kv=256, head_dim=128,
@@ -112,13 +113,32 @@ def test_lut_schedules(L):
         assert bsa.Lut.parse(f"bsa-lut 1\nrule * * * * 0 1 0 1 0 1 0 1 -> 128 64 {sched} 0 0").handle.value
 
 
-def test_lut_files(L):
+def test_lut_files(L, tmp_path):
     lut = bsa.Lut.load(bsa.DEFAULT_LUT)
     assert lut.handle.value
-    assert bsa.Lut.load(None).handle.value
-    with pytest.raises(bsa.BsaError) as e:
-        bsa.Lut.load("/nonexistent/table.lut")
-    assert e.value.status == 6
+    assert bsa.Lut.load(None).handle.value  # the built-in table
+    # A missing or malformed file gives the built-in table with a warning
+    # status (BSA_WARN_LUT_DEFAULT), not an error.
+    bad = tmp_path / "bad.lut"
+    bad.write_text("bsa-lut 1\nrule * * * * 0 1 0 1 0 1 0 1 -> 128 96 local 0 0\n")
+    for path, needle in (("/nonexistent/table.lut", "cannot open"), (str(bad), "malformed")):
+        out = ctypes.c_void_p()
+        st = L.bsa_lut_load(path.encode(), ctypes.byref(out))
+        msg = L.bsa_last_error().decode()
+        assert st == bsa.BSA_WARN_LUT_DEFAULT and out.value, (st, msg)
+        assert needle in msg and "built-in default" in msg, msg
+        L.bsa_lut_free(out)
+        with pytest.warns(RuntimeWarning, match="built-in default"):
+            assert bsa.Lut.load(path).handle.value
+    assert L.bsa_status_str(7).startswith(b"warning")
+
+
+def test_builtin_lut_is_the_packaged_table():
+    """The table compiled into the library is the packaged text, byte for
+    byte (build.py regenerates the include from lut/gfx950.lut)."""
+    from block_sparse_attention_08_amd import build
+    inc = open(build.LUT_INC).read()
+    assert inc == build.lut_include_text(open(bsa.DEFAULT_LUT).read())
 
 
 def test_default_lut_accepted_by_oracle(ref):

@@ -1,10 +1,12 @@
 """GPU tests of the runtime around the kernels: repeated and concurrent
-forward calls on one plan (each call takes its own set of work-queue
-counters from the plan's ring of 64), plans freed right after their forward
-and rebuilt on the same stream (stream-ordered plan memory), and forward
-calls on a stream other than the plan's. Outputs are compared with the
-oracle on every row, and across calls bit for bit (the kernels are
-deterministic: which workgroup computes a row never changes its value)."""
+forward calls on one plan (each call takes its own work-queue counters and
+split-KV partials from the stream-ordered pool), plans freed right after
+their forward and rebuilt on the same stream (stream-ordered plan memory),
+forward calls on a stream other than the plan's, plans freed right after
+calls on other streams, and the out-of-memory paths (allocation failures
+injected with BSA_TEST_FAIL_ALLOC). Outputs are compared with the oracle on
+every row, and across calls bit for bit (the kernels are deterministic:
+which workgroup computes a row never changes its value)."""
 import numpy as np
 import pytest
 
@@ -49,9 +51,9 @@ CASES = {
 
 
 @pytest.mark.parametrize("case", list(CASES))
-def test_repeated_forward_wraps_queue_ring(ref, case):
-    """70 forward calls on one plan (more than the ring's 64 counter sets):
-    every call writes the same bytes, and they match the oracle."""
+def test_repeated_forward(ref, case):
+    """70 forward calls on one plan: every call writes the same bytes, and
+    they match the oracle."""
     import torch
     make, lut_text = CASES[case]
     w = make()
@@ -136,4 +138,183 @@ def test_forward_on_another_stream(ref):
     plan.forward(q, k, v, o, lse, stream=fs)
     fs.synchronize()
     _check_all_rows(ref, w, q, k, v, o, lse, "other-stream")
+    plan.free()
+
+
+SPLIT_CASES = {
+    # forced split at 3 key tiles: almost every row becomes several items
+    "split3": (lambda seed: W.random_problem(batch=1, hq=3, sq=520, skv=1500, d=128, bq=64, bk=64,
+                                             density=0.5, empty_rows=0.05, seed=seed),
+               forced_lut_text(128, 64, "local", 3, 0)),
+    # the packaged table's video bucket (128-blocks, density <= 40%): split at
+    # 128 key tiles, which rows of ~140 tiles exceed
+    "packaged_split128": (lambda seed: W.random_problem(batch=1, hq=2, sq=512, skv=24000, d=128,
+                                                        bq=128, bk=128, density=0.38, seed=seed),
+                          None),
+}
+
+
+@pytest.mark.parametrize("case", list(SPLIT_CASES))
+def test_concurrent_forwards_different_inputs(ref, case):
+    """Forward calls on one plan in flight on two streams at once, each with
+    its own Q/K/V, under split-KV regimes: every output matches the oracle on
+    every row (calls must not share partial results or queue counters)."""
+    import torch
+    make, lut_text = SPLIT_CASES[case]
+    w = make(50)
+    say(f"[case] concurrent forwards, different inputs, {case}")
+    _, _, _, mask, table = to_device(w)
+    lut = bsa.Lut.parse(lut_text) if lut_text else bsa.Lut.load(bsa.DEFAULT_LUT)
+    plan = bsa.plan(w.problem_dict(), mask, table, lut)
+    st = plan.stats()
+    assert st["partial_slots"] > 0, st
+    inputs = []
+    for i in range(4):
+        g = torch.Generator().manual_seed(1000 + i)
+        q, k, v = (torch.randn(t.shape, generator=g).to(t.dtype) for t in w.make_qkv())
+        inputs.append((q, k, v, q.cuda(), k.cuda(), v.cuda()))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for rep in range(3):
+        for i, (_, _, _, qd, kd, vd) in enumerate(inputs):
+            s = (s1, s2)[i % 2]
+            o = torch.full_like(qd, float("nan"))
+            lse = torch.full((w.batch, w.hq, w.sq), float("nan"), dtype=torch.float32, device="cuda")
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                plan.forward(qd, kd, vd, o, lse, stream=s)
+            outs.append((i, o, lse))
+    torch.cuda.synchronize()
+    first = {}
+    for i, o, lse in outs:
+        if i in first:
+            assert torch.equal(o, first[i][0]) and torch.equal(lse, first[i][1]), f"input {i} differs"
+        else:
+            first[i] = (o, lse)
+            q, k, v = inputs[i][:3]
+            _check_all_rows(ref, w, q, k, v, o, lse, f"{case}/input {i}")
+    plan.free()
+
+
+def test_many_calls_in_flight(ref):
+    """More than 64 forward calls on one plan queued on four streams without
+    waiting (no limit on calls in flight), two inputs alternating: each output
+    equals the checked single-call result bit for bit."""
+    import torch
+    make, lut_text = SPLIT_CASES["split3"]
+    w = make(60)
+    say("[case] 96 calls in flight")
+    q0, k0, v0, mask, table = to_device(w)
+    plan = bsa.plan(w.problem_dict(), mask, table, bsa.Lut.parse(lut_text))
+    g = torch.Generator().manual_seed(77)
+    q1, k1, v1 = (torch.randn(t.shape, generator=g).to(t.dtype).cuda() for t in (q0, k0, v0))
+    ins = [(q0, k0, v0), (q1, k1, v1)]
+    refs = []
+    for q, k, v in ins:
+        o, lse = plan.forward(q, k, v)
+        torch.cuda.synchronize()
+        _check_all_rows(ref, w, q, k, v, o, lse, "in-flight/reference")
+        refs.append((o, lse))
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for i in range(96):
+        s = streams[i % 4]
+        q, k, v = ins[i % 2]
+        o = torch.empty_like(q)
+        lse = torch.empty((w.batch, w.hq, w.sq), dtype=torch.float32, device="cuda")
+        with torch.cuda.stream(s):
+            plan.forward(q, k, v, o, lse, stream=s)
+        outs.append((i % 2, o, lse))
+    torch.cuda.synchronize()
+    for n, (j, o, lse) in enumerate(outs):
+        assert torch.equal(o, refs[j][0]) and torch.equal(lse, refs[j][1]), f"call {n} differs"
+    plan.free()
+
+
+def test_plan_freed_after_calls_on_other_streams(ref):
+    """A plan freed right after forward calls queued on other streams (which
+    are then dropped): the release waits for them, so a new plan built on
+    the old plan's stream cannot overwrite lists those calls still read."""
+    import torch
+    make, lut_text = SPLIT_CASES["split3"]
+    w = make(70)
+    say("[case] plan freed after calls on other streams")
+    q, k, v, mask, table = to_device(w)
+    ps = torch.cuda.Stream()
+    ps.wait_stream(torch.cuda.current_stream())
+    plan = bsa.plan(w.problem_dict(), mask, table, bsa.Lut.parse(lut_text), stream=ps)
+    ready = torch.cuda.Event()
+    ready.record(ps)
+    outs = []
+    for _ in range(3):
+        s = torch.cuda.Stream()
+        s.wait_event(ready)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.batch, w.hq, w.sq), dtype=torch.float32, device="cuda")
+        plan.forward(q, k, v, o, lse, stream=s)
+        outs.append((o, lse))
+        del s
+    plan.free()
+    # a second plan on the same stream, from another mask, reuses the memory
+    w2 = make(71)
+    _, _, _, mask2, _ = to_device(w2)
+    plan2 = bsa.plan(w2.problem_dict(), mask2, None, bsa.Lut.parse(lut_text), stream=ps)
+    torch.cuda.synchronize()
+    for o, lse in outs:
+        _check_all_rows(ref, w, q, k, v, o, lse, "freed-after-other-streams")
+    plan2.free()
+
+
+def _status_of(fn):
+    try:
+        fn()
+    except bsa.BsaError as e:
+        return e.status, str(e)
+    return 0, ""
+
+
+def test_out_of_memory_paths(ref, monkeypatch):
+    """Every device and pinned-host allocation of plan, forward, backward and
+    block selection fails in turn (BSA_TEST_FAIL_ALLOC=n); each call returns
+    BSA_ERR_OUT_OF_MEMORY with nothing launched or leaked, and the same calls
+    succeed again once the variable is cleared."""
+    import torch
+    w = W.random_problem(batch=1, hq=2, sq=300, skv=520, d=128, bq=64, bk=64, density=0.4, seed=80)
+    q, k, v, mask, table = to_device(w)
+    lut = bsa.Lut.parse(forced_lut_text(128, 64, "local", 3, 0))
+    # bsa_plan: header (1), pinned read-back buffer (2), arena (3)
+    for n in (1, 2, 3):
+        monkeypatch.setenv("BSA_TEST_FAIL_ALLOC", str(n))
+        st, msg = _status_of(lambda: bsa.plan(w.problem_dict(), mask, table, lut))
+        say(f"[oom] plan alloc {n}: {st} {msg}")
+        assert st == 4, (n, st, msg)
+        monkeypatch.delenv("BSA_TEST_FAIL_ALLOC")
+    plan = bsa.plan(w.problem_dict(), mask, table, lut)
+    o, lse = plan.forward(q, k, v)
+    torch.cuda.synchronize()
+    _check_all_rows(ref, w, q, k, v, o, lse, "oom/after plan failures")
+    # bsa_forward: the call's scratch
+    monkeypatch.setenv("BSA_TEST_FAIL_ALLOC", "1")
+    st, msg = _status_of(lambda: plan.forward(q, k, v))
+    assert st == 4 and "scratch" in msg, (st, msg)
+    monkeypatch.delenv("BSA_TEST_FAIL_ALLOC")
+    # bsa_backward: its scratch
+    dout = torch.randn_like(q.float()).to(q.dtype)
+    monkeypatch.setenv("BSA_TEST_FAIL_ALLOC", "1")
+    st, msg = _status_of(lambda: plan.backward(q, k, v, o, lse, dout))
+    assert st == 4 and "scratch" in msg, (st, msg)
+    monkeypatch.delenv("BSA_TEST_FAIL_ALLOC")
+    # bsa_select_blocks: its scratch
+    monkeypatch.setenv("BSA_TEST_FAIL_ALLOC", "1")
+    st, msg = _status_of(lambda: bsa.select_blocks(w.problem_dict(), q, k, keep_tenths=3))
+    assert st == 4 and "selection" in msg, (st, msg)
+    monkeypatch.delenv("BSA_TEST_FAIL_ALLOC")
+    # everything works again
+    o2, lse2 = plan.forward(q, k, v)
+    dq, dk, dv = plan.backward(q, k, v, o2, lse2, dout)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    assert torch.isfinite(dq.float()).all() and torch.isfinite(dk.float()).all()
     plan.free()
