@@ -6,6 +6,14 @@ attention kernel and, when rows are split, the combine kernel) on one batch of
 seeded synthetic inputs already resident in HBM. The metric counts only the
 logical blocks the mask selects: 4 * bq * bk * D FLOPs per selected block.
 
+The headline workload is the long-video mixed-geometry configuration (the
+largest one that fits one GPU). The same JSON line carries a ``configs`` list
+with the forward time, effective TFLOP/s, fraction of the bf16 MFMA peak,
+fraction of HBM bandwidth over the streamed K/V bytes, and merge waste of
+every benchmark configuration (video-DiT, chunked prefill, the affine
+patterns at both block sizes and two wider windows, long video), each timed
+in this run.
+
 Plan and forward of a request run back to back on one stream. With
 ``--pipeline`` the line also reports requests pipelined as a serving runtime
 could run them (the plan of request i+1 built on a second stream while the
@@ -148,6 +156,84 @@ def effective_flops(w) -> float:
     return 4.0 * w.d * tot
 
 
+def streamed_bytes(w, tile: int = 128) -> float:
+    """K and V bytes streamed with no reuse beyond a 128-row query tile: for
+    every (batch, head) -- or (batch, kv group) in union mode, whose heads
+    share one table -- and every 128-row query tile, 4 * bk * D bytes (bf16 K
+    and V rows) per distinct key block that some query block overlapping the
+    tile selects and that the causal bound leaves reachable; plus Q, O and
+    LSE once. The no-reuse HBM traffic of the forward."""
+    esz = 2 if w.dtype == "bf16" else 4
+    tot = 0.0
+    for bm in range(w.mask_batches):
+        nb = w.batch if w.mask_broadcast else 1
+        gs = w.hq // w.hkv
+        for h in range(w.hq):
+            if w.gqa_union and h % gs:
+                continue  # the group's first head stands for the group
+            if w.gqa_union:
+                u = np.zeros(w.nkb(h), bool)
+                for h2 in range(h, h + gs):
+                    u |= w.head_mask(bm, h2).astype(bool).any(0)
+                blk = np.broadcast_to(u, (w.nqb(h), w.nkb(h)))
+            else:
+                blk = w.head_mask(bm, h).astype(bool)
+            bq, bk = w.bq[h], w.bk[h]
+            nt = -(-w.sq // tile)
+            if bq >= tile:
+                tb = blk[np.arange(nt) * tile // bq]
+            else:
+                per = tile // bq
+                pad = nt * per - blk.shape[0]
+                tb = np.concatenate([blk, np.zeros((pad, blk.shape[1]), bool)]).reshape(nt, per, -1).any(1)
+            k0 = np.arange(w.nkb(h)) * bk
+            if w.causal:
+                last_q = np.minimum((np.arange(nt) + 1) * tile, w.sq) - 1
+                tb = tb & (k0[None, :] <= (last_q + w.causal_offset)[:, None])
+            rk = np.minimum(bk, w.skv - k0).astype(np.float64)
+            tot += nb * float(tb.astype(np.float64).sum(0) @ rk) * 2 * w.d * esz
+    return tot + esz * 2 * w.batch * w.hq * w.sq * w.d + 4 * w.batch * w.hq * w.sq
+
+
+def pre_union_flops(w) -> float:
+    """4 * bq * bk * D per block a head selects itself (before the union),
+    causally feasible: the selected work of a union problem before the
+    query-block and group unions widen it."""
+    tot = 0.0
+    for bm in range(w.mask_batches):
+        nb = w.batch if w.mask_broadcast else 1
+        for h in range(w.hq):
+            blk = w.head_mask(bm, h).astype(bool).copy()
+            bq, bk = w.bq[h], w.bk[h]
+            if w.causal:
+                last_q = np.minimum(np.arange(w.nqb(h)) * bq + bq, w.sq) - 1
+                blk &= (np.arange(w.nkb(h)) * bk)[None, :] <= (last_q + w.causal_offset)[:, None]
+            tot += nb * float(blk.sum()) * bq * bk
+    return 4.0 * w.d * tot
+
+
+# Benchmark configurations reported in the ``configs`` list (forward only).
+CONFIGS = ["video_dit", "chunked_prefill", "affine_bs32", "affine_bs64", "affine_bs64_w4096",
+           "affine_bs64_w8192", "long_video"]
+
+
+def forward_rates(w, eff_flops: float, fwd_ms: float, stats: dict) -> dict:
+    """Forward rates of one workload against both rooflines."""
+    sb = streamed_bytes(w)
+    t_mfma = eff_flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = sb / (PEAK_HBM_GBS * 1e9)
+    tflops = eff_flops / (fwd_ms * 1e-3) / 1e12
+    gbs = sb / (fwd_ms * 1e-3) / 1e9
+    eff_area = eff_flops / (4.0 * w.d)
+    return {"forward_ms": round(fwd_ms, 4), "tflops": round(tflops, 3),
+            "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "streamed_bytes": int(sb), "streamed_gbs": round(gbs, 1),
+            "hbm_frac_streamed": round(gbs / PEAK_HBM_GBS, 4),
+            "bound": "hbm" if t_hbm > t_mfma else "mfma",
+            "area_ratio": round(stats["executed_tiles"] * stats["tile_q"] * stats["tile_k"] / eff_area, 4)
+            if eff_area else None}
+
+
 def cpu_baseline(w, q, k, v, target_s: float = 20.0, kv8=None):
     """The fp64 oracle timed on this host's cores over a bounded sample of
     query rows (whole 128-row tiles, spread over heads), in TFLOP/s of
@@ -207,7 +293,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="video_dit")
+    ap.add_argument("--workload", default="long_video")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration forward table")
+    ap.add_argument("--regret", action=argparse.BooleanOptionalAction, default=True,
+                    help="in the configuration table, also time every candidate regime and "
+                         "report the table's regret against the best")
     ap.add_argument("--lut", default=None, help="regime table (default: the packaged gfx950 table)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pipeline", action="store_true",
@@ -388,9 +479,22 @@ def main():
     esz = 2 if w.dtype == "bf16" else 4
     compulsory = esz * (q.numel() * 2 + k.numel() + v.numel()) + 4 * lse.numel()
     traffic = measured_traffic(args.workload, None)
-    roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic, "kernel": "k_attn", "compulsory_bytes": compulsory}
+    rates = forward_rates(w, eff_flops, fwd_avg, stats)
+    if rates["bound"] == "hbm":
+        # Gather-bound: the no-reuse K/V stream at 8 TB/s takes longer than the
+        # selected work at the MFMA peak, so the roofline is HBM bytes.
+        roofline = {"bound": "hbm", "achieved": rates["streamed_gbs"], "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": rates["hbm_frac_streamed"], "traffic": traffic,
+                    "kernel": "k_attn", "algorithmic_bytes": rates["streamed_bytes"],
+                    "algorithmic_bytes_def": "K+V rows streamed per 128-row query tile (no reuse "
+                                             "beyond the tile) + Q, O, LSE once",
+                    "mfma_frac": rates["mfma_frac"], "compulsory_bytes": compulsory}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": traffic, "kernel": "k_attn", "compulsory_bytes": compulsory,
+                    "hbm_frac_streamed": rates["hbm_frac_streamed"]}
+    roofline["area_ratio"] = rates["area_ratio"]
     if args.workload in HBM_BOUND:
         # Union tables: every head of a group selects the same blocks, so the
         # group reads effective_blocks / G blocks of K and of V once.
@@ -436,8 +540,88 @@ def main():
         line["backward"] = backward
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, q, k, v, kv8=kv8)
+    if not args.no_configs:
+        del q, k, v, o, lse, mask, table
+        torch.cuda.empty_cache()
+        line["configs"] = config_table(bsa, lut, args)
     print(json.dumps(line), flush=True)
 
+
+def config_table(bsa, lut, args):
+    """Forward time and rates of every benchmark configuration, measured
+    here with HIP events on the launch stream; with regret, also every forced
+    regime of a candidate set, and the table's regret against the best."""
+    import torch
+    out = []
+    stream = torch.cuda.current_stream()
+
+    def time_fwd(p, q, k, v, o, lse, reps):
+        for _ in range(max(args.warmup, 1)):
+            p.forward(q, k, v, o, lse, stream=stream)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            p.forward(q, k, v, o, lse, stream=stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    for name in CONFIGS:
+        w = workload(name)
+        q, k, v = w.make_qkv(device="cuda")
+        mask = torch.from_numpy(np.ascontiguousarray(w.mask)).cuda()
+        table = torch.from_numpy(np.ascontiguousarray(w.page_table)).cuda() if w.paged else None
+        o = torch.empty_like(q)
+        lse = torch.empty((w.batch, w.hq, w.sq), dtype=torch.float32, device="cuda")
+        p = bsa.plan(w.problem_dict(), mask, table, lut, stream=stream)
+        stats = p.stats()
+        fwd_ms = time_fwd(p, q, k, v, o, lse, args.steps)
+        p.free()
+        eff = effective_flops(w)
+        rec = {"workload": name, "density_pm": stats["density_pm"], "effective_flops": eff}
+        rec.update(forward_rates(w, eff, fwd_ms, stats))
+        rec["regime"] = {k2: stats[k2] for k2 in ("tile_q", "tile_k", "sched", "split", "pack")}
+        if w.gqa_union:
+            pre = pre_union_flops(w)
+            rec["pre_union_selected_flops"] = pre
+            rec["pre_union_selected_tflops"] = round(pre / (fwd_ms * 1e-3) / 1e12, 3)
+        if args.regret:
+            # Every candidate regime forced by a one-rule table; the table's own
+            # choice is timed again beside them with the same repetitions.
+            cands = []
+            for tq, tk in ((128, 64), (128, 128), (256, 64)):
+                for sched in ("local", "lpt", "dealt"):
+                    for split in ((0, 64) if w.gqa_union else (0, 128, 256)):
+                        for pack in ((0, 1, 2) if w.gqa_union else (0,)):
+                            cands.append((tq, tk, sched, split, pack))
+            times = {}
+            for c in cands:
+                try:
+                    pc = bsa.plan(w.problem_dict(), mask, table, bsa.Lut.forced(*c), stream=stream)
+                except bsa.BsaError:
+                    continue
+                sc = pc.stats()
+                key = (sc["tile_q"], sc["tile_k"], sc["sched"], sc["split"], sc["pack"])
+                if key not in times:
+                    times[key] = time_fwd(pc, q, k, v, o, lse, 3)
+                pc.free()
+            p = bsa.plan(w.problem_dict(), mask, table, lut, stream=stream)
+            t_table = time_fwd(p, q, k, v, o, lse, 3)
+            p.free()
+            best = min(times, key=times.get)
+            rec["regret"] = {"table_ms": round(t_table, 4), "best_ms": round(times[best], 4),
+                             "best_regime": dict(zip(("tile_q", "tile_k", "sched", "split", "pack"), best)),
+                             "regret": round(t_table / times[best] - 1.0, 4),
+                             "candidates": len(times)}
+        out.append(rec)
+        print(f"[config] {name}: {rec['forward_ms']} ms, {rec['tflops']} TFLOP/s, "
+              f"mfma {rec['mfma_frac']}, hbm(streamed) {rec['hbm_frac_streamed']}, "
+              f"area {rec['area_ratio']}" + (f", regret {rec['regret']['regret']}" if args.regret else ""),
+              file=sys.stderr, flush=True)
+        del q, k, v, o, lse, mask, table
+        torch.cuda.empty_cache()
+    return out
 
 if __name__ == "__main__":
     main()

@@ -58,7 +58,8 @@ class PlanInfo(ctypes.Structure):
                [(n, ctypes.c_int64) for n in ("rows", "entries", "items", "partial_slots",
                                               "combines", "logical_nnz", "logical_blocks",
                                               "density_pm", "imbalance16", "effective_blocks")] + \
-               [("effective_flops", ctypes.c_double), ("tile_live_subblocks", ctypes.c_int64)]
+               [("effective_flops", ctypes.c_double), ("tile_live_subblocks", ctypes.c_int64),
+                ("executed_tiles", ctypes.c_int64), ("partial_slot_bound", ctypes.c_int64)]
 
 
 class AcsrRun(ctypes.Structure):

@@ -233,8 +233,8 @@ FwdScratch fwd_scratch_layout(const Plan &P) {
   FwdScratch f;
   f.queue_off = 0;
   f.part_o_off = aligned(sizeof(int32_t) * kQueuesPerSet);
-  f.part_lse_off = f.part_o_off + aligned(sizeof(float) * (size_t)P.slot_cap * P.rg.tq * P.D);
-  f.bytes = f.part_lse_off + aligned(sizeof(float) * (size_t)P.slot_cap * P.rg.tq);
+  f.part_lse_off = f.part_o_off + aligned(sizeof(float) * (size_t)P.part_slots * P.rg.tq * P.D);
+  f.bytes = f.part_lse_off + aligned(sizeof(float) * (size_t)P.part_slots * P.rg.tq);
   return f;
 }
 
@@ -411,6 +411,27 @@ static bsa_status finish_plan(Plan &P, bsa_lut_t lut, const uint8_t *mask, const
   P.slot_cap = split > 0 ? std::min(2 * row_total / split + 1, P.nrows * cdiv(P.nkt, split)) : 0;
   P.comb_cap = split > 0 ? std::min(P.nrows, row_total / (split + 1) + 1) : 0;
   P.item_cap = P.nrows + P.slot_cap;
+  // A tighter bound on the slots, from the longest row a head can have: a
+  // split row of n entries takes ceil(n / split) slots, and a row of head h
+  // has at most min(nkt, mq * (largest logical row of h) * sk) entries (mq
+  // query blocks merged into the tile, each selected block covering sk key
+  // tiles); a union row at most nkt. Sizes the forward's partial buffers.
+  P.part_slots = 0;
+  if (split > 0) {
+    int64_t bound = 0;
+    for (int h = 0; h < P.Hq; ++h) {
+      if (P.uni && P.rg.pack && h % P.G) continue;  // a packed row serves the whole group
+      int64_t maxlen = P.nkt;
+      if (!P.uni) {
+        int64_t maxrow = 0;
+        for (int64_t bm = 0; bm < P.nbm; ++bm) maxrow = std::max(maxrow, P.feat[(bm * P.Hq + h) * 4 + 1]);
+        const int64_t mq = P.bq[h] < tq ? tq / P.bq[h] : 1, sk = P.bk[h] > tk ? P.bk[h] / tk : 1;
+        maxlen = std::min(P.nkt, mq * maxrow * sk);
+      }
+      if (maxlen > split) bound += (int64_t)P.B * P.nqt * cdiv(maxlen, split);
+    }
+    P.part_slots = std::min(P.slot_cap, bound);
+  }
   const int64_t lim = (int64_t(1) << 31) - 2;
   if (P.ent_cap > lim || P.item_cap > lim || P.nrows > lim || P.nlists > lim)
     return fail(BSA_ERR_UNSUPPORTED, "plan too large (more than 2^31 entries or rows)");
@@ -584,6 +605,7 @@ static bsa_status forward_common(bsa_plan_t plan, const bsa_tensor *q, const bsa
   a.queue = (int32_t *)(sb + fs.queue_off);
   a.part_o = fs.part_o_off != fs.part_lse_off ? (float *)(sb + fs.part_o_off) : nullptr;
   a.part_lse = fs.part_lse_off != fs.bytes ? (float *)(sb + fs.part_lse_off) : nullptr;
+  a.part_slots = P.part_slots;
   bsa_status st = attention_launch(P, a, s);
   plan_release(scratch, s);
   if (st == BSA_OK) st = note_stream_use(P, s);
@@ -754,6 +776,13 @@ bsa_status bsa_plan_stats(bsa_plan_t plan, bsa_plan_info *out) {
   int64_t bits = 0;
   for (uint32_t w : live) bits += __builtin_popcount(w);
   out->tile_live_subblocks = bits;
+  std::vector<int32_t> items((size_t)4 * cnt[CNT_ITEMS]);
+  if (!items.empty())
+    HIP_TRY(hipMemcpy(items.data(), P.items, sizeof(int32_t) * items.size(), hipMemcpyDeviceToHost));
+  int64_t executed = 0;
+  for (size_t i = 0; i < items.size(); i += 4) executed += items[i + 2] - items[i + 1];
+  out->executed_tiles = executed;
+  out->partial_slot_bound = P.part_slots;
   return BSA_OK;
 }
 

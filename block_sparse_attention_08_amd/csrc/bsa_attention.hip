@@ -287,6 +287,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
     const int iq_lo = geo.qbase >> hm.lq;
     const int niq = hm.lq >= 5 ? 1 : (32 >> hm.lq);
     const uint64_t wbits = ((1ull << (hm.mk * niq)) - 1ull) << (iq_lo * hm.mk);
+    const uint32_t wbits32 = (uint32_t)wbits;  // the wave's live bits (at most 32 per tile)
 
     if (e0 < e1) {
       load_tile(e0);
@@ -425,7 +426,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(AttnArgs a) {
           }
         if (hh == 0) a.lse[((int64_t)geo.b * a.Hq + geo.head) * a.Sq + qpos] = lse;
       }
-    } else if (qvalid) {  // the combine reads partials of existing rows only
+    } else if (qvalid && slot < a.part_slots) {  // the combine reads partials of existing rows only
       const int64_t prow = (int64_t)slot * kTileQ + 32 * wave + n;
       float *pp = a.part_o + prow * D;
 #pragma unroll
@@ -570,6 +571,8 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
   // needs more registers than the occupancy allows), whose loads are issued
   // from assembly for the same reason.
   constexpr bool RING = NS > 2 || D != 128 || KV8;
+  // Waves skip the tiles in which none of their query sub-blocks is live.
+  constexpr bool SKIP = !KV8 && !PAGED;
   __shared__ __attribute__((aligned(1024))) uint8_t lds_ring[RING ? 2 * NS * SLOT : 64];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_k0[RING ? 64 : SLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_k1[RING ? 64 : SLOT];
@@ -858,6 +861,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
     const int iq_lo = qbase >> hm.lq;
     const int niq = hm.lq >= 5 ? 1 : (32 >> hm.lq);
     const uint64_t wbits = ((1ull << (hm.mk * niq)) - 1ull) << (iq_lo * hm.mk);
+    const uint32_t wbits32 = (uint32_t)wbits;  // the wave's live bits (at most 32 per tile)
     const int qsub = ((qbase + n) >> hm.lq) * hm.mk;
 
     constexpr int STEPS = C::NKB * D / 16;     // K fragments per tile
@@ -908,7 +912,30 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
         if (j + 1 < nent) issue_v(j + 1, flip, m1);
       }
 
-      if (wlive) {
+      // A wave computes a tile only where one of its query sub-blocks is live
+      // in it (a merged tile often selects a key tile for some of its query
+      // blocks only); the S^T of tile j+1 is computed only if that tile is
+      // live for the wave, and its scores are used only then.
+      // (Only kernels whose tiles can merge query blocks: union and paged
+      // plans give every wave every entry, and e4m3 tiles would spill
+      // registers for the second path.)
+      const bool lj = SKIP ? wlive && (m0.lv & wbits32) != 0u : wlive;
+      const bool lj1 = SKIP && wlive && j + 1 < nent && (m1.lv & wbits32) != 0u;
+      if (!lj) {
+        if (lj1) {
+          const uint8_t *ks = kbuf(j + 1, flip);
+          bf16x8 kf[STEPS];
+#pragma unroll
+          for (int i = 0; i < 3 && i < STEPS; ++i) kf[i] = kfrag(ks, i);
+#pragma unroll
+          for (int i = 0; i < STEPS; ++i) {
+            if (i + 3 < STEPS) kf[i + 3] = kfrag(ks, i + 3);
+            const int t = i / (D / 16), cc = i % (D / 16);
+            s_next[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qb[cc], cc == 0 ? f32x16{} : s_next[t], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      } else {
       // ---- mask tile j (sequence end, causal diagonal, dead sub-blocks) ----
       // 32-bit scalar tests: positions and the causal offset are below 2^31.
       const int kb0 = m0.kt * TK;
@@ -978,6 +1005,17 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
       __builtin_amdgcn_s_setprio(1);
       uint32_t pw[C::NKB * 8];  // P as packed bf16 pairs
       float psum = 0.f;
+      auto exps = [&](int i) {
+#pragma unroll
+        for (int k2 = 0; k2 < EPS; k2 += 2) {
+          const int x = i * EPS + k2;
+          const float p0 = fexp2(__builtin_fmaf(s_cur[x / 16][x % 16], BSA_SL2, -m_use));
+          const float p1 = fexp2(__builtin_fmaf(s_cur[x / 16][x % 16 + 1], BSA_SL2, -m_use));
+          psum += p0;
+          psum += p1;
+          pw[x / 2] = pack_bf16x2(p0, p1);
+        }
+      };
       {
         const uint8_t *ks = kbuf(j + 1, flip);
         bf16x8 kf[STEPS];
@@ -988,15 +1026,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
           if (i + 3 < STEPS) kf[i + 3] = kfrag(ks, i + 3);
           const int t = i / (D / 16), cc = i % (D / 16);
           s_next[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qb[cc], cc == 0 ? f32x16{} : s_next[t], 0, 0, 0);
-#pragma unroll
-          for (int k2 = 0; k2 < EPS; k2 += 2) {
-            const int x = i * EPS + k2;
-            const float p0 = fexp2(__builtin_fmaf(s_cur[x / 16][x % 16], BSA_SL2, -m_use));
-            const float p1 = fexp2(__builtin_fmaf(s_cur[x / 16][x % 16 + 1], BSA_SL2, -m_use));
-            psum += p0;
-            psum += p1;
-            pw[x / 2] = pack_bf16x2(p0, p1);
-          }
+          exps(i);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -1042,7 +1072,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      }  // wlive
+      }  // lj
       if constexpr (KV8 && !KD) {
         if (j + 2 < nent) store8(k8r, kbuf(j + 2, par), false);
         if (j + 1 < nent) store8(v8r, vbuf(j + 1, flip), true);
@@ -1106,7 +1136,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
       if constexpr (NS == 2) __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       const uint8_t *ks = kbuf(0, Even{});
-      if (wlive) {
+      if (SKIP ? wlive && (m0.lv & wbits32) != 0u : wlive) {
 #pragma unroll
         for (int i = 0; i < STEPS; ++i) {
           const int t = i / (D / 16), cc = i % (D / 16);
@@ -1137,6 +1167,14 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
     // (paged K/V: +0.7%) or costs vector registers (D = 64 no longer fits
     // three waves per SIMD), so `a` is read as before.
     constexpr bool RELOAD = D == 128 && !KV8 && !PAGED;
+    // The scratch's slot count, read here from the kernel-argument segment
+    // (not kept in a scalar register through the tile loop).
+    auto slot_limit = [&]() -> int64_t {
+      const __attribute__((address_space(4))) AttnArgs *kp =
+          (const __attribute__((address_space(4))) AttnArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+      asm volatile("" : "+s"(kp));
+      return kp->part_slots;
+    };
     auto store_out = [&](const AttnArgs &oa) {
       const float l_tot = halfwave_sum(l_run);
       const float inv = l_tot > 0.f ? (KV8 ? ((const cfloat *)a.v_scale)[g_u] : 1.f) / l_tot : 0.f;
@@ -1154,7 +1192,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
             }
           if (hh == 0) oa.lse[((int64_t)b * oa.Hq + head) * oa.Sq + qpos] = lse;
         }
-      } else if (qvalid) {  // the combine reads partials of existing rows only
+      } else if (qvalid && slot < slot_limit()) {  // the combine reads partials of existing rows only
         const int64_t prow = (int64_t)slot * TQ + 32 * wave + n;
         float *pp = oa.part_o + prow * D;
 #pragma unroll
@@ -1194,6 +1232,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(AttnArgs a, const int32_t 
   const int ncomb = a.counters[CNT_COMB];
   for (int c = blockIdx.x; c < ncomb; c += gridDim.x) {
     const int r = comb[3 * c], s0 = comb[3 * c + 1], k = comb[3 * c + 2];
+    if (s0 + k > a.part_slots) continue;  // (never: the scratch holds every slot of the plan)
     for (int idx = threadIdx.x; idx < 2 * TQ; idx += kThreads) {
       const int row = idx >> 1, half = idx & 1;
       const RowPos geo = tile_row(a, r, row);

@@ -46,6 +46,7 @@ struct Plan {
   int32_t tr;  // query positions per physical row
   int64_t nqt, nkt, nlists, nrows, nlb, nbm, unkb;
   int64_t ent_cap, item_cap, slot_cap, comb_cap;
+  int64_t part_slots;  // bound on the partial slots a forward writes (sizes its scratch)
   // mask features (host copy) and aggregates
   std::vector<int64_t> feat;  // [nbm][Hq][4]: nnz, max row, empty rows, effective blocks
   int64_t total_nnz, total_blocks, density_pm, imb16, min_bq, min_bk;
@@ -84,6 +85,7 @@ struct AttnArgs {
   const uint32_t *ent_live;
   const HeadMeta *hm;
   float *part_o, *part_lse;
+  int64_t part_slots;  // partial slots the scratch holds (writes beyond are dropped)
   int64_t Sq, Skv, off, nqt;
   int32_t Hq, Hkv, G, tq, tr, pack, causal, paged, P, sched;
   float scale_log2;  // softmax scale * log2(e)
@@ -113,7 +115,8 @@ struct BwdArgs {
 // device's default pool), on the stream that uses them, so repeated requests
 // reuse freed blocks without waiting. With BSA_TEST_FAIL_ALLOC=n set, the
 // n-th allocation (device or pinned host) counted from when the variable
-// took that value fails, for tests of the out-of-memory paths.
+// took that value fails, for tests of the out-of-memory paths (the variable
+// is read at each allocation; a value change is seen there).
 hipError_t plan_alloc(void **ptr, size_t bytes, int device, hipStream_t stream);
 void plan_release(void *ptr, hipStream_t stream);
 bool alloc_fault_injected();

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 1
+#define BSA_ABI_VERSION 2
 
 typedef enum {
   BSA_OK = 0,
@@ -120,6 +120,11 @@ typedef struct {
   int64_t effective_blocks; /* blocks computed: after the union, causally feasible, all batches */
   double effective_flops;   /* sum over effective blocks of 4 * bq * bk * D */
   int64_t tile_live_subblocks; /* live (query sub-block, key sub-block) pairs over all entries */
+  int64_t executed_tiles;   /* (query tile, key tile) pairs the forward computes, over all work
+                               items: executed_tiles * tile_q * tile_k / (effective area) is the
+                               merge waste of the plan (1 = none) */
+  int64_t partial_slot_bound; /* partial slots a forward call's scratch is sized for, a bound
+                                 computed on the host before the plan exists (>= partial_slots) */
 } bsa_plan_info;
 
 /* ABI version of the library (BSA_ABI_VERSION it was built with). */

@@ -86,6 +86,7 @@ def run_gpu(ref, w, lut_text=None, device_gen=False, check_plan=True, label=""):
     torch.cuda.synchronize()
     check_written(o, lse, label or w.name)
     stats = plan.stats()
+    assert stats["partial_slots"] <= stats["partial_slot_bound"], stats
     plan.free()
     return q, k, v, o, lse, stats
 

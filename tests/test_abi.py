@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.bsa_abi_version() == 1
+    assert L.bsa_abi_version() == 2
     assert L.bsa_status_str(0) == b"ok" and L.bsa_status_str(6) == b"lookup table error"
     assert L.bsa_status_str(4) == b"out of memory"
 

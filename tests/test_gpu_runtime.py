@@ -295,23 +295,20 @@ def test_out_of_memory_paths(ref, monkeypatch):
     o, lse = plan.forward(q, k, v)
     torch.cuda.synchronize()
     _check_all_rows(ref, w, q, k, v, o, lse, "oom/after plan failures")
-    # bsa_forward: the call's scratch
-    monkeypatch.setenv("BSA_TEST_FAIL_ALLOC", "1")
-    st, msg = _status_of(lambda: plan.forward(q, k, v))
-    assert st == 4 and "scratch" in msg, (st, msg)
-    monkeypatch.delenv("BSA_TEST_FAIL_ALLOC")
-    # bsa_backward: its scratch
+    # The library reads the variable at each allocation and restarts its
+    # countdown when the value it sees changes, so every injection below is
+    # followed by a successful call (which sees the variable unset).
     dout = torch.randn_like(q.float()).to(q.dtype)
-    monkeypatch.setenv("BSA_TEST_FAIL_ALLOC", "1")
-    st, msg = _status_of(lambda: plan.backward(q, k, v, o, lse, dout))
-    assert st == 4 and "scratch" in msg, (st, msg)
-    monkeypatch.delenv("BSA_TEST_FAIL_ALLOC")
-    # bsa_select_blocks: its scratch
-    monkeypatch.setenv("BSA_TEST_FAIL_ALLOC", "1")
-    st, msg = _status_of(lambda: bsa.select_blocks(w.problem_dict(), q, k, keep_tenths=3))
-    assert st == 4 and "selection" in msg, (st, msg)
-    monkeypatch.delenv("BSA_TEST_FAIL_ALLOC")
-    # everything works again
+    calls = [("forward", lambda: plan.forward(q, k, v), "scratch"),
+             ("backward", lambda: plan.backward(q, k, v, o, lse, dout), "scratch"),
+             ("select", lambda: bsa.select_blocks(w.problem_dict(), q, k, keep_tenths=3), "selection")]
+    for name, fn, needle in calls:
+        monkeypatch.setenv("BSA_TEST_FAIL_ALLOC", "1")
+        st, msg = _status_of(fn)
+        say(f"[oom] {name}: {st} {msg}")
+        assert st == 4 and needle in msg, (name, st, msg)
+        monkeypatch.delenv("BSA_TEST_FAIL_ALLOC")
+        fn()  # works again
     o2, lse2 = plan.forward(q, k, v)
     dq, dk, dv = plan.backward(q, k, v, o2, lse2, dout)
     torch.cuda.synchronize()
