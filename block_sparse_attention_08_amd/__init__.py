@@ -111,6 +111,9 @@ def lib() -> ctypes.CDLL:
         L.bsa_lut_free.restype = None
         L.bsa_plan.argtypes = [P(Problem), vp, vp, vp, vp, P(vp)]
         L.bsa_forward.argtypes = [vp, P(Tensor), P(Tensor), P(Tensor), P(Tensor), vp, vp]
+        if hasattr(L, "bsa_forward_noalloc"):  # (absent from builds before ABI 2)
+            L.bsa_forward_noalloc.argtypes = [vp, P(Tensor), P(Tensor), P(Tensor), P(Tensor), vp, vp]
+            L.bsa_forward_noalloc.restype = ctypes.c_int
         L.bsa_plan_export.argtypes = [vp, vp, P(ctypes.c_size_t)]
         L.bsa_plan_stats.argtypes = [vp, P(PlanInfo)]
         L.bsa_plan_free.argtypes = [vp]
@@ -250,6 +253,17 @@ class Plan:
         _check(lib().bsa_forward(self._h, ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv),
                                  ctypes.byref(to), lse.data_ptr() if lse.numel() else None,
                                  _stream_handle(stream)))
+        return o, lse
+
+    def forward_noalloc(self, q, k, v, o, lse, stream=None):
+        """bsa_forward_noalloc: forward into caller-provided O and LSE with the
+        library's static device scratch (no allocation by the library)."""
+        p = self.problem
+        paged = bool(p.get("paged", 0))
+        tq, tk, tv, to = _tensor(q), _tensor(k, paged), _tensor(v, paged), _tensor(o)
+        _check(lib().bsa_forward_noalloc(self._h, ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv),
+                                         ctypes.byref(to), lse.data_ptr() if lse.numel() else None,
+                                         _stream_handle(stream)))
         return o, lse
 
     def forward_kv8(self, q, k8, v8, k_scale, v_scale, o=None, lse=None, stream=None):

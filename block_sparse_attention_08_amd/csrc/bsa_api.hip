@@ -238,6 +238,33 @@ FwdScratch fwd_scratch_layout(const Plan &P) {
   return f;
 }
 
+// Static forward scratch for bsa_forward_noalloc: one array per device,
+// allocated with the code object and held until the process ends. In host
+// code `scratch` names a host-side stand-in, not device memory, so its device
+// address is looked up once per device (with that device current) and only
+// that address is handed to kernels.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+static std::mutex g_static_mu;
+static std::vector<std::pair<int, void *>> g_static_addr;  // (device, address)
+
+static bsa_status static_scratch(int device, void **out) {
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  for (auto &d : g_static_addr)
+    if (d.first == device) {
+      *out = d.second;
+      return BSA_OK;
+    }
+  void *ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr)
+    return fail(BSA_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+  g_static_addr.emplace_back(device, ptr);
+  *out = ptr;
+  return BSA_OK;
+}
+
 }  // namespace bsa
 
 using namespace bsa;
@@ -534,11 +561,16 @@ bsa_status bsa_plan_acsr(const bsa_problem *pr, const bsa_acsr_head *heads, bsa_
 
 static bsa_status forward_common(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k,
                                  const bsa_tensor *v, bsa_tensor *o, float *lse, const float *k_scale,
-                                 const float *v_scale, void *stream);
+                                 const float *v_scale, void *stream, bool no_alloc = false);
 
 bsa_status bsa_forward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k, const bsa_tensor *v,
                        bsa_tensor *o, float *lse, void *stream) {
   return forward_common(plan, q, k, v, o, lse, nullptr, nullptr, stream);
+}
+
+bsa_status bsa_forward_noalloc(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k,
+                               const bsa_tensor *v, bsa_tensor *o, float *lse, void *stream) {
+  return forward_common(plan, q, k, v, o, lse, nullptr, nullptr, stream, true);
 }
 
 bsa_status bsa_forward_kv8(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k,
@@ -553,7 +585,7 @@ bsa_status bsa_forward_kv8(bsa_plan_t plan, const bsa_tensor *q, const bsa_tenso
 
 static bsa_status forward_common(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k,
                                  const bsa_tensor *v, bsa_tensor *o, float *lse, const float *k_scale,
-                                 const float *v_scale, void *stream) {
+                                 const float *v_scale, void *stream, bool no_alloc) {
   if (!plan || !q || !k || !v || !o) return fail(BSA_ERR_INVALID_ARG, "NULL plan or tensor");
   const Plan &P = *plan;
   const bool kv8 = k_scale != nullptr;
@@ -597,6 +629,19 @@ static bsa_status forward_common(bsa_plan_t plan, const bsa_tensor *q, const bsa
   const FwdScratch fs = fwd_scratch_layout(P);
   hipStream_t s = (hipStream_t)stream;
   void *scratch = nullptr;
+  if (no_alloc) {
+    // The device's static scratch array instead of the pool.
+    if (fs.bytes > kStaticScratchBytes)
+      return fail(BSA_ERR_UNSUPPORTED, "this plan's forward needs " + std::to_string(fs.bytes) +
+                                           " bytes of scratch; the static scratch holds " +
+                                           std::to_string(kStaticScratchBytes));
+    if (bsa_status st = static_scratch(P.device, &scratch)) return st;
+    a.queue = (int32_t *)((uint8_t *)scratch + fs.queue_off);
+    a.part_o = fs.part_o_off != fs.part_lse_off ? (float *)((uint8_t *)scratch + fs.part_o_off) : nullptr;
+    a.part_lse = fs.part_lse_off != fs.bytes ? (float *)((uint8_t *)scratch + fs.part_lse_off) : nullptr;
+    a.part_slots = P.part_slots;
+    return attention_launch(P, a, s);
+  }
   const hipError_t e = plan_alloc(&scratch, fs.bytes, P.device, s);
   if (e != hipSuccess)
     return fail(BSA_ERR_OUT_OF_MEMORY, "forward scratch of " + std::to_string(fs.bytes) +

@@ -205,6 +205,22 @@ bsa_status bsa_plan(const bsa_problem *problem, const uint8_t *mask, const int32
 bsa_status bsa_forward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k,
                        const bsa_tensor *v, bsa_tensor *o, float *lse, void *stream);
 
+/* bsa_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation, arguments, errors and results as bsa_forward, but the
+ * call's scratch (work-queue counters and split-KV partials) is a static
+ * device array of 64 MiB that the library holds on each device it runs on
+ * until the process ends, so the call allocates nothing. A plan whose
+ * scratch needs more (many split rows: see bsa_plan_info.partial_slot_bound,
+ * 4 * tile_q * (head_dim + 1) bytes per slot, plus 256) is rejected with
+ * BSA_ERR_UNSUPPORTED before anything is queued. Every call on a device
+ * shares that device's array: calls that overlap in time on one device (on
+ * any streams, any plans) race and must be serialised by the caller. Unlike
+ * bsa_forward, a call on a stream other than the plan's records no event for
+ * bsa_plan_free: order the plan's release after it yourself. */
+bsa_status bsa_forward_noalloc(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *k,
+                               const bsa_tensor *v, bsa_tensor *o, float *lse, void *stream);
+
 /* Attention forward with K and V stored as OCP FP8 E4M3 bytes (one byte per
  * element: sign, 4 exponent bits with bias 7, 3 mantissa bits; no
  * infinities), the low-precision KV cache of serving (CompactAttention
