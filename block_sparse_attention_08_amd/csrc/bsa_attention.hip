@@ -919,10 +919,8 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
       // (Only kernels whose tiles can merge query blocks: union and paged
       // plans give every wave every entry, and e4m3 tiles would spill
       // registers for the second path.)
-      const bool lj = SKIP ? wlive && (m0.lv & wbits32) != 0u : wlive;
-      const bool lj1 = SKIP && wlive && j + 1 < nent && (m1.lv & wbits32) != 0u;
-      if (!lj) {
-        if (lj1) {
+      if constexpr (SKIP) {
+        if (wlive && (m0.lv & wbits32) == 0u && j + 1 < nent && (m1.lv & wbits32) != 0u) {
           const uint8_t *ks = kbuf(j + 1, flip);
           bf16x8 kf[STEPS];
 #pragma unroll
@@ -935,7 +933,12 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
             __builtin_amdgcn_sched_barrier(0);
           }
         }
-      } else {
+      }
+      const bool lj = [&] {
+        if constexpr (SKIP) return wlive && (m0.lv & wbits32) != 0u;
+        else return wlive;
+      }();
+      if (lj) {
       // ---- mask tile j (sequence end, causal diagonal, dead sub-blocks) ----
       // 32-bit scalar tests: positions and the causal offset are below 2^31.
       const int kb0 = m0.kt * TK;
@@ -1136,7 +1139,11 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
       if constexpr (NS == 2) __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       const uint8_t *ks = kbuf(0, Even{});
-      if (SKIP ? wlive && (m0.lv & wbits32) != 0u : wlive) {
+      const bool l0 = [&] {
+        if constexpr (SKIP) return wlive && (m0.lv & wbits32) != 0u;
+        else return wlive;
+      }();
+      if (l0) {
 #pragma unroll
         for (int i = 0; i < STEPS; ++i) {
           const int t = i / (D / 16), cc = i % (D / 16);
@@ -1169,7 +1176,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
     constexpr bool RELOAD = D == 128 && !KV8 && !PAGED;
     // The scratch's slot count, read here from the kernel-argument segment
     // (not kept in a scalar register through the tile loop).
-    auto slot_limit = [&]() -> int64_t {
+    auto slot_limit = [&]() -> int {
       const __attribute__((address_space(4))) AttnArgs *kp =
           (const __attribute__((address_space(4))) AttnArgs *)__builtin_amdgcn_kernarg_segment_ptr();
       asm volatile("" : "+s"(kp));

@@ -85,12 +85,12 @@ struct AttnArgs {
   const uint32_t *ent_live;
   const HeadMeta *hm;
   float *part_o, *part_lse;
-  int64_t part_slots;  // partial slots the scratch holds (writes beyond are dropped)
   int64_t Sq, Skv, off, nqt;
   int32_t Hq, Hkv, G, tq, tr, pack, causal, paged, P, sched;
   float scale_log2;  // softmax scale * log2(e)
   int32_t kv8;       // K and V are OCP FP8 E4M3 bytes scaled per kv head by k_scale, v_scale
   const float *k_scale, *v_scale;
+  int32_t part_slots;  // partial slots the scratch holds (writes beyond are dropped)
 };
 
 struct BwdArgs {

@@ -2,11 +2,15 @@
 
 Tessera (abstract) picks an execution plan per request through a lookup table
 built from offline profiling. Table format 2: each rule also matches a range of
-the query length, so decode and short chunks get their own regime. This script is that offline step for libbsa: for
-each mask-shape bucket it times every candidate regime (tile rows, key tile,
-schedule, split threshold, GQA packing) on a representative seeded workload,
-one request = bsa_plan + bsa_forward, and writes the fastest regime of each
-bucket as a rule, in bucket order, followed by a catch-all default.
+the query length, so decode and short chunks get their own regime. This script is
+that offline step for libbsa: each mask-shape bucket has a few seeded training
+workloads (other seeds, window widths, densities, shapes and block sizes than
+the benchmark configurations, which stay held out); every candidate regime
+(tile rows, key tile, schedule, split threshold, GQA packing) is timed on each
+of them, one request = bsa_plan + bsa_forward, and the bucket's rule is the
+regime with the smallest geometric mean of its time relative to the best
+regime of each training workload. Rules are written in bucket order, followed
+by a catch-all default.
 
     python -m block_sparse_attention_08_amd.lut.build_lut [--out PATH] [--steps N]
 """
@@ -33,30 +37,39 @@ ANYSQ = "  0 " + BIG
 
 
 def buckets():
-    """(name, rule key fields and ranges, representative workload factory,
+    """(name, rule key fields and ranges, training workload factories,
     candidate regimes or None for the default set). Rules carry a fifth range
-    on the query length (table format 2); first match wins."""
+    on the query length (table format 2); first match wins. The training
+    workloads differ from the benchmark configurations (held out) in seed,
+    shape, window, density or block size."""
     from block_sparse_attention_08_amd import workloads as W
     return [
         # Decode and short chunks: a few queries per sequence over a long paged
         # cache with GQA union tables (split-KV keeps every CU busy).
         ("decode", "* bf16 1 1  0 " + BIG + "  0 " + BIG + "  0 " + BIG + "  0 " + BIGIMB + "  1 64",
-         lambda: W.decode(), decode_candidates()),
+         [lambda: W.decode(seed=11), lambda: W.decode(batch=8, q_len=4, context=32768, seed=12),
+          lambda: W.decode(batch=32, q_len=2, context=16384, seed=13)], decode_candidates()),
         # GQA union over a paged cache (chunked prefill).
         ("gqa-union", "* bf16 1 *  0 " + BIG + "  0 " + BIG + "  0 " + BIG + "  0 " + BIGIMB + ANYSQ,
-         lambda: W.chunked_prefill(), None),
+         [lambda: W.chunked_prefill(chunk=2048, context=32768, seed=11),
+          lambda: W.chunked_prefill(chunk=4096, context=49152, keep_tenths=2, seed=12),
+          lambda: W.chunked_prefill(hq=16, hkv=4, chunk=8192, context=65536, seed=13)], None),
         # Large blocks (>= 128), D=128, low density: 3-D video windows.
         ("video-128", "128 bf16 0 *  128 " + BIG + "  128 " + BIG + "  0 400  0 " + BIGIMB + ANYSQ,
-         lambda: W.video_dit(), None),
+         [lambda: W.video_dit(seed=11), lambda: W.video_dit(heads=16, p_global=0.06, seed=12),
+          lambda: W.video_dit(heads=24, grid=(16, 30, 40), window=(1, 1, 1), seed=13)], None),
         # Mixed block sizes with uneven rows (long video), D=128.
         ("mixed-128", "128 bf16 0 *  16 127  16 " + BIG + "  0 " + BIG + "  0 " + BIGIMB + ANYSQ,
-         lambda: W.long_video(), None),
+         [lambda: W.long_video(heads=20, seed=11), lambda: W.long_video(heads=24, grid=(16, 48, 80), seed=12),
+          lambda: W.long_video(heads=16, p_heavy=0.10, seed=13)], None),
         # Small blocks, D=64, low density (regular patterns).
         ("regular-64-sparse", "64 bf16 0 *  16 " + BIG + "  16 " + BIG + "  0 200  0 " + BIGIMB + ANYSQ,
-         lambda: W.affine(bs=64), None),
+         [lambda: W.affine(bs=64, window=512, s=16384), lambda: W.affine(bs=32, window=768, s=16384),
+          lambda: W.affine(bs=64, window=2048, s=32768, batch=1)], None),
         # Small blocks, D=64, dense windows.
         ("regular-64-dense", "64 bf16 0 *  16 " + BIG + "  16 " + BIG + "  201 " + BIG + "  0 " + BIGIMB + ANYSQ,
-         lambda: W.affine(bs=64, window=8192), None),
+         [lambda: W.affine(bs=64, window=6144), lambda: W.affine(bs=32, window=4096, s=8192),
+          lambda: W.affine(bs=64, window=12288, s=32768, batch=1)], None),
     ]
 
 
@@ -68,13 +81,16 @@ def decode_candidates():
     return out
 
 
-def candidates(union: bool):
+def candidates(union):
+    """Candidate regimes: union problems (union True) also try GQA packing
+    (pack 1 and 2); non-union problems (False) have none; None gives both
+    sets (packing is skipped for non-union workloads when timed)."""
     out = []
     for tq, tk, sched, split in itertools.product((128, 256), (64, 128), ("local", "lpt", "dealt"),
                                                   (0, 128, 256)):
         if tq == 256 and tk == 128:
             continue  # the planner turns it into 256 x 64
-        for pack in ((1, 0) if union else (0,)):
+        for pack in ((0,) if union is False else (0, 1, 2)):
             out.append((tq, tk, sched, split, pack))
     return out
 
@@ -117,35 +133,46 @@ def main():
              f"({dev.multi_processor_count} CUs), {args.steps} timed requests per regime.",
              "#   rule D dtype union paged bq_lo bq_hi bk_lo bk_hi dens_lo dens_hi imb_lo imb_hi "
              "sq_lo sq_hi -> Tq Tk sched split pack",
-             "# Each rule is the fastest regime (bsa_plan + bsa_forward) measured on the named"
-             " representative workload; first match wins."]
-    for name, key, make, cands in buckets():
-        w = make()
-        q, k, v = w.make_qkv(device="cuda")
-        mask = torch.from_numpy(np.ascontiguousarray(w.mask)).cuda()
-        table = torch.from_numpy(np.ascontiguousarray(w.page_table)).cuda() if w.paged else None
-        o = torch.empty_like(q)
-        lse = torch.empty((w.batch, w.hq, w.sq), dtype=torch.float32, device="cuda")
-        tensors = (q, k, v, mask, table, o, lse)
-        res = []
-        for reg in (cands or candidates(w.gqa_union)):
-            dt = time_regime(bsa, w, tensors, reg, args.steps)
-            res.append((dt, reg))
-            print(f"[lut] {name}: {reg} {dt * 1e3:.3f} ms", flush=True)
-        res.sort()
-        # Among regimes within 2% of the fastest, take the simplest one
+             "# Each rule is the regime with the best geometric-mean request time (bsa_plan +"
+             " bsa_forward) over its bucket's training workloads; first match wins."]
+    for name, key, makers, cands in buckets():
+        cands = cands or candidates(None)
+        rel = {c: [] for c in cands}
+        descr = []
+        for make in makers:
+            w = make()
+            q, k, v = w.make_qkv(device="cuda")
+            mask = torch.from_numpy(np.ascontiguousarray(w.mask)).cuda()
+            table = torch.from_numpy(np.ascontiguousarray(w.page_table)).cuda() if w.paged else None
+            o = torch.empty_like(q)
+            lse = torch.empty((w.batch, w.hq, w.sq), dtype=torch.float32, device="cuda")
+            tensors = (q, k, v, mask, table, o, lse)
+            res = {}
+            for reg in cands:
+                if reg[4] and not w.gqa_union:
+                    continue
+                res[reg] = time_regime(bsa, w, tensors, reg, args.steps)
+                print(f"[lut] {name} {w.name} B={w.batch} Hq={w.hq} S={w.sq}/{w.skv}: {reg} "
+                      f"{res[reg] * 1e3:.3f} ms", flush=True)
+            fastest = min(res.values())
+            for reg, dt in res.items():
+                rel[reg].append(dt / fastest)
+            descr.append(f"{w.name} B={w.batch} Hq={w.hq} S={w.sq}/{w.skv} D={w.d} "
+                         f"density {1000 * int(w.mask.sum()) // max(1, w.mask.size)}pm")
+            del q, k, v, o, lse, mask, table
+            torch.cuda.empty_cache()
+        score = {reg: float(np.exp(np.mean(np.log(r)))) for reg, r in rel.items() if len(r) == len(makers)}
+        # Among regimes within 2% of the best score, take the simplest one
         # (no split, 128-row and 64-key tiles, row order, packing).
-        fastest = res[0][0]
-        close = [(dt, reg) for dt, reg in res if dt <= fastest * 1.02]
+        best_score = min(score.values())
+        close = [(sc, reg) for reg, sc in score.items() if sc <= best_score * 1.02]
         simplicity = lambda reg: (reg[3] != 0, reg[0] != 128, reg[1] != 64, reg[2] != "local", reg[4] == 0)
-        best_dt, best = min(close, key=lambda x: (simplicity(x[1]), x[0]))
-        second = res[1][0] if len(res) > 1 else best_dt
+        sc, best = min(close, key=lambda x: (simplicity(x[1]), x[0]))
         tq, tk, sched, split, pack = best
-        lines.append(f"# {name}: {w.name} B={w.batch} Hq={w.hq} S={w.sq}/{w.skv} D={w.d}; best "
-                     f"{best_dt * 1e3:.3f} ms per request (next {second * 1e3:.3f} ms)")
+        lines.append(f"# {name}: trained on " + "; ".join(descr))
+        lines.append(f"#   geometric-mean time relative to each workload's best: {sc:.3f} "
+                     f"(best regime overall {best_score:.3f})")
         lines.append(f"rule {key} -> {tq} {tk} {sched} {split} {pack}")
-        del q, k, v, o, lse, mask, table
-        torch.cuda.empty_cache()
     lines.append("# Anything else: 128 x 64 tiles, row order, no split, GQA packing when possible.")
     lines.append("rule * * * * 0 " + BIG + " 0 " + BIG + " 0 " + BIG + " 0 " + BIGIMB + ANYSQ + " -> 128 64 local 0 1")
     text = "\n".join(lines) + "\n"
