@@ -602,7 +602,9 @@ def config_table(bsa, lut, args):
                 except bsa.BsaError:
                     continue
                 sc = pc.stats()
-                key = (sc["tile_q"], sc["tile_k"], sc["sched"], sc["split"], sc["pack"])
+                # (a split that no row reaches runs as no split)
+                key = (sc["tile_q"], sc["tile_k"], sc["sched"],
+                       sc["split"] if sc["partial_slots"] > 0 else 0, sc["pack"])
                 if c is None:
                     table_key = key
                 if key in plans:
@@ -610,9 +612,10 @@ def config_table(bsa, lut, args):
                 else:
                     plans[key] = pc
             times = {}
+            reps = max(5, min(20, int(200.0 / max(fwd_ms, 0.05))))  # about 0.2 s per measurement
             for rnd in range(2):  # two interleaved rounds, the better of the two kept
                 for key, pc in plans.items():
-                    t = time_fwd(pc, q, k, v, o, lse, 5)
+                    t = time_fwd(pc, q, k, v, o, lse, reps)
                     times[key] = min(times.get(key, t), t)
             for pc in plans.values():
                 pc.free()

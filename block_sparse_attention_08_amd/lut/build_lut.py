@@ -95,6 +95,18 @@ def candidates(union):
     return out
 
 
+def effective_regime(bsa, w, tensors, regime):
+    """The regime the planner actually runs for this workload: (Tq, Tk,
+    schedule, split, pack) after validation, with split 0 when no row is
+    split."""
+    q, k, v, mask, table, o, lse = tensors
+    p = bsa.plan(w.problem_dict(), mask, table, bsa.Lut.forced(*regime))
+    st = p.stats()
+    p.free()
+    sched = ("local", "lpt", "dealt")[st["sched"]]
+    return (st["tile_q"], st["tile_k"], sched, st["split"] if st["partial_slots"] > 0 else 0, st["pack"])
+
+
 def time_regime(bsa, w, tensors, regime, steps):
     import torch
     q, k, v, mask, table, o, lse = tensors
@@ -122,7 +134,7 @@ def time_regime(bsa, w, tensors, regime, steps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default=os.path.join(HERE, "gfx950.lut"))
-    ap.add_argument("--steps", type=int, default=6)
+    ap.add_argument("--steps", type=int, default=10)
     args = ap.parse_args()
     import torch
     import block_sparse_attention_08_amd as bsa
@@ -147,13 +159,23 @@ def main():
             o = torch.empty_like(q)
             lse = torch.empty((w.batch, w.hq, w.sq), dtype=torch.float32, device="cuda")
             tensors = (q, k, v, mask, table, o, lse)
-            res = {}
+            # Regimes that give the same plan execute alike: a split that no
+            # row reaches is no split, and the planner makes every regime
+            # valid for the problem. Each distinct effective regime is timed
+            # once (the better of two rounds) and stands for its nominal ones.
+            eff_of, timed = {}, {}
             for reg in cands:
                 if reg[4] and not w.gqa_union:
                     continue
-                res[reg] = time_regime(bsa, w, tensors, reg, args.steps)
-                print(f"[lut] {name} {w.name} B={w.batch} Hq={w.hq} S={w.sq}/{w.skv}: {reg} "
-                      f"{res[reg] * 1e3:.3f} ms", flush=True)
+                eff_of[reg] = effective_regime(bsa, w, tensors, reg)
+            for rnd in range(2):
+                for e in sorted(set(eff_of.values()), key=str):
+                    dt = time_regime(bsa, w, tensors, e, args.steps)
+                    timed[e] = min(timed.get(e, dt), dt)
+            res = {reg: timed[e] for reg, e in eff_of.items()}
+            for e, dt in sorted(timed.items(), key=lambda x: x[1]):
+                print(f"[lut] {name} {w.name} B={w.batch} Hq={w.hq} S={w.sq}/{w.skv}: {e} "
+                      f"{dt * 1e3:.3f} ms", flush=True)
             fastest = min(res.values())
             for reg, dt in res.items():
                 rel[reg].append(dt / fastest)
@@ -162,10 +184,10 @@ def main():
             del q, k, v, o, lse, mask, table
             torch.cuda.empty_cache()
         score = {reg: float(np.exp(np.mean(np.log(r)))) for reg, r in rel.items() if len(r) == len(makers)}
-        # Among regimes within 2% of the best score, take the simplest one
+        # Among regimes within 1% of the best score, take the simplest one
         # (no split, 128-row and 64-key tiles, row order, packing).
         best_score = min(score.values())
-        close = [(sc, reg) for reg, sc in score.items() if sc <= best_score * 1.02]
+        close = [(sc, reg) for reg, sc in score.items() if sc <= best_score * 1.01]
         simplicity = lambda reg: (reg[3] != 0, reg[0] != 128, reg[1] != 64, reg[2] != "local", reg[4] == 0)
         sc, best = min(close, key=lambda x: (simplicity(x[1]), x[0]))
         tq, tk, sched, split, pack = best

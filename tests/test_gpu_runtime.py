@@ -146,11 +146,14 @@ SPLIT_CASES = {
     "split3": (lambda seed: W.random_problem(batch=1, hq=3, sq=520, skv=1500, d=128, bq=64, bk=64,
                                              density=0.5, empty_rows=0.05, seed=seed),
                forced_lut_text(128, 64, "local", 3, 0)),
-    # the packaged table's video bucket (128-blocks, density <= 40%): split at
-    # 128 key tiles, which rows of ~140 tiles exceed
-    "packaged_split128": (lambda seed: W.random_problem(batch=1, hq=2, sq=512, skv=24000, d=128,
-                                                        bq=128, bk=128, density=0.38, seed=seed),
-                          None),
+    # split at 128 key tiles (rows of ~140 tiles exceed it), rows dealt to the XCDs
+    "split128_dealt": (lambda seed: W.random_problem(batch=1, hq=2, sq=512, skv=24000, d=128,
+                                                     bq=128, bk=128, density=0.38, seed=seed),
+                       forced_lut_text(128, 64, "dealt", 128, 0)),
+    # the packaged table's decode bucket (union tables over a paged cache,
+    # a few queries): rows split at 32 key tiles
+    "packaged_decode": (lambda seed: W.decode(batch=4, hq=8, hkv=2, q_len=3, context=8192, seed=seed),
+                        None),
 }
 
 
