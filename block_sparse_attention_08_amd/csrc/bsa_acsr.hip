@@ -191,3 +191,49 @@ void acsr_features(const bsa_problem &pr, const bsa_acsr_head *heads, int64_t *o
 }
 
 }  // namespace bsa
+
+namespace bsa {
+
+// Query-block interleave costs of an ACSR plan, counted on the host as the
+// mask planner's k_qil_cost counts them on the device: for each head with
+// 32- or 64-row blocks and each candidate s = 2^c with s * mq <= nq (mq =
+// 128 / bq), the key blocks that some query block of each 128-row tile
+// selects, summed over the tiles. A tile's rows are expanded from the runs
+// into one bit set of the head's key blocks.
+void acsr_qil_costs(const bsa_problem &pr, const bsa_acsr_head *heads, int64_t *out) {
+  for (int h = 0; h < pr.num_q_heads; ++h) {
+    const int64_t bq = pr.block_q[h], bk = pr.block_k[h];
+    const int64_t nq = (pr.seqlen_q + bq - 1) / bq, nk = (pr.seqlen_kv + bk - 1) / bk;
+    for (int c = 0; c < kQilCands; ++c) out[h * kQilCands + c] = 0;
+    if (bq < 32 || bq >= 128) continue;
+    const int64_t mq = 128 / bq;
+    const int lm = __builtin_ctz((unsigned)mq);
+    std::vector<uint64_t> bits((size_t)((nk + 63) / 64));
+    const bsa_acsr_head &d = heads[h];
+    for (int c = 0; c < kQilCands && (int64_t(1) << c) * mq <= nq; ++c) {
+      int64_t cost = 0;
+      for (int64_t t = 0; t < (nq + mq - 1) / mq; ++t) {
+        std::fill(bits.begin(), bits.end(), 0ull);
+        for (int64_t iq = 0; iq < mq; ++iq) {
+          const int64_t qb = qblock_of(t, iq, c, lm, nq);
+          if (qb >= nq) continue;
+          for (int j = 0; j < d.num_runs; ++j) {
+            const bsa_acsr_run &u = d.runs[j];
+            const int64_t f = acsr_first(u, qb);
+            // blocks f + stride * i in [0, nk), 0 <= i < count
+            int64_t i0 = f >= 0 ? 0 : (-f + u.stride - 1) / u.stride;
+            for (int64_t i = i0; i < u.count; ++i) {
+              const int64_t kb = f + u.stride * i;
+              if (kb >= nk) break;
+              bits[(size_t)(kb >> 6)] |= 1ull << (kb & 63);
+            }
+          }
+        }
+        for (uint64_t w : bits) cost += __builtin_popcountll(w);
+      }
+      out[h * kQilCands + c] = cost;
+    }
+  }
+}
+
+}  // namespace bsa

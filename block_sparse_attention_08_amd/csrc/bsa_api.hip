@@ -366,7 +366,9 @@ static bsa_status alloc_header(Plan &P, bool acsr, bsa_acsr_head **acsr_dev) {
   int64_t rows_per_bm = 0;
   for (int h = 0; h < P.Hq; ++h) rows_per_bm += cdiv(P.Sq, P.bq[h]);
   const size_t acsr_bytes = acsr ? sizeof(bsa_acsr_head) * P.Hq : 0;
-  const size_t pre_bytes = aligned(sizeof(int32_t) * CNT_N) + aligned(feat_bytes) +
+  const size_t cost_bytes = sizeof(unsigned long long) * kQilCands * P.Hq;
+  const size_t pre_bytes = aligned(sizeof(int32_t) * CNT_N) + aligned(feat_bytes) + aligned(cost_bytes) +
+                           aligned(sizeof(int64_t) * (kQilCands * P.Hq + 1)) +
                            aligned(sizeof(HeadMeta) * P.Hq) +
                            aligned((size_t)P.nbm * P.Hkv * std::max<int64_t>(P.unkb, 1)) +
                            aligned(sizeof(int32_t) * 2 * std::max<int64_t>(acsr ? 1 : P.nbm * rows_per_bm, 1)) +
@@ -380,6 +382,8 @@ static bsa_status alloc_header(Plan &P, bool acsr, bsa_acsr_head **acsr_dev) {
   pb += aligned(sizeof(int32_t) * CNT_N);
   P.feat_dev = (unsigned long long *)pb;
   pb += aligned(feat_bytes);
+  P.qil_dev = (unsigned long long *)pb;  // costs, then the cost kernel's wave offsets
+  pb += aligned(cost_bytes) + aligned(sizeof(int64_t) * (kQilCands * P.Hq + 1));
   P.hmeta = (HeadMeta *)pb;
   pb += aligned(sizeof(HeadMeta) * P.Hq);
   P.uni_bits = pb;
@@ -387,7 +391,8 @@ static bsa_status alloc_header(Plan &P, bool acsr, bsa_acsr_head **acsr_dev) {
   P.row_feat = (int32_t *)pb;
   pb += aligned(sizeof(int32_t) * 2 * std::max<int64_t>(acsr ? 1 : P.nbm * rows_per_bm, 1));
   if (acsr_dev) *acsr_dev = acsr ? (bsa_acsr_head *)pb : nullptr;
-  if (hipMemsetAsync(P.counters, 0, sizeof(int32_t) * CNT_N, P.stream) != hipSuccess)
+  if (hipMemsetAsync(P.counters, 0, sizeof(int32_t) * CNT_N, P.stream) != hipSuccess ||
+      hipMemsetAsync(P.qil_dev, 0, cost_bytes, P.stream) != hipSuccess)
     return fail(BSA_ERR_HIP, "hipMemsetAsync failed");
   return BSA_OK;
 }
@@ -412,6 +417,18 @@ static bsa_status finish_plan(Plan &P, bsa_lut_t lut, const uint8_t *mask, const
   }
   P.density_pm = P.total_blocks ? 1000 * P.total_nnz / P.total_blocks : 0;
   if (bsa_status s = choose_regime(P, lut)) return s;
+  // Query-block interleave per head (128-row tiles merging 32- or 64-row
+  // blocks, no union): the candidate s = 2^c with s * mq <= nq whose tiles
+  // list the fewest key blocks, the smallest on ties.
+  P.qil.assign(P.Hq, 1);
+  for (int h = 0; h < P.Hq; ++h) {
+    const int64_t bq = P.bq[h], nq = cdiv(P.Sq, bq);
+    if (P.uni || P.rg.tq != 128 || bq >= 128 || bq < 32 || P.qil_cost.empty()) continue;
+    const int64_t mq = 128 / bq;
+    int64_t best = P.qil_cost[h * kQilCands];
+    for (int c = 1; c < kQilCands && (int64_t(1) << c) * mq <= nq; ++c)
+      if (P.qil_cost[h * kQilCands + c] < best) best = P.qil_cost[h * kQilCands + c], P.qil[h] = 1 << c;
+  }
 
   // ---- geometry and capacities ----
   const int tq = P.rg.tq, tk = P.rg.tk;
@@ -511,7 +528,8 @@ bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *p
   // The one read-back of planning: counters and mask features, into pinned
   // host memory (a direct DMA, no staging through pageable memory).
   const size_t feat_bytes = sizeof(int64_t) * 4 * P.nbm * P.Hq;
-  const size_t head_bytes = aligned(sizeof(int32_t) * CNT_N) + feat_bytes;
+  const size_t cost_bytes = sizeof(int64_t) * kQilCands * P.Hq;
+  const size_t head_bytes = aligned(sizeof(int32_t) * CNT_N) + aligned(feat_bytes) + cost_bytes;
   PinnedBuf pin(head_bytes);
   if (!pin.p) return bail(fail(BSA_ERR_OUT_OF_MEMORY, "pinned host allocation failed"));
   if (hipMemcpyAsync(pin.p, P.counters, head_bytes, hipMemcpyDeviceToHost, P.stream) != hipSuccess ||
@@ -521,6 +539,8 @@ bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *p
   const int32_t *hc = (const int32_t *)pin.p;
   const int64_t *hf = (const int64_t *)((const uint8_t *)pin.p + aligned(sizeof(int32_t) * CNT_N));
   P.feat.assign(hf, hf + feat_bytes / 8);
+  const int64_t *hcost = (const int64_t *)((const uint8_t *)hf + aligned(feat_bytes));
+  P.qil_cost.assign(hcost, hcost + kQilCands * P.Hq);
   if (hc[CNT_BADPAGE]) return bail(fail(BSA_ERR_INVALID_ARG, "page table entry outside [0, num_pages)"));
 
   if (bsa_status s = finish_plan(P, lut, mask, page_table)) return bail(s);
@@ -773,6 +793,7 @@ bsa_status bsa_plan_export(bsa_plan_t plan, void *host_buf, size_t *bytes) {
   put(hdr, sizeof hdr);
   put(P.bq.data(), sizeof(int32_t) * P.Hq);
   put(P.bk.data(), sizeof(int32_t) * P.Hq);
+  put(P.qil.data(), sizeof(int32_t) * P.Hq);
   put(P.feat.data(), sizeof(int64_t) * P.feat.size());
   if (bsa_status s = put_dev(P.list_off, sizeof(int32_t) * (P.nlists + 1))) return s;
   if (bsa_status s = put_dev(P.ent_kt, sizeof(int32_t) * nent)) return s;

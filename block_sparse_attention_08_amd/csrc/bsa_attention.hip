@@ -98,7 +98,7 @@ __device__ __forceinline__ RowGeo row_geo(const AttnArgs &a, int r, int wave) {
     o.qbase = 0;
   } else {
     o.head = hrow;
-    o.q0 = qt * a.tq + 32 * wave;
+    o.q0 = tile_query(a.hm[hrow], __builtin_ctz(a.tq), qt, 32 * wave);  // (query-block interleave)
     o.qbase = 32 * wave;
   }
   o.g = o.head / a.G;
@@ -125,7 +125,7 @@ __device__ __forceinline__ RowPos tile_row(const AttnArgs &a, int r, int R) {
   } else if (a.pack) {
     o.head = hrow * a.G + R / a.tr, o.q = qt * a.tr + R % a.tr;
   } else {
-    o.head = hrow, o.q = qt * a.tq + R;
+    o.head = hrow, o.q = tile_query(a.hm[hrow], __builtin_ctz(a.tq), qt, R);
   }
   return o;
 }
@@ -692,10 +692,13 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
     const int head_w = a.pack ? hrow * a.G + (ilv ? 0 : (32 * wave) / a.tr) : hrow;
     const int head = ilv ? head_w + (32 * wave + n) % a.G : head_w;
     const int qbase = a.pack ? 0 : 32 * wave;
-    const int64_t q0 = ilv ? (int64_t)qt * a.tr + (32 * wave) / a.G
-                           : (a.pack ? (int64_t)qt * a.tr + (32 * wave) % a.tr : (int64_t)qt * a.tq + 32 * wave);
-    const int qd = ilv ? n / a.G : n;  // the lane's query is q0 + qd
     const HeadMeta hm = a.hm[head_w];
+    // (a tile that merges query blocks may take them interleaved: its
+    // 32-row slices then lie in different places of the sequence)
+    const int64_t q0 = ilv ? (int64_t)qt * a.tr + (32 * wave) / a.G
+                           : (a.pack ? (int64_t)qt * a.tr + (32 * wave) % a.tr
+                                     : tile_query(hm, __builtin_ctz(a.tq), qt, 32 * wave));
+    const int qd = ilv ? n / a.G : n;  // the lane's query is q0 + qd
     const int64_t qpos = q0 + qd;
     const bool qvalid = qpos < a.Sq;
     // A wave none of whose rows exist skips the arithmetic (it still loads

@@ -175,10 +175,11 @@ __global__ __launch_bounds__(2 * TQ, TQ == 128 ? 2 : 1) void k_bwd_dq(BwdArgs a)
   const int head = a.pack ? hrow * a.G + (32 * wave) / a.tr : hrow;
   const int g = (a.pack ? hrow * a.G : hrow) / a.G;
   const int qbase = a.pack ? 0 : 32 * wave;
-  const int64_t q0 = a.pack ? (int64_t)qt * a.tr + (32 * wave) % a.tr : (int64_t)qt * a.tq + 32 * wave;
+  const HeadMeta hm = a.hm[head];
+  // (through the query-block interleave of a merged tile)
+  const int64_t q0 = a.pack ? (int64_t)qt * a.tr + (32 * wave) % a.tr : tile_query(hm, __builtin_ctz(a.tq), qt, 32 * wave);
   const int64_t qpos = q0 + n;
   const bool qvalid = qpos < a.Sq;
-  const HeadMeta hm = a.hm[head];
   (void)WAVES;
 
   // Q and dO rows as B operands (lane: query n, dims 16c + 8hh .. +8); Delta.

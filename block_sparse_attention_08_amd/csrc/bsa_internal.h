@@ -21,8 +21,32 @@ struct HeadMeta {
   int64_t mask_off;  // offset of this head's [nqb][nkb] mask within one mask batch
   int64_t row_off;   // number of logical rows of the heads before this one
   int32_t nqb, nkb, bq, bk;
-  int32_t lq, lk, mk, pad;
+  int32_t lq, lk, mk;
+  int32_t lqil;      // log2 of the query-block interleave (0: consecutive blocks)
 };
+
+// Query-block interleave candidates: s = 1, 2, 4, 8 for 128-row tiles that
+// merge query blocks of 32 or 64 rows (non-union plans).
+constexpr int kQilCands = 4;
+
+// Logical query block of sub-block iq of physical tile t when a tile merges
+// 2^lm blocks with interleave 2^ls: in each full group of 2^(ls+lm) blocks,
+// tile t takes the blocks t mod 2^ls apart by 2^ls; blocks past the last
+// full group are merged consecutively. A partition of the head's nq blocks.
+__host__ __device__ inline int64_t qblock_of(int64_t t, int64_t iq, int ls, int lm, int64_t nq) {
+  const int lg = ls + lm;
+  const int64_t full = nq >> lg;
+  if (t < (full << ls)) return ((t >> ls) << lg) + (iq << ls) + (t & ((int64_t(1) << ls) - 1));
+  return (full << lg) + ((t - (full << ls)) << lm) + iq;
+}
+
+// Query position of row R (0 .. tq-1) of physical tile qt of a non-packed
+// row of the head with metadata m (ltq = log2 tq).
+__host__ __device__ inline int64_t tile_query(const HeadMeta &m, int ltq, int64_t qt, int R) {
+  if (m.lqil == 0) return (qt << ltq) + R;
+  const int64_t qb = qblock_of(qt, R >> m.lq, m.lqil, ltq - m.lq, m.nqb);
+  return (qb << m.lq) + (R & ((1 << m.lq) - 1));
+}
 
 // Counters written on the device by the planner.
 enum { CNT_ENT = 0, CNT_ITEMS = 1, CNT_SLOTS = 2, CNT_COMB = 3, CNT_BADPAGE = 4, CNT_N = 8 };
@@ -41,6 +65,8 @@ struct Plan {
   int32_t uni, paged, P, pps, npages, bcast;
   float scale;
   std::vector<int32_t> bq, bk;
+  std::vector<int32_t> qil;          // query-block interleave per head (1 = consecutive)
+  std::vector<int64_t> qil_cost;     // [Hq][kQilCands] key blocks listed per candidate
   // regime and geometry
   Regime rg;
   int32_t tr;  // query positions per physical row
@@ -57,6 +83,7 @@ struct Plan {
   size_t pre_bytes = 0, arena_bytes = 0;
   HeadMeta *hmeta;
   unsigned long long *feat_dev;
+  unsigned long long *qil_dev;  // [Hq][kQilCands] interleave costs (mask plans)
   int32_t *row_feat;  // per logical row: selected blocks, effective blocks
   int32_t *counters;
   uint8_t *uni_bits;
@@ -158,6 +185,8 @@ __host__ __device__ inline bool acsr_in_run(const bsa_acsr_run &u, int64_t f, in
 // work), and the per-head mask features [Hq][4] counted from the runs.
 bsa_status acsr_check(const bsa_problem &pr, const bsa_acsr_head *heads);
 void acsr_features(const bsa_problem &pr, const bsa_acsr_head *heads, int64_t *out);
+// Query-block interleave costs [Hq][kQilCands] counted from the runs.
+void acsr_qil_costs(const bsa_problem &pr, const bsa_acsr_head *heads, int64_t *out);
 // Planner side of an ACSR plan: head metadata and descriptors to the device
 // through kernel arguments (no host buffer has to outlive the call), features
 // on the host.

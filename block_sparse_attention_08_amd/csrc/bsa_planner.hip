@@ -147,6 +147,46 @@ __global__ void k_head_features(const int32_t *__restrict__ rowf, const HeadMeta
   }
 }
 
+// Query-block interleave costs: one wave per (mask batch, head, candidate
+// interleave s = 2^c, 128-row tile); it counts the key blocks that some
+// query block of the tile selects (the mask as given) and adds the count to
+// cost[h][c] (integer atomics: the sums do not depend on their order). Only
+// heads whose 32- or 64-row blocks merge into 128-row tiles, and only
+// candidates with s * mq <= nq, are counted; the host picks the cheapest.
+__global__ void k_qil_cost(const uint8_t *__restrict__ mask, const HeadMeta *__restrict__ hm, int Hq,
+                           int nbm, int64_t mask_bstride, const int64_t *__restrict__ wave_off,
+                           int64_t nwaves, unsigned long long *__restrict__ cost) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wv = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 6;
+  if (wv >= nwaves) return;
+  // wave_off[h * kQilCands + c] = first wave of (head, candidate), over all mask batches
+  int lo = 0, hi = Hq * kQilCands - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (wave_off[mid] <= wv) lo = mid;
+    else hi = mid - 1;
+  }
+  const int h = lo / kQilCands, c = lo % kQilCands;
+  const HeadMeta m = hm[h];
+  const int lm = 7 - __builtin_ctz(m.bq);  // 128-row tiles
+  const int64_t ntiles = ((int64_t)m.nqb + (1 << lm) - 1) >> lm;
+  const int64_t k = wv - wave_off[lo];
+  const int bm = (int)(k / ntiles);
+  const int64_t t = k % ntiles;
+  const uint8_t *mb = mask + bm * mask_bstride + m.mask_off;
+  int cnt = 0;
+  for (int64_t kb = lane; kb < m.nkb; kb += 64) {
+    int any = 0;
+    for (int iq = 0; iq < (1 << lm) && !any; ++iq) {
+      const int64_t qb = qblock_of(t, iq, c, lm, m.nqb);
+      any = qb < m.nqb && mb[qb * m.nkb + kb] != 0;
+    }
+    cnt += any;
+  }
+  cnt = wave_sum(cnt);
+  if (lane == 0 && cnt) atomicAdd(&cost[h * kQilCands + c], (unsigned long long)cnt);
+}
+
 // Count page-table entries that the keys [0, Skv) use and that point outside
 // the pool.
 __global__ void k_check_pages(const int32_t *__restrict__ table, int B, int pps, int64_t used,
@@ -194,7 +234,7 @@ __device__ __forceinline__ uint32_t live_bits(const MapArgs &a, int bm, int h, i
   const uint8_t *u = a.uni ? a.U + ((int64_t)bm * a.Hkv + g) * a.unkb : nullptr;
   uint32_t live = 0;
   for (int iq = 0; iq < mq; ++iq) {
-    const int64_t qb = bq < a.tq ? qt * mq + iq : (qt << ltq) >> lbq;
+    const int64_t qb = bq < a.tq ? qblock_of(qt, iq, m.lqil, ltq - lbq, m.nqb) : (qt << ltq) >> lbq;
     if (!u && qb >= m.nqb) continue;
     int64_t first[BSA_ACSR_MAX_RUNS];
     const int nruns = a.acsr ? a.acsr[h].num_runs : 0;
@@ -210,7 +250,7 @@ __device__ __forceinline__ uint32_t live_bits(const MapArgs &a, int bm, int h, i
         continue;
       }
       if (!u && a.causal) {
-        const int64_t q0 = qt * a.tq + iq * aq;
+        const int64_t q0 = bq < a.tq ? qb * bq : qt * a.tq;
         const int64_t qlast = min(q0 + aq, a.Sq) - 1;
         if (kt * a.tk + ik * ak > qlast + a.off) continue;
       }
@@ -536,8 +576,8 @@ __device__ __forceinline__ void tile_live(const KvIndexArgs &a, int lo, int hi, 
 // may see a key of the group: its row's list holds one of the tiles (in
 // union mode the group's table does), its queries exist, it is causally
 // feasible for the group's first key, and a live bit of its query
-// sub-blocks is set. Chunks are emitted in (head, query) order with their
-// first query, a packed word (head within the group | chunk index within
+// sub-blocks is set. Chunks are emitted in (head, tile, chunk) order with
+// their first query, a packed word (head within the group | chunk index within
 // the plan row << 8 | lq << 11 | lk << 16 | mk << 21) and the NKT live words.
 // EMIT = false counts them.
 template <bool EMIT, int NKT>
@@ -603,7 +643,8 @@ __global__ void k_kv_chunks(KvIndexArgs a) {
           rows &= rows - 1;
           uint32_t rl[NKT];
           for (int t = 0; t < NKT; ++t) rl[t] = __shfl(lv[t], bit);
-          const int64_t q0 = (qb + bit) * a.tq + 32 * lane;  // lane = chunk of the row
+          // lane = chunk of the row; its first query, through the interleave
+          const int64_t q0 = lane < cpr ? tile_query(m, __builtin_ctz(a.tq), qb + bit, 32 * lane) : a.Sq;
           bool ok = lane < cpr && feasible(q0);
           if (ok) {
             const int iq0 = (32 * lane) >> m.lq;
@@ -618,49 +659,6 @@ __global__ void k_kv_chunks(KvIndexArgs a) {
     }
   }
   if (!EMIT && lane == 0) a.cnt[bk] = (int32_t)run;
-}
-
-// Live-bit geometry of each head for tiles of tq x tk: query sub-blocks of
-// min(bq, tq) rows (one sub-block in union mode, whose bits are per key
-// sub-block only), key sub-blocks of min(bk, tk) keys, mk key sub-blocks per
-// tile. Block sizes are powers of two.
-__global__ void k_live_geom(HeadMeta *hm, int Hq, int tq, int tk, int uni) {
-  for (int h = threadIdx.x; h < Hq; h += blockDim.x) {
-    const int aq = min(hm[h].bq, tq), ak = min(hm[h].bk, tk);
-    hm[h].lq = uni ? 30 : __ffs(aq) - 1;
-    hm[h].lk = __ffs(ak) - 1;
-    hm[h].mk = tk / ak;
-  }
-}
-
-bsa_status plan_features(Plan &p, const uint8_t *mask, const int32_t *page_table) {
-  hipStream_t s = p.stream;
-  int64_t rows_per_bm = 0, mask_bstride = 0;
-  std::vector<HeadMeta> &hm = p.hmeta_host;
-  hm.assign(p.Hq, HeadMeta{});
-  for (int h = 0; h < p.Hq; ++h) {
-    const int64_t nq = (p.Sq + p.bq[h] - 1) / p.bq[h], nk = (p.Skv + p.bk[h] - 1) / p.bk[h];
-    hm[h] = HeadMeta{mask_bstride, rows_per_bm, (int32_t)nq, (int32_t)nk, p.bq[h], p.bk[h], 0, 0, 0, 0};
-    rows_per_bm += nq;
-    mask_bstride += nq * nk;
-  }
-  HIP_TRY(hipMemcpyAsync(p.hmeta, hm.data(), sizeof(HeadMeta) * p.Hq, hipMemcpyHostToDevice, s));
-  if (p.uni && p.unkb > 0)
-    hipLaunchKernelGGL(k_union, dim3(grid_for((int64_t)p.nbm * p.Hkv * p.unkb)), dim3(kThreads), 0,
-                       s, mask, p.hmeta, mask_bstride, p.Hkv, p.G, (int)p.nbm, p.unkb, p.uni_bits);
-  if (p.nbm * rows_per_bm > 0)
-    hipLaunchKernelGGL(k_row_features, dim3(grid_for(p.nbm * rows_per_bm * 64)), dim3(kThreads), 0,
-                       s, mask, p.hmeta, p.Hq, p.Hkv, p.G, (int)p.nbm, rows_per_bm, mask_bstride,
-                       p.uni ? p.uni_bits : nullptr, p.unkb, p.causal, p.off, p.Sq, p.row_feat);
-  hipLaunchKernelGGL(k_head_features, dim3((unsigned)(p.nbm * p.Hq)), dim3(kThreads), 0, s,
-                     p.row_feat, p.hmeta, p.Hq, rows_per_bm, p.feat_dev);
-  if (p.paged && p.Skv > 0) {
-    const int64_t used = (p.Skv + p.P - 1) / p.P;
-    hipLaunchKernelGGL(k_check_pages, dim3(grid_for(p.B * used)), dim3(kThreads), 0, s, page_table,
-                       p.B, p.pps, used, p.npages, p.counters);
-  }
-  HIP_TRY(hipGetLastError());
-  return BSA_OK;
 }
 
 // Small host data to device memory through kernel arguments: the arguments
@@ -689,6 +687,59 @@ static bsa_status put_async(void *dst, const void *src, size_t bytes, hipStream_
   return BSA_OK;
 }
 
+bsa_status plan_features(Plan &p, const uint8_t *mask, const int32_t *page_table) {
+  hipStream_t s = p.stream;
+  int64_t rows_per_bm = 0, mask_bstride = 0;
+  std::vector<HeadMeta> &hm = p.hmeta_host;
+  hm.assign(p.Hq, HeadMeta{});
+  for (int h = 0; h < p.Hq; ++h) {
+    const int64_t nq = (p.Sq + p.bq[h] - 1) / p.bq[h], nk = (p.Skv + p.bk[h] - 1) / p.bk[h];
+    hm[h] = HeadMeta{mask_bstride, rows_per_bm, (int32_t)nq, (int32_t)nk, p.bq[h], p.bk[h], 0, 0, 0, 0};
+    rows_per_bm += nq;
+    mask_bstride += nq * nk;
+  }
+  HIP_TRY(hipMemcpyAsync(p.hmeta, hm.data(), sizeof(HeadMeta) * p.Hq, hipMemcpyHostToDevice, s));
+  if (p.uni && p.unkb > 0)
+    hipLaunchKernelGGL(k_union, dim3(grid_for((int64_t)p.nbm * p.Hkv * p.unkb)), dim3(kThreads), 0,
+                       s, mask, p.hmeta, mask_bstride, p.Hkv, p.G, (int)p.nbm, p.unkb, p.uni_bits);
+  if (p.nbm * rows_per_bm > 0)
+    hipLaunchKernelGGL(k_row_features, dim3(grid_for(p.nbm * rows_per_bm * 64)), dim3(kThreads), 0,
+                       s, mask, p.hmeta, p.Hq, p.Hkv, p.G, (int)p.nbm, rows_per_bm, mask_bstride,
+                       p.uni ? p.uni_bits : nullptr, p.unkb, p.causal, p.off, p.Sq, p.row_feat);
+  hipLaunchKernelGGL(k_head_features, dim3((unsigned)(p.nbm * p.Hq)), dim3(kThreads), 0, s,
+                     p.row_feat, p.hmeta, p.Hq, rows_per_bm, p.feat_dev);
+  // Query-block interleave costs (non-union plans; the tile shape is not yet
+  // known, so 128-row tiles are assumed and the host keeps interleave 1 for
+  // any other shape). Wave offsets per (head, candidate) go as kernel
+  // arguments through a small device array written by k_put.
+  if (!p.uni) {
+    std::vector<int64_t> woff(p.Hq * kQilCands + 1, 0);
+    int64_t nw = 0;
+    for (int h = 0; h < p.Hq; ++h) {
+      const int64_t bq = p.bq[h], nq = (p.Sq + bq - 1) / bq;
+      for (int c = 0; c < kQilCands; ++c) {
+        woff[h * kQilCands + c] = nw;
+        const int64_t mq = bq < 128 ? 128 / bq : 1;
+        if (bq >= 32 && bq < 128 && (int64_t(1) << c) * mq <= nq) nw += p.nbm * ((nq + mq - 1) / mq);
+      }
+    }
+    woff[p.Hq * kQilCands] = nw;
+    if (nw > 0) {
+      int64_t *woff_dev = (int64_t *)(p.qil_dev + (size_t)p.Hq * kQilCands);
+      if (bsa_status st = put_async(woff_dev, woff.data(), sizeof(int64_t) * woff.size(), s)) return st;
+      hipLaunchKernelGGL(k_qil_cost, dim3(grid_for(nw * 64)), dim3(kThreads), 0, s, mask, p.hmeta, p.Hq,
+                         (int)p.nbm, mask_bstride, (const int64_t *)woff_dev, nw, p.qil_dev);
+    }
+  }
+  if (p.paged && p.Skv > 0) {
+    const int64_t used = (p.Skv + p.P - 1) / p.P;
+    hipLaunchKernelGGL(k_check_pages, dim3(grid_for(p.B * used)), dim3(kThreads), 0, s, page_table,
+                       p.B, p.pps, used, p.npages, p.counters);
+  }
+  HIP_TRY(hipGetLastError());
+  return BSA_OK;
+}
+
 bsa_status plan_features_acsr(Plan &p, const bsa_acsr_head *heads, bsa_acsr_head *dev_heads,
                               const bsa_problem &pr) {
   std::vector<HeadMeta> &hm = p.hmeta_host;
@@ -707,6 +758,8 @@ bsa_status plan_features_acsr(Plan &p, const bsa_acsr_head *heads, bsa_acsr_head
   p.acsr = dev_heads;
   p.feat.assign(4 * (size_t)p.Hq, 0);
   acsr_features(pr, heads, p.feat.data());
+  p.qil_cost.assign((size_t)kQilCands * p.Hq, 0);
+  acsr_qil_costs(pr, heads, p.qil_cost.data());
   return BSA_OK;
 }
 
@@ -743,21 +796,16 @@ bsa_status plan_build(Plan &p, const uint8_t *mask, const int32_t *page_table, v
   if ((size_t)(sp - (uint8_t *)scratch) > scratch_bytes)
     return fail(BSA_ERR_HIP, "planner scratch too small");
 
-  // Live-bit decoding per head now that the tile shape is known: written on
-  // the device for mask plans (so no host upload sits between the read-back
-  // and the mapping kernels); an ACSR plan has had no read-back and sends
-  // the finished head metadata in one go.
-  if (p.acsr) {
-    for (int h = 0; h < p.Hq; ++h) {
-      HeadMeta &m = p.hmeta_host[h];
-      const int aq = std::min(m.bq, p.rg.tq), ak = std::min(m.bk, p.rg.tk);
-      m.lq = __builtin_ctz(aq), m.lk = __builtin_ctz(ak), m.mk = p.rg.tk / ak;
-    }
-    if (bsa_status st = put_async(p.hmeta, p.hmeta_host.data(), sizeof(HeadMeta) * p.Hq, s)) return st;
-  } else {
-    hipLaunchKernelGGL(k_live_geom, dim3(1), dim3(kThreads), 0, s, p.hmeta, p.Hq, p.rg.tq, p.rg.tk,
-                       (int)p.uni);
+  // Live-bit decoding and query-block interleave per head, now that the
+  // tile shape is known, sent as kernel arguments (no host buffer has to
+  // outlive the call).
+  for (int h = 0; h < p.Hq; ++h) {
+    HeadMeta &m = p.hmeta_host[h];
+    const int aq = std::min(m.bq, p.rg.tq), ak = std::min(m.bk, p.rg.tk);
+    m.lq = p.uni ? 30 : __builtin_ctz(aq), m.lk = __builtin_ctz(ak), m.mk = p.rg.tk / ak;
+    m.lqil = __builtin_ctz(p.qil[h]);
   }
+  if (bsa_status st = put_async(p.hmeta, p.hmeta_host.data(), sizeof(HeadMeta) * p.Hq, s)) return st;
 
   MapArgs m{};
   m.mask = mask, m.U = p.uni_bits, m.acsr = p.acsr, m.hm = p.hmeta, m.page_table = page_table;

@@ -35,6 +35,7 @@ import numpy as np
 
 # Workload ids used as the first word of every SeedSequence.
 WID_TINY, WID_VIDEO, WID_PREFILL, WID_AFFINE, WID_LONG, WID_DECODE, WID_RANDOM = 1, 2, 3, 4, 5, 6, 9
+WID_PERIODIC = 10
 # Second word: which stream of random numbers.
 STREAM_QKV, STREAM_MASK, STREAM_PAGES, STREAM_DOUT = 0, 1, 2, 3
 
@@ -470,6 +471,31 @@ def long_video(heads: int = 40, grid=(30, 48, 80), d: int = 128, p_empty: float 
         blocks.append(m.astype(np.uint8))
     return Workload("long_video", 1, heads, heads, s, s, d, "bf16", bsz, bsz, _concat(blocks),
                     seed=(WID_LONG, seed))
+
+
+# --------------------------------------------------------------------------
+# Periodic rows (dilated patterns of several periods) with random blocks
+# --------------------------------------------------------------------------
+def periodic(batch: int = 2, bq=(32, 64, 64, 32), sq: int = 2048, skv: int = 1024, bk: int = 64,
+             d: int = 64, periods=(2, 4, 8, 1), p_random: float = 0.03, causal: bool = False,
+             causal_offset: int = 0, seed: int = 0) -> Workload:
+    """Per head h, key block kb is selected in query block qb when
+    (kb - qb) is a multiple of periods[h] (period 1: a band |kb - qb/2| <= 2),
+    plus Bernoulli(p_random) blocks; one mask per batch element."""
+    g = _rng(WID_PERIODIC, seed, STREAM_MASK)
+    hq = len(bq)
+    blocks = []
+    for _ in range(batch):
+        for h in range(hq):
+            nq, nk = cdiv(sq, bq[h]), cdiv(skv, bk)
+            qb = np.arange(nq)[:, None]
+            kb = np.arange(nk)[None, :]
+            per = periods[h]
+            m = ((kb - qb) % per == 0) if per > 1 else (np.abs(kb - qb // 2) <= 2)
+            m = m | (g.random((nq, nk)) < p_random)
+            blocks.append(m.astype(np.uint8))
+    return Workload("periodic", batch, hq, hq, sq, skv, d, "bf16", list(bq), [bk] * hq, _concat(blocks),
+                    causal=causal, causal_offset=causal_offset, seed=(WID_PERIODIC, seed))
 
 
 # --------------------------------------------------------------------------

@@ -583,6 +583,42 @@ static int item_cmp(const void *a, const void *b) {
   return x[1] < y[1] ? -1 : (x[1] > y[1]);
 }
 
+/* Query-block interleave: physical query tile t of a head whose logical
+ * blocks merge mq to a tile, with interleave s, gathers the blocks
+ *   (t / s) * s * mq + iq * s + t % s      (iq = 0 .. mq-1)
+ * while t lies in one of the floor(nq / (s * mq)) full groups of s * mq
+ * blocks, and consecutive blocks after them (s = 1 is the plain merge). The
+ * tiles are a partition of the head's query blocks, so the mapping keeps
+ * every selected interaction (Tessera, abstract: logical blocks retained,
+ * combined or subdivided while preserving the specified interactions). */
+static int64_t qblock(int64_t t, int64_t iq, int64_t s, int64_t mq, int64_t nq) {
+  const int64_t g = s * mq, full = nq / g;
+  if (t < full * s) return (t / s) * g + iq * s + t % s;
+  return full * g + (t - full * s) * mq + iq;
+}
+
+/* Key blocks listed by the tiles of one head under interleave s: for every
+ * mask batch and tile, the number of key blocks that some query block of
+ * the tile selects (the mask as given, before any causal bound). */
+static int64_t interleave_cost(const ref_problem *p, const uint8_t *mask, const int64_t *moff,
+                               int h, int64_t mq, int64_t s) {
+  const int64_t nq = ceil_div(p->sq, p->bq[h]), nk = ceil_div(p->skv, p->bk[h]);
+  int64_t cost = 0;
+  for (int bm = 0; bm < mask_batches(p); ++bm) {
+    const uint8_t *m = mask + moff[bm * p->hq + h];
+    for (int64_t t = 0; t < ceil_div(nq, mq); ++t)
+      for (int64_t kb = 0; kb < nk; ++kb) {
+        int any = 0;
+        for (int64_t iq = 0; iq < mq && !any; ++iq) {
+          const int64_t qb = qblock(t, iq, s, mq, nq);
+          if (qb < nq && m[qb * nk + kb]) any = 1;
+        }
+        cost += any;
+      }
+  }
+  return cost;
+}
+
 int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_table,
              const char *lut_text, const int32_t *force, uint8_t *image, size_t *bytes) {
   if (check_problem(p) || !bytes || (p->paged && !page_table)) return -1;
@@ -679,6 +715,23 @@ int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_tabl
   const int64_t nqt = ceil_div(p->sq, tr);
   const int nlb = (p->paged || !p->mask_broadcast) ? p->batch : 1;
 
+  /* 2b. Query-block interleave per head: 128-row tiles that merge query
+   * blocks of 32 rows or more (no union) take the interleave s in
+   * {1, 2, 4, 8} (s * mq <= the head's query blocks) whose tiles list the
+   * fewest key blocks, the smallest s on ties; every other head takes 1. */
+  int32_t *qil = (int32_t *)malloc(sizeof(int32_t) * p->hq);
+  for (int h = 0; h < p->hq; ++h) {
+    qil[h] = 1;
+    const int64_t bq = p->bq[h], nq = ceil_div(p->sq, bq);
+    if (p->gqa_union || tq != 128 || bq >= tq || bq < 32) continue;
+    const int64_t mq = tq / bq;
+    int64_t best = interleave_cost(p, mask, moff, h, mq, 1);
+    for (int64_t s = 2; s <= 8 && s * mq <= nq; s *= 2) {
+      const int64_t c = interleave_cost(p, mask, moff, h, mq, s);
+      if (c < best) best = c, qil[h] = (int32_t)s;
+    }
+  }
+
   /* 3. Physical mapping: per list, ascending key tiles with live bits over the
    * merged logical sub-blocks (keep / merge / subdivide). */
   int64_t nlists = p->gqa_union ? (int64_t)nlb * p->hkv : (int64_t)nlb * p->hq * nqt;
@@ -710,13 +763,13 @@ int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_tabl
       uint32_t live = 0;
       for (int64_t iq = 0; iq < mq; ++iq)
         for (int64_t ik = 0; ik < mk; ++ik) {
-          int64_t qb = bq < tq ? qt * mq + iq : (qt * tq) / bq;
+          int64_t qb = bq < tq ? qblock(qt, iq, qil[h], mq, nq) : (qt * tq) / bq;
           int64_t kb = bk < tk ? kt * mk + ik : (kt * tk) / bk;
           if (kb >= nk || (!u && qb >= nq)) continue;
           if (!(u ? u[kb] : m[qb * nk + kb])) continue;
           if (!u && p->causal) {
             /* Drop a sub-block whose first key lies after its last query. */
-            int64_t q0 = qt * tq + iq * aq;
+            int64_t q0 = bq < tq ? qb * bq : qt * tq;
             int64_t qlast = (q0 + aq < p->sq ? q0 + aq : p->sq) - 1;
             if (kt * tk + ik * ak > qlast + p->causal_offset) continue;
           }
@@ -737,7 +790,7 @@ int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_tabl
   }
   list_off[nlists] = nent;
   if (nent > INT32_MAX) {
-    free(moff), free(uni), free(feat), free(list_off), free(ekt), free(epage), free(elive);
+    free(moff), free(uni), free(feat), free(list_off), free(ekt), free(epage), free(elive), free(qil);
     return -3;
   }
 
@@ -816,6 +869,7 @@ int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_tabl
   put(&o, hdr, sizeof hdr);
   put(&o, p->bq, sizeof(int32_t) * p->hq);
   put(&o, p->bk, sizeof(int32_t) * p->hq);
+  put(&o, qil, sizeof(int32_t) * p->hq);
   put(&o, feat, sizeof(int64_t) * 4 * nbm * p->hq);
   for (int64_t l = 0; l <= nlists; ++l) {
     int32_t x = (int32_t)list_off[l];
@@ -831,7 +885,7 @@ int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_tabl
   int rc = (image && o.n > *bytes) ? -4 : 0;
   *bytes = o.n;
   free(moff), free(uni), free(feat), free(list_off), free(ekt), free(epage), free(elive);
-  free(row_ent), free(items), free(comb);
+  free(row_ent), free(items), free(comb), free(qil);
   return rc;
 }
 

@@ -3,7 +3,8 @@ the planner tests. Test infrastructure: written from the plan format, shares
 no code with either planner.
 
 Image layout (little-endian): the 8-byte magic ``BSAPLAN1``; 40 int64 header
-words; int32 bq[Hq], bk[Hq]; int64 features[mask batches][Hq][4]; int32
+words; int32 bq[Hq], bk[Hq], query-block interleave[Hq]; int64
+features[mask batches][Hq][4]; int32
 list_off[nlists + 1]; int32 kt[nent]; int32 page[nent] (paged only); uint32
 live[nent]; int32 rows[nrows][2]; int32 items[nitems][4]; int32
 combine[ncomb][3].
@@ -25,6 +26,7 @@ class Plan:
     h: dict
     bq: np.ndarray
     bk: np.ndarray
+    qil: np.ndarray
     feat: np.ndarray
     list_off: np.ndarray
     kt: np.ndarray
@@ -49,7 +51,7 @@ def decode(img: bytes) -> Plan:
         return a
 
     hq = h["hq"]
-    bq, bk = take(np.int32, hq), take(np.int32, hq)
+    bq, bk, qil = take(np.int32, hq), take(np.int32, hq), take(np.int32, hq)
     nbm = 1 if h["broadcast"] else h["batch"]
     feat = take(np.int64, nbm * hq * 4).reshape(nbm, hq, 4)
     list_off = take(np.int32, h["nlists"] + 1)
@@ -60,14 +62,28 @@ def decode(img: bytes) -> Plan:
     items = take(np.int32, 4 * h["nitems"]).reshape(-1, 4)
     comb = take(np.int32, 3 * h["ncomb"]).reshape(-1, 3)
     assert pos == len(img), (pos, len(img))
-    return Plan(h, bq, bk, feat, list_off, kt, page, live, rows, items, comb)
+    return Plan(h, bq, bk, qil, feat, list_off, kt, page, live, rows, items, comb)
+
+
+def qblock(t: int, iq: int, s: int, mq: int, nq: int) -> int:
+    """Logical query block of sub-block iq of tile t under interleave s
+    (written from the plan format: full groups of s*mq blocks hold s tiles
+    whose blocks are s apart; consecutive blocks after the last full group)."""
+    g = s * mq
+    full = nq // g
+    if t < full * s:
+        return (t // s) * g + iq * s + t % s
+    return full * g + (t - full * s) * mq + iq
 
 
 def row_geometry(p: Plan, r: int):
-    """(b, list of (head, q0, q1)) covered by physical row r.
+    """(b, list of (head, q0, q1, iq)) covered by physical row r: query rows
+    [q0, q1) of head, which are query sub-block iq of the tile (None: the
+    sub-block follows from the position, as in a contiguous tile).
 
     A packed row covers all heads of a group over Tq/G positions; the kernel's
-    four 32-row waves take heads in order.
+    four 32-row waves take heads in order. A tile that merges query blocks
+    lists each merged block, at the position the interleave gives it.
     """
     h = p.h
     nqt = h["nqt"]
@@ -77,21 +93,31 @@ def row_geometry(p: Plan, r: int):
     if h["pack"]:
         tr = h["tq"] // gs
         q0, q1 = qt * tr, min(h["sq"], (qt + 1) * tr)
-        return b, [(hh * gs + j, q0, q1) for j in range(gs)]
+        return b, [(hh * gs + j, q0, q1, None) for j in range(gs)]
+    bq = int(p.bq[hh])
+    if not h["union"] and bq < h["tq"]:
+        mq, nq = h["tq"] // bq, -(-h["sq"] // bq)
+        out = []
+        for iq in range(mq):
+            qb = qblock(qt, iq, int(p.qil[hh]), mq, nq)
+            if qb < nq:
+                out.append((hh, qb * bq, min(h["sq"], (qb + 1) * bq), iq))
+        return b, out
     q0, q1 = qt * h["tq"], min(h["sq"], (qt + 1) * h["tq"])
-    return b, [(hh, q0, q1)]
+    return b, [(hh, q0, q1, None)]
 
 
-def expand_row(p: Plan, r: int, head: int, q0: int, q1: int) -> np.ndarray:
+def expand_row(p: Plan, r: int, head: int, q0: int, q1: int, iq0=None) -> np.ndarray:
     """Element-level allowed matrix [q1-q0][skv] that the plan makes the kernel
-    compute for one head of row r: live bit of the sub-block, causal, bounds."""
+    compute for one head of row r: live bit of the sub-block, causal, bounds.
+    iq0: the query sub-block of rows [q0, q1) when given by row_geometry."""
     h = p.h
     tq, tk, skv = h["tq"], h["tk"], h["skv"]
     bq, bk = int(p.bq[head]), int(p.bk[head])
     union = h["union"]
     gs = h["hq"] // h["hkv"]
     tr = tq // gs if h["pack"] else tq
-    qt = q0 // tr
+    qt = (r % h["nqt"])
     out = np.zeros((q1 - q0, skv), bool)
     e0, e1 = p.rows[r]
     aq = tq if union else min(bq, tq)
@@ -104,8 +130,10 @@ def expand_row(p: Plan, r: int, head: int, q0: int, q1: int) -> np.ndarray:
         kj = np.arange(k0, k1)
         if union:
             iq = np.zeros_like(qi)
+        elif iq0 is not None:
+            iq = np.full_like(qi, iq0)
         else:
-            iq = (qi - qt * tq) // aq
+            iq = (qi - qt * tr) // aq
         ik = (kj - k0) // ak
         bit = (live >> (iq[:, None] * mk + ik[None, :])) & 1
         ok = bit.astype(bool)

@@ -111,6 +111,7 @@ CASES = {
                                           density=0.0, seed=407),
     "tiny_video": lambda: W.video_dit(heads=2, grid=(16, 6, 12), seed=1),
     "tiny_affine32": lambda: W.affine(bs=32, batch=2, heads=3, s=1024, window=128),
+    "periodic_interleave": lambda: W.periodic(sq=1000, skv=700, causal=True, causal_offset=80, seed=5),
 }
 
 

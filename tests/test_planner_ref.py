@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from block_sparse_attention_08_amd import workloads as W
-from tests.plan_image import decode, expand_row, row_geometry
+from tests.plan_image import decode, expand_row, qblock, row_geometry
 from tests.test_oracle_pins import element_mask
 
 
@@ -55,8 +55,8 @@ def check_worklist(p):
 def check_elements(w, p):
     for r in range(p.h["nrows"]):
         b, heads = row_geometry(p, r)
-        for head, q0, q1 in heads:
-            got = expand_row(p, r, head, q0, q1)
+        for head, q0, q1, iq in heads:
+            got = expand_row(p, r, head, q0, q1, iq)
             want = element_mask(w, b, head)[q0:q1]
             assert np.array_equal(got, want), (r, head, q0)
 
@@ -80,11 +80,14 @@ def test_exhaustive_4x4_masks(ref):
         ent_list = np.repeat(np.arange(h["nlists"]), np.diff(p.list_off))
         b_of = ent_list // nqt
         qt_of = ent_list % nqt
+        s_of = int(p.qil[0])
         for iq in range(mq):
             for ik in range(mk):
                 bit = (p.live >> np.uint32(iq * mk + ik)) & 1
                 sel = bit.astype(bool)
-                a = qt_of[sel] * mq + iq
+                # (tiles merge query sub-blocks through the head's interleave)
+                a = np.array([qblock(int(t), iq, s_of, mq, naq) if bq < 128 else int(t) * mq + iq
+                              for t in qt_of[sel]], np.int64)
                 c = p.kt[sel] * mk + ik
                 np.add.at(cov, (b_of[sel], a, c), 1)
         blk = allm.reshape(B, 4, 4)
@@ -251,3 +254,66 @@ def test_features_in_header(ref):
     assert p.h["density_pm"] == 1000 * nnz // tot
     imb = max(16 * f[b, h, 1] * w.nqb(h) // f[b, h, 0] for b in range(2) for h in range(2))
     assert p.h["imb16"] == imb and (p.h["min_bq"], p.h["min_bk"]) == (32, 32)
+
+
+# ---- query-block interleave ----
+
+def interleave_choice(w, h, tq=128):
+    """The interleave the plan specification gives head h, computed here from
+    its definition: among s in {1, 2, 4, 8} with s * mq <= nq, the one whose
+    tiles list the fewest key blocks (summed over mask batches), smallest on
+    ties; 1 for union plans, unmerged heads and blocks under 32 rows."""
+    bq = w.bq[h]
+    if w.gqa_union or bq >= tq or bq < 32:
+        return 1
+    mq, nq = tq // bq, -(-w.sq // bq)
+    masks = [w.head_mask(bm, h).astype(bool) for bm in range(w.mask_batches)]
+
+    def cost(s):
+        nt = -(-nq // mq)
+        qbs = np.array([[qblock(t, iq, s, mq, nq) for iq in range(mq)] for t in range(nt)])
+        tot = 0
+        for m in masks:
+            mp = np.concatenate([m, np.zeros((1, m.shape[1]), bool)])  # row nq: no block
+            tot += int(mp[np.minimum(qbs, nq)].any(1).sum())
+        return tot
+
+    best, bc = 1, cost(1)
+    for s in (2, 4, 8):
+        if s * mq > nq:
+            break
+        c = cost(s)
+        if c < bc:
+            best, bc = s, c
+    return best
+
+
+def test_interleave_dilated_pattern(ref):
+    """A dilated pattern (key block = query block mod 8) gathers query blocks
+    of one residue into a tile: every tile lists each of its key tiles for
+    all its query blocks, half as many entries as contiguous merging."""
+    w = W.affine(bs=64, batch=1, heads=3, s=4096, window=256, d=64)
+    p = decode(ref.plan(w, force=[128, 64, 0, 0, 0]))
+    assert list(p.qil) == [interleave_choice(w, h) for h in range(3)] == [1, 8, 1]
+    check_worklist(p)
+    check_elements(w, p)
+    nqt = p.h["nqt"]
+    for r in range(nqt, 2 * nqt):  # the dilated head: 64 key blocks, 8 per residue
+        e0, e1 = p.rows[r]
+        assert e1 - e0 == 64 // 8
+        assert (p.live[e0:e1] == 3).all()  # both query sub-blocks live in every entry
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_interleave_choice_random(ref, seed):
+    """Heads with planted periodic rows (periods 2, 4, 8) plus noise, merged
+    blocks of 32 and 64 rows, causal or not, per-batch masks: the planner's
+    interleave equals the definition's, and the plan covers the mask exactly."""
+    g = np.random.default_rng(seed)
+    w = W.periodic(sq=2048 + 64 * int(g.integers(0, 5)), causal=bool(seed % 2),
+                   causal_offset=int(g.integers(-200, 300)), seed=seed)
+    p = decode(ref.plan(w, force=[128, 64, seed % 3, 0, 0]))
+    assert list(p.qil) == [interleave_choice(w, h) for h in range(4)]
+    assert max(p.qil) > 1
+    check_worklist(p)
+    check_elements(w, p)
