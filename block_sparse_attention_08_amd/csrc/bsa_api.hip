@@ -1,6 +1,9 @@
 // libbsa C ABI: argument checking, regime lookup table, plan object, forward
 // launch, plan export and statistics.
 #include <algorithm>
+#include <chrono>
+#include <cstdarg>
+#include <cstdlib>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -16,10 +19,91 @@ namespace bsa {
 
 static thread_local std::string g_err;
 
+int log_level() {
+  const char *v = std::getenv("BSA_LOG");
+  return v ? std::max(0, std::min(3, std::atoi(v))) : 0;
+}
+
+bool trace_on() {
+  const char *v = std::getenv("BSA_TRACE");
+  return v && std::atoi(v) > 0;
+}
+
+void log_msg(int level, const char *fmt, ...) {
+  if (level > log_level()) return;
+  char buf[1024];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  std::fprintf(stderr, "[bsa] %s\n", buf);
+}
+
 bsa_status fail(bsa_status s, const std::string &msg) {
   g_err = msg;
+  log_msg(1, "%s: %s", bsa_status_str(s), msg.c_str());
   return s;
 }
+
+// Phase timers of one call (BSA_TRACE=1); inert otherwise. mark() closes the
+// phase that began at the previous mark: it takes the host clock and records
+// an event on the call's stream. report() waits for the last event and prints
+// each phase's host and stream time.
+class Trace {
+ public:
+  Trace(const char *what, hipStream_t s) : what_(what), s_(s), on_(trace_on()) {
+    if (on_) t0_ = std::chrono::steady_clock::now(), mark("start");
+  }
+  ~Trace() {
+    for (auto &m : marks_)
+      if (m.ev) (void)hipEventDestroy(m.ev);
+  }
+  Trace(const Trace &) = delete;
+  Trace &operator=(const Trace &) = delete;
+
+  void mark(const char *phase) {
+    if (!on_) return;
+    Mark m{phase, nullptr, std::chrono::duration<double, std::milli>(
+                               std::chrono::steady_clock::now() - t0_).count()};
+    if (hipEventCreate(&m.ev) != hipSuccess) m.ev = nullptr;
+    if (m.ev && hipEventRecord(m.ev, s_) != hipSuccess) {
+      (void)hipEventDestroy(m.ev);
+      m.ev = nullptr;
+    }
+    marks_.push_back(m);
+  }
+
+  void report(const std::string &detail = "") {
+    if (!on_ || marks_.size() < 2) return;
+    const bool synced = marks_.back().ev && hipEventSynchronize(marks_.back().ev) == hipSuccess;
+    std::string line = std::string("[bsa trace] ") + what_ + (detail.empty() ? "" : " (" + detail + ")") + ":";
+    char buf[160];
+    for (size_t i = 1; i < marks_.size(); ++i) {
+      float ms = -1.f;
+      if (!synced || !marks_[i - 1].ev || !marks_[i].ev ||
+          hipEventElapsedTime(&ms, marks_[i - 1].ev, marks_[i].ev) != hipSuccess)
+        ms = -1.f;
+      std::snprintf(buf, sizeof buf, " %s %.3f ms stream / %.3f ms host;", marks_[i].phase, ms,
+                    marks_[i].host_ms - marks_[i - 1].host_ms);
+      line += buf;
+    }
+    std::snprintf(buf, sizeof buf, " total %.3f ms host",
+                  std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0_).count());
+    std::fprintf(stderr, "%s%s\n", line.c_str(), buf);
+  }
+
+ private:
+  struct Mark {
+    const char *phase;
+    hipEvent_t ev;
+    double host_ms;
+  };
+  const char *what_;
+  hipStream_t s_;
+  bool on_;
+  std::chrono::steady_clock::time_point t0_;
+  std::vector<Mark> marks_;
+};
 
 #define HIP_TRY(expr)                                                          \
   do {                                                                         \
@@ -324,6 +408,7 @@ bsa_status bsa_lut_load(const char *path, bsa_lut_t *out) {
     ss << f.rdbuf();
     auto *l = new bsa_lut_s;
     if (parse_lut(ss.str().c_str(), l) == BSA_OK) {
+      log_msg(2, "lookup table %s: %zu rules", path, l->rules.size());
       *out = l;
       return BSA_OK;
     }
@@ -333,6 +418,7 @@ bsa_status bsa_lut_load(const char *path, bsa_lut_t *out) {
   // Missing or malformed file: the built-in table, with a warning status.
   if (bsa_status s = builtin()) return s;
   g_err = why + "; using the built-in default table";
+  log_msg(1, "%s: %s", bsa_status_str(BSA_WARN_LUT_DEFAULT), g_err.c_str());
   return BSA_WARN_LUT_DEFAULT;
 }
 
@@ -399,7 +485,8 @@ static bsa_status alloc_header(Plan &P, bool acsr, bsa_acsr_head **acsr_dev) {
 
 // Everything after the features (host copy in P.feat): aggregates, regime,
 // geometry and capacities, the arena, and the planning kernels.
-static bsa_status finish_plan(Plan &P, bsa_lut_t lut, const uint8_t *mask, const int32_t *page_table) {
+static bsa_status finish_plan(Plan &P, bsa_lut_t lut, const uint8_t *mask, const int32_t *page_table,
+                              Trace &tr) {
   // ---- aggregates and regime ----
   P.total_nnz = P.total_blocks = P.imb16 = 0;
   P.min_bq = P.min_bk = 1 << 30;
@@ -505,7 +592,25 @@ static bsa_status finish_plan(Plan &P, bsa_lut_t lut, const uint8_t *mask, const
     *pt.first = pt.second ? ap : nullptr;
     ap += aligned(pt.second);
   }
-  return plan_build(P, mask, page_table, ap, scratch);
+  tr.mark("host planning");
+  const bsa_status st = plan_build(P, mask, page_table, ap, scratch);
+  if (st == BSA_OK) tr.mark("build");
+  return st;
+}
+
+// BSA_LOG >= 2: the regime and the sizes of a new plan.
+static void log_plan(const Plan &P, const char *how) {
+  if (log_level() < 2) return;
+  static const char *const kSched[] = {"local", "lpt", "dealt"};
+  int interleaved = 0;
+  for (int q : P.qil) interleaved += q > 1;
+  log_msg(2,
+          "plan (%s): B=%d Hq=%d Hkv=%d Sq=%lld Skv=%lld D=%d density %lld/1000 -> Tq=%d Tk=%d %s "
+          "split=%d pack=%d; %lld rows, at most %lld items and %lld entries, %lld partial slots, "
+          "%d heads interleaved, %zu bytes",
+          how, P.B, P.Hq, P.Hkv, (long long)P.Sq, (long long)P.Skv, P.D, (long long)P.density_pm, P.rg.tq,
+          P.rg.tk, kSched[std::min(2, std::max(0, P.rg.sched))], P.rg.split, P.rg.pack, (long long)P.nrows,
+          (long long)P.item_cap, (long long)P.ent_cap, (long long)P.part_slots, interleaved, P.arena_bytes);
 }
 
 bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *page_table,
@@ -521,10 +626,12 @@ bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *p
     return s;
   };
   if (hipGetDevice(&P.device) != hipSuccess) return bail(fail(BSA_ERR_HIP, "hipGetDevice failed"));
+  Trace tr("plan", P.stream);
 
   // ---- phase 1: features (one device-to-host read) ----
   if (bsa_status s = alloc_header(P, false, nullptr)) return bail(s);
   if (bsa_status s = plan_features(P, mask, page_table)) return bail(s);
+  tr.mark("features");
   // The one read-back of planning: counters and mask features, into pinned
   // host memory (a direct DMA, no staging through pageable memory).
   const size_t feat_bytes = sizeof(int64_t) * 4 * P.nbm * P.Hq;
@@ -542,8 +649,11 @@ bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *p
   const int64_t *hcost = (const int64_t *)((const uint8_t *)hf + aligned(feat_bytes));
   P.qil_cost.assign(hcost, hcost + kQilCands * P.Hq);
   if (hc[CNT_BADPAGE]) return bail(fail(BSA_ERR_INVALID_ARG, "page table entry outside [0, num_pages)"));
+  tr.mark("read-back");
 
-  if (bsa_status s = finish_plan(P, lut, mask, page_table)) return bail(s);
+  if (bsa_status s = finish_plan(P, lut, mask, page_table, tr)) return bail(s);
+  log_plan(P, "mask");
+  tr.report("mask");
   *out = p;
   return BSA_OK;
 }
@@ -570,11 +680,15 @@ bsa_status bsa_plan_acsr(const bsa_problem *pr, const bsa_acsr_head *heads, bsa_
     return s;
   };
   if (hipGetDevice(&P.device) != hipSuccess) return bail(fail(BSA_ERR_HIP, "hipGetDevice failed"));
+  Trace tr("plan", P.stream);
   bsa_acsr_head *dev_heads = nullptr;
   if (bsa_status s = alloc_header(P, true, &dev_heads)) return bail(s);
   // features from the runs on the host: no read-back, so nothing blocks
   if (bsa_status s = plan_features_acsr(P, heads, dev_heads, *pr)) return bail(s);
-  if (bsa_status s = finish_plan(P, lut, nullptr, nullptr)) return bail(s);
+  tr.mark("features");
+  if (bsa_status s = finish_plan(P, lut, nullptr, nullptr, tr)) return bail(s);
+  log_plan(P, "affine runs");
+  tr.report("affine runs");
   *out = p;
   return BSA_OK;
 }
@@ -648,6 +762,10 @@ static bsa_status forward_common(bsa_plan_t plan, const bsa_tensor *q, const bsa
   // streams) never share it.
   const FwdScratch fs = fwd_scratch_layout(P);
   hipStream_t s = (hipStream_t)stream;
+  log_msg(3, "forward%s: plan %p, %lld rows, %zu scratch bytes, stream %p",
+          no_alloc ? " (static scratch)" : kv8 ? " (fp8 K/V)" : "", (const void *)plan,
+          (long long)P.nrows, fs.bytes, stream);
+  Trace tr("forward", s);
   void *scratch = nullptr;
   if (no_alloc) {
     // The device's static scratch array instead of the pool.
@@ -660,7 +778,9 @@ static bsa_status forward_common(bsa_plan_t plan, const bsa_tensor *q, const bsa
     a.part_o = fs.part_o_off != fs.part_lse_off ? (float *)((uint8_t *)scratch + fs.part_o_off) : nullptr;
     a.part_lse = fs.part_lse_off != fs.bytes ? (float *)((uint8_t *)scratch + fs.part_lse_off) : nullptr;
     a.part_slots = P.part_slots;
-    return attention_launch(P, a, s);
+    const bsa_status st = attention_launch(P, a, s);
+    if (st == BSA_OK) tr.mark("attention"), tr.report("static scratch");
+    return st;
   }
   const hipError_t e = plan_alloc(&scratch, fs.bytes, P.device, s);
   if (e != hipSuccess)
@@ -674,6 +794,7 @@ static bsa_status forward_common(bsa_plan_t plan, const bsa_tensor *q, const bsa
   bsa_status st = attention_launch(P, a, s);
   plan_release(scratch, s);
   if (st == BSA_OK) st = note_stream_use(P, s);
+  if (st == BSA_OK) tr.mark("attention"), tr.report(kv8 ? "fp8 K/V" : "");
   return st;
 }
 
@@ -731,6 +852,9 @@ bsa_status bsa_backward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *
   const size_t delta_bytes = (sizeof(float) * (size_t)std::max<int64_t>(P.B * (int64_t)P.Hq * P.Sq, 1) + 255) & ~(size_t)255;
   const int nkt_per = 128 / P.rg.tk;
   const size_t index_bytes = plan_kv_index_bytes(P, nkt_per);
+  log_msg(3, "backward: plan %p, %zu scratch bytes, stream %p", (const void *)plan,
+          delta_bytes + index_bytes, stream);
+  Trace tr("backward", s);
   void *scratch = nullptr;
   const hipError_t e = plan_alloc(&scratch, delta_bytes + index_bytes, P.device, s);
   if (e != hipSuccess) return fail(BSA_ERR_OUT_OF_MEMORY, std::string("backward scratch: ") + hipGetErrorString(e));
@@ -738,9 +862,11 @@ bsa_status bsa_backward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *
   KvIndex ix{};
   bsa_status st = plan_kv_index(P, nkt_per, (uint8_t *)scratch + delta_bytes, &ix, s);
   a.t_off = ix.off, a.t_q0 = ix.q0, a.t_meta = ix.meta, a.t_live = ix.live;
+  if (st == BSA_OK) tr.mark("key index");
   if (st == BSA_OK) st = backward_launch(P, a, s);
   plan_release(scratch, s);
   if (st == BSA_OK) st = note_stream_use(P, s);
+  if (st == BSA_OK) tr.mark("delta, dQ, dK/dV"), tr.report();
   return st;
 }
 

@@ -144,6 +144,17 @@ struct BwdArgs {
 // n-th allocation (device or pinned host) counted from when the variable
 // took that value fails, for tests of the out-of-memory paths (the variable
 // is read at each allocation; a value change is seen there).
+// Diagnostics to stderr, both read from the environment at each call.
+// BSA_LOG=n (0..3, default 0): 1 prints every error and warning status with
+// its message, 2 also each plan's regime and sizes, 3 also each forward and
+// backward launch. BSA_TRACE=1 prints per-phase times of each plan, forward
+// and backward call (host wall time, and the stream's time between events
+// recorded at the phase boundaries); it waits for the call's last event, so
+// a traced call is synchronous with its stream.
+int log_level();
+bool trace_on();
+void log_msg(int level, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+
 hipError_t plan_alloc(void **ptr, size_t bytes, int device, hipStream_t stream);
 void plan_release(void *ptr, hipStream_t stream);
 bool alloc_fault_injected();

@@ -38,6 +38,15 @@
  *     caller owns it. "stream" is a hipStream_t passed as void* (NULL: the
  *     null stream). Work is queued on that stream; bsa_forward never
  *     synchronises.
+ *   - Diagnostics go to stderr, under two environment variables read at each
+ *     call. BSA_LOG=n (0..3, default 0): 1 prints every error and warning
+ *     status with its message, 2 also each new plan's regime and sizes and
+ *     each loaded table, 3 also each forward and backward launch.
+ *     BSA_TRACE=1 prints the phases of each bsa_plan, bsa_plan_acsr,
+ *     bsa_forward and bsa_backward call with their host wall time and the
+ *     stream's time between events recorded at the phase boundaries; a
+ *     traced call waits for its last event (synchronous with its stream, so
+ *     not for use under graph capture). Neither changes any result.
  */
 #ifndef BSA_H
 #define BSA_H

@@ -133,6 +133,31 @@ def test_lut_files(L, tmp_path):
     assert L.bsa_status_str(7).startswith(b"warning")
 
 
+def test_log_levels(L, capfd, monkeypatch, tmp_path):
+    """BSA_LOG: 0 prints nothing; 1 prints errors and warnings with their
+    message; 2 also names a loaded table. Read at each call."""
+    monkeypatch.setenv("BSA_LOG", "0")
+    assert plan_status(L, head_dim=96)[0] == 2
+    assert "[bsa]" not in capfd.readouterr().err
+    monkeypatch.setenv("BSA_LOG", "1")
+    st, msg = plan_status(L, head_dim=96)
+    err = capfd.readouterr().err
+    assert st == 2 and f"[bsa] unsupported: {msg}" in err, err
+    out = ctypes.c_void_p()
+    assert L.bsa_lut_load(b"/nonexistent/table.lut", ctypes.byref(out)) == bsa.BSA_WARN_LUT_DEFAULT
+    L.bsa_lut_free(out)
+    err = capfd.readouterr().err
+    assert "[bsa] warning" in err and "cannot open" in err, err
+    assert L.bsa_lut_load(bsa.DEFAULT_LUT.encode(), ctypes.byref(out)) == 0
+    L.bsa_lut_free(out)
+    assert "rules" not in capfd.readouterr().err
+    monkeypatch.setenv("BSA_LOG", "2")
+    assert L.bsa_lut_load(bsa.DEFAULT_LUT.encode(), ctypes.byref(out)) == 0
+    L.bsa_lut_free(out)
+    n_rules = sum(1 for line in open(bsa.DEFAULT_LUT) if line.startswith("rule "))
+    assert f"[bsa] lookup table {bsa.DEFAULT_LUT}: {n_rules} rules" in capfd.readouterr().err
+
+
 def test_builtin_lut_is_the_packaged_table():
     """The table compiled into the library is the packaged text, byte for
     byte (build.py regenerates the include from lut/gfx950.lut)."""

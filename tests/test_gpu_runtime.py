@@ -151,8 +151,9 @@ SPLIT_CASES = {
                                                      bq=128, bk=128, density=0.38, seed=seed),
                        forced_lut_text(128, 64, "dealt", 128, 0)),
     # the packaged table's decode bucket (union tables over a paged cache,
-    # a few queries): rows split at 32 key tiles
-    "packaged_decode": (lambda seed: W.decode(batch=4, hq=8, hkv=2, q_len=3, context=8192, seed=seed),
+    # a few queries; the union of 4 heads' top tenth of 128 blocks covers
+    # about 90 key tiles): rows split at the table's threshold
+    "packaged_decode": (lambda seed: W.decode(batch=4, hq=8, hkv=2, q_len=3, context=16384, seed=seed),
                         None),
 }
 
@@ -318,3 +319,52 @@ def test_out_of_memory_paths(ref, monkeypatch):
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
     assert torch.isfinite(dq.float()).all() and torch.isfinite(dk.float()).all()
     plan.free()
+
+
+def test_trace_and_log(ref, monkeypatch, capfd):
+    """BSA_TRACE=1 prints the phases of each plan, forward and backward call
+    with their stream and host times; BSA_LOG=2 prints each plan's regime and
+    sizes, 3 also each launch. The outputs are the same bits as without
+    diagnostics."""
+    import re
+    import torch
+    w = W.random_problem(batch=1, hq=4, hkv=2, sq=500, skv=600, d=128, bq=64, bk=64, density=0.4,
+                         causal=True, causal_offset=100, seed=81)
+    q, k, v, mask, table = to_device(w)
+    lut = bsa.Lut.parse(forced_lut_text(128, 64, "lpt", 3, 0))
+    dout = torch.randn_like(q.float()).to(q.dtype)
+
+    def run():
+        plan = bsa.plan(w.problem_dict(), mask, table, lut)
+        o, lse = plan.forward(q, k, v)
+        grads = plan.backward(q, k, v, o, lse, dout)
+        torch.cuda.synchronize()
+        plan.free()
+        return (o, lse) + tuple(grads)
+
+    monkeypatch.delenv("BSA_TRACE", raising=False)
+    monkeypatch.delenv("BSA_LOG", raising=False)
+    quiet = run()
+    assert "[bsa" not in capfd.readouterr().err
+    monkeypatch.setenv("BSA_TRACE", "1")
+    monkeypatch.setenv("BSA_LOG", "3")
+    loud = run()
+    err = capfd.readouterr().err
+    say(err)
+    for a, b in zip(quiet, loud):
+        assert torch.equal(a, b)
+    num = r"(-?\d+\.\d+) ms stream / (\d+\.\d+) ms host;"
+    expect = {
+        "plan": r"\[bsa trace\] plan \(mask\): features N read-back N host planning N build N total",
+        "forward": r"\[bsa trace\] forward: attention N total",
+        "backward": r"\[bsa trace\] backward: key index N delta, dQ, dK/dV N total",
+    }
+    for name, pat in expect.items():
+        m = re.search(pat.replace(" N", " " + num), err)
+        assert m, (name, err)
+        times = [float(x) for x in m.groups()]
+        assert all(t >= 0 for t in times), (name, times)
+    assert re.search(r"\[bsa\] plan \(mask\): B=1 Hq=4 Hkv=2 Sq=500 Skv=600 D=128 .* -> Tq=128 Tk=64 lpt "
+                     r"split=3 pack=0; \d+ rows", err), err
+    assert re.search(r"\[bsa\] forward: plan 0x[0-9a-f]+, \d+ rows, \d+ scratch bytes", err), err
+    assert re.search(r"\[bsa\] backward: plan 0x[0-9a-f]+, \d+ scratch bytes", err), err
