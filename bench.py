@@ -39,6 +39,19 @@ sys.path.insert(0, ROOT)
 METRIC = "effective sparse-attn TFLOP/s (selected tiles only) + % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0
+# The vector-ALU roofline of the online softmax. Per score it needs at least a
+# scale-and-subtract, an exponential, a row-sum add and a row-maximum compare
+# (no packed fp32 arithmetic in this build). A wave64 instruction takes 4
+# cycles of a 16-lane SIMD; the exponential takes 8 (measured on gfx950: half
+# the FMA issue rate). 1,024 SIMDs at 2.4 GHz then finish at most
+# 1024 * 2.4e9 * 64 / 20 = 7.86e12 scores/s, i.e. 4*D FLOP of selected work
+# per score: 2.01 PFLOP/s at D = 64 (below the MFMA peak), 4.03 at D = 128.
+VALU_CYCLES_PER_64_SCORES = 4 + 8 + 4 + 4
+PEAK_SCORES_PER_S = 1024 * 2.4e9 * 64 / VALU_CYCLES_PER_64_SCORES
+
+
+def peak_alu_tflops(d: int) -> float:
+    return PEAK_SCORES_PER_S * 4 * d / 1e12
 
 
 def workload(name: str):
@@ -86,16 +99,24 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(name: str, launches_bytes):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
-    were taken on the current kernel source; else None."""
+def profile_record(name: str):
+    """The committed rocprofv3 record of a workload's attention kernel (HBM
+    bytes per launch; matrix-core and VALU busy fractions), if it was taken
+    on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
+
+
+def measured_traffic(name: str, launches_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    rec = profile_record(name)
+    return rec.get("hbm_bytes_per_launch") if rec else None
 
 
 def allowed_keys_per_row(w, b: int, h: int) -> np.ndarray:
@@ -217,21 +238,39 @@ CONFIGS = ["video_dit", "chunked_prefill", "affine_bs32", "affine_bs64", "affine
            "affine_bs64_w8192", "long_video"]
 
 
-def forward_rates(w, eff_flops: float, fwd_ms: float, stats: dict) -> dict:
-    """Forward rates of one workload against both rooflines."""
+def forward_rates(w, eff_flops: float, fwd_ms: float, stats: dict, name: str = None) -> dict:
+    """Forward rates of one workload against the three rooflines (MFMA, the
+    softmax's VALU work, HBM bytes streamed with no reuse beyond a 128-row
+    tile), and the bound: the unit the committed counters show busiest
+    (matrix core, VALU, or HBM traffic over this time) when they were taken
+    on the current kernel source, else the roofline with the longest time."""
     sb = streamed_bytes(w)
     t_mfma = eff_flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_alu = eff_flops / (peak_alu_tflops(w.d) * 1e12)
     t_hbm = sb / (PEAK_HBM_GBS * 1e9)
     tflops = eff_flops / (fwd_ms * 1e-3) / 1e12
     gbs = sb / (fwd_ms * 1e-3) / 1e9
     eff_area = eff_flops / (4.0 * w.d)
-    return {"forward_ms": round(fwd_ms, 4), "tflops": round(tflops, 3),
-            "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "streamed_bytes": int(sb), "streamed_gbs": round(gbs, 1),
-            "hbm_frac_streamed": round(gbs / PEAK_HBM_GBS, 4),
-            "bound": "hbm" if t_hbm > t_mfma else "mfma",
-            "area_ratio": round(stats["executed_tiles"] * stats["tile_q"] * stats["tile_k"] / eff_area, 4)
-            if eff_area else None}
+    out = {"forward_ms": round(fwd_ms, 4), "tflops": round(tflops, 3),
+           "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+           "alu_frac": round(tflops / peak_alu_tflops(w.d), 4),
+           "streamed_bytes": int(sb), "streamed_gbs": round(gbs, 1),
+           "hbm_frac_streamed": round(gbs / PEAK_HBM_GBS, 4),
+           "area_ratio": round(stats["executed_tiles"] * stats["tile_q"] * stats["tile_k"] / eff_area, 4)
+           if eff_area else None}
+    rec = profile_record(name) if name else None
+    if rec and "mfma_busy" in rec:
+        hbm = rec["hbm_bytes_per_launch"] / (fwd_ms * 1e-3) / (PEAK_HBM_GBS * 1e9)
+        busy = {"mfma": rec["mfma_busy"], "alu": rec["valu_busy"], "hbm": hbm}
+        out["bound"] = max(busy, key=busy.get)
+        out["bound_from"] = "counters"
+        out["counters"] = {"mfma_busy": round(rec["mfma_busy"], 4), "valu_busy": round(rec["valu_busy"], 4),
+                           "hbm_frac_measured": round(hbm, 4), "clock_ghz": round(rec["clock_ghz"], 3)}
+    else:
+        out["bound"] = max((t_mfma, "mfma"), (t_alu, "alu"), (t_hbm, "hbm"))[1]
+        out["bound_from"] = "model"
+    out["frac"] = {"mfma": out["mfma_frac"], "alu": out["alu_frac"], "hbm": out["hbm_frac_streamed"]}[out["bound"]]
+    return out
 
 
 def cpu_baseline(w, q, k, v, target_s: float = 20.0, kv8=None):
@@ -479,7 +518,7 @@ def main():
     esz = 2 if w.dtype == "bf16" else 4
     compulsory = esz * (q.numel() * 2 + k.numel() + v.numel()) + 4 * lse.numel()
     traffic = measured_traffic(args.workload, None)
-    rates = forward_rates(w, eff_flops, fwd_avg, stats)
+    rates = forward_rates(w, eff_flops, fwd_avg, stats, args.workload)
     if rates["bound"] == "hbm":
         # Gather-bound: the no-reuse K/V stream at 8 TB/s takes longer than the
         # selected work at the MFMA peak, so the roofline is HBM bytes.
@@ -489,12 +528,24 @@ def main():
                     "algorithmic_bytes_def": "K+V rows streamed per 128-row query tile (no reuse "
                                              "beyond the tile) + Q, O, LSE once",
                     "mfma_frac": rates["mfma_frac"], "compulsory_bytes": compulsory}
+    elif rates["bound"] == "alu":
+        # The softmax's VALU work per score (exponential at half the FMA
+        # rate) bounds it before the matrix cores: D = 64.
+        peak = peak_alu_tflops(w.d)
+        roofline = {"bound": "alu", "achieved": round(achieved, 3), "peak": round(peak, 1),
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                    "kernel": "k_attn", "peak_def": "7.86e12 scores/s (20 VALU cycles per 64 scores "
+                    "per SIMD at 2.4 GHz) x 4*D FLOP per score", "mfma_frac": rates["mfma_frac"],
+                    "compulsory_bytes": compulsory, "hbm_frac_streamed": rates["hbm_frac_streamed"]}
     else:
         roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                     "traffic": traffic, "kernel": "k_attn", "compulsory_bytes": compulsory,
                     "hbm_frac_streamed": rates["hbm_frac_streamed"]}
     roofline["area_ratio"] = rates["area_ratio"]
+    roofline["bound_from"] = rates["bound_from"]
+    if "counters" in rates:
+        roofline["counters"] = rates["counters"]
     if args.workload in HBM_BOUND:
         # Union tables: every head of a group selects the same blocks, so the
         # group reads effective_blocks / G blocks of K and of V once.
@@ -587,7 +638,7 @@ def config_table(bsa, lut, args):
         p.free()
         eff = effective_flops(w)
         rec = {"workload": name, "density_pm": stats["density_pm"], "effective_flops": eff}
-        rec.update(forward_rates(w, eff, fwd_ms, stats))
+        rec.update(forward_rates(w, eff, fwd_ms, stats, name))
         rec["regime"] = {k2: stats[k2] for k2 in ("tile_q", "tile_k", "sched", "split", "pack")}
         if w.gqa_union:
             pre = pre_union_flops(w)
@@ -633,8 +684,8 @@ def config_table(bsa, lut, args):
                              "candidates": len(times)}
         out.append(rec)
         print(f"[config] {name}: {rec['forward_ms']} ms, {rec['tflops']} TFLOP/s, "
-              f"mfma {rec['mfma_frac']}, hbm(streamed) {rec['hbm_frac_streamed']}, "
-              f"area {rec['area_ratio']}" + (f", regret {rec['regret']['regret']}" if args.regret else ""),
+              f"mfma {rec['mfma_frac']}, alu {rec['alu_frac']}, hbm(streamed) {rec['hbm_frac_streamed']}, "
+              f"bound {rec['bound']} ({rec['bound_from']}), area {rec['area_ratio']}" + (f", regret {rec['regret']['regret']}" if args.regret else ""),
               file=sys.stderr, flush=True)
         del q, k, v, o, lse, mask, table
         torch.cuda.empty_cache()
