@@ -619,6 +619,34 @@ static int64_t interleave_cost(const ref_problem *p, const uint8_t *mask, const 
   return cost;
 }
 
+/* Key tiles listed by the query tiles of one head when its query tiles
+ * take interleave sq_ (mq blocks each) and its key tiles gather mk key
+ * blocks with interleave s by the same rule (qblock over the key blocks):
+ * for every mask batch and query tile, the number of key tiles in which
+ * some query block of the tile selects one of the tile's key blocks (the
+ * mask as given). */
+static int64_t key_interleave_cost(const ref_problem *p, const uint8_t *mask, const int64_t *moff,
+                                   int h, int64_t mq, int64_t sq_, int64_t mk, int64_t s) {
+  const int64_t nq = ceil_div(p->sq, p->bq[h]), nk = ceil_div(p->skv, p->bk[h]);
+  int64_t cost = 0;
+  for (int bm = 0; bm < mask_batches(p); ++bm) {
+    const uint8_t *m = mask + moff[bm * p->hq + h];
+    for (int64_t t = 0; t < ceil_div(nq, mq); ++t)
+      for (int64_t kt = 0; kt < ceil_div(nk, mk); ++kt) {
+        int any = 0;
+        for (int64_t ik = 0; ik < mk && !any; ++ik) {
+          const int64_t kb = qblock(kt, ik, s, mk, nk);
+          for (int64_t iq = 0; iq < mq && !any && kb < nk; ++iq) {
+            const int64_t qb = qblock(t, iq, sq_, mq, nq);
+            if (qb < nq && m[qb * nk + kb]) any = 1;
+          }
+        }
+        cost += any;
+      }
+  }
+  return cost;
+}
+
 int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_table,
              const char *lut_text, const int32_t *force, uint8_t *image, size_t *bytes) {
   if (check_problem(p) || !bytes || (p->paged && !page_table)) return -1;
@@ -732,6 +760,28 @@ int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_tabl
     }
   }
 
+  /* 2c. Key-block interleave per head: when 128 x 64 tiles merge two
+   * 32-key blocks per key tile and the head's query tiles merge blocks of 32
+   * or 64 rows (no union, no paging, no causal bound), key tile kt gathers
+   * key blocks qblock(kt, ik, s, 2, nk) for the s in {1, 2, 4, 8}
+   * (2 s <= the head's key blocks) whose query tiles (with the interleave of
+   * 2b) list the fewest key tiles, the smallest s on ties; every other head
+   * takes 1 (key tile kt holds blocks 2 kt and 2 kt + 1). */
+  int32_t *kil = (int32_t *)malloc(sizeof(int32_t) * p->hq);
+  for (int h = 0; h < p->hq; ++h) {
+    kil[h] = 1;
+    const int64_t bq = p->bq[h], bk = p->bk[h], nk = ceil_div(p->skv, bk);
+    if (p->gqa_union || p->paged || p->causal || tq != 128 || tk != 64 || bk != 32 || bq >= tq ||
+        bq < 32)
+      continue;
+    const int64_t mq = tq / bq, mk = tk / bk;
+    int64_t best = key_interleave_cost(p, mask, moff, h, mq, qil[h], mk, 1);
+    for (int64_t s = 2; s <= 8 && s * mk <= nk; s *= 2) {
+      const int64_t c = key_interleave_cost(p, mask, moff, h, mq, qil[h], mk, s);
+      if (c < best) best = c, kil[h] = (int32_t)s;
+    }
+  }
+
   /* 3. Physical mapping: per list, ascending key tiles with live bits over the
    * merged logical sub-blocks (keep / merge / subdivide). */
   int64_t nlists = p->gqa_union ? (int64_t)nlb * p->hkv : (int64_t)nlb * p->hq * nqt;
@@ -764,7 +814,7 @@ int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_tabl
       for (int64_t iq = 0; iq < mq; ++iq)
         for (int64_t ik = 0; ik < mk; ++ik) {
           int64_t qb = bq < tq ? qblock(qt, iq, qil[h], mq, nq) : (qt * tq) / bq;
-          int64_t kb = bk < tk ? kt * mk + ik : (kt * tk) / bk;
+          int64_t kb = bk < tk ? qblock(kt, ik, kil[h], mk, nk) : (kt * tk) / bk;
           if (kb >= nk || (!u && qb >= nq)) continue;
           if (!(u ? u[kb] : m[qb * nk + kb])) continue;
           if (!u && p->causal) {
@@ -791,6 +841,7 @@ int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_tabl
   list_off[nlists] = nent;
   if (nent > INT32_MAX) {
     free(moff), free(uni), free(feat), free(list_off), free(ekt), free(epage), free(elive), free(qil);
+    free(kil);
     return -3;
   }
 
@@ -870,6 +921,7 @@ int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_tabl
   put(&o, p->bq, sizeof(int32_t) * p->hq);
   put(&o, p->bk, sizeof(int32_t) * p->hq);
   put(&o, qil, sizeof(int32_t) * p->hq);
+  put(&o, kil, sizeof(int32_t) * p->hq);
   put(&o, feat, sizeof(int64_t) * 4 * nbm * p->hq);
   for (int64_t l = 0; l <= nlists; ++l) {
     int32_t x = (int32_t)list_off[l];
@@ -885,7 +937,7 @@ int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_tabl
   int rc = (image && o.n > *bytes) ? -4 : 0;
   *bytes = o.n;
   free(moff), free(uni), free(feat), free(list_off), free(ekt), free(epage), free(elive);
-  free(row_ent), free(items), free(comb), free(qil);
+  free(row_ent), free(items), free(comb), free(qil), free(kil);
   return rc;
 }
 

@@ -3,7 +3,8 @@ the planner tests. Test infrastructure: written from the plan format, shares
 no code with either planner.
 
 Image layout (little-endian): the 8-byte magic ``BSAPLAN1``; 40 int64 header
-words; int32 bq[Hq], bk[Hq], query-block interleave[Hq]; int64
+words; int32 bq[Hq], bk[Hq], query-block interleave[Hq], key-block
+interleave[Hq]; int64
 features[mask batches][Hq][4]; int32
 list_off[nlists + 1]; int32 kt[nent]; int32 page[nent] (paged only); uint32
 live[nent]; int32 rows[nrows][2]; int32 items[nitems][4]; int32
@@ -27,6 +28,7 @@ class Plan:
     bq: np.ndarray
     bk: np.ndarray
     qil: np.ndarray
+    kil: np.ndarray
     feat: np.ndarray
     list_off: np.ndarray
     kt: np.ndarray
@@ -51,7 +53,7 @@ def decode(img: bytes) -> Plan:
         return a
 
     hq = h["hq"]
-    bq, bk, qil = take(np.int32, hq), take(np.int32, hq), take(np.int32, hq)
+    bq, bk, qil, kil = (take(np.int32, hq) for _ in range(4))
     nbm = 1 if h["broadcast"] else h["batch"]
     feat = take(np.int64, nbm * hq * 4).reshape(nbm, hq, 4)
     list_off = take(np.int32, h["nlists"] + 1)
@@ -62,7 +64,7 @@ def decode(img: bytes) -> Plan:
     items = take(np.int32, 4 * h["nitems"]).reshape(-1, 4)
     comb = take(np.int32, 3 * h["ncomb"]).reshape(-1, 3)
     assert pos == len(img), (pos, len(img))
-    return Plan(h, bq, bk, qil, feat, list_off, kt, page, live, rows, items, comb)
+    return Plan(h, bq, bk, qil, kil, feat, list_off, kt, page, live, rows, items, comb)
 
 
 def qblock(t: int, iq: int, s: int, mq: int, nq: int) -> int:
@@ -74,6 +76,24 @@ def qblock(t: int, iq: int, s: int, mq: int, nq: int) -> int:
     if t < full * s:
         return (t // s) * g + iq * s + t % s
     return full * g + (t - full * s) * mq + iq
+
+
+def key_ranges(p: Plan, head: int, kt: int):
+    """[(k0, k1, ik)]: the keys of key tile kt of a head, per key sub-block
+    ik (a tile merging key blocks lists each at the position its interleave
+    gives it; a tile within one key block is one range)."""
+    h = p.h
+    tk, skv = h["tk"], h["skv"]
+    bk = int(p.bk[head])
+    if bk >= tk:
+        return [(kt * tk, min(skv, (kt + 1) * tk), 0)]
+    mk, nk = tk // bk, -(-skv // bk)
+    out = []
+    for ik in range(mk):
+        kb = qblock(kt, ik, int(p.kil[head]), mk, nk)
+        if kb < nk:
+            out.append((kb * bk, min(skv, (kb + 1) * bk), ik))
+    return out
 
 
 def row_geometry(p: Plan, r: int):
@@ -126,19 +146,21 @@ def expand_row(p: Plan, r: int, head: int, q0: int, q1: int, iq0=None) -> np.nda
     qi = np.arange(q0, q1)
     for e in range(e0, e1):
         kt, live = int(p.kt[e]), int(p.live[e])
-        k0, k1 = kt * tk, min(skv, (kt + 1) * tk)
-        kj = np.arange(k0, k1)
         if union:
             iq = np.zeros_like(qi)
         elif iq0 is not None:
             iq = np.full_like(qi, iq0)
         else:
             iq = (qi - qt * tr) // aq
-        ik = (kj - k0) // ak
-        bit = (live >> (iq[:, None] * mk + ik[None, :])) & 1
-        ok = bit.astype(bool)
-        if h["causal"]:
-            ok &= kj[None, :] <= qi[:, None] + h["offset"]
-        assert not (out[:, k0:k1] & ok).any(), "key tile listed twice"
-        out[:, k0:k1] |= ok
+        for k0, k1, ik_b in key_ranges(p, head, kt):
+            kj = np.arange(k0, k1)
+            # sub-block within the tile: the range's own index when the tile
+            # merges key blocks, else the offset within a contiguous tile
+            ik = np.full_like(kj, ik_b) if bk < tk else (kj - k0) // ak
+            bit = (live >> (iq[:, None] * mk + ik[None, :])) & 1
+            ok = bit.astype(bool)
+            if h["causal"]:
+                ok &= kj[None, :] <= qi[:, None] + h["offset"]
+            assert not (out[:, k0:k1] & ok).any(), "key tile listed twice"
+            out[:, k0:k1] |= ok
     return out

@@ -80,15 +80,17 @@ def test_exhaustive_4x4_masks(ref):
         ent_list = np.repeat(np.arange(h["nlists"]), np.diff(p.list_off))
         b_of = ent_list // nqt
         qt_of = ent_list % nqt
-        s_of = int(p.qil[0])
+        s_of, sk_of = int(p.qil[0]), int(p.kil[0])
         for iq in range(mq):
             for ik in range(mk):
                 bit = (p.live >> np.uint32(iq * mk + ik)) & 1
                 sel = bit.astype(bool)
-                # (tiles merge query sub-blocks through the head's interleave)
+                # (tiles merge query and key sub-blocks through the head's
+                # interleaves)
                 a = np.array([qblock(int(t), iq, s_of, mq, naq) if bq < 128 else int(t) * mq + iq
                               for t in qt_of[sel]], np.int64)
-                c = p.kt[sel] * mk + ik
+                c = np.array([qblock(int(kt), ik, sk_of, mk, nak) if bk < tk else int(kt) * mk + ik
+                              for kt in p.kt[sel]], np.int64)
                 np.add.at(cov, (b_of[sel], a, c), 1)
         blk = allm.reshape(B, 4, 4)
         want = blk[:, (np.arange(naq) * aq) // bq][:, :, (np.arange(nak) * ak) // bk]
@@ -315,5 +317,76 @@ def test_interleave_choice_random(ref, seed):
     p = decode(ref.plan(w, force=[128, 64, seed % 3, 0, 0]))
     assert list(p.qil) == [interleave_choice(w, h) for h in range(4)]
     assert max(p.qil) > 1
+    check_worklist(p)
+    check_elements(w, p)
+
+
+# ---- key-block interleave ----
+
+def key_interleave_choice(w, h, qil, tq=128, tk=64):
+    """The key interleave the plan specification gives head h, from its
+    definition: for 128 x 64 tiles merging two 32-key blocks, query blocks
+    of 32 or 64 rows, no union, paging or causal bound, the s in
+    {1, 2, 4, 8} with 2 s <= nk whose query tiles (interleave qil) list the
+    fewest key tiles (summed over mask batches), smallest on ties; else 1."""
+    bq, bk = w.bq[h], w.bk[h]
+    if w.gqa_union or w.paged or w.causal or bk != 32 or bq >= tq or bq < 32:
+        return 1
+    mq, nq = tq // bq, -(-w.sq // bq)
+    mk, nk = tk // bk, -(-w.skv // bk)
+    nt, nkt = -(-nq // mq), -(-nk // mk)
+    qbs = np.array([[qblock(t, iq, qil, mq, nq) for iq in range(mq)] for t in range(nt)])
+    masks = []
+    for bm in range(w.mask_batches):
+        m = np.zeros((nq + 1, nk + 1), bool)  # row nq and column nk: no block
+        m[:nq, :nk] = w.head_mask(bm, h).astype(bool)
+        masks.append(m[np.minimum(qbs, nq)].any(1))  # [tile][key block]
+
+    def cost(s):
+        kbs = np.array([[qblock(kt, ik, s, mk, nk) for ik in range(mk)] for kt in range(nkt)])
+        return sum(int(sel[:, np.minimum(kbs, nk)].any(2).sum()) for sel in masks)
+
+    best, bc = 1, cost(1)
+    for s in (2, 4, 8):
+        if s * mk > nk:
+            break
+        c = cost(s)
+        if c < bc:
+            best, bc = s, c
+    return best
+
+
+def test_key_interleave_dilated_pattern(ref):
+    """A dilated pattern of 32-blocks (key block = query block mod 8): query
+    tiles gather four blocks of one residue and key tiles two key blocks of
+    one residue, so every listed tile is live in all eight sub-blocks, a
+    quarter of the entries of contiguous merging on both sides."""
+    w = W.affine(bs=32, batch=1, heads=3, s=4096, window=256, d=64)
+    p = decode(ref.plan(w, force=[128, 64, 0, 0, 0]))
+    assert list(p.qil) == [interleave_choice(w, h) for h in range(3)]
+    assert list(p.kil) == [key_interleave_choice(w, h, int(p.qil[h])) for h in range(3)]
+    assert (int(p.qil[1]), int(p.kil[1])) == (8, 8)
+    check_worklist(p)
+    check_elements(w, p)
+    nqt = p.h["nqt"]
+    for r in range(nqt, 2 * nqt):  # the dilated head: 128 key blocks, 16 per residue
+        e0, e1 = p.rows[r]
+        assert e1 - e0 == 128 // 8 // 2
+        assert (p.live[e0:e1] == 0xFF).all()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_key_interleave_choice_random(ref, seed):
+    """Periodic rows over 32-key blocks (ragged key length, per-batch masks,
+    merged query blocks of 32 and 64 rows), causal on odd seeds: the
+    planner's key interleave equals the definition's (1 under the causal
+    bound), and the plan covers the mask exactly."""
+    g = np.random.default_rng(100 + seed)
+    w = W.periodic(sq=2048 + 64 * int(g.integers(0, 5)), skv=1024 + 32 * int(g.integers(0, 7)),
+                   bk=32, causal=bool(seed % 2), causal_offset=int(g.integers(-200, 300)), seed=seed)
+    p = decode(ref.plan(w, force=[128, 64, seed % 3, 0, 0]))
+    assert list(p.qil) == [interleave_choice(w, h) for h in range(4)]
+    assert list(p.kil) == [key_interleave_choice(w, h, int(p.qil[h])) for h in range(4)]
+    assert (max(p.kil) > 1) == (not w.causal)
     check_worklist(p)
     check_elements(w, p)
