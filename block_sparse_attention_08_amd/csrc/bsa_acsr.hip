@@ -200,11 +200,13 @@ namespace bsa {
 // 128 / bq), the key blocks that some query block of each 128-row tile
 // selects, summed over the tiles. A tile's rows are expanded from the runs
 // into one bit set of the head's key blocks.
-void acsr_qil_costs(const bsa_problem &pr, const bsa_acsr_head *heads, int64_t *out) {
+void acsr_qil_costs(const bsa_problem &pr, const bsa_acsr_head *heads, int64_t *out, int64_t *kout) {
+  const bool keys_ok = !pr.causal && !pr.paged && pr.dtype == BSA_BF16 && pr.num_q_heads == pr.num_kv_heads;
   for (int h = 0; h < pr.num_q_heads; ++h) {
     const int64_t bq = pr.block_q[h], bk = pr.block_k[h];
     const int64_t nq = (pr.seqlen_q + bq - 1) / bq, nk = (pr.seqlen_kv + bk - 1) / bk;
     for (int c = 0; c < kQilCands; ++c) out[h * kQilCands + c] = 0;
+    for (int c = 0; c < kQilCands * kKilCands; ++c) kout[h * kQilCands * kKilCands + c] = 0;
     if (bq < 32 || bq >= 128) continue;
     const int64_t mq = 128 / bq;
     const int lm = __builtin_ctz((unsigned)mq);
@@ -220,6 +222,17 @@ void acsr_qil_costs(const bsa_problem &pr, const bsa_acsr_head *heads, int64_t *
           for (int j = 0; j < d.num_runs; ++j) {
             const bsa_acsr_run &u = d.runs[j];
             const int64_t f = acsr_first(u, qb);
+            if (u.stride == 1) {
+              // the interval [f, f + count) clipped to [0, nk), a word at a time
+              const int64_t lo = std::max<int64_t>(f, 0), hi = std::min<int64_t>(f + u.count, nk);
+              for (int64_t kb = lo; kb < hi;) {
+                const int64_t w = kb >> 6, end = std::min(hi, (w + 1) << 6);
+                const int n = (int)(end - kb);
+                bits[(size_t)w] |= (n == 64 ? ~0ull : ((1ull << n) - 1ull)) << (kb & 63);
+                kb = end;
+              }
+              continue;
+            }
             // blocks f + stride * i in [0, nk), 0 <= i < count
             int64_t i0 = f >= 0 ? 0 : (-f + u.stride - 1) / u.stride;
             for (int64_t i = i0; i < u.count; ++i) {
@@ -230,6 +243,21 @@ void acsr_qil_costs(const bsa_problem &pr, const bsa_acsr_head *heads, int64_t *
           }
         }
         for (uint64_t w : bits) cost += __builtin_popcountll(w);
+        // 64-key tiles (two 32-key blocks) with a selected block, per key
+        // interleave s' = 2^ck with 2 s' <= nk
+        if (keys_ok && bk == 32)
+          for (int ck = 0; ck < kKilCands && (int64_t(2) << ck) <= nk; ++ck) {
+            int64_t n = 0;
+            for (int64_t kt = 0; 2 * kt < nk; ++kt) {
+              bool any = false;
+              for (int ik = 0; ik < 2 && !any; ++ik) {
+                const int64_t kb = qblock_of(kt, ik, ck, 1, nk);
+                any = kb < nk && ((bits[(size_t)(kb >> 6)] >> (kb & 63)) & 1ull);
+              }
+              n += any;
+            }
+            kout[(h * kQilCands + c) * kKilCands + ck] += n;
+          }
       }
       out[h * kQilCands + c] = cost;
     }

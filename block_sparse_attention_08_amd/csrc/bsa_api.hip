@@ -452,7 +452,9 @@ static bsa_status alloc_header(Plan &P, bool acsr, bsa_acsr_head **acsr_dev) {
   int64_t rows_per_bm = 0;
   for (int h = 0; h < P.Hq; ++h) rows_per_bm += cdiv(P.Sq, P.bq[h]);
   const size_t acsr_bytes = acsr ? sizeof(bsa_acsr_head) * P.Hq : 0;
-  const size_t cost_bytes = sizeof(unsigned long long) * kQilCands * P.Hq;
+  // query-interleave costs [Hq][kQilCands], then key-interleave costs
+  // [Hq][kQilCands][kKilCands]
+  const size_t cost_bytes = sizeof(unsigned long long) * kQilCands * (1 + kKilCands) * P.Hq;
   const size_t pre_bytes = aligned(sizeof(int32_t) * CNT_N) + aligned(feat_bytes) + aligned(cost_bytes) +
                            aligned(sizeof(int64_t) * (kQilCands * P.Hq + 1)) +
                            aligned(sizeof(HeadMeta) * P.Hq) +
@@ -516,6 +518,24 @@ static bsa_status finish_plan(Plan &P, bsa_lut_t lut, const uint8_t *mask, const
     for (int c = 1; c < kQilCands && (int64_t(1) << c) * mq <= nq; ++c)
       if (P.qil_cost[h * kQilCands + c] < best) best = P.qil_cost[h * kQilCands + c], P.qil[h] = 1 << c;
   }
+  // Key-block interleave per head (64-key tiles merging two 32-key blocks,
+  // 128-row tiles merging 32- or 64-row blocks, bf16, one query head per kv
+  // head, no union, paging or causal bound): given the head's query
+  // interleave, the candidate s = 2^c with 2 s <= nk whose query tiles list
+  // the fewest key tiles, the smallest on ties.
+  P.kil.assign(P.Hq, 1);
+  for (int h = 0; h < P.Hq; ++h) {
+    const int64_t bq = P.bq[h], nk = cdiv(P.Skv, P.bk[h]);
+    if (P.uni || P.paged || P.causal || P.dtype != BSA_BF16 || P.G != 1 || P.rg.tq != 128 ||
+        P.rg.tk != 64 || P.bk[h] != 32 || bq >= 128 || bq < 32 || P.kil_cost.empty())
+      continue;
+    const int64_t *kc = &P.kil_cost[((size_t)h * kQilCands + __builtin_ctz(P.qil[h])) * kKilCands];
+    int64_t best = kc[0];
+    for (int c = 1; c < kKilCands && (int64_t(2) << c) <= nk; ++c)
+      if (kc[c] < best) best = kc[c], P.kil[h] = 1 << c;
+  }
+  P.key_interleaved = false;
+  for (int k : P.kil) P.key_interleaved |= k > 1;
 
   // ---- geometry and capacities ----
   const int tq = P.rg.tq, tk = P.rg.tk;
@@ -602,15 +622,16 @@ static bsa_status finish_plan(Plan &P, bsa_lut_t lut, const uint8_t *mask, const
 static void log_plan(const Plan &P, const char *how) {
   if (log_level() < 2) return;
   static const char *const kSched[] = {"local", "lpt", "dealt"};
-  int interleaved = 0;
+  int interleaved = 0, key_interleaved = 0;
   for (int q : P.qil) interleaved += q > 1;
+  for (int k : P.kil) key_interleaved += k > 1;
   log_msg(2,
           "plan (%s): B=%d Hq=%d Hkv=%d Sq=%lld Skv=%lld D=%d density %lld/1000 -> Tq=%d Tk=%d %s "
           "split=%d pack=%d; %lld rows, at most %lld items and %lld entries, %lld partial slots, "
-          "%d heads interleaved, %zu bytes",
+          "%d heads interleaved (%d on the key side), %zu bytes",
           how, P.B, P.Hq, P.Hkv, (long long)P.Sq, (long long)P.Skv, P.D, (long long)P.density_pm, P.rg.tq,
           P.rg.tk, kSched[std::min(2, std::max(0, P.rg.sched))], P.rg.split, P.rg.pack, (long long)P.nrows,
-          (long long)P.item_cap, (long long)P.ent_cap, (long long)P.part_slots, interleaved, P.arena_bytes);
+          (long long)P.item_cap, (long long)P.ent_cap, (long long)P.part_slots, interleaved, key_interleaved, P.arena_bytes);
 }
 
 bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *page_table,
@@ -635,7 +656,7 @@ bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *p
   // The one read-back of planning: counters and mask features, into pinned
   // host memory (a direct DMA, no staging through pageable memory).
   const size_t feat_bytes = sizeof(int64_t) * 4 * P.nbm * P.Hq;
-  const size_t cost_bytes = sizeof(int64_t) * kQilCands * P.Hq;
+  const size_t cost_bytes = sizeof(int64_t) * kQilCands * (1 + kKilCands) * P.Hq;
   const size_t head_bytes = aligned(sizeof(int32_t) * CNT_N) + aligned(feat_bytes) + cost_bytes;
   PinnedBuf pin(head_bytes);
   if (!pin.p) return bail(fail(BSA_ERR_OUT_OF_MEMORY, "pinned host allocation failed"));
@@ -648,6 +669,7 @@ bsa_status bsa_plan(const bsa_problem *pr, const uint8_t *mask, const int32_t *p
   P.feat.assign(hf, hf + feat_bytes / 8);
   const int64_t *hcost = (const int64_t *)((const uint8_t *)hf + aligned(feat_bytes));
   P.qil_cost.assign(hcost, hcost + kQilCands * P.Hq);
+  P.kil_cost.assign(hcost + kQilCands * P.Hq, hcost + kQilCands * (1 + kKilCands) * P.Hq);
   if (hc[CNT_BADPAGE]) return bail(fail(BSA_ERR_INVALID_ARG, "page table entry outside [0, num_pages)"));
   tr.mark("read-back");
 
@@ -920,6 +942,7 @@ bsa_status bsa_plan_export(bsa_plan_t plan, void *host_buf, size_t *bytes) {
   put(P.bq.data(), sizeof(int32_t) * P.Hq);
   put(P.bk.data(), sizeof(int32_t) * P.Hq);
   put(P.qil.data(), sizeof(int32_t) * P.Hq);
+  put(P.kil.data(), sizeof(int32_t) * P.Hq);
   put(P.feat.data(), sizeof(int64_t) * P.feat.size());
   if (bsa_status s = put_dev(P.list_off, sizeof(int32_t) * (P.nlists + 1))) return s;
   if (bsa_status s = put_dev(P.ent_kt, sizeof(int32_t) * nent)) return s;

@@ -493,6 +493,16 @@ __device__ __forceinline__ void dma16(v4u32 rsrc, int voff, uint32_t lds_addr) {
       : "v"(voff), "s"(rsrc), "s"(lds_addr)
       : "m0");
 }
+// The same with a uniform byte offset added to the lane's (soffset).
+__device__ __forceinline__ void dma16_so(v4u32 rsrc, int voff, uint32_t lds_addr, int soff) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, %3 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "s"(lds_addr), "s"(soff)
+      : "m0");
+}
 
 // s_waitcnt with only the vector-memory counter constrained (<= n, n < 64).
 #define BSA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
@@ -554,7 +564,7 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 w) {
 // steps, whose time goes to waiting on loads rather than to arithmetic): K
 // tile j+4 and V tile j+3 are issued at tile j, so three tiles stream while
 // one is used, with partial waits on the vector-memory counter.
-template <int D, int TK, int TQ, bool PAGED, bool KV8 = false, int NS = 2>
+template <int D, int TK, int TQ, bool PAGED, bool KV8 = false, int NS = 2, bool KIL = false>
 __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) void k_attn_bf16(AttnArgs a) {
   using C = CfgB<D, TK, TQ>;
   // e4m3 tiles at D = 128 stream into LDS as they are (KD)
@@ -693,6 +703,15 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
     const int head = ilv ? head_w + (32 * wave + n) % a.G : head_w;
     const int qbase = a.pack ? 0 : 32 * wave;
     const HeadMeta hm = a.hm[head_w];
+    // First key of key tile kt, and the keys skipped between its two 32-key
+    // blocks (key column c sits at x + c, plus y for c >= 32; contiguous
+    // tiles: (kt * TK, 0)). KIL: the plan has key-interleaved heads (then
+    // 128 x 64 tiles over contiguous K/V); other plans run without the
+    // arithmetic.
+    auto ktile = [&](int kt) -> int2 {
+      if constexpr (KIL) return key_tile_span(hm, kt);
+      return make_int2(kt * TK, 0);
+    };
     // (a tile that merges query blocks may take them interleaved: its
     // 32-row slices then lie in different places of the sequence)
     const int64_t q0 = ilv ? (int64_t)qt * a.tr + (32 * wave) / a.G
@@ -743,15 +762,17 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
     const uint8_t *v8base = (const uint8_t *)a.v + (PAGED ? 0 : b * a.v_sb) + g * a.v_sh;
     auto load8 = [&](const void *base_, int64_t sb, int64_t ss, const Meta &m, uint4 (&r)[L8 > 0 ? L8 : 1]) {
       const uint8_t *base = (const uint8_t *)base_;
-      const int k0 = m.kt * TK;
-      const int left = min(skv32 - k0, TK);
+      const int2 kt2 = ktile(m.kt);
+      const int k0 = kt2.x;
+      const int left = skv32 - k0;  // the tile's rows at positions below this exist
       const int prow = ptiles_pow2 ? (m.kt & (ptiles - 1)) * TK : (m.kt % max(ptiles, 1)) * TK;
       const uint8_t *tb = PAGED ? base + (int64_t)m.pg * sb + (int64_t)prow * ss : base + (int64_t)k0 * ss;
 #pragma unroll
       for (int u = 0; u < L8; ++u) {
         const int x = tid + C::THREADS * u;
         const int row = x / (D / 16), c8 = x % (D / 16);
-        r[u] = (x < TK * D / 16 && row < left) ? *(const uint4 *)(tb + (int64_t)row * ss + 16 * c8)
+        const int pos = row + (row >= 32 ? kt2.y : 0);
+        r[u] = (x < TK * D / 16 && pos < left) ? *(const uint4 *)(tb + (int64_t)pos * ss + 16 * c8)
                                                : make_uint4(0, 0, 0, 0);
       }
     };
@@ -773,8 +794,13 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
     // Rows past the sequence end lie beyond the descriptor's range and read 0.
     auto issue = [&](const uint16_t *base, int64_t sb, int64_t ss, const Meta &m, uint8_t *dst_tile,
                      int off0, int step) {
-      const int k0 = m.kt * TK;
-      const int left = min(skv32 - k0, TK);  // rows of the tile that exist
+      const int2 kt2 = ktile(m.kt);
+      const int k0 = kt2.x;
+      // rows of the tile's span that exist (its second block lies kt2.y rows
+      // further on in a key-interleaved tile; the rows between are not read)
+      const int left = min(skv32 - k0, TK + kt2.y);
+      // Extra byte offset of the loads that fill the tile's second 32-key block.
+      const int soff = kt2.y * (int)ss * 2;
       // Row of the tile within its page (pages hold whole key tiles).
       const int prow = ptiles_pow2 ? (m.kt & (ptiles - 1)) * TK : (m.kt % max(ptiles, 1)) * TK;
       const uint16_t *tb = PAGED ? base + (int64_t)m.pg * sb + (int64_t)prow * ss
@@ -789,7 +815,8 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
 #pragma unroll
         for (int u = 0; u < C::LOADS; ++u) {
           uint8_t *dst = dst_tile + (u * C::THREADS + wave * 64) * 16;
-          dma16(rs, off0 + u * step, (uint32_t)(uintptr_t)(lds_void *)dst);
+          if (KIL && u * C::RPL >= 32) dma16_so(rs, off0 + u * step, (uint32_t)(uintptr_t)(lds_void *)dst, soff);
+          else dma16(rs, off0 + u * step, (uint32_t)(uintptr_t)(lds_void *)dst);
         }
       } else {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)tb, 0, bytes, 0x00020000);
@@ -801,7 +828,8 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
 #pragma unroll
         for (int u = 0; u < C::LOADS; ++u) {
           uint8_t *dst = dst_tile + u * C::THREADS * 16 + wofs;  // lane-linear 1 KiB per wave
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, off0 + u * step, 0, 0, 0);
+          const int vo = off0 + u * step + (u * C::RPL >= 32 ? soff : 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, vo, 0, 0, 0);
         }
       }
     };
@@ -820,8 +848,10 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
     const int k8off0 = trow8 * (int)a.k_ss + ((tpos8 ^ swz8_k(trow8)) << 4);
     const int v8off0 = trow8 * (int)a.v_ss + ((tpos8 ^ swz8_v(trow8)) << 4);
     auto issue8 = [&](const uint8_t *base, int64_t sb, int64_t ss, const Meta &m, uint8_t *dst_tile, int off0) {
-      const int k0 = m.kt * TK;
-      const int left = min(skv32 - k0, TK);
+      const int2 kt2 = ktile(m.kt);
+      const int k0 = kt2.x;
+      const int left = min(skv32 - k0, TK + kt2.y);
+      const int soff = kt2.y * (int)ss;  // loads of the second 32-key block
       const int prow = ptiles_pow2 ? (m.kt & (ptiles - 1)) * TK : (m.kt % max(ptiles, 1)) * TK;
       const uint8_t *tb = PAGED ? base + (int64_t)m.pg * sb + (int64_t)prow * ss : base + (int64_t)k0 * ss;
       const int bytes = (left - 1) * (int)ss + D;
@@ -831,14 +861,16 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
 #pragma unroll
         for (int u = 0; u < LOADS8; ++u) {
           uint8_t *dst = dst_tile + (u * C::THREADS + wave * 64) * 16;
-          dma16(rs, off0 + u * RPL8 * (int)ss, (uint32_t)(uintptr_t)(lds_void *)dst);
+          if (KIL && u * RPL8 >= 32) dma16_so(rs, off0 + u * RPL8 * (int)ss, (uint32_t)(uintptr_t)(lds_void *)dst, soff);
+          else dma16(rs, off0 + u * RPL8 * (int)ss, (uint32_t)(uintptr_t)(lds_void *)dst);
         }
       } else {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)tb, 0, bytes, 0x00020000);
 #pragma unroll
         for (int u = 0; u < LOADS8; ++u) {
           uint8_t *dst = dst_tile + (u * C::THREADS + wave * 64) * 16;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, off0 + u * RPL8 * (int)ss, 0, 0, 0);
+          const int vo = off0 + u * RPL8 * (int)ss + (u * RPL8 >= 32 ? soff : 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, vo, 0, 0, 0);
         }
       }
     };
@@ -944,16 +976,19 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
       if (lj) {
       // ---- mask tile j (sequence end, causal diagonal, dead sub-blocks) ----
       // 32-bit scalar tests: positions and the causal offset are below 2^31.
-      const int kb0 = m0.kt * TK;
+      const int2 kt2 = ktile(m0.kt);
+      const int kb0 = kt2.x;
       const uint32_t live = m0.lv;
-      const bool need = (kb0 + TK > skv32) || (a.causal && kb0 + TK - 1 > qlim0) ||
+      const bool need = (kb0 + kt2.y + TK > skv32) || (a.causal && kb0 + TK - 1 > qlim0) ||
                         ((uint64_t)live & wbits) != wbits;
       if (need) {
         // Allowed keys of this lane's query as bit masks over the tile (64
         // keys per mask): live key sub-blocks, then the prefix of keys that
-        // exist and satisfy the causal bound.
+        // exist and satisfy the causal bound. (In a key-interleaved tile, never
+        // causal, the first block is whole whenever the second lies kt2.y
+        // further on, so the prefix counts from the second block's shift.)
         const uint32_t lbits = live >> qsub;
-        int lim = skv32 - kb0;
+        int lim = skv32 - kb0 - kt2.y;
         if (a.causal) lim = min(lim, qlim0 + qd + 1 - kb0);
         const int klim = max(0, min(lim, TK));
         const int ak = 1 << hm.lk;  // keys per live bit
@@ -1285,23 +1320,26 @@ __global__ void k_zero_queues(int *q) {
   if (threadIdx.x < kQueuesPerSet) q[threadIdx.x] = 0;
 }
 
-template <int D, int TK, bool BF, int TQ, bool PAGED = false, bool KV8 = false, int NS = 2>
+template <int D, int TK, bool BF, int TQ, bool PAGED = false, bool KV8 = false, int NS = 2, bool KIL = false>
 bsa_status launch_one(const Plan &p, const AttnArgs &a, hipStream_t s) {
-  if constexpr (BF && !KV8 && NS == 2)
+  if constexpr (BF && !KV8 && NS == 2 && !KIL)
     if (a.kv8) return launch_one<D, TK, BF, TQ, PAGED, true>(p, a, s);
-  if constexpr (BF && !PAGED && NS == 2)
+  if constexpr (BF && !PAGED && NS == 2 && !KIL)
     if (a.paged) return launch_one<D, TK, BF, TQ, true, KV8>(p, a, s);
+  // Plans with key-interleaved heads (128 x 64 tiles, contiguous K/V).
+  if constexpr (BF && !PAGED && NS == 2 && !KIL && TK == 64 && TQ == 128)
+    if (p.key_interleaved) return launch_one<D, TK, BF, TQ, PAGED, KV8, NS, true>(p, a, s);
   // Interleaved tiles (a few live rows each: decode steps) of e4m3 K/V stream
   // four deep (eight 8 KiB slots, two workgroups per CU). A bf16 ring that
   // deep needs 128 KiB of LDS, one workgroup per CU, and measured slower.
-  if constexpr (BF && NS == 2 && D == 128 && TK == 64 && TQ == 128 && KV8)
+  if constexpr (BF && NS == 2 && D == 128 && TK == 64 && TQ == 128 && KV8 && !KIL)
     if (a.pack == 2) return launch_one<D, TK, BF, TQ, PAGED, KV8, 4>(p, a, s);
   // Persistent grid: CUs x resident workgroups, per device (devices may
   // differ in CU count).
   constexpr int kMaxDev = 64;
   static std::atomic<int> grids[kMaxDev];
   const int threads = BF ? 64 * (TQ / 32) : kThreads;
-  auto kern = BF ? (void (*)(AttnArgs))k_attn_bf16<D, TK, TQ, PAGED, KV8, NS> : (void (*)(AttnArgs))k_attn<D, 64, false>;
+  auto kern = BF ? (void (*)(AttnArgs))k_attn_bf16<D, TK, TQ, PAGED, KV8, NS, KIL> : (void (*)(AttnArgs))k_attn<D, 64, false>;
   int dev = 0;
   HIP_TRY(hipGetDevice(&dev));
   int g = (dev >= 0 && dev < kMaxDev) ? grids[dev].load(std::memory_order_relaxed) : 0;

@@ -132,6 +132,16 @@ __device__ __forceinline__ void dma_b128(v4u32 rsrc, int voff, uint32_t lds_addr
       : "v"(voff), "s"(rsrc), "s"(lds_addr)
       : "m0");
 }
+// The same with a uniform byte offset added to the lane's (soffset).
+__device__ __forceinline__ void dma_b128_so(v4u32 rsrc, int voff, uint32_t lds_addr, int soff) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, %3 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "s"(lds_addr), "s"(soff)
+      : "m0");
+}
 __device__ __forceinline__ void dma_b32(v4u32 rsrc, int voff, uint32_t lds_addr) {
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
@@ -152,7 +162,7 @@ __device__ __forceinline__ uint32_t lds_addr_of(const uint8_t *p) {
 // past the sequence end read as zero), two buffers, the next tile's loads in
 // flight while the current one is computed. K is read as rows (the S^T
 // operand) and transposed (the K^T operand of dQ^T); V as rows.
-template <int D, int TK, int TQ>
+template <int D, int TK, int TQ, bool KIL = false>
 __global__ __launch_bounds__(2 * TQ, TQ == 128 ? 2 : 1) void k_bwd_dq(BwdArgs a) {
   constexpr int T = 2 * TQ;                     // 64 lanes per 32 query rows
   constexpr int WAVES = TQ / 32;
@@ -215,9 +225,16 @@ __global__ __launch_bounds__(2 * TQ, TQ == 128 ? 2 : 1) void k_bwd_dq(BwdArgs a)
   const int koff0 = trow * (int)a.k_ss * 2 + ((tpos ^ swz<D>(trow)) << 4);
   const int voff0 = trow * (int)a.v_ss * 2 + ((tpos ^ swz<D>(trow)) << 4);
   // Loads of tile j (entry e0 + j) into buffer j & 1: K at 2 * buf * TILEB, V after it.
+  // First key of a key tile and the keys between its two 32-key blocks
+  // (KIL: the plan has key-interleaved heads, with 128 x 64 tiles).
+  auto ktile = [&](int kt) -> int2 {
+    if constexpr (KIL) return key_tile_span(hm, kt);
+    return make_int2(kt * TK, 0);
+  };
   auto issue = [&](int j) {
-    const int k0 = ((const cint32 *)a.ent_kt)[e0 + j] * TK;
-    const int left = min(skv32 - k0, TK);
+    const int2 kt2 = ktile(((const cint32 *)a.ent_kt)[e0 + j]);
+    const int k0 = kt2.x;
+    const int left = min(skv32 - k0, TK + kt2.y);
     uint8_t *dst = lds + 2 * (j & 1) * TILEB;
     const v4u32 rk = raw_rsrc(Kb + (int64_t)k0 * a.k_ss, (left - 1) * (int)a.k_ss * 2 + D * 2);
     const v4u32 rv = raw_rsrc(Vb + (int64_t)k0 * a.v_ss, (left - 1) * (int)a.v_ss * 2 + D * 2);
@@ -226,8 +243,13 @@ __global__ __launch_bounds__(2 * TQ, TQ == 128 ? 2 : 1) void k_bwd_dq(BwdArgs a)
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       uint8_t *d = dst + (u * T + wave * 64) * 16;
-      dma_b128(rk, koff0 + u * RPL * (int)a.k_ss * 2, lds_addr_of(d));
-      dma_b128(rv, voff0 + u * RPL * (int)a.v_ss * 2, lds_addr_of(d + TILEB));
+      if (KIL && u * RPL >= 32) {  // rows of the tile's second 32-key block
+        dma_b128_so(rk, koff0 + u * RPL * (int)a.k_ss * 2, lds_addr_of(d), kt2.y * (int)a.k_ss * 2);
+        dma_b128_so(rv, voff0 + u * RPL * (int)a.v_ss * 2, lds_addr_of(d + TILEB), kt2.y * (int)a.v_ss * 2);
+      } else {
+        dma_b128(rk, koff0 + u * RPL * (int)a.k_ss * 2, lds_addr_of(d));
+        dma_b128(rv, voff0 + u * RPL * (int)a.v_ss * 2, lds_addr_of(d + TILEB));
+      }
     }
   };
 
@@ -249,9 +271,10 @@ __global__ __launch_bounds__(2 * TQ, TQ == 128 ? 2 : 1) void k_bwd_dq(BwdArgs a)
     if (j + 1 < nent) issue(j + 1);
     const uint8_t *__restrict__ ks = lds + 2 * (j & 1) * TILEB;
     const uint8_t *__restrict__ vs = ks + TILEB;
-    const int kb0 = ((const cint32 *)a.ent_kt)[e0 + j] * TK;
+    const int2 kt2 = ktile(((const cint32 *)a.ent_kt)[e0 + j]);
+    const int kb0 = kt2.x;
     const uint32_t live = ((const cuint32 *)a.ent_live)[e0 + j];
-    const bool need = (kb0 + TK > skv32) || (a.causal && kb0 + TK - 1 > qlim0) ||
+    const bool need = (kb0 + kt2.y + TK > skv32) || (a.causal && kb0 + TK - 1 > qlim0) ||
                       ((uint64_t)live & wbits) != wbits;
     // Allowed keys of this lane's query as bit masks over the tile.
     uint64_t km[(TK + 63) / 64];
@@ -259,7 +282,9 @@ __global__ __launch_bounds__(2 * TQ, TQ == 128 ? 2 : 1) void k_bwd_dq(BwdArgs a)
     for (int w64 = 0; w64 < (TK + 63) / 64; ++w64) km[w64] = ~0ull;
     if (need) {
       const uint32_t lbits = live >> qsub;
-      int lim = skv32 - kb0;
+      // (a key-interleaved tile, never causal, has its first block whole
+      // whenever the second lies kt2.y further on)
+      int lim = skv32 - kb0 - kt2.y;
       if (a.causal) lim = min(lim, qlim0 + n + 1 - kb0);
       const int klim = max(0, min(lim, TK));
       const int ak = 1 << hm.lk;
@@ -354,10 +379,16 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdArgs a) {
   const int item = blockIdx.x;
   const int kp = item % nkp, g = (item / nkp) % a.Hkv, b = item / (nkp * a.Hkv);
   const int kt0 = kp * NKT;
-  const int kb0 = kp * KW;                      // first key of the workgroup
   const int wkt = (32 * wave) / TKP;            // this wave's tile within the group
   const int kloc = (32 * wave) % TKP + n;       // this lane's key within its tile
-  const int key = kb0 + 32 * wave + n;
+  // This lane's key: the tile's first key plus its column, and past the
+  // first 32 keys the gap of a key-interleaved head's 64-key tile (one query
+  // head per kv head then, so the kv head's own metadata gives it).
+  int key = (kt0 + wkt) * TKP + kloc;
+  if constexpr (TKP == 64) {
+    const int2 kt2 = key_tile_span(a.hm[g * a.G], kt0 + wkt);
+    key = kt2.x + kloc + (kloc >= 32 ? kt2.y : 0);
+  }
   const int skv32 = (int)a.Skv, sq32 = (int)a.Sq;  // sequence lengths are below 2^31
   const bool kvalid = key < skv32;
   const int lb = a.nlb == 1 ? 0 : b;
@@ -563,16 +594,19 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdArgs a) {
 }
 
 template <int D, int TK>
-void launch_dq(const BwdArgs &a, int tq, unsigned grid, hipStream_t s) {
+void launch_dq(const BwdArgs &a, int tq, bool kil, unsigned grid, hipStream_t s) {
   if (tq == 256) hipLaunchKernelGGL((k_bwd_dq<D, TK, 256>), dim3(grid), dim3(512), 0, s, a);
+  else if constexpr (TK == 64)
+    if (kil) hipLaunchKernelGGL((k_bwd_dq<D, TK, 128, true>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_bwd_dq<D, TK, 128>), dim3(grid), dim3(256), 0, s, a);
   else hipLaunchKernelGGL((k_bwd_dq<D, TK, 128>), dim3(grid), dim3(256), 0, s, a);
 }
 
 template <int D>
-void launch_d(const BwdArgs &a, unsigned dq_grid, unsigned kv_grid, hipStream_t s) {
+void launch_d(const BwdArgs &a, bool kil, unsigned dq_grid, unsigned kv_grid, hipStream_t s) {
   if (dq_grid) {
-    if (a.tk == 128) launch_dq<D, 128>(a, a.tq, dq_grid, s);
-    else launch_dq<D, 64>(a, a.tq, dq_grid, s);
+    if (a.tk == 128) launch_dq<D, 128>(a, a.tq, false, dq_grid, s);
+    else launch_dq<D, 64>(a, a.tq, kil, dq_grid, s);
   }
   if (kv_grid) {
     if (a.tk == 128) hipLaunchKernelGGL((k_bwd_dkdv<D, 128>), dim3(kv_grid), dim3(256), 0, s, a);
@@ -587,8 +621,8 @@ bsa_status backward_launch(const Plan &p, const BwdArgs &a, hipStream_t s) {
   if (p.nrows > 0x7fffffff || kv_items > 0x7fffffff)
     return fail(BSA_ERR_UNSUPPORTED, "too many tiles for one launch");
   const unsigned dq_grid = (unsigned)p.nrows, kv_grid = (unsigned)kv_items;
-  if (p.D == 128) launch_d<128>(a, dq_grid, kv_grid, s);
-  else launch_d<64>(a, dq_grid, kv_grid, s);
+  if (p.D == 128) launch_d<128>(a, p.key_interleaved, dq_grid, kv_grid, s);
+  else launch_d<64>(a, p.key_interleaved, dq_grid, kv_grid, s);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(BSA_ERR_HIP, std::string("backward launch: ") + hipGetErrorString(e));
   return BSA_OK;

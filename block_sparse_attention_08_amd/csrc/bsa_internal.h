@@ -23,11 +23,15 @@ struct HeadMeta {
   int32_t nqb, nkb, bq, bk;
   int32_t lq, lk, mk;
   int32_t lqil;      // log2 of the query-block interleave (0: consecutive blocks)
+  int32_t lkil;      // log2 of the key-block interleave (0: consecutive blocks)
 };
 
 // Query-block interleave candidates: s = 1, 2, 4, 8 for 128-row tiles that
 // merge query blocks of 32 or 64 rows (non-union plans).
 constexpr int kQilCands = 4;
+// Key-block interleave candidates: s = 1, 2, 4, 8 for 64-key tiles that merge
+// two 32-key blocks (non-union, non-paged plans without a causal bound).
+constexpr int kKilCands = 4;
 
 // Logical query block of sub-block iq of physical tile t when a tile merges
 // 2^lm blocks with interleave 2^ls: in each full group of 2^(ls+lm) blocks,
@@ -46,6 +50,24 @@ __host__ __device__ inline int64_t tile_query(const HeadMeta &m, int ltq, int64_
   if (m.lqil == 0) return (qt << ltq) + R;
   const int64_t qb = qblock_of(qt, R >> m.lq, m.lqil, ltq - m.lq, m.nqb);
   return (qb << m.lq) + (R & ((1 << m.lq) - 1));
+}
+
+// Key block of key sub-block ik of key tile kt of the head with metadata m
+// when its tiles merge 2^lmk key blocks (the same partition as qblock_of).
+__host__ __device__ inline int64_t tile_key_block(const HeadMeta &m, int lmk, int64_t kt, int ik) {
+  return qblock_of(kt, ik, m.lkil, lmk, m.nkb);
+}
+
+// Key tile kt of 64 keys over two 32-key blocks of the head with metadata m:
+// (x, y) such that key column c of the tile is key x + c, plus y when
+// c >= 32 (y = 0 unless the head's key blocks are interleaved, then the
+// tile's blocks lie s apart in each full group of 2s blocks).
+__host__ __device__ inline int2 key_tile_span(const HeadMeta &m, int kt) {
+  const int ls = m.lkil;
+  if (ls == 0) return make_int2(kt * 64, 0);
+  const int lg = ls + 1, full = m.nkb >> lg;
+  if (kt < (full << ls)) return make_int2((((kt >> ls) << lg) + (kt & ((1 << ls) - 1))) * 32, ((1 << ls) - 1) * 32);
+  return make_int2(((full << lg) + ((kt - (full << ls)) << 1)) * 32, 0);
 }
 
 // Counters written on the device by the planner.
@@ -67,6 +89,9 @@ struct Plan {
   std::vector<int32_t> bq, bk;
   std::vector<int32_t> qil;          // query-block interleave per head (1 = consecutive)
   std::vector<int64_t> qil_cost;     // [Hq][kQilCands] key blocks listed per candidate
+  std::vector<int32_t> kil;          // key-block interleave per head (1 = consecutive)
+  bool key_interleaved = false;      // some head has kil > 1
+  std::vector<int64_t> kil_cost;     // [Hq][kQilCands][kKilCands] key tiles listed
   // regime and geometry
   Regime rg;
   int32_t tr;  // query positions per physical row
@@ -197,7 +222,7 @@ __host__ __device__ inline bool acsr_in_run(const bsa_acsr_run &u, int64_t f, in
 bsa_status acsr_check(const bsa_problem &pr, const bsa_acsr_head *heads);
 void acsr_features(const bsa_problem &pr, const bsa_acsr_head *heads, int64_t *out);
 // Query-block interleave costs [Hq][kQilCands] counted from the runs.
-void acsr_qil_costs(const bsa_problem &pr, const bsa_acsr_head *heads, int64_t *out);
+void acsr_qil_costs(const bsa_problem &pr, const bsa_acsr_head *heads, int64_t *out, int64_t *kout);
 // Planner side of an ACSR plan: head metadata and descriptors to the device
 // through kernel arguments (no host buffer has to outlive the call), features
 // on the host.

@@ -153,9 +153,13 @@ __global__ void k_head_features(const int32_t *__restrict__ rowf, const HeadMeta
 // cost[h][c] (integer atomics: the sums do not depend on their order). Only
 // heads whose 32- or 64-row blocks merge into 128-row tiles, and only
 // candidates with s * mq <= nq, are counted; the host picks the cheapest.
+// With keys_ok (no causal bound, no paging), heads of 32-key blocks also
+// count, per key interleave s' = 2^c' with 2 s' <= nk, the 64-key tiles in
+// which the tile selects a block, into kcost[h][c][c'].
 __global__ void k_qil_cost(const uint8_t *__restrict__ mask, const HeadMeta *__restrict__ hm, int Hq,
                            int nbm, int64_t mask_bstride, const int64_t *__restrict__ wave_off,
-                           int64_t nwaves, unsigned long long *__restrict__ cost) {
+                           int64_t nwaves, unsigned long long *__restrict__ cost, int keys_ok,
+                           unsigned long long *__restrict__ kcost) {
   const int lane = threadIdx.x & 63;
   const int64_t wv = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 6;
   if (wv >= nwaves) return;
@@ -185,6 +189,28 @@ __global__ void k_qil_cost(const uint8_t *__restrict__ mask, const HeadMeta *__r
   }
   cnt = wave_sum(cnt);
   if (lane == 0 && cnt) atomicAdd(&cost[h * kQilCands + c], (unsigned long long)cnt);
+  if (!keys_ok || m.bk != 32) return;
+  int kc[kKilCands] = {0, 0, 0, 0};
+  for (int64_t kt = lane; 2 * kt < m.nkb; kt += 64) {
+#pragma unroll
+    for (int ck = 0; ck < kKilCands; ++ck) {
+      if ((int64_t(2) << ck) > m.nkb) break;
+      int any = 0;
+      for (int ik = 0; ik < 2 && !any; ++ik) {
+        const int64_t kb = qblock_of(kt, ik, ck, 1, m.nkb);
+        for (int iq = 0; iq < (1 << lm) && !any && kb < m.nkb; ++iq) {
+          const int64_t qb = qblock_of(t, iq, c, lm, m.nqb);
+          any = qb < m.nqb && mb[qb * m.nkb + kb] != 0;
+        }
+      }
+      kc[ck] += any;
+    }
+  }
+#pragma unroll
+  for (int ck = 0; ck < kKilCands; ++ck) {
+    const int v = wave_sum(kc[ck]);
+    if (lane == 0 && v) atomicAdd(&kcost[(h * kQilCands + c) * kKilCands + ck], (unsigned long long)v);
+  }
 }
 
 // Count page-table entries that the keys [0, Skv) use and that point outside
@@ -240,7 +266,7 @@ __device__ __forceinline__ uint32_t live_bits(const MapArgs &a, int bm, int h, i
     const int nruns = a.acsr ? a.acsr[h].num_runs : 0;
     for (int j = 0; j < nruns; ++j) first[j] = acsr_first(a.acsr[h].runs[j], qb);
     for (int ik = 0; ik < mk; ++ik) {
-      const int64_t kb = bk < a.tk ? kt * mk + ik : (kt << ltk) >> lbk;
+      const int64_t kb = bk < a.tk ? tile_key_block(m, ltk - lbk, kt, ik) : (kt << ltk) >> lbk;
       if (kb >= m.nkb) continue;
       if (a.acsr) {
         bool sel = false;
@@ -725,10 +751,12 @@ bsa_status plan_features(Plan &p, const uint8_t *mask, const int32_t *page_table
     }
     woff[p.Hq * kQilCands] = nw;
     if (nw > 0) {
-      int64_t *woff_dev = (int64_t *)(p.qil_dev + (size_t)p.Hq * kQilCands);
+      unsigned long long *kcost = p.qil_dev + (size_t)p.Hq * kQilCands;
+      int64_t *woff_dev = (int64_t *)(kcost + (size_t)p.Hq * kQilCands * kKilCands);
       if (bsa_status st = put_async(woff_dev, woff.data(), sizeof(int64_t) * woff.size(), s)) return st;
       hipLaunchKernelGGL(k_qil_cost, dim3(grid_for(nw * 64)), dim3(kThreads), 0, s, mask, p.hmeta, p.Hq,
-                         (int)p.nbm, mask_bstride, (const int64_t *)woff_dev, nw, p.qil_dev);
+                         (int)p.nbm, mask_bstride, (const int64_t *)woff_dev, nw, p.qil_dev,
+                         (!p.causal && !p.paged && p.dtype == BSA_BF16 && p.G == 1) ? 1 : 0, kcost);
     }
   }
   if (p.paged && p.Skv > 0) {
@@ -759,7 +787,8 @@ bsa_status plan_features_acsr(Plan &p, const bsa_acsr_head *heads, bsa_acsr_head
   p.feat.assign(4 * (size_t)p.Hq, 0);
   acsr_features(pr, heads, p.feat.data());
   p.qil_cost.assign((size_t)kQilCands * p.Hq, 0);
-  acsr_qil_costs(pr, heads, p.qil_cost.data());
+  p.kil_cost.assign((size_t)kQilCands * kKilCands * p.Hq, 0);
+  acsr_qil_costs(pr, heads, p.qil_cost.data(), p.kil_cost.data());
   return BSA_OK;
 }
 
@@ -804,6 +833,7 @@ bsa_status plan_build(Plan &p, const uint8_t *mask, const int32_t *page_table, v
     const int aq = std::min(m.bq, p.rg.tq), ak = std::min(m.bk, p.rg.tk);
     m.lq = p.uni ? 30 : __builtin_ctz(aq), m.lk = __builtin_ctz(ak), m.mk = p.rg.tk / ak;
     m.lqil = __builtin_ctz(p.qil[h]);
+    m.lkil = __builtin_ctz(p.kil[h]);
   }
   if (bsa_status st = put_async(p.hmeta, p.hmeta_host.data(), sizeof(HeadMeta) * p.Hq, s)) return st;
 

@@ -270,8 +270,9 @@ bsa_status bsa_backward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *
                         const bsa_tensor *dout, bsa_tensor *dq, bsa_tensor *dk, bsa_tensor *dv,
                         void *stream);
 
-/* Canonical byte image of a plan (header, features, lists, entries, rows,
- * work list), for comparison with the reference planner. With host_buf NULL
+/* Canonical byte image of a plan (header; block sizes and the query- and
+ * key-block interleave of each head; features, lists, entries, rows, work
+ * list), for comparison with the reference planner. With host_buf NULL
  * only *bytes is set to the size needed; otherwise *bytes is the capacity on
  * input and the size on output. Synchronises with the plan's stream. */
 bsa_status bsa_plan_export(bsa_plan_t plan, void *host_buf, size_t *bytes);

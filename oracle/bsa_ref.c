@@ -762,7 +762,8 @@ int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_tabl
 
   /* 2c. Key-block interleave per head: when 128 x 64 tiles merge two
    * 32-key blocks per key tile and the head's query tiles merge blocks of 32
-   * or 64 rows (no union, no paging, no causal bound), key tile kt gathers
+   * or 64 rows (bf16, one query head per kv head, no union, no paging, no
+   * causal bound), key tile kt gathers
    * key blocks qblock(kt, ik, s, 2, nk) for the s in {1, 2, 4, 8}
    * (2 s <= the head's key blocks) whose query tiles (with the interleave of
    * 2b) list the fewest key tiles, the smallest s on ties; every other head
@@ -771,8 +772,8 @@ int ref_plan(const ref_problem *p, const uint8_t *mask, const int32_t *page_tabl
   for (int h = 0; h < p->hq; ++h) {
     kil[h] = 1;
     const int64_t bq = p->bq[h], bk = p->bk[h], nk = ceil_div(p->skv, bk);
-    if (p->gqa_union || p->paged || p->causal || tq != 128 || tk != 64 || bk != 32 || bq >= tq ||
-        bq < 32)
+    if (p->gqa_union || p->paged || p->causal || p->dtype != 0 || p->hq != p->hkv || tq != 128 ||
+        tk != 64 || bk != 32 || bq >= tq || bq < 32)
       continue;
     const int64_t mq = tq / bq, mk = tk / bk;
     int64_t best = key_interleave_cost(p, mask, moff, h, mq, qil[h], mk, 1);

@@ -112,6 +112,9 @@ CASES = {
     "tiny_video": lambda: W.video_dit(heads=2, grid=(16, 6, 12), seed=1),
     "tiny_affine32": lambda: W.affine(bs=32, batch=2, heads=3, s=1024, window=128),
     "periodic_interleave": lambda: W.periodic(sq=1000, skv=700, causal=True, causal_offset=80, seed=5),
+    # key-interleaved 64-key tiles, last key block partial
+    "periodic_keys": lambda: W.periodic(sq=1000, skv=1000, bk=32, seed=6),
+    "periodic_keys_d128": lambda: W.periodic(batch=1, sq=700, skv=1240, bk=32, d=128, seed=7),
 }
 
 

@@ -72,6 +72,9 @@ CASES = {
     "union_paged": lambda: W.random_problem(batch=2, hq=8, hkv=2, sq=200, skv=900, d=128, bq=128,
                                             bk=128, density=0.08, gqa_union=True, causal=True,
                                             causal_offset=700, paged=True, page_size=64, seed=603),
+    # key-interleaved 64-key tiles (32-key blocks s apart), last block partial
+    "periodic_keys_d64": lambda: W.periodic(batch=1, sq=640, skv=1000, bk=32, seed=604),
+    "periodic_keys_d128": lambda: W.periodic(batch=1, sq=640, skv=1000, bk=32, d=128, seed=605),
 }
 
 

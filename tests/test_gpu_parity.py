@@ -60,6 +60,11 @@ SMALL = {
     # merged query blocks taken interleaved (periods 2, 4, 8), causal, ragged
     "periodic_interleave": lambda: W.periodic(sq=1000, skv=700, causal=True, causal_offset=80, seed=3),
     "dilated_bs64": lambda: W.affine(bs=64, batch=1, heads=3, s=4096, window=256),
+    # 64-key tiles gathering 32-key blocks s apart (key interleave), the last
+    # key block partial, D = 64 and 128
+    "periodic_keys": lambda: W.periodic(sq=1000, skv=1000, bk=32, seed=7),
+    "periodic_keys_d128": lambda: W.periodic(batch=1, sq=777, skv=1240, bk=32, d=128, seed=8),
+    "dilated_bs32": lambda: W.affine(bs=32, batch=1, heads=3, s=4096, window=256),
     "decode_q1": lambda: W.decode(batch=3, hq=8, hkv=2, q_len=1, context=4096, seed=1),
     "decode_q5": lambda: W.decode(batch=2, hq=8, hkv=2, q_len=5, context=3072, seed=2),
     "short_chunk_q16": lambda: W.decode(batch=2, hq=4, hkv=1, d=64, q_len=16, context=2048, seed=3),
@@ -93,7 +98,7 @@ def test_small_default(ref, case):
 @pytest.mark.parametrize("regime", [r for r in REGIMES if r != "default"])
 @pytest.mark.parametrize("case", ["ragged_bf16_d128", "merge_small_blocks", "causal_offset",
                                   "union_paged_causal", "union_g2_ragged", "tiny_fp32",
-                                  "tiny_long_video", "periodic_interleave"])
+                                  "tiny_long_video", "periodic_interleave", "periodic_keys"])
 def test_small_forced_regimes(ref, case, regime):
     run_case(ref, SMALL[case](), lut_text=REGIMES[regime], label=f"{case}/{regime}")
 

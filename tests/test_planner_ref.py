@@ -326,11 +326,13 @@ def test_interleave_choice_random(ref, seed):
 def key_interleave_choice(w, h, qil, tq=128, tk=64):
     """The key interleave the plan specification gives head h, from its
     definition: for 128 x 64 tiles merging two 32-key blocks, query blocks
-    of 32 or 64 rows, no union, paging or causal bound, the s in
+    of 32 or 64 rows, bf16, one query head per kv head, no union, paging or
+    causal bound, the s in
     {1, 2, 4, 8} with 2 s <= nk whose query tiles (interleave qil) list the
     fewest key tiles (summed over mask batches), smallest on ties; else 1."""
     bq, bk = w.bq[h], w.bk[h]
-    if w.gqa_union or w.paged or w.causal or bk != 32 or bq >= tq or bq < 32:
+    if (w.gqa_union or w.paged or w.causal or w.dtype != "bf16" or w.hq != w.hkv or bk != 32
+            or bq >= tq or bq < 32):
         return 1
     mq, nq = tq // bq, -(-w.sq // bq)
     mk, nk = tk // bk, -(-w.skv // bk)
