@@ -13,6 +13,11 @@ regime of each training workload. Rules are written in bucket order, followed
 by a catch-all default.
 
     python -m block_sparse_attention_08_amd.lut.build_lut [--out PATH] [--steps N]
+        [--only NAME,NAME --base PATH]
+
+With --only, just the named buckets are profiled again; every other bucket
+keeps its rule and comment lines from the table at --base (default: the
+packaged table), in bucket order.
 """
 from __future__ import annotations
 
@@ -131,11 +136,34 @@ def time_regime(bsa, w, tensors, regime, steps):
     return dt
 
 
+def kept_buckets(text: str) -> dict:
+    """Per bucket name, its lines in an existing table: the comment lines
+    that start with "# name:" up to and including the bucket's rule line."""
+    out, cur = {}, None
+    for line in text.splitlines():
+        if line.startswith("# ") and ":" in line and not line.startswith("#   "):
+            name = line[2:].split(":")[0]
+            if " " not in name:
+                cur = name
+                out[cur] = []
+        if cur is not None:
+            out[cur].append(line)
+            if line.startswith("rule "):
+                cur = None
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default=os.path.join(HERE, "gfx950.lut"))
     ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--only", default="", help="comma-separated bucket names to profile again")
+    ap.add_argument("--base", default=os.path.join(HERE, "gfx950.lut"))
     args = ap.parse_args()
+    only = {n for n in args.only.split(",") if n}
+    kept = kept_buckets(open(args.base).read()) if only else {}
+    if only and not only <= {b[0] for b in buckets()}:
+        raise SystemExit(f"unknown bucket in --only: {sorted(only)}")
     import torch
     import block_sparse_attention_08_amd as bsa
 
@@ -148,6 +176,9 @@ def main():
              "# Each rule is the regime with the best geometric-mean request time (bsa_plan +"
              " bsa_forward) over its bucket's training workloads; first match wins."]
     for name, key, makers, cands in buckets():
+        if only and name not in only:
+            lines += kept[name]
+            continue
         cands = cands or candidates(None)
         rel = {c: [] for c in cands}
         descr = []
