@@ -1267,49 +1267,75 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
 }
 
 // Split-KV combine: O = sum_s w_s O_s / sum_s w_s with w_s = exp(lse_s - M),
-// LSE = M + ln sum_s w_s, M = max_s lse_s. A record covers one TQ-row tile;
-// two threads per row, each half of the head dimension.
+// LSE = M + ln sum_s w_s, M = max_s lse_s. A record covers one TQ-row tile.
 #undef BSA_SL2
 
 template <int D, bool BF, int TQ>
 __global__ __launch_bounds__(kThreads) void k_combine(AttnArgs a, const int32_t *__restrict__ comb) {
   using E = typename std::conditional<BF, uint16_t, float>::type;
+  // One wave per query row: a workgroup takes four rows of one record per
+  // step (so short and long records alike spread over the whole grid). The
+  // lanes hold D / 64 adjacent columns, so each slot's partial row is one
+  // contiguous read of the wave; the slot weights exp(lse_s - M) are the
+  // same on every lane.
+  constexpr int CPL = D / 64, RPW = kThreads / 64, QUADS = TQ / RPW;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ncomb = a.counters[CNT_COMB];
-  for (int c = blockIdx.x; c < ncomb; c += gridDim.x) {
+  for (int64_t unit = blockIdx.x; unit < (int64_t)ncomb * QUADS; unit += gridDim.x) {
+    const int c = (int)(unit / QUADS);
     const int r = comb[3 * c], s0 = comb[3 * c + 1], k = comb[3 * c + 2];
     if (s0 + k > a.part_slots) continue;  // (never: the scratch holds every slot of the plan)
-    for (int idx = threadIdx.x; idx < 2 * TQ; idx += kThreads) {
-      const int row = idx >> 1, half = idx & 1;
+    {
+      const int row = (int)(unit % QUADS) * RPW + wave;
       const RowPos geo = tile_row(a, r, row);
       const int64_t qpos = geo.q;
       if (qpos >= a.Sq) continue;
       float M = -INFINITY;
-      for (int s = 0; s < k; ++s) M = fmaxf(M, a.part_lse[(int64_t)(s0 + s) * TQ + row]);
+      for (int s = lane; s < k; s += 64) M = fmaxf(M, a.part_lse[(int64_t)(s0 + s) * TQ + row]);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
       E *op = (E *)a.o + geo.b * a.o_sb + geo.head * a.o_sh + qpos * a.o_ss;
+      float *lp = a.lse + ((int64_t)geo.b * a.Hq + geo.head) * a.Sq + qpos;
       if (M == -INFINITY) {
-        for (int d = half * (D / 2); d < (half + 1) * (D / 2); ++d) op[d] = (E)0;
-        if (half == 0) a.lse[((int64_t)geo.b * a.Hq + geo.head) * a.Sq + qpos] = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) op[CPL * lane + j] = (E)0;
+        if (lane == 0) *lp = -INFINITY;
         continue;
       }
-      float wsum = 0.f;
-      for (int s = 0; s < k; ++s) wsum += expf(a.part_lse[(int64_t)(s0 + s) * TQ + row] - M);
-      const float inv = 1.f / wsum;
-      for (int d4 = half * (D / 8); d4 < (half + 1) * (D / 8); ++d4) {
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int s = 0; s < k; ++s) {
-          const int64_t prow = (int64_t)(s0 + s) * TQ + row;
-          const float w = expf(a.part_lse[prow] - M);
-          const float4 x = *(const float4 *)(a.part_o + prow * D + 4 * d4);
-          acc.x += w * x.x, acc.y += w * x.y, acc.z += w * x.z, acc.w += w * x.w;
-        }
-        acc.x *= inv, acc.y *= inv, acc.z *= inv, acc.w *= inv;
-        if constexpr (BF) {
-          *(uint2 *)(op + 4 * d4) = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+      float ws = 0.f;
+      for (int s = lane; s < k; s += 64) ws += expf(a.part_lse[(int64_t)(s0 + s) * TQ + row] - M);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) ws += __shfl_xor(ws, o);
+      float acc[CPL];
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) acc[j] = 0.f;
+#pragma unroll 4
+      for (int s = 0; s < k; ++s) {
+        const int64_t prow = (int64_t)(s0 + s) * TQ + row;
+        const float w = expf(a.part_lse[prow] - M);
+        const float *src = a.part_o + prow * D + CPL * lane;
+        if constexpr (CPL == 2) {
+          const float2 x = *(const float2 *)src;
+          acc[0] += w * x.x, acc[1] += w * x.y;
         } else {
-          *(float4 *)(op + 4 * d4) = acc;
+          acc[0] += w * src[0];
         }
       }
-      if (half == 0) a.lse[((int64_t)geo.b * a.Hq + geo.head) * a.Sq + qpos] = M + logf(wsum);
+      const float inv = 1.f / ws;
+      if constexpr (BF && CPL == 2) {
+        *(uint32_t *)(op + 2 * lane) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+      } else {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          if constexpr (BF) {
+            const uint32_t pk = pack_bf16x2(acc[j] * inv, 0.f);
+            op[CPL * lane + j] = (E)(pk & 0xffffu);
+          } else {
+            op[CPL * lane + j] = acc[j] * inv;
+          }
+        }
+      }
+      if (lane == 0) *lp = M + logf(ws);
     }
   }
 }
@@ -1354,7 +1380,7 @@ bsa_status launch_one(const Plan &p, const AttnArgs &a, hipStream_t s) {
   if constexpr (BF) hipLaunchKernelGGL(k_zero_queues, dim3(1), dim3(64), 0, s, a.queue);
   hipLaunchKernelGGL(kern, dim3(g), dim3(threads), 0, s, a);
   if (p.rg.split > 0 && p.comb_cap > 0) {
-    const int cg = (int)std::min<int64_t>(p.comb_cap, 2048);
+    const int cg = (int)std::min<int64_t>(p.comb_cap * (TQ / (kThreads / 64)), 8192);
     hipLaunchKernelGGL((k_combine<D, BF, TQ>), dim3(cg), dim3(kThreads), 0, s, a, p.comb);
   }
   HIP_TRY(hipGetLastError());

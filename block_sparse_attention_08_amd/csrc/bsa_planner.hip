@@ -307,6 +307,48 @@ __global__ void k_map(MapArgs a) {
   const int bm = a.bcast ? 0 : lb;
   const int64_t base = EMIT ? a.list_off[l] : 0;
   int64_t run = 0;
+  const HeadMeta m = a.hm[h];
+  const int lbq = __builtin_ctz(m.bq), lbk = __builtin_ctz(m.bk);
+  const int ltq = __builtin_ctz(a.tq), ltk = __builtin_ctz(a.tk);
+  const int mq = (!a.uni && m.bq < a.tq) ? 1 << (ltq - lbq) : 1;
+  const int mk = m.bk < a.tk ? 1 << (ltk - lbk) : 1;
+  if (!a.uni && !a.acsr && mq <= 8) {
+    // Mask plans: the list's query blocks, their mask rows and causal
+    // limits do not depend on the key tile, so they are found once (the same
+    // live bits as live_bits below, for up to 8 query sub-blocks).
+    const int64_t aq = m.bq < a.tq ? m.bq : a.tq, ak = m.bk < a.tk ? m.bk : a.tk;
+    const uint8_t *mb = a.mask + bm * a.mask_bstride + m.mask_off;
+    int64_t rowoff[8], lim[8];
+    for (int iq = 0; iq < mq; ++iq) {
+      const int64_t qb = m.bq < a.tq ? qblock_of(qt, iq, m.lqil, ltq - lbq, m.nqb) : (qt << ltq) >> lbq;
+      rowoff[iq] = qb < m.nqb ? qb * m.nkb : -1;
+      const int64_t q0 = m.bq < a.tq ? qb * m.bq : qt * a.tq;
+      // a sub-block is dropped when its first key lies after its last query
+      lim[iq] = a.causal ? min(q0 + aq, a.Sq) - 1 + a.off : INT64_MAX;
+    }
+    for (int64_t k0 = 0; k0 < a.nkt; k0 += 64) {
+      const int64_t kt = k0 + lane;
+      uint32_t live = 0;
+      if (kt < a.nkt)
+        for (int ik = 0; ik < mk; ++ik) {
+          const int64_t kb = m.bk < a.tk ? tile_key_block(m, ltk - lbk, kt, ik) : (kt << ltk) >> lbk;
+          if (kb >= m.nkb) continue;
+          const int64_t kfirst = kt * a.tk + ik * ak;
+          for (int iq = 0; iq < mq; ++iq)
+            if (rowoff[iq] >= 0 && mb[rowoff[iq] + kb] && kfirst <= lim[iq]) live |= 1u << (iq * mk + ik);
+        }
+      const unsigned long long bal = __ballot(live != 0);
+      if (EMIT && live) {
+        const int64_t idx = base + run + __popcll(bal & (unsigned long long)lo_mask(lane));
+        a.ent_kt[idx] = (int32_t)kt;
+        a.ent_live[idx] = live;
+        if (a.paged) a.ent_page[idx] = a.page_table[(int64_t)lb * a.pps + (int)(kt * a.tk) / a.P];
+      }
+      run += __popcll(bal);
+    }
+    if (!EMIT && lane == 0) a.list_len[l] = (int32_t)run;
+    return;
+  }
   for (int64_t k0 = 0; k0 < a.nkt; k0 += 64) {
     const int64_t kt = k0 + lane;
     const uint32_t live = kt < a.nkt ? live_bits(a, bm, h, g, qt, kt) : 0u;
