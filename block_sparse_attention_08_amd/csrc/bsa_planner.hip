@@ -178,13 +178,16 @@ __global__ void k_qil_cost(const uint8_t *__restrict__ mask, const HeadMeta *__r
   const int bm = (int)(k / ntiles);
   const int64_t t = k % ntiles;
   const uint8_t *mb = mask + bm * mask_bstride + m.mask_off;
+  // the tile's mask rows (at most 4: 32- or 64-row blocks in 128-row tiles)
+  int64_t rowoff[4];
+  for (int iq = 0; iq < 4; ++iq) {
+    const int64_t qb = iq < (1 << lm) ? qblock_of(t, iq, c, lm, m.nqb) : m.nqb;
+    rowoff[iq] = qb < m.nqb ? qb * m.nkb : -1;
+  }
   int cnt = 0;
   for (int64_t kb = lane; kb < m.nkb; kb += 64) {
     int any = 0;
-    for (int iq = 0; iq < (1 << lm) && !any; ++iq) {
-      const int64_t qb = qblock_of(t, iq, c, lm, m.nqb);
-      any = qb < m.nqb && mb[qb * m.nkb + kb] != 0;
-    }
+    for (int iq = 0; iq < 4 && !any; ++iq) any = rowoff[iq] >= 0 && mb[rowoff[iq] + kb] != 0;
     cnt += any;
   }
   cnt = wave_sum(cnt);
@@ -198,10 +201,7 @@ __global__ void k_qil_cost(const uint8_t *__restrict__ mask, const HeadMeta *__r
       int any = 0;
       for (int ik = 0; ik < 2 && !any; ++ik) {
         const int64_t kb = qblock_of(kt, ik, ck, 1, m.nkb);
-        for (int iq = 0; iq < (1 << lm) && !any && kb < m.nkb; ++iq) {
-          const int64_t qb = qblock_of(t, iq, c, lm, m.nqb);
-          any = qb < m.nqb && mb[qb * m.nkb + kb] != 0;
-        }
+        for (int iq = 0; iq < 4 && !any && kb < m.nkb; ++iq) any = rowoff[iq] >= 0 && mb[rowoff[iq] + kb] != 0;
       }
       kc[ck] += any;
     }

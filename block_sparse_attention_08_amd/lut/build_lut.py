@@ -67,9 +67,14 @@ def buckets():
         ("mixed-128", "128 bf16 0 *  16 127  16 " + BIG + "  0 " + BIG + "  0 " + BIGIMB + ANYSQ,
          [lambda: W.long_video(heads=20, seed=11), lambda: W.long_video(heads=24, grid=(16, 48, 80), seed=12),
           lambda: W.long_video(heads=16, p_heavy=0.10, seed=13)], None),
+        # 32-token blocks, D=64, low density (regular patterns; tiles merge
+        # four query blocks and two key blocks).
+        ("regular-32-sparse", "64 bf16 0 *  16 32  16 32  0 200  0 " + BIGIMB + ANYSQ,
+         [lambda: W.affine(bs=32, window=768, s=16384), lambda: W.affine(bs=32, window=512, s=8192, batch=4),
+          lambda: W.affine(bs=32, window=1536, s=32768, batch=1)], None),
         # Small blocks, D=64, low density (regular patterns).
         ("regular-64-sparse", "64 bf16 0 *  16 " + BIG + "  16 " + BIG + "  0 200  0 " + BIGIMB + ANYSQ,
-         [lambda: W.affine(bs=64, window=512, s=16384), lambda: W.affine(bs=32, window=768, s=16384),
+         [lambda: W.affine(bs=64, window=512, s=16384), lambda: W.affine(bs=64, window=768, s=8192, batch=4),
           lambda: W.affine(bs=64, window=2048, s=32768, batch=1)], None),
         # Small blocks, D=64, dense windows.
         ("regular-64-dense", "64 bf16 0 *  16 " + BIG + "  16 " + BIG + "  201 " + BIG + "  0 " + BIGIMB + ANYSQ,
