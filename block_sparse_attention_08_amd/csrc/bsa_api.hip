@@ -451,6 +451,11 @@ static bsa_status alloc_header(Plan &P, bool acsr, bsa_acsr_head **acsr_dev) {
   const size_t feat_bytes = sizeof(int64_t) * 4 * P.nbm * P.Hq;
   int64_t rows_per_bm = 0;
   for (int h = 0; h < P.Hq; ++h) rows_per_bm += cdiv(P.Sq, P.bq[h]);
+  // Row bitmaps (mask plans without union: the interleave costs read them).
+  P.bits_per_bm = 0;
+  if (!acsr && !P.uni)
+    for (int h = 0; h < P.Hq; ++h) P.bits_per_bm += cdiv(P.Sq, P.bq[h]) * cdiv(cdiv(P.Skv, P.bk[h]), 64);
+  const size_t bits_bytes = sizeof(unsigned long long) * P.nbm * P.bits_per_bm;
   const size_t acsr_bytes = acsr ? sizeof(bsa_acsr_head) * P.Hq : 0;
   // query-interleave costs [Hq][kQilCands], then key-interleave costs
   // [Hq][kQilCands][kKilCands]
@@ -460,7 +465,7 @@ static bsa_status alloc_header(Plan &P, bool acsr, bsa_acsr_head **acsr_dev) {
                            aligned(sizeof(HeadMeta) * P.Hq) +
                            aligned((size_t)P.nbm * P.Hkv * std::max<int64_t>(P.unkb, 1)) +
                            aligned(sizeof(int32_t) * 2 * std::max<int64_t>(acsr ? 1 : P.nbm * rows_per_bm, 1)) +
-                           aligned(acsr_bytes);
+                           aligned(acsr_bytes) + aligned(bits_bytes);
   if (plan_alloc(&P.pre, pre_bytes, P.device, P.stream) != hipSuccess)
     return fail(BSA_ERR_OUT_OF_MEMORY, "device allocation of plan header failed");
   P.pre_bytes = pre_bytes;
@@ -479,6 +484,8 @@ static bsa_status alloc_header(Plan &P, bool acsr, bsa_acsr_head **acsr_dev) {
   P.row_feat = (int32_t *)pb;
   pb += aligned(sizeof(int32_t) * 2 * std::max<int64_t>(acsr ? 1 : P.nbm * rows_per_bm, 1));
   if (acsr_dev) *acsr_dev = acsr ? (bsa_acsr_head *)pb : nullptr;
+  pb += aligned(acsr_bytes);
+  P.row_bits = bits_bytes ? (unsigned long long *)pb : nullptr;
   if (hipMemsetAsync(P.counters, 0, sizeof(int32_t) * CNT_N, P.stream) != hipSuccess ||
       hipMemsetAsync(P.qil_dev, 0, cost_bytes, P.stream) != hipSuccess)
     return fail(BSA_ERR_HIP, "hipMemsetAsync failed");

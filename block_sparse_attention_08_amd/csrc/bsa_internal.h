@@ -20,6 +20,7 @@ namespace bsa {
 struct HeadMeta {
   int64_t mask_off;  // offset of this head's [nqb][nkb] mask within one mask batch
   int64_t row_off;   // number of logical rows of the heads before this one
+  int64_t bits_off;  // 64-bit words of the row bitmaps of the heads before this one
   int32_t nqb, nkb, bq, bk;
   int32_t lq, lk, mk;
   int32_t lqil;      // log2 of the query-block interleave (0: consecutive blocks)
@@ -110,6 +111,8 @@ struct Plan {
   unsigned long long *feat_dev;
   unsigned long long *qil_dev;  // [Hq][kQilCands] interleave costs (mask plans)
   int32_t *row_feat;  // per logical row: selected blocks, effective blocks
+  unsigned long long *row_bits;  // per logical row: its selected key blocks, one bit each
+  int64_t bits_per_bm = 0;       // words of row bitmaps per mask batch (0: none kept)
   int32_t *counters;
   uint8_t *uni_bits;
   const bsa_acsr_head *acsr = nullptr;  // device copy of the affine row descriptors (ACSR plans)

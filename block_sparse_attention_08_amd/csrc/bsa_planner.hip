@@ -74,7 +74,8 @@ __global__ void k_union(const uint8_t *__restrict__ mask, const HeadMeta *__rest
 __global__ void k_row_features(const uint8_t *__restrict__ mask, const HeadMeta *__restrict__ hm,
                                int Hq, int Hkv, int G, int nbm, int64_t rows_per_bm,
                                int64_t mask_bstride, const uint8_t *__restrict__ U, int64_t unkb,
-                               int causal, int64_t off, int64_t Sq, int32_t *__restrict__ rowf) {
+                               int causal, int64_t off, int64_t Sq, int32_t *__restrict__ rowf,
+                               unsigned long long *__restrict__ bits, int64_t bits_per_bm) {
   const int lane = threadIdx.x & 63;
   const int64_t wv = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 6;
   if (wv >= nbm * rows_per_bm) return;
@@ -95,11 +96,15 @@ __global__ void k_row_features(const uint8_t *__restrict__ mask, const HeadMeta 
   int64_t kbmax = m.nkb - 1;
   if (causal) kbmax = (qlast + off) < 0 ? -1 : (qlast + off) / m.bk;
   int cnt = 0, eff = 0;
+  // the row as a bitmap, one 64-bit word per 64 key blocks (when kept)
+  unsigned long long *brow = bits ? bits + bm * bits_per_bm + m.bits_off + qb * ((m.nkb + 63) >> 6) : nullptr;
   for (int64_t kb = lane; kb < m.nkb; kb += 64) {
     const int sel = row[kb] != 0;
     cnt += sel;
     const int es = urow ? (urow[kb] != 0) : sel;
     eff += es && kb <= kbmax;
+    const unsigned long long word = __ballot(sel);
+    if (brow && lane == 0) brow[kb >> 6] = word;
   }
   cnt = wave_sum(cnt);
   eff = wave_sum(eff);
@@ -156,8 +161,8 @@ __global__ void k_head_features(const int32_t *__restrict__ rowf, const HeadMeta
 // With keys_ok (no causal bound, no paging), heads of 32-key blocks also
 // count, per key interleave s' = 2^c' with 2 s' <= nk, the 64-key tiles in
 // which the tile selects a block, into kcost[h][c][c'].
-__global__ void k_qil_cost(const uint8_t *__restrict__ mask, const HeadMeta *__restrict__ hm, int Hq,
-                           int nbm, int64_t mask_bstride, const int64_t *__restrict__ wave_off,
+__global__ void k_qil_cost(const unsigned long long *__restrict__ bits, int64_t bits_per_bm,
+                           const HeadMeta *__restrict__ hm, int Hq, const int64_t *__restrict__ wave_off,
                            int64_t nwaves, unsigned long long *__restrict__ cost, int keys_ok,
                            unsigned long long *__restrict__ kcost) {
   const int lane = threadIdx.x & 63;
@@ -177,35 +182,46 @@ __global__ void k_qil_cost(const uint8_t *__restrict__ mask, const HeadMeta *__r
   const int64_t k = wv - wave_off[lo];
   const int bm = (int)(k / ntiles);
   const int64_t t = k % ntiles;
-  const uint8_t *mb = mask + bm * mask_bstride + m.mask_off;
-  // the tile's mask rows (at most 4: 32- or 64-row blocks in 128-row tiles)
-  int64_t rowoff[4];
+  const int64_t words = (m.nkb + 63) >> 6;
+  const unsigned long long *hb = bits + bm * bits_per_bm + m.bits_off;
+  // the tile's row bitmaps (at most 4: 32- or 64-row blocks in 128-row tiles)
+  const unsigned long long *rp[4];
   for (int iq = 0; iq < 4; ++iq) {
     const int64_t qb = iq < (1 << lm) ? qblock_of(t, iq, c, lm, m.nqb) : m.nqb;
-    rowoff[iq] = qb < m.nqb ? qb * m.nkb : -1;
+    rp[iq] = qb < m.nqb ? hb + qb * words : nullptr;
   }
+  const bool keys = keys_ok && m.bk == 32;
   int cnt = 0;
-  for (int64_t kb = lane; kb < m.nkb; kb += 64) {
-    int any = 0;
-    for (int iq = 0; iq < 4 && !any; ++iq) any = rowoff[iq] >= 0 && mb[rowoff[iq] + kb] != 0;
-    cnt += any;
+  int kc[kKilCands] = {0, 0, 0, 0};
+  for (int64_t w = lane; w < words; w += 64) {
+    // key blocks 64 w .. 64 w + 63 that some query block of the tile selects
+    unsigned long long x = 0;
+    for (int iq = 0; iq < 4; ++iq)
+      if (rp[iq]) x |= rp[iq][w];
+    cnt += __popcll(x);
+    if (keys) {
+      // 64-key tiles of two 32-key blocks under key interleave s = 2^ck: in
+      // a full group of 2s blocks, tile j holds blocks j and j + s (bit j of
+      // x | x >> s, j mod 2s < s); past the last full group, consecutive
+      // pairs. 2s divides 64, so a group never straddles two words.
+      constexpr unsigned long long kPat[kKilCands] = {0x5555555555555555ull, 0x3333333333333333ull,
+                                                      0x0F0F0F0F0F0F0F0Full, 0x00FF00FF00FF00FFull};
+#pragma unroll
+      for (int ck = 0; ck < kKilCands; ++ck) {
+        if ((int64_t(2) << ck) > m.nkb) break;
+        const int64_t fullend = (m.nkb >> (ck + 1)) << (ck + 1);  // blocks in full groups
+        const int64_t lo64 = w << 6;
+        const unsigned long long fm = fullend <= lo64 ? 0ull
+                                      : (fullend >= lo64 + 64 ? ~0ull : ((1ull << (fullend - lo64)) - 1ull));
+        const unsigned long long yf = (x | (x >> (1 << ck))) & kPat[ck] & fm;
+        const unsigned long long yt = (x | (x >> 1)) & kPat[0] & ~fm;
+        kc[ck] += __popcll(yf) + __popcll(yt);
+      }
+    }
   }
   cnt = wave_sum(cnt);
   if (lane == 0 && cnt) atomicAdd(&cost[h * kQilCands + c], (unsigned long long)cnt);
-  if (!keys_ok || m.bk != 32) return;
-  int kc[kKilCands] = {0, 0, 0, 0};
-  for (int64_t kt = lane; 2 * kt < m.nkb; kt += 64) {
-#pragma unroll
-    for (int ck = 0; ck < kKilCands; ++ck) {
-      if ((int64_t(2) << ck) > m.nkb) break;
-      int any = 0;
-      for (int ik = 0; ik < 2 && !any; ++ik) {
-        const int64_t kb = qblock_of(kt, ik, ck, 1, m.nkb);
-        for (int iq = 0; iq < 4 && !any && kb < m.nkb; ++iq) any = rowoff[iq] >= 0 && mb[rowoff[iq] + kb] != 0;
-      }
-      kc[ck] += any;
-    }
-  }
+  if (!keys) return;
 #pragma unroll
   for (int ck = 0; ck < kKilCands; ++ck) {
     const int v = wave_sum(kc[ck]);
@@ -757,14 +773,15 @@ static bsa_status put_async(void *dst, const void *src, size_t bytes, hipStream_
 
 bsa_status plan_features(Plan &p, const uint8_t *mask, const int32_t *page_table) {
   hipStream_t s = p.stream;
-  int64_t rows_per_bm = 0, mask_bstride = 0;
+  int64_t rows_per_bm = 0, mask_bstride = 0, bits_off = 0;
   std::vector<HeadMeta> &hm = p.hmeta_host;
   hm.assign(p.Hq, HeadMeta{});
   for (int h = 0; h < p.Hq; ++h) {
     const int64_t nq = (p.Sq + p.bq[h] - 1) / p.bq[h], nk = (p.Skv + p.bk[h] - 1) / p.bk[h];
-    hm[h] = HeadMeta{mask_bstride, rows_per_bm, (int32_t)nq, (int32_t)nk, p.bq[h], p.bk[h], 0, 0, 0, 0};
+    hm[h] = HeadMeta{mask_bstride, rows_per_bm, bits_off, (int32_t)nq, (int32_t)nk, p.bq[h], p.bk[h], 0, 0, 0, 0};
     rows_per_bm += nq;
     mask_bstride += nq * nk;
+    bits_off += nq * ((nk + 63) / 64);
   }
   HIP_TRY(hipMemcpyAsync(p.hmeta, hm.data(), sizeof(HeadMeta) * p.Hq, hipMemcpyHostToDevice, s));
   if (p.uni && p.unkb > 0)
@@ -773,7 +790,8 @@ bsa_status plan_features(Plan &p, const uint8_t *mask, const int32_t *page_table
   if (p.nbm * rows_per_bm > 0)
     hipLaunchKernelGGL(k_row_features, dim3(grid_for(p.nbm * rows_per_bm * 64)), dim3(kThreads), 0,
                        s, mask, p.hmeta, p.Hq, p.Hkv, p.G, (int)p.nbm, rows_per_bm, mask_bstride,
-                       p.uni ? p.uni_bits : nullptr, p.unkb, p.causal, p.off, p.Sq, p.row_feat);
+                       p.uni ? p.uni_bits : nullptr, p.unkb, p.causal, p.off, p.Sq, p.row_feat,
+                       p.row_bits, p.bits_per_bm);
   hipLaunchKernelGGL(k_head_features, dim3((unsigned)(p.nbm * p.Hq)), dim3(kThreads), 0, s,
                      p.row_feat, p.hmeta, p.Hq, rows_per_bm, p.feat_dev);
   // Query-block interleave costs (non-union plans; the tile shape is not yet
@@ -796,8 +814,8 @@ bsa_status plan_features(Plan &p, const uint8_t *mask, const int32_t *page_table
       unsigned long long *kcost = p.qil_dev + (size_t)p.Hq * kQilCands;
       int64_t *woff_dev = (int64_t *)(kcost + (size_t)p.Hq * kQilCands * kKilCands);
       if (bsa_status st = put_async(woff_dev, woff.data(), sizeof(int64_t) * woff.size(), s)) return st;
-      hipLaunchKernelGGL(k_qil_cost, dim3(grid_for(nw * 64)), dim3(kThreads), 0, s, mask, p.hmeta, p.Hq,
-                         (int)p.nbm, mask_bstride, (const int64_t *)woff_dev, nw, p.qil_dev,
+      hipLaunchKernelGGL(k_qil_cost, dim3(grid_for(nw * 64)), dim3(kThreads), 0, s, p.row_bits,
+                         p.bits_per_bm, p.hmeta, p.Hq, (const int64_t *)woff_dev, nw, p.qil_dev,
                          (!p.causal && !p.paged && p.dtype == BSA_BF16 && p.G == 1) ? 1 : 0, kcost);
     }
   }
@@ -817,7 +835,7 @@ bsa_status plan_features_acsr(Plan &p, const bsa_acsr_head *heads, bsa_acsr_head
   int64_t rows = 0, mask_off = 0;
   for (int h = 0; h < p.Hq; ++h) {
     const int64_t nq = (p.Sq + p.bq[h] - 1) / p.bq[h], nk = (p.Skv + p.bk[h] - 1) / p.bk[h];
-    hm[h] = HeadMeta{mask_off, rows, (int32_t)nq, (int32_t)nk, p.bq[h], p.bk[h], 0, 0, 0, 0};
+    hm[h] = HeadMeta{mask_off, rows, 0, (int32_t)nq, (int32_t)nk, p.bq[h], p.bk[h], 0, 0, 0, 0};
     rows += nq;
     mask_off += nq * nk;
   }
