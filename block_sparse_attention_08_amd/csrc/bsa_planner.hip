@@ -152,18 +152,21 @@ __global__ void k_head_features(const int32_t *__restrict__ rowf, const HeadMeta
   }
 }
 
-// Query-block interleave costs: one wave per (mask batch, head, candidate
-// interleave s = 2^c, 128-row tile); it counts the key blocks that some
-// query block of the tile selects (the mask as given) and adds the count to
-// cost[h][c] (integer atomics: the sums do not depend on their order). Only
+// Query-block interleave costs: one wave per (head, candidate interleave
+// s = 2^c) and 16 of its 128-row tiles (over the mask batches); it counts
+// the key blocks that some query block of a tile selects (the mask as given,
+// from the row bitmaps) and adds the sum to cost[h][c] (integer atomics: the
+// sums do not depend on their order). Only
 // heads whose 32- or 64-row blocks merge into 128-row tiles, and only
 // candidates with s * mq <= nq, are counted; the host picks the cheapest.
 // With keys_ok (no causal bound, no paging), heads of 32-key blocks also
 // count, per key interleave s' = 2^c' with 2 s' <= nk, the 64-key tiles in
 // which the tile selects a block, into kcost[h][c][c'].
+constexpr int kCostTiles = 16;  // tiles per wave of k_qil_cost (one atomic per wave and counter)
 __global__ void k_qil_cost(const unsigned long long *__restrict__ bits, int64_t bits_per_bm,
-                           const HeadMeta *__restrict__ hm, int Hq, const int64_t *__restrict__ wave_off,
-                           int64_t nwaves, unsigned long long *__restrict__ cost, int keys_ok,
+                           const HeadMeta *__restrict__ hm, int Hq, int nbm,
+                           const int64_t *__restrict__ wave_off, int64_t nwaves,
+                           unsigned long long *__restrict__ cost, int keys_ok,
                            unsigned long long *__restrict__ kcost) {
   const int lane = threadIdx.x & 63;
   const int64_t wv = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 6;
@@ -179,43 +182,48 @@ __global__ void k_qil_cost(const unsigned long long *__restrict__ bits, int64_t 
   const HeadMeta m = hm[h];
   const int lm = 7 - __builtin_ctz(m.bq);  // 128-row tiles
   const int64_t ntiles = ((int64_t)m.nqb + (1 << lm) - 1) >> lm;
-  const int64_t k = wv - wave_off[lo];
-  const int bm = (int)(k / ntiles);
-  const int64_t t = k % ntiles;
   const int64_t words = (m.nkb + 63) >> 6;
-  const unsigned long long *hb = bits + bm * bits_per_bm + m.bits_off;
-  // the tile's row bitmaps (at most 4: 32- or 64-row blocks in 128-row tiles)
-  const unsigned long long *rp[4];
-  for (int iq = 0; iq < 4; ++iq) {
-    const int64_t qb = iq < (1 << lm) ? qblock_of(t, iq, c, lm, m.nqb) : m.nqb;
-    rp[iq] = qb < m.nqb ? hb + qb * words : nullptr;
-  }
   const bool keys = keys_ok && m.bk == 32;
   int cnt = 0;
   int kc[kKilCands] = {0, 0, 0, 0};
-  for (int64_t w = lane; w < words; w += 64) {
-    // key blocks 64 w .. 64 w + 63 that some query block of the tile selects
-    unsigned long long x = 0;
-    for (int iq = 0; iq < 4; ++iq)
-      if (rp[iq]) x |= rp[iq][w];
-    cnt += __popcll(x);
-    if (keys) {
-      // 64-key tiles of two 32-key blocks under key interleave s = 2^ck: in
-      // a full group of 2s blocks, tile j holds blocks j and j + s (bit j of
-      // x | x >> s, j mod 2s < s); past the last full group, consecutive
-      // pairs. 2s divides 64, so a group never straddles two words.
-      constexpr unsigned long long kPat[kKilCands] = {0x5555555555555555ull, 0x3333333333333333ull,
-                                                      0x0F0F0F0F0F0F0F0Full, 0x00FF00FF00FF00FFull};
+  // tiles kCostTiles * (this wave's index within its (head, candidate)) ..,
+  // numbered over the mask batches
+  const int64_t k0 = (wv - wave_off[lo]) * kCostTiles;
+  for (int64_t k = k0; k < k0 + kCostTiles; ++k) {
+    const int bm = (int)(k / ntiles);
+    const int64_t t = k % ntiles;
+    if (bm >= nbm) break;
+    const unsigned long long *hb = bits + bm * bits_per_bm + m.bits_off;
+    // the tile's row bitmaps (at most 4: 32- or 64-row blocks in 128-row tiles)
+    const unsigned long long *rp[4];
+    for (int iq = 0; iq < 4; ++iq) {
+      const int64_t qb = iq < (1 << lm) ? qblock_of(t, iq, c, lm, m.nqb) : m.nqb;
+      rp[iq] = qb < m.nqb ? hb + qb * words : nullptr;
+    }
+    for (int64_t w = lane; w < words; w += 64) {
+      // key blocks 64 w .. 64 w + 63 that some query block of the tile selects
+      unsigned long long x = 0;
+      for (int iq = 0; iq < 4; ++iq)
+        if (rp[iq]) x |= rp[iq][w];
+      cnt += __popcll(x);
+      if (keys) {
+        // 64-key tiles of two 32-key blocks under key interleave s = 2^ck: in
+        // a full group of 2s blocks, tile j holds blocks j and j + s (bit j of
+        // x | x >> s, j mod 2s < s); past the last full group, consecutive
+        // pairs. 2s divides 64, so a group never straddles two words.
+        constexpr unsigned long long kPat[kKilCands] = {0x5555555555555555ull, 0x3333333333333333ull,
+                                                        0x0F0F0F0F0F0F0F0Full, 0x00FF00FF00FF00FFull};
 #pragma unroll
-      for (int ck = 0; ck < kKilCands; ++ck) {
-        if ((int64_t(2) << ck) > m.nkb) break;
-        const int64_t fullend = (m.nkb >> (ck + 1)) << (ck + 1);  // blocks in full groups
-        const int64_t lo64 = w << 6;
-        const unsigned long long fm = fullend <= lo64 ? 0ull
-                                      : (fullend >= lo64 + 64 ? ~0ull : ((1ull << (fullend - lo64)) - 1ull));
-        const unsigned long long yf = (x | (x >> (1 << ck))) & kPat[ck] & fm;
-        const unsigned long long yt = (x | (x >> 1)) & kPat[0] & ~fm;
-        kc[ck] += __popcll(yf) + __popcll(yt);
+        for (int ck = 0; ck < kKilCands; ++ck) {
+          if ((int64_t(2) << ck) > m.nkb) break;
+          const int64_t fullend = (m.nkb >> (ck + 1)) << (ck + 1);  // blocks in full groups
+          const int64_t lo64 = w << 6;
+          const unsigned long long fm = fullend <= lo64 ? 0ull
+                                        : (fullend >= lo64 + 64 ? ~0ull : ((1ull << (fullend - lo64)) - 1ull));
+          const unsigned long long yf = (x | (x >> (1 << ck))) & kPat[ck] & fm;
+          const unsigned long long yt = (x | (x >> 1)) & kPat[0] & ~fm;
+          kc[ck] += __popcll(yf) + __popcll(yt);
+        }
       }
     }
   }
@@ -806,7 +814,8 @@ bsa_status plan_features(Plan &p, const uint8_t *mask, const int32_t *page_table
       for (int c = 0; c < kQilCands; ++c) {
         woff[h * kQilCands + c] = nw;
         const int64_t mq = bq < 128 ? 128 / bq : 1;
-        if (bq >= 32 && bq < 128 && (int64_t(1) << c) * mq <= nq) nw += p.nbm * ((nq + mq - 1) / mq);
+        if (bq >= 32 && bq < 128 && (int64_t(1) << c) * mq <= nq)
+          nw += (p.nbm * ((nq + mq - 1) / mq) + kCostTiles - 1) / kCostTiles;
       }
     }
     woff[p.Hq * kQilCands] = nw;
@@ -815,7 +824,7 @@ bsa_status plan_features(Plan &p, const uint8_t *mask, const int32_t *page_table
       int64_t *woff_dev = (int64_t *)(kcost + (size_t)p.Hq * kQilCands * kKilCands);
       if (bsa_status st = put_async(woff_dev, woff.data(), sizeof(int64_t) * woff.size(), s)) return st;
       hipLaunchKernelGGL(k_qil_cost, dim3(grid_for(nw * 64)), dim3(kThreads), 0, s, p.row_bits,
-                         p.bits_per_bm, p.hmeta, p.Hq, (const int64_t *)woff_dev, nw, p.qil_dev,
+                         p.bits_per_bm, p.hmeta, p.Hq, (int)p.nbm, (const int64_t *)woff_dev, nw, p.qil_dev,
                          (!p.causal && !p.paged && p.dtype == BSA_BF16 && p.G == 1) ? 1 : 0, kcost);
     }
   }
