@@ -877,12 +877,24 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
     auto issue_k8 = [&](int j, auto par, const Meta &m) { issue8(k8base, a.k_sb, a.k_ss, m, kbuf(j, par), k8off0); };
     auto issue_v8 = [&](int j, auto par, const Meta &m) { issue8(v8base, a.v_sb, a.v_ss, m, vbuf(j, par), v8off0); };
     (void)issue_k8, (void)issue_v8;
+    // Lane offsets of the K fragments of the first 32-key block. The swizzle
+    // has a period of 16 rows at D = 128, so the second block's fragments
+    // lie 32 rows further on, and a fragment's address is a per-lane offset
+    // plus a constant (buffer base, block) that the LDS read carries as its
+    // immediate offset: no address arithmetic per tile.
+    int kofs[D / 16];
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) kofs[cc] = krow0 * C::ROWB + (((2 * cc + hh) ^ C::swz_k(krow0)) << 4);
+    (void)kofs;
     auto kfrag = [&](const uint8_t *ks, int i) {
       const int row = 32 * (i / (D / 16)) + krow0;
       if constexpr (KD) {
         const int c8 = i % (D / 16);  // 16 e4m3 bytes per k-step, 8 per half-wave
         const uint2 w = *(const uint2 *)(ks + row * D + ((c8 ^ swz8_k(row)) << 4) + 8 * hh);
         return __builtin_bit_cast(bf16x8, e4m3x8_to_bf16(w));
+      } else if constexpr (D == 128) {
+        static_assert(D != 128 || (32 % 16 == 0), "K swizzle period");
+        return *(const bf16x8 *)(ks + (i / (D / 16)) * 32 * C::ROWB + kofs[i % (D / 16)]);
       } else {
         const int c = 2 * (i % (D / 16)) + hh;
         return *(const bf16x8 *)(ks + row * C::ROWB + ((c ^ C::swz_k(row)) << 4));
@@ -1052,7 +1064,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
           const int x = i * EPS + k2;
           const float p0 = fexp2(__builtin_fmaf(s_cur[x / 16][x % 16], BSA_SL2, -m_use));
           const float p1 = fexp2(__builtin_fmaf(s_cur[x / 16][x % 16 + 1], BSA_SL2, -m_use));
-          psum += p0;
+          psum = x == 0 ? p0 : psum + p0;  // (no add of the initial zero)
           psum += p1;
           pw[x / 2] = pack_bf16x2(p0, p1);
         }
