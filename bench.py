@@ -671,9 +671,15 @@ def config_table(bsa, lut, args):
                     plans[key] = pc
             times = {}
             reps = max(5, min(20, int(200.0 / max(fwd_ms, 0.05))))  # about 0.2 s per measurement
-            for rnd in range(2):  # two interleaved rounds, the better of the two kept
-                for key, pc in plans.items():
-                    t = time_fwd(pc, q, k, v, o, lse, reps)
+            # Three interleaved rounds, the order rotated each round so that no
+            # regime always runs first; each measurement starts after a short
+            # stretch of its own forwards at full clock (a sub-millisecond
+            # forward timed right after the host's planning or the previous
+            # synchronisation runs up to 10% slow). The best round is kept.
+            order = list(plans.items())
+            for rnd in range(3):
+                for key, pc in order[rnd % len(order):] + order[:rnd % len(order)]:
+                    t = time_fwd(pc, q, k, v, o, lse, reps, warm_ms=30.0)
                     times[key] = min(times.get(key, t), t)
             for pc in plans.values():
                 pc.free()
