@@ -533,7 +533,11 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdArgs a) {
     f32x16 sb, db2;
     uint32_t pw[8], dw[8];
     float pe = 0.f, de = 0.f;
-    {
+    // One wave issues everything on its SIMD here, so instructions count: a
+    // chunk whose every row is allowed for every key of the wave (the usual
+    // case away from the causal diagonal and the sequence end) takes its
+    // exponentials without the per-score row test.
+    auto sdp_pass = [&](auto masked) {
       bf16x8 fr[SD];
 #pragma unroll
       for (int i = 0; i < kAheadSD; ++i) fr[i] = sdp_frag(tn, i);
@@ -547,9 +551,15 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdArgs a) {
 #pragma unroll
         for (int k2 = 0; k2 < 16 / SD; ++k2) {
           const int x = i * (16 / SD) + k2;  // accumulator index
-          const bool ok = (myrows >> (16 * (x >> 3) + (x & 7))) & 1u;
-          // Allowed pairs have a finite LSE (the row has a key).
-          const float p = ok ? fexp2(__builtin_fmaf(sa[x], a.scale_log2, -lrow[x] * kLog2e)) : 0.f;
+          const float arg = __builtin_fmaf(sa[x], a.scale_log2, -lrow[x] * kLog2e);
+          float p;
+          if constexpr (decltype(masked)::value) {
+            // Allowed pairs have a finite LSE (the row has a key).
+            const bool ok = (myrows >> (16 * (x >> 3) + (x & 7))) & 1u;
+            p = ok ? fexp2(arg) : 0.f;
+          } else {
+            p = fexp2(arg);
+          }
           const float dd = p * (da[x] - drow[x]);
           if (x & 1) {
             pw[x >> 1] = pack_bf16x2(pe, p);
@@ -560,7 +570,9 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-    }
+    };
+    if (__all(rows == 0xffffffffu)) sdp_pass(std::false_type{});
+    else sdp_pass(std::true_type{});
     {
       bf16x8 fr[KV];
 #pragma unroll
