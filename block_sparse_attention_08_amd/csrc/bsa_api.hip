@@ -875,10 +875,12 @@ bsa_status bsa_backward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *
   a.pack = P.rg.pack ? 1 : 0, a.uni = P.uni, a.causal = P.causal, a.nlb = (int)P.nlb;
   a.scale = P.scale, a.scale_log2 = P.scale * 1.4426950408889634f;
   // Scratch, stream-ordered and returned after the kernels: Delta (dO . O per
-  // query row) and the key-major chunk index (groups of 128 keys) that the
-  // dK/dV kernel walks.
+  // query row) and the LSE in log2 units, both written by the dQ kernel for
+  // the dK/dV kernel, and the key-major chunk index (groups of 128 keys) that
+  // the dK/dV kernel walks.
   if (P.G > 255) return fail(BSA_ERR_UNSUPPORTED, "backward supports up to 255 query heads per kv head");
-  const size_t delta_bytes = (sizeof(float) * (size_t)std::max<int64_t>(P.B * (int64_t)P.Hq * P.Sq, 1) + 255) & ~(size_t)255;
+  const size_t row_bytes = (sizeof(float) * (size_t)std::max<int64_t>(P.B * (int64_t)P.Hq * P.Sq, 1) + 255) & ~(size_t)255;
+  const size_t delta_bytes = 2 * row_bytes;  // Delta, then LSE * log2(e)
   const int nkt_per = 128 / P.rg.tk;
   const size_t index_bytes = plan_kv_index_bytes(P, nkt_per);
   log_msg(3, "backward: plan %p, %zu scratch bytes, stream %p", (const void *)plan,
@@ -888,6 +890,7 @@ bsa_status bsa_backward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *
   const hipError_t e = plan_alloc(&scratch, delta_bytes + index_bytes, P.device, s);
   if (e != hipSuccess) return fail(BSA_ERR_OUT_OF_MEMORY, std::string("backward scratch: ") + hipGetErrorString(e));
   a.delta = (float *)scratch;
+  a.lse2 = (float *)((uint8_t *)scratch + row_bytes);
   KvIndex ix{};
   bsa_status st = plan_kv_index(P, nkt_per, (uint8_t *)scratch + delta_bytes, &ix, s);
   a.t_off = ix.off, a.t_q0 = ix.q0, a.t_meta = ix.meta, a.t_live = ix.live;

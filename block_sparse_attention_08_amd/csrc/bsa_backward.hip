@@ -214,8 +214,10 @@ __global__ __launch_bounds__(2 * TQ, TQ == 128 ? 2 : 1) void k_bwd_dq(BwdArgs a)
   if (qvalid && hh == 0) a.delta[rowix] = delta;
   const float L = qvalid ? a.lse[rowix] : -INFINITY;
   // exp2(s * scale_log2 - lse2) is P; +inf makes P = 0 for rows without keys
-  // and for padding rows past the sequence end.
+  // and for padding rows past the sequence end. Kept for the dK/dV kernel,
+  // which then spends no multiply per score on it.
   const float lse2 = L == -INFINITY ? INFINITY : L * kLog2e;
+  if (qvalid && hh == 0) a.lse2[rowix] = lse2;
 
   const int e0 = a.row_ent[2 * r], nent = a.row_ent[2 * r + 1] - e0;
   const uint16_t *Kb = (const uint16_t *)a.k + b * a.k_sb + g * a.k_sh;
@@ -435,11 +437,11 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdArgs a) {
       dma_b128(rq, qoff0 + u * RPL * (int)a.q_ss * 2, lds_addr_of(dq_));
       dma_b128(rd, doff0 + u * RPL * (int)a.do_ss * 2, lds_addr_of(dq_ + CHB));
     }
-    // LSE (wave 0) and Delta (wave 1) of the chunk's rows, one dword per lane;
-    // waves 2 and 3 repeat the LSE load into a spare area so that every wave
-    // has the same number of loads in flight per chunk.
+    // LSE in log2 units (wave 0) and Delta (wave 1) of the chunk's rows, one
+    // dword per lane; waves 2 and 3 repeat the LSE load into a spare area so
+    // that every wave has the same number of loads in flight per chunk.
     const int64_t rix = ((int64_t)b * a.Hq + h) * a.Sq + q0;
-    const float *src = wave == 1 ? a.delta + rix : a.lse + rix;
+    const float *src = wave == 1 ? a.delta + rix : a.lse2 + rix;
     uint8_t *dl = dst + 2 * CHB + (wave == 1 ? 256 : (wave == 0 ? 0 : 512 + 256 * (wave - 2)));
     dma_b32(raw_rsrc(src, rows * 4), lane * 4, lds_addr_of(dl));
   };
@@ -551,7 +553,7 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdArgs a) {
 #pragma unroll
         for (int k2 = 0; k2 < 16 / SD; ++k2) {
           const int x = i * (16 / SD) + k2;  // accumulator index
-          const float arg = __builtin_fmaf(sa[x], a.scale_log2, -lrow[x] * kLog2e);
+          const float arg = __builtin_fmaf(sa[x], a.scale_log2, -lrow[x]);  // (lrow in log2 units)
           float p;
           if constexpr (decltype(masked)::value) {
             // Allowed pairs have a finite LSE (the row has a key).

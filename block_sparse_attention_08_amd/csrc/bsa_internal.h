@@ -152,6 +152,7 @@ struct BwdArgs {
   const void *q, *k, *v, *o, *dout;
   const float *lse;
   float *delta;  // [B][Hq][Sq]: dO . O per query row, written by the dQ kernel
+  float *lse2;   // [B][Hq][Sq]: LSE * log2(e) (+inf for rows without keys), written by the dQ kernel
   void *dq, *dk, *dv;
   int64_t q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, v_sb, v_sh, v_ss;
   int64_t o_sb, o_sh, o_ss, do_sb, do_sh, do_ss, dq_sb, dq_sh, dq_ss;
