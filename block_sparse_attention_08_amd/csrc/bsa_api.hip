@@ -870,6 +870,18 @@ bsa_status bsa_backward(bsa_plan_t plan, const bsa_tensor *q, const bsa_tensor *
   a.hm = P.hmeta;
   a.Sq = P.Sq, a.Skv = P.Skv, a.off = P.off, a.nqt = P.nqt, a.nkt = P.nkt;
   a.Hq = P.Hq, a.Hkv = P.Hkv, a.G = P.G, a.tq = P.rg.tq, a.tr = P.tr, a.tk = P.rg.tk;
+  {
+    // 32-bit chunk addressing in the dK/dV kernel when a kv group's span of
+    // Q and dO (in elements) fits in 31 bits.
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t qspan = (int64_t)(P.G - 1) * q->stride_h + (P.Sq - 1) * q->stride_s + P.D;
+    const int64_t dspan = (int64_t)(P.G - 1) * dout->stride_h + (P.Sq - 1) * dout->stride_s + P.D;
+    const bool ok = qspan < lim && dspan < lim && (int64_t)P.G * P.Sq < lim && q->stride_h < lim &&
+                    q->stride_s < lim && dout->stride_h < lim && dout->stride_s < lim;
+    a.grp32 = ok ? 1 : 0;
+    a.q_sh32 = ok ? (int32_t)q->stride_h : 0, a.q_ss32 = ok ? (int32_t)q->stride_s : 0;
+    a.do_sh32 = ok ? (int32_t)dout->stride_h : 0, a.do_ss32 = ok ? (int32_t)dout->stride_s : 0;
+  }
   // (an interleaved forward regime has the same rows; the backward lays
   // them out head after head)
   a.pack = P.rg.pack ? 1 : 0, a.uni = P.uni, a.causal = P.causal, a.nlb = (int)P.nlb;

@@ -423,27 +423,47 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdArgs a) {
   const int qoff0 = trow * (int)a.q_ss * 2 + ((tpos ^ swz<D>(trow)) << 4);
   const int doff0 = trow * (int)a.do_ss * 2 + ((tpos ^ swz<D>(trow)) << 4);
   // Loads of the chunk with first query q0 and packed word meta into buffer buf.
+  // The kv group's first head: Q and dO rows, and its LSE / Delta entries.
+  const uint16_t *qgrp = (const uint16_t *)a.q + b * a.q_sb + (int64_t)(g * a.G) * a.q_sh;
+  const uint16_t *dgrp = (const uint16_t *)a.dout + b * a.do_sb + (int64_t)(g * a.G) * a.do_sh;
+  const int64_t rgrp = ((int64_t)b * a.Hq + g * a.G) * a.Sq;
+  // LDS destinations as 32-bit addresses from the array's base, taken once
+  // (a generic pointer turned back into an LDS address costs a null test
+  // per load).
+  const uint32_t lds0 = lds_addr_of(lds);
   auto issue_qm = [&](int q0, int meta, int buf) {
-    const int h = g * a.G + (meta & 255);
-    uint8_t *dst = lds + buf * BUFB;
+    const int hl = meta & 255;                  // head within the group
+    const uint32_t dst = lds0 + buf * BUFB;
     const int rows = min(sq32 - q0, 32);        // rows of the chunk that exist (>= 1)
-    const uint16_t *qb_ = (const uint16_t *)a.q + b * a.q_sb + h * a.q_sh + (int64_t)q0 * a.q_ss;
-    const uint16_t *db_ = (const uint16_t *)a.dout + b * a.do_sb + h * a.do_sh + (int64_t)q0 * a.do_ss;
+    // Element offsets within the group: 32-bit products when the host found
+    // that every such offset fits (one wave issues every instruction here).
+    int64_t qo, dof, ro;
+    if (a.grp32) {
+      qo = (uint32_t)(hl * a.q_sh32 + q0 * a.q_ss32);
+      dof = (uint32_t)(hl * a.do_sh32 + q0 * a.do_ss32);
+      ro = (uint32_t)(hl * sq32 + q0);
+    } else {
+      qo = hl * a.q_sh + (int64_t)q0 * a.q_ss;
+      dof = hl * a.do_sh + (int64_t)q0 * a.do_ss;
+      ro = hl * a.Sq + q0;
+    }
+    const uint16_t *qb_ = qgrp + qo;
+    const uint16_t *db_ = dgrp + dof;
     const v4u32 rq = raw_rsrc(qb_, (rows - 1) * (int)a.q_ss * 2 + D * 2);
     const v4u32 rd = raw_rsrc(db_, (rows - 1) * (int)a.do_ss * 2 + D * 2);
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
-      uint8_t *dq_ = dst + (u * T + wave * 64) * 16;
-      dma_b128(rq, qoff0 + u * RPL * (int)a.q_ss * 2, lds_addr_of(dq_));
-      dma_b128(rd, doff0 + u * RPL * (int)a.do_ss * 2, lds_addr_of(dq_ + CHB));
+      const uint32_t dq_ = dst + (u * T + wave * 64) * 16;
+      dma_b128(rq, qoff0 + u * RPL * (int)a.q_ss * 2, dq_);
+      dma_b128(rd, doff0 + u * RPL * (int)a.do_ss * 2, dq_ + CHB);
     }
     // LSE in log2 units (wave 0) and Delta (wave 1) of the chunk's rows, one
     // dword per lane; waves 2 and 3 repeat the LSE load into a spare area so
     // that every wave has the same number of loads in flight per chunk.
-    const int64_t rix = ((int64_t)b * a.Hq + h) * a.Sq + q0;
+    const int64_t rix = rgrp + ro;
     const float *src = wave == 1 ? a.delta + rix : a.lse2 + rix;
-    uint8_t *dl = dst + 2 * CHB + (wave == 1 ? 256 : (wave == 0 ? 0 : 512 + 256 * (wave - 2)));
-    dma_b32(raw_rsrc(src, rows * 4), lane * 4, lds_addr_of(dl));
+    const uint32_t dl = dst + 2 * CHB + (wave == 1 ? 256 : (wave == 0 ? 0 : 512 + 256 * (wave - 2)));
+    dma_b32(raw_rsrc(src, rows * 4), lane * 4, dl);
   };
   auto issue = [&](int e, int buf) {
     issue_qm(((const cint32 *)a.t_q0)[e], ((const cint32 *)a.t_meta)[e], buf);

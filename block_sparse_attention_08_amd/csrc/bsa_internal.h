@@ -165,6 +165,11 @@ struct BwdArgs {
   int64_t Sq, Skv, off, nqt, nkt;
   int32_t Hq, Hkv, G, tq, tr, tk, pack, uni, causal, nlb;
   float scale, scale_log2;
+  // grp32: every element offset of Q and dO within one kv group's heads
+  // ((G-1) * head stride + (Sq-1) * row stride + D) and G * Sq fit in 31
+  // bits, so the dK/dV kernel forms its chunk addresses in 32-bit arithmetic
+  // from these stride copies (checked on the host; 0 otherwise).
+  int32_t grp32, q_sh32, q_ss32, do_sh32, do_ss32;
 };
 
 // Device allocations of plans and per-call scratch: stream-ordered (the
