@@ -314,19 +314,32 @@ __global__ __launch_bounds__(2 * TQ, TQ == 128 ? 2 : 1) void k_bwd_dq(BwdArgs a)
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(ks, kr, 2 * c + hh), qb[c], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(vs, kr, 2 * c + hh), dob[c], dp, 0, 0, 0);
       }
+      // dS of the block; tiles that need no mask (no sequence end, causal
+      // diagonal or dead sub-block; rows without keys have lse2 = +inf and
+      // so P = 0) skip the per-score key test.
       uint32_t dsw[8];
+      auto ds_block = [&](auto masked) {
 #pragma unroll
-      for (int jj = 0; jj < 16; jj += 2) {
-        float ds2[2];
+        for (int jj = 0; jj < 16; jj += 2) {
+          float ds2[2];
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const int kl = 32 * t + 16 * ((jj + x) >> 3) + ((jj + x) & 7);  // without the 8*hh term
-          const bool ok = (km[kl / 64] >> (kl % 64)) & 1ull;
-          const float p = ok ? fexp2(__builtin_fmaf(s[jj + x], a.scale_log2, -lse2)) : 0.f;
-          ds2[x] = p * (dp[jj + x] - delta);
+          for (int x = 0; x < 2; ++x) {
+            const float arg = __builtin_fmaf(s[jj + x], a.scale_log2, -lse2);
+            float p;
+            if constexpr (decltype(masked)::value) {
+              const int kl = 32 * t + 16 * ((jj + x) >> 3) + ((jj + x) & 7);  // without the 8*hh term
+              const bool ok = (km[kl / 64] >> (kl % 64)) & 1ull;
+              p = ok ? fexp2(arg) : 0.f;
+            } else {
+              p = fexp2(arg);
+            }
+            ds2[x] = p * (dp[jj + x] - delta);
+          }
+          dsw[jj / 2] = pack_bf16x2(ds2[0], ds2[1]);
         }
-        dsw[jj / 2] = pack_bf16x2(ds2[0], ds2[1]);
-      }
+      };
+      if (need) ds_block(std::true_type{});
+      else ds_block(std::false_type{});
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
         const bf16x8 bop = as_bf16x8(dsw[4 * c2], dsw[4 * c2 + 1], dsw[4 * c2 + 2], dsw[4 * c2 + 3]);
