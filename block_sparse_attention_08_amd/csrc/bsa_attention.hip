@@ -878,7 +878,7 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
     auto issue_v8 = [&](int j, auto par, const Meta &m) { issue8(v8base, a.v_sb, a.v_ss, m, vbuf(j, par), v8off0); };
     (void)issue_k8, (void)issue_v8;
     // Lane offsets of the K fragments of the first 32-key block. The swizzle
-    // has a period of 16 rows at D = 128, so the second block's fragments
+    // (swz_k: row & 15 at D = 128) has a period of 16 rows, so the second block's fragments
     // lie 32 rows further on, and a fragment's address is a per-lane offset
     // plus a constant (buffer base, block) that the LDS read carries as its
     // immediate offset: no address arithmetic per tile.
@@ -893,7 +893,6 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
         const uint2 w = *(const uint2 *)(ks + row * D + ((c8 ^ swz8_k(row)) << 4) + 8 * hh);
         return __builtin_bit_cast(bf16x8, e4m3x8_to_bf16(w));
       } else if constexpr (D == 128) {
-        static_assert(D != 128 || (32 % 16 == 0), "K swizzle period");
         return *(const bf16x8 *)(ks + (i / (D / 16)) * 32 * C::ROWB + kofs[i % (D / 16)]);
       } else {
         const int c = 2 * (i % (D / 16)) + hh;
