@@ -912,11 +912,24 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
 
     constexpr int STEPS = C::NKB * D / 16;     // K fragments per tile
     constexpr int EPS = C::NKB * 16 / STEPS;   // scores exponentiated per step (2 or 4)
+    // K fragment of S^T step i. The exponentials take tile j's 32-key score
+    // blocks in order, block 0 first. In the kernels that keep their tiles in
+    // one ring (not unrolled by two), the S^T MFMAs of tile j+1 beside them
+    // build its last block first and then blocks 0, 1, ...: block t < NKB-1
+    // is written in the steps right after the exponentials have taken block t,
+    // into the same registers, and only the last block is copied per tile.
+    // (Only the bf16 kernels over contiguous K/V: in the paged and e4m3 ring
+    // kernels the compiler then kept more copies, not fewer.)
+    constexpr bool ALIAS = RING && !PAGED && !KV8;
+    constexpr auto next_frag = [](int i) {
+      if constexpr (ALIAS) return ((i / (D / 16) + C::NKB - 1) % C::NKB) * (D / 16) + i % (D / 16);
+      else return i;
+    };
 
     // One tile iteration: softmax of tile j (scores in s_cur), S^T of tile
     // j+1 into s_next, O += V^T P^T of tile j.
     // par is the parity of j (std::integral_constant); flip that of j + 1.
-    auto tile = [&](int j, auto par, f32x16 (&s_cur)[C::NKB], f32x16 (&s_next)[C::NKB]) {
+    auto tile = [&](int j, auto par, auto &&s_cur, auto &&s_next) {
       const std::integral_constant<int, 1 - decltype(par)::value> flip;
       // K tile j+1 and V tile j have landed (this wave) ...
       if constexpr (NS == 2) {
@@ -970,11 +983,11 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
           const uint8_t *ks = kbuf(j + 1, flip);
           bf16x8 kf[STEPS];
 #pragma unroll
-          for (int i = 0; i < 3 && i < STEPS; ++i) kf[i] = kfrag(ks, i);
+          for (int i = 0; i < 3 && i < STEPS; ++i) kf[i] = kfrag(ks, next_frag(i));
 #pragma unroll
           for (int i = 0; i < STEPS; ++i) {
-            if (i + 3 < STEPS) kf[i + 3] = kfrag(ks, i + 3);
-            const int t = i / (D / 16), cc = i % (D / 16);
+            if (i + 3 < STEPS) kf[i + 3] = kfrag(ks, next_frag(i + 3));
+            const int t = next_frag(i) / (D / 16), cc = i % (D / 16);
             s_next[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qb[cc], cc == 0 ? f32x16{} : s_next[t], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -1072,11 +1085,11 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
         const uint8_t *ks = kbuf(j + 1, flip);
         bf16x8 kf[STEPS];
 #pragma unroll
-        for (int i = 0; i < 3 && i < STEPS; ++i) kf[i] = kfrag(ks, i);
+        for (int i = 0; i < 3 && i < STEPS; ++i) kf[i] = kfrag(ks, next_frag(i));
 #pragma unroll
         for (int i = 0; i < STEPS; ++i) {
-          if (i + 3 < STEPS) kf[i + 3] = kfrag(ks, i + 3);
-          const int t = i / (D / 16), cc = i % (D / 16);
+          if (i + 3 < STEPS) kf[i + 3] = kfrag(ks, next_frag(i + 3));
+          const int t = next_frag(i) / (D / 16), cc = i % (D / 16);
           s_next[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qb[cc], cc == 0 ? f32x16{} : s_next[t], 0, 0, 0);
           exps(i);
           __builtin_amdgcn_sched_barrier(0);
@@ -1206,10 +1219,26 @@ __global__ __launch_bounds__(64 * (TQ / 32), (TK == 128 && TQ == 128) ? 1 : 2) v
         if (j + 1 < nent) tile(j + 1, Odd{}, sb, sa);
       }
     } else {
-      for (int j = 0; j < nent; ++j) {
-        tile(j, Even{}, sa, sb);  // the buffers follow j itself
+      if constexpr (ALIAS) {
+        // Tile j+1's blocks 0 .. NKB-2 go straight into sa (see next_frag);
+        // its last block goes to sb and is copied.
+        struct SView {
+          f32x16 *p[C::NKB];
+          __device__ f32x16 &operator[](int t) const { return *p[t]; }
+        };
+        SView cur{}, nxt{};
 #pragma unroll
-        for (int t = 0; t < C::NKB; ++t) sa[t] = sb[t];
+        for (int t = 0; t < C::NKB; ++t) cur.p[t] = &sa[t], nxt.p[t] = t + 1 < C::NKB ? &sa[t] : &sb[t];
+        for (int j = 0; j < nent; ++j) {
+          tile(j, Even{}, cur, nxt);  // the buffers follow j itself
+          sa[C::NKB - 1] = sb[C::NKB - 1];
+        }
+      } else {
+        for (int j = 0; j < nent; ++j) {
+          tile(j, Even{}, sa, sb);  // the buffers follow j itself
+#pragma unroll
+          for (int t = 0; t < C::NKB; ++t) sa[t] = sb[t];
+        }
       }
     }
     __syncthreads();  // the next item's first loads reuse the buffers
