@@ -26,6 +26,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kScanBlock = 1024;  // elements per scan workgroup (4 per thread)
 constexpr int kLptKeys = 1024;    // longest-first key = min(item length, 1023)
+constexpr int kRowBatch = 8;      // mask loads in flight per lane (k_row_features)
+constexpr int kMapBatch = 8;      // key tiles per lane tested together (k_map)
 
 #define HIP_TRY(expr)                                                          \
   do {                                                                         \
@@ -77,7 +79,9 @@ __global__ void k_row_features(const uint8_t *__restrict__ mask, const HeadMeta 
                                int causal, int64_t off, int64_t Sq, int32_t *__restrict__ rowf,
                                unsigned long long *__restrict__ bits, int64_t bits_per_bm) {
   const int lane = threadIdx.x & 63;
-  const int64_t wv = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 6;
+  // one row per wave: the index is wave-uniform, so the head search, the
+  // head metadata and the row's base address are scalar
+  const int64_t wv = blockIdx.x * (int64_t)(blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wv >= nbm * rows_per_bm) return;
   const int bm = (int)(wv / rows_per_bm);
   const int64_t r = wv % rows_per_bm;
@@ -98,14 +102,38 @@ __global__ void k_row_features(const uint8_t *__restrict__ mask, const HeadMeta 
   int cnt = 0, eff = 0;
   // the row as a bitmap, one 64-bit word per 64 key blocks (when kept)
   unsigned long long *brow = bits ? bits + bm * bits_per_bm + m.bits_off + qb * ((m.nkb + 63) >> 6) : nullptr;
-  for (int64_t kb = lane; kb < m.nkb; kb += 64) {
-    const int sel = row[kb] != 0;
-    cnt += sel;
-    const int es = urow ? (urow[kb] != 0) : sel;
-    eff += es && kb <= kbmax;
-    const unsigned long long word = __ballot(sel);
-    if (brow && lane == 0) brow[kb >> 6] = word;
-  }
+  const int nkb = (int)m.nkb, kbm = (int)min<int64_t>(kbmax, nkb);  // key blocks are below 2^31
+  // kRowBatch mask bytes per lane are loaded before any is tested, so a wave
+  // waits once per 64 * kRowBatch key blocks rather than once per 64 (the
+  // kernel is bound by those waits). The loads take a clamped index and are
+  // tested afterwards, with no branch between them (a load under a lane
+  // condition would be waited for at once); lane u stores the batch's word u.
+  auto scan_row = [&](auto has_union) {
+    constexpr bool HU = decltype(has_union)::value;
+    for (int kb0 = 0; kb0 < nkb; kb0 += 64 * kRowBatch) {
+      uint8_t v[kRowBatch], uv[kRowBatch];
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) {
+        const uint32_t kc = (uint32_t)min(kb0 + 64 * u + lane, nkb - 1);
+        v[u] = row[kc];
+        if constexpr (HU) uv[u] = urow[kc];
+      }
+      unsigned long long mine = 0;
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) {
+        const int kb = kb0 + 64 * u + lane;
+        const int sel = kb < nkb && v[u] != 0;
+        cnt += sel;
+        const int es = HU ? (kb < nkb && uv[u] != 0) : sel;
+        eff += es && kb <= kbm;
+        const unsigned long long word = __ballot(sel);
+        if (lane == u) mine = word;
+      }
+      if (brow && lane < kRowBatch && kb0 + 64 * lane < nkb) brow[(kb0 >> 6) + lane] = mine;
+    }
+  };
+  if (urow) scan_row(std::true_type{});
+  else scan_row(std::false_type{});
   cnt = wave_sum(cnt);
   eff = wave_sum(eff);
   if (lane == 0) {
@@ -254,6 +282,8 @@ __global__ void k_check_pages(const int32_t *__restrict__ table, int B, int pps,
 struct MapArgs {
   const uint8_t *mask, *U;
   const bsa_acsr_head *acsr;  // affine row descriptors in place of mask bytes (ACSR plans)
+  const unsigned long long *bits;  // row bitmaps of the features pass (mask plans without union)
+  int64_t bits_per_bm;
   const HeadMeta *hm;
   const int32_t *page_table;
   int64_t mask_bstride, unkb, Sq, off, nqt, nkt, nlists;
@@ -312,7 +342,7 @@ __device__ __forceinline__ uint32_t live_bits(const MapArgs &a, int bm, int h, i
 
 // One wave per list. EMIT = false: count live tiles. EMIT = true: write them
 // at list_off[l] in ascending key-tile order (ballot + prefix popcount).
-template <bool EMIT>
+template <bool EMIT, bool BITS>
 __global__ void k_map(MapArgs a) {
   const int lane = threadIdx.x & 63;
   // one list per wave: the index is wave-uniform, so head metadata and
@@ -336,6 +366,75 @@ __global__ void k_map(MapArgs a) {
   const int ltq = __builtin_ctz(a.tq), ltk = __builtin_ctz(a.tk);
   const int mq = (!a.uni && m.bq < a.tq) ? 1 << (ltq - lbq) : 1;
   const int mk = m.bk < a.tk ? 1 << (ltk - lbk) : 1;
+  // Tile kt of the list is entry `run + (live tiles of lower lanes)` when
+  // live: entries come out in ascending key-tile order.
+  auto emit = [&](int kt, uint32_t live) {
+    const unsigned long long bal = __ballot(live != 0);
+    if (EMIT && live) {
+      const int64_t idx = base + run + __popcll(bal & (unsigned long long)lo_mask(lane));
+      a.ent_kt[idx] = (int32_t)kt;
+      a.ent_live[idx] = live;
+      if (a.paged) a.ent_page[idx] = a.page_table[(int64_t)lb * a.pps + (int)(kt * a.tk) / a.P];
+    }
+    run += __popcll(bal);
+  };
+  if constexpr (BITS) {
+    // Mask plans without union whose heads all have key blocks of at least
+    // one tile (bk >= tk) and at most 8 query sub-blocks per tile (the host
+    // launches this form only then): the 64 key tiles of a chunk fall in one
+    // 64-bit word of each row's bitmap (written by the features pass: bit kb
+    // of row qb is set iff the mask selects (qb, kb)), so a chunk costs one
+    // scalar load per query sub-block and a shift per lane, and no mask byte
+    // is read.
+    const int nkt32 = (int)a.nkt, sh = lbk - ltk;
+    const int64_t words = (m.nkb + 63) >> 6, aq = m.bq < a.tq ? m.bq : a.tq;
+    const unsigned long long *hb = a.bits + bm * a.bits_per_bm + m.bits_off;
+    const unsigned long long *wr[8];  // the sub-blocks' row bitmaps (null: no such row)
+    int klim[8];  // last key tile whose first key is within the causal limit
+#pragma unroll
+    for (int iq = 0; iq < 8; ++iq) {
+      wr[iq] = nullptr, klim[iq] = -1;
+      if (iq >= mq) continue;
+      const int64_t qb = m.bq < a.tq ? qblock_of(qt, iq, m.lqil, ltq - lbq, m.nqb) : (qt << ltq) >> lbq;
+      if (qb >= m.nqb) continue;
+      wr[iq] = hb + qb * words;
+      const int64_t q0 = m.bq < a.tq ? qb * m.bq : qt * a.tq;
+      // a sub-block is dropped when its first key lies after its last query
+      const int64_t lim = a.causal ? min(q0 + aq, a.Sq) - 1 + a.off : INT64_MAX;
+      klim[iq] = lim < 0 ? -1 : (int)min<int64_t>(lim >> ltk, INT32_MAX);
+    }
+    // Each row's bitmap is read 64 words at a time, one word per lane (one
+    // coalesced load per row, all rows' loads before any wait); a chunk
+    // takes its word from the lane that holds it.
+    for (int64_t wbase = 0; wbase < words; wbase += 64) {
+      unsigned long long rw[8];
+      const int64_t wl = min(wbase + lane, words - 1);
+#pragma unroll
+      for (int iq = 0; iq < 8; ++iq) rw[iq] = wr[iq] ? wr[iq][wl] : 0ull;
+      // the chunks of 64 key tiles whose key blocks lie in these words
+      const int kbeg = (int)((64 * wbase) << sh);
+      const int kend = (int)min<int64_t>(nkt32, (64 * (wbase + 64)) << sh);
+      for (int k0 = kbeg; k0 < kend; k0 += 64) {
+        const int kt = k0 + lane, kb0 = k0 >> sh;   // kb0: first key block of the chunk
+        const int bit = (kb0 & 63) + (lane >> sh);  // < 64: 64 >> sh divides kb0
+        const int wi = (int)((kb0 >> 6) - wbase);   // the lane holding the chunk's word
+        uint32_t live = 0;
+#pragma unroll
+        for (int iq = 0; iq < 8; ++iq) {
+          if (!wr[iq]) continue;
+          const unsigned long long wd =
+              ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(rw[iq] >> 32), wi) << 32) |
+              (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)rw[iq], wi);
+          if (((wd >> bit) & 1ull) && kt <= klim[iq]) live |= 1u << iq;
+        }
+        // (past the last tile a key block may still exist: Skv need not be a
+        // multiple of bk)
+        emit(kt, kt < nkt32 ? live : 0u);
+      }
+    }
+    if (!EMIT && lane == 0) a.list_len[l] = (int32_t)run;
+    return;
+  }
   if (!a.uni && !a.acsr && mq <= 8) {
     // Mask plans: the list's query blocks, their mask rows and causal
     // limits do not depend on the key tile, so they are found once (the same
@@ -350,25 +449,53 @@ __global__ void k_map(MapArgs a) {
       // a sub-block is dropped when its first key lies after its last query
       lim[iq] = a.causal ? min(q0 + aq, a.Sq) - 1 + a.off : INT64_MAX;
     }
-    for (int64_t k0 = 0; k0 < a.nkt; k0 += 64) {
-      const int64_t kt = k0 + lane;
-      uint32_t live = 0;
-      if (kt < a.nkt)
-        for (int ik = 0; ik < mk; ++ik) {
-          const int64_t kb = m.bk < a.tk ? tile_key_block(m, ltk - lbk, kt, ik) : (kt << ltk) >> lbk;
-          if (kb >= m.nkb) continue;
-          const int64_t kfirst = kt * a.tk + ik * ak;
-          for (int iq = 0; iq < mq; ++iq)
-            if (rowoff[iq] >= 0 && mb[rowoff[iq] + kb] && kfirst <= lim[iq]) live |= 1u << (iq * mk + ik);
+    const int nkb32 = (int)m.nkb, nkt32 = (int)a.nkt;
+    // kMapBatch key tiles per lane at a time: for each key sub-block and
+    // pair of query sub-blocks, the batch's mask bytes of both rows are
+    // loaded before any is tested, so a wave waits once per pair and batch
+    // rather than once per row and 64 tiles (the kernel is bound by those
+    // waits). Loads take a clamped index (a missing row reads row iq0 again)
+    // and are tested afterwards: a load under a lane condition would be
+    // waited for at once. Key tiles, key blocks and key positions are below
+    // 2^31, so the indices are 32-bit.
+    for (int k0 = 0; k0 < nkt32; k0 += 64 * kMapBatch) {
+      uint32_t live[kMapBatch];
+#pragma unroll
+      for (int u = 0; u < kMapBatch; ++u) live[u] = 0;
+      for (int ik = 0; ik < mk; ++ik) {
+        int kb[kMapBatch];
+#pragma unroll
+        for (int u = 0; u < kMapBatch; ++u) {
+          const int kt = k0 + 64 * u + lane;
+          kb[u] = kt >= nkt32 ? nkb32
+                  : (m.bk < a.tk ? (int)tile_key_block(m, ltk - lbk, kt, ik) : (int)(((uint32_t)kt << ltk) >> lbk));
         }
-      const unsigned long long bal = __ballot(live != 0);
-      if (EMIT && live) {
-        const int64_t idx = base + run + __popcll(bal & (unsigned long long)lo_mask(lane));
-        a.ent_kt[idx] = (int32_t)kt;
-        a.ent_live[idx] = live;
-        if (a.paged) a.ent_page[idx] = a.page_table[(int64_t)lb * a.pps + (int)(kt * a.tk) / a.P];
+#pragma unroll
+        for (int iq0 = 0; iq0 < 8; iq0 += 2) {  // (unrolled: rowoff and lim stay in registers)
+          if (iq0 >= mq) break;
+          const bool r0 = rowoff[iq0] >= 0, r1 = iq0 + 1 < mq && rowoff[iq0 + 1] >= 0;
+          if (!r0 && !r1) continue;
+          const uint8_t *m0 = mb + (r0 ? rowoff[iq0] : rowoff[iq0 + 1]);
+          const uint8_t *m1 = r1 ? mb + rowoff[iq0 + 1] : m0;
+          uint8_t v0[kMapBatch], v1[kMapBatch];
+#pragma unroll
+          for (int u = 0; u < kMapBatch; ++u) {
+            const uint32_t kc = (uint32_t)min(kb[u], nkb32 - 1);
+            v0[u] = m0[kc];
+            v1[u] = m1[kc];
+          }
+#pragma unroll
+          for (int u = 0; u < kMapBatch; ++u) {
+            if (kb[u] >= nkb32) continue;
+            // first key of the sub-block (exact for every tile that exists)
+            const int64_t kfirst = (int64_t)(k0 + 64 * u + lane) * a.tk + ik * ak;
+            if (r0 && v0[u] && kfirst <= lim[iq0]) live[u] |= 1u << (iq0 * mk + ik);
+            if (r1 && v1[u] && kfirst <= lim[iq0 + 1]) live[u] |= 1u << ((iq0 + 1) * mk + ik);
+          }
+        }
       }
-      run += __popcll(bal);
+#pragma unroll
+      for (int u = 0; u < kMapBatch; ++u) emit(k0 + 64 * u + lane, live[u]);
     }
     if (!EMIT && lane == 0) a.list_len[l] = (int32_t)run;
     return;
@@ -462,43 +589,58 @@ __global__ void k_scan_apply(const int32_t *in, int64_t n, const int32_t *__rest
   if (blockIdx.x == gridDim.x - 1 && threadIdx.x == kThreads - 1) out[n] = run;
 }
 
-// Whole scan in one workgroup (small arrays): each of 1024 threads owns a
-// contiguous segment, sums it (all loads in flight at once), the workgroup
-// scans the sums, and each thread rewrites its segment from its prefix. in
-// and out may be the same array (a thread reads each element before writing
-// it and touches only its own segment). Workgroup g scans the g-th of
-// gridDim.x arrays laid out `stride` elements apart.
-constexpr int kScanThreads = 1024;
+// Whole scan in one workgroup (small arrays), in batches of kScanBatch
+// rounds of 1024 consecutive elements: every thread loads its element of
+// each round of the batch (coalesced, all loads in flight at once), the waves
+// scan their 64-element pieces, and after one barrier each thread adds the
+// totals of the pieces before its own and of the earlier rounds. in and out
+// may be the same array (each element is read by the thread that writes it,
+// before it writes it). Workgroup g scans the g-th of gridDim.x arrays laid
+// out `stride` elements apart; out[n] receives the total.
+constexpr int kScanThreads = 1024, kScanBatch = 8;
 __global__ __launch_bounds__(kScanThreads) void k_scan_single(const int32_t *in, int64_t n,
                                                               int32_t *out, int64_t stride) {
-  __shared__ int wsum[kScanThreads / 64];
+  constexpr int NW = kScanThreads / 64;
+  __shared__ int wsum[kScanBatch][NW];
   in += blockIdx.x * stride;
   out += blockIdx.x * stride;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int64_t seg = (n + kScanThreads - 1) / kScanThreads;
-  const int64_t b0 = min(n, (int64_t)t * seg), b1 = min(n, b0 + seg);
-  int sum = 0;
-#pragma unroll 8
-  for (int64_t i = b0; i < b1; ++i) sum += in[i];
-  int x = sum;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
+  int carry = 0;  // total of the batches before this one
+  for (int64_t b0 = 0; b0 < n; b0 += (int64_t)kScanBatch * kScanThreads) {
+    int v[kScanBatch], x[kScanBatch];
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) {
+      // a clamped index, zeroed after the load (a load under a lane
+      // condition would be waited for at once)
+      const int64_t i = b0 + (int64_t)u * kScanThreads + t;
+      v[u] = in[min(i, n - 1)];
+      if (i >= n) v[u] = 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) {
+      x[u] = v[u];
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x[u], o);
+        if (lane >= o) x[u] += y;
+      }
+      if (lane == 63) wsum[u][w] = x[u];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) {
+      int before = 0, tot = 0;
+      for (int i = 0; i < NW; ++i) {
+        const int s = wsum[u][i];
+        before += i < w ? s : 0;
+        tot += s;
+      }
+      const int64_t i = b0 + (int64_t)u * kScanThreads + t;
+      if (i < n) out[i] = carry + before + x[u] - v[u];
+      carry += tot;
+    }
+    __syncthreads();  // wsum is rewritten by the next batch
   }
-  if (lane == 63) wsum[w] = x;
-  __syncthreads();
-  int before = 0, tot = 0;
-  for (int i = 0; i < kScanThreads / 64; ++i) {
-    before += i < w ? wsum[i] : 0;
-    tot += wsum[i];
-  }
-  int run = before + x - sum;
-  for (int64_t i = b0; i < b1; ++i) {
-    const int v = in[i];
-    out[i] = run;
-    run += v;
-  }
-  if (t == 0) out[n] = tot;
+  if (t == 0) out[n] = carry;
 }
 
 constexpr int64_t kSingleScanMax = 1 << 16;
@@ -908,6 +1050,7 @@ bsa_status plan_build(Plan &p, const uint8_t *mask, const int32_t *page_table, v
 
   MapArgs m{};
   m.mask = mask, m.U = p.uni_bits, m.acsr = p.acsr, m.hm = p.hmeta, m.page_table = page_table;
+  m.bits = p.row_bits, m.bits_per_bm = p.bits_per_bm;
   int64_t mask_bstride = 0;
   for (int h = 0; h < p.Hq; ++h)
     mask_bstride += ((p.Sq + p.bq[h] - 1) / p.bq[h]) * ((p.Skv + p.bk[h] - 1) / p.bk[h]);
@@ -919,9 +1062,19 @@ bsa_status plan_build(Plan &p, const uint8_t *mask, const int32_t *page_table, v
   m.ent_kt = p.ent_kt, m.ent_page = p.ent_page, m.ent_live = p.ent_live;
 
   const unsigned gl = grid_for(p.nlists * 64);
-  if (p.nlists > 0) hipLaunchKernelGGL(k_map<false>, dim3(gl), dim3(kThreads), 0, s, m);
+  // The bitmap form of k_map when every head allows it.
+  bool bits = p.row_bits != nullptr && !p.uni && !p.acsr;
+  for (int h = 0; h < p.Hq && bits; ++h)
+    bits = p.bk[h] >= p.rg.tk && (p.bq[h] >= p.rg.tq || p.rg.tq / p.bq[h] <= 8);
+  if (p.nlists > 0) {
+    if (bits) hipLaunchKernelGGL((k_map<false, true>), dim3(gl), dim3(kThreads), 0, s, m);
+    else hipLaunchKernelGGL((k_map<false, false>), dim3(gl), dim3(kThreads), 0, s, m);
+  }
   if (bsa_status st = scan(list_len, p.nlists, p.list_off, bsum, s)) return st;
-  if (p.nlists > 0) hipLaunchKernelGGL(k_map<true>, dim3(gl), dim3(kThreads), 0, s, m);
+  if (p.nlists > 0) {
+    if (bits) hipLaunchKernelGGL((k_map<true, true>), dim3(gl), dim3(kThreads), 0, s, m);
+    else hipLaunchKernelGGL((k_map<true, false>), dim3(gl), dim3(kThreads), 0, s, m);
+  }
 
   RowArgs ra{};
   ra.list_off = p.list_off, ra.ent_kt = p.ent_kt, ra.row_ent = p.row_ent;
