@@ -43,6 +43,27 @@ __device__ __forceinline__ int wave_sum(int x) {
 
 __device__ __forceinline__ int64_t lo_mask(int lane) { return (int64_t)((1ull << lane) - 1ull); }
 
+// The n lowest bits set (none for n <= 0, all for n >= 64).
+__device__ __forceinline__ unsigned long long prefix_mask(int64_t n) {
+  return n <= 0 ? 0ull : (n >= 64 ? ~0ull : (1ull << n) - 1ull);
+}
+
+// Key-block bits to key-tile bits when a block spans 2^sh tiles: the low
+// 64 >> sh bits of x, each repeated 2^sh times (sh >= 6: bit 0 for all 64).
+__device__ __forceinline__ unsigned long long spread_bits(unsigned long long x, int sh) {
+  if (sh >= 6) return (x & 1ull) ? ~0ull : 0ull;
+  x &= sh == 0 ? ~0ull : (1ull << (64 >> sh)) - 1ull;
+  for (int i = 0; i < sh; ++i) {  // each pass doubles every bit of the low 32
+    x = (x | (x << 16)) & 0x0000FFFF0000FFFFull;
+    x = (x | (x << 8)) & 0x00FF00FF00FF00FFull;
+    x = (x | (x << 4)) & 0x0F0F0F0F0F0F0F0Full;
+    x = (x | (x << 2)) & 0x3333333333333333ull;
+    x = (x | (x << 1)) & 0x5555555555555555ull;
+    x |= x << 1;
+  }
+  return x;
+}
+
 // -------------------------------------------------------------------------
 // Mask features and group union
 // -------------------------------------------------------------------------
@@ -402,6 +423,28 @@ __global__ void k_map(MapArgs a) {
       // a sub-block is dropped when its first key lies after its last query
       const int64_t lim = a.causal ? min(q0 + aq, a.Sq) - 1 + a.off : INT64_MAX;
       klim[iq] = lim < 0 ? -1 : (int)min<int64_t>(lim >> ltk, INT32_MAX);
+    }
+    if constexpr (!EMIT) {
+      // Count only: lane j takes chunk j (key tiles 64 j .. 64 j + 63) of
+      // each group of 64 chunks, builds its 64-bit live-tile mask from the
+      // rows' bitmap fields (each key block's bit spread over its 2^sh
+      // tiles, then cut at the causal limit and the last tile) and counts it.
+      int cnt = 0;
+      for (int c0 = 0; (int64_t)c0 * 64 < nkt32; c0 += 64) {
+        const int k0 = (c0 + lane) * 64;  // this lane's first tile (maybe past the end)
+        const int kb0 = k0 >> sh;
+        const int64_t wi = min<int64_t>(kb0 >> 6, words - 1);
+        unsigned long long any = 0;
+#pragma unroll
+        for (int iq = 0; iq < 8; ++iq) {
+          if (!wr[iq]) continue;
+          any |= spread_bits(wr[iq][wi] >> (kb0 & 63), sh) & prefix_mask((int64_t)klim[iq] - k0 + 1);
+        }
+        cnt += __popcll(any & prefix_mask((int64_t)nkt32 - k0));
+      }
+      cnt = wave_sum(cnt);
+      if (lane == 0) a.list_len[l] = (int32_t)cnt;
+      return;
     }
     // Each row's bitmap is read 64 words at a time, one word per lane (one
     // coalesced load per row, all rows' loads before any wait); a chunk
