@@ -456,14 +456,18 @@ def main():
     ms_pipe = timed(False)[0] if args.pipeline else None
 
     # Plan-only timing (the planner's own cost, one feature readback included
-    # for mask plans).
-    torch.cuda.synchronize()
-    tp = time.perf_counter()
-    for _ in range(5):
+    # for mask plans): host time from the call to its kernels' end, median of
+    # 20 after 3 warm-up plans.
+    plan_times = []
+    for i in range(23):
+        torch.cuda.synchronize()
+        tp = time.perf_counter()
         p = make_plan(stream)
         torch.cuda.synchronize()
+        if i >= 3:
+            plan_times.append((time.perf_counter() - tp) * 1e3)
         p.free()
-    plan_ms = (time.perf_counter() - tp) * 1e3 / 5
+    plan_ms = float(np.median(plan_times))
 
     select = None
     if sel_keep is not None:
