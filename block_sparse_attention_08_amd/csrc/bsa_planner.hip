@@ -478,6 +478,39 @@ __global__ void k_map(MapArgs a) {
     if (!EMIT && lane == 0) a.list_len[l] = (int32_t)run;
     return;
   }
+  if (a.uni && !a.acsr) {
+    // Union lists (one per batch and kv group, so few waves, each waiting on
+    // its own loads): the group's union row, kMapBatch key tiles per lane,
+    // each byte loaded at a clamped index before any is tested. The same
+    // live bits as live_bits below: one query sub-block, and no causal cut
+    // (the union spans every query block of the group).
+    const uint8_t *urow = a.U + ((int64_t)bm * a.Hkv + g) * a.unkb;
+    const int nkb32 = (int)m.nkb, nkt32 = (int)a.nkt;  // below 2^31
+    for (int k0 = 0; k0 < nkt32; k0 += 64 * kMapBatch) {
+      uint32_t live[kMapBatch];
+#pragma unroll
+      for (int u = 0; u < kMapBatch; ++u) live[u] = 0;
+      for (int ik = 0; ik < mk; ++ik) {
+        int kb[kMapBatch];
+        uint8_t v[kMapBatch];
+#pragma unroll
+        for (int u = 0; u < kMapBatch; ++u) {
+          const int kt = k0 + 64 * u + lane;
+          kb[u] = kt >= nkt32 ? nkb32
+                  : (m.bk < a.tk ? (int)tile_key_block(m, ltk - lbk, kt, ik) : (int)(((uint32_t)kt << ltk) >> lbk));
+        }
+#pragma unroll
+        for (int u = 0; u < kMapBatch; ++u) v[u] = urow[(uint32_t)min(kb[u], nkb32 - 1)];
+#pragma unroll
+        for (int u = 0; u < kMapBatch; ++u)
+          if (kb[u] < nkb32 && v[u]) live[u] |= 1u << ik;
+      }
+#pragma unroll
+      for (int u = 0; u < kMapBatch; ++u) emit(k0 + 64 * u + lane, live[u]);
+    }
+    if (!EMIT && lane == 0) a.list_len[l] = (int32_t)run;
+    return;
+  }
   if (!a.uni && !a.acsr && mq <= 8) {
     // Mask plans: the list's query blocks, their mask rows and causal
     // limits do not depend on the key tile, so they are found once (the same
