@@ -1330,36 +1330,79 @@ __global__ __launch_bounds__(kThreads) void k_combine(AttnArgs a, const int32_t 
       const RowPos geo = tile_row(a, r, row);
       const int64_t qpos = geo.q;
       if (qpos >= a.Sq) continue;
-      float M = -INFINITY;
-      for (int s = lane; s < k; s += 64) M = fmaxf(M, a.part_lse[(int64_t)(s0 + s) * TQ + row]);
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
       E *op = (E *)a.o + geo.b * a.o_sb + geo.head * a.o_sh + qpos * a.o_ss;
       float *lp = a.lse + ((int64_t)geo.b * a.Hq + geo.head) * a.Sq + qpos;
+      float M = -INFINITY, ws = 0.f;
+      float acc[CPL];
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) acc[j] = 0.f;
+      // The partial row of slot s at this lane's columns.
+      auto part = [&](int s, float *x) {
+        const float *src = a.part_o + ((int64_t)(s0 + s) * TQ + row) * D + CPL * lane;
+        if constexpr (CPL == 2) {
+          const float2 v = *(const float2 *)src;
+          x[0] = v.x, x[1] = v.y;
+        } else {
+          x[0] = src[0];
+        }
+      };
+      if (k <= 64) {
+        // One round of loads: lane s holds slot s's LSE, and the partial
+        // rows of the first kAhead slots are read beside it (they do not
+        // depend on the maximum); each slot's weight exp(lse_s - M) is then
+        // taken from the lane that holds it.
+        constexpr int kAhead = 8;
+        const float l = lane < k ? a.part_lse[(int64_t)(s0 + lane) * TQ + row] : -INFINITY;
+        float x[kAhead][CPL];
+#pragma unroll
+        for (int s = 0; s < kAhead; ++s)
+          if (s < k) part(s, x[s]);
+        M = l;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+        if (M != -INFINITY) {
+          const float wl = lane < k ? expf(l - M) : 0.f;
+          ws = wl;
+#pragma unroll
+          for (int o = 32; o >= 1; o >>= 1) ws += __shfl_xor(ws, o);
+#pragma unroll
+          for (int s = 0; s < kAhead; ++s)
+            if (s < k) {
+              const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s));
+#pragma unroll
+              for (int j = 0; j < CPL; ++j) acc[j] += w * x[s][j];
+            }
+          for (int s = kAhead; s < k; ++s) {
+            const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s));
+            float y[CPL];
+            part(s, y);
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) acc[j] += w * y[j];
+          }
+        }
+      } else {
+        for (int s = lane; s < k; s += 64) M = fmaxf(M, a.part_lse[(int64_t)(s0 + s) * TQ + row]);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+        if (M != -INFINITY) {
+          for (int s = lane; s < k; s += 64) ws += expf(a.part_lse[(int64_t)(s0 + s) * TQ + row] - M);
+#pragma unroll
+          for (int o = 32; o >= 1; o >>= 1) ws += __shfl_xor(ws, o);
+#pragma unroll 4
+          for (int s = 0; s < k; ++s) {
+            const float w = expf(a.part_lse[(int64_t)(s0 + s) * TQ + row] - M);
+            float y[CPL];
+            part(s, y);
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) acc[j] += w * y[j];
+          }
+        }
+      }
       if (M == -INFINITY) {
 #pragma unroll
         for (int j = 0; j < CPL; ++j) op[CPL * lane + j] = (E)0;
         if (lane == 0) *lp = -INFINITY;
         continue;
-      }
-      float ws = 0.f;
-      for (int s = lane; s < k; s += 64) ws += expf(a.part_lse[(int64_t)(s0 + s) * TQ + row] - M);
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) ws += __shfl_xor(ws, o);
-      float acc[CPL];
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) acc[j] = 0.f;
-#pragma unroll 4
-      for (int s = 0; s < k; ++s) {
-        const int64_t prow = (int64_t)(s0 + s) * TQ + row;
-        const float w = expf(a.part_lse[prow] - M);
-        const float *src = a.part_o + prow * D + CPL * lane;
-        if constexpr (CPL == 2) {
-          const float2 x = *(const float2 *)src;
-          acc[0] += w * x.x, acc[1] += w * x.y;
-        } else {
-          acc[0] += w * src[0];
-        }
       }
       const float inv = 1.f / ws;
       if constexpr (BF && CPL == 2) {
