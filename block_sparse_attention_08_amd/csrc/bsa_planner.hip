@@ -404,9 +404,8 @@ __global__ void k_map(MapArgs a) {
     // one tile (bk >= tk) and at most 8 query sub-blocks per tile (the host
     // launches this form only then): the 64 key tiles of a chunk fall in one
     // 64-bit word of each row's bitmap (written by the features pass: bit kb
-    // of row qb is set iff the mask selects (qb, kb)), so a chunk costs one
-    // scalar load per query sub-block and a shift per lane, and no mask byte
-    // is read.
+    // of row qb is set iff the mask selects (qb, kb)), so a chunk costs a few
+    // shifts per lane and query sub-block, and no mask byte is read.
     const int nkt32 = (int)a.nkt, sh = lbk - ltk;
     const int64_t words = (m.nkb + 63) >> 6, aq = m.bq < a.tq ? m.bq : a.tq;
     const unsigned long long *hb = a.bits + bm * a.bits_per_bm + m.bits_off;
@@ -459,7 +458,7 @@ __global__ void k_map(MapArgs a) {
       const int kend = (int)min<int64_t>(nkt32, (64 * (wbase + 64)) << sh);
       for (int k0 = kbeg; k0 < kend; k0 += 64) {
         const int kt = k0 + lane, kb0 = k0 >> sh;   // kb0: first key block of the chunk
-        const int bit = (kb0 & 63) + (lane >> sh);  // < 64: 64 >> sh divides kb0
+        const int bit = (kb0 & 63) + (lane >> sh);  // < 64: the chunk's blocks share a word
         const int wi = (int)((kb0 >> 6) - wbase);   // the lane holding the chunk's word
         uint32_t live = 0;
 #pragma unroll
@@ -475,7 +474,6 @@ __global__ void k_map(MapArgs a) {
         emit(kt, kt < nkt32 ? live : 0u);
       }
     }
-    if (!EMIT && lane == 0) a.list_len[l] = (int32_t)run;
     return;
   }
   if (a.uni && !a.acsr) {
