@@ -162,6 +162,20 @@ __device__ __forceinline__ uint32_t lds_addr_of(const uint8_t *p) {
 // past the sequence end read as zero), two buffers, the next tile's loads in
 // flight while the current one is computed. K is read as rows (the S^T
 // operand) and transposed (the K^T operand of dQ^T); V as rows.
+// Work item of workgroup b in a grid of n: workgroups are dispatched
+// round-robin over the 8 XCDs (workgroup b on XCD b % 8), so blocks of
+// kXcdRun consecutive items go to one XCD, the 8 XCDs taking 8 neighbouring
+// blocks at a time: the tiles that neighbouring items share (the query
+// tiles of a window, the key groups they see) stay in one XCD's L2. The
+// items past the last whole group of 8 * kXcdRun keep their own order.
+constexpr int kXcdRun = 64;
+__device__ __forceinline__ int xcd_item(int b, int n) {
+  const int full = n / (8 * kXcdRun) * (8 * kXcdRun);
+  if (b >= full) return b;
+  const int x = b & 7, i = b >> 3;
+  return ((i / kXcdRun) * 8 + x) * kXcdRun + i % kXcdRun;
+}
+
 template <int D, int TK, int TQ, bool KIL = false>
 __global__ __launch_bounds__(2 * TQ, TQ == 128 ? 2 : 1) void k_bwd_dq(BwdArgs a) {
   constexpr int T = 2 * TQ;                     // 64 lanes per 32 query rows
@@ -178,7 +192,7 @@ __global__ __launch_bounds__(2 * TQ, TQ == 128 ? 2 : 1) void k_bwd_dq(BwdArgs a)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hh = lane >> 5;
-  const int r = blockIdx.x;
+  const int r = xcd_item(blockIdx.x, gridDim.x);
   const int nqt = (int)a.nqt;
   const int nh = a.pack ? a.Hkv : a.Hq;
   const int qt = r % nqt, hrow = (r / nqt) % nh, b = r / (nqt * nh);
@@ -391,7 +405,7 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdArgs a) {
   const int n = lane & 31, hh = lane >> 5;
   const int nkt = (int)a.nkt, nqt = (int)a.nqt;
   const int nkp = (nkt + NKT - 1) / NKT;
-  const int item = blockIdx.x;
+  const int item = xcd_item(blockIdx.x, gridDim.x);
   const int kp = item % nkp, g = (item / nkp) % a.Hkv, b = item / (nkp * a.Hkv);
   const int kt0 = kp * NKT;
   const int wkt = (32 * wave) / TKP;            // this wave's tile within the group
