@@ -19,6 +19,7 @@
 #include <algorithm>
 #include <climits>
 #include <string>
+#include <type_traits>
 
 #include "bsa_internal.h"
 
@@ -65,91 +66,102 @@ __device__ __forceinline__ int2 query_block(const SelHeads &hs, int x) {
   return make_int2(h, x - hs.qm_off[h]);
 }
 
-// 8 consecutive elements (columns c0 .. c0+7 of one row) as fp32.
-__device__ __forceinline__ void load8(const SelArgs &a, const void *base, int64_t idx, float (&x)[8]) {
-  if (a.bf16) {
-    const uint4 v = *(const uint4 *)((const uint16_t *)base + idx);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      x[2 * u] = __uint_as_float(w[u] << 16);
-      x[2 * u + 1] = __uint_as_float(w[u] & 0xffff0000u);
-    }
+constexpr int kPoolRows = 16;  // rows of loads in flight per wave
+
+// Columns c0 .. c0 + CPL - 1 of one row as fp32 (BF: bf16 elements).
+template <int CPL, bool BF>
+__device__ __forceinline__ void load_cols(const void *base, int64_t idx, float (&x)[CPL]) {
+  if constexpr (BF && CPL == 2) {
+    const uint32_t w = *(const uint32_t *)((const uint16_t *)base + idx);
+    x[0] = __uint_as_float(w << 16), x[1] = __uint_as_float(w & 0xffff0000u);
+  } else if constexpr (BF) {
+    x[0] = __uint_as_float((uint32_t)((const uint16_t *)base)[idx] << 16);
+  } else if constexpr (CPL == 2) {
+    const float2 v = *(const float2 *)((const float *)base + idx);
+    x[0] = v.x, x[1] = v.y;
   } else {
-    const float4 p = *(const float4 *)((const float *)base + idx);
-    const float4 q = *(const float4 *)((const float *)base + idx + 4);
-    x[0] = p.x, x[1] = p.y, x[2] = p.z, x[3] = p.w, x[4] = q.x, x[5] = q.y, x[6] = q.z, x[7] = q.w;
+    x[0] = ((const float *)base)[idx];
   }
 }
 
-// Block means: a lane owns 8 consecutive columns of one block and sums them
-// over the block's rows in order (one fp32 addition per row and column), 4
-// rows of loads in flight; a workgroup pools kSelThreads / (D / 8) blocks.
-// row_at(r) gives the element index of column 0 of row r.
-template <typename RowAt>
-__device__ __forceinline__ void pool8(const SelArgs &a, const void *base, int64_t r0, int64_t r1, int c0,
-                                      RowAt row_at, float *out) {
-  float s[8];
+// Adds rows r0 .. r1-1 (row r at element off + r * stride) to the running
+// column sums s, in ascending order, one fp32 addition each. One wave per
+// block: lane l owns columns CPL l .. CPL l + CPL - 1 (CPL = D / 64, so a row
+// is one contiguous read of the wave). kPoolRows rows are loaded before any
+// is added (rows past the end load the last row again and are not added), so
+// a wave waits once per kPoolRows rows.
+template <int CPL, bool BF>
+__device__ __forceinline__ void pool_rows(const void *base, int64_t off, int64_t stride, int64_t r0,
+                                          int64_t r1, float (&s)[CPL]) {
+  const int c0 = CPL * (threadIdx.x & 63);
+  for (int64_t r = r0; r < r1; r += kPoolRows) {
+    float x[kPoolRows][CPL];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) s[u] = 0.0f;
-  int64_t r = r0;
-  for (; r + 4 <= r1; r += 4) {
-    float x[4][8];
+    for (int v = 0; v < kPoolRows; ++v) load_cols<CPL, BF>(base, off + min(r + v, r1 - 1) * stride + c0, x[v]);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) load8(a, base, row_at(r + v) + c0, x[v]);
+    for (int v = 0; v < kPoolRows; ++v)
+      if (r + v < r1)
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-#pragma unroll
-      for (int u = 0; u < 8; ++u) s[u] = __fadd_rn(s[u], x[v][u]);
+        for (int u = 0; u < CPL; ++u) s[u] = __fadd_rn(s[u], x[v][u]);
   }
-  for (; r < r1; ++r) {
-    float x[8];
-    load8(a, base, row_at(r) + c0, x);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) s[u] = __fadd_rn(s[u], x[u]);
-  }
-  const float n = (float)(r1 - r0);
-#pragma unroll
-  for (int u = 0; u < 8; ++u) out[c0 + u] = __fdiv_rn(s[u], n);
 }
 
-// Query block means of one batch: block x of the concatenation over heads.
+// The block mean from its column sums over n rows (one fp32 division).
+template <int CPL>
+__device__ __forceinline__ void store_mean(const float (&s)[CPL], int64_t n, float *out) {
+  const int c0 = CPL * (threadIdx.x & 63);
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) out[c0 + u] = __fdiv_rn(s[u], (float)n);
+}
+
+// Query block means of one batch: one wave per (head, query block).
+template <int CPL, bool BF>
 __global__ __launch_bounds__(kSelThreads) void k_pool_q(SelArgs a, SelHeads hs) {
   const int b = blockIdx.y;
-  const int lanes = a.D / 8, per = kSelThreads / lanes;
-  const int x = blockIdx.x * per + threadIdx.x / lanes;
-  if (threadIdx.x >= per * lanes || x >= a.qm_rows) return;
+  const int x = blockIdx.x * (kSelThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (x >= a.qm_rows) return;
   const int2 hq = query_block(hs, x);
   const int h = hq.x, qb = hq.y;
   const int64_t i0 = (int64_t)qb * hs.bq[h];
   const int64_t i1 = min<int64_t>(a.Sq, i0 + hs.bq[h]);
-  const int64_t base = b * a.q_sb + h * a.q_sh;
-  pool8(a, a.q, i0, i1, 8 * (threadIdx.x % lanes), [&](int64_t i) { return base + i * a.q_ss; },
-        a.qm + ((int64_t)b * a.qm_rows + x) * a.D);
+  float s[CPL];
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) s[u] = 0.0f;
+  pool_rows<CPL, BF>(a.q, b * a.q_sb + h * a.q_sh, a.q_ss, i0, i1, s);
+  store_mean<CPL>(s, i1 - i0, a.qm + ((int64_t)b * a.qm_rows + x) * a.D);
 }
 
 // Key block means of one batch: the key blocks of each distinct (kv group,
-// block size) pair are pooled once, through the page table when K is paged.
+// block size) pair are pooled once, one wave per key block; a paged K is
+// walked page by page (one page-table lookup per page, the sums carried
+// across pages in row order).
+template <int CPL, bool BF>
 __global__ __launch_bounds__(kSelThreads) void k_pool_k(SelArgs a, SelHeads hs) {
   const int b = blockIdx.y;
-  const int lanes = a.D / 8, per = kSelThreads / lanes;
-  const int row = blockIdx.x * per + threadIdx.x / lanes;
-  if (threadIdx.x >= per * lanes || row >= a.km_rows) return;
+  const int row = blockIdx.x * (kSelThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (row >= a.km_rows) return;
   int h = 0;
   while (h < hs.n && !(hs.lead[h] && row >= hs.km_off[h] && row < hs.km_off[h] + hs.nkb[h])) ++h;
   if (h == hs.n) return;  // not reached: the rows are exactly the leaders' key blocks
   const int g = hs.g[h], bk = hs.bk[h], kb = row - hs.km_off[h];
   const int64_t j0 = (int64_t)kb * bk, j1 = min<int64_t>(a.Skv, j0 + bk);
-  auto row_at = [&](int64_t j) -> int64_t {
-    if (a.paged) {
+  float s[CPL];
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) s[u] = 0.0f;
+  if (a.paged) {
+    for (int64_t j = j0; j < j1;) {
+      const int64_t pi = j / a.P, jend = min<int64_t>(j1, (pi + 1) * a.P);
       // entries outside [0, num_pages) are not followed (page 0 is read)
-      int64_t page = a.page_table[(int64_t)b * a.pps + j / a.P];
+      int64_t page = a.page_table[(int64_t)b * a.pps + pi];
       page = (page < 0 || page >= a.npages) ? 0 : page;
-      return page * a.k_sb + (j % a.P) * a.k_ss + g * a.k_sh;
+      // key j' of this page sits at page * k_sb + (j' - pi P) * k_ss + g * k_sh
+      pool_rows<CPL, BF>(a.k, page * a.k_sb + g * a.k_sh - pi * a.P * a.k_ss, a.k_ss, j, jend, s);
+      j = jend;
     }
-    return b * a.k_sb + g * a.k_sh + j * a.k_ss;
-  };
-  pool8(a, a.k, j0, j1, 8 * (threadIdx.x % lanes), row_at, a.km + ((int64_t)b * a.km_rows + row) * a.D);
+  } else {
+    pool_rows<CPL, BF>(a.k, b * a.k_sb + g * a.k_sh, a.k_ss, j0, j1, s);
+  }
+  store_mean<CPL>(s, j1 - j0, a.km + ((int64_t)b * a.km_rows + row) * a.D);
 }
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -280,12 +292,26 @@ bsa_status select_blocks(const bsa_problem &pr, int keep_tenths, int top_k, cons
   a.qm = (float *)scratch;
   a.km = (float *)((uint8_t *)scratch + ((qm_bytes + 255) & ~size_t(255)));
   a.mask = mask;
-  const int per = kSelThreads / (pr.head_dim / 8);  // blocks pooled per workgroup
-  hipLaunchKernelGGL(k_pool_q, dim3((unsigned)((qrows + per - 1) / per), (unsigned)B), dim3(kSelThreads),
-                     0, s, a, hs);
-  if (krows > 0 && pr.seqlen_kv > 0)
-    hipLaunchKernelGGL(k_pool_k, dim3((unsigned)((krows + per - 1) / per), (unsigned)B), dim3(kSelThreads),
-                       0, s, a, hs);
+  const int per = kSelThreads / 64;  // blocks pooled per workgroup (one wave each)
+  // (head_dim is 64 or 128: one or two columns per lane; bf16 or fp32)
+  auto pool = [&](auto cpl, auto bf) {
+    constexpr int CPL = decltype(cpl)::value;
+    constexpr bool BF = decltype(bf)::value;
+    hipLaunchKernelGGL((k_pool_q<CPL, BF>), dim3((unsigned)((qrows + per - 1) / per), (unsigned)B),
+                       dim3(kSelThreads), 0, s, a, hs);
+    if (krows > 0 && pr.seqlen_kv > 0)
+      hipLaunchKernelGGL((k_pool_k<CPL, BF>), dim3((unsigned)((krows + per - 1) / per), (unsigned)B),
+                         dim3(kSelThreads), 0, s, a, hs);
+  };
+  using One = std::integral_constant<int, 1>;
+  using Two = std::integral_constant<int, 2>;
+  if (a.D == 128) {
+    if (a.bf16) pool(Two{}, std::true_type{});
+    else pool(Two{}, std::false_type{});
+  } else {
+    if (a.bf16) pool(One{}, std::true_type{});
+    else pool(One{}, std::false_type{});
+  }
   const size_t lds = sizeof(unsigned long long) * kcap + sizeof(float) * 256 + ((maxk + 15) & ~15);
   hipError_t e = hipSuccess;
   if (lds > (size_t(64) << 10))
