@@ -198,9 +198,17 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelArgs a, SelHeads hs) 
   for (int i = threadIdx.x; i < npow; i += blockDim.x) {
     unsigned long long key = 0;  // padding sorts last
     if (i < ncand) {
-      const float *kr = km + (int64_t)i * a.D;
+      // four columns per load (pooled rows are D floats, 16-byte aligned),
+      // the multiply-adds still in ascending column order
+      const float4 *kr = (const float4 *)(km + (int64_t)i * a.D);
       float sc = 0.0f;
-      for (int d = 0; d < a.D; ++d) sc = __fmaf_rn(qm_s[d], kr[d], sc);
+      for (int d4 = 0; d4 < a.D / 4; ++d4) {
+        const float4 x = kr[d4];
+        sc = __fmaf_rn(qm_s[4 * d4], x.x, sc);
+        sc = __fmaf_rn(qm_s[4 * d4 + 1], x.y, sc);
+        sc = __fmaf_rn(qm_s[4 * d4 + 2], x.z, sc);
+        sc = __fmaf_rn(qm_s[4 * d4 + 3], x.w, sc);
+      }
       key = ((unsigned long long)order_key(sc) << 32) | (0xffffffffu - (uint32_t)i);
     }
     keys[i] = key;
